@@ -1,0 +1,423 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's formula: each checks it against a closed
+form, a brute force, an independent formulation (exact rationals, the
+Schur-complement form of the update, the optimality of the remaining weights)
+or an invariant that a plausible mistake (dropped factor 2, wrong sign,
+transposed operand, off-by-one group boundary, wrong rounding) would break.
+"""
+from fractions import Fraction
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+
+
+# ----------------------------------------------------------------- Hessian --
+def test_hessian_brute_force_integer_exact():
+    rng = np.random.default_rng(0)
+    X = rng.integers(-8, 9, size=(64, 16)).astype(np.float16)
+    H = O.hessian([X[:40], X[40:]])
+    Hb = np.zeros((16, 16))
+    for i in range(16):
+        for j in range(16):
+            acc = 0
+            for t in range(64):
+                acc += int(X[t, i]) * int(X[t, j])
+            Hb[i, j] = 2 * acc
+    assert np.array_equal(H, Hb)
+
+
+def test_hessian_symmetric_psd():
+    X = workloads.x_tokens(workloads.get("c0"), 0, 1).numpy()
+    H = O.hessian(X)
+    assert np.array_equal(H, H.T)
+    ev = np.linalg.eigvalsh(H)
+    assert ev.min() >= -1e-12 * np.abs(H).max()
+
+
+def test_hessian_is_second_difference_of_layer_loss():
+    """L(V) = ||X (V - W0)^T||_F^2 is quadratic; its second difference along E
+    is t^2 * sum_r e_r^T H e_r exactly (this fixes the factor 2 and the operand order)."""
+    rng = np.random.default_rng(1)
+    X = rng.standard_normal((50, 12))
+    W0 = rng.standard_normal((3, 12))
+    E = rng.standard_normal((3, 12))
+    t = 0.125
+
+    def L(V):
+        return float(np.sum((X @ (V - W0).T) ** 2))
+
+    lhs = L(W0 + t * E) - 2 * L(W0) + L(W0 - t * E)
+    H = O.hessian(X)
+    rhs = t * t * float(np.sum((E @ H) * E))
+    assert math.isclose(lhs, rhs, rel_tol=1e-12)
+
+
+# ---------------------------------------------------------- damp / order --
+def test_condition_closed_form_with_dead_feature():
+    H = np.diag([4.0, 0.0, 2.0]) + np.array([[0, 0, 1], [0, 0, 0], [1, 0, 0]], float)
+    Hd, mu = O.condition(H, 0.01)
+    assert mu == pytest.approx((4 + 1 + 2) / 3)  # dead feature counted as 1
+    assert np.allclose(np.diag(Hd), [4 + 0.07 / 3, 1 + 0.07 / 3, 2 + 0.07 / 3])
+    assert Hd[0, 2] == 1.0 and Hd[2, 0] == 1.0 and Hd[0, 1] == 0.0
+
+
+def test_column_order_desc_stable():
+    H = np.diag([3.0, 5.0, 3.0, 7.0, 5.0, 0.0])
+    assert list(O.column_order(H, True)) == [3, 1, 4, 0, 2, 5]
+    assert list(O.column_order(H, False)) == [0, 1, 2, 3, 4, 5]
+    assert list(O.column_order(np.eye(5), True)) == [0, 1, 2, 3, 4]
+
+
+# ------------------------------------------------------------------ factor --
+T1_H = np.array([[2.0, 1, 0], [1, 2, 1], [0, 1, 2]])
+T1_W = np.array([[0.4, 1.4, 3.0]])
+
+
+def test_factor_t1_closed_form():
+    U = O.hinv_chol(T1_H, np.arange(3))
+    r3 = math.sqrt(3.0)
+    want = np.array([[r3 / 2, -1 / r3, 1 / (2 * r3)],
+                     [0, math.sqrt(2 / 3), -1 / math.sqrt(6)],
+                     [0, 0, 1 / math.sqrt(2)]])
+    assert np.allclose(U, want, atol=1e-14, rtol=0)
+
+
+def test_factor_two_routes_and_residual():
+    X = workloads.x_tokens(workloads.get("c0"), 0, 1).numpy()
+    H = O.hessian(X)
+    Hd, _ = O.condition(H, 0.01)
+    perm = O.column_order(H, True)
+    U = O.hinv_chol(Hd, perm)
+    U2 = O.hinv_chol_reverse(Hd, perm)
+    assert np.allclose(np.tril(U, -1), 0)
+    assert np.all(np.diag(U) > 0)
+    assert np.abs(U - U2).max() <= 1e-10 * np.abs(U).max()
+    Hp = Hd[np.ix_(perm, perm)]
+    assert np.abs(U.T @ U @ Hp - np.eye(128)).max() < 1e-9
+
+
+def test_factor_not_pd_raises():
+    with pytest.raises(O.NotPositiveDefinite):
+        O.hinv_chol(-np.eye(4), np.arange(4))
+    with pytest.raises(O.NotPositiveDefinite):
+        O.hinv_chol(np.zeros((3, 3)), np.arange(3))
+
+
+# ---------------------------------------------------- sweep: toy traces --
+def test_t1_trace():
+    """1x3 layer, 2-bit asym, one group, damp 0.
+
+    Hand derivation (exact rationals): range of the original row [0, 3]
+    (zero included) -> s = 1, z = 0.  U' = U / diag(U) = [[1, -2/3, 1/3],
+    [0, 1, -1/2], [0, 0, 1]].  Step 0: 0.4 -> q 0, e = 2/5, w1 = 5/3,
+    w2 = 43/15.  Step 1: 5/3 -> q 2, e = -1/3, w2 = 27/10.  Step 2: q 3.
+    """
+    res = O.gptq(T1_W, T1_H, bits=2, group_size=-1, sym=False, damp_percent=0.0,
+                 desc_act=False)
+    assert res.codes.tolist() == [[0, 2, 3]]
+    assert res.scales.tolist() == [[1.0]] and res.zeros.tolist() == [[0]]
+    rt = O.rtn(T1_W, 2, -1, False)
+    assert rt.codes.tolist() == [[0, 1, 3]]
+    d_g = T1_W - res.what
+    d_r = T1_W - rt.what
+    assert float(np.sum((d_g @ T1_H) * d_g)) == pytest.approx(14 / 25, abs=1e-12)
+    assert float(np.sum((d_r @ T1_H) * d_r)) == pytest.approx(24 / 25, abs=1e-12)
+
+
+def test_t1_brute_force_optimum():
+    """GPTQ is greedy: for T1 it reaches the best of all 64 code triples on the
+    grid s = 1, z = 0 (the optimum value 14/25 is attained by [0,2,3] and [1,1,3])."""
+    best = min(
+        (float(((T1_W[0] - np.array(c)) @ T1_H @ (T1_W[0] - np.array(c)))), c)
+        for c in itertools.product(range(4), repeat=3))
+    assert best[0] == pytest.approx(14 / 25)
+    res = O.gptq(T1_W, T1_H, 2, -1, False, 0.0, False)
+    d = T1_W[0] - res.what[0]
+    assert float(d @ T1_H @ d) == pytest.approx(best[0])
+
+
+T2_H = np.array([[2.0, 1, 0, 0], [1, 5, 2, 0], [0, 2, 3, 1], [0, 0, 1, 4]])
+T2_W = np.array([[1.0, 1.0, -0.2, -0.6], [-0.2, 0.8, 1.0, -0.2]])
+
+
+def test_t2_trace_desc_act_groups():
+    """2x4 layer, 2-bit asym, group_size 2, desc_act, damp 0.
+
+    diag = [2,5,3,4] -> perm [1,3,2,0]; groups in quantization order are
+    {1,3} and {2,0} -> g_idx [1,0,1,0].  Row 0: group {1,3} from [1, -3/5]:
+    s = 8/15, z = 1; col 1: 23/8 -> 3; col 3: -9/88 -> 0.  Group {2,0} from
+    [-4/15, 29/30]: s = 37/90, z = 1; col 2: 13/37 -> 0; col 0: 124/37 -> 3.
+    Row 1: s = 1/3, z = 1; col 1: 17/5 -> 3; col 3: 18/55 -> 0.  Next group
+    from [17/15, -2/15]: s = 19/45, z = 0; col 2: 51/19 -> 3; col 0: -6/19 -> 0.
+    """
+    res = O.gptq(T2_W, T2_H, 2, 2, False, 0.0, True)
+    assert res.perm.tolist() == [1, 3, 2, 0]
+    assert res.g_idx.tolist() == [1, 0, 1, 0]
+    assert res.codes.tolist() == [[3, 3, 0, 0], [0, 3, 3, 0]]
+    assert res.zeros.tolist() == [[1, 1], [1, 0]]
+    assert np.allclose(res.scales, np.array([[8 / 15, 1 / 3], [37 / 90, 19 / 45]], np.float32))
+    # quality: sum_r d^T H d = 511/1620 for GPTQ
+    d = T2_W - res.what
+    # (scales are fp32, so the dequantized values carry fp32 rounding)
+    assert float(np.sum((d @ T2_H) * d)) == pytest.approx(511 / 1620, rel=1e-6)
+    # RTN, natural-order groups {0,1}, {2,3}; row 0 by hand: [1, 1] -> s = 1/3,
+    # z = 0 -> codes 3, 3; [-1/5, -3/5] -> s = 1/5, z = 3 -> codes 2, 0.
+    # (Row 1 lands on exact rounding ties and is not pinned.)
+    rt = O.rtn(T2_W, 2, 2, False)
+    assert rt.codes[0].tolist() == [3, 3, 2, 0]
+    d = T2_W - rt.what
+    assert float(np.sum((d @ T2_H) * d)) > 511 / 1620
+
+
+# ------------------------------------- sweep: independent exact formulation --
+def _round_half_even(x: Fraction) -> int:
+    f = math.floor(x)
+    r = x - f
+    if r > Fraction(1, 2):
+        return f + 1
+    if r < Fraction(1, 2):
+        return f
+    return f if f % 2 == 0 else f + 1
+
+
+def _solve(A, b):
+    """Exact Gaussian elimination on Fractions."""
+    n = len(b)
+    M = [list(A[i]) + [b[i]] for i in range(n)]
+    for c in range(n):
+        p = next(r for r in range(c, n) if M[r][c] != 0)
+        M[c], M[p] = M[p], M[c]
+        for r in range(n):
+            if r != c and M[r][c] != 0:
+                f = M[r][c] / M[c][c]
+                M[r] = [a - f * bb for a, bb in zip(M[r], M[c])]
+    return [M[i][n] / M[i][i] for i in range(n)]
+
+
+def _schur_gptq_row(w, Hp, bits, gs, sym):
+    """One row, quantization order, exact rationals, OBS re-fit form:
+    after fixing column j with error e, the remaining set F moves by
+    + e * H_FF^-1 H_Fj.  Returns (codes, min distance of any pre-rounding value
+    to a rounding boundary)."""
+    n = len(w)
+    maxq = 2 ** bits - 1
+    w = list(w)
+    codes = []
+    mind = Fraction(10)
+    s = z = None
+    for j in range(n):
+        if j % gs == 0:
+            grp = w[j:min(j + gs, n)]
+            lo, hi = min(min(grp), 0), max(max(grp), 0)
+            if sym:
+                hi = max(-lo, hi)
+                lo = -hi
+            if lo == hi:
+                lo, hi = Fraction(-1), Fraction(1)
+            s = (hi - lo) / maxq
+            if sym:
+                z = 2 ** (bits - 1)
+            else:
+                zp = -lo / s
+                mind = min(mind, abs(zp - math.floor(zp) - Fraction(1, 2)))
+                z = _round_half_even(zp)
+        p = w[j] / s
+        mind = min(mind, abs(p - math.floor(p) - Fraction(1, 2)))
+        q = min(max(_round_half_even(p) + z, 0), maxq)
+        codes.append(q)
+        e = w[j] - s * (q - z)
+        F = list(range(j + 1, n))
+        if F:
+            HFF = [[Hp[a][b] for b in F] for a in F]
+            HFj = [Hp[a][j] for a in F]
+            delta = _solve(HFF, HFj)
+            for t, k in enumerate(F):
+                w[k] += e * delta[t]
+    return codes, mind
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_sweep_matches_exact_schur_form(case):
+    rng = np.random.default_rng(100 + case)
+    n = 6
+    bits = [2, 3, 4, 8, 4, 3][case]
+    gs = [-1, 2, 3, 2, 6, -1][case]
+    sym = case in (2, 4)
+    desc = case % 2 == 1
+    A = rng.integers(-3, 4, size=(n + 2, n))
+    Hint = 2 * (A.T @ A) + np.diag(rng.integers(1, 4, size=n))
+    Wq = rng.integers(-40, 41, size=(3, n))  # multiples of 1/32
+    W = Wq / 32.0
+    res = O.gptq(W, Hint.astype(float), bits, gs, sym, 0.0, desc)
+    perm = res.perm
+    Hp = [[Fraction(int(Hint[perm[a], perm[b]])) for b in range(n)] for a in range(n)]
+    gse = n if gs == -1 else gs
+    for r in range(3):
+        wr = [Fraction(int(Wq[r, perm[j]]), 32) for j in range(n)]
+        codes, mind = _schur_gptq_row(wr, Hp, bits, gse, sym)
+        if mind < Fraction(1, 10 ** 6):
+            continue  # a value on a boundary: both roundings are correct
+        assert res.codes_perm[r].tolist() == codes
+
+
+def test_prefix_optimality_reconstructs_codes():
+    """Before column j is quantized, the remaining weights of a row are the
+    optimum of the layer loss with the prefix fixed:
+        w_F = w0_F - (q^_P - w0_P) H_PF H_FF^-1.
+    Rebuilding every step of C0 from that characterization (fp64, no sweep)
+    gives the oracle's codes wherever a value is not on a rounding boundary."""
+    cfg = workloads.get("c0")
+    W = workloads.weight(cfg).numpy().astype(np.float64)[:8]
+    X = workloads.x_tokens(cfg, 0, 1).numpy()
+    H = O.hessian(X)
+    res = O.gptq(W, H, cfg.bits, cfg.group_size, cfg.sym, cfg.damp, cfg.desc_act)
+    Hd, _ = O.condition(H, cfg.damp)
+    perm = res.perm
+    Hp = Hd[np.ix_(perm, perm)]
+    W0 = W[:, perm]
+    n = W.shape[1]
+    Q = res.what[:, perm]
+    gs = cfg.group_size
+    checked = 0
+    for j in range(n):
+        P, F = slice(0, j), slice(j, n)
+        if j == 0:
+            cur = W0.copy()
+        else:
+            corr = (Q[:, P] - W0[:, P]) @ Hp[P, F] @ np.linalg.inv(Hp[F, F])
+            cur = np.concatenate([Q[:, P], W0[:, F] - corr], axis=1)
+        if j % gs == 0:
+            g = j // gs
+            grp = cur[:, j:j + gs]
+            s, z, _ = O.group_params(grp.min(1), grp.max(1), cfg.bits, cfg.sym)
+            assert np.allclose(s, res.scales[g], rtol=1e-6)
+        s = res.scales[j // gs].astype(np.float64)
+        z = res.zeros[j // gs]
+        pre = cur[:, j] / s + z
+        dist = np.abs(pre - np.floor(pre) - 0.5)
+        q = np.clip(np.rint(cur[:, j] / s) + z, 0, 2 ** cfg.bits - 1)
+        ok = dist > 1e-6
+        assert np.array_equal(q[ok], res.codes_perm[ok, j])
+        checked += int(ok.sum())
+    assert checked > 0.99 * W.size
+
+
+# ------------------------------------------------------------ invariants --
+def _c0_problem(rows=None):
+    cfg = workloads.get("c0")
+    W = workloads.weight(cfg).numpy().astype(np.float64)
+    if rows is not None:
+        W = W[:rows]
+    H = O.hessian(workloads.x_tokens(cfg, 0, 1).numpy())
+    return cfg, W, H
+
+
+def test_h_identity_reduces_to_rtn_bit_exact():
+    for bits, gs, sym in [(4, 32, False), (2, 32, False), (3, -1, False), (8, 64, False),
+                          (4, 64, True), (3, 32, True)]:
+        W = workloads.boundary_safe_weight(16, 128, bits, gs, sym).numpy().astype(np.float64)
+        g = O.gptq(W, np.eye(128), bits, gs, sym, 0.01, True)
+        r = O.rtn(W, bits, gs, sym)
+        assert np.array_equal(g.codes, r.codes)
+        assert np.array_equal(g.scales, r.scales) and np.array_equal(g.zeros, r.zeros)
+        assert np.array_equal(g.perm, np.arange(128))
+        # RTN inside the grid range: every weight is within s/2 of its code point
+        s = r.scales[r.g_idx, :].T.astype(np.float64)
+        assert np.all(np.abs(W - r.what) <= 0.5 * s)
+        assert np.all(np.log2(r.scales) == np.round(np.log2(r.scales)))
+
+
+def test_scale_invariance_bit_identical():
+    cfg, W, H = _c0_problem()
+    a = O.gptq(W, H, 4, 32, False, 0.01, True)
+    b = O.gptq(W, 4.0 * H, 4, 32, False, 0.01, True)
+    assert np.array_equal(a.codes, b.codes)
+    assert np.array_equal(a.scales, b.scales) and np.array_equal(a.zeros, b.zeros)
+
+
+def test_permutation_equivariance():
+    cfg, W, H = _c0_problem()
+    a = O.gptq(W, H, 3, 32, False, 0.01, True)
+    p = a.perm
+    b = O.gptq(W[:, p], H[np.ix_(p, p)], 3, 32, False, 0.01, False)
+    assert np.array_equal(a.codes_perm, b.codes)
+    assert np.array_equal(a.scales, b.scales)
+    assert np.array_equal(a.codes[:, p], b.codes)
+
+
+def test_row_independence():
+    cfg, W, H = _c0_problem()
+    a = O.gptq(W, H, 4, 32, True, 0.01, False)
+    rows = [3, 17, 40]
+    b = O.gptq(W[rows], H, 4, 32, True, 0.01, False)
+    assert np.array_equal(a.codes[rows], b.codes)
+    assert np.array_equal(a.scales[:, rows], b.scales)
+
+
+def test_gptq_beats_rtn_on_correlated_inputs():
+    cfg, W, H = _c0_problem()
+    for bits, gs, sym, desc in [(4, 32, False, False), (3, 32, False, True),
+                                (2, -1, False, False), (4, 64, True, True)]:
+        g = O.gptq(W, H, bits, gs, sym, 0.01, desc)
+        r = O.rtn(W, bits, gs, sym)
+        assert O.layer_error(W, g.what, H) < O.layer_error(W, r.what, H)
+
+
+def test_dequantize_matches_sweep_output():
+    cfg, W, H = _c0_problem()
+    g = O.gptq(W, H, 4, 32, False, 0.01, True)
+    assert np.array_equal(O.dequantize(g.codes, g.scales, g.zeros, g.g_idx), g.what)
+
+
+def test_replay_records_and_follows_forced_codes():
+    cfg, W, H = _c0_problem(rows=4)
+    Hd, _ = O.condition(H, 0.01)
+    perm = O.column_order(H, False)
+    U = O.hinv_chol(Hd, perm)
+    base = O.gptq_sweep(W, U, perm, 4, 32, False)
+    forced = base.codes_perm.copy()
+    forced[1, 5] = (forced[1, 5] + 1) % 16
+    rep = O.gptq_sweep(W, U, perm, 4, 32, False, forced_codes=forced)
+    kinds = [(m[0], m[1], m[2]) for m in rep.mismatches]
+    assert ("code", 1, 5) in kinds
+    assert np.array_equal(rep.codes_perm[:, 5], forced[:, 5])
+    assert np.array_equal(rep.codes_perm[[0, 2, 3]], base.codes_perm[[0, 2, 3]])
+
+
+# ------------------------------------------------------------------ packing --
+def _words(codes, bits):
+    q = O.pack(np.array([codes]), bits)
+    return [int(v) & 0xFFFFFFFF for v in q[:, 0]]
+
+
+def test_pack_words_from_layout_definition():
+    # 4-bit codes 1..8, then zeros: first word 0x87654321
+    assert _words(list(range(1, 9)) + [0] * 24, 4)[0] == 0x87654321
+    # 2-bit codes k mod 4 for k < 16: every byte is 0b11100100
+    assert _words([k % 4 for k in range(32)], 2) == [0xE4E4E4E4, 0xE4E4E4E4]
+    # 8-bit codes 1..4
+    assert _words([1, 2, 3, 4] + [0] * 28, 8)[0] == 0x04030201
+    # 3-bit codes k mod 8: 32 codes -> 3 words, codes straddle word boundaries
+    assert _words([k % 8 for k in range(32)], 3) == [0x88FAC688, 0xC688FAC6, 0xFAC688FA]
+    assert _words([7] * 32, 3) == [0xFFFFFFFF] * 3
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_pack_roundtrip(bits):
+    rng = np.random.default_rng(bits)
+    c = rng.integers(0, 2 ** bits, size=(5, 96))
+    q = O.pack(c, bits)
+    assert q.shape == (96 * bits // 32, 5) and q.dtype == np.int32
+    assert np.array_equal(O.unpack(q, bits, 96), c)
+
+
+def test_g_index():
+    assert O.g_index([1, 3, 2, 0], 2).tolist() == [1, 0, 1, 0]
+    assert O.g_index([0, 1, 2], -1).tolist() == [0, 0, 0]
