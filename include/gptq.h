@@ -1,0 +1,181 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ layer quantizer.
+ *
+ * GPTQ quantizes one linear layer at a time against calibration data
+ * (glossary entry "gptq", paragraph "Method"): it builds the Hessian of the
+ * layer's reconstruction loss from calibration activations, then quantizes
+ * the weights column by column, pushing each column's rounding error onto
+ * the columns not yet quantized using the inverse Hessian (same entry,
+ * paragraphs "Key innovation" and "Algorithm").  The three calls below are
+ * that pipeline for one layer:
+ *
+ *   gptq_hessian_accumulate   H += 2 X^T X          (once per calibration chunk)
+ *   gptq_prepare              damp, order, factor   -> Hinv_chol, perm
+ *   gptq_quantize_layer       sweep + pack          -> qweight, scales, zeros, g_idx
+ *
+ * Conventions shared by every call
+ *   - Every array argument is DEVICE memory owned by the caller (HIP device
+ *     pointers), row-major, densely packed unless a leading dimension is given.
+ *     The library never allocates or frees device memory; scratch space comes
+ *     from the caller's workspace, sized by the *_workspace_bytes queries.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it and return; nothing is synchronised.  Results are valid once
+ *     the stream has reached that point.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failing check returns a nonzero gptq_status_t and leaves every output
+ *     untouched.  gptq_last_error_message() then names the failing argument.
+ *   - Conditions found on the device (a non-positive or non-finite Cholesky
+ *     pivot) are reported through a device int32 `info`, as LAPACK does.
+ *   - There is no CPU fallback.
+ *   - Calls are safe on different streams concurrently as long as they use
+ *     different workspaces and outputs.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = 1, /* a pointer, size or parameter is out of range      */
+  GPTQ_ERR_UNSUPPORTED = 2, /* a valid request this library does not implement   */
+  GPTQ_ERR_WORKSPACE = 3,   /* workspace_bytes below the size the query returned */
+  GPTQ_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed        */
+} gptq_status_t;
+
+typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype_t;
+
+/* Maximum matrix order accepted by gptq_prepare (one row of H is staged in
+ * the 160 KiB LDS of a gfx950 compute unit during the column gather). */
+#define GPTQ_MAX_PREPARE_N 32768
+
+/*
+ * Hessian accumulation:  H += 2 * X^T X   (upper triangle only).
+ *
+ * Glossary entry "gptq", paragraph "Algorithm" step (1): the Hessian of the
+ * layer loss with respect to the layer weights, approximated from the
+ * calibration data.  For the reconstruction loss sum_t ||(W - W^) x_t||^2 it
+ * is exactly 2 * sum_t x_t x_t^T; the sum (not the mean) is accumulated, so
+ * calibration data can be streamed in chunks of any size.
+ *
+ *   H      fp32 [n x n], row-major.  Entries H[i][j] with i <= j are read and
+ *          updated; entries below the diagonal are never touched.  The caller
+ *          zero-initialises H before the first chunk.
+ *   n      number of input features (columns of the layer's W), n >= 1.
+ *   X      calibration activations, [ntok x n] (tokens x features), row-major
+ *          with leading dimension ldx >= n, dtype GPTQ_F16 or GPTQ_BF16.
+ *   ntok   tokens in this chunk; ntok == 0 is a no-op returning GPTQ_OK.
+ *
+ * Products of fp16/bf16 values are exact in fp32; accumulation is fp32.
+ * Errors: INVALID_ARG (null pointers, n < 1, ntok < 0, ldx < n),
+ *         UNSUPPORTED (x_dtype not F16/BF16), HIP.
+ */
+int gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dtype,
+                            int64_t ntok, int64_t ldx, void* stream);
+
+/* Workspace (bytes) gptq_prepare needs for order n (0 if n is out of range). */
+size_t gptq_prepare_workspace_bytes(int64_t n);
+
+/*
+ * Damping, column order and the factor that drives the sweep.
+ *
+ *   - Damping ("GPTQ > Using AutoGPTQ in Practice", Key Parameters,
+ *     damp_percent): mu = mean(diag H); H_d = H + damp_percent * mu * I.
+ *     A feature whose diagonal entry is exactly 0 is given H_ii = 1 before
+ *     the mean is taken (it never fired; its weights cannot change the loss).
+ *   - Column order (same list, desc_act): with desc_act != 0 the columns are
+ *     processed by decreasing diag(H) (the raw diagonal; ties keep the lower
+ *     original index first); otherwise in natural order.
+ *   - Factor (same page, introduction: "Cholesky factorization"; glossary
+ *     "Algorithm" step (2): compensation "using H^-1"): Hinv_chol is U, the
+ *     upper-triangular Cholesky factor of (P H_d P^T)^-1, U^T U = H_p^-1,
+ *     computed as the inverse of the reverse Cholesky factor of H_p.
+ *
+ *   H          fp32 [n x n]; only the upper triangle (i <= j) is read.
+ *   n          1 <= n <= GPTQ_MAX_PREPARE_N.
+ *   damp_percent  >= 0 (0.01 means 1 %).
+ *   Hinv_chol  out: fp32 [n x n], row-major; upper triangle = U, strictly
+ *              lower triangle = 0.  Row/column j refers to the j-th column in
+ *              quantization order.
+ *   perm       out: int32 [n]; perm[j] = original column quantized j-th
+ *              (the identity when desc_act == 0).
+ *   info       out: device int32; 0 on success, k > 0 if the pivot of
+ *              quantization-order column k-1 was non-positive or not finite
+ *              (then Hinv_chol is not meaningful).
+ *   workspace  device memory of at least gptq_prepare_workspace_bytes(n).
+ * Errors: INVALID_ARG, UNSUPPORTED (n > GPTQ_MAX_PREPARE_N), WORKSPACE, HIP.
+ */
+int gptq_prepare(const float* H, int64_t n, float damp_percent, int desc_act,
+                 float* Hinv_chol, int32_t* perm, int32_t* info,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace (bytes) gptq_quantize_layer needs (0 if the arguments are invalid). */
+size_t gptq_quantize_workspace_bytes(int64_t out, int64_t in, int bits,
+                                     int group_size, int block);
+
+/*
+ * The column sweep and the packing.
+ *
+ * Glossary "gptq", "Algorithm" step (2) and "Key innovation": each weight, in
+ * quantization order, is quantized, its error computed, and the remaining
+ * weights of its row adjusted to compensate:  w_k -= (e / U_jj) * U_jk for
+ * k > j.  Groups (agent skill page "gptq", "Group-wise quantization"; handbook
+ * Key Parameters, group_size): group_size consecutive columns in quantization
+ * order share one scale and zero-point per output row; group_size == -1 means
+ * one group per row.  A group's scale and zero are taken when its first
+ * column comes up, from the group's current values:
+ *     lo = min(0, min w), hi = max(0, max w)
+ *     sym:   hi = max(-lo, hi), lo = -hi, zero = 2^(bits-1)
+ *     lo == hi  ->  lo = -1, hi = +1
+ *     scale = (hi - lo) / (2^bits - 1),   asym: zero = rint(-lo / scale)
+ *     code  = clamp(rint(w / scale) + zero, 0, 2^bits - 1)
+ * in IEEE fp32 with round-half-to-even.  Columns are swept in lazy blocks of
+ * `block` columns; the update of the columns right of a block is applied as a
+ * matrix product on the matrix cores (the set of updates is the same).
+ *
+ *   W          [out x in] row-major, dtype F16 / BF16 / F32, ORIGINAL column
+ *              order; not modified.
+ *   Hinv_chol  fp32 [in x in] upper triangle, as written by gptq_prepare
+ *              (any upper-triangular matrix with a positive diagonal is
+ *              accepted; the strictly lower triangle is ignored).
+ *   perm       int32 [in] from gptq_prepare, or NULL for the identity.
+ *   bits       2, 3, 4 or 8 (glossary "Quantization targets"; catalogue page).
+ *   group_size -1, or a positive divisor of `block`.
+ *   sym        0 = asymmetric, 1 = symmetric.
+ *   block      lazy block width: 32, 64 or 128.
+ *   in         a positive multiple of 32 (3-bit packs 32 codes in 3 words).
+ * Outputs (caller-allocated device memory, fully overwritten):
+ *   qweight    int32 [in*bits/32 x out]: for output row r, the codes of input
+ *              columns 0..in-1 (original order) form a little-endian bit
+ *              stream, column k at bits [k*bits, (k+1)*bits); word w of that
+ *              stream is qweight[w][r].
+ *   scales     fp32  [n_groups x out], n_groups = group_size == -1 ? 1
+ *              : ceil(in / group_size); group g = quantization-order columns
+ *              [g*group_size, (g+1)*group_size).
+ *   zeros      int32 [n_groups x out], values in [0, 2^bits - 1].
+ *   g_idx      int32 [in]: g_idx[k] = group of original column k.
+ * Errors: INVALID_ARG, UNSUPPORTED (bits, block), WORKSPACE, HIP.
+ */
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in,
+                        const float* Hinv_chol, const int32_t* perm,
+                        int bits, int group_size, int sym, int block,
+                        int32_t* qweight, float* scales, int32_t* zeros,
+                        int32_t* g_idx, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Static text for a gptq_status_t value. */
+const char* gptq_status_string(int status);
+
+/* Detail of the last failing call on the calling host thread ("" if none). */
+const char* gptq_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

@@ -1,0 +1,19 @@
+"""GPTQ layer-wise weight quantization on AMD Instinct MI355X (gfx950).
+
+The work runs in hand-written HIP kernels behind a C ABI (include/gptq.h,
+libgptq_mi355x.so); this package is the thin Python binding.
+"""
+from ._lib import (  # noqa: F401
+    GptqError,
+    GPTQ_BF16,
+    GPTQ_F16,
+    GPTQ_F32,
+    hessian_accumulate,
+    header_functions,
+    load,
+    n_groups,
+    prepare,
+    prepare_workspace_bytes,
+    quantize_layer,
+    quantize_workspace_bytes,
+)

@@ -1,0 +1,198 @@
+"""ctypes binding of libgptq_mi355x.so (argument marshalling only).
+
+Every step of the quantization runs in the HIP library; this module checks
+tensor devices / dtypes / shapes, passes raw device pointers plus the current
+HIP stream, and turns status codes into exceptions.  torch provides device
+memory and streams, nothing else.  There is no fallback: if the library is
+missing, loading fails with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgptq_mi355x.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "gptq.h")
+
+GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_UNSUPPORTED, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP = range(5)
+GPTQ_F16, GPTQ_BF16, GPTQ_F32 = 0, 1, 2
+MAX_PREPARE_N = 32768
+
+
+class GptqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/gptq.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gptq_[a-z_0-9]+)\s*\(", text, flags=re.M)
+
+
+def load():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m post_weight_quantization_12_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.gptq_hessian_accumulate.argtypes = [vp, i64, vp, c_int, i64, i64, vp]
+    lib.gptq_hessian_accumulate.restype = c_int
+    lib.gptq_prepare_workspace_bytes.argtypes = [i64]
+    lib.gptq_prepare_workspace_bytes.restype = ctypes.c_size_t
+    lib.gptq_prepare.argtypes = [vp, i64, ctypes.c_float, c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.gptq_prepare.restype = c_int
+    lib.gptq_quantize_workspace_bytes.argtypes = [i64, i64, c_int, c_int, c_int]
+    lib.gptq_quantize_workspace_bytes.restype = ctypes.c_size_t
+    lib.gptq_quantize_layer.argtypes = [vp, c_int, i64, i64, vp, vp, c_int, c_int, c_int, c_int,
+                                        vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.gptq_quantize_layer.restype = c_int
+    lib.gptq_status_string.argtypes = [c_int]
+    lib.gptq_status_string.restype = ctypes.c_char_p
+    lib.gptq_last_error_message.argtypes = []
+    lib.gptq_last_error_message.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != GPTQ_OK:
+        lib = load()
+        msg = lib.gptq_status_string(status).decode()
+        detail = lib.gptq_last_error_message().decode()
+        raise GptqError(status, f"{msg}: {detail}" if detail else msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float16:
+        return GPTQ_F16
+    if dt == torch.bfloat16:
+        return GPTQ_BF16
+    if dt == torch.float32:
+        return GPTQ_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _need_cuda(name, t):
+    if t is None or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+# ---------------------------------------------------------------- calls --
+def hessian_accumulate(H, X, stream=None):
+    """H (fp32 [n x n], upper triangle) += 2 X^T X for X [ntok x n] fp16/bf16."""
+    lib = load()
+    _need_cuda("H", H)
+    _need_cuda("X", X)
+    n = H.shape[0]
+    if H.dtype != _torch().float32 or H.dim() != 2 or H.shape[1] != n or not H.is_contiguous():
+        raise ValueError("H must be a contiguous fp32 [n x n] tensor")
+    if X.dim() != 2 or X.shape[1] != n or X.stride(1) != 1:
+        raise ValueError("X must be [ntok x n] with unit column stride")
+    _check(lib.gptq_hessian_accumulate(_ptr(H), n, _ptr(X), _dtype_code(X.dtype), X.shape[0],
+                                       X.stride(0) if X.shape[0] > 1 else n, _stream(stream)))
+    return H
+
+
+def prepare_workspace_bytes(n: int) -> int:
+    return int(load().gptq_prepare_workspace_bytes(n))
+
+
+def prepare(H, damp_percent: float, desc_act: bool, Hinv_chol=None, perm=None, info=None,
+            workspace=None, stream=None):
+    """Returns (Hinv_chol fp32 [n x n], perm int32 [n], info int32 [1]) on H's device."""
+    torch = _torch()
+    lib = load()
+    _need_cuda("H", H)
+    n = H.shape[0]
+    if H.dtype != torch.float32 or H.dim() != 2 or H.shape[1] != n or not H.is_contiguous():
+        raise ValueError("H must be a contiguous fp32 [n x n] tensor")
+    dev = H.device
+    if Hinv_chol is None:
+        Hinv_chol = torch.empty((n, n), dtype=torch.float32, device=dev)
+    if perm is None:
+        perm = torch.empty((n,), dtype=torch.int32, device=dev)
+    if info is None:
+        info = torch.empty((1,), dtype=torch.int32, device=dev)
+    need = prepare_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib.gptq_prepare(_ptr(H), n, float(damp_percent), int(bool(desc_act)), _ptr(Hinv_chol),
+                            _ptr(perm), _ptr(info), _ptr(workspace), workspace.numel(),
+                            _stream(stream)))
+    return Hinv_chol, perm, info
+
+
+def quantize_workspace_bytes(out: int, inp: int, bits: int, group_size: int, block: int) -> int:
+    return int(load().gptq_quantize_workspace_bytes(out, inp, bits, group_size, block))
+
+
+def n_groups(inp: int, group_size: int) -> int:
+    return 1 if group_size == -1 else -(-inp // group_size)
+
+
+def quantize_layer(W, Hinv_chol, perm, bits: int, group_size: int, sym: bool, block: int,
+                   qweight=None, scales=None, zeros=None, g_idx=None, workspace=None,
+                   stream=None):
+    """Returns (qweight int32 [in*bits/32 x out], scales fp32 [g x out],
+    zeros int32 [g x out], g_idx int32 [in])."""
+    torch = _torch()
+    lib = load()
+    _need_cuda("W", W)
+    _need_cuda("Hinv_chol", Hinv_chol)
+    if W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous [out x in] tensor")
+    out, inp = W.shape
+    if Hinv_chol.dtype != torch.float32 or tuple(Hinv_chol.shape) != (inp, inp) \
+            or not Hinv_chol.is_contiguous():
+        raise ValueError("Hinv_chol must be a contiguous fp32 [in x in] tensor")
+    if perm is not None and (perm.dtype != torch.int32 or perm.numel() != inp or not perm.is_cuda):
+        raise ValueError("perm must be a GPU int32 [in] tensor")
+    dev = W.device
+    g = n_groups(inp, group_size)
+    if qweight is None:
+        qweight = torch.empty((max(inp * bits // 32, 1), out), dtype=torch.int32, device=dev)
+    if scales is None:
+        scales = torch.empty((g, out), dtype=torch.float32, device=dev)
+    if zeros is None:
+        zeros = torch.empty((g, out), dtype=torch.int32, device=dev)
+    if g_idx is None:
+        g_idx = torch.empty((inp,), dtype=torch.int32, device=dev)
+    need = quantize_workspace_bytes(out, inp, bits, group_size, block)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib.gptq_quantize_layer(_ptr(W), _dtype_code(W.dtype), out, inp, _ptr(Hinv_chol),
+                                   _ptr(perm), int(bits), int(group_size), int(bool(sym)),
+                                   int(block), _ptr(qweight), _ptr(scales), _ptr(zeros),
+                                   _ptr(g_idx), _ptr(workspace), workspace.numel(),
+                                   _stream(stream)))
+    return qweight, scales, zeros, g_idx

@@ -1,0 +1,146 @@
+// extern "C" entry points of the gfx950 GPTQ library: argument validation
+// (before anything is enqueued), workspace checks, status strings.
+#include <cmath>
+#include <string>
+
+#include "../../include/gptq.h"
+#include "common.hpp"
+
+namespace gptq {
+namespace {
+thread_local std::string g_last_error;
+}
+void set_error(const std::string& msg) { g_last_error = msg; }
+void clear_error() { g_last_error.clear(); }
+const char* last_error_c() { return g_last_error.c_str(); }
+}  // namespace gptq
+
+using namespace gptq;
+
+namespace {
+
+int fail(int status, const std::string& msg) {
+  set_error(msg);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return GPTQ_OK;
+  return fail(GPTQ_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool valid_group(int gs, int block) {
+  if (gs == -1) return true;
+  return gs >= 4 && gs % 4 == 0 && gs <= block && block % gs == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dtype, int64_t ntok,
+                            int64_t ldx, void* stream) {
+  clear_error();
+  if (!H) return fail(GPTQ_ERR_INVALID_ARG, "H is NULL");
+  if (!X) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL");
+  if (n < 1) return fail(GPTQ_ERR_INVALID_ARG, "n must be >= 1");
+  if (ntok < 0) return fail(GPTQ_ERR_INVALID_ARG, "ntok must be >= 0");
+  if (ldx < n) return fail(GPTQ_ERR_INVALID_ARG, "ldx must be >= n");
+  if (x_dtype != GPTQ_F16 && x_dtype != GPTQ_BF16)
+    return fail(GPTQ_ERR_UNSUPPORTED, "x_dtype must be GPTQ_F16 or GPTQ_BF16");
+  const int64_t nt = (n + 127) / 128;
+  if (nt * (nt + 1) / 2 > 0x7FFFFFFFLL) return fail(GPTQ_ERR_UNSUPPORTED, "n too large");
+  if (ntok == 0) return GPTQ_OK;
+  return hip_status(launch_syrk(H, n, X, x_dtype, ntok, ldx, static_cast<hipStream_t>(stream)),
+                    "gptq_hessian_accumulate");
+}
+
+size_t gptq_prepare_workspace_bytes(int64_t n) {
+  if (n < 1 || n > GPTQ_MAX_PREPARE_N) return 0;
+  return prepare_workspace_bytes(n);
+}
+
+int gptq_prepare(const float* H, int64_t n, float damp_percent, int desc_act, float* Hinv_chol,
+                 int32_t* perm, int32_t* info, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  clear_error();
+  if (!H) return fail(GPTQ_ERR_INVALID_ARG, "H is NULL");
+  if (!Hinv_chol) return fail(GPTQ_ERR_INVALID_ARG, "Hinv_chol is NULL");
+  if (!perm) return fail(GPTQ_ERR_INVALID_ARG, "perm is NULL");
+  if (!info) return fail(GPTQ_ERR_INVALID_ARG, "info is NULL");
+  if (n < 1) return fail(GPTQ_ERR_INVALID_ARG, "n must be >= 1");
+  if (n > GPTQ_MAX_PREPARE_N)
+    return fail(GPTQ_ERR_UNSUPPORTED, "n exceeds GPTQ_MAX_PREPARE_N (32768)");
+  if (!(damp_percent >= 0.0f) || !std::isfinite(damp_percent))
+    return fail(GPTQ_ERR_INVALID_ARG, "damp_percent must be finite and >= 0");
+  if (static_cast<const void*>(H) == static_cast<const void*>(Hinv_chol))
+    return fail(GPTQ_ERR_INVALID_ARG, "H and Hinv_chol must not alias");
+  const size_t need = prepare_workspace_bytes(n);
+  if (!workspace) return fail(GPTQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(GPTQ_ERR_WORKSPACE, "workspace smaller than gptq_prepare_workspace_bytes(n) = " +
+                                        std::to_string(need));
+  return hip_status(run_prepare(H, n, damp_percent, desc_act ? 1 : 0, Hinv_chol, perm, info,
+                                workspace, static_cast<hipStream_t>(stream)),
+                    "gptq_prepare");
+}
+
+size_t gptq_quantize_workspace_bytes(int64_t out, int64_t in, int bits, int group_size,
+                                     int block) {
+  if (out < 1 || in < 32 || in % 32 != 0 || in > GPTQ_MAX_PREPARE_N) return 0;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return 0;
+  if (block != 32 && block != 64 && block != 128) return 0;
+  if (!valid_group(group_size, block)) return 0;
+  return quantize_workspace_bytes(out, in, bits, group_size, block);
+}
+
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in,
+                        const float* Hinv_chol, const int32_t* perm, int bits, int group_size,
+                        int sym, int block, int32_t* qweight, float* scales, int32_t* zeros,
+                        int32_t* g_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (!W) return fail(GPTQ_ERR_INVALID_ARG, "W is NULL");
+  if (!Hinv_chol) return fail(GPTQ_ERR_INVALID_ARG, "Hinv_chol is NULL");
+  if (!qweight || !scales || !zeros || !g_idx)
+    return fail(GPTQ_ERR_INVALID_ARG, "an output pointer (qweight/scales/zeros/g_idx) is NULL");
+  if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_BF16 && w_dtype != GPTQ_F32)
+    return fail(GPTQ_ERR_INVALID_ARG, "w_dtype must be GPTQ_F16, GPTQ_BF16 or GPTQ_F32");
+  if (out < 1) return fail(GPTQ_ERR_INVALID_ARG, "out must be >= 1");
+  if (out > 0x7FFFFFFFLL) return fail(GPTQ_ERR_UNSUPPORTED, "out too large");
+  if (in < 32 || in % 32 != 0)
+    return fail(GPTQ_ERR_INVALID_ARG, "in must be a positive multiple of 32");
+  if (in > GPTQ_MAX_PREPARE_N) return fail(GPTQ_ERR_UNSUPPORTED, "in exceeds 32768");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits must be 2, 3, 4 or 8");
+  if (block != 32 && block != 64 && block != 128)
+    return fail(GPTQ_ERR_UNSUPPORTED, "block must be 32, 64 or 128");
+  if (!valid_group(group_size, block))
+    return fail(GPTQ_ERR_INVALID_ARG,
+                "group_size must be -1 or a multiple of 4 that divides block");
+  if (sym != 0 && sym != 1) return fail(GPTQ_ERR_INVALID_ARG, "sym must be 0 or 1");
+  const size_t need = quantize_workspace_bytes(out, in, bits, group_size, block);
+  if (!workspace) return fail(GPTQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(GPTQ_ERR_WORKSPACE,
+                "workspace smaller than gptq_quantize_workspace_bytes(...) = " +
+                    std::to_string(need));
+  return hip_status(run_quantize(W, w_dtype, out, in, Hinv_chol, perm, bits, group_size, sym,
+                                 block, qweight, scales, zeros, g_idx, workspace,
+                                 static_cast<hipStream_t>(stream)),
+                    "gptq_quantize_layer");
+}
+
+const char* gptq_status_string(int status) {
+  switch (status) {
+    case GPTQ_OK: return "GPTQ_OK";
+    case GPTQ_ERR_INVALID_ARG: return "GPTQ_ERR_INVALID_ARG: invalid argument";
+    case GPTQ_ERR_UNSUPPORTED: return "GPTQ_ERR_UNSUPPORTED: unsupported request";
+    case GPTQ_ERR_WORKSPACE: return "GPTQ_ERR_WORKSPACE: workspace too small";
+    case GPTQ_ERR_HIP: return "GPTQ_ERR_HIP: HIP runtime error";
+    default: return "unknown gptq status";
+  }
+}
+
+const char* gptq_last_error_message(void) { return gptq::last_error_c(); }
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Shared declarations of the gfx950 GPTQ library (host side and device helpers).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+namespace gptq {
+
+// Vector types used with the gfx950 matrix-core builtins.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Error reporting to the C ABI (per host thread).
+void set_error(const std::string& msg);
+void clear_error();
+
+// Workspace carving: every piece 256-byte aligned.
+inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base ? base + used : nullptr);
+    used += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// fp32 matrix-core GEMM on row-major operands:
+//     C[M x N] = alpha * op(A) * op(B) + beta * C
+// op(A) is A [M x K] (transA = false) or A^T with A stored [K x M];
+// op(B) is B [K x N] (transB = false) or B^T with B stored [N x K].
+// kmode restricts each output tile's K range to where a triangular operand
+// can be nonzero (entries outside must still be zero in memory if read):
+enum KRange : int {
+  KR_FULL = 0,    // all of [0, K)
+  KR_LE_COL = 1,  // op(B)[k][j] == 0 for k > j  -> k < j0 + tile_n
+  KR_GE_COL = 2,  // op(B)[k][j] == 0 for k < j  -> k >= j0
+  KR_LE_ROW = 3,  // op(A)[i][k] == 0 for k > i  -> k < i0 + tile_m
+};
+struct GemmArgs {
+  int64_t M, N, K;
+  const float* A; int64_t lda; bool transA;
+  const float* B; int64_t ldb; bool transB;
+  float* C; int64_t ldc;
+  float alpha, beta;
+  int kmode;
+  bool lower_only;  // compute only tiles that touch the lower triangle (i >= j)
+};
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
+
+// Hessian SYRK: H(upper) += 2 X^T X.
+hipError_t launch_syrk(float* H, int64_t n, const void* X, int dtype, int64_t ntok,
+                       int64_t ldx, hipStream_t s);
+
+// gptq_prepare pipeline.
+size_t prepare_workspace_bytes(int64_t n);
+hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, float* U,
+                       int32_t* perm, int32_t* info, void* ws, hipStream_t s);
+
+// gptq_quantize_layer pipeline.
+size_t quantize_workspace_bytes(int64_t out, int64_t in, int bits, int gs, int block);
+hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, const float* U,
+                        const int32_t* perm, int bits, int gs, int sym, int block,
+                        int32_t* qweight, float* scales, int32_t* zeros, int32_t* g_idx,
+                        void* ws, hipStream_t s);
+
+}  // namespace gptq
+
+#define GPTQ_HIP_TRY(expr)                  \
+  do {                                      \
+    hipError_t _e = (expr);                 \
+    if (_e != hipSuccess) return _e;        \
+  } while (0)

@@ -1,0 +1,330 @@
+// gptq_prepare: damping, desc_act column order and U = upper Cholesky factor
+// of the inverse damped Hessian, in quantization order.
+//
+//   damp_percent ("GPTQ > Using AutoGPTQ in Practice", Key Parameters):
+//       H_d = H + damp * mean(diag H) * I   (a zero diagonal entry counts as 1)
+//   desc_act (same list): quantization order by decreasing diag(H), stable.
+//   factor: the sweep adjusts remaining weights using H^-1 (glossary "gptq",
+//       "Algorithm" step (2)); the object it needs is U with U^T U = H_p^-1.
+//
+// Route on the GPU (half the flops of "invert, then factor"): with J the
+// index reversal, factor A = J H_p J = L L^T (ordinary lower Cholesky), then
+// R = J L J is upper with H_p = R R^T, so H_p^-1 = R^-T R^-1 and U = R^-1 =
+// J L^-1 J.  L and L^-1 are computed together by one recursion
+//     [A11 .  ]    L11 = chol(A11), X11 = L11^-1            (recursive)
+//     [A21 A22] -> L21 = A21 X11^T,  A22 -= L21 L21^T       (fp32 MFMA GEMMs)
+//                  L22 = chol(A22), X22 = L22^-1            (recursive)
+//                  X21 = -X22 (L21 X11)                     (fp32 MFMA GEMMs)
+// whose leaves (<= 64 columns) run in one workgroup out of LDS.  X = L^-1 is
+// built directly in the output buffer and finally moved in place to
+// U[i][j] = X[n-1-i][n-1-j].
+#include "common.hpp"
+
+namespace gptq {
+namespace {
+
+constexpr int NB = 64;  // leaf order of the recursion
+
+__global__ void fill_f32_kernel(float* p, int64_t count, float v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__device__ inline uint32_t order_key(float d) {
+  // Monotone map float -> uint32 (ascending).  -0 counts as +0; NaN sorts lowest.
+  if (d != d) return 0u;
+  if (d == 0.0f) d = 0.0f;
+  const uint32_t u = __float_as_uint(d);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One workgroup: keys of the raw diagonal, mean of the (dead-fixed) diagonal,
+// damp_add = damp * mean; clears info.
+__global__ void __launch_bounds__(1024)
+diag_stats_kernel(const float* __restrict__ H, int64_t n, float damp, uint32_t* __restrict__ keys,
+                  float* __restrict__ damp_add, int32_t* __restrict__ info) {
+  __shared__ double red[1024];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const float d = H[i * n + i];
+    keys[i] = order_key(d);
+    s += (double)(d == 0.0f ? 1.0f : d);
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *damp_add = (float)((double)damp * (red[0] / (double)n));
+    *info = 0;
+  }
+}
+
+// perm[rank(i)] = i, rank by decreasing key, ties by index (stable).
+__global__ void __launch_bounds__(256)
+rank_kernel(const uint32_t* __restrict__ keys, int64_t n, int desc, int32_t* __restrict__ perm) {
+  __shared__ uint32_t sk[2048];
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (!desc) {
+    if (i < n) perm[i] = (int32_t)i;
+    return;
+  }
+  const uint32_t ki = i < n ? keys[i] : 0u;
+  int64_t rank = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += 2048) {
+    const int64_t cn = n - c0 < 2048 ? n - c0 : 2048;
+    __syncthreads();
+    for (int64_t t = threadIdx.x; t < cn; t += blockDim.x) sk[t] = keys[c0 + t];
+    __syncthreads();
+    for (int64_t t = 0; t < cn; ++t) {
+      const uint32_t kj = sk[t];
+      rank += (kj > ki) | ((kj == ki) & (c0 + t < i));
+    }
+  }
+  if (i < n) perm[rank] = (int32_t)i;
+}
+
+// S = H with the lower triangle mirrored from the upper (S fully symmetric).
+__global__ void __launch_bounds__(256)
+symmetrize_kernel(const float* __restrict__ H, int64_t n, float* __restrict__ S) {
+  __shared__ float t[32][33];
+  const int64_t bi = blockIdx.y, bj = blockIdx.x;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  if (bi < bj) {
+    for (int r = ty; r < 32; r += 8) {
+      const int64_t i = bi * 32 + r, j = bj * 32 + tx;
+      if (i < n && j < n) S[i * n + j] = H[i * n + j];
+    }
+    return;
+  }
+  // Tile (bj, bi) of H's upper part, read coalesced, written transposed.
+  for (int r = ty; r < 32; r += 8) {
+    const int64_t i = bj * 32 + r, j = bi * 32 + tx;
+    t[r][tx] = (i < n && j < n) ? H[i * n + j] : 0.0f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int64_t i = bi * 32 + r, j = bj * 32 + tx;
+    if (i < n && j < n) {
+      float v;
+      if (bi > bj) v = t[tx][r];
+      else v = (r <= tx) ? t[r][tx] : t[tx][r];  // diagonal tile: upper as is, lower mirrored
+      S[i * n + j] = v;
+    }
+  }
+}
+
+// A[a][b] (b <= a) = S[q(a)][q(b)] with q(a) = perm[n-1-a]; diagonal: dead fix + damp.
+__global__ void __launch_bounds__(256)
+gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict__ perm,
+              const float* __restrict__ damp_add, float* __restrict__ A) {
+  extern __shared__ float row[];
+  const int64_t a = blockIdx.x;
+  const int64_t src = perm[n - 1 - a];
+  for (int64_t t = threadIdx.x; t < n; t += blockDim.x) row[t] = S[src * n + t];
+  __syncthreads();
+  const float dadd = *damp_add;
+  for (int64_t b = threadIdx.x; b <= a; b += blockDim.x) {
+    float v = row[perm[n - 1 - b]];
+    if (b == a) v = (v == 0.0f ? 1.0f : v) + dadd;
+    A[a * n + b] = v;
+  }
+}
+
+// Leaf of the recursion: factor the m x m diagonal block at `off` (lower part
+// of A, leading dimension n) and invert the factor.  Writes L back into A and
+// L^-1 into X (lower part; X's upper part there stays zero).
+__global__ void __launch_bounds__(256)
+cholinv_leaf_kernel(float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t off, int m,
+                    int32_t* __restrict__ info) {
+  __shared__ float L[NB][NB + 1];
+  __shared__ float Y[NB][NB + 1];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < m * m; e += blockDim.x) {
+    const int i = e / m, j = e % m;
+    L[i][j] = (j <= i) ? A[(off + i) * n + off + j] : 0.0f;
+    Y[i][j] = (i == j) ? 1.0f : 0.0f;
+  }
+  __syncthreads();
+  // Right-looking Cholesky.
+  for (int k = 0; k < m; ++k) {
+    if (tid == 0) {
+      const float d = L[k][k];
+      if (!(d > 0.0f) || !(d < INFINITY)) {
+        // quantization-order column of this pivot is n-1-(off+k)
+        atomicCAS(info, 0, (int32_t)(n - (off + k)));
+      }
+      L[k][k] = sqrtf(d);
+    }
+    __syncthreads();
+    const float piv = L[k][k];
+    for (int i = k + 1 + tid; i < m; i += blockDim.x) L[i][k] = L[i][k] / piv;
+    __syncthreads();
+    const int w = m - k - 1;
+    for (int e = tid; e < w * w; e += blockDim.x) {
+      const int i = k + 1 + e / w, j = k + 1 + e % w;
+      if (j <= i) L[i][j] -= L[i][k] * L[j][k];
+    }
+    __syncthreads();
+  }
+  // Forward substitution L Y = I on all columns at once.
+  for (int k = 0; k < m; ++k) {
+    const float piv = L[k][k];
+    for (int c = tid; c <= k; c += blockDim.x) Y[k][c] = Y[k][c] / piv;
+    __syncthreads();
+    const int w = m - k - 1, h = k + 1;
+    for (int e = tid; e < w * h; e += blockDim.x) {
+      const int i = k + 1 + e / h, c = e % h;
+      Y[i][c] -= L[i][k] * Y[k][c];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < m * m; e += blockDim.x) {
+    const int i = e / m, j = e % m;
+    if (j <= i) {
+      A[(off + i) * n + off + j] = L[i][j];
+      X[(off + i) * n + off + j] = Y[i][j];
+    }
+  }
+}
+
+__global__ void copy2d_kernel(const float* __restrict__ src, int64_t lds, float* __restrict__ dst,
+                              int64_t ldd, int64_t rows, int64_t cols) {
+  const int64_t total = rows * cols;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = e / cols, c = e % cols;
+    dst[r * ldd + c] = src[r * lds + c];
+  }
+}
+
+// In place: U[i][j] = X[n-1-i][n-1-j] for i <= j, 0 below the diagonal.
+// X is lower triangular, so every strictly lower (a, b) moves to the strictly
+// upper (n-1-a, n-1-b) (which holds 0) and diagonal entries swap in pairs.
+__global__ void __launch_bounds__(256)
+reverse_inplace_kernel(float* __restrict__ U, int64_t n) {
+  const int64_t a = blockIdx.y;  // source row
+  for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b <= a;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    if (b < a) {
+      const float v = U[a * n + b];
+      U[(n - 1 - a) * n + (n - 1 - b)] = v;
+      U[a * n + b] = 0.0f;
+    } else if (a < n - 1 - a) {
+      const int64_t c = n - 1 - a;
+      const float v = U[a * n + a];
+      U[a * n + a] = U[c * n + c];
+      U[c * n + c] = v;
+    }
+  }
+}
+
+struct PrepCtx {
+  float* A;
+  float* X;
+  float* T;
+  int64_t n;
+  int32_t* info;
+  hipStream_t s;
+};
+
+hipError_t gemm(PrepCtx& c, int64_t M, int64_t N, int64_t K, const float* Am, int64_t lda, bool ta,
+                const float* Bm, int64_t ldb, bool tb, float* Cm, int64_t ldc, float alpha,
+                float beta, int kmode, bool lower) {
+  GemmArgs g{M, N, K, Am, lda, ta, Bm, ldb, tb, Cm, ldc, alpha, beta, kmode, lower};
+  return launch_gemm_f32(g, c.s);
+}
+
+hipError_t cholinv(PrepCtx& c, int64_t off, int64_t m) {
+  const int64_t n = c.n;
+  if (m <= NB) {
+    hipLaunchKernelGGL(cholinv_leaf_kernel, dim3(1), dim3(256), 0, c.s, c.A, c.X, n, off, (int)m,
+                       c.info);
+    return hipGetLastError();
+  }
+  const int64_t m1 = ((m / 2 + NB - 1) / NB) * NB;
+  const int64_t m2 = m - m1;
+  float* A11 = c.A + off * n + off;
+  float* A21 = c.A + (off + m1) * n + off;
+  float* A22 = c.A + (off + m1) * n + off + m1;
+  float* X11 = c.X + off * n + off;
+  float* X21 = c.X + (off + m1) * n + off;
+  float* X22 = c.X + (off + m1) * n + off + m1;
+  (void)A11;
+  GPTQ_HIP_TRY(cholinv(c, off, m1));
+  // L21 = A21 * X11^T  (X11 lower: op(B)[k][j] = X11[j][k] vanishes for k > j)
+  GPTQ_HIP_TRY(gemm(c, m2, m1, m1, A21, n, false, X11, n, true, c.T, m1, 1.0f, 0.0f, KR_LE_COL,
+                    false));
+  hipLaunchKernelGGL(copy2d_kernel, dim3(1024), dim3(256), 0, c.s, c.T, m1, A21, n, m2, m1);
+  GPTQ_HIP_TRY(hipGetLastError());
+  // A22 -= L21 L21^T (lower tiles)
+  GPTQ_HIP_TRY(gemm(c, m2, m2, m1, A21, n, false, A21, n, true, A22, n, -1.0f, 1.0f, KR_FULL,
+                    true));
+  GPTQ_HIP_TRY(cholinv(c, off + m1, m2));
+  // T = L21 * X11 (X11[k][j] vanishes for k < j)
+  GPTQ_HIP_TRY(gemm(c, m2, m1, m1, A21, n, false, X11, n, false, c.T, m1, 1.0f, 0.0f, KR_GE_COL,
+                    false));
+  // X21 = -X22 * T (X22[i][k] vanishes for k > i)
+  GPTQ_HIP_TRY(gemm(c, m2, m1, m2, X22, n, false, c.T, m1, false, X21, n, -1.0f, 0.0f, KR_LE_ROW,
+                    false));
+  return hipSuccess;
+}
+
+struct PrepLayout {
+  float* A;
+  float* T;
+  uint32_t* keys;
+  float* damp_add;
+  size_t bytes;
+};
+
+PrepLayout carve(void* ws, int64_t n) {
+  Carver c(ws);
+  PrepLayout l;
+  const int64_t m1max = ((n / 2 + NB - 1) / NB) * NB;
+  l.A = c.take<float>((size_t)n * n);
+  // every internal node has m2 <= m1 <= m1max, so m1max^2 holds any L21 / T block
+  l.T = c.take<float>((size_t)m1max * (size_t)m1max);
+  l.keys = c.take<uint32_t>((size_t)n);
+  l.damp_add = c.take<float>(1);
+  l.bytes = c.used;
+  return l;
+}
+
+}  // namespace
+
+size_t prepare_workspace_bytes(int64_t n) { return carve(nullptr, n).bytes; }
+
+hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, float* U,
+                       int32_t* perm, int32_t* info, void* ws, hipStream_t s) {
+  PrepLayout l = carve(ws, n);
+  hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp, l.keys, l.damp_add,
+                     info);
+  GPTQ_HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, l.keys, n,
+                     desc_act, perm);
+  GPTQ_HIP_TRY(hipGetLastError());
+  // S (symmetric H) is staged in the output buffer, gathered into A, then the
+  // output buffer is cleared and receives L^-1.
+  const unsigned nb32 = (unsigned)((n + 31) / 32);
+  hipLaunchKernelGGL(symmetrize_kernel, dim3(nb32, nb32), dim3(256), 0, s, H, n, U);
+  GPTQ_HIP_TRY(hipGetLastError());
+  const size_t lds = (size_t)n * sizeof(float);
+  GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)gather_kernel,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)n), dim3(256), lds, s, U, n, perm, l.damp_add,
+                     l.A);
+  GPTQ_HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(2048), dim3(256), 0, s, U, n * n, 0.0f);
+  GPTQ_HIP_TRY(hipGetLastError());
+  PrepCtx c{l.A, U, l.T, n, info, s};
+  GPTQ_HIP_TRY(cholinv(c, 0, n));
+  const unsigned gx = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(reverse_inplace_kernel, dim3(gx, (unsigned)n), dim3(256), 0, s, U, n);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

@@ -1,0 +1,415 @@
+// gptq_quantize_layer: the column sweep with error compensation, lazy block
+// updates on the matrix cores, and dense b-bit packing.
+//
+// Glossary entry "gptq", "Algorithm" step (2): for each weight in order,
+// quantize it, compute its error, adjust the remaining weights of the row to
+// compensate.  With U' = diag(U)^-1 U (U the upper Cholesky factor of the
+// inverse damped Hessian in quantization order) the adjustment after column j
+// is  w_k -= e_j * U'_jk  for k > j.  Rows never interact.
+//
+// Blocking: columns are swept in blocks of B (32/64/128).  Inside a block a
+// workgroup owns a slab of 32 rows; each row is spread over the 4 lanes of a
+// quad, lane q holding block columns 4r + q in registers (r < B/4), and U' of
+// the block sits in LDS, lane-interleaved so each lane reads its own
+// coefficients as float4.  Per column: the owning lane's value is broadcast
+// with a quad DPP move, all 4 lanes decide the code identically, and each lane
+// updates its remaining registers.  Group scale/zero ("gptq" agent skill page,
+// "Group-wise quantization") are taken at the group's first column from the
+// group's current values with two quad DPP reductions.
+//
+// Across blocks, the updates from a finished range of columns to the columns
+// right of it are applied as one fp32 GEMM (W[:, right] -= E[:, left] U'[left,
+// right]) on a recursive halving schedule: the left half is swept, one GEMM
+// carries all its updates to the right half, then the right half is swept.
+// Each pair (j < k) is updated exactly once, before column k is read.
+#include "common.hpp"
+
+namespace gptq {
+namespace {
+
+constexpr int SW_THREADS = 128;            // 2 waves
+constexpr int SW_ROWS = SW_THREADS / 4;    // rows per workgroup
+
+__device__ inline float dpp_bcast(float v, int lane_in_quad) {
+  // quad_perm [o, o, o, o]
+  int r;
+  switch (lane_in_quad) {
+    case 0: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x00, 0xF, 0xF, false); break;
+    case 1: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x55, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xAA, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xFF, 0xF, 0xF, false); break;
+  }
+  return __int_as_float(r);
+}
+__device__ inline float dpp_xor1(float v) {  // quad_perm [1, 0, 3, 2]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ inline float dpp_xor2(float v) {  // quad_perm [2, 3, 0, 1]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// Scale / zero of a group from its (row-wide) lo / hi, with 0 already included.
+__device__ inline void grid_params(float lo, float hi, int bits, int sym, float& s, float& z) {
+  const float maxq = (float)((1 << bits) - 1);
+  if (sym) {
+    hi = fmaxf(-lo, hi);
+    lo = -hi;
+  }
+  if (lo == hi) {
+    lo = -1.0f;
+    hi = 1.0f;
+  }
+  s = (hi - lo) / maxq;
+  z = sym ? (float)(1 << (bits - 1)) : rintf(-lo / s);
+}
+
+template <typename T>
+__device__ inline float to_f32(T v);
+template <>
+__device__ inline float to_f32<float>(float v) { return v; }
+template <>
+__device__ inline float to_f32<_Float16>(_Float16 v) { return (float)v; }
+template <>
+__device__ inline float to_f32<uint16_t>(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Wp[r][j] = W[r][perm[j]] as fp32 (perm == nullptr: identity).
+template <typename T>
+__global__ void __launch_bounds__(256)
+gather_w_kernel(const T* __restrict__ W, int64_t out, int64_t in, const int32_t* __restrict__ perm,
+                float* __restrict__ Wp) {
+  extern __shared__ float rowbuf[];
+  const int64_t r = blockIdx.x;
+  const T* src = W + r * in;
+  float* dst = Wp + r * in;
+  if (perm == nullptr) {
+    for (int64_t j = threadIdx.x; j < in; j += blockDim.x) dst[j] = to_f32<T>(src[j]);
+    return;
+  }
+  for (int64_t j = threadIdx.x; j < in; j += blockDim.x) rowbuf[j] = to_f32<T>(src[j]);
+  __syncthreads();
+  for (int64_t j = threadIdx.x; j < in; j += blockDim.x) {
+    int32_t p = perm[j];
+    if ((uint32_t)p >= (uint32_t)in) p = 0;  // never read outside the row
+    dst[j] = rowbuf[p];
+  }
+}
+
+// Up[j][k] = U[j][k] / U[j][j] for k > j, 0 for k <= j.
+__global__ void __launch_bounds__(256)
+uprime_kernel(const float* __restrict__ U, int64_t n, float* __restrict__ Up) {
+  const int64_t j = blockIdx.y;
+  const float d = U[j * n + j];
+  for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
+       k += (int64_t)gridDim.x * blockDim.x)
+    Up[j * n + k] = k > j ? U[j * n + k] / d : 0.0f;
+}
+
+// pinv[perm[j]] = j;  g_idx[perm[j]] = j / gs (0 for one group per row).
+__global__ void perm_tables_kernel(const int32_t* __restrict__ perm, int64_t in, int gs,
+                                   int32_t* __restrict__ pinv, int32_t* __restrict__ g_idx) {
+  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (j >= in) return;
+  int32_t p = perm ? perm[j] : (int32_t)j;
+  if ((uint32_t)p >= (uint32_t)in) p = 0;
+  pinv[p] = (int32_t)j;
+  g_idx[p] = gs > 0 ? (int32_t)(j / gs) : 0;
+}
+
+// One group per row: scale/zero from the whole original row.
+__global__ void __launch_bounds__(256)
+row_params_kernel(const float* __restrict__ Wp, int64_t out, int64_t in, int bits, int sym,
+                  float* __restrict__ scales, int32_t* __restrict__ zeros) {
+  __shared__ float slo[256], shi[256];
+  const int64_t r = blockIdx.x;
+  float lo = 0.0f, hi = 0.0f;
+  for (int64_t j = threadIdx.x; j < in; j += blockDim.x) {
+    const float v = Wp[r * in + j];
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  slo[threadIdx.x] = lo;
+  shi[threadIdx.x] = hi;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      slo[threadIdx.x] = fminf(slo[threadIdx.x], slo[threadIdx.x + w]);
+      shi[threadIdx.x] = fmaxf(shi[threadIdx.x], shi[threadIdx.x + w]);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    float s, z;
+    grid_params(slo[0], shi[0], bits, sym, s, z);
+    scales[r] = s;
+    zeros[r] = (int32_t)z;
+  }
+}
+
+// Sweep of block columns [c0, c0 + width) for a slab of 32 rows.
+// GS: group size (divides B, multiple of 4) or 0 = one group per row
+// (scales[0][r] / zeros[0][r] precomputed).
+template <int B, int GS>
+__global__ void __launch_bounds__(SW_THREADS)
+sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, int64_t in,
+             int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
+             int32_t* __restrict__ zeros, uint8_t* __restrict__ codes) {
+  constexpr int NR = B / 4;
+  constexpr int PITCH = NR + 4;
+  __shared__ __align__(16) float Ul[B * 4 * PITCH];
+
+  const int tid = threadIdx.x;
+  const int q = tid & 3;
+  const int64_t row = (int64_t)blockIdx.x * SW_ROWS + (tid >> 2);
+  const bool live = row < out;
+
+  // U' block, lane-interleaved: Ul[j][q][r] = U'[c0+j][c0+4r+q] (0 outside the block).
+  for (int e = tid; e < B * B; e += SW_THREADS) {
+    const int j = e / B, col = e % B;
+    float v = 0.0f;
+    if (j < width && col < width) v = Up[(c0 + j) * in + c0 + col];
+    Ul[j * 4 * PITCH + (col & 3) * PITCH + (col >> 2)] = v;
+  }
+
+  float w[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int col = 4 * r + q;
+    w[r] = (live && col < width) ? Wp[row * in + c0 + col] : 0.0f;
+  }
+  uint32_t cpk[NR / 4 > 0 ? NR / 4 : 1];
+#pragma unroll
+  for (int r = 0; r < (NR / 4 > 0 ? NR / 4 : 1); ++r) cpk[r] = 0;
+
+  const float maxq = (float)((1 << bits) - 1);
+  float s = 1.0f, z = 0.0f;
+  if constexpr (GS == 0) {
+    if (live) {
+      s = scales[row];
+      z = (float)zeros[row];
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    if (j >= width) break;
+    const int R = j / 4, o = j % 4;
+    if constexpr (GS > 0) {
+      if (j % GS == 0) {
+        // range of the group's current values, 0 included
+        float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          if (r >= j / 4 && r < (j + GS) / 4) {
+            lo = fminf(lo, w[r]);
+            hi = fmaxf(hi, w[r]);
+          }
+        }
+        lo = fminf(lo, dpp_xor1(lo));
+        hi = fmaxf(hi, dpp_xor1(hi));
+        lo = fminf(lo, dpp_xor2(lo));
+        hi = fmaxf(hi, dpp_xor2(hi));
+        grid_params(lo, hi, bits, sym, s, z);
+        if (live && q == 0) {
+          const int64_t g = (c0 + j) / GS;
+          scales[g * out + row] = s;
+          zeros[g * out + row] = (int32_t)z;
+        }
+      }
+    }
+    const float wj = dpp_bcast(w[R], o);
+    const float qf = fminf(fmaxf(rintf(wj / s) + z, 0.0f), maxq);
+    const float err = wj - s * (qf - z);
+    if (q == o) {
+      w[R] = err;
+      cpk[R / 4] |= (uint32_t)qf << (8 * (R % 4));
+    }
+    const float* urow = Ul + j * 4 * PITCH + q * PITCH;
+#pragma unroll
+    for (int r4 = (R / 4) * 4; r4 < NR; r4 += 4) {
+      const float4 u = *reinterpret_cast<const float4*>(urow + r4);
+      w[r4 + 0] = fmaf(-err, u.x, w[r4 + 0]);
+      if (r4 + 1 < NR) w[r4 + 1] = fmaf(-err, u.y, w[r4 + 1]);
+      if (r4 + 2 < NR) w[r4 + 2] = fmaf(-err, u.z, w[r4 + 2]);
+      if (r4 + 3 < NR) w[r4 + 3] = fmaf(-err, u.w, w[r4 + 3]);
+    }
+  }
+
+  if (live) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int col = 4 * r + q;
+      if (col < width) {
+        Wp[row * in + c0 + col] = w[r];  // the column's error, read by the trailing GEMMs
+        codes[row * in + c0 + col] = (uint8_t)((cpk[r / 4] >> (8 * (r % 4))) & 0xFF);
+      }
+    }
+  }
+}
+
+// qweight[u*bits + t][r]: word t of the 32-code unit u of row r (original column order).
+__global__ void __launch_bounds__(256)
+pack_kernel(const uint8_t* __restrict__ codes, const int32_t* __restrict__ pinv, int64_t out,
+            int64_t in, int bits, int32_t* __restrict__ qweight) {
+  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t u = blockIdx.y;
+  if (r >= out) return;
+  const uint8_t* crow = codes + r * in;
+  uint64_t acc = 0;
+  int nb = 0, t = 0;
+  for (int c = 0; c < 32; ++c) {
+    const uint32_t code = crow[pinv[u * 32 + c]];
+    acc |= (uint64_t)code << nb;
+    nb += bits;
+    if (nb >= 32) {
+      qweight[(u * bits + t) * out + r] = (int32_t)(uint32_t)acc;
+      acc >>= 32;
+      nb -= 32;
+      ++t;
+    }
+  }
+}
+
+template <int B>
+hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t in, int64_t c0,
+                        int width, int bits, int sym, float* scales, int32_t* zeros,
+                        uint8_t* codes, hipStream_t s) {
+  if (gs > B) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((out + SW_ROWS - 1) / SW_ROWS)), block(SW_THREADS);
+#define GPTQ_SWEEP_CASE(G)                                                                    \
+  case G:                                                                                     \
+    hipLaunchKernelGGL((sweep_kernel<B, (G > 0 ? G : 0)>), grid, block, 0, s, Wp, Up, out, in, \
+                       c0, width, bits, sym, scales, zeros, codes);                           \
+    break;
+  switch (gs > 0 ? gs : 0) {
+    GPTQ_SWEEP_CASE(0)
+    GPTQ_SWEEP_CASE(4)
+    GPTQ_SWEEP_CASE(8)
+    GPTQ_SWEEP_CASE(16)
+    GPTQ_SWEEP_CASE(32)
+    case 64:
+      if constexpr (B >= 64) {
+        hipLaunchKernelGGL((sweep_kernel<B, (B >= 64 ? 64 : 4)>), grid, block, 0, s, Wp, Up, out,
+                           in, c0, width, bits, sym, scales, zeros, codes);
+      }
+      break;
+    case 128:
+      if constexpr (B >= 128) {
+        hipLaunchKernelGGL((sweep_kernel<B, (B >= 128 ? 128 : 4)>), grid, block, 0, s, Wp, Up,
+                           out, in, c0, width, bits, sym, scales, zeros, codes);
+      }
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef GPTQ_SWEEP_CASE
+  return hipGetLastError();
+}
+
+struct QCtx {
+  float* Wp;
+  const float* Up;
+  int64_t out, in;
+  int bits, gs, sym, block;
+  float* scales;
+  int32_t* zeros;
+  uint8_t* codes;
+  hipStream_t s;
+};
+
+hipError_t sweep_block(QCtx& c, int64_t a, int64_t b) {
+  const int width = (int)(b - a);
+  switch (c.block) {
+    case 32: return launch_sweep<32>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
+                                     c.scales, c.zeros, c.codes, c.s);
+    case 64: return launch_sweep<64>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
+                                     c.scales, c.zeros, c.codes, c.s);
+    default: return launch_sweep<128>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
+                                      c.scales, c.zeros, c.codes, c.s);
+  }
+}
+
+// Columns [a, b): sweep the left half, carry its updates to the right half
+// with one GEMM, then the right half.
+hipError_t process(QCtx& c, int64_t a, int64_t b) {
+  const int64_t B = c.block;
+  if (b - a <= B) return sweep_block(c, a, b);
+  const int64_t nblk = (b - a + B - 1) / B;
+  const int64_t m = a + B * ((nblk + 1) / 2);
+  GPTQ_HIP_TRY(process(c, a, m));
+  GemmArgs g{c.out, b - m, m - a, c.Wp + a, c.in, false, c.Up + a * c.in + m, c.in, false,
+             c.Wp + m, c.in, -1.0f, 1.0f, KR_FULL, false};
+  GPTQ_HIP_TRY(launch_gemm_f32(g, c.s));
+  return process(c, m, b);
+}
+
+struct QLayout {
+  float* Wp;
+  float* Up;
+  uint8_t* codes;
+  int32_t* pinv;
+  size_t bytes;
+};
+
+QLayout carve(void* ws, int64_t out, int64_t in) {
+  Carver c(ws);
+  QLayout l;
+  l.Wp = c.take<float>((size_t)out * in);
+  l.Up = c.take<float>((size_t)in * in);
+  l.codes = c.take<uint8_t>((size_t)out * in);
+  l.pinv = c.take<int32_t>((size_t)in);
+  l.bytes = c.used;
+  return l;
+}
+
+}  // namespace
+
+size_t quantize_workspace_bytes(int64_t out, int64_t in, int, int, int) {
+  return carve(nullptr, out, in).bytes;
+}
+
+hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, const float* U,
+                        const int32_t* perm, int bits, int gs, int sym, int block,
+                        int32_t* qweight, float* scales, int32_t* zeros, int32_t* g_idx,
+                        void* ws, hipStream_t s) {
+  QLayout l = carve(ws, out, in);
+  const size_t lds = perm ? (size_t)in * sizeof(float) : 0;
+  if (wdtype == 0) {
+    auto k = gather_w_kernel<_Float16>;
+    GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds));
+    hipLaunchKernelGGL(k, dim3((unsigned)out), dim3(256), lds, s,
+                       static_cast<const _Float16*>(W), out, in, perm, l.Wp);
+  } else if (wdtype == 1) {
+    auto k = gather_w_kernel<uint16_t>;
+    GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds));
+    hipLaunchKernelGGL(k, dim3((unsigned)out), dim3(256), lds, s,
+                       static_cast<const uint16_t*>(W), out, in, perm, l.Wp);
+  } else {
+    auto k = gather_w_kernel<float>;
+    GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds));
+    hipLaunchKernelGGL(k, dim3((unsigned)out), dim3(256), lds, s, static_cast<const float*>(W),
+                       out, in, perm, l.Wp);
+  }
+  GPTQ_HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(uprime_kernel, dim3((unsigned)((in + 255) / 256), (unsigned)in), dim3(256), 0,
+                     s, U, in, l.Up);
+  GPTQ_HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(perm_tables_kernel, dim3((unsigned)((in + 255) / 256)), dim3(256), 0, s, perm,
+                     in, gs, l.pinv, g_idx);
+  GPTQ_HIP_TRY(hipGetLastError());
+  if (gs <= 0) {
+    hipLaunchKernelGGL(row_params_kernel, dim3((unsigned)out), dim3(256), 0, s, l.Wp, out, in,
+                       bits, sym, scales, zeros);
+    GPTQ_HIP_TRY(hipGetLastError());
+  }
+  QCtx c{l.Wp, l.Up, out, in, bits, gs, sym, block, scales, zeros, l.codes, s};
+  GPTQ_HIP_TRY(process(c, 0, in));
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((out + 255) / 256), (unsigned)(in / 32)),
+                     dim3(256), 0, s, l.codes, l.pinv, out, in, bits, qweight);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

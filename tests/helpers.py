@@ -1,0 +1,81 @@
+"""Shared test helpers: comparison of the HIP path with the oracle.
+
+The oracle is run on the very same input bytes the GPU receives.  Where a
+floating-point value decides an integer (a code, a zero-point), the oracle
+decides in float32 like the kernels; a disagreement is accepted only where
+the oracle's own pre-rounding value lies within 1e-3 (code units) of a
+rounding boundary, and at most 0.1 % of entries may disagree.  After such a
+disagreement the oracle continues from the GPU's decision (teacher forcing),
+so one boundary case cannot cascade along a row and every later value is
+still checked against an exact GPTQ continuation.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+
+CODE_WINDOW = 1e-3       # code units
+CODE_FRACTION = 1e-3     # at most 0.1 % of codes may differ
+SCALE_RTOL = 1e-3
+
+
+def np64(t) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy() if t.dtype != torch.int32 \
+        else t.detach().to("cpu").numpy()
+
+
+def gpu_codes(qweight, bits, inp):
+    return O.unpack(qweight.cpu().numpy(), bits, inp)
+
+
+def check_quantize_parity(W_t, U_t, perm_t, bits, gs, sym, qweight, scales, zeros, g_idx,
+                          rows=None):
+    """Stage check of gptq_quantize_layer against the oracle sweep in replay mode.
+
+    W_t, U_t, perm_t: the exact inputs the GPU got.  rows: optional subset of
+    output rows (rows are independent, so a subset is an exact check of those
+    rows).  Returns a dict of diagnostics; asserts the tolerances.
+    """
+    W = W_t.detach().cpu().to(torch.float64).numpy()
+    U = U_t.detach().cpu().to(torch.float64).numpy()
+    inp = W.shape[1]
+    perm = np.arange(inp) if perm_t is None else perm_t.cpu().numpy().astype(np.int64)
+    codes = gpu_codes(qweight, bits, inp)                   # [out x in], original order
+    sc = scales.cpu().numpy()
+    zr = zeros.cpu().numpy().astype(np.int64)
+    gi = g_idx.cpu().numpy().astype(np.int64)
+    if rows is None:
+        rows = np.arange(W.shape[0])
+    rows = np.asarray(rows)
+    codes_perm = codes[rows][:, perm]
+    ref = O.gptq_sweep(W[rows], U, perm, bits, gs, sym,
+                       forced_codes=codes_perm, forced_zeros=zr[:, rows])
+    assert np.array_equal(gi, O.g_index(perm, gs)), "g_idx differs"
+    code_mm = [m for m in ref.mismatches if m[0] == "code"]
+    zero_mm = [m for m in ref.mismatches if m[0] == "zero"]
+    total = codes_perm.size
+    worst = max([m[5] for m in ref.mismatches], default=0.0)
+    # boundary distance of the oracle's own pre-rounding value for every mismatch
+    far = [m for m in ref.mismatches if m[5] > CODE_WINDOW]
+    assert not far, f"{len(far)} decisions differ away from a rounding boundary, e.g. {far[:3]}"
+    assert len(code_mm) <= CODE_FRACTION * total, f"{len(code_mm)} of {total} codes differ"
+    assert len(zero_mm) <= CODE_FRACTION * zr[:, rows].size
+    rel = np.abs(sc[:, rows].astype(np.float64) - ref.scales.astype(np.float64)) / \
+        np.maximum(np.abs(ref.scales.astype(np.float64)), 1e-30)
+    assert rel.max() <= SCALE_RTOL, f"scale rel err {rel.max()}"
+    assert codes.min() >= 0 and codes.max() < 2 ** bits
+    return {"code_mismatches": len(code_mm), "zero_mismatches": len(zero_mm),
+            "entries": total, "worst_distance": worst, "scale_rel": float(rel.max())}
+
+
+def rel_fro(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def upper_mirror(H: np.ndarray) -> np.ndarray:
+    u = np.triu(H)
+    return u + np.triu(u, 1).T

@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every function include/gptq.h declares,
+and rejects invalid arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+
+import pytest
+
+import post_weight_quantization_12_amd as P
+from post_weight_quantization_12_amd import _lib as L
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return P.load()
+
+
+def test_exports_every_header_function(lib):
+    names = P.header_functions()
+    assert set(names) == {"gptq_hessian_accumulate", "gptq_prepare_workspace_bytes",
+                          "gptq_prepare", "gptq_quantize_workspace_bytes",
+                          "gptq_quantize_layer", "gptq_status_string",
+                          "gptq_last_error_message"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.gptq_status_string(s)
+    assert b"unknown" in lib.gptq_status_string(99)
+
+
+def test_hessian_argument_errors(lib):
+    f = lib.gptq_hessian_accumulate
+    assert f(None, 8, FAKE, 0, 4, 8, None) == L.GPTQ_ERR_INVALID_ARG
+    assert b"H" in lib.gptq_last_error_message()
+    assert f(FAKE, 8, None, 0, 4, 8, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, FAKE, 0, 4, 8, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 8, FAKE, 0, -1, 8, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 8, FAKE, 0, 4, 7, None) == L.GPTQ_ERR_INVALID_ARG
+    assert b"ldx" in lib.gptq_last_error_message()
+    assert f(FAKE, 8, FAKE, 2, 4, 8, None) == L.GPTQ_ERR_UNSUPPORTED
+    # ntok == 0 is a no-op that never touches the device
+    assert f(FAKE, 8, FAKE, 0, 0, 8, None) == L.GPTQ_OK
+    assert lib.gptq_last_error_message() == b""
+
+
+def test_prepare_argument_errors(lib):
+    f = lib.gptq_prepare
+    ws = lib.gptq_prepare_workspace_bytes(64)
+    assert ws > 64 * 64 * 4
+    assert lib.gptq_prepare_workspace_bytes(0) == 0
+    assert lib.gptq_prepare_workspace_bytes(L.MAX_PREPARE_N + 1) == 0
+    assert f(None, 64, 0.01, 0, FAKE, FAKE, FAKE, FAKE, ws, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 64, 0.01, 0, FAKE, None, FAKE, FAKE, ws, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 64, -0.1, 0, ctypes.c_void_p(8192), FAKE, FAKE, FAKE, ws, None) == \
+        L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 64, float("nan"), 0, ctypes.c_void_p(8192), FAKE, FAKE, FAKE, ws, None) == \
+        L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, L.MAX_PREPARE_N + 1, 0.01, 0, ctypes.c_void_p(8192), FAKE, FAKE, FAKE, ws,
+             None) == L.GPTQ_ERR_UNSUPPORTED
+    assert f(FAKE, 64, 0.01, 0, FAKE, ctypes.c_void_p(8192), FAKE, FAKE, ws, None) == \
+        L.GPTQ_ERR_INVALID_ARG  # H aliases Hinv_chol
+    assert f(FAKE, 64, 0.01, 0, ctypes.c_void_p(8192), FAKE, FAKE, FAKE, ws - 1, None) == \
+        L.GPTQ_ERR_WORKSPACE
+
+
+def _q(lib, out=16, inp=256, bits=4, gs=128, sym=0, block=128, ws=None, W=FAKE, dtype=0):
+    if ws is None:
+        ws = lib.gptq_quantize_workspace_bytes(out, inp, bits, gs, block) or 1
+    return lib.gptq_quantize_layer(W, dtype, out, inp, FAKE, None, bits, gs, sym, block,
+                                   FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+
+
+def test_quantize_argument_errors(lib):
+    assert lib.gptq_quantize_workspace_bytes(16, 256, 4, 128, 128) >= 16 * 256 * 4 + 256 * 256 * 4
+    assert _q(lib, W=None) == L.GPTQ_ERR_INVALID_ARG
+    assert _q(lib, dtype=7) == L.GPTQ_ERR_INVALID_ARG
+    assert _q(lib, out=0) == L.GPTQ_ERR_INVALID_ARG
+    assert _q(lib, inp=250) == L.GPTQ_ERR_INVALID_ARG
+    assert b"multiple of 32" in lib.gptq_last_error_message()
+    assert _q(lib, bits=5) == L.GPTQ_ERR_UNSUPPORTED
+    assert _q(lib, bits=1) == L.GPTQ_ERR_UNSUPPORTED
+    assert _q(lib, block=96) == L.GPTQ_ERR_UNSUPPORTED
+    assert _q(lib, gs=96) == L.GPTQ_ERR_INVALID_ARG     # does not divide block
+    assert _q(lib, gs=2) == L.GPTQ_ERR_INVALID_ARG      # not a multiple of 4
+    assert _q(lib, gs=256) == L.GPTQ_ERR_INVALID_ARG    # larger than block
+    assert _q(lib, gs=0) == L.GPTQ_ERR_INVALID_ARG
+    assert _q(lib, sym=2) == L.GPTQ_ERR_INVALID_ARG
+    assert _q(lib, ws=10) == L.GPTQ_ERR_WORKSPACE
+    assert lib.gptq_quantize_workspace_bytes(16, 256, 5, 128, 128) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        P.hessian_accumulate(torch.zeros(4, 4), torch.zeros(2, 4, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        P.prepare(torch.eye(4), 0.01, False)
