@@ -134,59 +134,83 @@ gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict_
   }
 }
 
-// Leaf of the recursion: factor the m x m diagonal block at `off` (lower part
-// of A, leading dimension n) and invert the factor.  Writes L back into A and
-// L^-1 into X (lower part; X's upper part there stays zero).
-__global__ void __launch_bounds__(256)
+// Leaf of the recursion: factor the m x m (m <= 64) diagonal block at `off`
+// (lower part of A, leading dimension n) and invert the factor, in one wave.
+//
+// Lane i keeps the not-yet-factored part of row i in a sliding register
+// window: at step k, a[t] holds column k + t, so the column being eliminated
+// is always a[0] and every register index is a compile-time constant while
+// the loop over k stays rolled (small code).  The scaled column k is shared
+// through LDS.  The inverse Y = L^-1 is built the same way with the rows of Y
+// broadcast through LDS.  Writes L into A and L^-1 into X (lower parts).
+__global__ void __launch_bounds__(64)
 cholinv_leaf_kernel(float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t off, int m,
                     int32_t* __restrict__ info) {
-  __shared__ float L[NB][NB + 1];
-  __shared__ float Y[NB][NB + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < m * m; e += blockDim.x) {
-    const int i = e / m, j = e % m;
-    L[i][j] = (j <= i) ? A[(off + i) * n + off + j] : 0.0f;
-    Y[i][j] = (i == j) ? 1.0f : 0.0f;
-  }
-  __syncthreads();
-  // Right-looking Cholesky.
+  __shared__ __align__(16) float col[2 * NB];   // column k of L, zero-padded
+  __shared__ __align__(16) float Ls[NB][NB + 1];  // the factor L (row i, column k)
+  __shared__ __align__(16) float yrow[NB];
+  const int lane = threadIdx.x;
+  const bool row_ok = lane < m;
+  const float* arow = A + (off + lane) * n + off;
+  float a[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) a[j] = (row_ok && j <= lane && j < m) ? arow[j] : 0.0f;
+  col[NB + lane] = 0.0f;
+
   for (int k = 0; k < m; ++k) {
-    if (tid == 0) {
-      const float d = L[k][k];
-      if (!(d > 0.0f) || !(d < INFINITY)) {
-        // quantization-order column of this pivot is n-1-(off+k)
-        atomicCAS(info, 0, (int32_t)(n - (off + k)));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[0]), k));
+    if (lane == 0 && (!(d > 0.0f) || !(d < INFINITY)))
+      atomicCAS(info, 0, (int32_t)(n - (off + k)));  // quantization-order column n-1-(off+k)
+    const float piv = sqrtf(d);
+    const float lik = lane > k ? a[0] / piv : (lane == k ? piv : 0.0f);
+    Ls[lane][k] = lik;
+    col[lane] = lane > k ? lik : 0.0f;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    // a[t] (column k+1+t after the shift) -= L[i][k] * L[k+1+t][k]
+    const float g = lane > k ? lik : 0.0f;
+#pragma unroll
+    for (int t = 0; t < NB - 1; ++t) a[t] = fmaf(-g, col[k + 1 + t], a[t + 1]);
+    a[NB - 1] = 0.0f;
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // Y = L^-1: row k of Y is final once divided by L[k][k]; rows i > k then
+  // subtract L[i][k] * Y[k][:].  y[c] holds column c (no shifting needed).
+  float y[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) y[c] = (c == lane) ? 1.0f : 0.0f;
+  for (int k = 0; k < m; ++k) {
+    if (lane == k) {
+      const float rpiv = 1.0f / Ls[k][k];
+#pragma unroll
+      for (int c = 0; c < NB; ++c) y[c] = y[c] * rpiv;
+#pragma unroll
+      for (int c4 = 0; c4 < NB; c4 += 4)
+        *reinterpret_cast<float4*>(yrow + c4) = make_float4(y[c4], y[c4 + 1], y[c4 + 2], y[c4 + 3]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    const float g = lane > k ? Ls[lane][k] : 0.0f;
+#pragma unroll
+    for (int c4 = 0; c4 < NB; c4 += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(yrow + c4);
+      y[c4 + 0] = fmaf(-g, v.x, y[c4 + 0]);
+      y[c4 + 1] = fmaf(-g, v.y, y[c4 + 1]);
+      y[c4 + 2] = fmaf(-g, v.z, y[c4 + 2]);
+      y[c4 + 3] = fmaf(-g, v.w, y[c4 + 3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (row_ok) {
+    float* lrow = A + (off + lane) * n + off;
+    float* xrow = X + (off + lane) * n + off;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j <= lane && j < m) {
+        lrow[j] = Ls[lane][j];
+        xrow[j] = y[j];
       }
-      L[k][k] = sqrtf(d);
-    }
-    __syncthreads();
-    const float piv = L[k][k];
-    for (int i = k + 1 + tid; i < m; i += blockDim.x) L[i][k] = L[i][k] / piv;
-    __syncthreads();
-    const int w = m - k - 1;
-    for (int e = tid; e < w * w; e += blockDim.x) {
-      const int i = k + 1 + e / w, j = k + 1 + e % w;
-      if (j <= i) L[i][j] -= L[i][k] * L[j][k];
-    }
-    __syncthreads();
-  }
-  // Forward substitution L Y = I on all columns at once.
-  for (int k = 0; k < m; ++k) {
-    const float piv = L[k][k];
-    for (int c = tid; c <= k; c += blockDim.x) Y[k][c] = Y[k][c] / piv;
-    __syncthreads();
-    const int w = m - k - 1, h = k + 1;
-    for (int e = tid; e < w * h; e += blockDim.x) {
-      const int i = k + 1 + e / h, c = e % h;
-      Y[i][c] -= L[i][k] * Y[k][c];
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < m * m; e += blockDim.x) {
-    const int i = e / m, j = e % m;
-    if (j <= i) {
-      A[(off + i) * n + off + j] = L[i][j];
-      X[(off + i) * n + off + j] = Y[i][j];
     }
   }
 }
@@ -241,7 +265,7 @@ hipError_t gemm(PrepCtx& c, int64_t M, int64_t N, int64_t K, const float* Am, in
 hipError_t cholinv(PrepCtx& c, int64_t off, int64_t m) {
   const int64_t n = c.n;
   if (m <= NB) {
-    hipLaunchKernelGGL(cholinv_leaf_kernel, dim3(1), dim3(256), 0, c.s, c.A, c.X, n, off, (int)m,
+    hipLaunchKernelGGL(cholinv_leaf_kernel, dim3(1), dim3(64), 0, c.s, c.A, c.X, n, off, (int)m,
                        c.info);
     return hipGetLastError();
   }

@@ -148,26 +148,63 @@ row_params_kernel(const float* __restrict__ Wp, int64_t out, int64_t in, int bit
 // Sweep of block columns [c0, c0 + width) for a slab of 32 rows.
 // GS: group size (divides B, multiple of 4) or 0 = one group per row
 // (scales[0][r] / zeros[0][r] precomputed).
+//
+// Lane q of a row's quad holds block columns 4r + q.  The registers form a
+// sliding window: at quad-step R (block columns 4R .. 4R+3), w[t] holds column
+// 4(R + t) + q, so the columns being quantized are always in w[0] and every
+// register index is a compile-time constant while the loop over R stays
+// rolled.  U' rows are stored pre-shifted to the same window:
+//     Ul[j][q][t] = U'[c0 + j][c0 + 4(j/4 + t) + q]   (0 outside the block),
+// which is 0 wherever that column is not right of j (U' is strictly upper).
+template <int B>
+struct SweepSmem {
+  static constexpr int NR = B / 4, PITCH = NR + 4, EP = B + 4;
+  static constexpr size_t UL = (size_t)B * 4 * PITCH;          // floats
+  static constexpr size_t ES = (size_t)SW_ROWS * EP;            // floats
+  static constexpr size_t BYTES = (UL + ES) * sizeof(float) + (size_t)SW_ROWS * B;
+};
+
 template <int B, int GS>
 __global__ void __launch_bounds__(SW_THREADS)
 sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, int64_t in,
              int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
              int32_t* __restrict__ zeros, uint8_t* __restrict__ codes) {
-  constexpr int NR = B / 4;
-  constexpr int PITCH = NR + 4;
-  __shared__ __align__(16) float Ul[B * 4 * PITCH];
+  using SM = SweepSmem<B>;
+  constexpr int NR = SM::NR, PITCH = SM::PITCH, EP = SM::EP;
+  extern __shared__ __align__(16) float smem[];
+  float* Ul = smem;
+  float* Es = smem + SM::UL;
+  uint8_t* Cs = reinterpret_cast<uint8_t*>(Es + SM::ES);
 
   const int tid = threadIdx.x;
-  const int q = tid & 3;
-  const int64_t row = (int64_t)blockIdx.x * SW_ROWS + (tid >> 2);
+  const int q = tid & 3, rl = tid >> 2;
+  const int64_t row0 = (int64_t)blockIdx.x * SW_ROWS;
+  const int64_t row = row0 + rl;
   const bool live = row < out;
 
-  // U' block, lane-interleaved: Ul[j][q][r] = U'[c0+j][c0+4r+q] (0 outside the block).
-  for (int e = tid; e < B * B; e += SW_THREADS) {
-    const int j = e / B, col = e % B;
-    float v = 0.0f;
-    if (j < width && col < width) v = Up[(c0 + j) * in + c0 + col];
-    Ul[j * 4 * PITCH + (col & 3) * PITCH + (col >> 2)] = v;
+  // Pre-shifted U' window: item (j, t) is the float4 of columns 4(j/4 + t) .. +3.
+  {
+    constexpr int ITEMS = B * NR / SW_THREADS;
+    float4 v[ITEMS];
+#pragma unroll
+    for (int p = 0; p < ITEMS; ++p) {
+      const int e = tid + p * SW_THREADS;
+      const int j = e / NR, t = e % NR;
+      const int c = 4 * (j / 4 + t);
+      v[p] = (j < width && c < width)
+                 ? *reinterpret_cast<const float4*>(Up + (c0 + j) * in + c0 + c)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int p = 0; p < ITEMS; ++p) {
+      const int e = tid + p * SW_THREADS;
+      const int j = e / NR, t = e % NR;
+      float* d = Ul + j * 4 * PITCH + t;
+      d[0 * PITCH] = v[p].x;
+      d[1 * PITCH] = v[p].y;
+      d[2 * PITCH] = v[p].z;
+      d[3 * PITCH] = v[p].w;
+    }
   }
 
   float w[NR];
@@ -176,9 +213,6 @@ sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, 
     const int col = 4 * r + q;
     w[r] = (live && col < width) ? Wp[row * in + c0 + col] : 0.0f;
   }
-  uint32_t cpk[NR / 4 > 0 ? NR / 4 : 1];
-#pragma unroll
-  for (int r = 0; r < (NR / 4 > 0 ? NR / 4 : 1); ++r) cpk[r] = 0;
 
   const float maxq = (float)((1 << bits) - 1);
   float s = 1.0f, z = 0.0f;
@@ -190,20 +224,16 @@ sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, 
   }
   __syncthreads();
 
-#pragma unroll
-  for (int j = 0; j < B; ++j) {
-    if (j >= width) break;
-    const int R = j / 4, o = j % 4;
+  const int nquads = width / 4;
+  for (int R = 0; R < nquads; ++R) {
     if constexpr (GS > 0) {
-      if (j % GS == 0) {
+      if ((4 * R) % GS == 0) {
         // range of the group's current values, 0 included
         float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          if (r >= j / 4 && r < (j + GS) / 4) {
-            lo = fminf(lo, w[r]);
-            hi = fmaxf(hi, w[r]);
-          }
+        for (int t = 0; t < GS / 4; ++t) {
+          lo = fminf(lo, w[t]);
+          hi = fmaxf(hi, w[t]);
         }
         lo = fminf(lo, dpp_xor1(lo));
         hi = fmaxf(hi, dpp_xor1(hi));
@@ -211,39 +241,52 @@ sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, 
         hi = fmaxf(hi, dpp_xor2(hi));
         grid_params(lo, hi, bits, sym, s, z);
         if (live && q == 0) {
-          const int64_t g = (c0 + j) / GS;
+          const int64_t g = (c0 + 4 * R) / GS;
           scales[g * out + row] = s;
           zeros[g * out + row] = (int32_t)z;
         }
       }
     }
-    const float wj = dpp_bcast(w[R], o);
-    const float qf = fminf(fmaxf(rintf(wj / s) + z, 0.0f), maxq);
-    const float err = wj - s * (qf - z);
-    if (q == o) {
-      w[R] = err;
-      cpk[R / 4] |= (uint32_t)qf << (8 * (R % 4));
-    }
-    const float* urow = Ul + j * 4 * PITCH + q * PITCH;
 #pragma unroll
-    for (int r4 = (R / 4) * 4; r4 < NR; r4 += 4) {
-      const float4 u = *reinterpret_cast<const float4*>(urow + r4);
-      w[r4 + 0] = fmaf(-err, u.x, w[r4 + 0]);
-      if (r4 + 1 < NR) w[r4 + 1] = fmaf(-err, u.y, w[r4 + 1]);
-      if (r4 + 2 < NR) w[r4 + 2] = fmaf(-err, u.z, w[r4 + 2]);
-      if (r4 + 3 < NR) w[r4 + 3] = fmaf(-err, u.w, w[r4 + 3]);
-    }
-  }
-
-  if (live) {
+    for (int o = 0; o < 4; ++o) {
+      const int j = 4 * R + o;
+      const float wj = dpp_bcast(w[0], o);
+      const float qf = fminf(fmaxf(rintf(wj / s) + z, 0.0f), maxq);
+      const float err = wj - s * (qf - z);
+      if (q == o) {
+        Es[rl * EP + j] = err;
+        Cs[rl * B + j] = (uint8_t)qf;
+      }
+      const float* urow = Ul + j * 4 * PITCH + q * PITCH;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int col = 4 * r + q;
-      if (col < width) {
-        Wp[row * in + c0 + col] = w[r];  // the column's error, read by the trailing GEMMs
-        codes[row * in + c0 + col] = (uint8_t)((cpk[r / 4] >> (8 * (r % 4))) & 0xFF);
+      for (int t = 0; t < NR; t += 4) {
+        const float4 u = *reinterpret_cast<const float4*>(urow + t);
+        w[t + 0] = fmaf(-err, u.x, w[t + 0]);
+        if (t + 1 < NR) w[t + 1] = fmaf(-err, u.y, w[t + 1]);
+        if (t + 2 < NR) w[t + 2] = fmaf(-err, u.z, w[t + 2]);
+        if (t + 3 < NR) w[t + 3] = fmaf(-err, u.w, w[t + 3]);
       }
     }
+#pragma unroll
+    for (int t = 0; t + 1 < NR; ++t) w[t] = w[t + 1];
+    w[NR - 1] = 0.0f;
+  }
+  __syncthreads();
+
+  // Errors (read by the trailing GEMMs) and codes, written out row-contiguous.
+  const int wq = width / 4;
+  for (int e = tid; e < SW_ROWS * wq; e += SW_THREADS) {
+    const int r = e / wq, c = (e % wq) * 4;
+    if (row0 + r < out)
+      *reinterpret_cast<float4*>(Wp + (row0 + r) * in + c0 + c) =
+          *reinterpret_cast<const float4*>(Es + r * EP + c);
+  }
+  const int w16 = width / 16;
+  for (int e = tid; e < SW_ROWS * w16; e += SW_THREADS) {
+    const int r = e / w16, c = (e % w16) * 16;
+    if (row0 + r < out)
+      *reinterpret_cast<uint4*>(codes + (row0 + r) * in + c0 + c) =
+          *reinterpret_cast<const uint4*>(Cs + r * B + c);
   }
 }
 
@@ -276,11 +319,16 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
                         uint8_t* codes, hipStream_t s) {
   if (gs > B) return hipErrorInvalidValue;
   dim3 grid((unsigned)((out + SW_ROWS - 1) / SW_ROWS)), block(SW_THREADS);
-#define GPTQ_SWEEP_CASE(G)                                                                    \
-  case G:                                                                                     \
-    hipLaunchKernelGGL((sweep_kernel<B, (G > 0 ? G : 0)>), grid, block, 0, s, Wp, Up, out, in, \
-                       c0, width, bits, sym, scales, zeros, codes);                           \
-    break;
+  const size_t lds = SweepSmem<B>::BYTES;
+#define GPTQ_SWEEP_CASE(G)                                                                     \
+  case G: {                                                                                    \
+    auto k = sweep_kernel<B, (G > 0 ? G : 0)>;                                                 \
+    GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,                                           \
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));   \
+    hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,  \
+                       zeros, codes);                                                          \
+    break;                                                                                     \
+  }
   switch (gs > 0 ? gs : 0) {
     GPTQ_SWEEP_CASE(0)
     GPTQ_SWEEP_CASE(4)
@@ -289,14 +337,20 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
     GPTQ_SWEEP_CASE(32)
     case 64:
       if constexpr (B >= 64) {
-        hipLaunchKernelGGL((sweep_kernel<B, (B >= 64 ? 64 : 4)>), grid, block, 0, s, Wp, Up, out,
-                           in, c0, width, bits, sym, scales, zeros, codes);
+        auto k = sweep_kernel<B, (B >= 64 ? 64 : 4)>;
+        GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+        hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,
+                           zeros, codes);
       }
       break;
     case 128:
       if constexpr (B >= 128) {
-        hipLaunchKernelGGL((sweep_kernel<B, (B >= 128 ? 128 : 4)>), grid, block, 0, s, Wp, Up,
-                           out, in, c0, width, bits, sym, scales, zeros, codes);
+        auto k = sweep_kernel<B, (B >= 128 ? 128 : 4)>;
+        GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+        hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,
+                           zeros, codes);
       }
       break;
     default:

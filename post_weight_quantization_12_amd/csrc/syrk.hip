@@ -27,6 +27,7 @@ struct SyrkCfg {
   static constexpr int WN = (NT / 64) / WM;
   static constexpr int FM = T / WM / 32;  // 32x32 fragments per wave along M
   static constexpr int FN = T / WN / 32;
+  static constexpr size_t LDS = (size_t)4 * T * LDSK * sizeof(uint16_t);  // 2 stages x (A, B)
 };
 
 __device__ inline uint32_t lo16pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
@@ -83,7 +84,10 @@ syrk_upper_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__
   const int tid = threadIdx.x;
   const int which = tid / T;          // 0: A panel (features i0..), 1: B panel (features j0..)
   const int local = tid % T;
-  const int fb = local % (T / 8), tb = local / (T / 8);
+  // Lanes take consecutive token blocks first: a 16-lane pass of the 16-byte
+  // LDS stores then covers tb = 0..7 (16-byte steps) times two feature blocks
+  // (144*8 B apart = 128 B mod 256), i.e. 16 distinct bank groups.
+  const int tb = local % (BK / 8), fb = local / (BK / 8);
   const int64_t col = (which ? j0 : i0) + fb * 8;
   uint16_t* sdst = which ? sB : sA;
 
@@ -182,7 +186,7 @@ hipError_t launch_t(float* H, int64_t n, const uint16_t* X, int64_t ntok, int64_
                     hipStream_t s) {
   const int nt = (int)((n + T - 1) / T);
   const int64_t tiles = (int64_t)nt * (nt + 1) / 2;
-  const size_t lds = (size_t)4 * T * LDSK * sizeof(uint16_t);
+  const size_t lds = SyrkCfg<T>::LDS;
   auto kern = syrk_upper_kernel<T, BF16, VEC>;
   GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)kern,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
@@ -198,7 +202,8 @@ hipError_t launch_syrk(float* H, int64_t n, const void* X, int dtype, int64_t nt
   const uint16_t* x = static_cast<const uint16_t*>(X);
   const bool vec = (n % 8 == 0) && (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
   const bool bf = dtype == 1;
-  constexpr int T = 128;
+  // 256 x 256 tiles (8 waves) halve the operand traffic per flop against 128 x 128.
+  constexpr int T = 256;
   if (bf) {
     return vec ? launch_t<T, true, true>(H, n, x, ntok, ldx, s)
                : launch_t<T, true, false>(H, n, x, ntok, ldx, s);
