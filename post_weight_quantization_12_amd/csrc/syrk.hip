@@ -181,6 +181,190 @@ syrk_upper_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Main path: direct-to-LDS loads + transposing LDS reads (gfx950).
+//
+// X panels stay in their natural token-major layout.  Each 16-byte chunk (8
+// features of one token) is copied straight from HBM into LDS by
+// buffer_load ... lds (no VGPR staging), 4 stages deep, so ~3 stages of loads
+// are in flight while one is consumed.  A stage holds 32 tokens x 256 features
+// of each operand panel; chunk (t, c) is stored at physical slot
+// t*32 + (c ^ 4*(t%4)) so that the transposing reads below hit 16 distinct
+// bank groups per 32-lane pass.
+//
+// MFMA operands come from ds_read_b64_tr_b16: within a 16-lane group, lane j
+// receives element j%4 of the 8-byte reads issued by lanes j/4 + 4i (i<4).
+// Lane L pointing at (token t0 + L/4, features f0 + 4*(L%4)) therefore gets
+// feature f0 + L at tokens t0..t0+3 -- one k-slot quarter of an A/B fragment.
+// Out-of-range tokens read as 0 through the buffer descriptor's size check.
+// 4 waves, each a 128 x 128 block of the 256 x 256 tile (16 accumulators).
+constexpr int DT = 256, DBK = 32, DS = 4, DNT = 256;
+constexpr int PANEL_BYTES = DBK * DT * 2;       // 16 KiB
+constexpr int STAGE_BYTES = 2 * PANEL_BYTES;    // A + B
+constexpr int DMA_PER_WAVE = 8;                 // 2 panels x 1024 chunks / 64 / 4 waves
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// s_waitcnt with vmcnt <= N and the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ inline v4i16_t ds_read_tr16(const char* lds_byte_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (v4i16_t __attribute__((address_space(3)))*)(
+          (__attribute__((address_space(3))) char*)(lds_byte_ptr)));
+}
+
+template <bool BF16>
+__device__ inline f32x16_t mfma_tr(v4i16_t lo, v4i16_t hi, v4i16_t blo, v4i16_t bhi, f32x16_t c) {
+  typedef short v8i16_t __attribute__((ext_vector_type(8)));
+  v8i16_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  v8i16_t b = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(DNT)
+syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X, int64_t ntok,
+                int64_t ldx) {
+  // One LDS object per stage: the compiler then tracks each stage's direct
+  // loads separately and only waits for the stage being read.
+  __shared__ __align__(16) char st0[STAGE_BYTES];
+  __shared__ __align__(16) char st1[STAGE_BYTES];
+  __shared__ __align__(16) char st2[STAGE_BYTES];
+  __shared__ __align__(16) char st3[STAGE_BYTES];
+  static_assert(DS == 4, "four stage buffers");
+
+  const int b = blockIdx.x;
+  int tj = (int)((sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
+  while ((tj + 1) * (tj + 2) / 2 <= b) ++tj;
+  while (tj * (tj + 1) / 2 > b) --tj;
+  const int ti = b - tj * (tj + 1) / 2;
+  const int64_t i0 = (int64_t)ti * DT, j0 = (int64_t)tj * DT;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // DMA: instruction q of this wave copies physical chunks [cb*64, cb*64+64) of panel q/4.
+  uint32_t voff[DMA_PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < DMA_PER_WAVE; ++q) {
+    const int panel = q / 4, cb = wave * 4 + (q % 4);
+    const int p = cb * 64 + lane;
+    const int t = p / 32, c = (p % 32) ^ (4 * (t % 4));
+    const int64_t col = (panel ? j0 : i0) + 8 * c;
+    voff[q] = (uint32_t)((t * ldx + col) * 2);
+  }
+  const int nk = (int)((ntok + DBK - 1) / DBK);
+  auto issue = [&](int st, char* stage) {
+    const int64_t k0 = (int64_t)st * DBK;
+    const uint16_t* base = X + k0 * ldx;
+    const int64_t rem = (ntok - k0) * ldx * 2;
+    const uint32_t num = rem <= 0 ? 0u : rem > 0xFFFFFFFFLL ? 0xFFFFFFFFu : (uint32_t)rem;
+    const uint16_t* rbase = rem <= 0 ? X : base;  // nothing is read past the end
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)rbase, (short)0, (int)num, 0x00020000);
+#pragma unroll
+    for (int q = 0; q < DMA_PER_WAVE; ++q) {
+      const int panel = q / 4, cb = wave * 4 + (q % 4);
+      char* dst = stage + panel * PANEL_BYTES + cb * 64 * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) char*)dst),
+          16, voff[q], 0, 0, 0);
+    }
+  };
+
+  // Transposing-read byte offsets within a panel, per lane (substep 0, first 4 tokens).
+  const int g = lane >> 4, L = lane & 15;
+  const int trow = 8 * (g >> 1) + (L >> 2);               // token row within the substep
+  const int cx = 2 * (g & 1) + ((L & 3) >> 1);            // chunk within a 32-feature fragment
+  const int half8 = (L & 1) * 8;
+  const int xsw = 4 * (L >> 2);                           // = 4 * (trow % 4)
+  int aoff[4], boff[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    aoff[f] = (trow * 32 + ((wm * 16 + f * 4 + cx) ^ xsw)) * 16 + half8;
+    boff[f] = PANEL_BYTES + (trow * 32 + ((wn * 16 + f * 4 + cx) ^ xsw)) * 16 + half8;
+  }
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+
+  auto compute = [&](const char* stage) {
+#pragma unroll
+    for (int s = 0; s < DBK / 16; ++s) {
+      const int so = s * 16 * 32 * 16;  // 16 token rows
+      v4i16_t alo[4], ahi[4], blo[4], bhi[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        alo[f] = ds_read_tr16(stage + so + aoff[f]);
+        ahi[f] = ds_read_tr16(stage + so + aoff[f] + 4 * 32 * 16);
+        blo[f] = ds_read_tr16(stage + so + boff[f]);
+        bhi[f] = ds_read_tr16(stage + so + boff[f] + 4 * 32 * 16);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[a][c] = mfma_tr<BF16>(alo[a], ahi[a], blo[c], bhi[c], acc[a][c]);
+    }
+  };
+  // One pipeline step: stage k (in `cur`) has landed for this wave once at
+  // most the two later stages' loads are outstanding; the barrier makes every
+  // wave's part visible and frees `nxt` (read in the previous step).  Stages
+  // past the end are loaded too, through a zero-size descriptor (they read as
+  // zeros and add nothing), so the loop has no data-dependent branches and the
+  // compiler can track each stage buffer's loads exactly.
+  auto step = [&](int k, const char* cur, char* nxt) {
+    wait_vmcnt<(DS - 2) * DMA_PER_WAVE>();
+    __builtin_amdgcn_s_barrier();
+    issue(k + DS - 1, nxt);
+    compute(cur);
+  };
+
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+  for (int kt = 0; kt < nk; kt += 4) {
+    step(kt + 0, st0, st3);
+    step(kt + 1, st1, st0);
+    step(kt + 2, st2, st1);
+    step(kt + 3, st3, st2);
+  }
+  wait_vmcnt<0>();
+
+  // Epilogue, one 32x32 block at a time (keeps the H loads from piling up in VGPRs).
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t j = j0 + wn * 128 + c * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t i = i0 + wm * 128 + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        if (i < n && j < n && i <= j) {
+          float* p = H + i * n + j;
+          *p = *p + 2.0f * acc[a][c][v];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int T, bool BF16, bool VEC>
 hipError_t launch_t(float* H, int64_t n, const uint16_t* X, int64_t ntok, int64_t ldx,
                     hipStream_t s) {
@@ -200,16 +384,20 @@ hipError_t launch_t(float* H, int64_t n, const uint16_t* X, int64_t ntok, int64_
 hipError_t launch_syrk(float* H, int64_t n, const void* X, int dtype, int64_t ntok,
                        int64_t ldx, hipStream_t s) {
   const uint16_t* x = static_cast<const uint16_t*>(X);
-  const bool vec = (n % 8 == 0) && (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+  const bool aligned = (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
   const bool bf = dtype == 1;
-  // 256 x 256 tiles (8 waves) halve the operand traffic per flop against 128 x 128.
-  constexpr int T = 256;
-  if (bf) {
-    return vec ? launch_t<T, true, true>(H, n, x, ntok, ldx, s)
-               : launch_t<T, true, false>(H, n, x, ntok, ldx, s);
+  if (aligned) {
+    // direct-to-LDS pipeline (16-byte chunks need 16-byte aligned rows)
+    const int nt = (int)((n + DT - 1) / DT);
+    const int64_t tiles = (int64_t)nt * (nt + 1) / 2;
+    auto kern = bf ? syrk_dma_kernel<true> : syrk_dma_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(DNT), 0, s, H, n, x, ntok, ldx);
+    return hipGetLastError();
   }
-  return vec ? launch_t<T, false, true>(H, n, x, ntok, ldx, s)
-             : launch_t<T, false, false>(H, n, x, ntok, ldx, s);
+  // Unaligned rows: register-staged kernel with element loads.
+  constexpr int T = 256;
+  return bf ? launch_t<T, true, false>(H, n, x, ntok, ldx, s)
+            : launch_t<T, false, false>(H, n, x, ntok, ldx, s);
 }
 
 }  // namespace gptq
