@@ -231,6 +231,41 @@ __device__ inline f32x16_t mfma_tr(v4i16_t lo, v4i16_t hi, v4i16_t blo, v4i16_t 
                                                   __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
 }
 
+// Tile order for the upper triangle (ti <= tj), L2-aware.  Workgroups are
+// dispatched to the 8 XCDs round-robin (block b -> XCD b % 8) and each XCD has
+// its own L2, so block b takes logical tile (b % 8) * per_xcd + b / 8: every
+// XCD walks its own contiguous run of the logical order.  The logical order
+// visits row groups of G tile rows; inside a group it goes column by column,
+// so the ~32 tiles one XCD runs at a time share G row panels and a few
+// column panels, and those panels are read from HBM once per XCD.
+constexpr int TILE_GROUP = 8;
+__device__ inline bool syrk_tile(int b, int nt, int& ti, int& tj) {
+  const int64_t total = (int64_t)nt * (nt + 1) / 2;
+  const int64_t per_xcd = (total + 7) / 8;
+  int64_t o = (int64_t)(b % 8) * per_xcd + b / 8;
+  if (o >= total) return false;
+  for (int g0 = 0; g0 < nt; g0 += TILE_GROUP) {
+    const int gsz = nt - g0 < TILE_GROUP ? nt - g0 : TILE_GROUP;
+    const int64_t tri = (int64_t)gsz * (gsz + 1) / 2;
+    const int64_t cnt = tri + (int64_t)gsz * (nt - g0 - gsz);
+    if (o < cnt) {
+      if (o < tri) {  // triangle: column g0 + d holds d + 1 tiles
+        int d = 0;
+        while ((int64_t)(d + 1) * (d + 2) / 2 <= o) ++d;
+        tj = g0 + d;
+        ti = g0 + (int)(o - (int64_t)d * (d + 1) / 2);
+      } else {
+        const int64_t r = o - tri;
+        tj = g0 + gsz + (int)(r / gsz);
+        ti = g0 + (int)(r % gsz);
+      }
+      return true;
+    }
+    o -= cnt;
+  }
+  return false;
+}
+
 template <bool BF16>
 __global__ void __launch_bounds__(DNT)
 syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X, int64_t ntok,
@@ -243,11 +278,8 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   __shared__ __align__(16) char st3[STAGE_BYTES];
   static_assert(DS == 4, "four stage buffers");
 
-  const int b = blockIdx.x;
-  int tj = (int)((sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
-  while ((tj + 1) * (tj + 2) / 2 <= b) ++tj;
-  while (tj * (tj + 1) / 2 > b) --tj;
-  const int ti = b - tj * (tj + 1) / 2;
+  int ti, tj;
+  if (!syrk_tile(blockIdx.x, (int)((n + DT - 1) / DT), ti, tj)) return;
   const int64_t i0 = (int64_t)ti * DT, j0 = (int64_t)tj * DT;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -304,48 +336,69 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
 
-  auto compute = [&](const char* stage) {
+  // Operands of one 16-token substep: 4 A and 4 B fragments, two 4-token
+  // halves each.
+  struct Frags {
+    v4i16_t alo[4], ahi[4], blo[4], bhi[4];
+  };
+  auto load = [&](Frags& F, const char* stage, int sub) {
+    const int so = sub * 16 * 32 * 16;  // 16 token rows
 #pragma unroll
-    for (int s = 0; s < DBK / 16; ++s) {
-      const int so = s * 16 * 32 * 16;  // 16 token rows
-      v4i16_t alo[4], ahi[4], blo[4], bhi[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        alo[f] = ds_read_tr16(stage + so + aoff[f]);
-        ahi[f] = ds_read_tr16(stage + so + aoff[f] + 4 * 32 * 16);
-        blo[f] = ds_read_tr16(stage + so + boff[f]);
-        bhi[f] = ds_read_tr16(stage + so + boff[f] + 4 * 32 * 16);
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[a][c] = mfma_tr<BF16>(alo[a], ahi[a], blo[c], bhi[c], acc[a][c]);
+    for (int f = 0; f < 4; ++f) {
+      F.alo[f] = ds_read_tr16(stage + so + aoff[f]);
+      F.ahi[f] = ds_read_tr16(stage + so + aoff[f] + 4 * 32 * 16);
+      F.blo[f] = ds_read_tr16(stage + so + boff[f]);
+      F.bhi[f] = ds_read_tr16(stage + so + boff[f] + 4 * 32 * 16);
     }
   };
-  // One pipeline step: stage k (in `cur`) has landed for this wave once at
-  // most the two later stages' loads are outstanding; the barrier makes every
-  // wave's part visible and frees `nxt` (read in the previous step).  Stages
-  // past the end are loaded too, through a zero-size descriptor (they read as
-  // zeros and add nothing), so the loop has no data-dependent branches and the
-  // compiler can track each stage buffer's loads exactly.
-  auto step = [&](int k, const char* cur, char* nxt) {
+  auto mma = [&](const Frags& F) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[a][c] = mfma_tr<BF16>(F.alo[a], F.ahi[a], F.blo[c], F.bhi[c], acc[a][c]);
+  };
+
+  // Software pipeline.  Per stage k (buffer `cur`, next stage in `nxt`):
+  //   read substep 1 of k | MFMAs of substep 0 of k
+  //   wait: own LDS reads done, own loads of stage k+1 landed (two later stages
+  //   may still be in flight); barrier: everyone's stage k+1 is visible and
+  //   nobody reads stage k any more -> refill `cur` with stage k+4
+  //   read substep 0 of k+1 | MFMAs of substep 1 of k
+  // Stages past the end are loaded through a zero-size descriptor (they read
+  // as zeros and add nothing), so the loop has no data-dependent branches and
+  // the compiler tracks each stage buffer's loads exactly.
+  Frags F0, F1;
+  auto stage_step = [&](int k, char* cur, const char* nxt) {
+    load(F1, cur, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(F0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x3 << 14) | 0xF);  // lgkmcnt(0), vmcnt untouched
     wait_vmcnt<(DS - 2) * DMA_PER_WAVE>();
     __builtin_amdgcn_s_barrier();
-    issue(k + DS - 1, nxt);
-    compute(cur);
+    issue(k + DS, cur);
+    load(F0, nxt, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(F1);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   issue(0, st0);
   issue(1, st1);
   issue(2, st2);
+  issue(3, st3);
+  wait_vmcnt<(DS - 1) * DMA_PER_WAVE>();
+  __builtin_amdgcn_s_barrier();
+  load(F0, st0, 0);
   for (int kt = 0; kt < nk; kt += 4) {
-    step(kt + 0, st0, st3);
-    step(kt + 1, st1, st0);
-    step(kt + 2, st2, st1);
-    step(kt + 3, st3, st2);
+    stage_step(kt + 0, st0, st1);
+    stage_step(kt + 1, st1, st2);
+    stage_step(kt + 2, st2, st3);
+    stage_step(kt + 3, st3, st0);
   }
   wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x3 << 14) | 0xF);
 
   // Epilogue, one 32x32 block at a time (keeps the H loads from piling up in VGPRs).
 #pragma unroll
@@ -390,8 +443,9 @@ hipError_t launch_syrk(float* H, int64_t n, const void* X, int dtype, int64_t nt
     // direct-to-LDS pipeline (16-byte chunks need 16-byte aligned rows)
     const int nt = (int)((n + DT - 1) / DT);
     const int64_t tiles = (int64_t)nt * (nt + 1) / 2;
+    const int64_t blocks = (tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
     auto kern = bf ? syrk_dma_kernel<true> : syrk_dma_kernel<false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(DNT), 0, s, H, n, x, ntok, ldx);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(DNT), 0, s, H, n, x, ntok, ldx);
     return hipGetLastError();
   }
   // Unaligned rows: register-staged kernel with element loads.
