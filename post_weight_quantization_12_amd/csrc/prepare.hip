@@ -135,82 +135,202 @@ gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict_
 }
 
 // Leaf of the recursion: factor the m x m (m <= 64) diagonal block at `off`
-// (lower part of A, leading dimension n) and invert the factor, in one wave.
-//
-// Lane i keeps the not-yet-factored part of row i in a sliding register
-// window: at step k, a[t] holds column k + t, so the column being eliminated
-// is always a[0] and every register index is a compile-time constant while
-// the loop over k stays rolled (small code).  The scaled column k is shared
-// through LDS.  The inverse Y = L^-1 is built the same way with the rows of Y
-// broadcast through LDS.  Writes L into A and L^-1 into X (lower parts).
-__global__ void __launch_bounds__(64)
+// (lower part of A, leading dimension n) and invert the factor, in one
+// workgroup of 4 waves, blocked by 16 columns:
+//   for each 16-column panel: the 16 x 16 diagonal block is factored (and
+//   inverted) by 16 lanes of wave 0 in registers, broadcasting through
+//   readlane; the rows below are solved against it and the trailing block
+//   updated by all 256 threads out of LDS.
+//   then the off-diagonal blocks of L^-1, block row by block row:
+//   X[p][q] = -Dinv_p * sum_{q <= r < p} L[p][r] X[r][q].
+// Rows >= m are padded with the identity (so every pivot is defined) and are
+// not written back.  Writes L into A and L^-1 into X (lower parts).
+constexpr int LP = NB + 4;  // padded LDS row (16-byte aligned rows, 272 B apart)
+
+__device__ inline float bcast(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ inline float dot16(const float* a, const float* b) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; k += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(a + k);
+    const float4 y = *reinterpret_cast<const float4*>(b + k);
+    acc = fmaf(x.x, y.x, acc);
+    acc = fmaf(x.y, y.y, acc);
+    acc = fmaf(x.z, y.z, acc);
+    acc = fmaf(x.w, y.w, acc);
+  }
+  return acc;
+}
+
+__global__ void __launch_bounds__(256)
 cholinv_leaf_kernel(float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t off, int m,
                     int32_t* __restrict__ info) {
-  __shared__ __align__(16) float col[2 * NB];   // column k of L, zero-padded
-  __shared__ __align__(16) float Ls[NB][NB + 1];  // the factor L (row i, column k)
-  __shared__ __align__(16) float yrow[NB];
-  const int lane = threadIdx.x;
-  const bool row_ok = lane < m;
-  const float* arow = A + (off + lane) * n + off;
-  float a[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) a[j] = (row_ok && j <= lane && j < m) ? arow[j] : 0.0f;
-  col[NB + lane] = 0.0f;
+  __shared__ __align__(16) float Ls[NB * LP];
+  __shared__ __align__(16) float Xs[NB * LP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  for (int k = 0; k < m; ++k) {
-    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[0]), k));
-    if (lane == 0 && (!(d > 0.0f) || !(d < INFINITY)))
-      atomicCAS(info, 0, (int32_t)(n - (off + k)));  // quantization-order column n-1-(off+k)
-    const float piv = sqrtf(d);
-    const float lik = lane > k ? a[0] / piv : (lane == k ? piv : 0.0f);
-    Ls[lane][k] = lik;
-    col[lane] = lane > k ? lik : 0.0f;
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    // a[t] (column k+1+t after the shift) -= L[i][k] * L[k+1+t][k]
-    const float g = lane > k ? lik : 0.0f;
+  {
+    // All 16 loads per thread are issued before any is used (addresses of
+    // masked-out elements are clamped to the block's first element).
+    float v[NB * NB / 256];
 #pragma unroll
-    for (int t = 0; t < NB - 1; ++t) a[t] = fmaf(-g, col[k + 1 + t], a[t + 1]);
-    a[NB - 1] = 0.0f;
-    __builtin_amdgcn_wave_barrier();
+    for (int q = 0; q < NB * NB / 256; ++q) {
+      const int e = tid + 256 * q, i = e / NB, j = e % NB;
+      const bool ok = i < m && j <= i;
+      const float* src = A + (ok ? (off + i) * n + off + j : off * n + off);
+      v[q] = *src;
+    }
+#pragma unroll
+    for (int q = 0; q < NB * NB / 256; ++q) {
+      const int e = tid + 256 * q, i = e / NB, j = e % NB;
+      const bool ok = i < m && j <= i;
+      Ls[i * LP + j] = ok ? v[q] : (i == j ? 1.0f : 0.0f);
+      Xs[i * LP + j] = 0.0f;
+    }
   }
+  __syncthreads();
 
-  // Y = L^-1: row k of Y is final once divided by L[k][k]; rows i > k then
-  // subtract L[i][k] * Y[k][:].  y[c] holds column c (no shifting needed).
-  float y[NB];
 #pragma unroll
-  for (int c = 0; c < NB; ++c) y[c] = (c == lane) ? 1.0f : 0.0f;
-  for (int k = 0; k < m; ++k) {
-    if (lane == k) {
-      const float rpiv = 1.0f / Ls[k][k];
+  for (int c = 0; c < NB; c += 16) {
+    // (1) 16 x 16 diagonal block: Cholesky and inverse in wave 0's registers
+    // (reciprocal square root per pivot; no divisions).
+    if (wave == 0) {
+      const int li = lane & 15;
+      float d[16], rinv[16];
 #pragma unroll
-      for (int c = 0; c < NB; ++c) y[c] = y[c] * rpiv;
+      for (int j = 0; j < 16; ++j) d[j] = (j <= li) ? Ls[(c + li) * LP + c + j] : 0.0f;
 #pragma unroll
-      for (int c4 = 0; c4 < NB; c4 += 4)
-        *reinterpret_cast<float4*>(yrow + c4) = make_float4(y[c4], y[c4 + 1], y[c4 + 2], y[c4 + 3]);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    const float g = lane > k ? Ls[lane][k] : 0.0f;
+      for (int k = 0; k < 16; ++k) {
+        const float dk = bcast(d[k], k);
+        if (lane == 0 && (!(dk > 0.0f) || !(dk < INFINITY)) && c + k < m)
+          atomicCAS(info, 0, (int32_t)(n - (off + c + k)));  // quantization-order column
+        const float r = __builtin_amdgcn_rsqf(dk);
+        rinv[k] = r;                                   // 1 / L[k][k]
+        const float lik = li > k ? d[k] * r : (li == k ? dk * r : 0.0f);
+        d[k] = lik;
+        const float g = li > k ? lik : 0.0f;
 #pragma unroll
-    for (int c4 = 0; c4 < NB; c4 += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(yrow + c4);
-      y[c4 + 0] = fmaf(-g, v.x, y[c4 + 0]);
-      y[c4 + 1] = fmaf(-g, v.y, y[c4 + 1]);
-      y[c4 + 2] = fmaf(-g, v.z, y[c4 + 2]);
-      y[c4 + 3] = fmaf(-g, v.w, y[c4 + 3]);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-  if (row_ok) {
-    float* lrow = A + (off + lane) * n + off;
-    float* xrow = X + (off + lane) * n + off;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (j <= lane && j < m) {
-        lrow[j] = Ls[lane][j];
-        xrow[j] = y[j];
+        for (int j = k + 1; j < 16; ++j) d[j] = fmaf(-g, bcast(lik, j), d[j]);
       }
+      // Y = L_D^-1, rows of Y broadcast with readlane (right-looking).
+      float y[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) y[j] = (j == li) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (li == k) {
+#pragma unroll
+          for (int j = 0; j <= k; ++j) y[j] *= rinv[k];
+        }
+        const float g = li > k ? d[k] : 0.0f;
+#pragma unroll
+        for (int j = 0; j <= k; ++j) y[j] = fmaf(-g, bcast(y[j], k), y[j]);
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          Ls[(c + li) * LP + c + j] = j <= li ? d[j] : 0.0f;
+          Xs[(c + li) * LP + c + j] = j <= li ? y[j] : 0.0f;
+        }
+      }
+    }
+    __syncthreads();
+    const int rows = NB - c - 16;
+    if (rows > 0) {
+      // (2) panel solve: L[r][c+j] = sum_k A[r][c+k] * Dinv[j][k] (Dinv upper part is 0).
+      float res[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const int e = tid + 256 * q;
+        res[q] = 0.0f;
+        if (e < rows * 16) {
+          const int r = c + 16 + e / 16, j = e % 16;
+          res[q] = dot16(Ls + r * LP + c, Xs + (c + j) * LP + c);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const int e = tid + 256 * q;
+        if (e < rows * 16) Ls[(c + 16 + e / 16) * LP + c + e % 16] = res[q];
+      }
+      __syncthreads();
+      // (3) trailing update of the lower part: A[r][s] -= sum_k L[r][c+k] L[s][c+k].
+#pragma unroll
+      for (int q = 0; q < 9; ++q) {
+        const int e = tid + 256 * q;
+        if (e < rows * rows) {
+          const int r = c + 16 + e / rows, s2 = c + 16 + e % rows;
+          if (s2 <= r) Ls[r * LP + s2] -= dot16(Ls + r * LP + c, Ls + s2 * LP + c);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // Off-diagonal blocks of L^-1, one block row at a time:
+  //   T = L[r0.., 0..r0) X[0..r0, 0..r0)   (X lower: the sum can run over all k < r0)
+  //   X[r0.., 0..r0) = -Dinv_r0 T
+#pragma unroll
+  for (int pb = 1; pb < NB / 16; ++pb) {
+    const int r0 = 16 * pb, cols = r0;
+    float t[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int e = tid + 256 * q;
+      t[q] = 0.0f;
+      if (e < 16 * cols) {
+        const int i = e / cols, j = e % cols;
+        const float* lrow = Ls + (r0 + i) * LP;
+        float acc = 0.0f;
+#pragma unroll
+        for (int k4 = 0; k4 < r0; k4 += 4) {
+          const float4 l = *reinterpret_cast<const float4*>(lrow + k4);
+          acc = fmaf(l.x, Xs[(k4 + 0) * LP + j], acc);
+          acc = fmaf(l.y, Xs[(k4 + 1) * LP + j], acc);
+          acc = fmaf(l.z, Xs[(k4 + 2) * LP + j], acc);
+          acc = fmaf(l.w, Xs[(k4 + 3) * LP + j], acc);
+        }
+        t[q] = acc;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int e = tid + 256 * q;
+      if (e < 16 * cols) Xs[(r0 + e / cols) * LP + e % cols] = t[q];  // T, scaled below
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int e = tid + 256 * q;
+      t[q] = 0.0f;
+      if (e < 16 * cols) {
+        const int i = e / cols, j = e % cols;
+        const float* drow = Xs + (r0 + i) * LP + r0;  // Dinv row i (upper part 0)
+        float acc = 0.0f;
+#pragma unroll
+        for (int l = 0; l < 16; ++l) acc = fmaf(drow[l], Xs[(r0 + l) * LP + j], acc);
+        t[q] = -acc;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int e = tid + 256 * q;
+      if (e < 16 * cols) Xs[(r0 + e / cols) * LP + e % cols] = t[q];
+    }
+    __syncthreads();
+  }
+
+  for (int e = tid; e < m * m; e += 256) {
+    const int i = e / m, j = e % m;
+    if (j <= i) {
+      A[(off + i) * n + off + j] = Ls[i * LP + j];
+      X[(off + i) * n + off + j] = Xs[i * LP + j];
     }
   }
 }
@@ -265,7 +385,7 @@ hipError_t gemm(PrepCtx& c, int64_t M, int64_t N, int64_t K, const float* Am, in
 hipError_t cholinv(PrepCtx& c, int64_t off, int64_t m) {
   const int64_t n = c.n;
   if (m <= NB) {
-    hipLaunchKernelGGL(cholinv_leaf_kernel, dim3(1), dim3(64), 0, c.s, c.A, c.X, n, off, (int)m,
+    hipLaunchKernelGGL(cholinv_leaf_kernel, dim3(1), dim3(256), 0, c.s, c.A, c.X, n, off, (int)m,
                        c.info);
     return hipGetLastError();
   }
