@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--config", default="c1", choices=["c1", "c2", "c3", "c4a", "c4b"])
     ap.add_argument("--chunk-samples", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (a reference kernel "
+                         "of known traffic for calibrating rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -159,7 +162,6 @@ def main():
         return e
 
     def step(record):
-        marks = {}
         e0 = ev()
         H.zero_()
         syrk_ev = []
@@ -176,10 +178,16 @@ def main():
         if record is not None:
             record.append((e0, e1, e2, e3, syrk_ev))
 
+    if args.copy_probe:
+        src = torch.empty((1 << 30) // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
-    assert int(info.item()) == 0, "factorization failed"
 
     recs = []
     torch.cuda.synchronize()
@@ -188,6 +196,7 @@ def main():
         step(recs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    assert int(info.item()) == 0, "factorization failed"
 
     ms_step = wall * 1e3 / args.steps
     hess_ms = [r[0].elapsed_time(r[1]) for r in recs]
