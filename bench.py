@@ -239,7 +239,7 @@ def main():
                      "quantize": mean(quant_ms)},
         "layer_weights_per_s": weights / (layer_ms * 1e-3),
         "roofline": {
-            "kernel": "syrk_upper_kernel (gptq_hessian_accumulate)",
+            "kernel": "syrk_dma_kernel (gptq_hessian_accumulate)",
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_FP16_TFLOPS,
