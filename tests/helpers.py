@@ -38,19 +38,20 @@ def check_quantize_parity(W_t, U_t, perm_t, bits, gs, sym, qweight, scales, zero
     output rows (rows are independent, so a subset is an exact check of those
     rows).  Returns a dict of diagnostics; asserts the tolerances.
     """
-    W = W_t.detach().cpu().to(torch.float64).numpy()
+    out, inp = W_t.shape
+    if rows is None:
+        rows = np.arange(out)
+    rows = np.asarray(rows)
+    W = W_t.detach()[torch.from_numpy(rows)].cpu().to(torch.float64).numpy()
     U = U_t.detach().cpu().to(torch.float64).numpy()
-    inp = W.shape[1]
     perm = np.arange(inp) if perm_t is None else perm_t.cpu().numpy().astype(np.int64)
-    codes = gpu_codes(qweight, bits, inp)                   # [out x in], original order
+    qsel = qweight.detach()[:, torch.from_numpy(rows).to(qweight.device)]
+    codes = gpu_codes(qsel, bits, inp)                       # [rows x in], original order
     sc = scales.cpu().numpy()
     zr = zeros.cpu().numpy().astype(np.int64)
     gi = g_idx.cpu().numpy().astype(np.int64)
-    if rows is None:
-        rows = np.arange(W.shape[0])
-    rows = np.asarray(rows)
-    codes_perm = codes[rows][:, perm]
-    ref = O.gptq_sweep(W[rows], U, perm, bits, gs, sym,
+    codes_perm = codes[:, perm]
+    ref = O.gptq_sweep(W, U, perm, bits, gs, sym,
                        forced_codes=codes_perm, forced_zeros=zr[:, rows])
     assert np.array_equal(gi, O.g_index(perm, gs)), "g_idx differs"
     code_mm = [m for m in ref.mismatches if m[0] == "code"]
