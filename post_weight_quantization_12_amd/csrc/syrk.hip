@@ -186,8 +186,8 @@ syrk_upper_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__
 //
 // X panels stay in their natural token-major layout.  Each 16-byte chunk (8
 // features of one token) is copied straight from HBM into LDS by
-// buffer_load ... lds (no VGPR staging), 4 stages deep, so ~3 stages of loads
-// are in flight while one is consumed.  A stage holds 32 tokens x 256 features
+// buffer_load ... lds (no VGPR staging), 5 stages deep (the whole 160 KiB LDS),
+// so ~4 stages of loads are in flight while one is consumed.  A stage holds 32 tokens x 256 features
 // of each operand panel; chunk (t, c) is stored at physical slot
 // t*32 + (c ^ 4*(t%4)) so that the transposing reads below hit 16 distinct
 // bank groups per 32-lane pass.
@@ -198,7 +198,7 @@ syrk_upper_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__
 // feature f0 + L at tokens t0..t0+3 -- one k-slot quarter of an A/B fragment.
 // Out-of-range tokens read as 0 through the buffer descriptor's size check.
 // 4 waves, each a 128 x 128 block of the 256 x 256 tile (16 accumulators).
-constexpr int DT = 256, DBK = 32, DS = 4, DNT = 256;
+constexpr int DT = 256, DBK = 32, DS = 5, DNT = 256;
 constexpr int PANEL_BYTES = DBK * DT * 2;       // 16 KiB
 constexpr int STAGE_BYTES = 2 * PANEL_BYTES;    // A + B
 constexpr int DMA_PER_WAVE = 8;                 // 2 panels x 1024 chunks / 64 / 4 waves
@@ -276,7 +276,8 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   __shared__ __align__(16) char st1[STAGE_BYTES];
   __shared__ __align__(16) char st2[STAGE_BYTES];
   __shared__ __align__(16) char st3[STAGE_BYTES];
-  static_assert(DS == 4, "four stage buffers");
+  __shared__ __align__(16) char st4[STAGE_BYTES];
+  static_assert(DS == 5, "five stage buffers (160 KiB, the whole LDS)");
 
   int ti, tj;
   if (!syrk_tile(blockIdx.x, (int)((n + DT - 1) / DT), ti, tj)) return;
@@ -388,14 +389,16 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   issue(1, st1);
   issue(2, st2);
   issue(3, st3);
+  issue(4, st4);
   wait_vmcnt<(DS - 1) * DMA_PER_WAVE>();
   __builtin_amdgcn_s_barrier();
   load(F0, st0, 0);
-  for (int kt = 0; kt < nk; kt += 4) {
+  for (int kt = 0; kt < nk; kt += DS) {
     stage_step(kt + 0, st0, st1);
     stage_step(kt + 1, st1, st2);
     stage_step(kt + 2, st2, st3);
-    stage_step(kt + 3, st3, st0);
+    stage_step(kt + 3, st3, st4);
+    stage_step(kt + 4, st4, st0);
   }
   wait_vmcnt<0>();
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x3 << 14) | 0xF);
