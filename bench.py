@@ -144,6 +144,7 @@ def main():
     U = torch.empty((n, n), dtype=torch.float32, device=dev)
     perm = torch.empty((n,), dtype=torch.int32, device=dev)
     info = torch.empty((1,), dtype=torch.int32, device=dev)
+    wsh = torch.empty((P.hessian_workspace_bytes(n),), dtype=torch.uint8, device=dev)
     wsp = torch.empty((P.prepare_workspace_bytes(n),), dtype=torch.uint8, device=dev)
     g = P.n_groups(n, cfg.group_size)
     qweight = torch.empty((n * cfg.bits // 32, out), dtype=torch.int32, device=dev)
@@ -167,7 +168,7 @@ def main():
         syrk_ev = []
         for c in chunks:
             a = ev()
-            P.hessian_accumulate(H, c, stream)
+            P.hessian_accumulate(H, c, stream, wsh)
             syrk_ev.append((a, ev()))
         e1 = ev()
         P.prepare(H, cfg.damp, cfg.desc_act, U, perm, info, wsp, stream)

@@ -54,6 +54,11 @@ typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype_t;
  * the 160 KiB LDS of a gfx950 compute unit during the column gather). */
 #define GPTQ_MAX_PREPARE_N 32768
 
+/* Workspace (bytes) gptq_hessian_accumulate can use for order n on the
+ * current device (two 256 x 256 fp32 partial tiles per compute unit plus one
+ * counter per tile; 0 if n < 1). */
+size_t gptq_hessian_workspace_bytes(int64_t n);
+
 /*
  * Hessian accumulation:  H += 2 * X^T X   (upper triangle only).
  *
@@ -70,13 +75,20 @@ typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype_t;
  *   X      calibration activations, [ntok x n] (tokens x features), row-major
  *          with leading dimension ldx >= n, dtype GPTQ_F16 or GPTQ_BF16.
  *   ntok   tokens in this chunk; ntok == 0 is a no-op returning GPTQ_OK.
+ *   workspace  NULL, or device memory of at least
+ *          gptq_hessian_workspace_bytes(n).  With a workspace, a layer too
+ *          small to fill the GPU with whole 256 x 256 tiles is split over all
+ *          compute units along the tokens (partial tiles are combined in a
+ *          fixed order: results do not depend on timing).  Calls that share a
+ *          workspace must not overlap.
  *
  * Products of fp16/bf16 values are exact in fp32; accumulation is fp32.
  * Errors: INVALID_ARG (null pointers, n < 1, ntok < 0, ldx < n),
- *         UNSUPPORTED (x_dtype not F16/BF16), HIP.
+ *         UNSUPPORTED (x_dtype not F16/BF16), WORKSPACE, HIP.
  */
 int gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dtype,
-                            int64_t ntok, int64_t ldx, void* stream);
+                            int64_t ntok, int64_t ldx, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Workspace (bytes) gptq_prepare needs for order n (0 if n is out of range). */
 size_t gptq_prepare_workspace_bytes(int64_t n);

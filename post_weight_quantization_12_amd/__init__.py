@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     GPTQ_F16,
     GPTQ_F32,
     hessian_accumulate,
+    hessian_workspace_bytes,
     header_functions,
     load,
     n_groups,

@@ -48,7 +48,9 @@ def load():
             "`python -m post_weight_quantization_12_amd.build` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
-    lib.gptq_hessian_accumulate.argtypes = [vp, i64, vp, c_int, i64, i64, vp]
+    lib.gptq_hessian_workspace_bytes.argtypes = [i64]
+    lib.gptq_hessian_workspace_bytes.restype = ctypes.c_size_t
+    lib.gptq_hessian_accumulate.argtypes = [vp, i64, vp, c_int, i64, i64, vp, ctypes.c_size_t, vp]
     lib.gptq_hessian_accumulate.restype = c_int
     lib.gptq_prepare_workspace_bytes.argtypes = [i64]
     lib.gptq_prepare_workspace_bytes.restype = ctypes.c_size_t
@@ -108,8 +110,15 @@ def _need_cuda(name, t):
 
 
 # ---------------------------------------------------------------- calls --
-def hessian_accumulate(H, X, stream=None):
-    """H (fp32 [n x n], upper triangle) += 2 X^T X for X [ntok x n] fp16/bf16."""
+def hessian_workspace_bytes(n: int) -> int:
+    return int(load().gptq_hessian_workspace_bytes(n))
+
+
+def hessian_accumulate(H, X, stream=None, workspace=None):
+    """H (fp32 [n x n], upper triangle) += 2 X^T X for X [ntok x n] fp16/bf16.
+
+    ``workspace``: None, or a GPU byte tensor of at least
+    hessian_workspace_bytes(n) (enables the stream-K schedule on small n)."""
     lib = load()
     _need_cuda("H", H)
     _need_cuda("X", X)
@@ -118,8 +127,10 @@ def hessian_accumulate(H, X, stream=None):
         raise ValueError("H must be a contiguous fp32 [n x n] tensor")
     if X.dim() != 2 or X.shape[1] != n or X.stride(1) != 1:
         raise ValueError("X must be [ntok x n] with unit column stride")
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
     _check(lib.gptq_hessian_accumulate(_ptr(H), n, _ptr(X), _dtype_code(X.dtype), X.shape[0],
-                                       X.stride(0) if X.shape[0] > 1 else n, _stream(stream)))
+                                       X.stride(0) if X.shape[0] > 1 else n, ws_ptr, ws_bytes,
+                                       _stream(stream)))
     return H
 
 

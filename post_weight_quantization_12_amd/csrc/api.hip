@@ -38,8 +38,14 @@ bool valid_group(int gs, int block) {
 
 extern "C" {
 
+size_t gptq_hessian_workspace_bytes(int64_t n) {
+  if (n < 1) return 0;
+  return syrk_workspace_bytes(n);
+}
+
 int gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dtype, int64_t ntok,
-                            int64_t ldx, void* stream) {
+                            int64_t ldx, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   clear_error();
   if (!H) return fail(GPTQ_ERR_INVALID_ARG, "H is NULL");
   if (!X) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL");
@@ -50,8 +56,13 @@ int gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dtype, int
     return fail(GPTQ_ERR_UNSUPPORTED, "x_dtype must be GPTQ_F16 or GPTQ_BF16");
   const int64_t nt = (n + 127) / 128;
   if (nt * (nt + 1) / 2 > 0x7FFFFFFFLL) return fail(GPTQ_ERR_UNSUPPORTED, "n too large");
+  if (workspace != nullptr && workspace_bytes < syrk_workspace_bytes(n))
+    return fail(GPTQ_ERR_WORKSPACE,
+                "workspace smaller than gptq_hessian_workspace_bytes(n) = " +
+                    std::to_string(syrk_workspace_bytes(n)) + " (or pass NULL)");
   if (ntok == 0) return GPTQ_OK;
-  return hip_status(launch_syrk(H, n, X, x_dtype, ntok, ldx, static_cast<hipStream_t>(stream)),
+  return hip_status(launch_syrk(H, n, X, x_dtype, ntok, ldx, workspace, workspace_bytes,
+                                static_cast<hipStream_t>(stream)),
                     "gptq_hessian_accumulate");
 }
 

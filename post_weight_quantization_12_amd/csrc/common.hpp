@@ -58,9 +58,10 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
-// Hessian SYRK: H(upper) += 2 X^T X.
+// Hessian SYRK: H(upper) += 2 X^T X.  ws (optional) enables the stream-K schedule.
+size_t syrk_workspace_bytes(int64_t n);
 hipError_t launch_syrk(float* H, int64_t n, const void* X, int dtype, int64_t ntok,
-                       int64_t ldx, hipStream_t s);
+                       int64_t ldx, void* ws, size_t ws_bytes, hipStream_t s);
 
 // gptq_prepare pipeline.
 size_t prepare_workspace_bytes(int64_t n);

@@ -17,7 +17,8 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = P.header_functions()
-    assert set(names) == {"gptq_hessian_accumulate", "gptq_prepare_workspace_bytes",
+    assert set(names) == {"gptq_hessian_workspace_bytes", "gptq_hessian_accumulate",
+                          "gptq_prepare_workspace_bytes",
                           "gptq_prepare", "gptq_quantize_workspace_bytes",
                           "gptq_quantize_layer", "gptq_status_string",
                           "gptq_last_error_message"}
@@ -33,16 +34,20 @@ def test_status_strings(lib):
 
 def test_hessian_argument_errors(lib):
     f = lib.gptq_hessian_accumulate
-    assert f(None, 8, FAKE, 0, 4, 8, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(None, 8, FAKE, 0, 4, 8, None, 0, None) == L.GPTQ_ERR_INVALID_ARG
     assert b"H" in lib.gptq_last_error_message()
-    assert f(FAKE, 8, None, 0, 4, 8, None) == L.GPTQ_ERR_INVALID_ARG
-    assert f(FAKE, 0, FAKE, 0, 4, 8, None) == L.GPTQ_ERR_INVALID_ARG
-    assert f(FAKE, 8, FAKE, 0, -1, 8, None) == L.GPTQ_ERR_INVALID_ARG
-    assert f(FAKE, 8, FAKE, 0, 4, 7, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 8, None, 0, 4, 8, None, 0, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, FAKE, 0, 4, 8, None, 0, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 8, FAKE, 0, -1, 8, None, 0, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 8, FAKE, 0, 4, 7, None, 0, None) == L.GPTQ_ERR_INVALID_ARG
     assert b"ldx" in lib.gptq_last_error_message()
-    assert f(FAKE, 8, FAKE, 2, 4, 8, None) == L.GPTQ_ERR_UNSUPPORTED
+    assert f(FAKE, 8, FAKE, 2, 4, 8, None, 0, None) == L.GPTQ_ERR_UNSUPPORTED
+    # a workspace, when given, must be at least the queried size
+    ws = lib.gptq_hessian_workspace_bytes(8)
+    assert ws > 0 and lib.gptq_hessian_workspace_bytes(0) == 0
+    assert f(FAKE, 8, FAKE, 0, 4, 8, FAKE, ws - 1, None) == L.GPTQ_ERR_WORKSPACE
     # ntok == 0 is a no-op that never touches the device
-    assert f(FAKE, 8, FAKE, 0, 0, 8, None) == L.GPTQ_OK
+    assert f(FAKE, 8, FAKE, 0, 0, 8, None, 0, None) == L.GPTQ_OK
     assert lib.gptq_last_error_message() == b""
 
 

@@ -58,8 +58,9 @@ def test_hessian_full_size_sampled(cname):
     X = _x_full(cfg)
     n = cfg.inp
     H = torch.zeros((n, n), dtype=torch.float32, device=DEV)
+    ws = torch.empty((P.hessian_workspace_bytes(n),), dtype=torch.uint8, device=DEV)
     for t0 in range(0, cfg.tokens, CHUNK):
-        P.hessian_accumulate(H, X[t0:t0 + CHUNK])
+        P.hessian_accumulate(H, X[t0:t0 + CHUNK], workspace=ws)
     torch.cuda.synchronize()
     idx = _sample_features(cfg)
     cols = X[:, idx].to("cpu").numpy().astype(np.float64)       # the same fp16 bytes

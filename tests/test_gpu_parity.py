@@ -23,37 +23,44 @@ def _banner(msg):
     print(f"[case] {msg}", flush=True)
 
 
-def _hessian_gpu(X_list, n):
+def _hessian_gpu(X_list, n, streamk=True):
     H = torch.zeros((n, n), dtype=torch.float32, device=DEV)
+    ws = torch.empty((P.hessian_workspace_bytes(n),), dtype=torch.uint8, device=DEV) \
+        if streamk else None
     for X in X_list:
-        P.hessian_accumulate(H, X.to(DEV))
+        P.hessian_accumulate(H, X.to(DEV), workspace=ws)
     torch.cuda.synchronize()
     return H
 
 
 # --------------------------------------------------------------------- SYRK --
-def test_syrk_c0_matches_oracle_and_leaves_lower_untouched():
-    _banner("syrk c0")
+@pytest.mark.parametrize("streamk", [False, True])
+def test_syrk_c0_matches_oracle_and_leaves_lower_untouched(streamk):
+    _banner(f"syrk c0 streamk={streamk}")
     cfg = workloads.get("c0")
     X = workloads.x_tokens(cfg, 0, 1)
-    H = _hessian_gpu([X], cfg.inp).cpu().numpy()
+    H = _hessian_gpu([X], cfg.inp, streamk).cpu().numpy()
     Ho = O.hessian(X.numpy())
     assert np.all(np.tril(H, -1) == 0)
     assert rel_fro(upper_mirror(H), Ho) <= 1e-3
     assert rel_fro(upper_mirror(H), Ho) <= 1e-6  # fp16 products are exact, fp32 sums
 
 
+@pytest.mark.parametrize("streamk", [False, True])
 @pytest.mark.parametrize("n,ntok,ldx,chunks", [(200, 77, 200, 1), (264, 1000, 272, 3),
-                                               (128, 64, 128, 2), (8, 5, 8, 1)])
-def test_syrk_integer_inputs_bit_exact(n, ntok, ldx, chunks):
-    _banner(f"syrk integer n={n} ntok={ntok} ldx={ldx}")
+                                               (128, 64, 128, 2), (8, 5, 8, 1),
+                                               (520, 3000, 520, 2)])
+def test_syrk_integer_inputs_bit_exact(n, ntok, ldx, chunks, streamk):
+    _banner(f"syrk integer n={n} ntok={ntok} ldx={ldx} streamk={streamk}")
     g = torch.Generator().manual_seed(n + ntok)
     Xfull = torch.randint(-8, 9, (ntok, ldx), generator=g).to(torch.float16)
     parts = torch.tensor_split(Xfull, chunks, dim=0)
     H = torch.zeros((n, n), dtype=torch.float32, device=DEV)
+    ws = torch.empty((P.hessian_workspace_bytes(n),), dtype=torch.uint8, device=DEV) \
+        if streamk else None
     for part in parts:
         xd = part.to(DEV)
-        P.hessian_accumulate(H, xd[:, :n])
+        P.hessian_accumulate(H, xd[:, :n], workspace=ws)
     torch.cuda.synchronize()
     Ho = O.hessian(Xfull[:, :n].numpy())
     Hg = H.cpu().numpy().astype(np.float64)
@@ -76,6 +83,9 @@ def test_syrk_heavy_tailed_many_tokens():
     cfg = workloads.get("c3").shrink(inp=512, tokens_per_sample=2048, n_outliers=4)
     X = workloads.x_tokens(cfg, 0, 2)
     H = _hessian_gpu([X], 512).cpu().numpy()
+    H2 = _hessian_gpu([X], 512, streamk=False).cpu().numpy()
+    assert np.array_equal(H, _hessian_gpu([X], 512).cpu().numpy())  # run-to-run identical
+    assert rel_fro(upper_mirror(H2), upper_mirror(H)) <= 1e-6
     Ho = O.hessian(X.numpy())
     assert rel_fro(upper_mirror(H), Ho) <= 1e-3
 
