@@ -65,7 +65,9 @@ def build(verbose: bool = False) -> str:
         msg = "\n".join(f"--- {s}\n{t}" for s, t in failed)
         raise RuntimeError(f"HIP build failed:\n{msg}")
     tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: an unresolved symbol (e.g. a kernel whose host stub was not
+    # emitted) fails the link instead of the first load.
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     os.replace(tmp, LIB)
     return LIB

@@ -15,6 +15,16 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// s_waitcnt with vmcnt <= N and the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0) (LDS reads and writes of this wave done), vmcnt untouched.
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x3 << 14) | 0xF); }
+
 // Error reporting to the C ABI (per host thread).
 void set_error(const std::string& msg);
 void clear_error();

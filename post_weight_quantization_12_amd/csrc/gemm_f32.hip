@@ -6,12 +6,21 @@
 // of the quantization sweep (W[:, right] -= E[:, left] * U'[left, right]).
 // fp32 operands keep the sweep's accumulated error at fp32 level.
 //
-// Tiles BM x BN (128 or 64), BK = 16, 256 threads = 2 x 2 waves.  Both
-// operands are staged k-contiguous in LDS (rows of 16 floats + 4 pad, so each
-// lane's 8 k-values are two conflict-free ds_read_b128).  In one 32x32x2 MFMA
-// the two lane halves carry two different k; over the 8 MFMAs of a stage,
-// lane half h carries k = 8h + u for MFMA u.  Any fixed assignment of k to
-// (MFMA, half) gives the same sum as long as A and B use the same one.
+// Two kernels:
+//  * gemm_f32_dma (16-byte aligned operands, K a multiple of 32): both
+//    operands go straight from memory to LDS with buffer_load ... lds (no
+//    register staging), NS-stage ring, 32 k per stage.  Each operand keeps its
+//    memory layout in LDS: a k-contiguous operand (A not transposed, B
+//    transposed) as rows of 32 floats whose 16-byte chunks are XOR-swizzled
+//    by row % 8, read 4 k at a time with ds_read_b128; an m/n-contiguous
+//    operand as 32 rows of k, read one float per lane (a half-wave reads 128
+//    contiguous bytes).  Masked output elements get buffer offsets past the
+//    descriptor's range, so the epilogue is branch-free.
+//  * gemm_f32_kernel (anything else): register-staged double buffer, BK = 16.
+//
+// In one 32x32x2 MFMA the two lane halves carry two different k.  Any fixed
+// assignment of k to (MFMA, half) gives the same sum as long as A and B use
+// the same one.
 #include "common.hpp"
 
 namespace gptq {
@@ -207,14 +216,248 @@ hipError_t launch_tile(const GemmArgs& g, bool vec, hipStream_t s) {
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS kernel.
+constexpr int DK = 32;  // k per stage
+
+// LDS image of one operand tile for one stage: R rows (of M or N) x DK.
+// K-contiguous: [R][8 chunks of 4 floats], chunk c of row r at c ^ (r % 8).
+// MN-contiguous: [DK][R].
+template <int R, bool KC>
+struct OpTile {
+  static constexpr int FLOATS = R * DK;
+  static constexpr int IPW = R / 32;  // buffer_load_lds per wave (4 waves, 64 x 16 B each)
+  // Byte offset (from the operand's stage base) lane `lane` of instruction q of
+  // wave `wave` loads; the instruction's LDS destination is chunk (wave*IPW+q)*64.
+  __device__ static uint32_t voff(int wave, int q, int lane, int64_t ld) {
+    const int slot = (wave * IPW + q) * 64 + lane;
+    if constexpr (KC) {
+      const int row = slot >> 3, lch = (slot & 7) ^ (row & 7);
+      return (uint32_t)(((int64_t)row * ld + lch * 4) * 4);
+    } else {
+      const int krow = slot / (R / 4), ch = slot % (R / 4);
+      return (uint32_t)(((int64_t)krow * ld + ch * 4) * 4);
+    }
+  }
+  // The 16 k values (k = 16 h + u, u < 16) of row/column `r` for lane half h.
+  __device__ static void frag(const float* t, int r, int h, float (&v)[16]) {
+    if constexpr (KC) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 x = *reinterpret_cast<const float4*>(t + r * DK + (((4 * h + c) ^ (r & 7)) * 4));
+        v[4 * c + 0] = x.x; v[4 * c + 1] = x.y; v[4 * c + 2] = x.z; v[4 * c + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = t[(16 * h + u) * R + r];
+    }
+  }
+};
+
+// LDS destination of a direct load (generic -> LDS address space).
+#define GPTQ_LDS(p) \
+  ((__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) char*)(char*)(p)))
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int num = bytes <= 0 ? 0 : bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num, 0x00020000);
+}
+
+// IPW direct loads of 64 x 16 bytes from `base` (byte extent `bytes`; 0 = all
+// zeros) into consecutive 1 KiB pieces of LDS starting at `lds`.
+template <int IPW>
+__device__ __attribute__((always_inline)) inline void issue_stage(const char* base, int64_t bytes,
+                                                                  const uint32_t* voff,
+                                                                  float* lds) {
+  __amdgpu_buffer_rsrc_t rs = rsrc(base, bytes);
+#pragma unroll
+  for (int q = 0; q < IPW; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GPTQ_LDS(lds + q * 256), 16, voff[q], 0, 0, 0);
+}
+
+template <int BM, int BN, int NS, bool TA, bool TB>
+__global__ void __launch_bounds__(256)
+gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+             const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
+             float alpha, float beta, int kmode, int lower_only, int tiles_n) {
+  constexpr bool AKC = !TA, BKC = TB;  // k-contiguous in memory
+  using TA_ = OpTile<BM, AKC>;
+  using TB_ = OpTile<BN, BKC>;
+  constexpr int FM = BM / 64, FN = BN / 64;
+  constexpr int IPW = TA_::IPW + TB_::IPW;
+  constexpr int STAGE = TA_::FLOATS + TB_::FLOATS;
+  static_assert(NS == 2 || NS == 3, "2 or 3 stages");
+  __shared__ __align__(16) float st0[STAGE];
+  __shared__ __align__(16) float st1[STAGE];
+  __shared__ __align__(16) float st2[NS == 3 ? STAGE : 4];
+
+  // Tile order.  Full K: XCD-contiguous runs of the row-major order (blocks
+  // are dispatched to the 8 XCDs round-robin, so neighbouring tiles share an
+  // L2).  Triangular K ranges: the tiles with the most k go first (longest
+  // processing time first), so the last wave is not a few long tiles.
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int tiles_m = nb / tiles_n;
+  int ti, tj;
+  if (kmode == KR_LE_COL) {
+    tj = tiles_n - 1 - b / tiles_m; ti = b % tiles_m;
+  } else if (kmode == KR_GE_COL) {
+    tj = b / tiles_m; ti = b % tiles_m;
+  } else if (kmode == KR_LE_ROW) {
+    ti = tiles_m - 1 - b / tiles_n; tj = b % tiles_n;
+  } else {
+    const int t = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+    ti = t / tiles_n; tj = t % tiles_n;
+  }
+  const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
+  if (lower_only && j0 >= i0 + BM) return;
+
+  int64_t kbeg = 0, kend = K;
+  if (kmode == KR_LE_COL) kend = j0 + BN < K ? j0 + BN : K;
+  else if (kmode == KR_GE_COL) kbeg = j0;
+  else if (kmode == KR_LE_ROW) kend = i0 + BM < K ? i0 + BM : K;
+  kbeg = kbeg / DK * DK;
+  const int nk = kend > kbeg ? (int)((kend - kbeg + DK - 1) / DK) : 0;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // Operand bases at k = kbeg and their byte extents (rows/columns past the
+  // matrix read as zero or only feed masked outputs).
+  const float* abase = AKC ? A + i0 * lda + kbeg : A + kbeg * lda + i0;
+  const int64_t aext = AKC ? ((M - i0 - 1) * lda + (K - kbeg)) * 4 : ((K - kbeg - 1) * lda + (M - i0)) * 4;
+  const float* bbase = BKC ? B + j0 * ldb + kbeg : B + kbeg * ldb + j0;
+  const int64_t bext = BKC ? ((N - j0 - 1) * ldb + (K - kbeg)) * 4 : ((K - kbeg - 1) * ldb + (N - j0)) * 4;
+  const int64_t astep = AKC ? DK * 4 : DK * lda * 4;  // bytes per stage
+  const int64_t bstep = BKC ? DK * 4 : DK * ldb * 4;
+
+  uint32_t va[TA_::IPW], vb[TB_::IPW];
+#pragma unroll
+  for (int q = 0; q < TA_::IPW; ++q) va[q] = TA_::voff(wave, q, lane, lda);
+#pragma unroll
+  for (int q = 0; q < TB_::IPW; ++q) vb[q] = TB_::voff(wave, q, lane, ldb);
+
+  auto issue = [&](int s, float* stage) __device__ __attribute__((always_inline)) {
+    const bool live = s < nk;
+    issue_stage<TA_::IPW>(live ? (const char*)abase + s * astep : (const char*)A,
+                          live ? aext - s * astep : 0, va, stage + wave * TA_::IPW * 256);
+    issue_stage<TB_::IPW>(live ? (const char*)bbase + s * bstep : (const char*)B,
+                          live ? bext - s * bstep : 0, vb, stage + TA_::FLOATS + wave * TB_::IPW * 256);
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int c = 0; c < FN; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+
+  const int h = lane >> 5;
+  auto compute = [&](const float* stage) __device__ __attribute__((always_inline)) {
+    float av[FM][16], bv[FN][16];
+#pragma unroll
+    for (int a = 0; a < FM; ++a) TA_::frag(stage, wm * (BM / 2) + a * 32 + (lane & 31), h, av[a]);
+#pragma unroll
+    for (int c = 0; c < FN; ++c)
+      TB_::frag(stage + TA_::FLOATS, wn * (BN / 2) + c * 32 + (lane & 31), h, bv[c]);
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int c = 0; c < FN; ++c)
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a][u], bv[c][u], acc[a][c], 0, 0, 0);
+  };
+  // Stage k: own loads of k landed, barrier (everyone's landed, everyone is
+  // done reading k - 1), refill k - 1's buffer with k + NS - 1, compute k.
+  auto step = [&](int k, const float* cur, float* prev) __device__ __attribute__((always_inline)) {
+    wait_vmcnt<(NS - 2) * IPW>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    issue(k + NS - 1, prev);
+    compute(cur);
+  };
+
+  if (nk > 0) {
+    issue(0, st0);
+    if constexpr (NS == 3) issue(1, st1);
+    int kt = 0;
+    if constexpr (NS == 2) {
+      for (; kt + 2 <= nk; kt += 2) {
+        step(kt, st0, st1);
+        step(kt + 1, st1, st0);
+      }
+      if (kt < nk) step(kt, st0, st1);
+    } else {
+      for (; kt + 3 <= nk; kt += 3) {
+        step(kt, st0, st2);
+        step(kt + 1, st1, st0);
+        step(kt + 2, st2, st1);
+      }
+      if (kt < nk) step(kt, st0, st2);
+      if (kt + 1 < nk) step(kt + 1, st1, st0);
+    }
+    wait_vmcnt<0>();
+  }
+
+  // Epilogue: C tile through a buffer descriptor, 16 elements per 32 x 32 block.
+  const int64_t cext = ((M - i0 - 1) * ldc + (N - j0)) * 4;
+  __amdgpu_buffer_rsrc_t rc = rsrc(C + i0 * ldc + j0, cext);
+  const bool rd = beta != 0.0f;
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int c = 0; c < FN; ++c) {
+      const int jl = wn * (BN / 2) + c * 32 + (lane & 31);
+      uint32_t off[16];
+      float cv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int il = wm * (BM / 2) + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const bool in = i0 + il < M && j0 + jl < N;
+        off[v] = in ? (uint32_t)(((int64_t)il * ldc + jl) * 4) : 0x80000000u;
+        cv[v] = rd ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, (int)off[v], 0, 0))
+                   : 0.0f;
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float r = alpha * acc[a][c][v];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rd ? r + beta * cv[v] : r), rc,
+                                              (int)off[v], 0, 0);
+      }
+    }
+}
+
+template <int BM, int BN, int NS, bool TA, bool TB>
+hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
+  const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_f32_dma<BM, BN, NS, TA, TB>), dim3((unsigned)(tm * tn)), dim3(256), 0,
+                     s, g.M, g.N, g.K, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, g.alpha, g.beta,
+                     g.kmode, (int)g.lower_only, (int)tn);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int NS>
+hipError_t launch_dma_t(const GemmArgs& g, hipStream_t s) {
+  if (!g.transA && !g.transB) return launch_dma<BM, BN, NS, false, false>(g, s);
+  if (!g.transA && g.transB) return launch_dma<BM, BN, NS, false, true>(g, s);
+  if (g.transA && !g.transB) return launch_dma<BM, BN, NS, true, false>(g, s);
+  return launch_dma<BM, BN, NS, true, true>(g, s);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const bool vec = al16(g.A) && al16(g.B) && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
                    g.M % 4 == 0 && g.N % 4 == 0 && g.K % 4 == 0;
-  // 128x128 tiles when that still fills the chip, else 64x64.
   const int64_t big = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+  if (vec && g.K % DK == 0 && g.K > 0) {
+    // 128x128 tiles when that still fills the chip, else 64x64.
+    if (big >= 256) return launch_dma_t<128, 128, 2>(g, s);
+    return launch_dma_t<64, 64, 3>(g, s);
+  }
   if (big >= 512) return launch_tile<128, 128>(g, vec, s);
   return launch_tile<64, 64>(g, vec, s);
 }

@@ -204,14 +204,6 @@ constexpr int STAGE_BYTES = 2 * PANEL_BYTES;    // A + B
 constexpr int DMA_PER_WAVE = 8;                 // 2 panels x 1024 chunks / 64 / 4 waves
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
-// s_waitcnt with vmcnt <= N and the other counters left alone (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 __device__ inline v4i16_t ds_read_tr16(const char* lds_byte_ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (v4i16_t __attribute__((address_space(3)))*)(
