@@ -65,6 +65,12 @@ struct GemmArgs {
   float alpha, beta;
   int kmode;
   bool lower_only;  // compute only tiles that touch the lower triangle (i >= j)
+  // Products as three fp16 MFMAs on split operands (x = hi + lo, both fp16;
+  // the lo*lo term dropped), fp32 accumulation: about 2^-22 relative per
+  // product for operands of magnitude ~1 (values must stay below 65504 and
+  // are resolved down to ~2^-24 absolute).  Used only where the operands are
+  // scaled to that range; falls back to fp32 MFMAs on unaligned shapes.
+  bool split16 = false;
 };
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 

@@ -263,6 +263,18 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num, 0x00020000);
 }
 
+// 16 fp32 values -> fp16 high parts and fp16 rounded remainders, as two
+// 8-element MFMA operands each.
+__device__ __attribute__((always_inline)) inline void split16(const float (&v)[16], half8_t (&hi)[2],
+                                                              half8_t (&lo)[2]) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const _Float16 x = (_Float16)v[e];
+    hi[e >> 3][e & 7] = x;
+    lo[e >> 3][e & 7] = (_Float16)(v[e] - (float)x);
+  }
+}
+
 // IPW direct loads of 64 x 16 bytes from `base` (byte extent `bytes`; 0 = all
 // zeros) into consecutive 1 KiB pieces of LDS starting at `lds`.
 template <int IPW>
@@ -275,7 +287,7 @@ __device__ __attribute__((always_inline)) inline void issue_stage(const char* ba
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GPTQ_LDS(lds + q * 256), 16, voff[q], 0, 0, 0);
 }
 
-template <int BM, int BN, int NS, bool TA, bool TB>
+template <int BM, int BN, int NS, bool TA, bool TB, bool X3>
 __global__ void __launch_bounds__(256)
 gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
              const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
@@ -361,13 +373,34 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
 #pragma unroll
     for (int c = 0; c < FN; ++c)
       TB_::frag(stage + TA_::FLOATS, wn * (BN / 2) + c * 32 + (lane & 31), h, bv[c]);
+    if constexpr (!X3) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < 16; ++u)
 #pragma unroll
-      for (int a = 0; a < FM; ++a)
+        for (int a = 0; a < FM; ++a)
 #pragma unroll
-        for (int c = 0; c < FN; ++c)
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a][u], bv[c][u], acc[a][c], 0, 0, 0);
+          for (int c = 0; c < FN; ++c)
+            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a][u], bv[c][u], acc[a][c], 0, 0, 0);
+    } else {
+      // Split fp16 products: x = hi + lo (hi = fp16(x), lo = fp16(x - hi)),
+      // a b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi with fp32 accumulation.  MFMA
+      // k-step q (16 k) takes this lane's values 8q..8q+7 (k = 16h + 8q + e).
+      half8_t ah[FM][2], al[FM][2], bh[FN][2], bl[FN][2];
+#pragma unroll
+      for (int a = 0; a < FM; ++a) split16(av[a], ah[a], al[a]);
+#pragma unroll
+      for (int c = 0; c < FN; ++c) split16(bv[c], bh[c], bl[c]);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+          for (int c = 0; c < FN; ++c) {
+            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[a][q], bh[c][q], acc[a][c], 0, 0, 0);
+            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[a][q], bl[c][q], acc[a][c], 0, 0, 0);
+            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[a][q], bh[c][q], acc[a][c], 0, 0, 0);
+          }
+    }
   };
   // Stage k: own loads of k landed, barrier (everyone's landed, everyone is
   // done reading k - 1), refill k - 1's buffer with k + NS - 1, compute k.
@@ -429,21 +462,21 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
     }
 }
 
-template <int BM, int BN, int NS, bool TA, bool TB>
+template <int BM, int BN, int NS, bool TA, bool TB, bool X3>
 hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_f32_dma<BM, BN, NS, TA, TB>), dim3((unsigned)(tm * tn)), dim3(256), 0,
-                     s, g.M, g.N, g.K, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, g.alpha, g.beta,
+  hipLaunchKernelGGL((gemm_f32_dma<BM, BN, NS, TA, TB, X3>), dim3((unsigned)(tm * tn)), dim3(256),
+                     0, s, g.M, g.N, g.K, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, g.alpha, g.beta,
                      g.kmode, (int)g.lower_only, (int)tn);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int NS>
+template <int BM, int BN, int NS, bool X3>
 hipError_t launch_dma_t(const GemmArgs& g, hipStream_t s) {
-  if (!g.transA && !g.transB) return launch_dma<BM, BN, NS, false, false>(g, s);
-  if (!g.transA && g.transB) return launch_dma<BM, BN, NS, false, true>(g, s);
-  if (g.transA && !g.transB) return launch_dma<BM, BN, NS, true, false>(g, s);
-  return launch_dma<BM, BN, NS, true, true>(g, s);
+  if (!g.transA && !g.transB) return launch_dma<BM, BN, NS, false, false, X3>(g, s);
+  if (!g.transA && g.transB) return launch_dma<BM, BN, NS, false, true, X3>(g, s);
+  if (g.transA && !g.transB) return launch_dma<BM, BN, NS, true, false, X3>(g, s);
+  return launch_dma<BM, BN, NS, true, true, X3>(g, s);
 }
 
 }  // namespace
@@ -455,8 +488,12 @@ hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
   const int64_t big = ((g.M + 127) / 128) * ((g.N + 127) / 128);
   if (vec && g.K % DK == 0 && g.K > 0) {
     // 128x128 tiles when that still fills the chip, else 64x64.
-    if (big >= 256) return launch_dma_t<128, 128, 2>(g, s);
-    return launch_dma_t<64, 64, 3>(g, s);
+    if (g.split16) {
+      if (big >= 256) return launch_dma_t<128, 128, 2, true>(g, s);
+      return launch_dma_t<64, 64, 3, true>(g, s);
+    }
+    if (big >= 256) return launch_dma_t<128, 128, 2, false>(g, s);
+    return launch_dma_t<64, 64, 3, false>(g, s);
   }
   if (big >= 512) return launch_tile<128, 128>(g, vec, s);
   return launch_tile<64, 64>(g, vec, s);

@@ -18,6 +18,12 @@
 // whose leaves (<= 64 columns) run in one workgroup out of LDS.  X = L^-1 is
 // built directly in the output buffer and finally moved in place to
 // U[i][j] = X[n-1-i][n-1-j].
+//
+// Scaling: the recursion runs on A' = D A D with D = diag(2^-e_i) chosen so
+// that A'_ii lies in [0.5, 2) (exact: powers of two).  Then L' = D L, every
+// |L'_ij| < 1.5, and X' = L'^-1 = X D^-1, so X = X' D is recovered exactly.
+// With entries of order one the recursion's products can run as split fp16
+// MFMAs (three fp16 products per fp32 product, fp32 accumulation).
 #include "common.hpp"
 
 namespace gptq {
@@ -117,20 +123,38 @@ symmetrize_kernel(const float* __restrict__ H, int64_t n, float* __restrict__ S)
   }
 }
 
-// A[a][b] (b <= a) = S[q(a)][q(b)] with q(a) = perm[n-1-a]; diagonal: dead fix + damp.
+// dsc[a] = 2^-floor(E/2) where d = m 2^E (m in [0.5, 1)) is the damped,
+// dead-fixed diagonal entry at position a of A (q(a) = perm[n-1-a]), so that
+// d * dsc^2 lies in [0.5, 2).
+__global__ void scale_kernel(const float* __restrict__ H, int64_t n,
+                             const int32_t* __restrict__ perm, const float* __restrict__ damp_add,
+                             float* __restrict__ dsc) {
+  const int64_t a = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (a >= n) return;
+  const int64_t q = perm[n - 1 - a];
+  const float h = H[q * n + q];
+  const float d = (h == 0.0f ? 1.0f : h) + *damp_add;
+  int e = 0;
+  (void)frexpf(d, &e);
+  dsc[a] = (d > 0.0f && d < INFINITY) ? ldexpf(1.0f, -(e >> 1)) : 1.0f;
+}
+
+// A[a][b] (b <= a) = dsc[a] dsc[b] S[q(a)][q(b)] with q(a) = perm[n-1-a];
+// diagonal: dead fix + damp before scaling.
 __global__ void __launch_bounds__(256)
 gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict__ perm,
-              const float* __restrict__ damp_add, float* __restrict__ A) {
+              const float* __restrict__ damp_add, const float* __restrict__ dsc,
+              float* __restrict__ A) {
   extern __shared__ float row[];
   const int64_t a = blockIdx.x;
   const int64_t src = perm[n - 1 - a];
   for (int64_t t = threadIdx.x; t < n; t += blockDim.x) row[t] = S[src * n + t];
   __syncthreads();
-  const float dadd = *damp_add;
+  const float dadd = *damp_add, da = dsc[a];
   for (int64_t b = threadIdx.x; b <= a; b += blockDim.x) {
     float v = row[perm[n - 1 - b]];
     if (b == a) v = (v == 0.0f ? 1.0f : v) + dadd;
-    A[a * n + b] = v;
+    A[a * n + b] = (v * da) * dsc[b];
   }
 }
 
@@ -345,23 +369,26 @@ __global__ void copy2d_kernel(const float* __restrict__ src, int64_t lds, float*
   }
 }
 
-// In place: U[i][j] = X[n-1-i][n-1-j] for i <= j, 0 below the diagonal.
-// X is lower triangular, so every strictly lower (a, b) moves to the strictly
-// upper (n-1-a, n-1-b) (which holds 0) and diagonal entries swap in pairs.
+// In place: U[i][j] = X[n-1-i][n-1-j] for i <= j, 0 below the diagonal, where
+// X = X' D (column b of the computed X' times dsc[b]).  X' is lower
+// triangular, so every strictly lower (a, b) moves to the strictly upper
+// (n-1-a, n-1-b) (which holds 0) and diagonal entries swap in pairs.
 __global__ void __launch_bounds__(256)
-reverse_inplace_kernel(float* __restrict__ U, int64_t n) {
+reverse_inplace_kernel(float* __restrict__ U, int64_t n, const float* __restrict__ dsc) {
   const int64_t a = blockIdx.y;  // source row
   for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b <= a;
        b += (int64_t)gridDim.x * blockDim.x) {
     if (b < a) {
-      const float v = U[a * n + b];
+      const float v = U[a * n + b] * dsc[b];
       U[(n - 1 - a) * n + (n - 1 - b)] = v;
       U[a * n + b] = 0.0f;
     } else if (a < n - 1 - a) {
       const int64_t c = n - 1 - a;
-      const float v = U[a * n + a];
-      U[a * n + a] = U[c * n + c];
+      const float v = U[a * n + a] * dsc[a];
+      U[a * n + a] = U[c * n + c] * dsc[c];
       U[c * n + c] = v;
+    } else if (a == n - 1 - a) {
+      U[a * n + a] *= dsc[a];
     }
   }
 }
@@ -379,6 +406,7 @@ hipError_t gemm(PrepCtx& c, int64_t M, int64_t N, int64_t K, const float* Am, in
                 const float* Bm, int64_t ldb, bool tb, float* Cm, int64_t ldc, float alpha,
                 float beta, int kmode, bool lower) {
   GemmArgs g{M, N, K, Am, lda, ta, Bm, ldb, tb, Cm, ldc, alpha, beta, kmode, lower};
+  g.split16 = true;  // operands are O(1) after the scaling
   return launch_gemm_f32(g, c.s);
 }
 
@@ -422,6 +450,7 @@ struct PrepLayout {
   float* T;
   uint32_t* keys;
   float* damp_add;
+  float* dsc;
   size_t bytes;
 };
 
@@ -434,6 +463,7 @@ PrepLayout carve(void* ws, int64_t n) {
   l.T = c.take<float>((size_t)m1max * (size_t)m1max);
   l.keys = c.take<uint32_t>((size_t)n);
   l.damp_add = c.take<float>(1);
+  l.dsc = c.take<float>((size_t)n);
   l.bytes = c.used;
   return l;
 }
@@ -459,15 +489,18 @@ hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, floa
   const size_t lds = (size_t)n * sizeof(float);
   GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)gather_kernel,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, H, n, perm,
+                     l.damp_add, l.dsc);
+  GPTQ_HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)n), dim3(256), lds, s, U, n, perm, l.damp_add,
-                     l.A);
+                     l.dsc, l.A);
   GPTQ_HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(fill_f32_kernel, dim3(2048), dim3(256), 0, s, U, n * n, 0.0f);
   GPTQ_HIP_TRY(hipGetLastError());
   PrepCtx c{l.A, U, l.T, n, info, s};
   GPTQ_HIP_TRY(cholinv(c, 0, n));
   const unsigned gx = (unsigned)((n + 255) / 256);
-  hipLaunchKernelGGL(reverse_inplace_kernel, dim3(gx, (unsigned)n), dim3(256), 0, s, U, n);
+  hipLaunchKernelGGL(reverse_inplace_kernel, dim3(gx, (unsigned)n), dim3(256), 0, s, U, n, l.dsc);
   return hipGetLastError();
 }
 
