@@ -18,10 +18,11 @@
 // group's current values with two quad DPP reductions.
 //
 // Across blocks, the updates from a finished range of columns to the columns
-// right of it are applied as one fp32 GEMM (W[:, right] -= E[:, left] U'[left,
-// right]) on a recursive halving schedule: the left half is swept, one GEMM
-// carries all its updates to the right half, then the right half is swept.
-// Each pair (j < k) is updated exactly once, before column k is read.
+// right of it are applied as one GEMM (W[:, right] -= E[:, left] U'[left,
+// right], fp32 accumulation) on a recursive halving schedule: the left half is
+// swept, one GEMM carries all its updates to the right half, then the right
+// half is swept.  Each pair (j < k) is updated exactly once, before column k
+// is read.
 #include "common.hpp"
 
 namespace gptq {
@@ -168,7 +169,8 @@ template <int B, int GS>
 __global__ void __launch_bounds__(SW_THREADS)
 sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, int64_t in,
              int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
-             int32_t* __restrict__ zeros, uint8_t* __restrict__ codes) {
+             int32_t* __restrict__ zeros, uint8_t* __restrict__ codes,
+             float* __restrict__ emax) {
   using SM = SweepSmem<B>;
   constexpr int NR = SM::NR, PITCH = SM::PITCH, EP = SM::EP;
   extern __shared__ __align__(16) float smem[];
@@ -273,6 +275,15 @@ sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, 
   }
   __syncthreads();
 
+  // Largest |error| of each row in this block (sizes the split products of
+  // the trailing GEMMs).
+  {
+    float m = 0.0f;
+    for (int c = q; c < width; c += 4) m = fmaxf(m, fabsf(Es[rl * EP + c]));
+    m = fmaxf(m, dpp_xor1(m));
+    m = fmaxf(m, dpp_xor2(m));
+    if (live && q == 0) emax[(c0 / B) * out + row] = m;
+  }
   // Errors (read by the trailing GEMMs) and codes, written out row-contiguous.
   const int wq = width / 4;
   for (int e = tid; e < SW_ROWS * wq; e += SW_THREADS) {
@@ -316,7 +327,7 @@ pack_kernel(const uint8_t* __restrict__ codes, const int32_t* __restrict__ pinv,
 template <int B>
 hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t in, int64_t c0,
                         int width, int bits, int sym, float* scales, int32_t* zeros,
-                        uint8_t* codes, hipStream_t s) {
+                        uint8_t* codes, float* emax, hipStream_t s) {
   if (gs > B) return hipErrorInvalidValue;
   dim3 grid((unsigned)((out + SW_ROWS - 1) / SW_ROWS)), block(SW_THREADS);
   const size_t lds = SweepSmem<B>::BYTES;
@@ -326,7 +337,7 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
     GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,                                           \
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));   \
     hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,  \
-                       zeros, codes);                                                          \
+                       zeros, codes, emax);                                                    \
     break;                                                                                     \
   }
   switch (gs > 0 ? gs : 0) {
@@ -341,7 +352,7 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
         GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
         hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,
-                           zeros, codes);
+                           zeros, codes, emax);
       }
       break;
     case 128:
@@ -350,7 +361,7 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
         GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
         hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,
-                           zeros, codes);
+                           zeros, codes, emax);
       }
       break;
     default:
@@ -358,6 +369,20 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
   }
 #undef GPTQ_SWEEP_CASE
   return hipGetLastError();
+}
+
+// rs[r] = 2^(14 - e) with m = max over blocks [b0, b1) of emax = f 2^e
+// (f in [0.5, 1)), so every scaled error of the row is below 2^14 in
+// magnitude; 1 for an all-zero (or non-finite) row.
+__global__ void row_scale_kernel(const float* __restrict__ emax, int64_t out, int64_t b0,
+                                 int64_t b1, float* __restrict__ rs) {
+  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (r >= out) return;
+  float m = 0.0f;
+  for (int64_t k = b0; k < b1; ++k) m = fmaxf(m, emax[k * out + r]);
+  int e = 0;
+  (void)frexpf(m, &e);
+  rs[r] = (m > 0.0f && m < INFINITY) ? ldexpf(1.0f, 14 - e) : 1.0f;
 }
 
 struct QCtx {
@@ -368,6 +393,8 @@ struct QCtx {
   float* scales;
   int32_t* zeros;
   uint8_t* codes;
+  float* emax;  // [in / block][out] largest |error| per row and block
+  float* rs;    // [out] row scales of the current trailing GEMM
   hipStream_t s;
 };
 
@@ -375,16 +402,19 @@ hipError_t sweep_block(QCtx& c, int64_t a, int64_t b) {
   const int width = (int)(b - a);
   switch (c.block) {
     case 32: return launch_sweep<32>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
-                                     c.scales, c.zeros, c.codes, c.s);
+                                     c.scales, c.zeros, c.codes, c.emax, c.s);
     case 64: return launch_sweep<64>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
-                                     c.scales, c.zeros, c.codes, c.s);
+                                     c.scales, c.zeros, c.codes, c.emax, c.s);
     default: return launch_sweep<128>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
-                                      c.scales, c.zeros, c.codes, c.s);
+                                      c.scales, c.zeros, c.codes, c.emax, c.s);
   }
 }
 
 // Columns [a, b): sweep the left half, carry its updates to the right half
-// with one GEMM, then the right half.
+// with one GEMM, then the right half.  GEMMs over 512 or more columns of
+// errors use split fp16 products with each error row scaled by a power of two
+// (from the sweeps' per-row maxima) so that it spans the fp16 range.
+constexpr int64_t SPLIT_MIN_K = 512;
 hipError_t process(QCtx& c, int64_t a, int64_t b) {
   const int64_t B = c.block;
   if (b - a <= B) return sweep_block(c, a, b);
@@ -393,6 +423,13 @@ hipError_t process(QCtx& c, int64_t a, int64_t b) {
   GPTQ_HIP_TRY(process(c, a, m));
   GemmArgs g{c.out, b - m, m - a, c.Wp + a, c.in, false, c.Up + a * c.in + m, c.in, false,
              c.Wp + m, c.in, -1.0f, 1.0f, KR_FULL, false};
+  if (m - a >= SPLIT_MIN_K) {
+    hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((c.out + 255) / 256)), dim3(256), 0, c.s,
+                       c.emax, c.out, a / B, m / B, c.rs);
+    GPTQ_HIP_TRY(hipGetLastError());
+    g.split16 = true;
+    g.row_scale = c.rs;
+  }
   GPTQ_HIP_TRY(launch_gemm_f32(g, c.s));
   return process(c, m, b);
 }
@@ -402,31 +439,35 @@ struct QLayout {
   float* Up;
   uint8_t* codes;
   int32_t* pinv;
+  float* emax;
+  float* rs;
   size_t bytes;
 };
 
-QLayout carve(void* ws, int64_t out, int64_t in) {
+QLayout carve(void* ws, int64_t out, int64_t in, int block) {
   Carver c(ws);
   QLayout l;
   l.Wp = c.take<float>((size_t)out * in);
   l.Up = c.take<float>((size_t)in * in);
   l.codes = c.take<uint8_t>((size_t)out * in);
   l.pinv = c.take<int32_t>((size_t)in);
+  l.emax = c.take<float>((size_t)out * (size_t)((in + block - 1) / block));
+  l.rs = c.take<float>((size_t)out);
   l.bytes = c.used;
   return l;
 }
 
 }  // namespace
 
-size_t quantize_workspace_bytes(int64_t out, int64_t in, int, int, int) {
-  return carve(nullptr, out, in).bytes;
+size_t quantize_workspace_bytes(int64_t out, int64_t in, int, int, int block) {
+  return carve(nullptr, out, in, block).bytes;
 }
 
 hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, const float* U,
                         const int32_t* perm, int bits, int gs, int sym, int block,
                         int32_t* qweight, float* scales, int32_t* zeros, int32_t* g_idx,
                         void* ws, hipStream_t s) {
-  QLayout l = carve(ws, out, in);
+  QLayout l = carve(ws, out, in, block);
   const size_t lds = perm ? (size_t)in * sizeof(float) : 0;
   if (wdtype == 0) {
     auto k = gather_w_kernel<_Float16>;
@@ -459,7 +500,7 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                        bits, sym, scales, zeros);
     GPTQ_HIP_TRY(hipGetLastError());
   }
-  QCtx c{l.Wp, l.Up, out, in, bits, gs, sym, block, scales, zeros, l.codes, s};
+  QCtx c{l.Wp, l.Up, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.emax, l.rs, s};
   GPTQ_HIP_TRY(process(c, 0, in));
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((out + 255) / 256), (unsigned)(in / 32)),
                      dim3(256), 0, s, l.codes, l.pinv, out, in, bits, qweight);
