@@ -55,6 +55,19 @@ def load_traffic(kernel_file: str, workload: str, launch_units: float):
     return float(d["hbm_bytes_per_launch"])
 
 
+def syrk_kernel_name(n: int) -> str:
+    """Kernels one gptq_hessian_accumulate launch runs (with a workspace): the
+    stream-K schedule adds a fix-up kernel when 256 x 256 tiles would leave
+    more than a quarter of the compute units idle."""
+    import torch
+    nt = (n + 255) // 256
+    tiles = nt * (nt + 1) // 2
+    cus = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    if 4 * tiles < 3 * min(cus, 512):
+        return "syrk_dma_kernel + syrk_streamk_fixup (gptq_hessian_accumulate, stream-K)"
+    return "syrk_dma_kernel (gptq_hessian_accumulate)"
+
+
 def cpu_baseline(cfg, steps_tokens: int):
     """The oracle, untuned, on a bounded sample of the same workload:
     Hessian over one 2048-token sample, the full prepare at the layer's n,
@@ -240,7 +253,7 @@ def main():
                      "quantize": mean(quant_ms)},
         "layer_weights_per_s": weights / (layer_ms * 1e-3),
         "roofline": {
-            "kernel": "syrk_dma_kernel (gptq_hessian_accumulate)",
+            "kernel": syrk_kernel_name(n),
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_FP16_TFLOPS,
