@@ -12,9 +12,10 @@
 // R = J L J is upper with H_p = R R^T, so H_p^-1 = R^-T R^-1 and U = R^-1 =
 // J L^-1 J.  L and L^-1 are computed together by one recursion
 //     [A11 .  ]    L11 = chol(A11), X11 = L11^-1            (recursive)
-//     [A21 A22] -> L21 = A21 X11^T,  A22 -= L21 L21^T       (fp32 MFMA GEMMs)
+//     [A21 A22] -> L21 = A21 X11^T,  A22 -= L21 L21^T       (MFMA GEMMs)
+//                  T2 = L21 X11                             (MFMA GEMM)
 //                  L22 = chol(A22), X22 = L22^-1            (recursive)
-//                  X21 = -X22 (L21 X11)                     (fp32 MFMA GEMMs)
+//                  X21 = -X22 T2                            (MFMA GEMM)
 // whose leaves (<= 64 columns) run in one workgroup out of LDS.  X = L^-1 is
 // built directly in the output buffer and finally moved in place to
 // U[i][j] = X[n-1-i][n-1-j].
@@ -359,16 +360,6 @@ cholinv_leaf_kernel(float* __restrict__ A, float* __restrict__ X, int64_t n, int
   }
 }
 
-__global__ void copy2d_kernel(const float* __restrict__ src, int64_t lds, float* __restrict__ dst,
-                              int64_t ldd, int64_t rows, int64_t cols) {
-  const int64_t total = rows * cols;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = e / cols, c = e % cols;
-    dst[r * ldd + c] = src[r * lds + c];
-  }
-}
-
 // In place: U[i][j] = X[n-1-i][n-1-j] for i <= j, 0 below the diagonal, where
 // X = X' D (column b of the computed X' times dsc[b]).  X' is lower
 // triangular, so every strictly lower (a, b) moves to the strictly upper
@@ -396,7 +387,8 @@ reverse_inplace_kernel(float* __restrict__ U, int64_t n, const float* __restrict
 struct PrepCtx {
   float* A;
   float* X;
-  float* T;
+  float* T;    // L21 of the node being processed (reused by every level)
+  float* T2;   // stack of L21 X11 blocks, one per recursion depth
   int64_t n;
   int32_t* info;
   hipStream_t s;
@@ -410,7 +402,12 @@ hipError_t gemm(PrepCtx& c, int64_t M, int64_t N, int64_t K, const float* Am, in
   return launch_gemm_f32(g, c.s);
 }
 
-hipError_t cholinv(PrepCtx& c, int64_t off, int64_t m) {
+// Node [off, off + m) with its L21 X11 block at t2 (room for m2 x m1, and
+// below it the stack of the deeper levels).  The left child only leaves
+// X11 behind for this node; L21 is needed only by the two products issued
+// before the right child runs, so it lives in the shared T, and the right
+// child's result X22 meets T2 = L21 X11 afterwards.
+hipError_t cholinv(PrepCtx& c, int64_t off, int64_t m, float* t2) {
   const int64_t n = c.n;
   if (m <= NB) {
     hipLaunchKernelGGL(cholinv_leaf_kernel, dim3(1), dim3(256), 0, c.s, c.A, c.X, n, off, (int)m,
@@ -419,35 +416,43 @@ hipError_t cholinv(PrepCtx& c, int64_t off, int64_t m) {
   }
   const int64_t m1 = ((m / 2 + NB - 1) / NB) * NB;
   const int64_t m2 = m - m1;
-  float* A11 = c.A + off * n + off;
   float* A21 = c.A + (off + m1) * n + off;
   float* A22 = c.A + (off + m1) * n + off + m1;
   float* X11 = c.X + off * n + off;
   float* X21 = c.X + (off + m1) * n + off;
   float* X22 = c.X + (off + m1) * n + off + m1;
-  (void)A11;
-  GPTQ_HIP_TRY(cholinv(c, off, m1));
+  float* next = t2 + m2 * m1;  // deeper levels
+  GPTQ_HIP_TRY(cholinv(c, off, m1, next));
   // L21 = A21 * X11^T  (X11 lower: op(B)[k][j] = X11[j][k] vanishes for k > j)
   GPTQ_HIP_TRY(gemm(c, m2, m1, m1, A21, n, false, X11, n, true, c.T, m1, 1.0f, 0.0f, KR_LE_COL,
                     false));
-  hipLaunchKernelGGL(copy2d_kernel, dim3(1024), dim3(256), 0, c.s, c.T, m1, A21, n, m2, m1);
-  GPTQ_HIP_TRY(hipGetLastError());
   // A22 -= L21 L21^T (lower tiles)
-  GPTQ_HIP_TRY(gemm(c, m2, m2, m1, A21, n, false, A21, n, true, A22, n, -1.0f, 1.0f, KR_FULL,
+  GPTQ_HIP_TRY(gemm(c, m2, m2, m1, c.T, m1, false, c.T, m1, true, A22, n, -1.0f, 1.0f, KR_FULL,
                     true));
-  GPTQ_HIP_TRY(cholinv(c, off + m1, m2));
-  // T = L21 * X11 (X11[k][j] vanishes for k < j)
-  GPTQ_HIP_TRY(gemm(c, m2, m1, m1, A21, n, false, X11, n, false, c.T, m1, 1.0f, 0.0f, KR_GE_COL,
+  // T2 = L21 * X11 (X11[k][j] vanishes for k < j)
+  GPTQ_HIP_TRY(gemm(c, m2, m1, m1, c.T, m1, false, X11, n, false, t2, m1, 1.0f, 0.0f, KR_GE_COL,
                     false));
-  // X21 = -X22 * T (X22[i][k] vanishes for k > i)
-  GPTQ_HIP_TRY(gemm(c, m2, m1, m2, X22, n, false, c.T, m1, false, X21, n, -1.0f, 0.0f, KR_LE_ROW,
+  GPTQ_HIP_TRY(cholinv(c, off + m1, m2, next));
+  // X21 = -X22 * T2 (X22[i][k] vanishes for k > i)
+  GPTQ_HIP_TRY(gemm(c, m2, m1, m2, X22, n, false, t2, m1, false, X21, n, -1.0f, 0.0f, KR_LE_ROW,
                     false));
   return hipSuccess;
+}
+
+// Floats of the T2 stack for a node of order m (its own block plus the
+// deeper levels' largest chain).
+int64_t t2_floats(int64_t m) {
+  if (m <= NB) return 0;
+  const int64_t m1 = ((m / 2 + NB - 1) / NB) * NB;
+  const int64_t m2 = m - m1;
+  const int64_t a = t2_floats(m1), b = t2_floats(m2);
+  return m2 * m1 + (a > b ? a : b);
 }
 
 struct PrepLayout {
   float* A;
   float* T;
+  float* T2;
   uint32_t* keys;
   float* damp_add;
   float* dsc;
@@ -459,8 +464,9 @@ PrepLayout carve(void* ws, int64_t n) {
   PrepLayout l;
   const int64_t m1max = ((n / 2 + NB - 1) / NB) * NB;
   l.A = c.take<float>((size_t)n * n);
-  // every internal node has m2 <= m1 <= m1max, so m1max^2 holds any L21 / T block
+  // every internal node has m2 <= m1 <= m1max, so m1max^2 holds any L21 block
   l.T = c.take<float>((size_t)m1max * (size_t)m1max);
+  l.T2 = c.take<float>((size_t)(t2_floats(n) > 0 ? t2_floats(n) : 1));
   l.keys = c.take<uint32_t>((size_t)n);
   l.damp_add = c.take<float>(1);
   l.dsc = c.take<float>((size_t)n);
@@ -497,8 +503,8 @@ hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, floa
   GPTQ_HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(fill_f32_kernel, dim3(2048), dim3(256), 0, s, U, n * n, 0.0f);
   GPTQ_HIP_TRY(hipGetLastError());
-  PrepCtx c{l.A, U, l.T, n, info, s};
-  GPTQ_HIP_TRY(cholinv(c, 0, n));
+  PrepCtx c{l.A, U, l.T, l.T2, n, info, s};
+  GPTQ_HIP_TRY(cholinv(c, 0, n, l.T2));
   const unsigned gx = (unsigned)((n + 255) / 256);
   hipLaunchKernelGGL(reverse_inplace_kernel, dim3(gx, (unsigned)n), dim3(256), 0, s, U, n, l.dsc);
   return hipGetLastError();
