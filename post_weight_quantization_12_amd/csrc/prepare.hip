@@ -47,15 +47,17 @@ __device__ inline uint32_t order_key(float d) {
 }
 
 // One workgroup: keys of the raw diagonal, mean of the (dead-fixed) diagonal,
-// damp_add = damp * mean; clears info.
+// damp_add = damp * mean; clears info and the rank counters.
 __global__ void __launch_bounds__(1024)
 diag_stats_kernel(const float* __restrict__ H, int64_t n, float damp, uint32_t* __restrict__ keys,
-                  float* __restrict__ damp_add, int32_t* __restrict__ info) {
+                  int32_t* __restrict__ rank, float* __restrict__ damp_add,
+                  int32_t* __restrict__ info) {
   __shared__ double red[1024];
   double s = 0.0;
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
     const float d = H[i * n + i];
     keys[i] = order_key(d);
+    rank[i] = 0;
     s += (double)(d == 0.0f ? 1.0f : d);
   }
   red[threadIdx.x] = s;
@@ -70,28 +72,53 @@ diag_stats_kernel(const float* __restrict__ H, int64_t n, float damp, uint32_t* 
   }
 }
 
-// perm[rank(i)] = i, rank by decreasing key, ties by index (stable).
+// rank(i) = #{j : key_j > key_i, or key_j == key_i and j < i}: decreasing
+// key, ties by index (stable).  Block (x, y) counts, for its 256 keys i, the
+// keys j of chunk y (RANK_CHUNK of them) and adds the count to rank[i]
+// (integer adds: the result does not depend on their order).
+constexpr int RANK_CHUNK = 1024;
 __global__ void __launch_bounds__(256)
-rank_kernel(const uint32_t* __restrict__ keys, int64_t n, int desc, int32_t* __restrict__ perm) {
-  __shared__ uint32_t sk[2048];
+rank_count_kernel(const uint32_t* __restrict__ keys, int64_t n, int desc,
+                  int32_t* __restrict__ rank) {
+  __shared__ __align__(16) uint32_t sk[RANK_CHUNK];
+  if (!desc) return;
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (!desc) {
-    if (i < n) perm[i] = (int32_t)i;
-    return;
-  }
-  const uint32_t ki = i < n ? keys[i] : 0u;
-  int64_t rank = 0;
-  for (int64_t c0 = 0; c0 < n; c0 += 2048) {
-    const int64_t cn = n - c0 < 2048 ? n - c0 : 2048;
-    __syncthreads();
-    for (int64_t t = threadIdx.x; t < cn; t += blockDim.x) sk[t] = keys[c0 + t];
-    __syncthreads();
-    for (int64_t t = 0; t < cn; ++t) {
+  const int64_t c0 = (int64_t)blockIdx.y * RANK_CHUNK;
+  const int64_t cn = n - c0 < RANK_CHUNK ? n - c0 : RANK_CHUNK;
+  for (int64_t t = threadIdx.x; t < RANK_CHUNK; t += blockDim.x)
+    sk[t] = t < cn ? keys[c0 + t] : 0u;
+  __syncthreads();
+  if (i >= n) return;
+  const uint32_t ki = keys[i];
+  int cnt = 0;
+  if (c0 + cn <= i) {  // every j of the chunk precedes i: ties count
+#pragma unroll 4
+    for (int t = 0; t < RANK_CHUNK; t += 4) {
+      const uint4 k4 = *reinterpret_cast<const uint4*>(sk + t);
+      cnt += (k4.x >= ki) + (k4.y >= ki) + (k4.z >= ki) + (k4.w >= ki);
+    }
+    cnt -= (int)(RANK_CHUNK - cn) * (ki == 0u);  // padding keys are 0
+  } else if (c0 > i) {  // every j follows i: strict only
+#pragma unroll 4
+    for (int t = 0; t < RANK_CHUNK; t += 4) {
+      const uint4 k4 = *reinterpret_cast<const uint4*>(sk + t);
+      cnt += (k4.x > ki) + (k4.y > ki) + (k4.z > ki) + (k4.w > ki);
+    }
+  } else {
+    for (int t = 0; t < (int)cn; ++t) {
       const uint32_t kj = sk[t];
-      rank += (kj > ki) | ((kj == ki) & (c0 + t < i));
+      cnt += (kj > ki) | ((kj == ki) & (c0 + t < i));
     }
   }
-  if (i < n) perm[rank] = (int32_t)i;
+  if (cnt) atomicAdd(rank + i, cnt);
+}
+
+// perm[rank(i)] = i (desc_act) or perm[i] = i.
+__global__ void rank_scatter_kernel(const int32_t* __restrict__ rank, int64_t n, int desc,
+                                    int32_t* __restrict__ perm) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  perm[desc ? rank[i] : i] = (int32_t)i;
 }
 
 // S = H with the lower triangle mirrored from the upper (S fully symmetric).
@@ -146,16 +173,51 @@ __global__ void __launch_bounds__(256)
 gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict__ perm,
               const float* __restrict__ damp_add, const float* __restrict__ dsc,
               float* __restrict__ A) {
-  extern __shared__ float row[];
+  extern __shared__ __align__(16) float row[];
   const int64_t a = blockIdx.x;
   const int64_t src = perm[n - 1 - a];
-  for (int64_t t = threadIdx.x; t < n; t += blockDim.x) row[t] = S[src * n + t];
+  // Stage the source row, 4 float4 loads per thread in flight.
+  if ((n & 3) == 0) {
+    const float4* s4 = reinterpret_cast<const float4*>(S + src * n);
+    float4* r4 = reinterpret_cast<float4*>(row);
+    const int64_t n4 = n / 4;
+    for (int64_t t0 = threadIdx.x; t0 < n4; t0 += 4 * (int64_t)blockDim.x) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t t = t0 + u * (int64_t)blockDim.x;
+        v[u] = t < n4 ? s4[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t t = t0 + u * (int64_t)blockDim.x;
+        if (t < n4) r4[t] = v[u];
+      }
+    }
+  } else {
+    for (int64_t t = threadIdx.x; t < n; t += blockDim.x) row[t] = S[src * n + t];
+  }
   __syncthreads();
   const float dadd = *damp_add, da = dsc[a];
-  for (int64_t b = threadIdx.x; b <= a; b += blockDim.x) {
-    float v = row[perm[n - 1 - b]];
-    if (b == a) v = (v == 0.0f ? 1.0f : v) + dadd;
-    A[a * n + b] = (v * da) * dsc[b];
+  // 8 elements per thread in flight (the loop is latency-bound otherwise).
+  for (int64_t b0 = threadIdx.x; b0 <= a; b0 += 8 * (int64_t)blockDim.x) {
+    int32_t q[8];
+    float sc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t b = b0 + u * (int64_t)blockDim.x;
+      q[u] = b <= a ? perm[n - 1 - b] : 0;
+      sc[u] = b <= a ? dsc[b] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t b = b0 + u * (int64_t)blockDim.x;
+      if (b <= a) {
+        float v = row[q[u]];
+        if (b == a) v = (v == 0.0f ? 1.0f : v) + dadd;
+        A[a * n + b] = (v * da) * sc[u];
+      }
+    }
   }
 }
 
@@ -454,6 +516,7 @@ struct PrepLayout {
   float* T;
   float* T2;
   uint32_t* keys;
+  int32_t* rank;
   float* damp_add;
   float* dsc;
   size_t bytes;
@@ -468,6 +531,7 @@ PrepLayout carve(void* ws, int64_t n) {
   l.T = c.take<float>((size_t)m1max * (size_t)m1max);
   l.T2 = c.take<float>((size_t)(t2_floats(n) > 0 ? t2_floats(n) : 1));
   l.keys = c.take<uint32_t>((size_t)n);
+  l.rank = c.take<int32_t>((size_t)n);
   l.damp_add = c.take<float>(1);
   l.dsc = c.take<float>((size_t)n);
   l.bytes = c.used;
@@ -481,11 +545,16 @@ size_t prepare_workspace_bytes(int64_t n) { return carve(nullptr, n).bytes; }
 hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, float* U,
                        int32_t* perm, int32_t* info, void* ws, hipStream_t s) {
   PrepLayout l = carve(ws, n);
-  hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp, l.keys, l.damp_add,
-                     info);
+  hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp, l.keys, l.rank,
+                     l.damp_add, info);
   GPTQ_HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, l.keys, n,
-                     desc_act, perm);
+  const unsigned nb256 = (unsigned)((n + 255) / 256);
+  if (desc_act) {
+    hipLaunchKernelGGL(rank_count_kernel, dim3(nb256, (unsigned)((n + RANK_CHUNK - 1) / RANK_CHUNK)),
+                       dim3(256), 0, s, l.keys, n, desc_act, l.rank);
+    GPTQ_HIP_TRY(hipGetLastError());
+  }
+  hipLaunchKernelGGL(rank_scatter_kernel, dim3(nb256), dim3(256), 0, s, l.rank, n, desc_act, perm);
   GPTQ_HIP_TRY(hipGetLastError());
   // S (symmetric H) is staged in the output buffer, gathered into A, then the
   // output buffer is cleared and receives L^-1.

@@ -78,31 +78,81 @@ template <typename T>
 __global__ void __launch_bounds__(256)
 gather_w_kernel(const T* __restrict__ W, int64_t out, int64_t in, const int32_t* __restrict__ perm,
                 float* __restrict__ Wp) {
-  extern __shared__ float rowbuf[];
+  extern __shared__ __align__(16) float rowbuf[];
   const int64_t r = blockIdx.x;
   const T* src = W + r * in;
   float* dst = Wp + r * in;
+  const bool vec = (reinterpret_cast<uintptr_t>(W) & 15) == 0;  // rows then are too (in % 32 == 0)
+  if (!vec) {
+    for (int64_t j = threadIdx.x; j < in; j += blockDim.x) rowbuf[j] = to_f32<T>(src[j]);
+  } else {
+    // Stage the row as fp32, 4 x 16-byte loads per thread in flight.
+    constexpr int PER = 16 / sizeof(T);  // elements per 16-byte load
+    const uint4* s16 = reinterpret_cast<const uint4*>(src);
+    const int64_t nv = in / PER;
+    for (int64_t t0 = threadIdx.x; t0 < nv; t0 += 4 * (int64_t)blockDim.x) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t t = t0 + u * (int64_t)blockDim.x;
+        v[u] = t < nv ? s16[t] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t t = t0 + u * (int64_t)blockDim.x;
+        if (t < nv) {
+          const T* e = reinterpret_cast<const T*>(&v[u]);
+#pragma unroll
+          for (int q = 0; q < PER; ++q) rowbuf[t * PER + q] = to_f32<T>(e[q]);
+        }
+      }
+    }
+  }
+  __syncthreads();
   if (perm == nullptr) {
-    for (int64_t j = threadIdx.x; j < in; j += blockDim.x) dst[j] = to_f32<T>(src[j]);
+    for (int64_t j = threadIdx.x; j < in; j += blockDim.x) dst[j] = rowbuf[j];
     return;
   }
-  for (int64_t j = threadIdx.x; j < in; j += blockDim.x) rowbuf[j] = to_f32<T>(src[j]);
-  __syncthreads();
-  for (int64_t j = threadIdx.x; j < in; j += blockDim.x) {
-    int32_t p = perm[j];
-    if ((uint32_t)p >= (uint32_t)in) p = 0;  // never read outside the row
-    dst[j] = rowbuf[p];
+  // 8 elements per thread in flight (the loop is latency-bound otherwise).
+  for (int64_t j0 = threadIdx.x; j0 < in; j0 += 8 * (int64_t)blockDim.x) {
+    int32_t p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = j0 + u * (int64_t)blockDim.x;
+      p[u] = j < in ? perm[j] : 0;
+      if ((uint32_t)p[u] >= (uint32_t)in) p[u] = 0;  // never read outside the row
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = j0 + u * (int64_t)blockDim.x;
+      if (j < in) dst[j] = rowbuf[p[u]];
+    }
   }
 }
 
-// Up[j][k] = U[j][k] / U[j][j] for k > j, 0 for k <= j.
+// Up[j][k] = U[j][k] / U[j][j] for k > j and 0 for 4*floor(j/4) <= k <= j.
+// Columns further left are never read (the sweep's window of row j starts at
+// column 4*floor(j/4); the trailing GEMMs read only columns right of their
+// rows) and are not written.  One float4 per thread.
 __global__ void __launch_bounds__(256)
 uprime_kernel(const float* __restrict__ U, int64_t n, float* __restrict__ Up) {
   const int64_t j = blockIdx.y;
+  const int64_t k0 = 4 * (j / 4) + 4 * (blockIdx.x * (int64_t)blockDim.x + threadIdx.x);
+  if (k0 >= n) return;
   const float d = U[j * n + j];
-  for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < n;
-       k += (int64_t)gridDim.x * blockDim.x)
-    Up[j * n + k] = k > j ? U[j * n + k] / d : 0.0f;
+  const float* src = U + j * n + k0;
+  float* dst = Up + j * n + k0;
+  if (k0 + 4 <= n && (n & 3) == 0) {
+    const float4 u = *reinterpret_cast<const float4*>(src);
+    float4 r;
+    r.x = k0 + 0 > j ? u.x / d : 0.0f;
+    r.y = k0 + 1 > j ? u.y / d : 0.0f;
+    r.z = k0 + 2 > j ? u.z / d : 0.0f;
+    r.w = k0 + 3 > j ? u.w / d : 0.0f;
+    *reinterpret_cast<float4*>(dst) = r;
+  } else {
+    for (int e = 0; e < 4 && k0 + e < n; ++e) dst[e] = k0 + e > j ? src[e] / d : 0.0f;
+  }
 }
 
 // pinv[perm[j]] = j;  g_idx[perm[j]] = j / gs (0 for one group per row).
@@ -301,25 +351,58 @@ sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, 
   }
 }
 
-// qweight[u*bits + t][r]: word t of the 32-code unit u of row r (original column order).
+// qweight[u*bits + t][r]: word t of the 32-code unit u of row r (original
+// column order).  A workgroup stages pinv and R rows of codes (quantization
+// order) in LDS, then packs (unit, row) pairs with the R rows of a unit on
+// neighbouring threads, so the permuted reads hit LDS and the word stores of
+// a unit cover R consecutive rows.
 __global__ void __launch_bounds__(256)
 pack_kernel(const uint8_t* __restrict__ codes, const int32_t* __restrict__ pinv, int64_t out,
-            int64_t in, int bits, int32_t* __restrict__ qweight) {
-  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int64_t u = blockIdx.y;
-  if (r >= out) return;
-  const uint8_t* crow = codes + r * in;
-  uint64_t acc = 0;
-  int nb = 0, t = 0;
-  for (int c = 0; c < 32; ++c) {
-    const uint32_t code = crow[pinv[u * 32 + c]];
-    acc |= (uint64_t)code << nb;
-    nb += bits;
-    if (nb >= 32) {
-      qweight[(u * bits + t) * out + r] = (int32_t)(uint32_t)acc;
-      acc >>= 32;
-      nb -= 32;
-      ++t;
+            int64_t in, int bits, int R, int32_t* __restrict__ qweight) {
+  extern __shared__ __align__(16) uint8_t psm[];
+  int32_t* pl = reinterpret_cast<int32_t*>(psm);
+  uint8_t* cl = psm + in * sizeof(int32_t);
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  const int rows = (int)(out - r0 < R ? out - r0 : R);
+  for (int64_t j = threadIdx.x; j < in; j += blockDim.x) {
+    int32_t p = pinv[j];
+    pl[j] = (uint32_t)p < (uint32_t)in ? p : 0;  // never read outside the row
+  }
+  const int64_t v16 = in / 16;  // in is a multiple of 32
+  for (int64_t e0 = threadIdx.x; e0 < rows * v16; e0 += 4 * (int64_t)blockDim.x) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t e = e0 + u * (int64_t)blockDim.x;
+      v[u] = e < rows * v16 ? *reinterpret_cast<const uint4*>(codes + r0 * in + e * 16)
+                            : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t e = e0 + u * (int64_t)blockDim.x;
+      if (e < rows * v16) *reinterpret_cast<uint4*>(cl + e * 16) = v[u];
+    }
+  }
+  __syncthreads();
+  const int64_t units = in / 32;
+  for (int64_t t = threadIdx.x; t < units * R; t += blockDim.x) {
+    const int64_t u = t / R;
+    const int rr = (int)(t % R);
+    if (rr >= rows) continue;
+    const uint8_t* crow = cl + (int64_t)rr * in;
+    const int32_t* pu = pl + u * 32;
+    uint64_t acc = 0;
+    int nb = 0, w = 0;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      acc |= (uint64_t)crow[pu[c]] << nb;
+      nb += bits;
+      if (nb >= 32) {
+        qweight[(u * bits + w) * out + r0 + rr] = (int32_t)(uint32_t)acc;
+        acc >>= 32;
+        nb -= 32;
+        ++w;
+      }
     }
   }
 }
@@ -468,7 +551,7 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                         int32_t* qweight, float* scales, int32_t* zeros, int32_t* g_idx,
                         void* ws, hipStream_t s) {
   QLayout l = carve(ws, out, in, block);
-  const size_t lds = perm ? (size_t)in * sizeof(float) : 0;
+  const size_t lds = (size_t)in * sizeof(float);
   if (wdtype == 0) {
     auto k = gather_w_kernel<_Float16>;
     GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -489,8 +572,8 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                        out, in, perm, l.Wp);
   }
   GPTQ_HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(uprime_kernel, dim3((unsigned)((in + 255) / 256), (unsigned)in), dim3(256), 0,
-                     s, U, in, l.Up);
+  hipLaunchKernelGGL(uprime_kernel, dim3((unsigned)((in / 4 + 256) / 256), (unsigned)in), dim3(256),
+                     0, s, U, in, l.Up);
   GPTQ_HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(perm_tables_kernel, dim3((unsigned)((in + 255) / 256)), dim3(256), 0, s, perm,
                      in, gs, l.pinv, g_idx);
@@ -502,8 +585,14 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
   }
   QCtx c{l.Wp, l.Up, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.emax, l.rs, s};
   GPTQ_HIP_TRY(process(c, 0, in));
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((out + 255) / 256), (unsigned)(in / 32)),
-                     dim3(256), 0, s, l.codes, l.pinv, out, in, bits, qweight);
+  // rows per packing workgroup: as many (up to 16) as fit next to pinv in 160 KiB of LDS
+  int R = 16;
+  while (R > 1 && (size_t)in * (4 + R) > 160 * 1024) R /= 2;
+  const size_t plds = (size_t)in * (4 + R);
+  GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)pack_kernel,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds));
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((out + R - 1) / R)), dim3(256), plds, s, l.codes,
+                     l.pinv, out, in, bits, R, qweight);
   return hipGetLastError();
 }
 
