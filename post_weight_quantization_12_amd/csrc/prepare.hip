@@ -16,7 +16,7 @@
 //                  T2 = L21 X11                             (MFMA GEMM)
 //                  L22 = chol(A22), X22 = L22^-1            (recursive)
 //                  X21 = -X22 T2                            (MFMA GEMM)
-// whose leaves (<= 64 columns) run in one workgroup out of LDS.  X = L^-1 is
+// whose leaves (<= 128 columns) run in one workgroup out of LDS.  X = L^-1 is
 // built directly in the output buffer and finally moved in place to
 // U[i][j] = X[n-1-i][n-1-j].
 //
@@ -30,7 +30,7 @@
 namespace gptq {
 namespace {
 
-constexpr int NB = 64;  // leaf order of the recursion
+constexpr int NB = 128;  // leaf order of the recursion
 
 __global__ void fill_f32_kernel(float* p, int64_t count, float v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < count;
@@ -221,206 +221,249 @@ gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict_
   }
 }
 
-// Leaf of the recursion: factor the m x m (m <= 64) diagonal block at `off`
-// (lower part of A, leading dimension n) and invert the factor, in one
-// workgroup of 4 waves, blocked by 16 columns:
-//   for each 16-column panel: the 16 x 16 diagonal block is factored (and
-//   inverted) by 16 lanes of wave 0 in registers, broadcasting through
-//   readlane; the rows below are solved against it and the trailing block
-//   updated by all 256 threads out of LDS.
-//   then the off-diagonal blocks of L^-1, block row by block row:
-//   X[p][q] = -Dinv_p * sum_{q <= r < p} L[p][r] X[r][q].
-// Rows >= m are padded with the identity (so every pivot is defined) and are
-// not written back.  Writes L into A and L^-1 into X (lower parts).
-constexpr int LP = NB + 4;  // padded LDS row (16-byte aligned rows, 272 B apart)
+// Leaf of the recursion: X = L^-1 for the m x m (m <= NB) diagonal block at
+// `off` (lower part of A, leading dimension n), in one workgroup of 8 waves
+// out of LDS, blocked by 16 columns.  Per 16-column step c:
+//   (a) wave 0 factors the 16 x 16 diagonal block in registers (readlane
+//       broadcasts, one rsqrt per pivot) while wave 1 inverts the previous
+//       step's diagonal block (off the critical path);
+//   (b) every row below is solved against the new block by forward
+//       substitution (one thread per row);
+//   (c) the trailing lower block is updated in 16 x 16 tiles on the matrix
+//       cores (v_mfma_f32_16x16x4f32).
+// Then the off-diagonal blocks of X by doubling (blocks of 32, 64, 128):
+//   T = L21 X11, X21 = -X22 T, again in 16 x 16 MFMA tiles over all waves.
+// Rows >= m are padded with the identity (so every pivot is defined).  Only
+// X is written back (lower part, rows and columns < m): the recursion never
+// reads L again.
+constexpr int LP = NB + 4;  // padded LDS row (16-byte aligned rows)
+constexpr int LEAF_THREADS = 512;
+constexpr int NSTEP = NB / 16;
 
 __device__ inline float bcast(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-__device__ inline float dot16(const float* a, const float* b) {
-  float acc = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 16; k += 4) {
-    const float4 x = *reinterpret_cast<const float4*>(a + k);
-    const float4 y = *reinterpret_cast<const float4*>(b + k);
-    acc = fmaf(x.x, y.x, acc);
-    acc = fmaf(x.y, y.y, acc);
-    acc = fmaf(x.z, y.z, acc);
-    acc = fmaf(x.w, y.w, acc);
+// acc += sgn * sum_{k<K} a(r, k) b(k, c) for one 16 x 16 tile (v_mfma_f32_16x16x4f32:
+// lane l supplies a(l%16, k0 + l/16) and b(k0 + l/16, l%16) and holds rows
+// 4(l/16)..+3 of column l%16).  a(r, k) = A[r*LP + k]; b(k, c) = BT ? B[c*LP + k] : B[k*LP + c].
+template <bool BT>
+__device__ inline f32x4_t tile16(const float* A, const float* B, int K, f32x4_t acc, float sgn,
+                                  int lane) {
+  const int r = lane & 15, kq = lane >> 4;
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    const float a = sgn * A[r * LP + k0 + kq];
+    const float b = BT ? B[r * LP + k0 + kq] : B[(k0 + kq) * LP + r];
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
   }
   return acc;
 }
+__device__ inline f32x4_t load_tile(const float* C, int lane) {
+  f32x4_t v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = C[(4 * (lane >> 4) + q) * LP + (lane & 15)];
+  return v;
+}
+__device__ inline void store_tile(float* C, f32x4_t v, int lane) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) C[(4 * (lane >> 4) + q) * LP + (lane & 15)] = v[q];
+}
 
-__global__ void __launch_bounds__(256)
-cholinv_leaf_kernel(float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t off, int m,
-                    int32_t* __restrict__ info) {
+__global__ void __launch_bounds__(LEAF_THREADS)
+cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t off,
+                    int m, int32_t* __restrict__ info) {
   __shared__ __align__(16) float Ls[NB * LP];
   __shared__ __align__(16) float Xs[NB * LP];
+  __shared__ float rinv_s[NB];  // 1 / L_jj
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15;
 
   {
-    // All 16 loads per thread are issued before any is used (addresses of
-    // masked-out elements are clamped to the block's first element).
-    float v[NB * NB / 256];
+    // 8 loads per thread in flight (addresses of masked-out elements are
+    // clamped to the block's first element).
+    constexpr int PER = NB * NB / LEAF_THREADS;
 #pragma unroll
-    for (int q = 0; q < NB * NB / 256; ++q) {
-      const int e = tid + 256 * q, i = e / NB, j = e % NB;
-      const bool ok = i < m && j <= i;
-      const float* src = A + (ok ? (off + i) * n + off + j : off * n + off);
-      v[q] = *src;
-    }
+    for (int q0 = 0; q0 < PER; q0 += 8) {
+      float v[8];
 #pragma unroll
-    for (int q = 0; q < NB * NB / 256; ++q) {
-      const int e = tid + 256 * q, i = e / NB, j = e % NB;
-      const bool ok = i < m && j <= i;
-      Ls[i * LP + j] = ok ? v[q] : (i == j ? 1.0f : 0.0f);
-      Xs[i * LP + j] = 0.0f;
+      for (int u = 0; u < 8; ++u) {
+        const int e = tid + LEAF_THREADS * (q0 + u), i = e / NB, j = e % NB;
+        const bool ok = i < m && j <= i;
+        v[u] = A[ok ? (off + i) * n + off + j : off * n + off];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = tid + LEAF_THREADS * (q0 + u), i = e / NB, j = e % NB;
+        const bool ok = i < m && j <= i;
+        Ls[i * LP + j] = ok ? v[u] : (i == j ? 1.0f : 0.0f);
+        Xs[i * LP + j] = 0.0f;
+      }
     }
   }
   __syncthreads();
 
+  // Y = (diagonal block b of L)^-1 into Xs, by one wave (lanes 0..15 hold rows):
+  // row k of Y = (e_k - sum_{j<k} L_kj Y_j) / L_kk, rows broadcast by readlane.
+  auto invert_block = [&](int b) {
+    const int c = 16 * b;
+    float d[16], y[16];
 #pragma unroll
-  for (int c = 0; c < NB; c += 16) {
-    // (1) 16 x 16 diagonal block: Cholesky and inverse in wave 0's registers
-    // (reciprocal square root per pivot; no divisions).
+    for (int j = 0; j < 16; ++j) {
+      d[j] = j < li ? Ls[(c + li) * LP + c + j] : 0.0f;
+      y[j] = j == li ? 1.0f : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (li == k) {
+        const float rk = rinv_s[c + k];
+#pragma unroll
+        for (int j = 0; j <= k; ++j) y[j] *= rk;
+      }
+      const float g = li > k ? d[k] : 0.0f;
+#pragma unroll
+      for (int j = 0; j <= k; ++j) y[j] = fmaf(-g, bcast(y[j], k), y[j]);
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) Xs[(c + li) * LP + c + j] = j <= li ? y[j] : 0.0f;
+    }
+  };
+
+#pragma unroll 1
+  for (int step = 0; step < NSTEP; ++step) {
+    const int c = 16 * step;
     if (wave == 0) {
-      const int li = lane & 15;
-      float d[16], rinv[16];
+      // (a) 16 x 16 diagonal block: Cholesky in registers.  The first bad
+      // pivot and the reciprocals are recorded after the loop (no branches
+      // inside it).
+      float d[16], rv[16];
+      const float* rowp = Ls + (c + li) * LP + c;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) d[j] = (j <= li) ? Ls[(c + li) * LP + c + j] : 0.0f;
+      for (int j = 0; j < 16; j += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(rowp + j);
+        d[j] = v.x; d[j + 1] = v.y; d[j + 2] = v.z; d[j + 3] = v.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) d[j] = j <= li ? d[j] : 0.0f;
+      int fail = -1;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const float dk = bcast(d[k], k);
-        if (lane == 0 && (!(dk > 0.0f) || !(dk < INFINITY)) && c + k < m)
-          atomicCAS(info, 0, (int32_t)(n - (off + c + k)));  // quantization-order column
+        if (fail < 0 && !(dk > 0.0f && dk < INFINITY) && c + k < m) fail = k;
         const float r = __builtin_amdgcn_rsqf(dk);
-        rinv[k] = r;                                   // 1 / L[k][k]
+        rv[k] = r;  // 1 / L[k][k]
         const float lik = li > k ? d[k] * r : (li == k ? dk * r : 0.0f);
         d[k] = lik;
         const float g = li > k ? lik : 0.0f;
 #pragma unroll
         for (int j = k + 1; j < 16; ++j) d[j] = fmaf(-g, bcast(lik, j), d[j]);
       }
-      // Y = L_D^-1, rows of Y broadcast with readlane (right-looking).
-      float y[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) y[j] = (j == li) ? 1.0f : 0.0f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        if (li == k) {
-#pragma unroll
-          for (int j = 0; j <= k; ++j) y[j] *= rinv[k];
-        }
-        const float g = li > k ? d[k] : 0.0f;
-#pragma unroll
-        for (int j = 0; j <= k; ++j) y[j] = fmaf(-g, bcast(y[j], k), y[j]);
-      }
       if (lane < 16) {
+        float* wrow = Ls + (c + li) * LP + c;
+#pragma unroll
+        for (int j = 0; j < 16; j += 4)
+          *reinterpret_cast<float4*>(wrow + j) = make_float4(j + 0 <= li ? d[j] : 0.0f, j + 1 <= li ? d[j + 1] : 0.0f,
+                                                           j + 2 <= li ? d[j + 2] : 0.0f, j + 3 <= li ? d[j + 3] : 0.0f);
+      }
+      if (lane == 0) {
+        if (fail >= 0) atomicCAS(info, 0, (int32_t)(n - (off + c + fail)));  // quantization-order column
+#pragma unroll
+        for (int k = 0; k < 16; ++k) rinv_s[c + k] = rv[k];
+      }
+    } else if (wave == 1 && step > 0) {
+      invert_block(step - 1);
+    }
+    __syncthreads();
+      const int rows = NB - c - 16;
+    if (rows > 0) {
+      // (b) L[i][c+j] = (A[i][c+j] - sum_{q<j} L[i][c+q] L[c+j][c+q]) / L[c+j][c+j]
+      if (tid < rows) {
+        float* row = Ls + (c + 16 + tid) * LP + c;
+        float x[16];
+#pragma unroll
+        for (int q = 0; q < 16; q += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(row + q);
+          x[q] = v.x; x[q + 1] = v.y; x[q + 2] = v.z; x[q + 3] = v.w;
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          Ls[(c + li) * LP + c + j] = j <= li ? d[j] : 0.0f;
-          Xs[(c + li) * LP + c + j] = j <= li ? y[j] : 0.0f;
-        }
-      }
-    }
-    __syncthreads();
-    const int rows = NB - c - 16;
-    if (rows > 0) {
-      // (2) panel solve: L[r][c+j] = sum_k A[r][c+k] * Dinv[j][k] (Dinv upper part is 0).
-      float res[3];
+          const float* lj = Ls + (c + j) * LP + c;  // same address in every lane
+          float sacc = x[j];
 #pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const int e = tid + 256 * q;
-        res[q] = 0.0f;
-        if (e < rows * 16) {
-          const int r = c + 16 + e / 16, j = e % 16;
-          res[q] = dot16(Ls + r * LP + c, Xs + (c + j) * LP + c);
+          for (int q = 0; q < j; ++q) sacc = fmaf(-x[q], lj[q], sacc);
+          x[j] = sacc * rinv_s[c + j];
         }
+#pragma unroll
+        for (int q = 0; q < 16; q += 4)
+          *reinterpret_cast<float4*>(row + q) = make_float4(x[q], x[q + 1], x[q + 2], x[q + 3]);
       }
       __syncthreads();
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const int e = tid + 256 * q;
-        if (e < rows * 16) Ls[(c + 16 + e / 16) * LP + c + e % 16] = res[q];
-      }
-      __syncthreads();
-      // (3) trailing update of the lower part: A[r][s] -= sum_k L[r][c+k] L[s][c+k].
-#pragma unroll
-      for (int q = 0; q < 9; ++q) {
-        const int e = tid + 256 * q;
-        if (e < rows * rows) {
-          const int r = c + 16 + e / rows, s2 = c + 16 + e % rows;
-          if (s2 <= r) Ls[r * LP + s2] -= dot16(Ls + r * LP + c, Ls + s2 * LP + c);
+          // (c) trailing update of the lower part, 16 x 16 tiles on the matrix cores:
+      //     A[r][s] -= sum_q L[r][c+q] L[s][c+q]   (r >= s >= c + 16)
+      {
+        const int nt = rows / 16, base = c + 16;
+        for (int t = wave; t < nt * (nt + 1) / 2; t += LEAF_THREADS / 64) {
+          int ti = 0;
+          while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+          const int tj = t - ti * (ti + 1) / 2;
+          float* C = Ls + (base + 16 * ti) * LP + base + 16 * tj;
+          f32x4_t acc = load_tile(C, lane);
+          acc = tile16<true>(Ls + (base + 16 * ti) * LP + c, Ls + (base + 16 * tj) * LP + c, 16, acc,
+                             -1.0f, lane);
+          store_tile(C, acc, lane);
         }
       }
       __syncthreads();
-    }
+        }
   }
+  if (wave == 1) invert_block(NSTEP - 1);
+  __syncthreads();
 
-  // Off-diagonal blocks of L^-1, one block row at a time:
-  //   T = L[r0.., 0..r0) X[0..r0, 0..r0)   (X lower: the sum can run over all k < r0)
-  //   X[r0.., 0..r0) = -Dinv_r0 T
+  // Off-diagonal blocks of X by doubling: for blocks of 2s (s = 16, 32, 64)
+  //   T = L21 X11 (into the X21 area), X21 = -X22 T,
+  // with every level's tiles spread over the 8 waves (16 x 16 MFMA tiles).
+#pragma unroll 1
+  for (int sz = 16; sz < NB; sz *= 2) {
+    const int per = (sz / 16) * (sz / 16), tiles = (NB / (2 * sz)) * per;
+    for (int t = wave; t < tiles; t += LEAF_THREADS / 64) {
+      const int o = (t / per) * 2 * sz, ti = (t % per) / (sz / 16), tj = (t % per) % (sz / 16);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = tile16<false>(Ls + (o + sz + 16 * ti) * LP + o, Xs + o * LP + o + 16 * tj, sz, acc,
+                          1.0f, lane);
+      store_tile(Xs + (o + sz + 16 * ti) * LP + o + 16 * tj, acc, lane);
+    }
+    __syncthreads();
+    constexpr int HOLD = (NB / 2 / 16) * (NB / 2 / 16) / (LEAF_THREADS / 64);  // tiles per wave, top level
+    f32x4_t res[HOLD];
 #pragma unroll
-  for (int pb = 1; pb < NB / 16; ++pb) {
-    const int r0 = 16 * pb, cols = r0;
-    float t[3];
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int e = tid + 256 * q;
-      t[q] = 0.0f;
-      if (e < 16 * cols) {
-        const int i = e / cols, j = e % cols;
-        const float* lrow = Ls + (r0 + i) * LP;
-        float acc = 0.0f;
-#pragma unroll
-        for (int k4 = 0; k4 < r0; k4 += 4) {
-          const float4 l = *reinterpret_cast<const float4*>(lrow + k4);
-          acc = fmaf(l.x, Xs[(k4 + 0) * LP + j], acc);
-          acc = fmaf(l.y, Xs[(k4 + 1) * LP + j], acc);
-          acc = fmaf(l.z, Xs[(k4 + 2) * LP + j], acc);
-          acc = fmaf(l.w, Xs[(k4 + 3) * LP + j], acc);
-        }
-        t[q] = acc;
+    for (int h = 0; h < HOLD; ++h) {
+      const int t = wave + h * (LEAF_THREADS / 64);
+      res[h] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      if (t < tiles) {
+        const int o = (t / per) * 2 * sz, ti = (t % per) / (sz / 16), tj = (t % per) % (sz / 16);
+        res[h] = tile16<false>(Xs + (o + sz + 16 * ti) * LP + o + sz, Xs + (o + sz) * LP + o + 16 * tj,
+                               sz, res[h], -1.0f, lane);
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int e = tid + 256 * q;
-      if (e < 16 * cols) Xs[(r0 + e / cols) * LP + e % cols] = t[q];  // T, scaled below
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int e = tid + 256 * q;
-      t[q] = 0.0f;
-      if (e < 16 * cols) {
-        const int i = e / cols, j = e % cols;
-        const float* drow = Xs + (r0 + i) * LP + r0;  // Dinv row i (upper part 0)
-        float acc = 0.0f;
-#pragma unroll
-        for (int l = 0; l < 16; ++l) acc = fmaf(drow[l], Xs[(r0 + l) * LP + j], acc);
-        t[q] = -acc;
+    for (int h = 0; h < HOLD; ++h) {
+      const int t = wave + h * (LEAF_THREADS / 64);
+      if (t < tiles) {
+        const int o = (t / per) * 2 * sz, ti = (t % per) / (sz / 16), tj = (t % per) % (sz / 16);
+        store_tile(Xs + (o + sz + 16 * ti) * LP + o + 16 * tj, res[h], lane);
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int e = tid + 256 * q;
-      if (e < 16 * cols) Xs[(r0 + e / cols) * LP + e % cols] = t[q];
     }
-    __syncthreads();
-  }
 
-  for (int e = tid; e < m * m; e += 256) {
-    const int i = e / m, j = e % m;
-    if (j <= i) {
-      A[(off + i) * n + off + j] = Ls[i * LP + j];
-      X[(off + i) * n + off + j] = Xs[i * LP + j];
-    }
+  for (int i = tid / NB; i < m; i += LEAF_THREADS / NB) {
+    const int j = tid % NB;
+    if (j <= i) X[(off + i) * n + off + j] = Xs[i * LP + j];
   }
 }
+
 
 // In place: U[i][j] = X[n-1-i][n-1-j] for i <= j, 0 below the diagonal, where
 // X = X' D (column b of the computed X' times dsc[b]).  X' is lower
@@ -472,8 +515,8 @@ hipError_t gemm(PrepCtx& c, int64_t M, int64_t N, int64_t K, const float* Am, in
 hipError_t cholinv(PrepCtx& c, int64_t off, int64_t m, float* t2) {
   const int64_t n = c.n;
   if (m <= NB) {
-    hipLaunchKernelGGL(cholinv_leaf_kernel, dim3(1), dim3(256), 0, c.s, c.A, c.X, n, off, (int)m,
-                       c.info);
+    hipLaunchKernelGGL(cholinv_leaf_kernel, dim3(1), dim3(LEAF_THREADS), 0, c.s, c.A, c.X, n, off,
+                       (int)m, c.info);
     return hipGetLastError();
   }
   const int64_t m1 = ((m / 2 + NB - 1) / NB) * NB;
