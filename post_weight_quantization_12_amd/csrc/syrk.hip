@@ -197,11 +197,10 @@ syrk_upper_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__
 // Lane L pointing at (token t0 + L/4, features f0 + 4*(L%4)) therefore gets
 // feature f0 + L at tokens t0..t0+3 -- one k-slot quarter of an A/B fragment.
 // Out-of-range tokens read as 0 through the buffer descriptor's size check.
-// 4 waves, each a 128 x 128 block of the 256 x 256 tile (16 accumulators).
-constexpr int DT = 256, DBK = 32, DS = 5, DNT = 256;
+// Waves split the 256 x 256 tile into 64 x 128 or 128 x 128 blocks (SyrkShape).
+constexpr int DT = 256, DBK = 32, DS = 5;
 constexpr int PANEL_BYTES = DBK * DT * 2;       // 16 KiB
 constexpr int STAGE_BYTES = 2 * PANEL_BYTES;    // A + B
-constexpr int DMA_PER_WAVE = 8;                 // 2 panels x 1024 chunks / 64 / 4 waves
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 __device__ inline v4i16_t ds_read_tr16(const char* lds_byte_ptr) {
@@ -280,8 +279,44 @@ struct StreamK {
 };
 constexpr int PART_FLOATS = DT * DT;
 
+// Waves per workgroup: 8 (two per SIMD, each a 64 x 128 block: 8
+// accumulators) for whole tiles -- the second wave on a SIMD keeps its matrix
+// pipe busy while the first waits at a barrier or on LDS (6-7 % faster than
+// one 128 x 128 wave per SIMD); 4 (one 128 x 128 block per wave) for the
+// stream-K variant, whose longer epilogue does not fit two waves' registers.
+template <bool STREAMK>
+struct SyrkShape {
+  static constexpr int NW = STREAMK ? 4 : 8;      // waves
+  static constexpr int WM = NW / 2;               // row blocks
+  static constexpr int FA = DT / WM / 32;         // 32-row A fragments per wave
+  static constexpr int FB = 4;                    // 32-column B fragments per wave
+  static constexpr int DMA = 2 * DT * DBK * 2 / 16 / 64 / NW;  // 16-byte loads per wave per stage
+};
+
+// One substep's MFMAs with the other substep's transposing LDS reads spread
+// between them (4 waves: 16 MFMAs / 16 reads; 8 waves: 8 MFMAs / 12 reads).
+// A macro: the scheduling builtins need literal group ids.
+#define GPTQ_SYRK_INTERLEAVE(FA, ID)                                  \
+  do {                                                                \
+    if constexpr ((FA) == 4) {                                        \
+      _Pragma("unroll") for (int i_ = 0; i_ < 16; ++i_) {             \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);           \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);           \
+      }                                                               \
+    } else {                                                          \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {              \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);           \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, ID);           \
+      }                                                               \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {              \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);           \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);           \
+      }                                                               \
+    }                                                                 \
+  } while (0)
+
 template <bool BF16, bool STREAMK>
-__global__ void __launch_bounds__(DNT)
+__global__ void __launch_bounds__(SyrkShape<STREAMK>::NW * 64)
 syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X, int64_t ntok,
                 int64_t ldx, StreamK sk) {
   // One LDS object per stage: the compiler then tracks each stage's direct
@@ -297,7 +332,10 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   const int nk = (int)((ntok + DBK - 1) / DBK);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  using SS = SyrkShape<STREAMK>;
+  constexpr int FA = SS::FA, FB = SS::FB, DMA_PER_WAVE = SS::DMA, RW = DT / SS::WM;
+  static_assert(FA <= 4 && FB <= 4 && DMA_PER_WAVE <= 8, "array sizes below");
+  const int wm = wave % SS::WM, wn = wave / SS::WM;
 
   // Transposing-read byte offsets within a panel, per lane (substep 0, first 4 tokens).
   const int g = lane >> 4, L = lane & 15;
@@ -305,15 +343,18 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   const int cx = 2 * (g & 1) + ((L & 3) >> 1);            // chunk within a 32-feature fragment
   const int half8 = (L & 1) * 8;
   const int xsw = 4 * (L >> 2);                           // = 4 * (trow % 4)
+  // Arrays have literal sizes (4 / 8, the 4-wave maxima): with sizes that
+  // depend on the template parameter the host compiler emits no kernel.
   int aoff[4], boff[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    aoff[f] = (trow * 32 + ((wm * 16 + f * 4 + cx) ^ xsw)) * 16 + half8;
+  for (int f = 0; f < FA; ++f)
+    aoff[f] = (trow * 32 + ((wm * (RW / 8) + f * 4 + cx) ^ xsw)) * 16 + half8;
+#pragma unroll
+  for (int f = 0; f < FB; ++f)
     boff[f] = PANEL_BYTES + (trow * 32 + ((wn * 16 + f * 4 + cx) ^ xsw)) * 16 + half8;
-  }
 
   f32x16_t acc[4][4];
-  uint32_t voff[DMA_PER_WAVE];
+  uint32_t voff[8];
   int64_t tok_end = ntok;
 
   auto issue = [&](int st, char* stage) {
@@ -326,7 +367,7 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
         __builtin_amdgcn_make_buffer_rsrc((void*)rbase, (short)0, (int)num, 0x00020000);
 #pragma unroll
     for (int q = 0; q < DMA_PER_WAVE; ++q) {
-      const int panel = q / 4, cb = wave * 4 + (q % 4);
+      const int gq = wave * DMA_PER_WAVE + q, panel = gq / 16, cb = gq % 16;
       char* dst = stage + panel * PANEL_BYTES + cb * 64 * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) char*)dst),
@@ -342,21 +383,23 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   auto load = [&](Frags& F, const char* stage, int sub) {
     const int so = sub * 16 * 32 * 16;  // 16 token rows
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < FA; ++f) {
       F.alo[f] = ds_read_tr16(stage + so + aoff[f]);
       F.ahi[f] = ds_read_tr16(stage + so + aoff[f] + 4 * 32 * 16);
+    }
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
       F.blo[f] = ds_read_tr16(stage + so + boff[f]);
       F.bhi[f] = ds_read_tr16(stage + so + boff[f] + 4 * 32 * 16);
     }
   };
   auto mma = [&](const Frags& F) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < FA; ++a)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < FB; ++c)
         acc[a][c] = mfma_tr<BF16>(F.alo[a], F.ahi[a], F.blo[c], F.bhi[c], acc[a][c]);
   };
-
   // Software pipeline.  Per stage k (buffer `cur`, next stage in `nxt`):
   //   read substep 1 of k | MFMAs of substep 0 of k
   //   wait: own LDS reads done, own loads of stage k+1 landed (three later
@@ -367,17 +410,13 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   // read as zeros and add nothing), so the loop has no data-dependent branches
   // and the compiler tracks each stage buffer's loads exactly.
   Frags F0, F1;
-  // Each substep's 16 transposing LDS reads are issued one after each of the
-  // other substep's 16 MFMAs, so the wave never sits on a block of reads
-  // while its matrix pipe drains (4% at n = 11008).
+  // Each substep's transposing LDS reads are issued between the other
+  // substep's MFMAs, so the wave never sits on a block of reads while its
+  // matrix pipe drains (4 % at n = 11008).
   auto stage_step = [&](int k, char* cur, const char* nxt) {
     load(F1, cur, 1);
     mma(F0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    }
+    GPTQ_SYRK_INTERLEAVE(FA, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkm0();
     wait_vmcnt<(DS - 2) * DMA_PER_WAVE>();
@@ -386,11 +425,7 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
     __builtin_amdgcn_sched_barrier(0);
     load(F0, nxt, 0);
     mma(F1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-    }
+    GPTQ_SYRK_INTERLEAVE(FA, 1);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -398,7 +433,7 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   auto run = [&](int64_t i0, int64_t j0, int k0, int k1) {
 #pragma unroll
     for (int q = 0; q < DMA_PER_WAVE; ++q) {
-      const int panel = q / 4, cb = wave * 4 + (q % 4);
+      const int gq = wave * DMA_PER_WAVE + q, panel = gq / 16, cb = gq % 16;
       const int p = cb * 64 + lane;
       const int t = p / 32, c = (p % 32) ^ (4 * (t % 4));
       const int64_t col = (panel ? j0 : i0) + 8 * c;
@@ -406,9 +441,9 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
     }
     tok_end = (int64_t)k1 * DBK < ntok ? (int64_t)k1 * DBK : ntok;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < FA; ++a)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < FB; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
     issue(k0 + 0, st0);
@@ -442,15 +477,15 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
     __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(H + i0 * n + j0), (short)0, num, 0x00020000);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < FA; ++a)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < FB; ++c) {
         const int jl = wn * 128 + c * 32 + (lane & 31);
         uint32_t off[16];
         float hv[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int il = wm * 128 + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const int il = wm * RW + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
           const bool in = i0 + il < n && j0 + jl < n && i0 + il <= j0 + jl;
           off[v] = in ? (uint32_t)(((int64_t)il * n + jl) * 4) : 0x80000000u;
           hv[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)off[v], 0, 0));
@@ -465,13 +500,13 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   // A partial tile: acc stored row-major (256 x 256) to `part`.
   auto store_part = [&](float* part) __attribute__((always_inline)) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < FA; ++a)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < FB; ++c) {
         const int jl = wn * 128 + c * 32 + (lane & 31);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int il = wm * 128 + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const int il = wm * RW + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
           part[il * DT + jl] = acc[a][c][v];
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -594,7 +629,8 @@ hipError_t launch_syrk(float* H, int64_t n, const void* X, int dtype, int64_t nt
       sk.partial = static_cast<float*>(ws);
       sk.units = (tiles * nk + nwg - 1) / nwg;
       auto kern = bf ? syrk_dma_kernel<true, true> : syrk_dma_kernel<false, true>;
-      hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(DNT), 0, s, H, n, x, ntok, ldx, sk);
+      hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(SyrkShape<true>::NW * 64), 0, s, H, n, x,
+                         ntok, ldx, sk);
       GPTQ_HIP_TRY(hipGetLastError());
       if (sk.units < nk)
         hipLaunchKernelGGL(syrk_streamk_fixup, dim3((unsigned)tiles, DT / FIX_ROWS), dim3(DT), 0,
@@ -603,7 +639,8 @@ hipError_t launch_syrk(float* H, int64_t n, const void* X, int dtype, int64_t nt
     }
     const int64_t blocks = (tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
     auto kern = bf ? syrk_dma_kernel<true, false> : syrk_dma_kernel<false, false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(DNT), 0, s, H, n, x, ntok, ldx, sk);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(SyrkShape<false>::NW * 64), 0, s, H, n, x,
+                       ntok, ldx, sk);
     return hipGetLastError();
   }
   // Unaligned rows: register-staged kernel with element loads.
