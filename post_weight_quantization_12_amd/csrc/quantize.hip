@@ -407,11 +407,249 @@ pack_kernel(const uint8_t* __restrict__ codes, const int32_t* __restrict__ pinv,
   }
 }
 
+// Sweep with 16 lanes per row (group sizes that are multiples of 16, or one
+// group per row): lane q of a row's 16-lane DPP row holds block columns
+// 16r + q (r < B/16) as a sliding window (w[t] = column 16(R + t) + q at step
+// R), the owning lane's value is broadcast with DPP row_newbcast (one VALU
+// op), group min/max reduce over the 16 lanes with DPP, and the U' window is
+// stored pre-shifted per lane:
+//     Ul[j][q][t] = U'[c0 + j][c0 + 16(j/16 + t) + q]   (0 unless right of j).
+// Four times the lanes of the quad layout per row: 4x fewer updates per lane
+// and per column, and 4x the rows in flight.
+constexpr int S16_THREADS = 256;
+constexpr int S16_ROWS = S16_THREADS / 16;
+
+template <int B>
+struct Sweep16Smem {
+  static constexpr int NR = B / 16, PITCH = (NR + 4 + 3) / 4 * 4, EP = B + 4;
+  static constexpr size_t UL = (size_t)B * 16 * PITCH;  // floats
+  static constexpr size_t ES = (size_t)S16_ROWS * EP;    // floats
+  static constexpr size_t BYTES = (UL + ES) * sizeof(float) + (size_t)S16_ROWS * B;
+};
+
+// Value of lane o of each 16-lane row, to every lane of the row (o constant
+// after unrolling).
+__device__ inline float row_bcast16(float v, int o) {
+  const int x = __float_as_int(v);
+  int r;
+  switch (o) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, x, 0x150, 0xF, 0xF, false); break;
+    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x151, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x152, 0xF, 0xF, false); break;
+    case 3: r = __builtin_amdgcn_update_dpp(0, x, 0x153, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, x, 0x154, 0xF, 0xF, false); break;
+    case 5: r = __builtin_amdgcn_update_dpp(0, x, 0x155, 0xF, 0xF, false); break;
+    case 6: r = __builtin_amdgcn_update_dpp(0, x, 0x156, 0xF, 0xF, false); break;
+    case 7: r = __builtin_amdgcn_update_dpp(0, x, 0x157, 0xF, 0xF, false); break;
+    case 8: r = __builtin_amdgcn_update_dpp(0, x, 0x158, 0xF, 0xF, false); break;
+    case 9: r = __builtin_amdgcn_update_dpp(0, x, 0x159, 0xF, 0xF, false); break;
+    case 10: r = __builtin_amdgcn_update_dpp(0, x, 0x15A, 0xF, 0xF, false); break;
+    case 11: r = __builtin_amdgcn_update_dpp(0, x, 0x15B, 0xF, 0xF, false); break;
+    case 12: r = __builtin_amdgcn_update_dpp(0, x, 0x15C, 0xF, 0xF, false); break;
+    case 13: r = __builtin_amdgcn_update_dpp(0, x, 0x15D, 0xF, 0xF, false); break;
+    case 14: r = __builtin_amdgcn_update_dpp(0, x, 0x15E, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, x, 0x15F, 0xF, 0xF, false); break;
+  }
+  return __int_as_float(r);
+}
+// Min / max over a 16-lane row (quad swaps, then rotations by 4 and 8).
+__device__ inline float row_min16(float v) {
+  v = fminf(v, dpp_xor1(v));
+  v = fminf(v, dpp_xor2(v));
+  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  return v;
+}
+__device__ inline float row_max16(float v) {
+  v = fmaxf(v, dpp_xor1(v));
+  v = fmaxf(v, dpp_xor2(v));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  return v;
+}
+
+template <int B, int GS>
+__global__ void __launch_bounds__(S16_THREADS)
+sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, int64_t in,
+               int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
+               int32_t* __restrict__ zeros, uint8_t* __restrict__ codes,
+               float* __restrict__ emax) {
+  using SM = Sweep16Smem<B>;
+  constexpr int NR = SM::NR, PITCH = SM::PITCH, EP = SM::EP;
+  static_assert(GS % 16 == 0, "group size a multiple of 16 (0: one group per row)");
+  extern __shared__ __align__(16) float smem16[];
+  float* Ul = smem16;
+  float* Es = smem16 + SM::UL;
+  uint8_t* Cs = reinterpret_cast<uint8_t*>(Es + SM::ES);
+
+  const int tid = threadIdx.x;
+  const int q = tid & 15, rl = tid >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * S16_ROWS;
+  const int64_t row = row0 + rl;
+  const bool live = row < out;
+
+  // Pre-shifted U' window.  Item (j, t, h): the float4 of block columns
+  // 16(j/16 + t) + 4h .. +3 of U' row c0 + j, spread to lanes 4h .. 4h+3;
+  // columns not right of j are stored as 0.
+  {
+    constexpr int ITEMS = B * NR * 4;
+    constexpr int PER = ITEMS / S16_THREADS;
+    static_assert(ITEMS % S16_THREADS == 0, "whole items per thread");
+#pragma unroll
+    for (int p0 = 0; p0 < PER; p0 += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = tid + (p0 + u) * S16_THREADS;
+        const int j = e / (NR * 4), t = (e / 4) % NR, h = e % 4;
+        const int c = 16 * (j / 16 + t) + 4 * h;
+        v[u] = (p0 + u < PER && j < width && c < width)
+                   ? *reinterpret_cast<const float4*>(Up + (c0 + j) * in + c0 + c)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (p0 + u < PER) {
+          const int e = tid + (p0 + u) * S16_THREADS;
+          const int j = e / (NR * 4), t = (e / 4) % NR, h = e % 4;
+          const int c = 16 * (j / 16 + t) + 4 * h;
+          float* d = Ul + (j * 16 + 4 * h) * PITCH + t;
+          d[0 * PITCH] = c + 0 > j ? v[u].x : 0.0f;
+          d[1 * PITCH] = c + 1 > j ? v[u].y : 0.0f;
+          d[2 * PITCH] = c + 2 > j ? v[u].z : 0.0f;
+          d[3 * PITCH] = c + 3 > j ? v[u].w : 0.0f;
+        }
+      }
+    }
+  }
+
+  float w[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int col = 16 * r + q;
+    w[r] = (live && col < width) ? Wp[row * in + c0 + col] : 0.0f;
+  }
+  const float maxq = (float)((1 << bits) - 1);
+  float s = 1.0f, z = 0.0f;
+  if constexpr (GS == 0) {
+    if (live) {
+      s = scales[row];
+      z = (float)zeros[row];
+    }
+  }
+  __syncthreads();
+
+  const int nsteps = width / 16;
+  for (int R = 0; R < nsteps; ++R) {
+    if constexpr (GS > 0) {
+      if ((16 * R) % GS == 0) {
+        // range of the group's current values, 0 included
+        float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+        for (int t = 0; t < GS / 16; ++t) {
+          lo = fminf(lo, w[t]);
+          hi = fmaxf(hi, w[t]);
+        }
+        lo = row_min16(lo);
+        hi = row_max16(hi);
+        grid_params(lo, hi, bits, sym, s, z);
+        if (live && q == 0) {
+          const int64_t g = (c0 + 16 * R) / GS;
+          scales[g * out + row] = s;
+          zeros[g * out + row] = (int32_t)z;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 0; o < 16; ++o) {
+      const int j = 16 * R + o;
+      const float wj = row_bcast16(w[0], o);
+      const float qf = fminf(fmaxf(rintf(wj / s) + z, 0.0f), maxq);
+      const float err = wj - s * (qf - z);
+      if (q == o) {
+        Es[rl * EP + j] = err;
+        Cs[rl * B + j] = (uint8_t)qf;
+      }
+      const float* urow = Ul + (j * 16 + q) * PITCH;
+#pragma unroll
+      for (int t = 0; t < NR; t += 4) {
+        const float4 u = *reinterpret_cast<const float4*>(urow + t);
+        w[t + 0] = fmaf(-err, u.x, w[t + 0]);
+        if (t + 1 < NR) w[t + 1] = fmaf(-err, u.y, w[t + 1]);
+        if (t + 2 < NR) w[t + 2] = fmaf(-err, u.z, w[t + 2]);
+        if (t + 3 < NR) w[t + 3] = fmaf(-err, u.w, w[t + 3]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t + 1 < NR; ++t) w[t] = w[t + 1];
+    w[NR - 1] = 0.0f;
+  }
+  __syncthreads();
+
+  // Largest |error| of each row in this block (sizes the split products of
+  // the trailing GEMMs).
+  {
+    float m = 0.0f;
+    for (int c = q; c < width; c += 16) m = fmaxf(m, fabsf(Es[rl * EP + c]));
+    m = row_max16(m);
+    if (live && q == 0) emax[(c0 / B) * out + row] = m;
+  }
+  // Errors (read by the trailing GEMMs) and codes, written out row-contiguous.
+  const int wq = width / 4;
+  for (int e = tid; e < S16_ROWS * wq; e += S16_THREADS) {
+    const int r = e / wq, c = (e % wq) * 4;
+    if (row0 + r < out)
+      *reinterpret_cast<float4*>(Wp + (row0 + r) * in + c0 + c) =
+          *reinterpret_cast<const float4*>(Es + r * EP + c);
+  }
+  const int w16 = width / 16;
+  for (int e = tid; e < S16_ROWS * w16; e += S16_THREADS) {
+    const int r = e / w16, c = (e % w16) * 16;
+    if (row0 + r < out)
+      *reinterpret_cast<uint4*>(codes + (row0 + r) * in + c0 + c) =
+          *reinterpret_cast<const uint4*>(Cs + r * B + c);
+  }
+}
+
+template <int B, int GS>
+hipError_t launch_sweep16(float* Wp, const float* Up, int64_t out, int64_t in, int64_t c0,
+                          int width, int bits, int sym, float* scales, int32_t* zeros,
+                          uint8_t* codes, float* emax, hipStream_t s) {
+  auto k = sweep16_kernel<B, GS>;
+  const size_t lds = Sweep16Smem<B>::BYTES;
+  GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)lds));
+  hipLaunchKernelGGL(k, dim3((unsigned)((out + S16_ROWS - 1) / S16_ROWS)), dim3(S16_THREADS), lds,
+                     s, Wp, Up, out, in, c0, width, bits, sym, scales, zeros, codes, emax);
+  return hipGetLastError();
+}
+
 template <int B>
 hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t in, int64_t c0,
                         int width, int bits, int sym, float* scales, int32_t* zeros,
                         uint8_t* codes, float* emax, hipStream_t s) {
   if (gs > B) return hipErrorInvalidValue;
+  // 16 lanes per row where the group size allows it.
+  switch (gs > 0 ? gs : 0) {
+    case 0: return launch_sweep16<B, 0>(Wp, Up, out, in, c0, width, bits, sym, scales, zeros,
+                                        codes, emax, s);
+    case 16: return launch_sweep16<B, 16>(Wp, Up, out, in, c0, width, bits, sym, scales, zeros,
+                                          codes, emax, s);
+    case 32: return launch_sweep16<B, 32>(Wp, Up, out, in, c0, width, bits, sym, scales, zeros,
+                                          codes, emax, s);
+    case 64:
+      if constexpr (B >= 64)
+        return launch_sweep16<B, (B >= 64 ? 64 : 16)>(Wp, Up, out, in, c0, width, bits, sym,
+                                                       scales, zeros, codes, emax, s);
+      break;
+    case 128:
+      if constexpr (B >= 128)
+        return launch_sweep16<B, (B >= 128 ? 128 : 16)>(Wp, Up, out, in, c0, width, bits, sym,
+                                                         scales, zeros, codes, emax, s);
+      break;
+    default:
+      break;
+  }
   dim3 grid((unsigned)((out + SW_ROWS - 1) / SW_ROWS)), block(SW_THREADS);
   const size_t lds = SweepSmem<B>::BYTES;
 #define GPTQ_SWEEP_CASE(G)                                                                     \
