@@ -66,9 +66,9 @@ struct GemmArgs {
   int kmode;
   bool lower_only;  // compute only tiles that touch the lower triangle (i >= j)
   // Products as three fp16 MFMAs on split operands (x = hi + lo, both fp16;
-  // the lo*lo term dropped), fp32 accumulation: about 2^-22 relative per
-  // product for operands of magnitude ~1 (values must stay below 65504 and
-  // are resolved down to ~2^-24 absolute).  Used only where the operands are
+  // the lo*lo term dropped), fp32 accumulation: about 2^-20 relative per
+  // operand for values of magnitude ~1 (values must stay below 65504 and are
+  // resolved down to ~2^-24 absolute).  Used only where the operands are
   // scaled to that range; falls back to fp32 MFMAs on unaligned shapes.
   bool split16 = false;
   // With split16: optional per-row powers of two for op(A) (length M).  Row i

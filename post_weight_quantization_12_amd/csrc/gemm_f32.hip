@@ -263,15 +263,23 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num, 0x00020000);
 }
 
-// 16 fp32 values -> fp16 high parts and fp16 rounded remainders, as two
-// 8-element MFMA operands each.
+// 16 fp32 values -> fp16 high parts and fp16 remainders, as two 8-element
+// MFMA operands each.  hi = x with the mantissa cut to 10 bits (exact in
+// fp16 in its normal range), lo = x - hi (exact in fp32) rounded toward zero
+// to fp16: |x - hi - lo| <= 2^-20 |x| there, and <= 2^-24 in absolute terms
+// below it.  Three VALU ops per value (and, sub, half of two packed cvts).
 __device__ __attribute__((always_inline)) inline void split16(const float (&v)[16], half8_t (&hi)[2],
                                                               half8_t (&lo)[2]) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const _Float16 x = (_Float16)v[e];
-    hi[e >> 3][e & 7] = x;
-    lo[e >> 3][e & 7] = (_Float16)(v[e] - (float)x);
+  for (int e = 0; e < 16; e += 2) {
+    const float h0 = __uint_as_float(__float_as_uint(v[e]) & 0xFFFFE000u);
+    const float h1 = __uint_as_float(__float_as_uint(v[e + 1]) & 0xFFFFE000u);
+    const auto hp = __builtin_amdgcn_cvt_pkrtz(h0, h1);
+    const auto lp = __builtin_amdgcn_cvt_pkrtz(v[e] - h0, v[e + 1] - h1);
+    hi[e >> 3][e & 7] = hp[0];
+    hi[e >> 3][(e & 7) + 1] = hp[1];
+    lo[e >> 3][e & 7] = lp[0];
+    lo[e >> 3][(e & 7) + 1] = lp[1];
   }
 }
 
@@ -390,8 +398,8 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
           for (int c = 0; c < FN; ++c)
             acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a][u], bv[c][u], acc[a][c], 0, 0, 0);
     } else {
-      // Split fp16 products: x = hi + lo (hi = fp16(x), lo = fp16(x - hi)),
-      // a b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi with fp32 accumulation.  MFMA
+      // Split fp16 products: x = hi + lo (split16), a b ~ a_hi b_hi +
+      // a_hi b_lo + a_lo b_hi with fp32 accumulation.  MFMA
       // k-step q (16 k) takes this lane's values 8q..8q+7 (k = 16h + 8q + e).
       half8_t ah[FM][2], al[FM][2], bh[FN][2], bl[FN][2];
 #pragma unroll
