@@ -55,8 +55,9 @@ typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype_t;
 #define GPTQ_MAX_PREPARE_N 32768
 
 /* Workspace (bytes) gptq_hessian_accumulate can use for order n on the
- * current device (two 256 x 256 fp32 partial tiles per compute unit plus one
- * counter per tile; 0 if n < 1). */
+ * current device: two 256 x 256 fp32 partial tiles for each workgroup of the
+ * token-split schedule (one workgroup per compute unit, at most 512; about
+ * 128 MiB on a 256-CU device).  The size does not depend on n. */
 size_t gptq_hessian_workspace_bytes(int64_t n);
 
 /*
