@@ -279,39 +279,32 @@ struct StreamK {
 };
 constexpr int PART_FLOATS = DT * DT;
 
-// Waves per workgroup: 8 (two per SIMD, each a 64 x 128 block: 8
-// accumulators) for whole tiles -- the second wave on a SIMD keeps its matrix
-// pipe busy while the first waits at a barrier or on LDS (6-7 % faster than
-// one 128 x 128 wave per SIMD); 4 (one 128 x 128 block per wave) for the
-// stream-K variant, whose longer epilogue does not fit two waves' registers.
+// Waves per workgroup: 8, two per SIMD, each a 64 x 128 block (8
+// accumulators): the second wave on a SIMD keeps its matrix pipe busy while
+// the first waits at a barrier or on LDS (6-7 % faster on whole tiles than
+// one 128 x 128 wave per SIMD, 11 % under stream-K at n = 4096).
 template <bool STREAMK>
 struct SyrkShape {
-  static constexpr int NW = STREAMK ? 4 : 8;      // waves
+  static constexpr int NW = 8;                    // waves
   static constexpr int WM = NW / 2;               // row blocks
   static constexpr int FA = DT / WM / 32;         // 32-row A fragments per wave
   static constexpr int FB = 4;                    // 32-column B fragments per wave
   static constexpr int DMA = 2 * DT * DBK * 2 / 16 / 64 / NW;  // 16-byte loads per wave per stage
 };
 
-// One substep's MFMAs with the other substep's transposing LDS reads spread
-// between them (4 waves: 16 MFMAs / 16 reads; 8 waves: 8 MFMAs / 12 reads).
-// A macro: the scheduling builtins need literal group ids.
+// One substep's MFMAs (8 per wave) with the other substep's 12 transposing
+// LDS reads spread between them.  A macro: the scheduling builtins need
+// literal group ids.
 #define GPTQ_SYRK_INTERLEAVE(FA, ID)                                  \
   do {                                                                \
-    if constexpr ((FA) == 4) {                                        \
-      _Pragma("unroll") for (int i_ = 0; i_ < 16; ++i_) {             \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);           \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);           \
-      }                                                               \
-    } else {                                                          \
-      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {              \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);           \
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, ID);           \
-      }                                                               \
-      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {              \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);           \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);           \
-      }                                                               \
+    static_assert((FA) == 2, "schedule written for 64 x 128 blocks"); \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);             \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, ID);             \
+    }                                                                 \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);             \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);             \
     }                                                                 \
   } while (0)
 
@@ -334,7 +327,7 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   using SS = SyrkShape<STREAMK>;
   constexpr int FA = SS::FA, FB = SS::FB, DMA_PER_WAVE = SS::DMA, RW = DT / SS::WM;
-  static_assert(FA <= 4 && FB <= 4 && DMA_PER_WAVE <= 8, "array sizes below");
+  static_assert(FA == 2 && FB == 4 && DMA_PER_WAVE == 4, "array sizes below");
   const int wm = wave % SS::WM, wn = wave / SS::WM;
 
   // Transposing-read byte offsets within a panel, per lane (substep 0, first 4 tokens).
@@ -343,9 +336,9 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   const int cx = 2 * (g & 1) + ((L & 3) >> 1);            // chunk within a 32-feature fragment
   const int half8 = (L & 1) * 8;
   const int xsw = 4 * (L >> 2);                           // = 4 * (trow % 4)
-  // Arrays have literal sizes (4 / 8, the 4-wave maxima): with sizes that
-  // depend on the template parameter the host compiler emits no kernel.
-  int aoff[4], boff[4];
+  // Arrays have literal sizes: with sizes that depend on the template
+  // parameter the host compiler emits no kernel.
+  int aoff[2], boff[4];
 #pragma unroll
   for (int f = 0; f < FA; ++f)
     aoff[f] = (trow * 32 + ((wm * (RW / 8) + f * 4 + cx) ^ xsw)) * 16 + half8;
@@ -353,8 +346,8 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   for (int f = 0; f < FB; ++f)
     boff[f] = PANEL_BYTES + (trow * 32 + ((wn * 16 + f * 4 + cx) ^ xsw)) * 16 + half8;
 
-  f32x16_t acc[4][4];
-  uint32_t voff[8];
+  f32x16_t acc[2][4];
+  uint32_t voff[4];
   int64_t tok_end = ntok;
 
   // Logical stage st of the current segment [seg_k0, seg_k1) reads token
@@ -383,7 +376,7 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   // Operands of one 16-token substep: 4 A and 4 B fragments, two 4-token
   // halves each.
   struct Frags {
-    v4i16_t alo[4], ahi[4], blo[4], bhi[4];
+    v4i16_t alo[2], ahi[2], blo[4], bhi[4];
   };
   auto load = [&](Frags& F, const char* stage, int sub) {
     const int so = sub * 16 * 32 * 16;  // 16 token rows
@@ -485,16 +478,21 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
     const int num = rem < 0x7FFFFFF0LL ? (int)rem : 0x7FFFFFF0;
     __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(H + i0 * n + j0), (short)0, num, 0x00020000);
+    // Under stream-K, an opaque copy of the lane index: inside the loop over
+    // segments the compiler would otherwise hoist all 128 element offsets
+    // (loop invariant) above the loop and spill them.
+    int ln = lane;
+    if constexpr (STREAMK) asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int a = 0; a < FA; ++a)
 #pragma unroll
       for (int c = 0; c < FB; ++c) {
-        const int jl = wn * 128 + c * 32 + (lane & 31);
+        const int jl = wn * 128 + c * 32 + (ln & 31);
         uint32_t off[16];
         float hv[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int il = wm * RW + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const int il = wm * RW + a * 32 + (v >> 2) * 8 + (ln >> 5) * 4 + (v & 3);
           const bool in = i0 + il < n && j0 + jl < n && i0 + il <= j0 + jl;
           off[v] = in ? (uint32_t)(((int64_t)il * n + jl) * 4) : 0x80000000u;
           hv[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)off[v], 0, 0));
@@ -508,14 +506,16 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
   };
   // A partial tile: acc stored row-major (256 x 256) to `part`.
   auto store_part = [&](float* part) __attribute__((always_inline)) {
+    int ln = lane;  // opaque, as in store_h
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int a = 0; a < FA; ++a)
 #pragma unroll
       for (int c = 0; c < FB; ++c) {
-        const int jl = wn * 128 + c * 32 + (lane & 31);
+        const int jl = wn * 128 + c * 32 + (ln & 31);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int il = wm * RW + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const int il = wm * RW + a * 32 + (v >> 2) * 8 + (ln >> 5) * 4 + (v & 3);
           part[il * DT + jl] = acc[a][c][v];
         }
         __builtin_amdgcn_sched_barrier(0);
