@@ -2,7 +2,8 @@
 
 One step = the whole per-layer path on one batch of synthetic calibration
 data already resident in HBM:
-    H = 0; H += 2 X_c^T X_c for every chunk (gptq_hessian_accumulate)
+    H = 0; H += 2 X^T X over all calibration tokens (one
+    gptq_hessian_accumulate call by default; --chunk-samples streams chunks)
     gptq_prepare (damp, desc_act order, U = chol(H_p^-1) upper)
     gptq_quantize_layer (sweep + lazy GEMMs + pack)
 value = weights quantized per second = out * in / step time.
@@ -13,6 +14,11 @@ group 128, damp 0.01, block 128).  --config c3 selects the 4096 x 11008
 down_proj layer, c4a / c4b the 8192 x 28672 70B down_proj layer.
 
 Prints ONE JSON line (rank 0; this build is single-GPU).
+
+--summarize DIR (no GPU): turns the rocprofv3 output of the profiling
+commands (DIR/trace, DIR/FETCH_SIZE, DIR/WRITE_SIZE, see PROFILE_COMMANDS)
+into profiles/layer_<config>_kernel_stats.md and
+profiles/syrk_<config>_traffic.json.
 """
 from __future__ import annotations
 
@@ -40,9 +46,10 @@ def kernel_source_sha(name: str) -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(kernel_file: str, workload: str, launch_units: float):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    --pmc summary, or None when there is none or the kernel source changed."""
+def load_traffic(kernel_file: str, workload: str, call_tokens: int):
+    """HBM bytes per gptq_hessian_accumulate call from the committed rocprofv3
+    --pmc summary, or None when there is none, it was taken with another call
+    size, or the kernel source changed since."""
     path = os.path.join(ROOT, "profiles", f"syrk_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -52,20 +59,123 @@ def load_traffic(kernel_file: str, workload: str, launch_units: float):
         return None
     if d.get("source_sha") != kernel_source_sha(kernel_file):
         return None
-    return float(d["hbm_bytes_per_launch"])
+    if d.get("call_tokens") != call_tokens:
+        return None
+    return float(d["hbm_bytes_per_call"])
 
 
-def syrk_kernel_name(n: int) -> str:
-    """Kernels one gptq_hessian_accumulate launch runs (with a workspace): the
-    stream-K schedule adds a fix-up kernel when 256 x 256 tiles would leave
-    more than a quarter of the compute units idle."""
-    import torch
+def syrk_schedule(n: int, ntok: int, cus: int):
+    """(kernels, launches) of one gptq_hessian_accumulate call with a
+    workspace, following the library's choice (syrk.hip, launch_syrk): whole
+    256 x 256 tiles (one launch per 32768 tokens) when they fill the
+    workgroup rounds to 90 %, else the token-split schedule for calls of at
+    least 256 stages of 32 tokens per token block, else stream-K."""
+    nwg = min(max(cus // 8 * 8, 8), 512)
     nt = (n + 255) // 256
     tiles = nt * (nt + 1) // 2
-    cus = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
-    if 4 * tiles < 3 * min(cus, 512):
-        return "syrk_dma_kernel + syrk_streamk_fixup (gptq_hessian_accumulate, stream-K)"
-    return "syrk_dma_kernel (gptq_hessian_accumulate)"
+    nk = (ntok + 31) // 32
+    rounds = (tiles + nwg - 1) // nwg
+    if 10 * tiles < 9 * rounds * nwg:
+        blocks = 1
+        while blocks < 8 and tiles * blocks // 8 < 4 * (nwg // 8):
+            blocks *= 2
+        if nk // blocks >= 256:
+            return (f"syrk_dma_kernel + syrk_ksplit_fixup (token split, {blocks} blocks)", 1)
+        if 4 * tiles < 3 * nwg:
+            return ("syrk_dma_kernel + syrk_streamk_fixup (stream-K)", 1)
+    launches = (ntok + 32767) // 32768
+    return (f"syrk_dma_kernel (whole tiles, {launches} launches of <= 32768 tokens)", launches)
+
+
+PROFILE_COMMANDS = {
+    "trace": ("rocprofv3 --kernel-trace --stats -T -d {d}/trace -o t --output-format csv -- "
+              "python -u bench.py --config {c} --steps 2 --warmup 1 --no-cpu-baseline"),
+    "FETCH_SIZE": ("rocprofv3 --pmc FETCH_SIZE -T -d {d}/FETCH_SIZE -o p --output-format csv -- "
+                   "python -u bench.py --config {c} --steps 1 --warmup 0 --no-cpu-baseline "
+                   "--copy-probe"),
+    "WRITE_SIZE": ("rocprofv3 --pmc WRITE_SIZE -T -d {d}/WRITE_SIZE -o p --output-format csv -- "
+                   "python -u bench.py --config {c} --steps 1 --warmup 0 --no-cpu-baseline "
+                   "--copy-probe"),
+}
+
+
+def summarize(cfg_name: str, d: str):
+    """Write the profiles/ summaries from rocprofv3 CSV output in d (the
+    PROFILE_COMMANDS run with the default call size).  FETCH_SIZE and
+    WRITE_SIZE are scaled by what they read for the 1 GiB device copy that
+    --copy-probe runs (a kernel of known traffic)."""
+    import csv
+    import workloads
+    cfg = workloads.get(cfg_name)
+    n = cfg.inp
+    shape = (f"W {cfg.out}x{n}, {cfg.bits}-bit g{cfg.group_size}, desc_act "
+             f"{'on' if cfg.desc_act else 'off'}")
+    rows = list(csv.DictReader(open(os.path.join(d, "trace", "t_kernel_stats.csv"))))
+    lines = [f"# rocprofv3 kernel statistics: bench.py --config {cfg_name} ({shape})", "",
+             "Command (run from the repository root on one MI355X):", "",
+             "    " + PROFILE_COMMANDS["trace"].format(d=d, c=cfg_name), "",
+             "3 steps in the trace (1 warm-up + 2 timed), one gptq_hessian_accumulate call over",
+             f"all {cfg.tokens} calibration tokens per step; the at::native / Cijk / copyBuffer",
+             "kernels come from torch's seeded input generation before the timed region.", "",
+             "| kernel | calls | total ms | avg us | min us | max us |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        name = r["Name"]
+        if name.startswith("_Z"):
+            name = name[:60]
+        name = name.split("(")[0].replace("void ", "")[:70]
+        lines.append(f"| {name} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    with open(os.path.join(ROOT, "profiles", f"layer_{cfg_name}_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    GiB = 1 << 30
+    per = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = list(csv.DictReader(open(os.path.join(d, ctr, "p_counter_collection.csv"))))
+        syrk = collections_sum(rows, lambda k: k.startswith("syrk_"))
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        per[ctr] = (syrk, copy)
+    ff = (GiB / 1024) / per["FETCH_SIZE"][1]
+    wf = (GiB / 1024) / per["WRITE_SIZE"][1]
+    fetch_b = per["FETCH_SIZE"][0][0] * 1024 * ff
+    write_b = per["WRITE_SIZE"][0][0] * 1024 * wf
+    alg = cfg.tokens * n * 2 + 2 * (n * (n + 1) // 2) * 4
+    out = {
+        "kernels": per["FETCH_SIZE"][0][1],
+        "source": "post_weight_quantization_12_amd/csrc/syrk.hip",
+        "source_sha": kernel_source_sha("syrk.hip"),
+        "workload": f"{cfg_name}: {shape}; X {cfg.samples}x{cfg.tokens_per_sample} tokens fp16",
+        "call_tokens": cfg.tokens,
+        "commands": [PROFILE_COMMANDS[c].format(d=d, c=cfg_name)
+                     for c in ("FETCH_SIZE", "WRITE_SIZE")],
+        "fetch_kib_per_call": round(per["FETCH_SIZE"][0][0], 1),
+        "write_kib_per_call": round(per["WRITE_SIZE"][0][0], 1),
+        "copy_probe": {"kernel": "__amd_rocclr_copyBuffer (torch device copy of 1 GiB)",
+                       "bytes_read": GiB, "bytes_written": GiB,
+                       "fetch_kib": round(per["FETCH_SIZE"][1], 1),
+                       "write_kib": round(per["WRITE_SIZE"][1], 1)},
+        "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+        "hbm_bytes_per_call": int(fetch_b + write_b),
+        "algorithmic_bytes_per_call": alg,
+        "traffic_over_algorithmic": round((fetch_b + write_b) / alg, 2),
+    }
+    with open(os.path.join(ROOT, "profiles", f"syrk_{cfg_name}_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def collections_sum(rows, pick):
+    """(sum of Counter_Value over the dispatches whose kernel name matches,
+    {kernel: dispatches})."""
+    total, names = 0.0, {}
+    for r in rows:
+        k = r["Kernel_Name"].strip()  # base names (rocprofv3 -T)
+        if pick(k):
+            total += float(r["Counter_Value"])
+            names[k] = names.get(k, 0) + 1
+    return total, names
 
 
 def cpu_baseline(cfg, steps_tokens: int):
@@ -115,13 +225,20 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c1", choices=["c1", "c2", "c3", "c4a", "c4b"])
-    ap.add_argument("--chunk-samples", type=int, default=16)
+    ap.add_argument("--chunk-samples", type=int, default=None,
+                    help="calibration samples per gptq_hessian_accumulate call "
+                         "(default: all of them in one call)")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="write the profiles/ summaries from rocprofv3 output in DIR and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference kernel "
                          "of known traffic for calibrating rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
 
+    if args.summarize:
+        summarize(args.config, args.summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this GPTQ build runs on one GPU only (no sharding, no collectives); "
               "run with --gpus 1", file=sys.stderr)
@@ -166,7 +283,7 @@ def main():
     g_idx = torch.empty((n,), dtype=torch.int32, device=dev)
     wsq = torch.empty((P.quantize_workspace_bytes(out, n, cfg.bits, cfg.group_size, cfg.block),),
                       dtype=torch.uint8, device=dev)
-    chunk = args.chunk_samples * T
+    chunk = (args.chunk_samples or cfg.samples) * T
     chunks = [X[i:i + chunk] for i in range(0, cfg.tokens, chunk)]
     stream = torch.cuda.current_stream()
 
@@ -222,6 +339,7 @@ def main():
     hess_tflops = syrk_flops_total / (mean(hess_ms) * 1e-3) / 1e12
     syrk_launch_flops = float(chunk) * n * (n + 1)
     syrk_launch_ms = mean(launch_ms)
+    kernels, launches = syrk_schedule(n, chunk, torch.cuda.get_device_properties(0).multi_processor_count)
     achieved = syrk_launch_flops / (syrk_launch_ms * 1e-3) / 1e12
     weights = out * n
     layer_ms = mean(prep_ms) + mean(quant_ms)
@@ -253,14 +371,15 @@ def main():
                      "quantize": mean(quant_ms)},
         "layer_weights_per_s": weights / (layer_ms * 1e-3),
         "roofline": {
-            "kernel": syrk_kernel_name(n),
+            "kernel": f"{kernels} = one gptq_hessian_accumulate call",
+            "kernel_launches_per_call": launches,
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_FP16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP16_TFLOPS,
-            "launch_ms": syrk_launch_ms,
-            "flops_per_launch": syrk_launch_flops,
+            "call_ms": syrk_launch_ms,
+            "flops_per_call": syrk_launch_flops,
             "traffic": load_traffic("syrk.hip", cfg.name, chunk),
         },
     }

@@ -55,9 +55,11 @@ typedef enum { GPTQ_F16 = 0, GPTQ_BF16 = 1, GPTQ_F32 = 2 } gptq_dtype_t;
 #define GPTQ_MAX_PREPARE_N 32768
 
 /* Workspace (bytes) gptq_hessian_accumulate can use for order n on the
- * current device: two 256 x 256 fp32 partial tiles for each workgroup of the
- * token-split schedule (one workgroup per compute unit, at most 512; about
- * 128 MiB on a 256-CU device).  The size does not depend on n. */
+ * current device: 256 x 256 fp32 partial tiles for the schedules that split
+ * tiles along the tokens, which run when the 256 x 256 tiles of H cannot
+ * fill the compute units in whole rounds (e.g. 335 MiB at n = 4096 on a
+ * 256-CU device); 0 where whole tiles are always used (e.g. n = 11008) or
+ * n < 1. */
 size_t gptq_hessian_workspace_bytes(int64_t n);
 
 /*
@@ -81,7 +83,9 @@ size_t gptq_hessian_workspace_bytes(int64_t n);
  *          small to fill the GPU with whole 256 x 256 tiles is split over all
  *          compute units along the tokens (partial tiles are combined in a
  *          fixed order: results do not depend on timing).  Calls that share a
- *          workspace must not overlap.
+ *          workspace must not overlap.  Long calls (all calibration tokens
+ *          at once) let the library choose the token blocks; chunks of any
+ *          size give the same sum up to fp32 rounding order.
  *
  * Products of fp16/bf16 values are exact in fp32; accumulation is fp32.
  * Errors: INVALID_ARG (null pointers, n < 1, ntok < 0, ldx < n),

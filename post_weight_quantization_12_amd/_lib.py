@@ -118,7 +118,8 @@ def hessian_accumulate(H, X, stream=None, workspace=None):
     """H (fp32 [n x n], upper triangle) += 2 X^T X for X [ntok x n] fp16/bf16.
 
     ``workspace``: None, or a GPU byte tensor of at least
-    hessian_workspace_bytes(n) (enables the stream-K schedule on small n)."""
+    hessian_workspace_bytes(n) (lets small layers split tiles along the
+    tokens)."""
     lib = load()
     _need_cuda("H", H)
     _need_cuda("X", X)

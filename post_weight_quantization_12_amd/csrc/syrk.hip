@@ -4,14 +4,25 @@
 // weights is 2 * sum_t x_t x_t^T over calibration tokens (glossary entry
 // "gptq", "Algorithm" step (1)).  X arrives tokens x features, row-major, so
 // both MFMA operands are column panels of X: the contraction runs over tokens,
-// which are the strided dimension in memory.  Each thread loads an 8-token x
-// 8-feature block with 16-byte loads, transposes it in registers and stores
-// feature-major rows (8 consecutive tokens per 16 bytes) into LDS, from which
-// every MFMA operand is one ds_read_b128.
+// which are the strided dimension in memory.
 //
-// Tiles: T x T output tiles of the upper triangle only; K (tokens) is staged
-// BK = 64 at a time, double-buffered in LDS.  MFMA: v_mfma_f32_32x32x16_{f16,bf16}
-// (fp16/bf16 products are exact in fp32; accumulation is fp32).
+// Main kernel (syrk_dma_kernel, rows 16-byte aligned): 256 x 256 output tiles
+// of the upper triangle; 32-token stages of the two column panels are copied
+// straight from memory into LDS (buffer_load ... lds, five stages in flight)
+// and read transposed into MFMA operands (ds_read_b64_tr_b16);
+// v_mfma_f32_32x32x16_{f16,bf16} (products exact in fp32, fp32 accumulation).
+// Three schedules, chosen per call:
+//   * whole tiles, one launch per 32768 tokens, when the tiles fill the
+//     workgroup rounds (n = 11008: 990 tiles, 3.9 rounds of 256);
+//   * token split (a workspace, long calls, few tiles): every XCD works on
+//     its own block of tokens, tiles round by round, partial tiles summed by
+//     a second kernel;
+//   * stream-K (a workspace, short calls, few tiles): equal runs of (tile,
+//     stage) units, split tiles summed by a second kernel.
+// Rows that are not 16-byte aligned use syrk_upper_kernel: each thread
+// gathers an 8-token x 8-feature block (element loads), transposes it in
+// registers and stores feature-major rows into LDS (64-token stages, double
+// buffered), from which every MFMA operand is one ds_read_b128.
 #include "common.hpp"
 
 namespace gptq {
@@ -276,8 +287,60 @@ struct StreamK {
   float* partial;   // [nwg][2][256 * 256], row-major tiles
   int64_t units;    // units per workgroup
   int nwg;          // workgroups (a multiple of 8)
+  int ks;           // > 0: token-split schedule with ks token blocks (below)
 };
 constexpr int PART_FLOATS = DT * DT;
+
+// Token-split schedule.  The tokens are cut into S blocks (S = 1, 2, 4, 8);
+// XCD x works on block x % S, and the tiles are divided evenly among the
+// 8 / S XCDs that share a block.  Inside an XCD the C workgroups take the
+// XCD's tiles round by round, all over the same token range, so the ~C tiles
+// of a round read the same token rows together and share them in the XCD's
+// L2.  The tiles left after the whole rounds are cut along the tokens into
+// s = C / r pieces each, so the last round is as long as the others divided
+// by s and no workgroup idles.  Every (tile, block, piece) item leaves one
+// partial; a second kernel adds a tile's partials to H in a fixed order.
+struct KsXcd {
+  int64_t t0, tn;   // tiles [t0, t0 + tn) of the grouped order
+  int64_t base;     // first partial slot of this XCD
+  int64_t items;    // q * C + r * s
+  int q, r, sp;     // whole rounds, tiles left, pieces per tile left
+};
+__host__ __device__ inline KsXcd ks_xcd(int x, int S, int C, int64_t T) {
+  const int G = 8 / S;
+  KsXcd k{0, 0, 0, 0, 0, 0, 0};
+  for (int y = 0; y <= x; ++y) {
+    const int g = y / S;
+    const int64_t t0 = T * g / G, t1 = T * (g + 1) / G, tn = t1 - t0;
+    const int q = (int)(tn / C), r = (int)(tn % C), sp = r > 0 ? C / r : 0;
+    const int64_t items = (int64_t)q * C + (int64_t)r * sp;
+    if (y == x) {
+      k.t0 = t0; k.tn = tn; k.q = q; k.r = r; k.sp = sp; k.items = items;
+    } else {
+      k.base += items;
+    }
+  }
+  return k;
+}
+// Token stages [k0, k1) of item i of an XCD on block b; tile o (grouped order).
+__device__ inline void ks_item(const KsXcd& k, int64_t i, int b, int S, int C, int nk,
+                               int64_t& o, int& k0, int& k1) {
+  const int bk = (nk + S - 1) / S;
+  const int lo = b * bk < nk ? b * bk : nk, hi = (b + 1) * bk < nk ? (b + 1) * bk : nk;
+  const int64_t whole = (int64_t)k.q * C;
+  if (i < whole) {
+    o = k.t0 + i;
+    k0 = lo;
+    k1 = hi;
+  } else {
+    const int64_t j = i - whole;
+    const int p = (int)(j % k.sp);
+    o = k.t0 + whole + j / k.sp;
+    const int len = hi - lo;
+    k0 = lo + (int)((int64_t)len * p / k.sp);
+    k1 = lo + (int)((int64_t)len * (p + 1) / k.sp);
+  }
+}
 
 // Waves per workgroup: 8, two per SIMD, each a 64 x 128 block (8
 // accumulators): the second wave on a SIMD keeps its matrix pipe busy while
@@ -527,6 +590,21 @@ syrk_dma_kernel(float* __restrict__ H, int64_t n, const uint16_t* __restrict__ X
     if (!syrk_tile(blockIdx.x, nt, ti, tj)) return;
     run((int64_t)ti * DT, (int64_t)tj * DT, 0, nk, false);
     store_h((int64_t)ti * DT, (int64_t)tj * DT);
+  } else if (sk.ks > 0) {
+    const int S = sk.ks, C = sk.nwg / 8, x = blockIdx.x % 8;
+    const KsXcd k = ks_xcd(x, S, C, (int64_t)nt * (nt + 1) / 2);
+#pragma nounroll
+    for (int64_t i = blockIdx.x / 8; i < k.items; i += C) {
+      int64_t o;
+      int k0, k1;
+      ks_item(k, i, x % S, S, C, nk, o, k0, k1);
+      int ti, tj;
+      tile_of(o, nt, ti, tj);
+      ti = __builtin_amdgcn_readfirstlane(ti);
+      tj = __builtin_amdgcn_readfirstlane(tj);
+      run((int64_t)ti * DT, (int64_t)tj * DT, k0, k1, false);
+      store_part(sk.partial + (k.base + i) * PART_FLOATS);
+    }
   } else {
     const int64_t total = (int64_t)nt * (nt + 1) / 2 * nk;
     const int lam = (blockIdx.x % 8) * (sk.nwg / 8) + blockIdx.x / 8;  // XCD-contiguous runs
@@ -589,6 +667,43 @@ syrk_streamk_fixup(float* __restrict__ H, int64_t n, int nk, const float* __rest
   }
 }
 
+// Token-split schedule: H += 2 * (sum of a tile's partials: blocks in order,
+// pieces in order).  Grid: (tiles, DT / FIX_ROWS).
+__global__ void __launch_bounds__(DT)
+syrk_ksplit_fixup(float* __restrict__ H, int64_t n, int S, int C, const float* __restrict__ partial) {
+  const int nt = (int)((n + DT - 1) / DT);
+  const int64_t T = (int64_t)nt * (nt + 1) / 2;
+  const int64_t o = blockIdx.x;
+  int ti, tj;
+  tile_of(o, nt, ti, tj);
+  const int r0 = blockIdx.y * FIX_ROWS, jl = threadIdx.x;
+  float sum[FIX_ROWS];
+#pragma unroll
+  for (int r = 0; r < FIX_ROWS; ++r) sum[r] = 0.0f;
+  const int G = 8 / S;
+  const int g = (int)((o * G + G - 1) / T);  // first group whose range holds o
+  int gg = g;
+  while (gg > 0 && T * gg / G > o) --gg;
+  while (T * (gg + 1) / G <= o) ++gg;
+  for (int b = 0; b < S; ++b) {
+    const KsXcd k = ks_xcd(gg * S + b, S, C, T);
+    const int64_t lt = o - k.t0, whole = (int64_t)k.q * C;
+    const int64_t first = lt < whole ? lt : whole + (lt - whole) * k.sp;
+    const int cnt = lt < whole ? 1 : k.sp;
+    for (int p = 0; p < cnt; ++p) {
+      const float* part = partial + (k.base + first + p) * (int64_t)PART_FLOATS + (int64_t)r0 * DT + jl;
+#pragma unroll
+      for (int r = 0; r < FIX_ROWS; ++r) sum[r] += part[r * DT];
+    }
+  }
+  const int64_t j = (int64_t)tj * DT + jl;
+#pragma unroll
+  for (int r = 0; r < FIX_ROWS; ++r) {
+    const int64_t i = (int64_t)ti * DT + r0 + r;
+    if (i < n && j < n && i <= j) H[i * n + j] += 2.0f * sum[r];
+  }
+}
+
 template <int T, bool BF16, bool VEC>
 hipError_t launch_t(float* H, int64_t n, const uint16_t* X, int64_t ntok, int64_t ldx,
                     hipStream_t s) {
@@ -618,11 +733,46 @@ int sk_workgroups() {
   return cus < MAX_SK_WG ? cus : MAX_SK_WG;
 }
 size_t partial_bytes(int nwg) { return align_up((size_t)nwg * 2 * PART_FLOATS * sizeof(float)); }
+
+// Whole-tile launches cover at most this many tokens.
+constexpr int64_t WHOLE_CHUNK = 32768;
+// The token-split schedule needs at least this many 32-token stages per
+// block: shorter items pay the pipeline fill, the partial store and the
+// fix-up for too little work (measured at n = 4096: 4 % faster than
+// stream-K at 256 stages per block, 11 % slower at 128, 17 % faster at 1024).
+constexpr int KS_MIN_STAGES = 256;
+// The split schedules are used when whole tiles leave the last round less
+// than 90 % full (at n = 4096, 136 tiles on 256 workgroups; at n = 8192,
+// 528 tiles: 2.06 rounds).
+inline bool split_schedules(int64_t T, int nwg) {
+  const int64_t rounds = (T + nwg - 1) / nwg;
+  return 10 * T < 9 * rounds * (int64_t)nwg;
+}
+// Token blocks for T tiles on nwg workgroups: enough blocks that each XCD
+// has at least four rounds of items, at most 8.
+int ks_blocks(int64_t T, int nwg) {
+  const int C = nwg / 8;
+  int S = 1;
+  while (S < 8 && T * S / 8 < 4 * (int64_t)C) S *= 2;
+  return S;
+}
+size_t ks_bytes(int64_t n, int nwg) {
+  const int nt = (int)((n + DT - 1) / DT);
+  const int64_t T = (int64_t)nt * (nt + 1) / 2;
+  const int S = ks_blocks(T, nwg), C = nwg / 8;
+  int64_t items = 0;
+  for (int x = 0; x < 8; ++x) items += ks_xcd(x, S, C, T).items;
+  return align_up((size_t)items * PART_FLOATS * sizeof(float));
+}
 }  // namespace
 
 size_t syrk_workspace_bytes(int64_t n) {
-  (void)n;
-  return partial_bytes(sk_workgroups());
+  const int nwg = sk_workgroups();
+  const int nt = (int)((n + DT - 1) / DT);
+  const int64_t T = (int64_t)nt * (nt + 1) / 2;
+  if (!split_schedules(T, nwg)) return 0;  // whole tiles only
+  const size_t a = 4 * T < 3 * (int64_t)nwg ? partial_bytes(nwg) : 0, b = ks_bytes(n, nwg);
+  return a > b ? a : b;
 }
 
 hipError_t launch_syrk(float* H, int64_t n, const void* X, int dtype, int64_t ntok,
@@ -635,28 +785,44 @@ hipError_t launch_syrk(float* H, int64_t n, const void* X, int dtype, int64_t nt
     const int nt = (int)((n + DT - 1) / DT);
     const int64_t tiles = (int64_t)nt * (nt + 1) / 2;
     const int nwg = sk_workgroups();
-    StreamK sk{nullptr, 0, nwg};
-    // Stream-K when whole tiles would leave more than a quarter of the compute
-    // units idle (measured: at 82 % occupancy the partial tiles cost more than
-    // the idle units).
-    if (ws != nullptr && ws_bytes >= syrk_workspace_bytes(n) && 4 * tiles < 3 * (int64_t)nwg) {
-      const int nk = (int)((ntok + DBK - 1) / DBK);
-      sk.partial = static_cast<float*>(ws);
-      sk.units = (tiles * nk + nwg - 1) / nwg;
-      auto kern = bf ? syrk_dma_kernel<true, true> : syrk_dma_kernel<false, true>;
-      hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(SyrkShape<true>::NW * 64), 0, s, H, n, x,
-                         ntok, ldx, sk);
-      GPTQ_HIP_TRY(hipGetLastError());
-      if (sk.units < nk)
-        hipLaunchKernelGGL(syrk_streamk_fixup, dim3((unsigned)tiles, DT / FIX_ROWS), dim3(DT), 0,
-                           s, H, n, nk, sk.partial, sk.units);
-      return hipGetLastError();
+    const int nk = (int)((ntok + DBK - 1) / DBK);
+    StreamK sk{static_cast<float*>(ws), 0, nwg, 0};
+    auto kern_sk = bf ? syrk_dma_kernel<true, true> : syrk_dma_kernel<false, true>;
+    const bool have_ws = ws != nullptr && ws_bytes >= syrk_workspace_bytes(n);
+    if (have_ws && split_schedules(tiles, nwg)) {
+      const int S = ks_blocks(tiles, nwg);
+      if (nk / S >= KS_MIN_STAGES) {
+        sk.ks = S;
+        hipLaunchKernelGGL(kern_sk, dim3((unsigned)nwg), dim3(SyrkShape<true>::NW * 64), 0, s, H,
+                           n, x, ntok, ldx, sk);
+        GPTQ_HIP_TRY(hipGetLastError());
+        hipLaunchKernelGGL(syrk_ksplit_fixup, dim3((unsigned)tiles, DT / FIX_ROWS), dim3(DT), 0,
+                           s, H, n, S, nwg / 8, sk.partial);
+        return hipGetLastError();
+      }
+      if (4 * tiles < 3 * (int64_t)nwg) {
+        sk.units = (tiles * nk + nwg - 1) / nwg;
+        hipLaunchKernelGGL(kern_sk, dim3((unsigned)nwg), dim3(SyrkShape<true>::NW * 64), 0, s, H,
+                           n, x, ntok, ldx, sk);
+        GPTQ_HIP_TRY(hipGetLastError());
+        if (sk.units < nk)
+          hipLaunchKernelGGL(syrk_streamk_fixup, dim3((unsigned)tiles, DT / FIX_ROWS), dim3(DT), 0,
+                             s, H, n, nk, sk.partial, sk.units);
+        return hipGetLastError();
+      }
     }
+    // Whole tiles, one launch per WHOLE_CHUNK tokens: all workgroups of a
+    // launch start at the same token stage and stay close, so the X rows they
+    // read together stay in L2 (one launch over 262144 tokens is 5-7 % slower).
     const int64_t blocks = (tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
     auto kern = bf ? syrk_dma_kernel<true, false> : syrk_dma_kernel<false, false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(SyrkShape<false>::NW * 64), 0, s, H, n, x,
-                       ntok, ldx, sk);
-    return hipGetLastError();
+    for (int64_t t0 = 0; t0 < ntok; t0 += WHOLE_CHUNK) {
+      const int64_t len = ntok - t0 < WHOLE_CHUNK ? ntok - t0 : WHOLE_CHUNK;
+      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(SyrkShape<false>::NW * 64), 0, s, H, n,
+                         x + t0 * ldx, len, ldx, sk);
+      GPTQ_HIP_TRY(hipGetLastError());
+    }
+    return hipSuccess;
   }
   // Unaligned rows: register-staged kernel with element loads.
   constexpr int T = 256;

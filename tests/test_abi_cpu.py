@@ -45,6 +45,10 @@ def test_hessian_argument_errors(lib):
     # a workspace, when given, must be at least the queried size
     ws = lib.gptq_hessian_workspace_bytes(8)
     assert ws > 0 and lib.gptq_hessian_workspace_bytes(0) == 0
+    # whole 256 x 256 tiles fill the GPU at n = 11008 (990 tiles): no workspace
+    assert lib.gptq_hessian_workspace_bytes(11008) == 0
+    # n = 4096 (136 tiles): the token-split partials, one 256 KiB tile per item
+    assert lib.gptq_hessian_workspace_bytes(4096) >= 1024 * 256 * 1024
     assert f(FAKE, 8, FAKE, 0, 4, 8, FAKE, ws - 1, None) == L.GPTQ_ERR_WORKSPACE
     # ntok == 0 is a no-op that never touches the device
     assert f(FAKE, 8, FAKE, 0, 0, 8, None, 0, None) == L.GPTQ_OK

@@ -46,10 +46,13 @@ def test_syrk_c0_matches_oracle_and_leaves_lower_untouched(streamk):
     assert rel_fro(upper_mirror(H), Ho) <= 1e-6  # fp16 products are exact, fp32 sums
 
 
+# With a workspace, short calls on few tiles take the stream-K schedule and
+# calls of >= 65536 tokens the token-split one (70001 and 2 x 70001 below).
 @pytest.mark.parametrize("streamk", [False, True])
 @pytest.mark.parametrize("n,ntok,ldx,chunks", [(200, 77, 200, 1), (264, 1000, 272, 3),
                                                (128, 64, 128, 2), (8, 5, 8, 1),
-                                               (520, 3000, 520, 2)])
+                                               (520, 3000, 520, 2), (520, 70001, 520, 1),
+                                               (264, 140002, 272, 2)])
 def test_syrk_integer_inputs_bit_exact(n, ntok, ldx, chunks, streamk):
     _banner(f"syrk integer n={n} ntok={ntok} ldx={ldx} streamk={streamk}")
     g = torch.Generator().manual_seed(n + ntok)
@@ -86,6 +89,21 @@ def test_syrk_heavy_tailed_many_tokens():
     H2 = _hessian_gpu([X], 512, streamk=False).cpu().numpy()
     assert np.array_equal(H, _hessian_gpu([X], 512).cpu().numpy())  # run-to-run identical
     assert rel_fro(upper_mirror(H2), upper_mirror(H)) <= 1e-6
+    Ho = O.hessian(X.numpy())
+    assert rel_fro(upper_mirror(H), Ho) <= 1e-3
+
+
+def test_syrk_token_split_matches_oracle():
+    """The token-split schedule (a workspace and 71680 tokens in one call at
+    n = 1000) against the oracle, against whole tiles, and run to run."""
+    _banner("syrk token split n=1000 tokens=71680")
+    cfg = workloads.get("c3").shrink(inp=1000, tokens_per_sample=2048, n_outliers=4)
+    X = workloads.x_tokens(cfg, 0, 35)
+    H = _hessian_gpu([X], 1000).cpu().numpy()
+    assert np.array_equal(H, _hessian_gpu([X], 1000).cpu().numpy())  # run-to-run identical
+    H2 = _hessian_gpu([X], 1000, streamk=False).cpu().numpy()
+    assert rel_fro(upper_mirror(H2), upper_mirror(H)) <= 1e-6
+    assert np.all(np.tril(H, -1) == 0)
     Ho = O.hessian(X.numpy())
     assert rel_fro(upper_mirror(H), Ho) <= 1e-3
 
