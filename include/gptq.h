@@ -125,6 +125,13 @@ size_t gptq_prepare_workspace_bytes(int64_t n);
  *              quantization-order column k-1 was non-positive or not finite
  *              (then Hinv_chol is not meaningful).
  *   workspace  device memory of at least gptq_prepare_workspace_bytes(n).
+ *
+ * The factorization runs on the caller's stream and on two helper streams
+ * the library creates once per device (default priority): they wait for the
+ * caller's earlier work and the caller's stream waits for them before the
+ * call returns, so on the caller's stream the call behaves as one ordered
+ * operation.  Calls on one device enqueue one after the other (a host-side
+ * lock); calls that share a workspace must not overlap.
  * Errors: INVALID_ARG, UNSUPPORTED (n > GPTQ_MAX_PREPARE_N), WORKSPACE, HIP.
  */
 int gptq_prepare(const float* H, int64_t n, float damp_percent, int desc_act,

@@ -27,6 +27,9 @@
 // MFMAs (three fp16 products per fp32 product, fp32 accumulation).
 #include "common.hpp"
 
+#include <map>
+#include <mutex>
+
 namespace gptq {
 namespace {
 
@@ -225,13 +228,16 @@ gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict_
 // `off` (lower part of A, leading dimension n), in one workgroup of 8 waves
 // out of LDS, blocked by 16 columns.  Per 16-column step c:
 //   (a) wave 0 factors the 16 x 16 diagonal block in registers (readlane
-//       broadcasts, one rsqrt per pivot) while wave 1 inverts the previous
-//       step's diagonal block (off the critical path);
+//       broadcasts, one rsqrt per pivot);
 //   (b) every row below is solved against the new block by forward
 //       substitution (one thread per row);
 //   (c) the trailing lower block is updated in 16 x 16 tiles on the matrix
 //       cores (v_mfma_f32_16x16x4f32).
-// Then the off-diagonal blocks of X by doubling (blocks of 32, 64, 128):
+// Then the eight diagonal blocks are inverted, one per wave, all at once
+// (inside the step loop the inversion of the previous block on a second wave
+// took longer than the factorization and held up every step: 4.9 k against
+// 3.9 k cycles), and the off-diagonal blocks of X are formed by doubling
+// (blocks of 32, 64, 128):
 //   T = L21 X11, X21 = -X22 T, again in 16 x 16 MFMA tiles over all waves.
 // Rows >= m are padded with the identity (so every pivot is defined).  Only
 // X is written back (lower part, rows and columns < m): the recursion never
@@ -371,8 +377,6 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
 #pragma unroll
         for (int k = 0; k < 16; ++k) rinv_s[c + k] = rv[k];
       }
-    } else if (wave == 1 && step > 0) {
-      invert_block(step - 1);
     }
     __syncthreads();
       const int rows = NB - c - 16;
@@ -417,7 +421,8 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
       __syncthreads();
         }
   }
-  if (wave == 1) invert_block(NSTEP - 1);
+  static_assert(NSTEP <= LEAF_THREADS / 64, "one diagonal block per wave");
+  if (wave < NSTEP) invert_block(wave);
   __syncthreads();
 
   // Off-diagonal blocks of X by doubling: for blocks of 2s (s = 16, 32, 64)
@@ -544,6 +549,108 @@ hipError_t cholinv(PrepCtx& c, int64_t off, int64_t m, float* t2) {
   return hipSuccess;
 }
 
+// Streams and events of the blocked schedule, one set per device, created on
+// first use (default priority, non-blocking).
+struct SideStreams {
+  hipStream_t upd = nullptr, inv = nullptr;
+  hipEvent_t fork = nullptr, panel = nullptr, upd_done = nullptr, leaf = nullptr,
+             join_upd = nullptr, join_inv = nullptr;
+};
+std::mutex side_mu;
+hipError_t side_streams(SideStreams*& out) {
+  static std::map<int, SideStreams> per_dev;
+  int dev = 0;
+  GPTQ_HIP_TRY(hipGetDevice(&dev));
+  SideStreams& ss = per_dev[dev];
+  if (ss.upd == nullptr) {
+    GPTQ_HIP_TRY(hipStreamCreateWithFlags(&ss.upd, hipStreamNonBlocking));
+    GPTQ_HIP_TRY(hipStreamCreateWithFlags(&ss.inv, hipStreamNonBlocking));
+    hipEvent_t* evs[] = {&ss.fork, &ss.panel, &ss.upd_done, &ss.leaf, &ss.join_upd, &ss.join_inv};
+    for (hipEvent_t* e : evs) GPTQ_HIP_TRY(hipEventCreateWithFlags(e, hipEventDisableTiming));
+  }
+  out = &ss;
+  return hipSuccess;
+}
+
+// Blocked right-looking Cholesky with inversion, W-column blocks j (W from
+// outer_width; a block is factored by the recursion above, one leaf when
+// W = NB):
+//   diag:   L_jj, X_jj = L_jj^-1                        (main stream)
+//   panel:  P_j^T = X_jj A[j+1:, j]^T into the unused upper triangle,
+//           row block j (so L below the diagonal is kept transposed there)
+//   next:   block column j+1 -= P_j P_j[j+1]^T          (main stream)
+//   rest:   A[j+2:, j+2:] -= P_j P_j^T, lower tiles     (update stream)
+//   inv:    X[j, :j] = -X_jj (L[j, :j] X[:j, :j])       (inverse stream)
+// The main stream carries only the diagonal blocks and the two skinny
+// products each one needs; the trailing update of step j runs while block
+// j+1 factors, and the off-diagonal blocks of X trail behind on their own
+// stream.  Lookahead of one block: "next" of step j+1 waits for "rest" of
+// step j (it updates the first columns "rest" wrote).  Products in the
+// upper triangle of diagonal tiles (lower-only GEMMs compute whole tiles)
+// land in the diagonal blocks' upper parts, which nothing reads.
+// Columns per block of the blocked schedule: single leaves up to n = 4096;
+// above, the skinny K = 128 products of the update and inverse streams cost
+// more than they hide, and wider blocks (factored by the recursion) are
+// faster; the trailing update re-reads the trailing matrix once per block,
+// about n^3 / (3 W) * 8 bytes, so the largest layers take the widest
+// (measured: n = 4096: 2.32 ms at 128, 2.40 at 256; n = 11008: 13.5 ms at
+// 128, 10.2 at 512, 10.3 at 1024; n = 28672: 99 ms at 512, 84.8 at 1024,
+// 83.9 at 2048, 87.5 at 4096).
+constexpr int64_t OUTER_MAX = 2048;
+int64_t outer_width(int64_t n) { return n <= 4096 ? NB : n <= 12288 ? 512 : OUTER_MAX; }
+hipError_t cholinv_blocked(PrepCtx& c, float* tbuf) {
+  const int64_t n = c.n;
+  const int64_t W = outer_width(n);
+  SideStreams* ss = nullptr;
+  GPTQ_HIP_TRY(side_streams(ss));
+  std::lock_guard<std::mutex> lock(side_mu);
+  const hipStream_t M = c.s;
+  PrepCtx cu = c, ci = c;
+  cu.s = ss->upd;
+  ci.s = ss->inv;
+  GPTQ_HIP_TRY(hipEventRecord(ss->fork, M));
+  GPTQ_HIP_TRY(hipStreamWaitEvent(ss->upd, ss->fork, 0));
+  GPTQ_HIP_TRY(hipStreamWaitEvent(ss->inv, ss->fork, 0));
+  bool pending_rest = false;
+  for (int64_t o = 0; o < n; o += W) {
+    const int64_t m = n - o < W ? n - o : W;
+    const int64_t rest = n - o - m;
+    GPTQ_HIP_TRY(cholinv(c, o, m, c.T2));
+    if (o > 0) {
+      GPTQ_HIP_TRY(hipEventRecord(ss->leaf, M));
+      GPTQ_HIP_TRY(hipStreamWaitEvent(ss->inv, ss->leaf, 0));
+      GPTQ_HIP_TRY(gemm(ci, m, o, o, c.A + o, n, true, c.X, n, false, tbuf, o, 1.0f, 0.0f,
+                        KR_GE_COL, false));
+      GPTQ_HIP_TRY(gemm(ci, m, o, m, c.X + o * n + o, n, false, tbuf, o, false, c.X + o * n, n,
+                        -1.0f, 0.0f, KR_LE_ROW, false));
+    }
+    if (rest == 0) break;
+    float* U_j = c.A + o * n + o + m;
+    GPTQ_HIP_TRY(gemm(c, m, rest, m, c.X + o * n + o, n, false, c.A + (o + m) * n + o, n, true,
+                      U_j, n, 1.0f, 0.0f, KR_LE_ROW, false));
+    if (pending_rest) GPTQ_HIP_TRY(hipStreamWaitEvent(M, ss->upd_done, 0));
+    const int64_t m2 = rest < W ? rest : W;
+    GPTQ_HIP_TRY(gemm(c, rest, m2, m, U_j, n, true, U_j, n, false, c.A + (o + m) * n + o + m, n,
+                      -1.0f, 1.0f, KR_FULL, true));
+    pending_rest = false;
+    if (rest > m2) {
+      GPTQ_HIP_TRY(hipEventRecord(ss->panel, M));
+      GPTQ_HIP_TRY(hipStreamWaitEvent(ss->upd, ss->panel, 0));
+      const int64_t r2 = rest - m2;
+      float* C = c.A + (o + m + m2) * n + o + m + m2;
+      GPTQ_HIP_TRY(gemm(cu, r2, r2, m, U_j + m2, n, true, U_j + m2, n, false, C, n, -1.0f, 1.0f,
+                        KR_FULL, true));
+      GPTQ_HIP_TRY(hipEventRecord(ss->upd_done, ss->upd));
+      pending_rest = true;
+    }
+  }
+  GPTQ_HIP_TRY(hipEventRecord(ss->join_upd, ss->upd));
+  GPTQ_HIP_TRY(hipEventRecord(ss->join_inv, ss->inv));
+  GPTQ_HIP_TRY(hipStreamWaitEvent(M, ss->join_upd, 0));
+  GPTQ_HIP_TRY(hipStreamWaitEvent(M, ss->join_inv, 0));
+  return hipSuccess;
+}
+
 // Floats of the T2 stack for a node of order m (its own block plus the
 // deeper levels' largest chain).
 int64_t t2_floats(int64_t m) {
@@ -558,6 +665,7 @@ struct PrepLayout {
   float* A;
   float* T;
   float* T2;
+  float* TB;
   uint32_t* keys;
   int32_t* rank;
   float* damp_add;
@@ -568,11 +676,15 @@ struct PrepLayout {
 PrepLayout carve(void* ws, int64_t n) {
   Carver c(ws);
   PrepLayout l;
-  const int64_t m1max = ((n / 2 + NB - 1) / NB) * NB;
+  // the recursion factors diagonal blocks of at most w columns
+  const int64_t w = n < outer_width(n) ? n : outer_width(n);
+  const int64_t m1max = ((w / 2 + NB - 1) / NB) * NB;
   l.A = c.take<float>((size_t)n * n);
   // every internal node has m2 <= m1 <= m1max, so m1max^2 holds any L21 block
-  l.T = c.take<float>((size_t)m1max * (size_t)m1max);
-  l.T2 = c.take<float>((size_t)(t2_floats(n) > 0 ? t2_floats(n) : 1));
+  l.T = c.take<float>((size_t)(m1max > 0 ? m1max * m1max : 1));
+  l.T2 = c.take<float>((size_t)(t2_floats(w) > 0 ? t2_floats(w) : 1));
+  // T = L[j, :j] X[:j, :j] of the inverse stream: at most w x n
+  l.TB = c.take<float>((size_t)w * (size_t)n);
   l.keys = c.take<uint32_t>((size_t)n);
   l.rank = c.take<int32_t>((size_t)n);
   l.damp_add = c.take<float>(1);
@@ -616,7 +728,7 @@ hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, floa
   hipLaunchKernelGGL(fill_f32_kernel, dim3(2048), dim3(256), 0, s, U, n * n, 0.0f);
   GPTQ_HIP_TRY(hipGetLastError());
   PrepCtx c{l.A, U, l.T, l.T2, n, info, s};
-  GPTQ_HIP_TRY(cholinv(c, 0, n, l.T2));
+  GPTQ_HIP_TRY(cholinv_blocked(c, l.TB));
   const unsigned gx = (unsigned)((n + 255) / 256);
   hipLaunchKernelGGL(reverse_inplace_kernel, dim3(gx, (unsigned)n), dim3(256), 0, s, U, n, l.dsc);
   return hipGetLastError();

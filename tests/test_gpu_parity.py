@@ -116,8 +116,10 @@ def _oracle_h(cfg, s1=1, tokens=None):
     return X, H32
 
 
+# n <= 4096 factors 128-column blocks one leaf at a time; above, 512-column
+# blocks through the recursion (4500: eight whole blocks and a ragged one).
 @pytest.mark.parametrize("n,desc", [(128, False), (128, True), (200, True), (1000, True),
-                                    (1024, False)])
+                                    (1024, False), (4500, True)])
 def test_prepare_matches_oracle(n, desc):
     _banner(f"prepare n={n} desc={desc}")
     cfg = workloads.get("c1").shrink(inp=n, tokens_per_sample=max(2 * n, 256))
