@@ -1,6 +1,7 @@
 // extern "C" entry points of the gfx950 GPTQ library: argument validation
 // (before anything is enqueued), workspace checks, status strings.
 #include <cmath>
+#include <map>
 #include <string>
 
 #include "../../include/gptq.h"
@@ -13,6 +14,26 @@ thread_local std::string g_last_error;
 void set_error(const std::string& msg) { g_last_error = msg; }
 void clear_error() { g_last_error.clear(); }
 const char* last_error_c() { return g_last_error.c_str(); }
+
+std::mutex& helper_mutex() {
+  static std::mutex mu;
+  return mu;
+}
+hipError_t helper_streams(HelperStreams*& out) {
+  static std::map<int, HelperStreams> per_dev;  // guarded by helper_mutex()
+  int dev = 0;
+  GPTQ_HIP_TRY(hipGetDevice(&dev));
+  auto it = per_dev.find(dev);
+  if (it == per_dev.end()) {
+    HelperStreams h;
+    GPTQ_HIP_TRY(hipStreamCreateWithFlags(&h.a, hipStreamNonBlocking));
+    GPTQ_HIP_TRY(hipStreamCreateWithFlags(&h.b, hipStreamNonBlocking));
+    for (hipEvent_t& e : h.ev) GPTQ_HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    it = per_dev.emplace(dev, h).first;
+  }
+  out = &it->second;
+  return hipSuccess;
+}
 }  // namespace gptq
 
 using namespace gptq;

@@ -5,6 +5,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 namespace gptq {
@@ -24,6 +25,19 @@ __device__ inline void wait_vmcnt() {
 }
 // s_waitcnt lgkmcnt(0) (LDS reads and writes of this wave done), vmcnt untouched.
 __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0x3 << 14) | 0xF); }
+
+// Helper streams of one device for calls that spread their work: two
+// non-blocking streams (default priority) and six timing-free events,
+// created on first use and kept until the process ends.  A call takes
+// helper_mutex() before helper_streams() and holds it while it enqueues, so
+// calls from several host threads never interleave their event records and
+// waits; it forks from and joins back into the caller's stream.
+struct HelperStreams {
+  hipStream_t a = nullptr, b = nullptr;
+  hipEvent_t ev[6] = {};
+};
+std::mutex& helper_mutex();
+hipError_t helper_streams(HelperStreams*& out);
 
 // Error reporting to the C ABI (per host thread).
 void set_error(const std::string& msg);

@@ -27,9 +27,6 @@
 // MFMAs (three fp16 products per fp32 product, fp32 accumulation).
 #include "common.hpp"
 
-#include <map>
-#include <mutex>
-
 namespace gptq {
 namespace {
 
@@ -549,29 +546,6 @@ hipError_t cholinv(PrepCtx& c, int64_t off, int64_t m, float* t2) {
   return hipSuccess;
 }
 
-// Streams and events of the blocked schedule, one set per device, created on
-// first use (default priority, non-blocking).
-struct SideStreams {
-  hipStream_t upd = nullptr, inv = nullptr;
-  hipEvent_t fork = nullptr, panel = nullptr, upd_done = nullptr, leaf = nullptr,
-             join_upd = nullptr, join_inv = nullptr;
-};
-std::mutex side_mu;
-hipError_t side_streams(SideStreams*& out) {
-  static std::map<int, SideStreams> per_dev;
-  int dev = 0;
-  GPTQ_HIP_TRY(hipGetDevice(&dev));
-  SideStreams& ss = per_dev[dev];
-  if (ss.upd == nullptr) {
-    GPTQ_HIP_TRY(hipStreamCreateWithFlags(&ss.upd, hipStreamNonBlocking));
-    GPTQ_HIP_TRY(hipStreamCreateWithFlags(&ss.inv, hipStreamNonBlocking));
-    hipEvent_t* evs[] = {&ss.fork, &ss.panel, &ss.upd_done, &ss.leaf, &ss.join_upd, &ss.join_inv};
-    for (hipEvent_t* e : evs) GPTQ_HIP_TRY(hipEventCreateWithFlags(e, hipEventDisableTiming));
-  }
-  out = &ss;
-  return hipSuccess;
-}
-
 // Blocked right-looking Cholesky with inversion, W-column blocks j (W from
 // outer_width; a block is factored by the recursion above, one leaf when
 // W = NB):
@@ -601,24 +575,26 @@ int64_t outer_width(int64_t n) { return n <= 4096 ? NB : n <= 12288 ? 512 : OUTE
 hipError_t cholinv_blocked(PrepCtx& c, float* tbuf) {
   const int64_t n = c.n;
   const int64_t W = outer_width(n);
-  SideStreams* ss = nullptr;
-  GPTQ_HIP_TRY(side_streams(ss));
-  std::lock_guard<std::mutex> lock(side_mu);
-  const hipStream_t M = c.s;
+  std::lock_guard<std::mutex> lock(helper_mutex());
+  HelperStreams* hs = nullptr;
+  GPTQ_HIP_TRY(helper_streams(hs));
+  const hipStream_t M = c.s, UPD = hs->a, INV = hs->b;
+  hipEvent_t ev_fork = hs->ev[0], ev_panel = hs->ev[1], ev_upd = hs->ev[2], ev_diag = hs->ev[3],
+             ev_join_upd = hs->ev[4], ev_join_inv = hs->ev[5];
   PrepCtx cu = c, ci = c;
-  cu.s = ss->upd;
-  ci.s = ss->inv;
-  GPTQ_HIP_TRY(hipEventRecord(ss->fork, M));
-  GPTQ_HIP_TRY(hipStreamWaitEvent(ss->upd, ss->fork, 0));
-  GPTQ_HIP_TRY(hipStreamWaitEvent(ss->inv, ss->fork, 0));
+  cu.s = UPD;
+  ci.s = INV;
+  GPTQ_HIP_TRY(hipEventRecord(ev_fork, M));
+  GPTQ_HIP_TRY(hipStreamWaitEvent(UPD, ev_fork, 0));
+  GPTQ_HIP_TRY(hipStreamWaitEvent(INV, ev_fork, 0));
   bool pending_rest = false;
   for (int64_t o = 0; o < n; o += W) {
     const int64_t m = n - o < W ? n - o : W;
     const int64_t rest = n - o - m;
     GPTQ_HIP_TRY(cholinv(c, o, m, c.T2));
     if (o > 0) {
-      GPTQ_HIP_TRY(hipEventRecord(ss->leaf, M));
-      GPTQ_HIP_TRY(hipStreamWaitEvent(ss->inv, ss->leaf, 0));
+      GPTQ_HIP_TRY(hipEventRecord(ev_diag, M));
+      GPTQ_HIP_TRY(hipStreamWaitEvent(INV, ev_diag, 0));
       GPTQ_HIP_TRY(gemm(ci, m, o, o, c.A + o, n, true, c.X, n, false, tbuf, o, 1.0f, 0.0f,
                         KR_GE_COL, false));
       GPTQ_HIP_TRY(gemm(ci, m, o, m, c.X + o * n + o, n, false, tbuf, o, false, c.X + o * n, n,
@@ -628,26 +604,26 @@ hipError_t cholinv_blocked(PrepCtx& c, float* tbuf) {
     float* U_j = c.A + o * n + o + m;
     GPTQ_HIP_TRY(gemm(c, m, rest, m, c.X + o * n + o, n, false, c.A + (o + m) * n + o, n, true,
                       U_j, n, 1.0f, 0.0f, KR_LE_ROW, false));
-    if (pending_rest) GPTQ_HIP_TRY(hipStreamWaitEvent(M, ss->upd_done, 0));
+    if (pending_rest) GPTQ_HIP_TRY(hipStreamWaitEvent(M, ev_upd, 0));
     const int64_t m2 = rest < W ? rest : W;
     GPTQ_HIP_TRY(gemm(c, rest, m2, m, U_j, n, true, U_j, n, false, c.A + (o + m) * n + o + m, n,
                       -1.0f, 1.0f, KR_FULL, true));
     pending_rest = false;
     if (rest > m2) {
-      GPTQ_HIP_TRY(hipEventRecord(ss->panel, M));
-      GPTQ_HIP_TRY(hipStreamWaitEvent(ss->upd, ss->panel, 0));
+      GPTQ_HIP_TRY(hipEventRecord(ev_panel, M));
+      GPTQ_HIP_TRY(hipStreamWaitEvent(UPD, ev_panel, 0));
       const int64_t r2 = rest - m2;
       float* C = c.A + (o + m + m2) * n + o + m + m2;
       GPTQ_HIP_TRY(gemm(cu, r2, r2, m, U_j + m2, n, true, U_j + m2, n, false, C, n, -1.0f, 1.0f,
                         KR_FULL, true));
-      GPTQ_HIP_TRY(hipEventRecord(ss->upd_done, ss->upd));
+      GPTQ_HIP_TRY(hipEventRecord(ev_upd, UPD));
       pending_rest = true;
     }
   }
-  GPTQ_HIP_TRY(hipEventRecord(ss->join_upd, ss->upd));
-  GPTQ_HIP_TRY(hipEventRecord(ss->join_inv, ss->inv));
-  GPTQ_HIP_TRY(hipStreamWaitEvent(M, ss->join_upd, 0));
-  GPTQ_HIP_TRY(hipStreamWaitEvent(M, ss->join_inv, 0));
+  GPTQ_HIP_TRY(hipEventRecord(ev_join_upd, UPD));
+  GPTQ_HIP_TRY(hipEventRecord(ev_join_inv, INV));
+  GPTQ_HIP_TRY(hipStreamWaitEvent(M, ev_join_upd, 0));
+  GPTQ_HIP_TRY(hipStreamWaitEvent(M, ev_join_inv, 0));
   return hipSuccess;
 }
 
