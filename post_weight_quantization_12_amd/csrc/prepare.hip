@@ -247,6 +247,35 @@ __device__ inline float bcast(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// d += c[lane o of this 16-lane row] * ng in one instruction (v_fmac_f32
+// with a DPP row_newbcast source; o must be a constant after unrolling).
+// "first" puts two wait states in front: DPP may not read a register that
+// a VALU instruction wrote less than two instructions before, and c is
+// computed just before the first use.
+#define GPTQ_FMAC_BCAST(O)                                                          \
+  case O:                                                                           \
+    if (first)                                                                      \
+      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:" #O            \
+                   " row_mask:0xf bank_mask:0xf"                                    \
+                   : "+v"(d)                                                        \
+                   : "v"(c), "v"(ng));                                              \
+    else                                                                            \
+      asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #O                     \
+                   " row_mask:0xf bank_mask:0xf"                                    \
+                   : "+v"(d)                                                        \
+                   : "v"(c), "v"(ng));                                              \
+    break;
+__device__ inline void fmac_bcast(float& d, float c, float ng, int o, bool first) {
+  switch (o) {
+    GPTQ_FMAC_BCAST(0) GPTQ_FMAC_BCAST(1) GPTQ_FMAC_BCAST(2) GPTQ_FMAC_BCAST(3)
+    GPTQ_FMAC_BCAST(4) GPTQ_FMAC_BCAST(5) GPTQ_FMAC_BCAST(6) GPTQ_FMAC_BCAST(7)
+    GPTQ_FMAC_BCAST(8) GPTQ_FMAC_BCAST(9) GPTQ_FMAC_BCAST(10) GPTQ_FMAC_BCAST(11)
+    GPTQ_FMAC_BCAST(12) GPTQ_FMAC_BCAST(13) GPTQ_FMAC_BCAST(14) GPTQ_FMAC_BCAST(15)
+    default: break;
+  }
+}
+#undef GPTQ_FMAC_BCAST
+
 // acc += sgn * sum_{k<K} a(r, k) b(k, c) for one 16 x 16 tile (v_mfma_f32_16x16x4f32:
 // lane l supplies a(l%16, k0 + l/16) and b(k0 + l/16, l%16) and holds rows
 // 4(l/16)..+3 of column l%16).  a(r, k) = A[r*LP + k]; b(k, c) = BT ? B[c*LP + k] : B[k*LP + c].
@@ -349,6 +378,11 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) d[j] = j <= li ? d[j] : 0.0f;
+      // Pivot k: column k of L is c = d[k] / sqrt(d_kk) in the rows >= k
+      // (0 above, where the lanes hold upper-triangle entries); every lane
+      // then takes d[j] -= c * c_j for j > k, c_j arriving from lane j by a
+      // DPP broadcast fused into the FMA.  Lane k also updates its own
+      // upper entries (k, j > k): garbage that the store masks.
       int fail = -1;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -356,11 +390,13 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
         if (fail < 0 && !(dk > 0.0f && dk < INFINITY) && c + k < m) fail = k;
         const float r = __builtin_amdgcn_rsqf(dk);
         rv[k] = r;  // 1 / L[k][k]
-        const float lik = li > k ? d[k] * r : (li == k ? dk * r : 0.0f);
-        d[k] = lik;
-        const float g = li > k ? lik : 0.0f;
+        const float ck = li >= k ? d[k] * r : 0.0f;
+        d[k] = ck;
+        const float ng = -ck;
 #pragma unroll
-        for (int j = k + 1; j < 16; ++j) d[j] = fmaf(-g, bcast(lik, j), d[j]);
+        for (int j = k + 1; j < 16; ++j) fmac_bcast(d[j], ck, ng, j, j == k + 1);
+        // two wait states before the next pivot's broadcast of d[k + 1]
+        asm volatile("s_nop 1");
       }
       if (lane < 16) {
         float* wrow = Ls + (c + li) * LP + c;
