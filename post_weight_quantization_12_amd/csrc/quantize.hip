@@ -433,22 +433,22 @@ __device__ inline float row_bcast16(float v, int o) {
   const int x = __float_as_int(v);
   int r;
   switch (o) {
-    case 0: r = __builtin_amdgcn_update_dpp(0, x, 0x150, 0xF, 0xF, false); break;
-    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x151, 0xF, 0xF, false); break;
-    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x152, 0xF, 0xF, false); break;
-    case 3: r = __builtin_amdgcn_update_dpp(0, x, 0x153, 0xF, 0xF, false); break;
-    case 4: r = __builtin_amdgcn_update_dpp(0, x, 0x154, 0xF, 0xF, false); break;
-    case 5: r = __builtin_amdgcn_update_dpp(0, x, 0x155, 0xF, 0xF, false); break;
-    case 6: r = __builtin_amdgcn_update_dpp(0, x, 0x156, 0xF, 0xF, false); break;
-    case 7: r = __builtin_amdgcn_update_dpp(0, x, 0x157, 0xF, 0xF, false); break;
-    case 8: r = __builtin_amdgcn_update_dpp(0, x, 0x158, 0xF, 0xF, false); break;
-    case 9: r = __builtin_amdgcn_update_dpp(0, x, 0x159, 0xF, 0xF, false); break;
-    case 10: r = __builtin_amdgcn_update_dpp(0, x, 0x15A, 0xF, 0xF, false); break;
-    case 11: r = __builtin_amdgcn_update_dpp(0, x, 0x15B, 0xF, 0xF, false); break;
-    case 12: r = __builtin_amdgcn_update_dpp(0, x, 0x15C, 0xF, 0xF, false); break;
-    case 13: r = __builtin_amdgcn_update_dpp(0, x, 0x15D, 0xF, 0xF, false); break;
-    case 14: r = __builtin_amdgcn_update_dpp(0, x, 0x15E, 0xF, 0xF, false); break;
-    default: r = __builtin_amdgcn_update_dpp(0, x, 0x15F, 0xF, 0xF, false); break;
+    case 0: r = __builtin_amdgcn_mov_dpp(x, 0x150, 0xF, 0xF, true); break;
+    case 1: r = __builtin_amdgcn_mov_dpp(x, 0x151, 0xF, 0xF, true); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(x, 0x152, 0xF, 0xF, true); break;
+    case 3: r = __builtin_amdgcn_mov_dpp(x, 0x153, 0xF, 0xF, true); break;
+    case 4: r = __builtin_amdgcn_mov_dpp(x, 0x154, 0xF, 0xF, true); break;
+    case 5: r = __builtin_amdgcn_mov_dpp(x, 0x155, 0xF, 0xF, true); break;
+    case 6: r = __builtin_amdgcn_mov_dpp(x, 0x156, 0xF, 0xF, true); break;
+    case 7: r = __builtin_amdgcn_mov_dpp(x, 0x157, 0xF, 0xF, true); break;
+    case 8: r = __builtin_amdgcn_mov_dpp(x, 0x158, 0xF, 0xF, true); break;
+    case 9: r = __builtin_amdgcn_mov_dpp(x, 0x159, 0xF, 0xF, true); break;
+    case 10: r = __builtin_amdgcn_mov_dpp(x, 0x15A, 0xF, 0xF, true); break;
+    case 11: r = __builtin_amdgcn_mov_dpp(x, 0x15B, 0xF, 0xF, true); break;
+    case 12: r = __builtin_amdgcn_mov_dpp(x, 0x15C, 0xF, 0xF, true); break;
+    case 13: r = __builtin_amdgcn_mov_dpp(x, 0x15D, 0xF, 0xF, true); break;
+    case 14: r = __builtin_amdgcn_mov_dpp(x, 0x15E, 0xF, 0xF, true); break;
+    default: r = __builtin_amdgcn_mov_dpp(x, 0x15F, 0xF, 0xF, true); break;
   }
   return __int_as_float(r);
 }
@@ -537,7 +537,19 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out
       z = (float)zeros[row];
     }
   }
+  float rs = 1.0f / s;
   __syncthreads();
+
+  // U' row of the column being swept, loaded one column ahead so the LDS
+  // latency stays off the column-to-column dependency chain.
+  constexpr int NU = (NR + 3) / 4;
+  auto load_u = [&](int j, float4* dst) {
+    const float* urow = Ul + (j * 16 + q) * PITCH;
+#pragma unroll
+    for (int t = 0; t < NU; ++t) dst[t] = *reinterpret_cast<const float4*>(urow + 4 * t);
+  };
+  float4 ub[NU];
+  load_u(0, ub);
 
   const int nsteps = width / 16;
   for (int R = 0; R < nsteps; ++R) {
@@ -553,6 +565,7 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out
         lo = row_min16(lo);
         hi = row_max16(hi);
         grid_params(lo, hi, bits, sym, s, z);
+        rs = 1.0f / s;
         if (live && q == 0) {
           const int64_t g = (c0 + 16 * R) / GS;
           scales[g * out + row] = s;
@@ -560,26 +573,44 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out
         }
       }
     }
+    float my_err = 0.0f, my_code = 0.0f;  // this lane's column of the step
 #pragma unroll
     for (int o = 0; o < 16; ++o) {
       const int j = 16 * R + o;
+      float4 un[NU];
+#pragma unroll
+      for (int t = 0; t < NU; ++t) un[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (o < 15 || j + 1 < width) load_u(j + 1, un);
       const float wj = row_bcast16(w[0], o);
-      const float qf = fminf(fmaxf(rintf(wj / s) + z, 0.0f), maxq);
-      const float err = wj - s * (qf - z);
-      if (q == o) {
-        Es[rl * EP + j] = err;
-        Cs[rl * B + j] = (uint8_t)qf;
+      // rint(wj / s) with the quotient correctly rounded, without the
+      // division on the dependency chain: y = wj * (1/s) is within
+      // |y| 2^-22 of the rounded quotient, so rint(y) is the same integer
+      // unless y lies that close to a half-integer; those rare lanes (and a
+      // zero or non-finite s) divide.
+      const float y = wj * rs;
+      const float qr = rintf(y);
+      // clamp(qr + z, 0, maxq) - z in one step (small integers: exact)
+      float qz = __builtin_amdgcn_fmed3f(qr, -z, maxq - z);
+      float err = wj - s * qz;
+      if (!(0.5f - fabsf(y - qr) >= fabsf(y) * 0x1p-21f + 0x1p-126f)) {
+        qz = __builtin_amdgcn_fmed3f(rintf(wj / s), -z, maxq - z);
+        err = wj - s * qz;
       }
-      const float* urow = Ul + (j * 16 + q) * PITCH;
+      my_err = q == o ? err : my_err;
+      my_code = q == o ? qz + z : my_code;
 #pragma unroll
       for (int t = 0; t < NR; t += 4) {
-        const float4 u = *reinterpret_cast<const float4*>(urow + t);
+        const float4 u = ub[t / 4];
         w[t + 0] = fmaf(-err, u.x, w[t + 0]);
         if (t + 1 < NR) w[t + 1] = fmaf(-err, u.y, w[t + 1]);
         if (t + 2 < NR) w[t + 2] = fmaf(-err, u.z, w[t + 2]);
         if (t + 3 < NR) w[t + 3] = fmaf(-err, u.w, w[t + 3]);
       }
+#pragma unroll
+      for (int t = 0; t < NU; ++t) ub[t] = un[t];
     }
+    Es[rl * EP + 16 * R + q] = my_err;
+    Cs[rl * B + 16 * R + q] = (uint8_t)my_code;
 #pragma unroll
     for (int t = 0; t + 1 < NR; ++t) w[t] = w[t + 1];
     w[NR - 1] = 0.0f;
