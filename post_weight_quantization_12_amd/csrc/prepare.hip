@@ -615,7 +615,7 @@ hipError_t cholinv_blocked(PrepCtx& c, float* tbuf) {
   HelperStreams* hs = nullptr;
   GPTQ_HIP_TRY(helper_streams(hs));
   const hipStream_t M = c.s, UPD = hs->a, INV = hs->b;
-  hipEvent_t ev_fork = hs->ev[0], ev_panel = hs->ev[1], ev_upd = hs->ev[2], ev_diag = hs->ev[3],
+  hipEvent_t ev_fork = hs->ev[0], ev_step = hs->ev[1], ev_upd = hs->ev[2],
              ev_join_upd = hs->ev[4], ev_join_inv = hs->ev[5];
   PrepCtx cu = c, ci = c;
   cu.s = UPD;
@@ -623,33 +623,48 @@ hipError_t cholinv_blocked(PrepCtx& c, float* tbuf) {
   GPTQ_HIP_TRY(hipEventRecord(ev_fork, M));
   GPTQ_HIP_TRY(hipStreamWaitEvent(UPD, ev_fork, 0));
   GPTQ_HIP_TRY(hipStreamWaitEvent(INV, ev_fork, 0));
+  // One event record and at most one wait per block on the caller's stream
+  // (each costs several microseconds of queue latency on the critical
+  // chain): the record after the next-block update releases both helper
+  // streams.
+  auto inverse_step = [&](int64_t o, int64_t m) -> hipError_t {
+    GPTQ_HIP_TRY(hipStreamWaitEvent(INV, ev_step, 0));
+    // T = L[j, :j] X[:j, :j] = (U[:o, o:o+m])^T X[:o, :o]   (X lower: k >= col)
+    GPTQ_HIP_TRY(gemm(ci, m, o, o, c.A + o, n, true, c.X, n, false, tbuf, o, 1.0f, 0.0f,
+                      KR_GE_COL, false));
+    // X[j, :j] = -X_jj T   (X_jj lower: k <= row)
+    return gemm(ci, m, o, m, c.X + o * n + o, n, false, tbuf, o, false, c.X + o * n, n, -1.0f,
+                0.0f, KR_LE_ROW, false);
+  };
   bool pending_rest = false;
   for (int64_t o = 0; o < n; o += W) {
     const int64_t m = n - o < W ? n - o : W;
     const int64_t rest = n - o - m;
     GPTQ_HIP_TRY(cholinv(c, o, m, c.T2));
-    if (o > 0) {
-      GPTQ_HIP_TRY(hipEventRecord(ev_diag, M));
-      GPTQ_HIP_TRY(hipStreamWaitEvent(INV, ev_diag, 0));
-      GPTQ_HIP_TRY(gemm(ci, m, o, o, c.A + o, n, true, c.X, n, false, tbuf, o, 1.0f, 0.0f,
-                        KR_GE_COL, false));
-      GPTQ_HIP_TRY(gemm(ci, m, o, m, c.X + o * n + o, n, false, tbuf, o, false, c.X + o * n, n,
-                        -1.0f, 0.0f, KR_LE_ROW, false));
+    if (rest == 0) {
+      if (o > 0) {
+        GPTQ_HIP_TRY(hipEventRecord(ev_step, M));
+        GPTQ_HIP_TRY(inverse_step(o, m));
+      }
+      break;
     }
-    if (rest == 0) break;
     float* U_j = c.A + o * n + o + m;
+    // P_j^T = X_jj A[o+m:, o:o+m]^T
     GPTQ_HIP_TRY(gemm(c, m, rest, m, c.X + o * n + o, n, false, c.A + (o + m) * n + o, n, true,
                       U_j, n, 1.0f, 0.0f, KR_LE_ROW, false));
     if (pending_rest) GPTQ_HIP_TRY(hipStreamWaitEvent(M, ev_upd, 0));
     const int64_t m2 = rest < W ? rest : W;
+    // block column j+1 (rows o+m..n, m2 columns) -= P_j P_j[0:m2]^T
     GPTQ_HIP_TRY(gemm(c, rest, m2, m, U_j, n, true, U_j, n, false, c.A + (o + m) * n + o + m, n,
                       -1.0f, 1.0f, KR_FULL, true));
+    GPTQ_HIP_TRY(hipEventRecord(ev_step, M));
     pending_rest = false;
+    if (o > 0) GPTQ_HIP_TRY(inverse_step(o, m));
     if (rest > m2) {
-      GPTQ_HIP_TRY(hipEventRecord(ev_panel, M));
-      GPTQ_HIP_TRY(hipStreamWaitEvent(UPD, ev_panel, 0));
+      GPTQ_HIP_TRY(hipStreamWaitEvent(UPD, ev_step, 0));
       const int64_t r2 = rest - m2;
       float* C = c.A + (o + m + m2) * n + o + m + m2;
+      // the rest of the trailing matrix -= P_j P_j^T (lower tiles)
       GPTQ_HIP_TRY(gemm(cu, r2, r2, m, U_j + m2, n, true, U_j + m2, n, false, C, n, -1.0f, 1.0f,
                         KR_FULL, true));
       GPTQ_HIP_TRY(hipEventRecord(ev_upd, UPD));
