@@ -311,7 +311,29 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15;
 
-  {
+  // Whole blocks with 16-byte aligned rows move as float4 (all eight loads
+  // of a thread in flight at once); ragged or unaligned blocks element-wise.
+  const bool vec = m == NB && (n & 3) == 0 && (off & 3) == 0;
+  if (vec) {
+    constexpr int PER4 = NB * NB / 4 / LEAF_THREADS;
+    float4 v[PER4];
+#pragma unroll
+    for (int u = 0; u < PER4; ++u) {
+      const int e = tid + LEAF_THREADS * u, i = e / (NB / 4), j = 4 * (e % (NB / 4));
+      v[u] = *reinterpret_cast<const float4*>(A + (off + i) * n + off + j);
+    }
+#pragma unroll
+    for (int u = 0; u < PER4; ++u) {
+      const int e = tid + LEAF_THREADS * u, i = e / (NB / 4), j = 4 * (e % (NB / 4));
+      float4 l;
+      l.x = j + 0 <= i ? v[u].x : 0.0f;
+      l.y = j + 1 <= i ? v[u].y : 0.0f;
+      l.z = j + 2 <= i ? v[u].z : 0.0f;
+      l.w = j + 3 <= i ? v[u].w : 0.0f;
+      *reinterpret_cast<float4*>(Ls + i * LP + j) = l;
+      *reinterpret_cast<float4*>(Xs + i * LP + j) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
     // 8 loads per thread in flight (addresses of masked-out elements are
     // clamped to the block's first element).
     constexpr int PER = NB * NB / LEAF_THREADS;
@@ -496,9 +518,20 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
     __syncthreads();
     }
 
-  for (int i = tid / NB; i < m; i += LEAF_THREADS / NB) {
-    const int j = tid % NB;
-    if (j <= i) X[(off + i) * n + off + j] = Xs[i * LP + j];
+  if (vec) {
+    // whole rows of the block: the entries above the diagonal are the zeros
+    // X already holds there
+#pragma unroll
+    for (int u = 0; u < NB * NB / 4 / LEAF_THREADS; ++u) {
+      const int e = tid + LEAF_THREADS * u, i = e / (NB / 4), j = 4 * (e % (NB / 4));
+      *reinterpret_cast<float4*>(X + (off + i) * n + off + j) =
+          *reinterpret_cast<const float4*>(Xs + i * LP + j);
+    }
+  } else {
+    for (int i = tid / NB; i < m; i += LEAF_THREADS / NB) {
+      const int j = tid % NB;
+      if (j <= i) X[(off + i) * n + off + j] = Xs[i * LP + j];
+    }
   }
 }
 
