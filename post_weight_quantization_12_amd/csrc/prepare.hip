@@ -279,17 +279,30 @@ __device__ inline void fmac_bcast(float& d, float c, float ng, int o, bool first
 // acc += sgn * sum_{k<K} a(r, k) b(k, c) for one 16 x 16 tile (v_mfma_f32_16x16x4f32:
 // lane l supplies a(l%16, k0 + l/16) and b(k0 + l/16, l%16) and holds rows
 // 4(l/16)..+3 of column l%16).  a(r, k) = A[r*LP + k]; b(k, c) = BT ? B[c*LP + k] : B[k*LP + c].
-template <bool BT>
-__device__ inline f32x4_t tile16(const float* A, const float* B, int K, f32x4_t acc, float sgn,
+// All operands are read first and the K/4 products go to up to four
+// accumulators in turn, so neither the LDS latency nor the MFMA latency
+// serializes the loop.
+template <bool BT, int K>
+__device__ inline f32x4_t tile16(const float* A, const float* B, f32x4_t acc, float sgn,
                                   int lane) {
   const int r = lane & 15, kq = lane >> 4;
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += 4) {
-    const float a = sgn * A[r * LP + k0 + kq];
-    const float b = BT ? B[r * LP + k0 + kq] : B[(k0 + kq) * LP + r];
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+  constexpr int NK = K / 4, NA = NK < 4 ? NK : 4;
+  float a[NK], b[NK];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    a[i] = sgn * A[r * LP + 4 * i + kq];
+    b[i] = BT ? B[r * LP + 4 * i + kq] : B[(4 * i + kq) * LP + r];
   }
-  return acc;
+  f32x4_t part[NA];
+  part[0] = acc;
+#pragma unroll
+  for (int p = 1; p < NA; ++p) part[p] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NK; ++i)
+    part[i % NA] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], part[i % NA], 0, 0, 0);
+#pragma unroll
+  for (int p = 1; p < NA; ++p) part[0] += part[p];
+  return part[0];
 }
 __device__ inline f32x4_t load_tile(const float* C, int lane) {
   f32x4_t v;
@@ -300,6 +313,43 @@ __device__ inline f32x4_t load_tile(const float* C, int lane) {
 __device__ inline void store_tile(float* C, f32x4_t v, int lane) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) C[(4 * (lane >> 4) + q) * LP + (lane & 15)] = v[q];
+}
+
+// One doubling level of the leaf's inverse: for each pair of SZ-blocks on the
+// diagonal, T = L21 X11 (into the X21 area), then X21 = -X22 T.
+template <int SZ>
+__device__ inline void doubling_level(const float* Ls, float* Xs, int wave, int lane) {
+  constexpr int PER = (SZ / 16) * (SZ / 16), TILES = (NB / (2 * SZ)) * PER;
+  constexpr int NWAVE = LEAF_THREADS / 64, HOLD = (TILES + NWAVE - 1) / NWAVE;
+  for (int t = wave; t < TILES; t += NWAVE) {
+    const int o = (t / PER) * 2 * SZ, ti = (t % PER) / (SZ / 16), tj = (t % PER) % (SZ / 16);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    acc = tile16<false, SZ>(Ls + (o + SZ + 16 * ti) * LP + o, Xs + o * LP + o + 16 * tj, acc,
+                            1.0f, lane);
+    store_tile(Xs + (o + SZ + 16 * ti) * LP + o + 16 * tj, acc, lane);
+  }
+  __syncthreads();
+  f32x4_t res[HOLD];
+#pragma unroll
+  for (int h = 0; h < HOLD; ++h) {
+    const int t = wave + h * NWAVE;
+    res[h] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    if (t < TILES) {
+      const int o = (t / PER) * 2 * SZ, ti = (t % PER) / (SZ / 16), tj = (t % PER) % (SZ / 16);
+      res[h] = tile16<false, SZ>(Xs + (o + SZ + 16 * ti) * LP + o + SZ,
+                                 Xs + (o + SZ) * LP + o + 16 * tj, res[h], -1.0f, lane);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < HOLD; ++h) {
+    const int t = wave + h * NWAVE;
+    if (t < TILES) {
+      const int o = (t / PER) * 2 * SZ, ti = (t % PER) / (SZ / 16), tj = (t % PER) % (SZ / 16);
+      store_tile(Xs + (o + SZ + 16 * ti) * LP + o + 16 * tj, res[h], lane);
+    }
+  }
+  __syncthreads();
 }
 
 __global__ void __launch_bounds__(LEAF_THREADS)
@@ -468,8 +518,8 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
           const int tj = t - ti * (ti + 1) / 2;
           float* C = Ls + (base + 16 * ti) * LP + base + 16 * tj;
           f32x4_t acc = load_tile(C, lane);
-          acc = tile16<true>(Ls + (base + 16 * ti) * LP + c, Ls + (base + 16 * tj) * LP + c, 16, acc,
-                             -1.0f, lane);
+          acc = tile16<true, 16>(Ls + (base + 16 * ti) * LP + c, Ls + (base + 16 * tj) * LP + c,
+                                 acc, -1.0f, lane);
           store_tile(C, acc, lane);
         }
       }
@@ -483,40 +533,10 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
   // Off-diagonal blocks of X by doubling: for blocks of 2s (s = 16, 32, 64)
   //   T = L21 X11 (into the X21 area), X21 = -X22 T,
   // with every level's tiles spread over the 8 waves (16 x 16 MFMA tiles).
-#pragma unroll 1
-  for (int sz = 16; sz < NB; sz *= 2) {
-    const int per = (sz / 16) * (sz / 16), tiles = (NB / (2 * sz)) * per;
-    for (int t = wave; t < tiles; t += LEAF_THREADS / 64) {
-      const int o = (t / per) * 2 * sz, ti = (t % per) / (sz / 16), tj = (t % per) % (sz / 16);
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = tile16<false>(Ls + (o + sz + 16 * ti) * LP + o, Xs + o * LP + o + 16 * tj, sz, acc,
-                          1.0f, lane);
-      store_tile(Xs + (o + sz + 16 * ti) * LP + o + 16 * tj, acc, lane);
-    }
-    __syncthreads();
-    constexpr int HOLD = (NB / 2 / 16) * (NB / 2 / 16) / (LEAF_THREADS / 64);  // tiles per wave, top level
-    f32x4_t res[HOLD];
-#pragma unroll
-    for (int h = 0; h < HOLD; ++h) {
-      const int t = wave + h * (LEAF_THREADS / 64);
-      res[h] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      if (t < tiles) {
-        const int o = (t / per) * 2 * sz, ti = (t % per) / (sz / 16), tj = (t % per) % (sz / 16);
-        res[h] = tile16<false>(Xs + (o + sz + 16 * ti) * LP + o + sz, Xs + (o + sz) * LP + o + 16 * tj,
-                               sz, res[h], -1.0f, lane);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < HOLD; ++h) {
-      const int t = wave + h * (LEAF_THREADS / 64);
-      if (t < tiles) {
-        const int o = (t / per) * 2 * sz, ti = (t % per) / (sz / 16), tj = (t % per) % (sz / 16);
-        store_tile(Xs + (o + sz + 16 * ti) * LP + o + 16 * tj, res[h], lane);
-      }
-    }
-    __syncthreads();
-    }
+  doubling_level<16>(Ls, Xs, wave, lane);
+  doubling_level<32>(Ls, Xs, wave, lane);
+  doubling_level<64>(Ls, Xs, wave, lane);
+  static_assert(NB == 128, "three doubling levels");
 
   if (vec) {
     // whole rows of the block: the entries above the diagonal are the zeros
