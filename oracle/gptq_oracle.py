@@ -52,6 +52,7 @@ __all__ = [
     "pack",
     "unpack",
     "dequantize",
+    "dequant_matmul",
     "layer_error",
 ]
 
@@ -400,6 +401,22 @@ def dequantize(codes, scales, zeros, g_idx) -> np.ndarray:
     s = np.asarray(scales, dtype=np.float64)[g, :].T
     z = np.asarray(zeros, dtype=np.float64)[g, :].T
     return s * (codes - z)
+
+
+def dequant_matmul(x, qweight, scales, zeros, g_idx, bits: int) -> np.ndarray:
+    """Y = X W^T with W the layer's dequantized weights, in float64.
+
+    [GLOSS] paragraph "Inference": the quantized layer is applied by
+    dequantizing the weights during the computation and multiplying.  The
+    definition written out: Y[t, r] = sum_k X[t, k] * s[g_idx[k], r] *
+    (code[r, k] - z[g_idx[k], r]), with code[r, k] the k-th b-bit field of
+    row r's little-endian bit stream in qweight (the packed layer as
+    gptq_quantize_layer writes it; see ``unpack``).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[1]
+    codes = unpack(qweight, bits, n)
+    return x @ dequantize(codes, scales, zeros, g_idx).T
 
 
 def layer_error(W, What, H) -> float:

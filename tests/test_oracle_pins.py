@@ -421,3 +421,75 @@ def test_pack_roundtrip(bits):
 def test_g_index():
     assert O.g_index([1, 3, 2, 0], 2).tolist() == [1, 0, 1, 0]
     assert O.g_index([0, 1, 2], -1).tolist() == [0, 0, 0]
+
+
+# ----------------------------------------------------------- dequant_matmul --
+def test_dequant_matmul_worked_example():
+    # One output row, 32 inputs, 4-bit: word 0 = 0x87654321 holds codes
+    # 1..8 for inputs 0..7, the other words are 0.  Groups of 16: group 0
+    # scale 0.5 zero 1, group 1 scale 2 zero 0.  W^ = 0.5 k for k < 8,
+    # -0.5 for 8 <= k < 16, 0 above.  Token 1 (all ones): 0.5*28 - 0.5*8 = 10;
+    # token 2 (x_k = k): 0.5*140 - 0.5*92 = 24.
+    qw = np.zeros((4, 1), dtype=np.int64)
+    qw[0, 0] = 0x87654321
+    qw = qw.astype(np.uint32).view(np.int32)
+    scales = np.array([[0.5], [2.0]], dtype=np.float32)
+    zeros = np.array([[1], [0]], dtype=np.int32)
+    g_idx = np.array([0] * 16 + [1] * 16, dtype=np.int32)
+    x = np.stack([np.ones(32), np.arange(32.0)])
+    y = O.dequant_matmul(x, qw, scales, zeros, g_idx, 4)
+    assert y.shape == (2, 1)
+    assert y[:, 0].tolist() == [10.0, 24.0]
+
+
+def _bit_loop_codes(qweight, bits, n):
+    """Codes by walking the bit stream one bit at a time (independent of
+    O.unpack's vectorized form)."""
+    q = np.asarray(qweight).astype(np.int64) & 0xFFFFFFFF
+    out = q.shape[1]
+    codes = np.zeros((out, n), dtype=np.int64)
+    for r in range(out):
+        for k in range(n):
+            v = 0
+            for i in range(bits):
+                pos = k * bits + i
+                v |= ((int(q[pos // 32, r]) >> (pos % 32)) & 1) << i
+            codes[r, k] = v
+    return codes
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_dequant_matmul_brute_force(bits):
+    rng = np.random.default_rng(10 + bits)
+    out, n, t, gs = 3, 64, 2, 16
+    codes = rng.integers(0, 2 ** bits, size=(out, n))
+    qw = O.pack(codes, bits)
+    perm = rng.permutation(n)
+    g_idx = O.g_index(perm, gs)
+    scales = rng.uniform(0.1, 1.0, size=(n // gs, out)).astype(np.float32)
+    zeros = rng.integers(0, 2 ** bits, size=(n // gs, out)).astype(np.int32)
+    x = rng.normal(size=(t, n)).astype(np.float16).astype(np.float64)
+    y = O.dequant_matmul(x, qw, scales, zeros, g_idx, bits)
+    c2 = _bit_loop_codes(qw, bits, n)
+    ref = np.zeros((t, out))
+    for a in range(t):
+        for r in range(out):
+            ref[a, r] = sum(x[a, k] * float(scales[g_idx[k], r]) * (c2[r, k] - int(zeros[g_idx[k], r]))
+                            for k in range(n))
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_dequant_matmul_input_permutation_invariant():
+    # Reordering the input features (X columns, the codes' positions in the
+    # stream, g_idx) together leaves Y unchanged.
+    rng = np.random.default_rng(3)
+    out, n, gs, bits = 5, 96, 32, 4
+    codes = rng.integers(0, 16, size=(out, n))
+    g_idx = O.g_index(rng.permutation(n), gs)
+    scales = rng.uniform(0.1, 1.0, size=(n // gs, out)).astype(np.float32)
+    zeros = rng.integers(0, 16, size=(n // gs, out)).astype(np.int32)
+    x = rng.normal(size=(4, n))
+    y = O.dequant_matmul(x, O.pack(codes, bits), scales, zeros, g_idx, bits)
+    p = rng.permutation(n)
+    y2 = O.dequant_matmul(x[:, p], O.pack(codes[:, p], bits), scales, zeros, g_idx[p], bits)
+    assert np.allclose(y, y2, rtol=1e-12, atol=1e-12)
