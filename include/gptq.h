@@ -192,6 +192,46 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in,
                         int32_t* g_idx, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* Workspace (bytes) gptq_dequant_matmul needs for M token rows, in inputs and
+ * out outputs: the partial sums of the split input range when M <= 16 (e.g.
+ * 8 x 1 x 4096 fp32 for one token of a 4096 x 4096 layer); 0 otherwise. */
+size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out);
+
+/*
+ * Dequantize-on-the-fly matmul: Y = X W^T for a layer quantized by
+ * gptq_quantize_layer.
+ *
+ * Glossary entry "gptq", paragraph "Inference": the quantized weights are
+ * dequantized during the computation and multiplied.  Here
+ *     W[r][k] = scales[g_idx[k]][r] * (code[r][k] - zeros[g_idx[k]][r]),
+ * code[r][k] the k-th b-bit field of row r's little-endian bit stream
+ * (qweight[j][r] is word j of it), and Y[t][r] = sum_k X[t][k] W[r][k].
+ *
+ *   X        fp16 [M x in], row-major, leading dimension ldx >= in, ldx a
+ *            multiple of 8, X 16-byte aligned.  M == 0 is a no-op.
+ *   qweight  int32 [in * bits / 32 x out]; scales fp32 and zeros int32
+ *            [n_groups x out]; g_idx int32 [in] with values in
+ *            [0, n_groups) (not checked: device data).
+ *   in       a positive multiple of 32; out >= 1; bits 2, 3, 4 or 8.
+ *   Y        out: [M x out], row-major, ldy >= out, y_dtype GPTQ_F32 or
+ *            GPTQ_F16 (the fp32 sum rounded to nearest).
+ *   workspace  device memory of gptq_dequant_matmul_workspace_bytes(M, in,
+ *            out) bytes, or NULL when that is 0.
+ *
+ * Arithmetic: M <= 16 dequantizes each weight in fp32 and accumulates fp32
+ * FMAs (HBM-bound on qweight); larger M rounds each dequantized weight to
+ * fp16 (scale rounded to fp16, then one rounding of the product) and
+ * multiplies on the fp16 matrix cores with fp32 accumulation.  Results do
+ * not depend on timing.  Calls that share a workspace must not overlap.
+ * Errors: INVALID_ARG, UNSUPPORTED (x_dtype not F16, bits, alignment),
+ *         WORKSPACE, HIP.
+ */
+int gptq_dequant_matmul(const void* X, int x_dtype, int64_t M, int64_t in, int64_t ldx,
+                        const int32_t* qweight, const float* scales, const int32_t* zeros,
+                        const int32_t* g_idx, int64_t n_groups, int64_t out, int bits, void* Y,
+                        int y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* Static text for a gptq_status_t value. */
 const char* gptq_status_string(int status);
 

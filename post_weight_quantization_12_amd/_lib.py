@@ -61,6 +61,11 @@ def load():
     lib.gptq_quantize_layer.argtypes = [vp, c_int, i64, i64, vp, vp, c_int, c_int, c_int, c_int,
                                         vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.gptq_quantize_layer.restype = c_int
+    lib.gptq_dequant_matmul_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.gptq_dequant_matmul_workspace_bytes.restype = ctypes.c_size_t
+    lib.gptq_dequant_matmul.argtypes = [vp, c_int, i64, i64, i64, vp, vp, vp, vp, i64, i64, c_int,
+                                        vp, c_int, i64, vp, ctypes.c_size_t, vp]
+    lib.gptq_dequant_matmul.restype = c_int
     lib.gptq_status_string.argtypes = [c_int]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_last_error_message.argtypes = []
@@ -208,3 +213,51 @@ def quantize_layer(W, Hinv_chol, perm, bits: int, group_size: int, sym: bool, bl
                                    _ptr(g_idx), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
     return qweight, scales, zeros, g_idx
+
+
+def dequant_matmul_workspace_bytes(M: int, inp: int, out: int) -> int:
+    return int(load().gptq_dequant_matmul_workspace_bytes(M, inp, out))
+
+
+def dequant_matmul(X, qweight, scales, zeros, g_idx, bits: int, out_dtype=None, Y=None,
+                   workspace=None, stream=None):
+    """Y = X W^T with W dequantized on the fly from the packed layer
+    (qweight int32 [in*bits/32 x out], scales fp32 / zeros int32
+    [n_groups x out], g_idx int32 [in]) for fp16 X [M x in].  Y is fp32
+    (default) or fp16 [M x out]."""
+    torch = _torch()
+    lib = load()
+    for name, t in (("X", X), ("qweight", qweight), ("scales", scales), ("zeros", zeros),
+                    ("g_idx", g_idx)):
+        _need_cuda(name, t)
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be [M x in] with unit column stride")
+    M, inp = X.shape
+    if qweight.dtype != torch.int32 or qweight.dim() != 2 or not qweight.is_contiguous():
+        raise ValueError("qweight must be a contiguous int32 [in*bits/32 x out] tensor")
+    if qweight.shape[0] * 32 != inp * bits:
+        raise ValueError("qweight rows must be in * bits / 32")
+    out = qweight.shape[1]
+    G = scales.shape[0]
+    if scales.dtype != torch.float32 or tuple(scales.shape) != (G, out) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous fp32 [n_groups x out] tensor")
+    if zeros.dtype != torch.int32 or tuple(zeros.shape) != (G, out) or not zeros.is_contiguous():
+        raise ValueError("zeros must be a contiguous int32 [n_groups x out] tensor")
+    if g_idx.dtype != torch.int32 or tuple(g_idx.shape) != (inp,):
+        raise ValueError("g_idx must be an int32 [in] tensor")
+    if out_dtype is None:
+        out_dtype = torch.float32 if Y is None else Y.dtype
+    if Y is None:
+        Y = torch.empty((M, out), dtype=out_dtype, device=X.device)
+    if Y.dim() != 2 or tuple(Y.shape) != (M, out) or Y.stride(1) != 1:
+        raise ValueError("Y must be [M x out] with unit column stride")
+    if workspace is None:
+        need = dequant_matmul_workspace_bytes(M, inp, out)
+        workspace = torch.empty((need,), dtype=torch.uint8, device=X.device) if need else None
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
+    _check(lib.gptq_dequant_matmul(_ptr(X), _dtype_code(X.dtype), M, inp,
+                                   X.stride(0) if M > 1 else inp, _ptr(qweight), _ptr(scales),
+                                   _ptr(zeros), _ptr(g_idx), G, out, bits, _ptr(Y),
+                                   _dtype_code(Y.dtype), Y.stride(0) if M > 1 else out, ws_ptr,
+                                   ws_bytes, _stream(stream)))
+    return Y

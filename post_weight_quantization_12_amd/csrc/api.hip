@@ -162,6 +162,48 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in,
                     "gptq_quantize_layer");
 }
 
+size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out) {
+  if (M < 1 || in < 32 || in % 32 != 0 || out < 1) return 0;
+  return dequant_matmul_workspace_bytes(M, in, out);
+}
+
+int gptq_dequant_matmul(const void* X, int x_dtype, int64_t M, int64_t in, int64_t ldx,
+                        const int32_t* qweight, const float* scales, const int32_t* zeros,
+                        const int32_t* g_idx, int64_t n_groups, int64_t out, int bits, void* Y,
+                        int y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  clear_error();
+  if (!X) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL");
+  if (!qweight || !scales || !zeros || !g_idx)
+    return fail(GPTQ_ERR_INVALID_ARG, "qweight, scales, zeros or g_idx is NULL");
+  if (!Y) return fail(GPTQ_ERR_INVALID_ARG, "Y is NULL");
+  if (M < 0) return fail(GPTQ_ERR_INVALID_ARG, "M must be >= 0");
+  if (in < 32 || in % 32 != 0)
+    return fail(GPTQ_ERR_INVALID_ARG, "in must be a positive multiple of 32");
+  if (out < 1) return fail(GPTQ_ERR_INVALID_ARG, "out must be >= 1");
+  if (n_groups < 1) return fail(GPTQ_ERR_INVALID_ARG, "n_groups must be >= 1");
+  if (ldx < in) return fail(GPTQ_ERR_INVALID_ARG, "ldx must be >= in");
+  if (ldy < out) return fail(GPTQ_ERR_INVALID_ARG, "ldy must be >= out");
+  if (x_dtype != GPTQ_F16) return fail(GPTQ_ERR_UNSUPPORTED, "x_dtype must be GPTQ_F16");
+  if (y_dtype != GPTQ_F16 && y_dtype != GPTQ_F32)
+    return fail(GPTQ_ERR_INVALID_ARG, "y_dtype must be GPTQ_F16 or GPTQ_F32");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits must be 2, 3, 4 or 8");
+  if (ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(X) & 15) != 0)
+    return fail(GPTQ_ERR_UNSUPPORTED, "X rows must be 16-byte aligned (ldx a multiple of 8)");
+  if (M == 0) return GPTQ_OK;
+  const size_t need = dequant_matmul_workspace_bytes(M, in, out);
+  if (need > 0 && !workspace) return fail(GPTQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(GPTQ_ERR_WORKSPACE,
+                "workspace smaller than gptq_dequant_matmul_workspace_bytes(...) = " +
+                    std::to_string(need));
+  return hip_status(run_dequant_matmul(X, M, in, ldx, qweight, scales, zeros, g_idx, out, bits, Y,
+                                       y_dtype == GPTQ_F16 ? 1 : 0, ldy, workspace,
+                                       static_cast<hipStream_t>(stream)),
+                    "gptq_dequant_matmul");
+}
+
 const char* gptq_status_string(int status) {
   switch (status) {
     case GPTQ_OK: return "GPTQ_OK";

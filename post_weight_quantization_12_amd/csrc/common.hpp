@@ -110,6 +110,16 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                         int32_t* qweight, float* scales, int32_t* zeros, int32_t* g_idx,
                         void* ws, hipStream_t s);
 
+// Dequantize-on-the-fly matmul Y = X W^T from the packed layer.  Up to
+// DQ_SMALL_M_MAX token rows take the HBM-bound kernel (its workspace holds
+// the split input range's partial sums), more the MFMA tiles.
+constexpr int DQ_SMALL_M_MAX = 16;
+size_t dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out);
+hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
+                              const int32_t* qweight, const float* scales, const int32_t* zeros,
+                              const int32_t* g_idx, int64_t out, int bits, void* Y, int y_f16,
+                              int64_t ldy, void* ws, hipStream_t s);
+
 }  // namespace gptq
 
 #define GPTQ_HIP_TRY(expr)                  \

@@ -1,0 +1,385 @@
+// Dequantize-on-the-fly matmul Y = X W^T from the packed layer on gfx950.
+//
+// The glossary entry "gptq" (paragraph "Inference") applies a quantized
+// layer by dequantizing its weights during the computation and multiplying.
+// The layer arrives as gptq_quantize_layer writes it: qweight int32
+// [in * b / 32 x out] (row r's codes form a little-endian b-bit stream along
+// the input dimension, word j of that stream in qweight[j][r]), scales fp32
+// and zeros int32 [n_groups x out], g_idx int32 [in]:
+//     W[r][k] = scales[g_idx[k]][r] * (code[r][k] - zeros[g_idx[k]][r]).
+// A 32-code chunk of a row's stream is exactly b words, so every kernel here
+// walks the input dimension 32 k at a time, whatever b is.
+//
+// Two kernels:
+//   * few tokens (M <= 16, decode): HBM-bound on qweight.  Lane = output
+//     column (a wave's 64 columns read 256 contiguous bytes per word row),
+//     the four waves of a workgroup take interleaved chunks of the
+//     workgroup's input range, weights are dequantized exactly in fp32 and
+//     multiplied into up to 16 token rows held in registers; X's slice of
+//     the input range is staged in LDS.  The input dimension is split over
+//     several workgroups (grid >= 2 per compute unit); their partial sums go
+//     to the workspace and a second kernel adds them in a fixed order.
+//   * many tokens (prefill): 128 x 128 tiles on v_mfma_f32_32x32x16_f16.
+//     Per 32-k chunk the X tile goes to LDS as is (k contiguous: an MFMA A
+//     operand is one 16-byte read) and the weight tile is dequantized into
+//     LDS as fp16 column-major (k contiguous: a B operand is one 16-byte
+//     read): a code pair becomes the half2 (1024 + q0, 1024 + q1) by OR-ing
+//     it into 0x6400 0x6400, minus (1024 + z) (exact: integers below 2048),
+//     times the fp16 scale (one rounding).
+#include "common.hpp"
+
+namespace gptq {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int DQ_CHUNK = 32;   // k per chunk
+constexpr int SMALL_COLS = 64; // output columns per small-M workgroup
+constexpr int SMALL_LDS_MAX = 64 * 1024;
+
+// Code k (0..31, a constant after unrolling) of a chunk whose B words are
+// w[0..B-1] (w[B] == 0).
+template <int B>
+__device__ inline uint32_t chunk_code(const uint32_t* w, int k) {
+  const int pos = k * B, wi = pos / 32, off = pos % 32;
+  const uint32_t lo = w[wi] >> off;
+  const uint32_t v = off + B <= 32 ? lo : (lo | (w[wi + 1] << (32 - off)));
+  return v & ((1u << B) - 1u);
+}
+
+// ---------------------------------------------------------------- small M --
+// Grid: (ceil(out / 64), nsplit).  Workgroup (bx, by) covers columns
+// [64 bx, 64 bx + 64) and chunks [by * cps, min((by + 1) * cps, in / 32)).
+// MB = token rows held per lane (>= M, a power of two up to 16).
+template <int B, int MB>
+__global__ void __launch_bounds__(256)
+dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
+                const uint32_t* __restrict__ qw, const float* __restrict__ scales,
+                const int32_t* __restrict__ zeros, const int32_t* __restrict__ g_idx,
+                int64_t out, int64_t cps, float* __restrict__ part, void* __restrict__ Y,
+                int y_f16, int64_t ldy) {
+  extern __shared__ __align__(16) float xs[];  // [len][MB], fp32 (k-major)
+  const int tid = threadIdx.x, lane = tid & 63;
+  // uniform: the chunk index, g_idx reads and the group test stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t col = (int64_t)blockIdx.x * SMALL_COLS + lane;
+  const bool live = col < out;
+  const int64_t colc = live ? col : out - 1;  // loads stay in bounds, unconditional
+  const int64_t nch = in / DQ_CHUNK;
+  const int64_t c0 = (int64_t)blockIdx.y * cps;
+  const int64_t c1 = c0 + cps < nch ? c0 + cps : nch;
+  const int len = (int)((c1 - c0) * DQ_CHUNK);
+  for (int e = tid; e < MB * len; e += 256) {
+    const int m = e / len, k = e % len;
+    xs[k * MB + m] = m < M ? (float)X[m * ldx + c0 * DQ_CHUNK + k] : 0.0f;
+  }
+  __syncthreads();
+
+  float acc[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[m] = 0.0f;
+  for (int64_t c = c0 + wave; c < c1; c += 4) {
+    uint32_t w[B + 1];
+#pragma unroll
+    for (int i = 0; i < B; ++i) w[i] = qw[(c * B + i) * out + colc];
+    w[B] = 0u;
+    const int64_t kb = c * DQ_CHUNK;
+    const int xo = (int)(kb - c0 * DQ_CHUNK);
+    // the chunk's groups (uniform); one group for all 32 k is the common case
+    int gk[DQ_CHUNK];
+    bool one = true;
+#pragma unroll
+    for (int k = 0; k < DQ_CHUNK; ++k) {
+      gk[k] = g_idx[kb + k];
+      one = one && gk[k] == gk[0];
+    }
+    float sk[DQ_CHUNK], zk[DQ_CHUNK];
+    if (one) {
+      const float s = scales[gk[0] * out + colc], z = (float)zeros[gk[0] * out + colc];
+#pragma unroll
+      for (int k = 0; k < DQ_CHUNK; ++k) { sk[k] = s; zk[k] = z; }
+    } else {
+#pragma unroll
+      for (int k = 0; k < DQ_CHUNK; ++k) {
+        sk[k] = scales[gk[k] * out + colc];
+        zk[k] = (float)zeros[gk[k] * out + colc];
+      }
+    }
+#pragma unroll
+    for (int k4 = 0; k4 < DQ_CHUNK; k4 += 4) {
+      // x[k4 .. k4 + 3][0 .. MB): 4 MB contiguous floats
+      float xv[4 * MB];
+#pragma unroll
+      for (int q = 0; q < MB; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(xs + (xo + k4) * MB + 4 * q);
+        xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = k4 + kk;
+        const float wv = sk[k] * ((float)chunk_code<B>(w, k) - zk[k]);
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[m] = fmaf(xv[kk * MB + m], wv, acc[m]);
+      }
+    }
+  }
+  // the four waves' sums, in wave order
+  __syncthreads();
+  float* red = xs;  // [4][MB][64]
+#pragma unroll
+  for (int m = 0; m < MB; ++m) red[(wave * MB + m) * 64 + lane] = acc[m];
+  __syncthreads();
+  for (int e = tid; e < MB * 64; e += 256) {
+    const int m = e / 64, l = e % 64;
+    const int64_t cc = (int64_t)blockIdx.x * SMALL_COLS + l;
+    if (m >= M || cc >= out) continue;
+    const float v = ((red[(0 * MB + m) * 64 + l] + red[(1 * MB + m) * 64 + l]) +
+                     red[(2 * MB + m) * 64 + l]) + red[(3 * MB + m) * 64 + l];
+    if (gridDim.y > 1) {
+      part[((int64_t)blockIdx.y * M + m) * out + cc] = v;
+    } else if (y_f16) {
+      static_cast<_Float16*>(Y)[m * ldy + cc] = (_Float16)v;
+    } else {
+      static_cast<float*>(Y)[m * ldy + cc] = v;
+    }
+  }
+}
+
+// Y = sum of the nsplit partials, in split order.
+__global__ void __launch_bounds__(256)
+dq_reduce_kernel(const float* __restrict__ part, int nsplit, int64_t M, int64_t out,
+                 void* __restrict__ Y, int y_f16, int64_t ldy) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= M * out) return;
+  const int64_t m = e / out, cc = e % out;
+  float v = part[e];
+  for (int s = 1; s < nsplit; ++s) v += part[(int64_t)s * M * out + e];
+  if (y_f16)
+    static_cast<_Float16*>(Y)[m * ldy + cc] = (_Float16)v;
+  else
+    static_cast<float*>(Y)[m * ldy + cc] = v;
+}
+
+// ---------------------------------------------------------------- MFMA path --
+constexpr int TB = 128;          // tile rows (tokens) and columns (outputs)
+constexpr int XP = DQ_CHUNK + 8; // LDS pitch in halves (80 bytes, 16-byte aligned rows)
+
+// Grid: (ceil(out / 128), ceil(M / 128)); 4 waves, each a 64 x 64 block.
+template <int B>
+__global__ void __launch_bounds__(256)
+dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
+               const uint32_t* __restrict__ qw, const float* __restrict__ scales,
+               const int32_t* __restrict__ zeros, const int32_t* __restrict__ g_idx,
+               int64_t out, void* __restrict__ Y, int y_f16, int64_t ldy) {
+  __shared__ __align__(16) _Float16 Xs[TB * XP];
+  __shared__ __align__(16) _Float16 Ws[TB * XP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t m0 = (int64_t)blockIdx.y * TB, n0 = (int64_t)blockIdx.x * TB;
+  // weight dequantization: column wc, codes 16 wh .. 16 wh + 15 of each chunk
+  const int wc = tid % TB;
+  const int wh = __builtin_amdgcn_readfirstlane(tid / TB);  // uniform within a wave
+  const int64_t wcol = n0 + wc;
+  const int64_t wcolc = wcol < out ? wcol : out - 1;  // in-bounds loads; columns >= out never stored
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+  const int64_t nch = in / DQ_CHUNK;
+  for (int64_t c = 0; c < nch; ++c) {
+    const int64_t kb = c * DQ_CHUNK;
+    // X tile: rows t / 4 and t / 4 + 64, k-octet t % 4
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = tid / 4 + 64 * i, o = 8 * (tid % 4);
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (m0 + r < M) v = *reinterpret_cast<const uint4*>(X + (m0 + r) * ldx + kb + o);
+      *reinterpret_cast<uint4*>(Xs + r * XP + o) = v;
+    }
+    // weight tile: 16 codes of column wc
+    {
+      uint32_t w[B + 1];
+#pragma unroll
+      for (int i = 0; i < B; ++i) w[i] = qw[(c * B + i) * out + wcolc];
+      w[B] = 0u;
+      // groups of the 16 k (uniform within the wave)
+      int gk[16];
+      bool one = true;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        gk[k] = g_idx[kb + 16 * wh + k];
+        one = one && gk[k] == gk[0];
+      }
+      half2_t sh[8], zz[8];
+      if (one) {
+        const float s = scales[gk[0] * out + wcolc], z = (float)zeros[gk[0] * out + wcolc];
+        const half2_t s2 = {(_Float16)s, (_Float16)s};
+        const half2_t z2 = {(_Float16)(1024.0f + z), (_Float16)(1024.0f + z)};
+#pragma unroll
+        for (int p = 0; p < 8; ++p) { sh[p] = s2; zz[p] = z2; }
+      } else {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const float s0 = scales[gk[2 * p] * out + wcolc], s1 = scales[gk[2 * p + 1] * out + wcolc];
+          const float z0 = (float)zeros[gk[2 * p] * out + wcolc];
+          const float z1 = (float)zeros[gk[2 * p + 1] * out + wcolc];
+          sh[p] = (half2_t){(_Float16)s0, (_Float16)s1};
+          zz[p] = (half2_t){(_Float16)(1024.0f + z0), (_Float16)(1024.0f + z1)};
+        }
+      }
+      uint32_t packed[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int k = 16 * wh + 2 * p;
+        const uint32_t q2 =
+            chunk_code<B>(w, k) | (chunk_code<B>(w, k + 1) << 16) | 0x64006400u;
+        const half2_t d = (__builtin_bit_cast(half2_t, q2) - zz[p]) * sh[p];
+        packed[p] = __builtin_bit_cast(uint32_t, d);
+      }
+      *reinterpret_cast<uint4*>(Ws + wc * XP + 16 * wh) =
+          make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      *reinterpret_cast<uint4*>(Ws + wc * XP + 16 * wh + 8) =
+          make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < DQ_CHUNK; kk += 16) {
+      const int ko = kk + 8 * (lane >> 5);
+      half8_t af[2], bf[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        af[a] = *reinterpret_cast<const half8_t*>(Xs + (wm * 64 + a * 32 + (lane & 31)) * XP + ko);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        bf[b] = *reinterpret_cast<const half8_t*>(Ws + (wn * 64 + b * 32 + (lane & 31)) * XP + ko);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // 32 x 32 block layout: element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4,
+  // column l % 32
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t r = m0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int64_t cc = n0 + wn * 64 + b * 32 + (lane & 31);
+        if (r < M && cc < out) {
+          if (y_f16)
+            static_cast<_Float16*>(Y)[r * ldy + cc] = (_Float16)acc[a][b][v];
+          else
+            static_cast<float*>(Y)[r * ldy + cc] = acc[a][b][v];
+        }
+      }
+}
+
+// ------------------------------------------------------------------- plan --
+struct SmallPlan {
+  int mb;        // token rows per lane
+  int64_t cps;   // chunks per split
+  int nsplit;
+  size_t lds;    // bytes
+};
+SmallPlan small_plan(int64_t M, int64_t in, int64_t out) {
+  SmallPlan p;
+  p.mb = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+  const int64_t nch = in / DQ_CHUNK;
+  const int64_t ncolwg = (out + SMALL_COLS - 1) / SMALL_COLS;
+  // at least 512 workgroups, each split at least 4 chunks (one per wave), X
+  // slice and the final reduction within SMALL_LDS_MAX
+  int64_t ns = (512 + ncolwg - 1) / ncolwg;
+  if (ns > nch / 4) ns = nch / 4;
+  if (ns < 1) ns = 1;
+  int64_t cps = (nch + ns - 1) / ns;
+  const int64_t cps_max = SMALL_LDS_MAX / ((int64_t)p.mb * DQ_CHUNK * 4);
+  if (cps > cps_max) cps = cps_max;
+  p.cps = cps;
+  p.nsplit = (int)((nch + cps - 1) / cps);
+  const size_t xsb = (size_t)p.mb * cps * DQ_CHUNK * 4, redb = (size_t)4 * p.mb * 64 * 4;
+  p.lds = xsb > redb ? xsb : redb;
+  return p;
+}
+
+template <int B, int MB>
+hipError_t launch_small_t(const SmallPlan& p, const _Float16* X, int64_t M, int64_t in,
+                          int64_t ldx, const uint32_t* qw, const float* scales,
+                          const int32_t* zeros, const int32_t* g_idx, int64_t out, float* part,
+                          void* Y, int y_f16, int64_t ldy, hipStream_t s) {
+  auto k = dq_small_kernel<B, MB>;
+  GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)p.lds));
+  dim3 grid((unsigned)((out + SMALL_COLS - 1) / SMALL_COLS), (unsigned)p.nsplit);
+  hipLaunchKernelGGL(k, grid, dim3(256), p.lds, s, X, M, in, ldx, qw, scales, zeros, g_idx, out,
+                     p.cps, part, Y, y_f16, ldy);
+  return hipGetLastError();
+}
+template <int B>
+hipError_t launch_small_b(const SmallPlan& p, const _Float16* X, int64_t M, int64_t in,
+                          int64_t ldx, const uint32_t* qw, const float* scales,
+                          const int32_t* zeros, const int32_t* g_idx, int64_t out, float* part,
+                          void* Y, int y_f16, int64_t ldy, hipStream_t s) {
+  switch (p.mb) {
+    case 1: return launch_small_t<B, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s);
+    case 2: return launch_small_t<B, 2>(p, X, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s);
+    case 4: return launch_small_t<B, 4>(p, X, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s);
+    case 8: return launch_small_t<B, 8>(p, X, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s);
+    default: return launch_small_t<B, 16>(p, X, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s);
+  }
+}
+
+}  // namespace
+
+size_t dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out) {
+  if (M > DQ_SMALL_M_MAX) return 0;
+  const SmallPlan p = small_plan(M, in, out);
+  return p.nsplit > 1 ? align_up((size_t)p.nsplit * M * out * sizeof(float)) : 0;
+}
+
+hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
+                              const int32_t* qweight, const float* scales, const int32_t* zeros,
+                              const int32_t* g_idx, int64_t out, int bits, void* Y, int y_f16,
+                              int64_t ldy, void* ws, hipStream_t s) {
+  const _Float16* x = static_cast<const _Float16*>(X);
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(qweight);
+  if (M <= DQ_SMALL_M_MAX) {
+    const SmallPlan p = small_plan(M, in, out);
+    float* part = static_cast<float*>(ws);
+    hipError_t e;
+    switch (bits) {
+      case 2: e = launch_small_b<2>(p, x, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s); break;
+      case 3: e = launch_small_b<3>(p, x, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s); break;
+      case 8: e = launch_small_b<8>(p, x, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s); break;
+      default: e = launch_small_b<4>(p, x, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s); break;
+    }
+    GPTQ_HIP_TRY(e);
+    if (p.nsplit > 1) {
+      const int64_t total = M * out;
+      hipLaunchKernelGGL(dq_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                         part, p.nsplit, M, out, Y, y_f16, ldy);
+      GPTQ_HIP_TRY(hipGetLastError());
+    }
+    return hipSuccess;
+  }
+  dim3 grid((unsigned)((out + TB - 1) / TB), (unsigned)((M + TB - 1) / TB));
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(dq_mfma_kernel<2>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
+    case 3: hipLaunchKernelGGL(dq_mfma_kernel<3>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
+    case 8: hipLaunchKernelGGL(dq_mfma_kernel<8>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
+    default: hipLaunchKernelGGL(dq_mfma_kernel<4>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gptq

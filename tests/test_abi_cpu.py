@@ -20,7 +20,8 @@ def test_exports_every_header_function(lib):
     assert set(names) == {"gptq_hessian_workspace_bytes", "gptq_hessian_accumulate",
                           "gptq_prepare_workspace_bytes",
                           "gptq_prepare", "gptq_quantize_workspace_bytes",
-                          "gptq_quantize_layer", "gptq_status_string",
+                          "gptq_quantize_layer", "gptq_dequant_matmul_workspace_bytes",
+                          "gptq_dequant_matmul", "gptq_status_string",
                           "gptq_last_error_message"}
     for n in names:
         assert hasattr(lib, n), n
@@ -107,3 +108,43 @@ def test_binding_refuses_cpu_tensors():
         P.hessian_accumulate(torch.zeros(4, 4), torch.zeros(2, 4, dtype=torch.float16))
     with pytest.raises(ValueError):
         P.prepare(torch.eye(4), 0.01, False)
+
+
+def test_dequant_matmul_argument_errors(lib):
+    f = lib.gptq_dequant_matmul
+    A16 = ctypes.c_void_p(4096)   # 16-byte aligned, never dereferenced
+    ok = dict(X=A16, xd=L.GPTQ_F16, M=2, inp=64, ldx=64, q=FAKE, s=FAKE, z=FAKE, g=FAKE, G=2,
+              out=8, bits=4, Y=FAKE, yd=L.GPTQ_F32, ldy=8)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        ws = lib.gptq_dequant_matmul_workspace_bytes(a["M"], a["inp"], a["out"])
+        return f(a["X"], a["xd"], a["M"], a["inp"], a["ldx"], a["q"], a["s"], a["z"], a["g"],
+                 a["G"], a["out"], a["bits"], a["Y"], a["yd"], a["ldy"],
+                 kw.get("ws", FAKE if ws else None), kw.get("wsb", ws), None)
+
+    assert call(X=None) == L.GPTQ_ERR_INVALID_ARG
+    assert call(q=None) == L.GPTQ_ERR_INVALID_ARG
+    assert call(Y=None) == L.GPTQ_ERR_INVALID_ARG
+    assert call(M=-1) == L.GPTQ_ERR_INVALID_ARG
+    assert call(inp=48, ldx=48) == L.GPTQ_ERR_INVALID_ARG
+    assert b"multiple of 32" in lib.gptq_last_error_message()
+    assert call(out=0) == L.GPTQ_ERR_INVALID_ARG
+    assert call(G=0) == L.GPTQ_ERR_INVALID_ARG
+    assert call(ldx=32) == L.GPTQ_ERR_INVALID_ARG
+    assert call(ldy=4) == L.GPTQ_ERR_INVALID_ARG
+    assert call(xd=L.GPTQ_BF16) == L.GPTQ_ERR_UNSUPPORTED
+    assert call(yd=L.GPTQ_BF16) == L.GPTQ_ERR_INVALID_ARG
+    assert call(bits=5) == L.GPTQ_ERR_UNSUPPORTED
+    assert call(ldx=68) == L.GPTQ_ERR_UNSUPPORTED
+    assert call(X=ctypes.c_void_p(4098)) == L.GPTQ_ERR_UNSUPPORTED
+    # the small-M path splits the input range: a workspace is required
+    need = lib.gptq_dequant_matmul_workspace_bytes(1, 4096, 4096)
+    assert need > 0 and lib.gptq_dequant_matmul_workspace_bytes(64, 4096, 4096) == 0
+    assert lib.gptq_dequant_matmul_workspace_bytes(0, 4096, 4096) == 0
+    assert call(M=1, inp=4096, ldx=4096, out=4096, ldy=4096, ws=None, wsb=0) == \
+        L.GPTQ_ERR_INVALID_ARG
+    assert call(M=1, inp=4096, ldx=4096, out=4096, ldy=4096, ws=FAKE, wsb=need - 1) == \
+        L.GPTQ_ERR_WORKSPACE
+    # M == 0 is a no-op that never touches the device
+    assert call(M=0) == L.GPTQ_OK
