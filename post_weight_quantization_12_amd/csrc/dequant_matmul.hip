@@ -36,6 +36,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 constexpr int DQ_CHUNK = 32;   // k per chunk
 constexpr int SMALL_COLS = 64; // output columns per small-M workgroup
 constexpr int SMALL_LDS_MAX = 64 * 1024;
+constexpr int SMALL_DEPTH = 4;  // chunks whose words a lane loads ahead
 
 // Code k (0..31, a constant after unrolling) of a chunk whose B words are
 // w[0..B-1] (w[B] == 0).
@@ -69,59 +70,99 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
   const int64_t c0 = (int64_t)blockIdx.y * cps;
   const int64_t c1 = c0 + cps < nch ? c0 + cps : nch;
   const int len = (int)((c1 - c0) * DQ_CHUNK);
-  for (int e = tid; e < MB * len; e += 256) {
-    const int m = e / len, k = e % len;
-    xs[k * MB + m] = m < M ? (float)X[m * ldx + c0 * DQ_CHUNK + k] : 0.0f;
+  // X slice, 8 halves per 16-byte load (rows are 16-byte aligned)
+  for (int e = tid; e < MB * (len / 8); e += 256) {
+    const int m = e / (len / 8), k8 = 8 * (e % (len / 8));
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (m < M) v = *reinterpret_cast<const uint4*>(X + m * ldx + c0 * DQ_CHUNK + k8);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half2_t h = __builtin_bit_cast(half2_t, u[j]);
+      xs[(k8 + 2 * j) * MB + m] = (float)h.x;
+      xs[(k8 + 2 * j + 1) * MB + m] = (float)h.y;
+    }
   }
   __syncthreads();
 
   float acc[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) acc[m] = 0.0f;
-  for (int64_t c = c0 + wave; c < c1; c += 4) {
-    uint32_t w[B + 1];
+  // Chunks c0 + wave, + 4, + 8, ... in blocks of SMALL_DEPTH; the words of
+  // the next block are loaded before the current one is used, so a lane
+  // keeps 2 * SMALL_DEPTH * B loads in flight and the memory latency
+  // overlaps the dequantization.
+  auto load_block = [&](int64_t cb, uint32_t (*w)[B + 1]) {
 #pragma unroll
-    for (int i = 0; i < B; ++i) w[i] = qw[(c * B + i) * out + colc];
-    w[B] = 0u;
-    const int64_t kb = c * DQ_CHUNK;
-    const int xo = (int)(kb - c0 * DQ_CHUNK);
-    // the chunk's groups (uniform); one group for all 32 k is the common case
-    int gk[DQ_CHUNK];
-    bool one = true;
+    for (int d = 0; d < SMALL_DEPTH; ++d) {
+      const int64_t c = cb + 4 * d < c1 ? cb + 4 * d : c0;  // past the end: a valid dummy
 #pragma unroll
-    for (int k = 0; k < DQ_CHUNK; ++k) {
-      gk[k] = g_idx[kb + k];
-      one = one && gk[k] == gk[0];
+      for (int i = 0; i < B; ++i) w[d][i] = qw[(c * B + i) * out + colc];
+      w[d][B] = 0u;
     }
-    float sk[DQ_CHUNK], zk[DQ_CHUNK];
-    if (one) {
-      const float s = scales[gk[0] * out + colc], z = (float)zeros[gk[0] * out + colc];
+  };
+  uint32_t wcur[SMALL_DEPTH][B + 1], wnxt[SMALL_DEPTH][B + 1];
+  load_block(c0 + wave, wcur);
+  for (int64_t cb = c0 + wave; cb < c1; cb += 4 * SMALL_DEPTH) {
+    load_block(cb + 4 * SMALL_DEPTH, wnxt);
 #pragma unroll
-      for (int k = 0; k < DQ_CHUNK; ++k) { sk[k] = s; zk[k] = z; }
-    } else {
+    for (int d = 0; d < SMALL_DEPTH; ++d) {
+      const int64_t c = cb + 4 * d;
+      if (c >= c1) break;  // uniform
+      const int64_t kb = c * DQ_CHUNK;
+      const int xo = (int)(kb - c0 * DQ_CHUNK);
+      // the chunk's groups (uniform); one group for all 32 k is the common case
+      int gk[DQ_CHUNK];
+      bool one = true;
 #pragma unroll
       for (int k = 0; k < DQ_CHUNK; ++k) {
-        sk[k] = scales[gk[k] * out + colc];
-        zk[k] = (float)zeros[gk[k] * out + colc];
+        gk[k] = g_idx[kb + k];
+        one = one && gk[k] == gk[0];
+      }
+      if (one) {
+        // w = s q - s z: one FMA per weight after the code's conversion
+        const float sc = scales[gk[0] * out + colc];
+        const float nsz = -sc * (float)zeros[gk[0] * out + colc];
+#pragma unroll
+        for (int k4 = 0; k4 < DQ_CHUNK; k4 += 4) {
+          float xv[4 * MB];
+#pragma unroll
+          for (int q = 0; q < MB; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(xs + (xo + k4) * MB + 4 * q);
+            xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+          }
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const float wv = fmaf((float)chunk_code<B>(wcur[d], k4 + kk), sc, nsz);
+#pragma unroll
+            for (int m = 0; m < MB; ++m) acc[m] = fmaf(xv[kk * MB + m], wv, acc[m]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k4 = 0; k4 < DQ_CHUNK; k4 += 4) {
+          float xv[4 * MB];
+#pragma unroll
+          for (int q = 0; q < MB; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(xs + (xo + k4) * MB + 4 * q);
+            xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+          }
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int k = k4 + kk;
+            const float sc = scales[gk[k] * out + colc];
+            const float nsz = -sc * (float)zeros[gk[k] * out + colc];
+            const float wv = fmaf((float)chunk_code<B>(wcur[d], k), sc, nsz);
+#pragma unroll
+            for (int m = 0; m < MB; ++m) acc[m] = fmaf(xv[kk * MB + m], wv, acc[m]);
+          }
+        }
       }
     }
 #pragma unroll
-    for (int k4 = 0; k4 < DQ_CHUNK; k4 += 4) {
-      // x[k4 .. k4 + 3][0 .. MB): 4 MB contiguous floats
-      float xv[4 * MB];
+    for (int d = 0; d < SMALL_DEPTH; ++d)
 #pragma unroll
-      for (int q = 0; q < MB; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(xs + (xo + k4) * MB + 4 * q);
-        xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int k = k4 + kk;
-        const float wv = sk[k] * ((float)chunk_code<B>(w, k) - zk[k]);
-#pragma unroll
-        for (int m = 0; m < MB; ++m) acc[m] = fmaf(xv[kk * MB + m], wv, acc[m]);
-      }
-    }
+      for (int i = 0; i <= B; ++i) wcur[d][i] = wnxt[d][i];
   }
   // the four waves' sums, in wave order
   __syncthreads();
@@ -297,10 +338,10 @@ SmallPlan small_plan(int64_t M, int64_t in, int64_t out) {
   p.mb = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
   const int64_t nch = in / DQ_CHUNK;
   const int64_t ncolwg = (out + SMALL_COLS - 1) / SMALL_COLS;
-  // at least 512 workgroups, each split at least 4 chunks (one per wave), X
-  // slice and the final reduction within SMALL_LDS_MAX
+  // about 512 workgroups, each wave at least 2 * SMALL_DEPTH chunks, X slice
+  // and the final reduction within SMALL_LDS_MAX
   int64_t ns = (512 + ncolwg - 1) / ncolwg;
-  if (ns > nch / 4) ns = nch / 4;
+  if (ns > nch / (8 * SMALL_DEPTH)) ns = nch / (8 * SMALL_DEPTH);
   if (ns < 1) ns = 1;
   int64_t cps = (nch + ns - 1) / ns;
   const int64_t cps_max = SMALL_LDS_MAX / ((int64_t)p.mb * DQ_CHUNK * 4);
