@@ -15,6 +15,9 @@ down_proj layer, c4a / c4b the 8192 x 28672 70B down_proj layer.
 
 Prints ONE JSON line (rank 0; this build is single-GPU).
 
+--dequant-tokens M times gptq_dequant_matmul instead (X of M fp16 tokens times
+the config's packed layer, random codes) and prints one JSON line for it.
+
 --summarize DIR (no GPU): turns the rocprofv3 output of the profiling
 commands (DIR/trace, DIR/FETCH_SIZE, DIR/WRITE_SIZE, see PROFILE_COMMANDS)
 into profiles/layer_<config>_kernel_stats.md and
@@ -238,6 +241,171 @@ def cpu_baseline(cfg, steps_tokens: int):
     }
 
 
+def dequant_cpu_baseline(cfg, M, words, scales, zeros, g_idx, x):
+    """The oracle's dequant_matmul, untuned, on a column sample of the layer
+    (the first `cols` output columns, all M tokens), scaled to all columns."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    torch.set_num_threads(max(1, len(os.sched_getaffinity(0))))
+    cols = min(cfg.out, max(64, (1 << 24) // cfg.inp))
+    wn = words[:, :cols].cpu().numpy()
+    sn = scales[:, :cols].cpu().numpy()
+    zn = zeros[:, :cols].cpu().numpy()
+    gn = g_idx.cpu().numpy()
+    xn = x.cpu().numpy()
+    t0 = time.perf_counter()
+    O.dequant_matmul(xn, wn, sn, zn, gn, cfg.bits)
+    t = (time.perf_counter() - t0) * cfg.out / cols
+    return {
+        "value": 2.0 * M * cfg.inp * cfg.out / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"{cols} of {cfg.out} output columns, all {M} tokens "
+                   f"({t * cols / cfg.out:.2f} s, scaled x{cfg.out / cols:.0f}); fp64 NumPy"),
+    }
+
+
+def dequant_main(args):
+    """--dequant-tokens M: gptq_dequant_matmul Y = X W^T (X fp16 [M x in], the
+    packed layer of the config's shape and bit width, Y fp16) timed on its own.
+    Roofline: HBM for M <= 16 (algorithmic bytes = packed words + scales +
+    zeros + g_idx + X + Y), fp16 MFMA above (2 M in out flop)."""
+    import torch
+
+    import post_weight_quantization_12_amd as P
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workloads.get(args.config)
+    M, n, out = args.dequant_tokens, cfg.inp, cfg.out
+    gs = n if cfg.group_size == -1 else cfg.group_size
+    words, scales, zeros, order = workloads.packed_layer_draws(cfg, dev, 0)
+    g_idx = torch.empty((n,), dtype=torch.int32, device=dev)
+    g_idx[order] = (torch.arange(n, device=dev) // gs).to(torch.int32)  # group of a column
+    gx = workloads.generator(dev, 0, cfg.cfg_id, 6, M)
+    X = torch.randn((M, n), generator=gx, device=dev).to(torch.float16)
+    Y = torch.empty((M, out), dtype=torch.float16, device=dev)
+    wsb = P.dequant_matmul_workspace_bytes(M, n, out)
+    ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] dequant_matmul {cfg.name}: X {M}x{n} fp16, packed W {out}x{n} "
+        f"{cfg.bits}-bit g{cfg.group_size} desc_act={cfg.desc_act}, Y fp16")
+
+    x_order = None
+    order_ms = None
+    if cfg.desc_act and not args.dequant_as_packed:
+        # act-order layer: re-ordered by group once, as at load time
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        words, g_idx, x_order = P.dequant_group_order(words, g_idx, cfg.bits, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        order_ms = a.elapsed_time(b)
+        wsb = P.dequant_matmul_workspace_bytes(M, n, out, True)
+        ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
+
+    def call():
+        P.dequant_matmul(X, words, scales, zeros, g_idx, cfg.bits, x_order=x_order, Y=Y,
+                         workspace=ws if wsb else None, stream=stream)
+
+    reps = 50
+    for _ in range(args.warmup * reps):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            call()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = sum(a.elapsed_time(b) for a, b in evs) / (args.steps * reps)
+
+    # the same product with dense fp16 weights (hipBLASLt through torch), for context
+    Wd = torch.randn((out, n), device=dev).to(torch.float16)
+    for _ in range(reps):
+        torch.matmul(X, Wd.t())
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        torch.matmul(X, Wd.t())
+    b.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = a.elapsed_time(b) / reps
+    del Wd
+
+    flops = 2.0 * M * n * out
+    G = scales.shape[0]
+    alg_bytes = float(n * cfg.bits // 8 * out + 8 * G * out + 4 * n + 2 * M * n + 2 * M * out
+                      + (4 * n if x_order is not None else 0))
+    small = M <= 16
+    if small:
+        achieved, peak, unit, bound = alg_bytes / (call_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+        kernel = ("dq_small_kernel" + (" + dq_reduce_kernel" if wsb else ""))
+    else:
+        achieved, peak, unit, bound = flops / (call_ms * 1e-3) / 1e12, PEAK_FP16_TFLOPS, "TFLOP/s", "mfma"
+        kernel = ("dq_gather_x_kernel + " if x_order is not None else "") + "dq_mfma_kernel"
+    result = {
+        "metric": "dequantize-on-the-fly matmul Y = X W^T from the packed layer, TFLOP/s",
+        "value": flops / (call_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "calls_per_step": reps,
+        "us_per_call": call_ms * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 X, fp32 dequant + accumulate" if small else "f16 X and dequantized W, f32 accumulate",
+        "data": "synthetic (seeded random codes, scales, zeros and column order)",
+        "config": {
+            "workload": (f"{cfg.name} packed layer: W {out}x{n} {cfg.bits}-bit g{cfg.group_size} "
+                         f"desc_act={cfg.desc_act}, X {M} tokens fp16, Y fp16"),
+            "tokens": M, "out": out, "in": n, "bits": cfg.bits, "group_size": cfg.group_size,
+            "desc_act": cfg.desc_act,
+            "layer": ("group-ordered (gptq_dequant_group_order, once)" if x_order is not None
+                      else "as packed"),
+        },
+        "group_order_ms_once": order_ms,
+        "dense_fp16_us_per_call": dense_ms * 1e3,
+        "speedup_vs_dense_fp16": dense_ms / call_ms,
+        "roofline": {
+            "kernel": f"{kernel} = one gptq_dequant_matmul call",
+            "kernel_launches_per_call": 2 if (wsb and (small or x_order is not None)) else 1,
+            "bound": bound,
+            "achieved": achieved,
+            "peak": peak,
+            "unit": unit,
+            "frac": achieved / peak,
+            "call_ms": call_ms,
+            "bytes_per_call": alg_bytes,
+            "flops_per_call": flops,
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = dequant_cpu_baseline(cfg, M, words, scales, zeros, g_idx, X)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +418,12 @@ def main():
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="write the profiles/ summaries from rocprofv3 output in DIR and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dequant-tokens", type=int, default=None, metavar="M",
+                    help="time gptq_dequant_matmul with M tokens on the config's packed layer "
+                         "instead of the quantization step")
+    ap.add_argument("--dequant-as-packed", action="store_true",
+                    help="with --dequant-tokens on an act-order config: use the layer as packed "
+                         "instead of its group order")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference kernel "
                          "of known traffic for calibrating rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -262,6 +436,10 @@ def main():
         print("bench.py: this GPTQ build runs on one GPU only (no sharding, no collectives); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.dequant_tokens is not None:
+        dequant_main(args)
+        return
 
     import torch
 

@@ -193,9 +193,11 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in,
                         void* stream);
 
 /* Workspace (bytes) gptq_dequant_matmul needs for M token rows, in inputs and
- * out outputs: the partial sums of the split input range when M <= 16 (e.g.
- * 8 x 1 x 4096 fp32 for one token of a 4096 x 4096 layer); 0 otherwise. */
-size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out);
+ * out outputs, with (has_order != 0) or without an x_order: the partial sums
+ * of the split input range when M <= 16 (e.g. 8 x 1 x 4096 fp32 for one token
+ * of a 4096 x 4096 layer); for M > 16 the gathered copy of X (M x in fp16)
+ * when has_order, else 0. */
+size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order);
 
 /*
  * Dequantize-on-the-fly matmul: Y = X W^T for a layer quantized by
@@ -203,34 +205,72 @@ size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out);
  *
  * Glossary entry "gptq", paragraph "Inference": the quantized weights are
  * dequantized during the computation and multiplied.  Here
- *     W[r][k] = scales[g_idx[k]][r] * (code[r][k] - zeros[g_idx[k]][r]),
- * code[r][k] the k-th b-bit field of row r's little-endian bit stream
- * (qweight[j][r] is word j of it), and Y[t][r] = sum_k X[t][k] W[r][k].
+ *     W[r][p] = scales[g_idx[p]][r] * (code[r][p] - zeros[g_idx[p]][r]),
+ * code[r][p] the p-th b-bit field of row r's little-endian bit stream
+ * (qweight[j][r] is word j of it), and
+ *     Y[t][r] = sum_p X[t][x_order[p]] W[r][p]
+ * (x_order NULL: x_order[p] = p, the layer as gptq_quantize_layer writes it;
+ * with the outputs of gptq_dequant_group_order, the same product).
  *
  *   X        fp16 [M x in], row-major, leading dimension ldx >= in, ldx a
  *            multiple of 8, X 16-byte aligned.  M == 0 is a no-op.
  *   qweight  int32 [in * bits / 32 x out]; scales fp32 and zeros int32
  *            [n_groups x out]; g_idx int32 [in] with values in
  *            [0, n_groups) (not checked: device data).
+ *   x_order  int32 [in], a permutation of 0..in-1 (not checked), or NULL.
  *   in       a positive multiple of 32; out >= 1; bits 2, 3, 4 or 8.
  *   Y        out: [M x out], row-major, ldy >= out, y_dtype GPTQ_F32 or
  *            GPTQ_F16 (the fp32 sum rounded to nearest).
  *   workspace  device memory of gptq_dequant_matmul_workspace_bytes(M, in,
- *            out) bytes, or NULL when that is 0.
+ *            out, x_order != NULL) bytes, or NULL when that is 0.
  *
  * Arithmetic: M <= 16 dequantizes each weight in fp32 and accumulates fp32
  * FMAs (HBM-bound on qweight); larger M rounds each dequantized weight to
  * fp16 (scale rounded to fp16, then one rounding of the product) and
  * multiplies on the fp16 matrix cores with fp32 accumulation.  Results do
  * not depend on timing.  Calls that share a workspace must not overlap.
+ * A chunk of 32 positions whose g_idx entries are all equal is dequantized
+ * with one scale and zero; chunks that mix groups (act-order layers as
+ * packed) read them per position and run several times slower:
+ * gptq_dequant_group_order turns such a layer into one without them.
  * Errors: INVALID_ARG, UNSUPPORTED (x_dtype not F16, bits, alignment),
  *         WORKSPACE, HIP.
  */
 int gptq_dequant_matmul(const void* X, int x_dtype, int64_t M, int64_t in, int64_t ldx,
                         const int32_t* qweight, const float* scales, const int32_t* zeros,
-                        const int32_t* g_idx, int64_t n_groups, int64_t out, int bits, void* Y,
-                        int y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
-                        void* stream);
+                        const int32_t* g_idx, const int32_t* x_order, int64_t n_groups,
+                        int64_t out, int bits, void* Y, int y_dtype, int64_t ldy,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace (bytes) of gptq_dequant_group_order for in input positions. */
+size_t gptq_dequant_group_order_workspace_bytes(int64_t in);
+
+/*
+ * Group order of a packed layer, for gptq_dequant_matmul.
+ *
+ * With desc_act ("desc_act", Key Parameters of "GPTQ > Using AutoGPTQ in
+ * Practice") the groups follow the permuted column order, so g_idx of the
+ * packed layer (original order) jumps between groups from one position to
+ * the next.  This call sorts the input positions by group, ties by position
+ * (stable): x_order[p] = the position of rank p, g_idx_sorted[p] =
+ * g_idx[x_order[p]] (non-decreasing) and qweight_sorted the codes re-packed
+ * in that order (code_sorted[r][p] = code[r][x_order[p]]).  Scales and zeros
+ * are unchanged.  gptq_dequant_matmul(..., qweight_sorted, scales, zeros,
+ * g_idx_sorted, x_order, ...) then computes the same Y as with the layer as
+ * packed, the input column of each term being the same.  Meant to run once
+ * per layer when it is loaded.
+ *
+ *   qweight, g_idx   the packed layer as above (device); in a positive
+ *                    multiple of 32; out >= 1; bits 2, 3, 4 or 8.
+ *   qweight_sorted   out: int32 [in * bits / 32 x out] (not aliasing qweight).
+ *   g_idx_sorted, x_order  out: int32 [in].
+ *   workspace        gptq_dequant_group_order_workspace_bytes(in) bytes.
+ * Errors: INVALID_ARG, UNSUPPORTED (bits), WORKSPACE, HIP.
+ */
+int gptq_dequant_group_order(const int32_t* qweight, const int32_t* g_idx, int64_t in,
+                             int64_t out, int bits, int32_t* qweight_sorted,
+                             int32_t* g_idx_sorted, int32_t* x_order, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Static text for a gptq_status_t value. */
 const char* gptq_status_string(int status);

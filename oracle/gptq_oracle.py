@@ -53,6 +53,7 @@ __all__ = [
     "unpack",
     "dequantize",
     "dequant_matmul",
+    "group_order",
     "layer_error",
 ]
 
@@ -403,7 +404,7 @@ def dequantize(codes, scales, zeros, g_idx) -> np.ndarray:
     return s * (codes - z)
 
 
-def dequant_matmul(x, qweight, scales, zeros, g_idx, bits: int) -> np.ndarray:
+def dequant_matmul(x, qweight, scales, zeros, g_idx, bits: int, x_order=None) -> np.ndarray:
     """Y = X W^T with W the layer's dequantized weights, in float64.
 
     [GLOSS] paragraph "Inference": the quantized layer is applied by
@@ -411,12 +412,34 @@ def dequant_matmul(x, qweight, scales, zeros, g_idx, bits: int) -> np.ndarray:
     definition written out: Y[t, r] = sum_k X[t, k] * s[g_idx[k], r] *
     (code[r, k] - z[g_idx[k], r]), with code[r, k] the k-th b-bit field of
     row r's little-endian bit stream in qweight (the packed layer as
-    gptq_quantize_layer writes it; see ``unpack``).
+    gptq_quantize_layer writes it; see ``unpack``).  With x_order (a layer
+    from ``group_order``), packed position k multiplies X column
+    x_order[k] instead of column k.
     """
     x = np.asarray(x, dtype=np.float64)
+    if x_order is not None:
+        x = x[:, np.asarray(x_order, dtype=np.int64)]
     n = x.shape[1]
     codes = unpack(qweight, bits, n)
     return x @ dequantize(codes, scales, zeros, g_idx).T
+
+
+def group_order(qweight, g_idx, bits: int):
+    """(qweight_sorted, g_idx_sorted, x_order) of a packed layer.
+
+    With desc_act ([HANDB] Key Parameters) the groups are formed in the
+    permuted column order, so the packed layer's g_idx (original order)
+    changes group from one input to the next.  Sorting the inputs by group,
+    ties kept in input order (a stable sort), gives x_order; the codes are
+    re-packed in that order and g_idx_sorted = g_idx[x_order].  The product
+    with X[:, x_order] is the same sum over the same terms.
+    """
+    g = np.asarray(g_idx, dtype=np.int64)
+    n = g.shape[0]
+    x_order = np.argsort(g, kind="stable")
+    codes = unpack(qweight, bits, n)
+    return (pack(codes[:, x_order], bits), g[x_order].astype(np.int32),
+            x_order.astype(np.int32))
 
 
 def layer_error(W, What, H) -> float:

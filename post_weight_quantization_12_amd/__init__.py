@@ -8,6 +8,8 @@ from ._lib import (  # noqa: F401
     GPTQ_BF16,
     GPTQ_F16,
     GPTQ_F32,
+    dequant_group_order,
+    dequant_group_order_workspace_bytes,
     dequant_matmul,
     dequant_matmul_workspace_bytes,
     hessian_accumulate,

@@ -61,11 +61,16 @@ def load():
     lib.gptq_quantize_layer.argtypes = [vp, c_int, i64, i64, vp, vp, c_int, c_int, c_int, c_int,
                                         vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.gptq_quantize_layer.restype = c_int
-    lib.gptq_dequant_matmul_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.gptq_dequant_matmul_workspace_bytes.argtypes = [i64, i64, i64, c_int]
     lib.gptq_dequant_matmul_workspace_bytes.restype = ctypes.c_size_t
-    lib.gptq_dequant_matmul.argtypes = [vp, c_int, i64, i64, i64, vp, vp, vp, vp, i64, i64, c_int,
-                                        vp, c_int, i64, vp, ctypes.c_size_t, vp]
+    lib.gptq_dequant_matmul.argtypes = [vp, c_int, i64, i64, i64, vp, vp, vp, vp, vp, i64, i64,
+                                        c_int, vp, c_int, i64, vp, ctypes.c_size_t, vp]
     lib.gptq_dequant_matmul.restype = c_int
+    lib.gptq_dequant_group_order_workspace_bytes.argtypes = [i64]
+    lib.gptq_dequant_group_order_workspace_bytes.restype = ctypes.c_size_t
+    lib.gptq_dequant_group_order.argtypes = [vp, vp, i64, i64, c_int, vp, vp, vp, vp,
+                                             ctypes.c_size_t, vp]
+    lib.gptq_dequant_group_order.restype = c_int
     lib.gptq_status_string.argtypes = [c_int]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_last_error_message.argtypes = []
@@ -215,16 +220,18 @@ def quantize_layer(W, Hinv_chol, perm, bits: int, group_size: int, sym: bool, bl
     return qweight, scales, zeros, g_idx
 
 
-def dequant_matmul_workspace_bytes(M: int, inp: int, out: int) -> int:
-    return int(load().gptq_dequant_matmul_workspace_bytes(M, inp, out))
+def dequant_matmul_workspace_bytes(M: int, inp: int, out: int, has_order: bool = False) -> int:
+    return int(load().gptq_dequant_matmul_workspace_bytes(M, inp, out, int(bool(has_order))))
 
 
-def dequant_matmul(X, qweight, scales, zeros, g_idx, bits: int, out_dtype=None, Y=None,
-                   workspace=None, stream=None):
+def dequant_matmul(X, qweight, scales, zeros, g_idx, bits: int, x_order=None, out_dtype=None,
+                   Y=None, workspace=None, stream=None):
     """Y = X W^T with W dequantized on the fly from the packed layer
     (qweight int32 [in*bits/32 x out], scales fp32 / zeros int32
-    [n_groups x out], g_idx int32 [in]) for fp16 X [M x in].  Y is fp32
-    (default) or fp16 [M x out]."""
+    [n_groups x out], g_idx int32 [in]) for fp16 X [M x in].  x_order
+    (int32 [in], optional): packed position p multiplies X column
+    x_order[p] (the layer from dequant_group_order).  Y is fp32 (default) or
+    fp16 [M x out]."""
     torch = _torch()
     lib = load()
     for name, t in (("X", X), ("qweight", qweight), ("scales", scales), ("zeros", zeros),
@@ -245,6 +252,10 @@ def dequant_matmul(X, qweight, scales, zeros, g_idx, bits: int, out_dtype=None, 
         raise ValueError("zeros must be a contiguous int32 [n_groups x out] tensor")
     if g_idx.dtype != torch.int32 or tuple(g_idx.shape) != (inp,):
         raise ValueError("g_idx must be an int32 [in] tensor")
+    if x_order is not None:
+        _need_cuda("x_order", x_order)
+        if x_order.dtype != torch.int32 or tuple(x_order.shape) != (inp,):
+            raise ValueError("x_order must be an int32 [in] tensor")
     if out_dtype is None:
         out_dtype = torch.float32 if Y is None else Y.dtype
     if Y is None:
@@ -252,12 +263,45 @@ def dequant_matmul(X, qweight, scales, zeros, g_idx, bits: int, out_dtype=None, 
     if Y.dim() != 2 or tuple(Y.shape) != (M, out) or Y.stride(1) != 1:
         raise ValueError("Y must be [M x out] with unit column stride")
     if workspace is None:
-        need = dequant_matmul_workspace_bytes(M, inp, out)
+        need = dequant_matmul_workspace_bytes(M, inp, out, x_order is not None)
         workspace = torch.empty((need,), dtype=torch.uint8, device=X.device) if need else None
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
     _check(lib.gptq_dequant_matmul(_ptr(X), _dtype_code(X.dtype), M, inp,
                                    X.stride(0) if M > 1 else inp, _ptr(qweight), _ptr(scales),
-                                   _ptr(zeros), _ptr(g_idx), G, out, bits, _ptr(Y),
-                                   _dtype_code(Y.dtype), Y.stride(0) if M > 1 else out, ws_ptr,
-                                   ws_bytes, _stream(stream)))
+                                   _ptr(zeros), _ptr(g_idx),
+                                   None if x_order is None else _ptr(x_order), G, out, bits,
+                                   _ptr(Y), _dtype_code(Y.dtype), Y.stride(0) if M > 1 else out,
+                                   ws_ptr, ws_bytes, _stream(stream)))
     return Y
+
+
+def dequant_group_order_workspace_bytes(inp: int) -> int:
+    return int(load().gptq_dequant_group_order_workspace_bytes(inp))
+
+
+def dequant_group_order(qweight, g_idx, bits: int, stream=None):
+    """(qweight_sorted, g_idx_sorted, x_order): the packed layer's input
+    positions sorted by group (stable) and its codes re-packed in that order,
+    for dequant_matmul(X, qweight_sorted, scales, zeros, g_idx_sorted, bits,
+    x_order=x_order)."""
+    torch = _torch()
+    lib = load()
+    _need_cuda("qweight", qweight)
+    _need_cuda("g_idx", g_idx)
+    if qweight.dtype != torch.int32 or qweight.dim() != 2 or not qweight.is_contiguous():
+        raise ValueError("qweight must be a contiguous int32 [in*bits/32 x out] tensor")
+    inp = g_idx.shape[0]
+    if g_idx.dtype != torch.int32 or g_idx.dim() != 1 or not g_idx.is_contiguous():
+        raise ValueError("g_idx must be a contiguous int32 [in] tensor")
+    if qweight.shape[0] * 32 != inp * bits:
+        raise ValueError("qweight rows must be in * bits / 32")
+    out = qweight.shape[1]
+    qs = torch.empty_like(qweight)
+    gs = torch.empty_like(g_idx)
+    order = torch.empty_like(g_idx)
+    ws = torch.empty((dequant_group_order_workspace_bytes(inp),), dtype=torch.uint8,
+                     device=qweight.device)
+    _check(lib.gptq_dequant_group_order(_ptr(qweight), _ptr(g_idx), inp, out, int(bits),
+                                        _ptr(qs), _ptr(gs), _ptr(order), _ptr(ws), ws.numel(),
+                                        _stream(stream)))
+    return qs, gs, order

@@ -162,16 +162,16 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in,
                     "gptq_quantize_layer");
 }
 
-size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out) {
+size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order) {
   if (M < 1 || in < 32 || in % 32 != 0 || out < 1) return 0;
-  return dequant_matmul_workspace_bytes(M, in, out);
+  return dequant_matmul_workspace_bytes(M, in, out, has_order ? 1 : 0);
 }
 
 int gptq_dequant_matmul(const void* X, int x_dtype, int64_t M, int64_t in, int64_t ldx,
                         const int32_t* qweight, const float* scales, const int32_t* zeros,
-                        const int32_t* g_idx, int64_t n_groups, int64_t out, int bits, void* Y,
-                        int y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        const int32_t* g_idx, const int32_t* x_order, int64_t n_groups,
+                        int64_t out, int bits, void* Y, int y_dtype, int64_t ldy,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
   if (!X) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL");
   if (!qweight || !scales || !zeros || !g_idx)
@@ -192,16 +192,48 @@ int gptq_dequant_matmul(const void* X, int x_dtype, int64_t M, int64_t in, int64
   if (ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(X) & 15) != 0)
     return fail(GPTQ_ERR_UNSUPPORTED, "X rows must be 16-byte aligned (ldx a multiple of 8)");
   if (M == 0) return GPTQ_OK;
-  const size_t need = dequant_matmul_workspace_bytes(M, in, out);
+  const size_t need = dequant_matmul_workspace_bytes(M, in, out, x_order ? 1 : 0);
   if (need > 0 && !workspace) return fail(GPTQ_ERR_INVALID_ARG, "workspace is NULL");
   if (workspace_bytes < need)
     return fail(GPTQ_ERR_WORKSPACE,
                 "workspace smaller than gptq_dequant_matmul_workspace_bytes(...) = " +
                     std::to_string(need));
-  return hip_status(run_dequant_matmul(X, M, in, ldx, qweight, scales, zeros, g_idx, out, bits, Y,
-                                       y_dtype == GPTQ_F16 ? 1 : 0, ldy, workspace,
-                                       static_cast<hipStream_t>(stream)),
+  return hip_status(run_dequant_matmul(X, M, in, ldx, qweight, scales, zeros, g_idx, x_order, out,
+                                       bits, Y, y_dtype == GPTQ_F16 ? 1 : 0, ldy, workspace,
+                                       workspace_bytes, static_cast<hipStream_t>(stream)),
                     "gptq_dequant_matmul");
+}
+
+size_t gptq_dequant_group_order_workspace_bytes(int64_t in) {
+  if (in < 1) return 0;
+  return dequant_group_order_workspace_bytes(in);
+}
+
+int gptq_dequant_group_order(const int32_t* qweight, const int32_t* g_idx, int64_t in,
+                             int64_t out, int bits, int32_t* qweight_sorted,
+                             int32_t* g_idx_sorted, int32_t* x_order, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (!qweight || !g_idx) return fail(GPTQ_ERR_INVALID_ARG, "qweight or g_idx is NULL");
+  if (!qweight_sorted || !g_idx_sorted || !x_order)
+    return fail(GPTQ_ERR_INVALID_ARG, "qweight_sorted, g_idx_sorted or x_order is NULL");
+  if (qweight_sorted == qweight)
+    return fail(GPTQ_ERR_INVALID_ARG, "qweight_sorted must not alias qweight");
+  if (in < 32 || in % 32 != 0)
+    return fail(GPTQ_ERR_INVALID_ARG, "in must be a positive multiple of 32");
+  if (out < 1) return fail(GPTQ_ERR_INVALID_ARG, "out must be >= 1");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits must be 2, 3, 4 or 8");
+  const size_t need = dequant_group_order_workspace_bytes(in);
+  if (!workspace) return fail(GPTQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(GPTQ_ERR_WORKSPACE,
+                "workspace smaller than gptq_dequant_group_order_workspace_bytes(in) = " +
+                    std::to_string(need));
+  return hip_status(run_dequant_group_order(qweight, g_idx, in, out, bits, qweight_sorted,
+                                            g_idx_sorted, x_order, workspace,
+                                            static_cast<hipStream_t>(stream)),
+                    "gptq_dequant_group_order");
 }
 
 const char* gptq_status_string(int status) {

@@ -103,6 +103,11 @@ size_t prepare_workspace_bytes(int64_t n);
 hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, float* U,
                        int32_t* perm, int32_t* info, void* ws, hipStream_t s);
 
+// order[r] = the index i of rank r when the n keys are sorted by decreasing
+// value, ties by increasing index (a stable sort).  rank: n ints of scratch.
+hipError_t launch_stable_order_desc(const uint32_t* keys, int64_t n, int32_t* rank,
+                                    int32_t* order, hipStream_t s);
+
 // gptq_quantize_layer pipeline.
 size_t quantize_workspace_bytes(int64_t out, int64_t in, int bits, int gs, int block);
 hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, const float* U,
@@ -113,12 +118,21 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
 // Dequantize-on-the-fly matmul Y = X W^T from the packed layer.  Up to
 // DQ_SMALL_M_MAX token rows take the HBM-bound kernel (its workspace holds
 // the split input range's partial sums), more the MFMA tiles.
+// With x_order, packed position p reads input column x_order[p]; the
+// matrix-core path gathers X into its workspace first.
 constexpr int DQ_SMALL_M_MAX = 16;
-size_t dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out);
+size_t dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order);
 hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
                               const int32_t* qweight, const float* scales, const int32_t* zeros,
-                              const int32_t* g_idx, int64_t out, int bits, void* Y, int y_f16,
-                              int64_t ldy, void* ws, hipStream_t s);
+                              const int32_t* g_idx, const int32_t* x_order, int64_t out, int bits,
+                              void* Y, int y_f16, int64_t ldy, void* ws, size_t ws_bytes,
+                              hipStream_t s);
+// The layer's input positions re-ordered by group (stable), repacked.
+size_t dequant_group_order_workspace_bytes(int64_t in);
+hipError_t run_dequant_group_order(const int32_t* qweight, const int32_t* g_idx, int64_t in,
+                                   int64_t out, int bits, int32_t* qweight_sorted,
+                                   int32_t* g_idx_sorted, int32_t* x_order, void* ws,
+                                   hipStream_t s);
 
 }  // namespace gptq
 

@@ -52,14 +52,16 @@ __device__ inline uint32_t chunk_code(const uint32_t* w, int k) {
 // Grid: (ceil(out / 64), nsplit).  Workgroup (bx, by) covers columns
 // [64 bx, 64 bx + 64) and chunks [by * cps, min((by + 1) * cps, in / 32)).
 // MB = token rows held per lane (>= M, a power of two up to 16).
+// LDS: the X slice [len][MB] fp32 (k-major), then cg[cps]: the group of each
+// chunk of the slice when all its 32 k share one, else -1.
 template <int B, int MB>
 __global__ void __launch_bounds__(256)
 dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
                 const uint32_t* __restrict__ qw, const float* __restrict__ scales,
                 const int32_t* __restrict__ zeros, const int32_t* __restrict__ g_idx,
-                int64_t out, int64_t cps, float* __restrict__ part, void* __restrict__ Y,
-                int y_f16, int64_t ldy) {
-  extern __shared__ __align__(16) float xs[];  // [len][MB], fp32 (k-major)
+                const int32_t* __restrict__ x_order, int64_t out, int64_t cps,
+                float* __restrict__ part, void* __restrict__ Y, int y_f16, int64_t ldy) {
+  extern __shared__ __align__(16) float xs[];
   const int tid = threadIdx.x, lane = tid & 63;
   // uniform: the chunk index, g_idx reads and the group test stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -70,59 +72,81 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
   const int64_t c0 = (int64_t)blockIdx.y * cps;
   const int64_t c1 = c0 + cps < nch ? c0 + cps : nch;
   const int len = (int)((c1 - c0) * DQ_CHUNK);
-  // X slice, 8 halves per 16-byte load (rows are 16-byte aligned)
-  for (int e = tid; e < MB * (len / 8); e += 256) {
-    const int m = e / (len / 8), k8 = 8 * (e % (len / 8));
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (m < M) v = *reinterpret_cast<const uint4*>(X + m * ldx + c0 * DQ_CHUNK + k8);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const half2_t h = __builtin_bit_cast(half2_t, u[j]);
-      xs[(k8 + 2 * j) * MB + m] = (float)h.x;
-      xs[(k8 + 2 * j + 1) * MB + m] = (float)h.y;
+  int* cg = reinterpret_cast<int*>(xs + (size_t)len * MB);
+  if (x_order) {
+    // X columns of the slice's positions, gathered
+    for (int e = tid; e < MB * len; e += 256) {
+      const int m = e / len, k = e % len;
+      float v = 0.0f;
+      if (m < M) v = (float)X[m * ldx + x_order[c0 * DQ_CHUNK + k]];
+      xs[k * MB + m] = v;
     }
+  } else {
+    // X slice, 8 halves per 16-byte load (rows are 16-byte aligned)
+    for (int e = tid; e < MB * (len / 8); e += 256) {
+      const int m = e / (len / 8), k8 = 8 * (e % (len / 8));
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (m < M) v = *reinterpret_cast<const uint4*>(X + m * ldx + c0 * DQ_CHUNK + k8);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const half2_t h = __builtin_bit_cast(half2_t, u[j]);
+        xs[(k8 + 2 * j) * MB + m] = (float)h.x;
+        xs[(k8 + 2 * j + 1) * MB + m] = (float)h.y;
+      }
+    }
+  }
+  for (int c = tid; c < (int)(c1 - c0); c += 256) {
+    const int32_t* gp = g_idx + (c0 + c) * DQ_CHUNK;
+    const int g0 = gp[0];
+    bool one = true;
+    for (int k = 1; k < DQ_CHUNK; ++k) one = one && gp[k] == g0;
+    cg[c] = one ? g0 : -1;
   }
   __syncthreads();
 
   float acc[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) acc[m] = 0.0f;
-  // Chunks c0 + wave, + 4, + 8, ... in blocks of SMALL_DEPTH; the words of
-  // the next block are loaded before the current one is used, so a lane
-  // keeps 2 * SMALL_DEPTH * B loads in flight and the memory latency
+  // Chunks c0 + wave, + 4, + 8, ... in blocks of SMALL_DEPTH.  The words of
+  // the next block, and the scale and zero of each of its single-group
+  // chunks, are loaded before the current block is used, so a lane keeps
+  // 2 * SMALL_DEPTH * (B + 2) loads in flight and the memory latency
   // overlaps the dequantization.
-  auto load_block = [&](int64_t cb, uint32_t (*w)[B + 1]) {
+  struct Blk {
+    uint32_t w[SMALL_DEPTH][B + 1];
+    float s[SMALL_DEPTH];
+    int32_t z[SMALL_DEPTH];
+    int g[SMALL_DEPTH];
+  };
+  auto load_block = [&](int64_t cb, Blk& k) {
 #pragma unroll
     for (int d = 0; d < SMALL_DEPTH; ++d) {
       const int64_t c = cb + 4 * d < c1 ? cb + 4 * d : c0;  // past the end: a valid dummy
 #pragma unroll
-      for (int i = 0; i < B; ++i) w[d][i] = qw[(c * B + i) * out + colc];
-      w[d][B] = 0u;
+      for (int i = 0; i < B; ++i) k.w[d][i] = qw[(c * B + i) * out + colc];
+      k.w[d][B] = 0u;
+      k.g[d] = __builtin_amdgcn_readfirstlane(cg[c - c0]);
+      const int64_t gi = k.g[d] >= 0 ? k.g[d] : 0;
+      k.s[d] = scales[gi * out + colc];
+      k.z[d] = zeros[gi * out + colc];
     }
   };
-  uint32_t wcur[SMALL_DEPTH][B + 1], wnxt[SMALL_DEPTH][B + 1];
-  load_block(c0 + wave, wcur);
+  Blk cur, nxt;
+  load_block(c0 + wave, cur);
   for (int64_t cb = c0 + wave; cb < c1; cb += 4 * SMALL_DEPTH) {
-    load_block(cb + 4 * SMALL_DEPTH, wnxt);
+    load_block(cb + 4 * SMALL_DEPTH, nxt);
 #pragma unroll
     for (int d = 0; d < SMALL_DEPTH; ++d) {
       const int64_t c = cb + 4 * d;
       if (c >= c1) break;  // uniform
       const int64_t kb = c * DQ_CHUNK;
       const int xo = (int)(kb - c0 * DQ_CHUNK);
-      // the chunk's groups (uniform); one group for all 32 k is the common case
-      int gk[DQ_CHUNK];
-      bool one = true;
-#pragma unroll
-      for (int k = 0; k < DQ_CHUNK; ++k) {
-        gk[k] = g_idx[kb + k];
-        one = one && gk[k] == gk[0];
-      }
-      if (one) {
-        // w = s q - s z: one FMA per weight after the code's conversion
-        const float sc = scales[gk[0] * out + colc];
-        const float nsz = -sc * (float)zeros[gk[0] * out + colc];
+      if (cur.g[d] >= 0) {
+        // one group for all 32 k: w = s q - s z, one FMA per weight after
+        // the code's conversion
+        const float sc = cur.s[d];
+        const float nsz = -sc * (float)cur.z[d];
 #pragma unroll
         for (int k4 = 0; k4 < DQ_CHUNK; k4 += 4) {
           float xv[4 * MB];
@@ -133,12 +157,13 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
           }
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
-            const float wv = fmaf((float)chunk_code<B>(wcur[d], k4 + kk), sc, nsz);
+            const float wv = fmaf((float)chunk_code<B>(cur.w[d], k4 + kk), sc, nsz);
 #pragma unroll
             for (int m = 0; m < MB; ++m) acc[m] = fmaf(xv[kk * MB + m], wv, acc[m]);
           }
         }
       } else {
+        // the chunk's groups (uniform), one scale and zero per k
 #pragma unroll
         for (int k4 = 0; k4 < DQ_CHUNK; k4 += 4) {
           float xv[4 * MB];
@@ -150,19 +175,17 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             const int k = k4 + kk;
-            const float sc = scales[gk[k] * out + colc];
-            const float nsz = -sc * (float)zeros[gk[k] * out + colc];
-            const float wv = fmaf((float)chunk_code<B>(wcur[d], k), sc, nsz);
+            const int64_t g = g_idx[kb + k];
+            const float sc = scales[g * out + colc];
+            const float nsz = -sc * (float)zeros[g * out + colc];
+            const float wv = fmaf((float)chunk_code<B>(cur.w[d], k), sc, nsz);
 #pragma unroll
             for (int m = 0; m < MB; ++m) acc[m] = fmaf(xv[kk * MB + m], wv, acc[m]);
           }
         }
       }
     }
-#pragma unroll
-    for (int d = 0; d < SMALL_DEPTH; ++d)
-#pragma unroll
-      for (int i = 0; i <= B; ++i) wcur[d][i] = wnxt[d][i];
+    cur = nxt;
   }
   // the four waves' sums, in wave order
   __syncthreads();
@@ -326,6 +349,59 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
       }
 }
 
+// ------------------------------------------------------------ group order --
+// Xp[m][p] = X[m][x_order[p]] (the matrix-core path's X in packed order).
+__global__ void __launch_bounds__(256)
+dq_gather_x_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
+                   const int32_t* __restrict__ x_order, _Float16* __restrict__ Xp) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= in) return;
+  const int64_t k = x_order[p];
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) Xp[m * in + p] = X[m * ldx + k];
+}
+
+// keys[k] = ~g_idx[k]: decreasing key = increasing group.
+__global__ void dq_group_keys_kernel(const int32_t* __restrict__ g_idx, int64_t in,
+                                     uint32_t* __restrict__ keys) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k < in) keys[k] = ~(uint32_t)g_idx[k];
+}
+
+__global__ void dq_gather_i32_kernel(const int32_t* __restrict__ src,
+                                     const int32_t* __restrict__ idx, int64_t n,
+                                     int32_t* __restrict__ dst) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p < n) dst[p] = src[idx[p]];
+}
+
+// qs: column col's codes in x_order, re-packed.  Grid (ceil(out / 256), in / 32):
+// thread = one column, one chunk of 32 sorted positions (= B output words).
+template <int B>
+__global__ void __launch_bounds__(256)
+dq_repack_kernel(const uint32_t* __restrict__ qw, const int32_t* __restrict__ x_order,
+                 int64_t out, uint32_t* __restrict__ qs) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= out) return;
+  const int64_t c = blockIdx.y;
+  uint32_t w[B + 1];
+#pragma unroll
+  for (int i = 0; i <= B; ++i) w[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < DQ_CHUNK; ++j) {
+    const int64_t bit = (int64_t)x_order[c * DQ_CHUNK + j] * B;
+    const int64_t wi = bit >> 5;
+    const int off = (int)(bit & 31);
+    uint32_t v = qw[wi * out + col] >> off;
+    if (off + B > 32) v |= qw[(wi + 1) * out + col] << (32 - off);
+    v &= (1u << B) - 1u;
+    const int pos = j * B, pw = pos >> 5, po = pos & 31;
+    w[pw] |= v << po;
+    if (po + B > 32) w[pw + 1] |= v >> (32 - po);
+  }
+#pragma unroll
+  for (int i = 0; i < B; ++i) qs[(c * B + i) * out + col] = w[i];
+}
+
 // ------------------------------------------------------------------- plan --
 struct SmallPlan {
   int mb;        // token rows per lane
@@ -344,11 +420,11 @@ SmallPlan small_plan(int64_t M, int64_t in, int64_t out) {
   if (ns > nch / (8 * SMALL_DEPTH)) ns = nch / (8 * SMALL_DEPTH);
   if (ns < 1) ns = 1;
   int64_t cps = (nch + ns - 1) / ns;
-  const int64_t cps_max = SMALL_LDS_MAX / ((int64_t)p.mb * DQ_CHUNK * 4);
+  const int64_t cps_max = SMALL_LDS_MAX / (((int64_t)p.mb * DQ_CHUNK + 1) * 4);
   if (cps > cps_max) cps = cps_max;
   p.cps = cps;
   p.nsplit = (int)((nch + cps - 1) / cps);
-  const size_t xsb = (size_t)p.mb * cps * DQ_CHUNK * 4, redb = (size_t)4 * p.mb * 64 * 4;
+  const size_t xsb = ((size_t)p.mb * cps * DQ_CHUNK + cps) * 4, redb = (size_t)4 * p.mb * 64 * 4;
   p.lds = xsb > redb ? xsb : redb;
   return p;
 }
@@ -356,53 +432,57 @@ SmallPlan small_plan(int64_t M, int64_t in, int64_t out) {
 template <int B, int MB>
 hipError_t launch_small_t(const SmallPlan& p, const _Float16* X, int64_t M, int64_t in,
                           int64_t ldx, const uint32_t* qw, const float* scales,
-                          const int32_t* zeros, const int32_t* g_idx, int64_t out, float* part,
-                          void* Y, int y_f16, int64_t ldy, hipStream_t s) {
+                          const int32_t* zeros, const int32_t* g_idx, const int32_t* xo,
+                          int64_t out, float* part, void* Y, int y_f16, int64_t ldy,
+                          hipStream_t s) {
   auto k = dq_small_kernel<B, MB>;
   GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)p.lds));
   dim3 grid((unsigned)((out + SMALL_COLS - 1) / SMALL_COLS), (unsigned)p.nsplit);
-  hipLaunchKernelGGL(k, grid, dim3(256), p.lds, s, X, M, in, ldx, qw, scales, zeros, g_idx, out,
-                     p.cps, part, Y, y_f16, ldy);
+  hipLaunchKernelGGL(k, grid, dim3(256), p.lds, s, X, M, in, ldx, qw, scales, zeros, g_idx, xo,
+                     out, p.cps, part, Y, y_f16, ldy);
   return hipGetLastError();
 }
 template <int B>
 hipError_t launch_small_b(const SmallPlan& p, const _Float16* X, int64_t M, int64_t in,
                           int64_t ldx, const uint32_t* qw, const float* scales,
-                          const int32_t* zeros, const int32_t* g_idx, int64_t out, float* part,
-                          void* Y, int y_f16, int64_t ldy, hipStream_t s) {
+                          const int32_t* zeros, const int32_t* g_idx, const int32_t* xo,
+                          int64_t out, float* part, void* Y, int y_f16, int64_t ldy,
+                          hipStream_t s) {
   switch (p.mb) {
-    case 1: return launch_small_t<B, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s);
-    case 2: return launch_small_t<B, 2>(p, X, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s);
-    case 4: return launch_small_t<B, 4>(p, X, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s);
-    case 8: return launch_small_t<B, 8>(p, X, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s);
-    default: return launch_small_t<B, 16>(p, X, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s);
+    case 1: return launch_small_t<B, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    case 2: return launch_small_t<B, 2>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    case 4: return launch_small_t<B, 4>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    case 8: return launch_small_t<B, 8>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    default: return launch_small_t<B, 16>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
   }
 }
 
 }  // namespace
 
-size_t dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out) {
-  if (M > DQ_SMALL_M_MAX) return 0;
+size_t dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order) {
+  if (M > DQ_SMALL_M_MAX) return has_order ? align_up((size_t)M * in * sizeof(_Float16)) : 0;
   const SmallPlan p = small_plan(M, in, out);
   return p.nsplit > 1 ? align_up((size_t)p.nsplit * M * out * sizeof(float)) : 0;
 }
 
 hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
                               const int32_t* qweight, const float* scales, const int32_t* zeros,
-                              const int32_t* g_idx, int64_t out, int bits, void* Y, int y_f16,
-                              int64_t ldy, void* ws, hipStream_t s) {
+                              const int32_t* g_idx, const int32_t* x_order, int64_t out, int bits,
+                              void* Y, int y_f16, int64_t ldy, void* ws, size_t ws_bytes,
+                              hipStream_t s) {
   const _Float16* x = static_cast<const _Float16*>(X);
   const uint32_t* qw = reinterpret_cast<const uint32_t*>(qweight);
+  const int32_t* xo = x_order;
   if (M <= DQ_SMALL_M_MAX) {
     const SmallPlan p = small_plan(M, in, out);
     float* part = static_cast<float*>(ws);
     hipError_t e;
     switch (bits) {
-      case 2: e = launch_small_b<2>(p, x, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s); break;
-      case 3: e = launch_small_b<3>(p, x, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s); break;
-      case 8: e = launch_small_b<8>(p, x, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s); break;
-      default: e = launch_small_b<4>(p, x, M, in, ldx, qw, scales, zeros, g_idx, out, part, Y, y_f16, ldy, s); break;
+      case 2: e = launch_small_b<2>(p, x, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s); break;
+      case 3: e = launch_small_b<3>(p, x, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s); break;
+      case 8: e = launch_small_b<8>(p, x, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s); break;
+      default: e = launch_small_b<4>(p, x, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s); break;
     }
     GPTQ_HIP_TRY(e);
     if (p.nsplit > 1) {
@@ -413,12 +493,52 @@ hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
     }
     return hipSuccess;
   }
+  if (xo) {
+    // X in packed order into the workspace, then the plain product on it
+    if (ws_bytes < (size_t)M * in * sizeof(_Float16)) return hipErrorInvalidValue;
+    _Float16* xp = static_cast<_Float16*>(ws);
+    hipLaunchKernelGGL(dq_gather_x_kernel, dim3((unsigned)((in + 255) / 256), (unsigned)(M < 1024 ? M : 1024)),
+                       dim3(256), 0, s, x, M, in, ldx, xo, xp);
+    GPTQ_HIP_TRY(hipGetLastError());
+    x = xp;
+    ldx = in;
+  }
   dim3 grid((unsigned)((out + TB - 1) / TB), (unsigned)((M + TB - 1) / TB));
   switch (bits) {
     case 2: hipLaunchKernelGGL(dq_mfma_kernel<2>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
     case 3: hipLaunchKernelGGL(dq_mfma_kernel<3>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
     case 8: hipLaunchKernelGGL(dq_mfma_kernel<8>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
     default: hipLaunchKernelGGL(dq_mfma_kernel<4>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
+  }
+  return hipGetLastError();
+}
+
+size_t dequant_group_order_workspace_bytes(int64_t in) {
+  return 2 * align_up((size_t)in * sizeof(int32_t));
+}
+
+hipError_t run_dequant_group_order(const int32_t* qweight, const int32_t* g_idx, int64_t in,
+                                   int64_t out, int bits, int32_t* qweight_sorted,
+                                   int32_t* g_idx_sorted, int32_t* x_order, void* ws,
+                                   hipStream_t s) {
+  uint32_t* keys = static_cast<uint32_t*>(ws);
+  int32_t* rank = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                             align_up((size_t)in * sizeof(int32_t)));
+  const unsigned nb = (unsigned)((in + 255) / 256);
+  hipLaunchKernelGGL(dq_group_keys_kernel, dim3(nb), dim3(256), 0, s, g_idx, in, keys);
+  GPTQ_HIP_TRY(hipGetLastError());
+  GPTQ_HIP_TRY(launch_stable_order_desc(keys, in, rank, x_order, s));
+  hipLaunchKernelGGL(dq_gather_i32_kernel, dim3(nb), dim3(256), 0, s, g_idx, x_order, in,
+                     g_idx_sorted);
+  GPTQ_HIP_TRY(hipGetLastError());
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(qweight);
+  uint32_t* qs = reinterpret_cast<uint32_t*>(qweight_sorted);
+  dim3 grid((unsigned)((out + 255) / 256), (unsigned)(in / DQ_CHUNK));
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(dq_repack_kernel<2>, grid, dim3(256), 0, s, qw, x_order, out, qs); break;
+    case 3: hipLaunchKernelGGL(dq_repack_kernel<3>, grid, dim3(256), 0, s, qw, x_order, out, qs); break;
+    case 8: hipLaunchKernelGGL(dq_repack_kernel<8>, grid, dim3(256), 0, s, qw, x_order, out, qs); break;
+    default: hipLaunchKernelGGL(dq_repack_kernel<4>, grid, dim3(256), 0, s, qw, x_order, out, qs); break;
   }
   return hipGetLastError();
 }

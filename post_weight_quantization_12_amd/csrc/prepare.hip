@@ -777,6 +777,20 @@ PrepLayout carve(void* ws, int64_t n) {
 
 size_t prepare_workspace_bytes(int64_t n) { return carve(nullptr, n).bytes; }
 
+hipError_t launch_stable_order_desc(const uint32_t* keys, int64_t n, int32_t* rank,
+                                    int32_t* order, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const unsigned nb256 = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(nb256 < 2048 ? nb256 : 2048), dim3(256), 0, s,
+                     reinterpret_cast<float*>(rank), n, 0.0f);  // all-zero bits: int 0
+  GPTQ_HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(rank_count_kernel, dim3(nb256, (unsigned)((n + RANK_CHUNK - 1) / RANK_CHUNK)),
+                     dim3(256), 0, s, keys, n, 1, rank);
+  GPTQ_HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(rank_scatter_kernel, dim3(nb256), dim3(256), 0, s, rank, n, 1, order);
+  return hipGetLastError();
+}
+
 hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, float* U,
                        int32_t* perm, int32_t* info, void* ws, hipStream_t s) {
   PrepLayout l = carve(ws, n);

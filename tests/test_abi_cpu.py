@@ -21,7 +21,8 @@ def test_exports_every_header_function(lib):
                           "gptq_prepare_workspace_bytes",
                           "gptq_prepare", "gptq_quantize_workspace_bytes",
                           "gptq_quantize_layer", "gptq_dequant_matmul_workspace_bytes",
-                          "gptq_dequant_matmul", "gptq_status_string",
+                          "gptq_dequant_matmul", "gptq_dequant_group_order_workspace_bytes",
+                          "gptq_dequant_group_order", "gptq_status_string",
                           "gptq_last_error_message"}
     for n in names:
         assert hasattr(lib, n), n
@@ -113,14 +114,15 @@ def test_binding_refuses_cpu_tensors():
 def test_dequant_matmul_argument_errors(lib):
     f = lib.gptq_dequant_matmul
     A16 = ctypes.c_void_p(4096)   # 16-byte aligned, never dereferenced
-    ok = dict(X=A16, xd=L.GPTQ_F16, M=2, inp=64, ldx=64, q=FAKE, s=FAKE, z=FAKE, g=FAKE, G=2,
-              out=8, bits=4, Y=FAKE, yd=L.GPTQ_F32, ldy=8)
+    ok = dict(X=A16, xd=L.GPTQ_F16, M=2, inp=64, ldx=64, q=FAKE, s=FAKE, z=FAKE, g=FAKE,
+              xo=None, G=2, out=8, bits=4, Y=FAKE, yd=L.GPTQ_F32, ldy=8)
 
     def call(**kw):
         a = dict(ok, **kw)
-        ws = lib.gptq_dequant_matmul_workspace_bytes(a["M"], a["inp"], a["out"])
+        ws = lib.gptq_dequant_matmul_workspace_bytes(a["M"], a["inp"], a["out"],
+                                                     int(a["xo"] is not None))
         return f(a["X"], a["xd"], a["M"], a["inp"], a["ldx"], a["q"], a["s"], a["z"], a["g"],
-                 a["G"], a["out"], a["bits"], a["Y"], a["yd"], a["ldy"],
+                 a["xo"], a["G"], a["out"], a["bits"], a["Y"], a["yd"], a["ldy"],
                  kw.get("ws", FAKE if ws else None), kw.get("wsb", ws), None)
 
     assert call(X=None) == L.GPTQ_ERR_INVALID_ARG
@@ -139,12 +141,38 @@ def test_dequant_matmul_argument_errors(lib):
     assert call(ldx=68) == L.GPTQ_ERR_UNSUPPORTED
     assert call(X=ctypes.c_void_p(4098)) == L.GPTQ_ERR_UNSUPPORTED
     # the small-M path splits the input range: a workspace is required
-    need = lib.gptq_dequant_matmul_workspace_bytes(1, 4096, 4096)
-    assert need > 0 and lib.gptq_dequant_matmul_workspace_bytes(64, 4096, 4096) == 0
-    assert lib.gptq_dequant_matmul_workspace_bytes(0, 4096, 4096) == 0
+    need = lib.gptq_dequant_matmul_workspace_bytes(1, 4096, 4096, 0)
+    assert need > 0 and lib.gptq_dequant_matmul_workspace_bytes(64, 4096, 4096, 0) == 0
+    assert lib.gptq_dequant_matmul_workspace_bytes(0, 4096, 4096, 0) == 0
+    # with an x_order the matrix-core path gathers X (M x in fp16) first
+    assert lib.gptq_dequant_matmul_workspace_bytes(64, 4096, 4096, 1) >= 64 * 4096 * 2
+    assert call(M=64, xo=FAKE, ws=None, wsb=0) == L.GPTQ_ERR_INVALID_ARG
+    assert call(M=64, xo=FAKE, ws=FAKE, wsb=64 * 64 * 2 - 1) == L.GPTQ_ERR_WORKSPACE
     assert call(M=1, inp=4096, ldx=4096, out=4096, ldy=4096, ws=None, wsb=0) == \
         L.GPTQ_ERR_INVALID_ARG
     assert call(M=1, inp=4096, ldx=4096, out=4096, ldy=4096, ws=FAKE, wsb=need - 1) == \
         L.GPTQ_ERR_WORKSPACE
     # M == 0 is a no-op that never touches the device
     assert call(M=0) == L.GPTQ_OK
+
+
+def test_dequant_group_order_argument_errors(lib):
+    f = lib.gptq_dequant_group_order
+    Q2 = ctypes.c_void_p(8192)
+    ws = lib.gptq_dequant_group_order_workspace_bytes(64)
+    assert ws >= 2 * 64 * 4 and lib.gptq_dequant_group_order_workspace_bytes(0) == 0
+
+    def call(q=FAKE, g=FAKE, inp=64, out=8, bits=4, qs=Q2, gs=FAKE, xo=FAKE, w=FAKE, wsb=ws):
+        return f(q, g, inp, out, bits, qs, gs, xo, w, wsb, None)
+
+    assert call(q=None) == L.GPTQ_ERR_INVALID_ARG
+    assert call(g=None) == L.GPTQ_ERR_INVALID_ARG
+    assert call(qs=None) == L.GPTQ_ERR_INVALID_ARG
+    assert call(xo=None) == L.GPTQ_ERR_INVALID_ARG
+    assert call(qs=FAKE) == L.GPTQ_ERR_INVALID_ARG
+    assert b"alias" in lib.gptq_last_error_message()
+    assert call(inp=48) == L.GPTQ_ERR_INVALID_ARG
+    assert call(out=0) == L.GPTQ_ERR_INVALID_ARG
+    assert call(bits=5) == L.GPTQ_ERR_UNSUPPORTED
+    assert call(w=None) == L.GPTQ_ERR_INVALID_ARG
+    assert call(wsb=ws - 1) == L.GPTQ_ERR_WORKSPACE

@@ -123,3 +123,70 @@ def test_quantized_layer_end_to_end(M):
     rel = np.linalg.norm(Y.cpu().numpy() - y_full) / np.linalg.norm(y_full)
     print(f"  vs unquantized layer: rel {rel:.3f}")
     assert rel < 0.2   # 4-bit g64 of Gaussian weights: a few percent
+
+
+ORDER_CASES = [
+    # name, out, in, bits, gs, desc
+    ("down_like_4b_g128_desc", 300, 11008, 4, 128, True),
+    ("3b_g32_desc", 70, 256, 3, 32, True),
+    ("8b_g64_desc", 257, 512, 8, 64, True),
+    ("2b_g16_desc", 33, 96, 2, 16, True),      # groups of 16: chunks still hold two
+    ("4b_g128_in_order", 64, 1024, 4, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", ORDER_CASES, ids=[c[0] for c in ORDER_CASES])
+def test_group_order_matches_oracle(case):
+    """gptq_dequant_group_order against the oracle (integer work: bit-exact),
+    then the product on the re-ordered layer against the oracle's product on
+    the layer as packed, through both kernels."""
+    name, out, inp, bits, gs, desc = case
+    _banner(f"dequant_group_order {name} out={out} in={inp} {bits}b g{gs}")
+    qw, scales, zeros, g_idx = _layer(out, inp, bits, gs, desc, seed=out + inp + 3 * bits)
+    qs_o, gs_o, order_o = O.group_order(qw, g_idx, bits)
+    qw_d, g_d = torch.from_numpy(qw).to(DEV), torch.from_numpy(g_idx).to(DEV)
+    qs, gsrt, order = P.dequant_group_order(qw_d, g_d, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(order.cpu().numpy(), order_o)
+    assert np.array_equal(gsrt.cpu().numpy(), gs_o)
+    assert np.array_equal(qs.cpu().numpy(), qs_o)
+    sc_d, z_d = torch.from_numpy(scales).to(DEV), torch.from_numpy(zeros).to(DEV)
+    for M in (1, 5, 40):
+        g = torch.Generator().manual_seed(M + inp)
+        X = torch.randn((M, inp), generator=g).to(torch.float16)
+        Y = P.dequant_matmul(X.to(DEV), qs, sc_d, z_d, gsrt, bits, x_order=order)
+        Y2 = P.dequant_matmul(X.to(DEV), qs, sc_d, z_d, gsrt, bits, x_order=order)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y2)
+        print(f"  M={M}")
+        _check(X, qw, scales, zeros, g_idx, bits, Y)
+
+
+def test_group_order_full_size_sampled():
+    """8192 x 28672 4-bit g64 act-order layer (the 70B down_proj shape): the
+    order and sorted g_idx in full, the re-packed words on sampled columns,
+    and one decode product on sampled columns."""
+    out, inp, bits, gs = 8192, 28672, 4, 64
+    _banner(f"dequant_group_order full size out={out} in={inp} {bits}b g{gs}")
+    rng = np.random.default_rng(77)
+    perm = rng.permutation(inp)
+    g_idx = O.g_index(perm, gs).astype(np.int32)
+    G = inp // gs
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    qw_d = torch.randint(-2 ** 31, 2 ** 31 - 1, (inp * bits // 32, out), generator=gen,
+                         device=DEV, dtype=torch.int64).to(torch.int32)
+    sc_d = 1e-3 + 4.9e-2 * torch.rand((G, out), generator=gen, device=DEV)
+    z_d = torch.randint(0, 2 ** bits, (G, out), generator=gen, device=DEV, dtype=torch.int32)
+    g_d = torch.from_numpy(g_idx).to(DEV)
+    qs, gsrt, order = P.dequant_group_order(qw_d, g_d, bits)
+    X = torch.randn((1, inp), generator=torch.Generator().manual_seed(6)).to(torch.float16)
+    Y = P.dequant_matmul(X.to(DEV), qs, sc_d, z_d, gsrt, bits, x_order=order)
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([[0, 1, 255, 256, out - 1],
+                                     rng.choice(out, 27, replace=False)]))
+    qw_c = qw_d[:, cols].cpu().numpy()
+    qs_o, gs_o, order_o = O.group_order(qw_c, g_idx, bits)
+    assert np.array_equal(order.cpu().numpy(), order_o)
+    assert np.array_equal(gsrt.cpu().numpy(), gs_o)
+    assert np.array_equal(qs[:, cols].cpu().numpy(), qs_o)
+    _check(X, qw_d.cpu().numpy(), sc_d.cpu().numpy(), z_d.cpu().numpy(), g_idx, bits, Y, cols)

@@ -493,3 +493,41 @@ def test_dequant_matmul_input_permutation_invariant():
     p = rng.permutation(n)
     y2 = O.dequant_matmul(x[:, p], O.pack(codes[:, p], bits), scales, zeros, g_idx[p], bits)
     assert np.allclose(y, y2, rtol=1e-12, atol=1e-12)
+
+
+def test_group_order_hand_example():
+    # g_idx 2 0 1 0 2 1 over 32 inputs (pattern repeated): sorted by group with
+    # ties in input order, the first group-0 inputs are 1, 3, 7, 9, ...
+    g_idx = np.array([2, 0, 1, 0, 2, 1] * 5 + [0, 1], dtype=np.int32)
+    codes = np.arange(32).reshape(1, 32) % 16
+    qs, gs, order = O.group_order(O.pack(codes, 4), g_idx, 4)
+    zeros_at = [k for k in range(32) if g_idx[k] == 0]
+    ones_at = [k for k in range(32) if g_idx[k] == 1]
+    twos_at = [k for k in range(32) if g_idx[k] == 2]
+    assert order.tolist() == zeros_at + ones_at + twos_at
+    assert order[:4].tolist() == [1, 3, 7, 9]
+    assert gs.tolist() == [0] * len(zeros_at) + [1] * len(ones_at) + [2] * len(twos_at)
+    # position p of the re-packed stream holds the code of input order[p]
+    assert _bit_loop_codes(qs, 4, 32)[0].tolist() == [int(codes[0, k]) for k in order]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_group_order_same_product_exactly(bits):
+    # Integer X and power-of-two scales: every term and partial sum is exact
+    # in fp64, so the re-ordered layer must give the identical Y.
+    rng = np.random.default_rng(20 + bits)
+    out, n, gs = 4, 128, 32
+    codes = rng.integers(0, 2 ** bits, size=(out, n))
+    g_idx = O.g_index(rng.permutation(n), gs)
+    scales = (2.0 ** rng.integers(-6, 0, size=(n // gs, out))).astype(np.float32)
+    zeros = rng.integers(0, 2 ** bits, size=(n // gs, out)).astype(np.int32)
+    x = rng.integers(-8, 9, size=(3, n)).astype(np.float64)
+    qw = O.pack(codes, bits)
+    qs, gsrt, order = O.group_order(qw, g_idx, bits)
+    assert sorted(order.tolist()) == list(range(n))
+    assert np.all(np.diff(gsrt) >= 0)
+    y = O.dequant_matmul(x, qw, scales, zeros, g_idx, bits)
+    y2 = O.dequant_matmul(x, qs, scales, zeros, gsrt, bits, x_order=order)
+    assert np.array_equal(y, y2)
+    # the ordered layer's chunks of 32 inputs each hold one group
+    assert all(len(set(gsrt[c:c + 32].tolist())) == 1 for c in range(0, n, 32))

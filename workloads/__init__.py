@@ -27,7 +27,7 @@ import torch
 
 __all__ = ["Config", "CONFIGS", "get", "weight", "x_sample", "x_tokens",
            "outlier_channels", "boundary_safe_weight", "synthetic_hinv_chol",
-           "generator"]
+           "generator", "packed_layer_draws"]
 
 
 @dataclass(frozen=True)
@@ -223,3 +223,28 @@ def synthetic_hinv_chol(n: int, device="cpu", seed: int = 0, row_norm: float = 0
     U = torch.triu(m, 1) * (sig * d)[:, None]
     U += torch.diag(d)
     return U.contiguous()
+
+
+def packed_layer_draws(cfg: Config, device="cpu", seed: int = 0):
+    """Random contents for a packed layer of cfg's shape and bit width.
+
+    Returns (words, scales, zeros, order): words int32 [inp * bits / 32 x out]
+    uniformly random (every b-bit field is a uniform code), scales fp32
+    [G x out] uniform in [1e-3, 5e-2], zeros int32 [G x out] uniform in
+    [0, 2^bits), G = number of groups of cfg.group_size along inp, and order a
+    random permutation of the inp columns when cfg.desc_act (else the
+    identity), the column order a desc_act layer's groups follow.
+    """
+    gs = cfg.inp if cfg.group_size == -1 else cfg.group_size
+    G = -(-cfg.inp // gs)
+    g = generator(device, seed, cfg.cfg_id, 5, cfg.bits * 1000 + gs)
+    words = torch.randint(-2 ** 31, 2 ** 31 - 1, (cfg.inp * cfg.bits // 32, cfg.out),
+                          generator=g, device=device, dtype=torch.int64).to(torch.int32)
+    scales = 1e-3 + 4.9e-2 * torch.rand((G, cfg.out), generator=g, device=device)
+    zeros = torch.randint(0, 2 ** cfg.bits, (G, cfg.out), generator=g, device=device,
+                          dtype=torch.int32)
+    if cfg.desc_act:
+        order = torch.randperm(cfg.inp, generator=g, device=device)
+    else:
+        order = torch.arange(cfg.inp, device=device)
+    return words, scales, zeros, order
