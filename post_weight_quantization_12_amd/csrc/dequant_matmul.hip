@@ -14,9 +14,10 @@
 //   * few tokens (M <= 16, decode): HBM-bound on qweight.  Lane = output
 //     column (a wave's 64 columns read 256 contiguous bytes per word row),
 //     the four waves of a workgroup take interleaved chunks of the
-//     workgroup's input range, weights are dequantized exactly in fp32 and
-//     multiplied into up to 16 token rows held in registers; X's slice of
-//     the input range is staged in LDS.  The input dimension is split over
+//     workgroup's input range; per chunk, exact (q - z) code pairs in fp16
+//     meet X pairs in v_dot2_f32_f16 (fp32 sums, up to 16 token rows held
+//     in registers) and the sum is scaled once; X's slice of the input range
+//     is staged in LDS as fp16 pairs.  The input dimension is split over
 //     several workgroups (grid >= 2 per compute unit); their partial sums go
 //     to the workspace and a second kernel adds them in a fixed order.
 //   * many tokens (prefill): 128 x 128 tiles on v_mfma_f32_32x32x16_f16.
@@ -48,12 +49,55 @@ __device__ inline uint32_t chunk_code(const uint32_t* w, int k) {
   return v & ((1u << B) - 1u);
 }
 
+// Code pairs.  A chunk's 32 codes form 16 pairs whose two b-bit fields sit
+// at the same offsets of the two halves of one word (for b = 2, 4, 8), so
+// one shift and one AND extract a pair as (lo, hi) 16-bit lanes:
+//   b = 4: pair p = (code 8j + i, code 8j + i + 4), j = p / 4, i = p % 4
+//   b = 8: pair p = (code 4j + i, code 4j + i + 2), j = p / 2, i = p % 2
+//   b = 2: pair p = (code 16j + i, code 16j + i + 8), j = p / 8, i = p % 8
+//   b = 3: pair p = (code 2p, code 2p + 1), fields gathered one by one.
+template <int B>
+__host__ __device__ constexpr int pair_code(int p, int hi) {
+  return B == 4 ? 8 * (p / 4) + p % 4 + 4 * hi
+       : B == 8 ? 4 * (p / 2) + p % 2 + 2 * hi
+       : B == 2 ? 16 * (p / 8) + p % 8 + 8 * hi
+       : 2 * p + hi;
+}
+// (a & m) | o in one VALU op.  gfx950's three-operand encoding takes no
+// literal, so the masks live in registers the caller keeps.
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(o));
+  return d;
+}
+// Pair p of a chunk whose words are w, as the fp16 pair (1024 + lo, 1024 + hi).
+// m = the pair mask of B (0x000F000F for B = 4, ...), o = 0x64006400.
+template <int B>
+__device__ inline uint32_t pair_magic(const uint32_t* w, int p, uint32_t m, uint32_t o) {
+  if constexpr (B == 4) return and_or(w[p / 4] >> (4 * (p % 4)), m, o);
+  if constexpr (B == 8) return and_or(w[p / 2] >> (8 * (p % 2)), m, o);
+  if constexpr (B == 2) return and_or(w[p / 8] >> (2 * (p % 8)), m, o);
+  return chunk_code<B>(w, 2 * p) | (chunk_code<B>(w, 2 * p + 1) << 16) | 0x64006400u;
+}
+template <int B>
+__host__ __device__ constexpr uint32_t pair_mask() {
+  return B == 4 ? 0x000F000Fu : B == 8 ? 0x00FF00FFu : B == 2 ? 0x00030003u : 0u;
+}
+
 // ---------------------------------------------------------------- small M --
 // Grid: (ceil(out / 64), nsplit).  Workgroup (bx, by) covers columns
 // [64 bx, 64 bx + 64) and chunks [by * cps, min((by + 1) * cps, in / 32)).
 // MB = token rows held per lane (>= M, a power of two up to 16).
-// LDS: the X slice [len][MB] fp32 (k-major), then cg[cps]: the group of each
-// chunk of the slice when all its 32 k share one, else -1.
+// LDS: xp[pair][MB], the X slice as fp16 pairs in the chunks' pair order
+// (pair p of chunk c at 16 c + p), then cg[cps]: the group of each chunk of
+// the slice when all its 32 k share one, else -1.
+//
+// A single-group chunk is summed as s * sum_k x_k (q_k - z): each pair
+// (q_a - z, q_b - z) is formed exactly in fp16 (0x6400 | q is 1024 + q,
+// minus 1024 + z: integers below 2048) and v_dot2_f32_f16 multiplies it with
+// the X pair into an fp32 sum (products of fp16 values are exact in fp32);
+// the chunk's sum is scaled by s once.  Mixed-group chunks dequantize each
+// weight in fp32 as s (q - z).
 template <int B, int MB>
 __global__ void __launch_bounds__(256)
 dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
@@ -61,7 +105,7 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
                 const int32_t* __restrict__ zeros, const int32_t* __restrict__ g_idx,
                 const int32_t* __restrict__ x_order, int64_t out, int64_t cps,
                 float* __restrict__ part, void* __restrict__ Y, int y_f16, int64_t ldy) {
-  extern __shared__ __align__(16) float xs[];
+  extern __shared__ __align__(16) uint32_t xp[];
   const int tid = threadIdx.x, lane = tid & 63;
   // uniform: the chunk index, g_idx reads and the group test stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -71,32 +115,40 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
   const int64_t nch = in / DQ_CHUNK;
   const int64_t c0 = (int64_t)blockIdx.y * cps;
   const int64_t c1 = c0 + cps < nch ? c0 + cps : nch;
-  const int len = (int)((c1 - c0) * DQ_CHUNK);
-  int* cg = reinterpret_cast<int*>(xs + (size_t)len * MB);
-  if (x_order) {
-    // X columns of the slice's positions, gathered
-    for (int e = tid; e < MB * len; e += 256) {
-      const int m = e / len, k = e % len;
-      float v = 0.0f;
-      if (m < M) v = (float)X[m * ldx + x_order[c0 * DQ_CHUNK + k]];
-      xs[k * MB + m] = v;
-    }
-  } else {
-    // X slice, 8 halves per 16-byte load (rows are 16-byte aligned)
-    for (int e = tid; e < MB * (len / 8); e += 256) {
-      const int m = e / (len / 8), k8 = 8 * (e % (len / 8));
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (m < M) v = *reinterpret_cast<const uint4*>(X + m * ldx + c0 * DQ_CHUNK + k8);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  const int ncl = (int)(c1 - c0);
+  int* cg = reinterpret_cast<int*>(xp + (size_t)ncl * 16 * MB);
+  // X slice: one thread per (row, chunk): 32 halves in, 16 pairs out
+  for (int e = tid; e < MB * ncl; e += 256) {
+    const int m = e / ncl, c = e % ncl;
+    _Float16 xv[DQ_CHUNK];
+    if (m >= M) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const half2_t h = __builtin_bit_cast(half2_t, u[j]);
-        xs[(k8 + 2 * j) * MB + m] = (float)h.x;
-        xs[(k8 + 2 * j + 1) * MB + m] = (float)h.y;
+      for (int k = 0; k < DQ_CHUNK; ++k) xv[k] = (_Float16)0.0f;
+    } else if (x_order) {
+      const int32_t* xo = x_order + (c0 + c) * DQ_CHUNK;
+#pragma unroll
+      for (int k = 0; k < DQ_CHUNK; ++k) xv[k] = X[m * ldx + xo[k]];
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(X + m * ldx + (c0 + c) * DQ_CHUNK);
+#pragma unroll
+      for (int q = 0; q < DQ_CHUNK / 8; ++q) {
+        const uint4 v = src[q];
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const half2_t h = __builtin_bit_cast(half2_t, u[j]);
+          xv[8 * q + 2 * j] = h.x;
+          xv[8 * q + 2 * j + 1] = h.y;
+        }
       }
     }
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const half2_t h = {xv[pair_code<B>(p, 0)], xv[pair_code<B>(p, 1)]};
+      xp[(16 * c + p) * MB + m] = __builtin_bit_cast(uint32_t, h);
+    }
   }
-  for (int c = tid; c < (int)(c1 - c0); c += 256) {
+  for (int c = tid; c < ncl; c += 256) {
     const int32_t* gp = g_idx + (c0 + c) * DQ_CHUNK;
     const int g0 = gp[0];
     bool one = true;
@@ -112,7 +164,7 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
   // the next block, and the scale and zero of each of its single-group
   // chunks, are loaded before the current block is used, so a lane keeps
   // 2 * SMALL_DEPTH * (B + 2) loads in flight and the memory latency
-  // overlaps the dequantization.
+  // overlaps the arithmetic.
   struct Blk {
     uint32_t w[SMALL_DEPTH][B + 1];
     float s[SMALL_DEPTH];
@@ -133,6 +185,7 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
     }
   };
   Blk cur, nxt;
+  const uint32_t pm = pair_mask<B>(), pmagic = 0x64006400u;
   load_block(c0 + wave, cur);
   for (int64_t cb = c0 + wave; cb < c1; cb += 4 * SMALL_DEPTH) {
     load_block(cb + 4 * SMALL_DEPTH, nxt);
@@ -140,47 +193,50 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
     for (int d = 0; d < SMALL_DEPTH; ++d) {
       const int64_t c = cb + 4 * d;
       if (c >= c1) break;  // uniform
-      const int64_t kb = c * DQ_CHUNK;
-      const int xo = (int)(kb - c0 * DQ_CHUNK);
+      const uint32_t* xc = xp + (size_t)(c - c0) * 16 * MB;
       if (cur.g[d] >= 0) {
-        // one group for all 32 k: w = s q - s z, one FMA per weight after
-        // the code's conversion
-        const float sc = cur.s[d];
-        const float nsz = -sc * (float)cur.z[d];
+        const _Float16 zf = (_Float16)(1024 + cur.z[d]);
+        const half2_t zz = {zf, zf};
+        // two partial sums per row (even and odd pairs): shorter dependency chains
+        float cs[2][MB];
 #pragma unroll
-        for (int k4 = 0; k4 < DQ_CHUNK; k4 += 4) {
-          float xv[4 * MB];
+        for (int m = 0; m < MB; ++m) cs[0][m] = cs[1][m] = 0.0f;
+#pragma unroll
+        for (int p4 = 0; p4 < 16; p4 += 4) {
+          uint32_t xv[4 * MB];
 #pragma unroll
           for (int q = 0; q < MB; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(xs + (xo + k4) * MB + 4 * q);
+            const uint4 v = *reinterpret_cast<const uint4*>(xc + p4 * MB + 4 * q);
             xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
           }
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const float wv = fmaf((float)chunk_code<B>(cur.w[d], k4 + kk), sc, nsz);
+          for (int pp = 0; pp < 4; ++pp) {
+            const half2_t h =
+                __builtin_bit_cast(half2_t, pair_magic<B>(cur.w[d], p4 + pp, pm, pmagic)) - zz;
 #pragma unroll
-            for (int m = 0; m < MB; ++m) acc[m] = fmaf(xv[kk * MB + m], wv, acc[m]);
+            for (int m = 0; m < MB; ++m)
+              cs[pp & 1][m] = __builtin_amdgcn_fdot2(
+                  h, __builtin_bit_cast(half2_t, xv[pp * MB + m]), cs[pp & 1][m], false);
           }
         }
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[m] = fmaf(cur.s[d], cs[0][m] + cs[1][m], acc[m]);
       } else {
         // the chunk's groups (uniform), one scale and zero per k
+        const int64_t kb = c * DQ_CHUNK;
 #pragma unroll
-        for (int k4 = 0; k4 < DQ_CHUNK; k4 += 4) {
-          float xv[4 * MB];
+        for (int p = 0; p < 16; ++p) {
 #pragma unroll
-          for (int q = 0; q < MB; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(xs + (xo + k4) * MB + 4 * q);
-            xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
-          }
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int k = k4 + kk;
+          for (int hi = 0; hi < 2; ++hi) {
+            const int k = pair_code<B>(p, hi);
             const int64_t g = g_idx[kb + k];
             const float sc = scales[g * out + colc];
-            const float nsz = -sc * (float)zeros[g * out + colc];
-            const float wv = fmaf((float)chunk_code<B>(cur.w[d], k), sc, nsz);
+            const float wv = sc * (float)((int)chunk_code<B>(cur.w[d], k) - zeros[g * out + colc]);
 #pragma unroll
-            for (int m = 0; m < MB; ++m) acc[m] = fmaf(xv[kk * MB + m], wv, acc[m]);
+            for (int m = 0; m < MB; ++m) {
+              const half2_t xh = __builtin_bit_cast(half2_t, xc[p * MB + m]);
+              acc[m] = fmaf((float)(hi ? xh.y : xh.x), wv, acc[m]);
+            }
           }
         }
       }
@@ -189,7 +245,7 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
   }
   // the four waves' sums, in wave order
   __syncthreads();
-  float* red = xs;  // [4][MB][64]
+  float* red = reinterpret_cast<float*>(xp);  // [4][MB][64]
 #pragma unroll
   for (int m = 0; m < MB; ++m) red[(wave * MB + m) * 64 + lane] = acc[m];
   __syncthreads();
@@ -420,11 +476,11 @@ SmallPlan small_plan(int64_t M, int64_t in, int64_t out) {
   if (ns > nch / (8 * SMALL_DEPTH)) ns = nch / (8 * SMALL_DEPTH);
   if (ns < 1) ns = 1;
   int64_t cps = (nch + ns - 1) / ns;
-  const int64_t cps_max = SMALL_LDS_MAX / (((int64_t)p.mb * DQ_CHUNK + 1) * 4);
+  const int64_t cps_max = SMALL_LDS_MAX / (((int64_t)p.mb * 16 + 1) * 4);
   if (cps > cps_max) cps = cps_max;
   p.cps = cps;
   p.nsplit = (int)((nch + cps - 1) / cps);
-  const size_t xsb = ((size_t)p.mb * cps * DQ_CHUNK + cps) * 4, redb = (size_t)4 * p.mb * 64 * 4;
+  const size_t xsb = ((size_t)p.mb * cps * 16 + cps) * 4, redb = (size_t)4 * p.mb * 64 * 4;
   p.lds = xsb > redb ? xsb : redb;
   return p;
 }
