@@ -85,9 +85,12 @@ __host__ __device__ constexpr uint32_t pair_mask() {
 }
 
 // ---------------------------------------------------------------- small M --
-// Grid: (ceil(out / 64), nsplit).  Workgroup (bx, by) covers columns
-// [64 bx, 64 bx + 64) and chunks [by * cps, min((by + 1) * cps, in / 32)).
-// MB = token rows held per lane (>= M, a power of two up to 16).
+// Grid: (ceil(out / (64 CPL)), nsplit).  Workgroup (bx, by) covers columns
+// [64 CPL bx, 64 CPL (bx + 1)) and chunks [by * cps, min((by + 1) * cps, in / 32));
+// lane l of every wave owns the CPL adjacent columns from 64 CPL bx + CPL l
+// (CPL = 4: one 16-byte load per word row), and the four waves take
+// interleaved chunks of the range.  MB = token rows held per lane (>= M, a
+// power of two up to 16).
 // LDS: xp[pair][MB], the X slice as fp16 pairs in the chunks' pair order
 // (pair p of chunk c at 16 c + p), then cg[cps]: the group of each chunk of
 // the slice when all its 32 k share one, else -1.
@@ -98,20 +101,29 @@ __host__ __device__ constexpr uint32_t pair_mask() {
 // the X pair into an fp32 sum (products of fp16 values are exact in fp32);
 // the chunk's sum is scaled by s once.  Mixed-group chunks dequantize each
 // weight in fp32 as s (q - z).
-template <int B, int MB>
+template <int B, int CPL>
+__host__ __device__ constexpr int small_depth() {
+  // chunks per prefetched block: about 16 words per column group in flight
+  return CPL == 1 ? SMALL_DEPTH : B == 8 ? 1 : B == 2 ? 4 : 2;
+}
+
+template <int B, int MB, int CPL>
 __global__ void __launch_bounds__(256)
 dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
                 const uint32_t* __restrict__ qw, const float* __restrict__ scales,
                 const int32_t* __restrict__ zeros, const int32_t* __restrict__ g_idx,
                 const int32_t* __restrict__ x_order, int64_t out, int64_t cps,
                 float* __restrict__ part, void* __restrict__ Y, int y_f16, int64_t ldy) {
+  constexpr int D = small_depth<B, CPL>();
+  constexpr int COLS = 64 * CPL;
+  constexpr int NP = CPL == 1 ? 2 : 1;  // partial sums per (column, row)
   extern __shared__ __align__(16) uint32_t xp[];
   const int tid = threadIdx.x, lane = tid & 63;
   // uniform: the chunk index, g_idx reads and the group test stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t col = (int64_t)blockIdx.x * SMALL_COLS + lane;
-  const bool live = col < out;
-  const int64_t colc = live ? col : out - 1;  // loads stay in bounds, unconditional
+  const int64_t colb = (int64_t)blockIdx.x * COLS + (int64_t)lane * CPL;
+  // loads stay in bounds, unconditional (CPL = 4 implies out % 4 == 0)
+  const int64_t colc = colb + CPL <= out ? colb : out - CPL;
   const int64_t nch = in / DQ_CHUNK;
   const int64_t c0 = (int64_t)blockIdx.y * cps;
   const int64_t c1 = c0 + cps < nch ? c0 + cps : nch;
@@ -148,59 +160,87 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
       xp[(16 * c + p) * MB + m] = __builtin_bit_cast(uint32_t, h);
     }
   }
-  for (int c = tid; c < ncl; c += 256) {
-    const int32_t* gp = g_idx + (c0 + c) * DQ_CHUNK;
-    const int g0 = gp[0];
-    bool one = true;
-    for (int k = 1; k < DQ_CHUNK; ++k) one = one && gp[k] == g0;
-    cg[c] = one ? g0 : -1;
+  // chunk groups: a wave reads 64 consecutive g_idx (two chunks) per step
+  for (int c2 = 2 * wave; c2 < ncl; c2 += 8) {
+    const int k = 32 * c2 + lane;
+    const int g = k < 32 * ncl ? g_idx[c0 * DQ_CHUNK + k] : 0;
+    const int g0 = __shfl(g, lane & 32);
+    const uint64_t diff = __ballot(g != g0);
+    if ((lane & 31) == 0 && k < 32 * ncl)
+      cg[c2 + (lane >> 5)] = ((lane ? (diff >> 32) : (diff & 0xffffffffull)) == 0) ? g0 : -1;
   }
   __syncthreads();
 
-  float acc[MB];
+  float acc[CPL][MB];
 #pragma unroll
-  for (int m = 0; m < MB; ++m) acc[m] = 0.0f;
-  // Chunks c0 + wave, + 4, + 8, ... in blocks of SMALL_DEPTH.  The words of
-  // the next block, and the scale and zero of each of its single-group
-  // chunks, are loaded before the current block is used, so a lane keeps
-  // 2 * SMALL_DEPTH * (B + 2) loads in flight and the memory latency
-  // overlaps the arithmetic.
+  for (int j = 0; j < CPL; ++j)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[j][m] = 0.0f;
+  // Chunks c0 + wave, + 4, + 8, ... in blocks of D.  The words of the next
+  // block, and the scales and zeros of each of its single-group chunks, are
+  // loaded before the current block is used, so the memory latency overlaps
+  // the arithmetic.
   struct Blk {
-    uint32_t w[SMALL_DEPTH][B + 1];
-    float s[SMALL_DEPTH];
-    int32_t z[SMALL_DEPTH];
-    int g[SMALL_DEPTH];
+    uint32_t w[D][B][CPL];
+    float s[D][CPL];
+    int32_t z[D][CPL];
+    int g[D];
   };
   auto load_block = [&](int64_t cb, Blk& k) {
 #pragma unroll
-    for (int d = 0; d < SMALL_DEPTH; ++d) {
+    for (int d = 0; d < D; ++d) {
       const int64_t c = cb + 4 * d < c1 ? cb + 4 * d : c0;  // past the end: a valid dummy
 #pragma unroll
-      for (int i = 0; i < B; ++i) k.w[d][i] = qw[(c * B + i) * out + colc];
-      k.w[d][B] = 0u;
+      for (int i = 0; i < B; ++i) {
+        const uint32_t* src = qw + (c * B + i) * out + colc;
+        if constexpr (CPL == 4) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src);
+          k.w[d][i][0] = v.x; k.w[d][i][1] = v.y; k.w[d][i][2] = v.z; k.w[d][i][3] = v.w;
+        } else {
+          k.w[d][i][0] = *src;
+        }
+      }
       k.g[d] = __builtin_amdgcn_readfirstlane(cg[c - c0]);
       const int64_t gi = k.g[d] >= 0 ? k.g[d] : 0;
-      k.s[d] = scales[gi * out + colc];
-      k.z[d] = zeros[gi * out + colc];
+      if constexpr (CPL == 4) {
+        const float4 sv = *reinterpret_cast<const float4*>(scales + gi * out + colc);
+        const int4 zv = *reinterpret_cast<const int4*>(zeros + gi * out + colc);
+        k.s[d][0] = sv.x; k.s[d][1] = sv.y; k.s[d][2] = sv.z; k.s[d][3] = sv.w;
+        k.z[d][0] = zv.x; k.z[d][1] = zv.y; k.z[d][2] = zv.z; k.z[d][3] = zv.w;
+      } else {
+        k.s[d][0] = scales[gi * out + colc];
+        k.z[d][0] = zeros[gi * out + colc];
+      }
     }
   };
   Blk cur, nxt;
   const uint32_t pm = pair_mask<B>(), pmagic = 0x64006400u;
   load_block(c0 + wave, cur);
-  for (int64_t cb = c0 + wave; cb < c1; cb += 4 * SMALL_DEPTH) {
-    load_block(cb + 4 * SMALL_DEPTH, nxt);
+  for (int64_t cb = c0 + wave; cb < c1; cb += 4 * D) {
+    load_block(cb + 4 * D, nxt);
 #pragma unroll
-    for (int d = 0; d < SMALL_DEPTH; ++d) {
+    for (int d = 0; d < D; ++d) {
       const int64_t c = cb + 4 * d;
       if (c >= c1) break;  // uniform
       const uint32_t* xc = xp + (size_t)(c - c0) * 16 * MB;
       if (cur.g[d] >= 0) {
-        const _Float16 zf = (_Float16)(1024 + cur.z[d]);
-        const half2_t zz = {zf, zf};
-        // two partial sums per row (even and odd pairs): shorter dependency chains
-        float cs[2][MB];
+        half2_t zz[CPL];
+        uint32_t wj[CPL][B + 1];
 #pragma unroll
-        for (int m = 0; m < MB; ++m) cs[0][m] = cs[1][m] = 0.0f;
+        for (int j = 0; j < CPL; ++j) {
+          const _Float16 zf = (_Float16)(1024 + cur.z[d][j]);
+          zz[j] = (half2_t){zf, zf};
+#pragma unroll
+          for (int i = 0; i < B; ++i) wj[j][i] = cur.w[d][i][j];
+          wj[j][B] = 0u;
+        }
+        float cs[CPL][NP][MB];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+          for (int q = 0; q < NP; ++q)
+#pragma unroll
+            for (int m = 0; m < MB; ++m) cs[j][q][m] = 0.0f;
 #pragma unroll
         for (int p4 = 0; p4 < 16; p4 += 4) {
           uint32_t xv[4 * MB];
@@ -210,32 +250,46 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
             xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
           }
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            const half2_t h =
-                __builtin_bit_cast(half2_t, pair_magic<B>(cur.w[d], p4 + pp, pm, pmagic)) - zz;
+          for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-            for (int m = 0; m < MB; ++m)
-              cs[pp & 1][m] = __builtin_amdgcn_fdot2(
-                  h, __builtin_bit_cast(half2_t, xv[pp * MB + m]), cs[pp & 1][m], false);
-          }
+            for (int j = 0; j < CPL; ++j) {
+              const half2_t h =
+                  __builtin_bit_cast(half2_t, pair_magic<B>(wj[j], p4 + pp, pm, pmagic)) - zz[j];
+#pragma unroll
+              for (int m = 0; m < MB; ++m)
+                cs[j][pp % NP][m] = __builtin_amdgcn_fdot2(
+                    h, __builtin_bit_cast(half2_t, xv[pp * MB + m]), cs[j][pp % NP][m], false);
+            }
         }
 #pragma unroll
-        for (int m = 0; m < MB; ++m) acc[m] = fmaf(cur.s[d], cs[0][m] + cs[1][m], acc[m]);
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+          for (int m = 0; m < MB; ++m)
+            acc[j][m] = fmaf(cur.s[d][j], NP == 2 ? cs[j][0][m] + cs[j][NP - 1][m] : cs[j][0][m],
+                             acc[j][m]);
       } else {
         // the chunk's groups (uniform), one scale and zero per k
         const int64_t kb = c * DQ_CHUNK;
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
+        for (int j = 0; j < CPL; ++j) {
+          uint32_t wj[B + 1];
 #pragma unroll
-          for (int hi = 0; hi < 2; ++hi) {
-            const int k = pair_code<B>(p, hi);
-            const int64_t g = g_idx[kb + k];
-            const float sc = scales[g * out + colc];
-            const float wv = sc * (float)((int)chunk_code<B>(cur.w[d], k) - zeros[g * out + colc]);
+          for (int i = 0; i < B; ++i) wj[i] = cur.w[d][i][j];
+          wj[B] = 0u;
+#pragma unroll 4
+          for (int p = 0; p < 16; ++p) {
 #pragma unroll
-            for (int m = 0; m < MB; ++m) {
-              const half2_t xh = __builtin_bit_cast(half2_t, xc[p * MB + m]);
-              acc[m] = fmaf((float)(hi ? xh.y : xh.x), wv, acc[m]);
+            for (int hi = 0; hi < 2; ++hi) {
+              const int k = pair_code<B>(p, hi);
+              const int64_t g = g_idx[kb + k];
+              const float sc = scales[g * out + colc + j];
+              const float wv =
+                  sc * (float)((int)chunk_code<B>(wj, k) - zeros[g * out + colc + j]);
+#pragma unroll
+              for (int m = 0; m < MB; ++m) {
+                const half2_t xh = __builtin_bit_cast(half2_t, xc[p * MB + m]);
+                acc[j][m] = fmaf((float)(hi ? xh.y : xh.x), wv, acc[j][m]);
+              }
             }
           }
         }
@@ -245,16 +299,18 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
   }
   // the four waves' sums, in wave order
   __syncthreads();
-  float* red = reinterpret_cast<float*>(xp);  // [4][MB][64]
+  float* red = reinterpret_cast<float*>(xp);  // [4][MB][COLS]
 #pragma unroll
-  for (int m = 0; m < MB; ++m) red[(wave * MB + m) * 64 + lane] = acc[m];
+  for (int j = 0; j < CPL; ++j)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) red[(wave * MB + m) * COLS + lane * CPL + j] = acc[j][m];
   __syncthreads();
-  for (int e = tid; e < MB * 64; e += 256) {
-    const int m = e / 64, l = e % 64;
-    const int64_t cc = (int64_t)blockIdx.x * SMALL_COLS + l;
+  for (int e = tid; e < MB * COLS; e += 256) {
+    const int m = e / COLS, l = e % COLS;
+    const int64_t cc = (int64_t)blockIdx.x * COLS + l;
     if (m >= M || cc >= out) continue;
-    const float v = ((red[(0 * MB + m) * 64 + l] + red[(1 * MB + m) * 64 + l]) +
-                     red[(2 * MB + m) * 64 + l]) + red[(3 * MB + m) * 64 + l];
+    const float v = ((red[(0 * MB + m) * COLS + l] + red[(1 * MB + m) * COLS + l]) +
+                     red[(2 * MB + m) * COLS + l]) + red[(3 * MB + m) * COLS + l];
     if (gridDim.y > 1) {
       part[((int64_t)blockIdx.y * M + m) * out + cc] = v;
     } else if (y_f16) {
@@ -461,40 +517,48 @@ dq_repack_kernel(const uint32_t* __restrict__ qw, const int32_t* __restrict__ x_
 // ------------------------------------------------------------------- plan --
 struct SmallPlan {
   int mb;        // token rows per lane
+  int cpl;       // columns per lane
   int64_t cps;   // chunks per split
   int nsplit;
   size_t lds;    // bytes
 };
-SmallPlan small_plan(int64_t M, int64_t in, int64_t out) {
+// cpl 4 needs out % 4 == 0 and 16-byte aligned qweight, scales and zeros;
+// it is taken for up to 4 token rows.
+SmallPlan small_plan(int64_t M, int64_t in, int64_t out, int cpl) {
   SmallPlan p;
   p.mb = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+  p.cpl = cpl;
   const int64_t nch = in / DQ_CHUNK;
-  const int64_t ncolwg = (out + SMALL_COLS - 1) / SMALL_COLS;
-  // about 512 workgroups, each wave at least 2 * SMALL_DEPTH chunks, X slice
-  // and the final reduction within SMALL_LDS_MAX
+  const int64_t cols = 64 * (int64_t)cpl;
+  const int64_t ncolwg = (out + cols - 1) / cols;
+  // about 512 workgroups, each wave at least two blocks of chunks (cpl 1)
+  // or two chunks (cpl 4), X slice and the final reduction within LDS
   int64_t ns = (512 + ncolwg - 1) / ncolwg;
-  if (ns > nch / (8 * SMALL_DEPTH)) ns = nch / (8 * SMALL_DEPTH);
+  const int64_t ns_max = cpl == 1 ? nch / (8 * SMALL_DEPTH) : nch / 8;
+  if (ns > ns_max) ns = ns_max;
   if (ns < 1) ns = 1;
   int64_t cps = (nch + ns - 1) / ns;
   const int64_t cps_max = SMALL_LDS_MAX / (((int64_t)p.mb * 16 + 1) * 4);
   if (cps > cps_max) cps = cps_max;
   p.cps = cps;
   p.nsplit = (int)((nch + cps - 1) / cps);
-  const size_t xsb = ((size_t)p.mb * cps * 16 + cps) * 4, redb = (size_t)4 * p.mb * 64 * 4;
+  const size_t xsb = ((size_t)p.mb * cps * 16 + cps) * 4;
+  const size_t redb = (size_t)4 * p.mb * cols * 4;
   p.lds = xsb > redb ? xsb : redb;
   return p;
 }
+bool cpl4_ok(int64_t M, int64_t out) { return M <= 4 && out % 4 == 0; }
 
-template <int B, int MB>
+template <int B, int MB, int CPL>
 hipError_t launch_small_t(const SmallPlan& p, const _Float16* X, int64_t M, int64_t in,
                           int64_t ldx, const uint32_t* qw, const float* scales,
                           const int32_t* zeros, const int32_t* g_idx, const int32_t* xo,
                           int64_t out, float* part, void* Y, int y_f16, int64_t ldy,
                           hipStream_t s) {
-  auto k = dq_small_kernel<B, MB>;
+  auto k = dq_small_kernel<B, MB, CPL>;
   GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)p.lds));
-  dim3 grid((unsigned)((out + SMALL_COLS - 1) / SMALL_COLS), (unsigned)p.nsplit);
+  dim3 grid((unsigned)((out + 64 * CPL - 1) / (64 * CPL)), (unsigned)p.nsplit);
   hipLaunchKernelGGL(k, grid, dim3(256), p.lds, s, X, M, in, ldx, qw, scales, zeros, g_idx, xo,
                      out, p.cps, part, Y, y_f16, ldy);
   return hipGetLastError();
@@ -505,12 +569,19 @@ hipError_t launch_small_b(const SmallPlan& p, const _Float16* X, int64_t M, int6
                           const int32_t* zeros, const int32_t* g_idx, const int32_t* xo,
                           int64_t out, float* part, void* Y, int y_f16, int64_t ldy,
                           hipStream_t s) {
+  if (p.cpl == 4) {
+    switch (p.mb) {
+      case 1: return launch_small_t<B, 1, 4>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+      case 2: return launch_small_t<B, 2, 4>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+      default: return launch_small_t<B, 4, 4>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    }
+  }
   switch (p.mb) {
-    case 1: return launch_small_t<B, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
-    case 2: return launch_small_t<B, 2>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
-    case 4: return launch_small_t<B, 4>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
-    case 8: return launch_small_t<B, 8>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
-    default: return launch_small_t<B, 16>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    case 1: return launch_small_t<B, 1, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    case 2: return launch_small_t<B, 2, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    case 4: return launch_small_t<B, 4, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    case 8: return launch_small_t<B, 8, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    default: return launch_small_t<B, 16, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
   }
 }
 
@@ -518,8 +589,16 @@ hipError_t launch_small_b(const SmallPlan& p, const _Float16* X, int64_t M, int6
 
 size_t dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order) {
   if (M > DQ_SMALL_M_MAX) return has_order ? align_up((size_t)M * in * sizeof(_Float16)) : 0;
-  const SmallPlan p = small_plan(M, in, out);
-  return p.nsplit > 1 ? align_up((size_t)p.nsplit * M * out * sizeof(float)) : 0;
+  // either column layout may run (alignment decides): the larger need
+  size_t need = 0;
+  for (int cpl = 1; cpl <= (cpl4_ok(M, out) ? 4 : 1); cpl += 3) {
+    const SmallPlan p = small_plan(M, in, out, cpl);
+    if (p.nsplit > 1) {
+      const size_t b = align_up((size_t)p.nsplit * M * out * sizeof(float));
+      need = b > need ? b : need;
+    }
+  }
+  return need;
 }
 
 hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
@@ -531,7 +610,9 @@ hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
   const uint32_t* qw = reinterpret_cast<const uint32_t*>(qweight);
   const int32_t* xo = x_order;
   if (M <= DQ_SMALL_M_MAX) {
-    const SmallPlan p = small_plan(M, in, out);
+    const bool aligned = ((reinterpret_cast<uintptr_t>(qweight) | reinterpret_cast<uintptr_t>(scales) |
+                           reinterpret_cast<uintptr_t>(zeros)) & 15) == 0;
+    const SmallPlan p = small_plan(M, in, out, cpl4_ok(M, out) && aligned ? 4 : 1);
     float* part = static_cast<float*>(ws);
     hipError_t e;
     switch (bits) {

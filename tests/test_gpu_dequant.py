@@ -65,6 +65,11 @@ CASES = [
     ("m17_2b_f16", 17, 256, 130, 2, 32, True, torch.float16),
     ("m200_4b_desc", 200, 1024, 384, 4, 128, True, torch.float32),
     ("m512_3b_g64", 512, 2048, 1024, 3, 64, False, torch.float32),
+    # four columns per lane (out % 4 == 0, M <= 4), ragged last workgroup
+    ("m3_4b_g64_ragged", 3, 512, 260, 4, 64, False, torch.float16),
+    ("m2_8b_g32_desc", 2, 256, 132, 8, 32, True, torch.float32),
+    ("m1_3b_g128", 1, 1024, 516, 3, 128, False, torch.float32),
+    ("m4_2b_g128", 4, 2048, 1028, 2, 128, False, torch.float32),
 ]
 
 
@@ -100,6 +105,29 @@ def test_dequant_matmul_strided_x_and_y():
     torch.cuda.synchronize()
     assert torch.all(Ybig[:, out:] == 7.0)   # nothing written past ldy's row
     _check(X.cpu(), qw, scales, zeros, g_idx, bits, Y)
+
+
+def test_dequant_matmul_unaligned_scales():
+    """scales and zeros 4 bytes off a 16-byte boundary: the one-column-per-lane
+    layout runs (same result as from aligned copies)."""
+    _banner("dequant_matmul unaligned scales / zeros")
+    M, inp, out, bits = 2, 256, 64, 4
+    qw, scales, zeros, g_idx = _layer(out, inp, bits, 64, False, seed=12)
+    G = scales.shape[0]
+    sbuf = torch.zeros(G * out + 1, dtype=torch.float32, device=DEV)
+    zbuf = torch.zeros(G * out + 1, dtype=torch.int32, device=DEV)
+    sc_u = sbuf[1:].view(G, out)
+    z_u = zbuf[1:].view(G, out)
+    sc_u.copy_(torch.from_numpy(scales))
+    z_u.copy_(torch.from_numpy(zeros))
+    assert sc_u.data_ptr() % 16 != 0 and z_u.data_ptr() % 16 != 0
+    X = torch.randn((M, inp), generator=torch.Generator().manual_seed(3)).to(torch.float16)
+    qw_d, g_d = torch.from_numpy(qw).to(DEV), torch.from_numpy(g_idx).to(DEV)
+    Y = P.dequant_matmul(X.to(DEV), qw_d, sc_u, z_u, g_d, bits)
+    Ya = P.dequant_matmul(X.to(DEV), qw_d, sc_u.clone(), z_u.clone(), g_d, bits)
+    torch.cuda.synchronize()
+    _check(X, qw, scales, zeros, g_idx, bits, Y)
+    _check(X, qw, scales, zeros, g_idx, bits, Ya)
 
 
 @pytest.mark.parametrize("M", [1, 64])
