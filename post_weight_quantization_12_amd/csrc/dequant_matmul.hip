@@ -129,6 +129,53 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
   const int64_t c1 = c0 + cps < nch ? c0 + cps : nch;
   const int ncl = (int)(c1 - c0);
   int* cg = reinterpret_cast<int*>(xp + (size_t)ncl * 16 * MB);
+  // Chunks c0 + wave, + 4, + 8, ... in blocks of D.  The words of the next
+  // block, and the scales and zeros of each of its single-group chunks, are
+  // loaded before the current block is used, so the memory latency overlaps
+  // the arithmetic.
+  struct Blk {
+    uint32_t w[D][B][CPL];
+    float s[D][CPL];
+    int32_t z[D][CPL];
+    int g[D];
+  };
+  auto load_words = [&](int64_t cb, Blk& k) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int64_t c = cb + 4 * d < c1 ? cb + 4 * d : c0;  // past the end: a valid dummy, unused
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const uint32_t* src = qw + (c * B + i) * out + colc;
+        if constexpr (CPL == 4) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src);
+          k.w[d][i][0] = v.x; k.w[d][i][1] = v.y; k.w[d][i][2] = v.z; k.w[d][i][3] = v.w;
+        } else {
+          k.w[d][i][0] = *src;
+        }
+      }
+    }
+  };
+  auto load_groups = [&](int64_t cb, Blk& k) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int64_t c = cb + 4 * d < c1 ? cb + 4 * d : c0;
+      k.g[d] = __builtin_amdgcn_readfirstlane(cg[c - c0]);
+      const int64_t gi = k.g[d] >= 0 ? k.g[d] : 0;
+      if constexpr (CPL == 4) {
+        const float4 sv = *reinterpret_cast<const float4*>(scales + gi * out + colc);
+        const int4 zv = *reinterpret_cast<const int4*>(zeros + gi * out + colc);
+        k.s[d][0] = sv.x; k.s[d][1] = sv.y; k.s[d][2] = sv.z; k.s[d][3] = sv.w;
+        k.z[d][0] = zv.x; k.z[d][1] = zv.y; k.z[d][2] = zv.z; k.z[d][3] = zv.w;
+      } else {
+        k.s[d][0] = scales[gi * out + colc];
+        k.z[d][0] = zeros[gi * out + colc];
+      }
+    }
+  };
+  Blk cur, nxt;
+  // the first block's words are independent of the staging below: in flight
+  // while it runs
+  load_words(c0 + wave, cur);
   // X slice: one thread per (row, chunk): 32 halves in, 16 pairs out
   for (int e = tid; e < MB * ncl; e += 256) {
     const int m = e / ncl, c = e % ncl;
@@ -176,48 +223,9 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
   for (int j = 0; j < CPL; ++j)
 #pragma unroll
     for (int m = 0; m < MB; ++m) acc[j][m] = 0.0f;
-  // Chunks c0 + wave, + 4, + 8, ... in blocks of D.  The words of the next
-  // block, and the scales and zeros of each of its single-group chunks, are
-  // loaded before the current block is used, so the memory latency overlaps
-  // the arithmetic.
-  struct Blk {
-    uint32_t w[D][B][CPL];
-    float s[D][CPL];
-    int32_t z[D][CPL];
-    int g[D];
-  };
-  auto load_block = [&](int64_t cb, Blk& k) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int64_t c = cb + 4 * d < c1 ? cb + 4 * d : c0;  // past the end: a valid dummy
-#pragma unroll
-      for (int i = 0; i < B; ++i) {
-        const uint32_t* src = qw + (c * B + i) * out + colc;
-        if constexpr (CPL == 4) {
-          const uint4 v = *reinterpret_cast<const uint4*>(src);
-          k.w[d][i][0] = v.x; k.w[d][i][1] = v.y; k.w[d][i][2] = v.z; k.w[d][i][3] = v.w;
-        } else {
-          k.w[d][i][0] = *src;
-        }
-      }
-      k.g[d] = __builtin_amdgcn_readfirstlane(cg[c - c0]);
-      const int64_t gi = k.g[d] >= 0 ? k.g[d] : 0;
-      if constexpr (CPL == 4) {
-        const float4 sv = *reinterpret_cast<const float4*>(scales + gi * out + colc);
-        const int4 zv = *reinterpret_cast<const int4*>(zeros + gi * out + colc);
-        k.s[d][0] = sv.x; k.s[d][1] = sv.y; k.s[d][2] = sv.z; k.s[d][3] = sv.w;
-        k.z[d][0] = zv.x; k.z[d][1] = zv.y; k.z[d][2] = zv.z; k.z[d][3] = zv.w;
-      } else {
-        k.s[d][0] = scales[gi * out + colc];
-        k.z[d][0] = zeros[gi * out + colc];
-      }
-    }
-  };
-  Blk cur, nxt;
   const uint32_t pm = pair_mask<B>(), pmagic = 0x64006400u;
-  load_block(c0 + wave, cur);
-  for (int64_t cb = c0 + wave; cb < c1; cb += 4 * D) {
-    load_block(cb + 4 * D, nxt);
+  load_groups(c0 + wave, cur);
+  auto process = [&](int64_t cb, const Blk& cur) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int64_t c = cb + 4 * d;
@@ -295,7 +303,20 @@ dq_small_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t l
         }
       }
     }
-    cur = nxt;
+  };
+  // two buffers in turn; a block past the end is neither loaded nor used
+  for (int64_t cb = c0 + wave; cb < c1; cb += 8 * D) {
+    if (cb + 4 * D < c1) {
+      load_words(cb + 4 * D, nxt);
+      load_groups(cb + 4 * D, nxt);
+    }
+    process(cb, cur);
+    if (cb + 4 * D >= c1) break;
+    if (cb + 8 * D < c1) {
+      load_words(cb + 8 * D, cur);
+      load_groups(cb + 8 * D, cur);
+    }
+    process(cb + 4 * D, nxt);
   }
   // the four waves' sums, in wave order
   __syncthreads();
@@ -327,9 +348,17 @@ dq_reduce_kernel(const float* __restrict__ part, int nsplit, int64_t M, int64_t 
                  void* __restrict__ Y, int y_f16, int64_t ldy) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= M * out) return;
-  const int64_t m = e / out, cc = e % out;
+  const int64_t m = e / out, cc = e % out, stride = M * out;
   float v = part[e];
-  for (int s = 1; s < nsplit; ++s) v += part[(int64_t)s * M * out + e];
+  int s = 1;
+  for (; s + 8 <= nsplit; s += 8) {  // eight loads in flight, added in split order
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = part[(int64_t)(s + j) * stride + e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += t[j];
+  }
+  for (; s < nsplit; ++s) v += part[(int64_t)s * stride + e];
   if (y_f16)
     static_cast<_Float16*>(Y)[m * ldy + cc] = (_Float16)v;
   else
