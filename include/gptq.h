@@ -193,10 +193,12 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in,
                         void* stream);
 
 /* Workspace (bytes) gptq_dequant_matmul needs for M token rows, in inputs and
- * out outputs, with (has_order != 0) or without an x_order: the partial sums
- * of the split input range when M <= 16 (e.g. 8 x 1 x 4096 fp32 for one token
- * of a 4096 x 4096 layer); for M > 16 the gathered copy of X (M x in fp16)
- * when has_order, else 0. */
+ * out outputs, with (has_order != 0) or without an x_order: the fp32 partial
+ * sums when the input range is split over several workgroups (always for
+ * M <= 16, e.g. 16 x 1 x 4096 for one token of a 4096 x 4096 layer; for
+ * M > 16 when the output tiles alone would not fill the GPU), plus, for
+ * M > 16 with an x_order, the gathered copy of X (M x in fp16).  0 when
+ * neither applies (e.g. M = 2048 on a 4096 x 4096 layer). */
 size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order);
 
 /*

@@ -29,6 +29,8 @@
 //     times the fp16 scale (one rounding).
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace gptq {
 namespace {
 
@@ -369,15 +371,23 @@ dq_reduce_kernel(const float* __restrict__ part, int nsplit, int64_t M, int64_t 
 constexpr int TB = 128;          // tile rows (tokens) and columns (outputs)
 constexpr int XP = DQ_CHUNK + 8; // LDS pitch in halves (80 bytes, 16-byte aligned rows)
 
-// Grid: (ceil(out / 128), ceil(M / 128)); 4 waves, each a 64 x 64 block.
+// Grid: (ceil(out / 128), ceil(M / 128), nsplit); 4 waves, each a 64 x 64
+// block.  Split z covers chunks [z cps, min((z + 1) cps, in / 32)); with
+// more than one split the fp32 sums go to part[z][M][out] for
+// dq_reduce_kernel.
+// Two LDS buffers: while the matrix cores work on chunk c, the X tile and
+// the weight words of chunk c + 1 (and the scale and zero of its group) are
+// in flight; they are dequantized into the other buffer afterwards, and one
+// barrier per chunk separates the two.  g_idx is read two chunks ahead.
 template <int B>
 __global__ void __launch_bounds__(256)
 dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
                const uint32_t* __restrict__ qw, const float* __restrict__ scales,
                const int32_t* __restrict__ zeros, const int32_t* __restrict__ g_idx,
-               int64_t out, void* __restrict__ Y, int y_f16, int64_t ldy) {
-  __shared__ __align__(16) _Float16 Xs[TB * XP];
-  __shared__ __align__(16) _Float16 Ws[TB * XP];
+               int64_t out, int64_t cps, float* __restrict__ part, void* __restrict__ Y,
+               int y_f16, int64_t ldy) {
+  __shared__ __align__(16) _Float16 Xs[2][TB * XP];
+  __shared__ __align__(16) _Float16 Ws[2][TB * XP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -387,6 +397,9 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
   const int wh = __builtin_amdgcn_readfirstlane(tid / TB);  // uniform within a wave
   const int64_t wcol = n0 + wc;
   const int64_t wcolc = wcol < out ? wcol : out - 1;  // in-bounds loads; columns >= out never stored
+  const int64_t nch_all = in / DQ_CHUNK;
+  const int64_t cbeg = (int64_t)blockIdx.z * cps;
+  const int64_t nch = cbeg + cps < nch_all ? cbeg + cps : nch_all;  // end of this split
 
   f32x16_t acc[2][2];
 #pragma unroll
@@ -396,79 +409,113 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  const int64_t nch = in / DQ_CHUNK;
-  for (int64_t c = 0; c < nch; ++c) {
+  uint4 xr[2];        // X tile part: rows tid / 4 and tid / 4 + 64, k-octet tid % 4
+  uint32_t wr[B + 1]; // the weight words of column wc
+  int gA[16], gB[16]; // groups of the staged chunk's 16 k, and of the chunk after
+  float sA;           // scale and zero of gA[0]
+  int32_t zA;
+  bool oneA;
+  auto load_g = [&](int64_t c, int* g) {
+    const int64_t cc = c < nch ? c : nch - 1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) g[k] = g_idx[cc * DQ_CHUNK + 16 * wh + k];
+  };
+  auto fetch = [&](int64_t c) {
     const int64_t kb = c * DQ_CHUNK;
-    // X tile: rows t / 4 and t / 4 + 64, k-octet t % 4
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = tid / 4 + 64 * i, o = 8 * (tid % 4);
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (m0 + r < M) v = *reinterpret_cast<const uint4*>(X + (m0 + r) * ldx + kb + o);
-      *reinterpret_cast<uint4*>(Xs + r * XP + o) = v;
+      xr[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (m0 + r < M) xr[i] = *reinterpret_cast<const uint4*>(X + (m0 + r) * ldx + kb + o);
     }
-    // weight tile: 16 codes of column wc
-    {
-      uint32_t w[B + 1];
 #pragma unroll
-      for (int i = 0; i < B; ++i) w[i] = qw[(c * B + i) * out + wcolc];
-      w[B] = 0u;
-      // groups of the 16 k (uniform within the wave)
-      int gk[16];
-      bool one = true;
+    for (int i = 0; i < B; ++i) wr[i] = qw[(c * B + i) * out + wcolc];
+    wr[B] = 0u;
+    bool one = true;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        gk[k] = g_idx[kb + 16 * wh + k];
-        one = one && gk[k] == gk[0];
-      }
-      half2_t sh[8], zz[8];
-      if (one) {
-        const float s = scales[gk[0] * out + wcolc], z = (float)zeros[gk[0] * out + wcolc];
-        const half2_t s2 = {(_Float16)s, (_Float16)s};
-        const half2_t z2 = {(_Float16)(1024.0f + z), (_Float16)(1024.0f + z)};
+    for (int k = 1; k < 16; ++k) one = one && gA[k] == gA[0];
+    oneA = one;
+    sA = scales[(int64_t)gA[0] * out + wcolc];
+    zA = zeros[(int64_t)gA[0] * out + wcolc];
+  };
+  auto stage = [&](int buf) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) { sh[p] = s2; zz[p] = z2; }
-      } else {
+    for (int i = 0; i < 2; ++i) {
+      const int r = tid / 4 + 64 * i, o = 8 * (tid % 4);
+      *reinterpret_cast<uint4*>(&Xs[buf][r * XP + o]) = xr[i];
+    }
+    half2_t sh[8], zz[8];
+    if (oneA) {
+      const half2_t s2 = {(_Float16)sA, (_Float16)sA};
+      const half2_t z2 = {(_Float16)(1024.0f + (float)zA), (_Float16)(1024.0f + (float)zA)};
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const float s0 = scales[gk[2 * p] * out + wcolc], s1 = scales[gk[2 * p + 1] * out + wcolc];
-          const float z0 = (float)zeros[gk[2 * p] * out + wcolc];
-          const float z1 = (float)zeros[gk[2 * p + 1] * out + wcolc];
-          sh[p] = (half2_t){(_Float16)s0, (_Float16)s1};
-          zz[p] = (half2_t){(_Float16)(1024.0f + z0), (_Float16)(1024.0f + z1)};
-        }
-      }
-      uint32_t packed[8];
+      for (int p = 0; p < 8; ++p) { sh[p] = s2; zz[p] = z2; }
+    } else {
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        const int k = 16 * wh + 2 * p;
-        const uint32_t q2 =
-            chunk_code<B>(w, k) | (chunk_code<B>(w, k + 1) << 16) | 0x64006400u;
+        const float s0 = scales[(int64_t)gA[2 * p] * out + wcolc];
+        const float s1 = scales[(int64_t)gA[2 * p + 1] * out + wcolc];
+        const float z0 = (float)zeros[(int64_t)gA[2 * p] * out + wcolc];
+        const float z1 = (float)zeros[(int64_t)gA[2 * p + 1] * out + wcolc];
+        sh[p] = (half2_t){(_Float16)s0, (_Float16)s1};
+        zz[p] = (half2_t){(_Float16)(1024.0f + z0), (_Float16)(1024.0f + z1)};
+      }
+    }
+    uint32_t packed[8];
+    // the code offset 16 wh as a constant: wr is indexed statically (registers)
+    auto deq = [&](auto half) {
+      constexpr int k0 = 16 * decltype(half)::value;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const uint32_t q2 = chunk_code<B>(wr, k0 + 2 * p) |
+                            (chunk_code<B>(wr, k0 + 2 * p + 1) << 16) | 0x64006400u;
         const half2_t d = (__builtin_bit_cast(half2_t, q2) - zz[p]) * sh[p];
         packed[p] = __builtin_bit_cast(uint32_t, d);
       }
-      *reinterpret_cast<uint4*>(Ws + wc * XP + 16 * wh) =
-          make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      *reinterpret_cast<uint4*>(Ws + wc * XP + 16 * wh + 8) =
-          make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    };
+    if (wh == 0)
+      deq(std::integral_constant<int, 0>());
+    else
+      deq(std::integral_constant<int, 1>());
+    *reinterpret_cast<uint4*>(&Ws[buf][wc * XP + 16 * wh]) =
+        make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    *reinterpret_cast<uint4*>(&Ws[buf][wc * XP + 16 * wh + 8]) =
+        make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  };
+
+  load_g(cbeg, gA);
+  load_g(cbeg + 1, gB);
+  fetch(cbeg);
+  stage(0);
+  __syncthreads();
+  for (int64_t c = cbeg; c < nch; ++c) {
+    const int buf = (int)((c - cbeg) & 1);
+    const bool more = c + 1 < nch;  // uniform
+    if (more) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) gA[k] = gB[k];
+      fetch(c + 1);
+      load_g(c + 2, gB);
     }
-    __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < DQ_CHUNK; kk += 16) {
       const int ko = kk + 8 * (lane >> 5);
       half8_t af[2], bf[2];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
-        af[a] = *reinterpret_cast<const half8_t*>(Xs + (wm * 64 + a * 32 + (lane & 31)) * XP + ko);
+        af[a] = *reinterpret_cast<const half8_t*>(
+            &Xs[buf][(wm * 64 + a * 32 + (lane & 31)) * XP + ko]);
 #pragma unroll
       for (int b = 0; b < 2; ++b)
-        bf[b] = *reinterpret_cast<const half8_t*>(Ws + (wn * 64 + b * 32 + (lane & 31)) * XP + ko);
+        bf[b] = *reinterpret_cast<const half8_t*>(
+            &Ws[buf][(wn * 64 + b * 32 + (lane & 31)) * XP + ko]);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
+    if (more) stage(buf ^ 1);
     __syncthreads();
   }
   // 32 x 32 block layout: element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4,
@@ -482,12 +529,25 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
         const int64_t r = m0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         const int64_t cc = n0 + wn * 64 + b * 32 + (lane & 31);
         if (r < M && cc < out) {
-          if (y_f16)
+          if (gridDim.z > 1)
+            part[((int64_t)blockIdx.z * M + r) * out + cc] = acc[a][b][v];
+          else if (y_f16)
             static_cast<_Float16*>(Y)[r * ldy + cc] = (_Float16)acc[a][b][v];
           else
             static_cast<float*>(Y)[r * ldy + cc] = acc[a][b][v];
         }
       }
+}
+
+// Splits of the input range for the tile kernel: about 512 workgroups, each
+// split at least 8 chunks.
+int64_t mfma_chunks_per_split(int64_t M, int64_t in, int64_t out) {
+  const int64_t nch = in / DQ_CHUNK;
+  const int64_t tiles = ((out + TB - 1) / TB) * ((M + TB - 1) / TB);
+  int64_t ns = (512 + tiles - 1) / tiles;
+  if (ns > nch / 8) ns = nch / 8;
+  if (ns < 1) ns = 1;
+  return (nch + ns - 1) / ns;
 }
 
 // ------------------------------------------------------------ group order --
@@ -617,7 +677,13 @@ hipError_t launch_small_b(const SmallPlan& p, const _Float16* X, int64_t M, int6
 }  // namespace
 
 size_t dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order) {
-  if (M > DQ_SMALL_M_MAX) return has_order ? align_up((size_t)M * in * sizeof(_Float16)) : 0;
+  if (M > DQ_SMALL_M_MAX) {
+    // [gathered X when has_order][split partials when more than one split]
+    const int64_t cps = mfma_chunks_per_split(M, in, out);
+    const int64_t ns = (in / DQ_CHUNK + cps - 1) / cps;
+    return (has_order ? align_up((size_t)M * in * sizeof(_Float16)) : 0) +
+           (ns > 1 ? align_up((size_t)ns * M * out * sizeof(float)) : 0);
+  }
   // either column layout may run (alignment decides): the larger need
   size_t need = 0;
   for (int cpl = 1; cpl <= (cpl4_ok(M, out) ? 4 : 1); cpl += 3) {
@@ -659,24 +725,36 @@ hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
     }
     return hipSuccess;
   }
+  if (ws_bytes < dequant_matmul_workspace_bytes(M, in, out, xo ? 1 : 0)) return hipErrorInvalidValue;
+  char* wsp = static_cast<char*>(ws);
   if (xo) {
     // X in packed order into the workspace, then the plain product on it
-    if (ws_bytes < (size_t)M * in * sizeof(_Float16)) return hipErrorInvalidValue;
-    _Float16* xp = static_cast<_Float16*>(ws);
+    _Float16* xp = reinterpret_cast<_Float16*>(wsp);
     hipLaunchKernelGGL(dq_gather_x_kernel, dim3((unsigned)((in + 255) / 256), (unsigned)(M < 1024 ? M : 1024)),
                        dim3(256), 0, s, x, M, in, ldx, xo, xp);
     GPTQ_HIP_TRY(hipGetLastError());
     x = xp;
     ldx = in;
+    wsp += align_up((size_t)M * in * sizeof(_Float16));
   }
-  dim3 grid((unsigned)((out + TB - 1) / TB), (unsigned)((M + TB - 1) / TB));
+  const int64_t cps = mfma_chunks_per_split(M, in, out);
+  const int64_t ns = (in / DQ_CHUNK + cps - 1) / cps;
+  float* part = ns > 1 ? reinterpret_cast<float*>(wsp) : nullptr;
+  dim3 grid((unsigned)((out + TB - 1) / TB), (unsigned)((M + TB - 1) / TB), (unsigned)ns);
   switch (bits) {
-    case 2: hipLaunchKernelGGL(dq_mfma_kernel<2>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
-    case 3: hipLaunchKernelGGL(dq_mfma_kernel<3>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
-    case 8: hipLaunchKernelGGL(dq_mfma_kernel<8>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
-    default: hipLaunchKernelGGL(dq_mfma_kernel<4>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, Y, y_f16, ldy); break;
+    case 2: hipLaunchKernelGGL(dq_mfma_kernel<2>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, cps, part, Y, y_f16, ldy); break;
+    case 3: hipLaunchKernelGGL(dq_mfma_kernel<3>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, cps, part, Y, y_f16, ldy); break;
+    case 8: hipLaunchKernelGGL(dq_mfma_kernel<8>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, cps, part, Y, y_f16, ldy); break;
+    default: hipLaunchKernelGGL(dq_mfma_kernel<4>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, cps, part, Y, y_f16, ldy); break;
   }
-  return hipGetLastError();
+  GPTQ_HIP_TRY(hipGetLastError());
+  if (ns > 1) {
+    const int64_t total = M * out;
+    hipLaunchKernelGGL(dq_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       part, (int)ns, M, out, Y, y_f16, ldy);
+    GPTQ_HIP_TRY(hipGetLastError());
+  }
+  return hipSuccess;
 }
 
 size_t dequant_group_order_workspace_bytes(int64_t in) {
