@@ -102,6 +102,105 @@ PROFILE_COMMANDS = {
 }
 
 
+DEQUANT_PROFILE_COMMANDS = {
+    "trace": ("rocprofv3 --kernel-trace --stats -T -d {d}/trace -o t --output-format csv -- "
+              "python -u bench.py --config {c} --dequant-tokens {m} --steps 2 --warmup 1 "
+              "--no-cpu-baseline"),
+    "FETCH_SIZE": ("rocprofv3 --pmc FETCH_SIZE -T -d {d}/FETCH_SIZE -o p --output-format csv -- "
+                   "python -u bench.py --config {c} --dequant-tokens {m} --steps 1 --warmup 1 "
+                   "--no-cpu-baseline --copy-probe"),
+    "WRITE_SIZE": ("rocprofv3 --pmc WRITE_SIZE -T -d {d}/WRITE_SIZE -o p --output-format csv -- "
+                   "python -u bench.py --config {c} --dequant-tokens {m} --steps 1 --warmup 1 "
+                   "--no-cpu-baseline --copy-probe"),
+}
+DQ_KERNELS = ("dq_small_kernel", "dq_reduce_kernel", "dq_mfma_kernel", "dq_gather_x_kernel")
+
+
+def _dq_kernel(name: str) -> bool:
+    return any(k in name for k in DQ_KERNELS)
+
+
+def load_dequant_traffic(cfg_name: str, M: int):
+    """HBM bytes per gptq_dequant_matmul call from the committed rocprofv3
+    summary, or None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"dequant_{cfg_name}_m{M}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("source_sha") != kernel_source_sha("dequant_matmul.hip"):
+        return None
+    return float(d["hbm_bytes_per_call"])
+
+
+def summarize_dequant(cfg_name: str, M: int, d: str):
+    """profiles/dequant_<config>_m<M>_kernel_stats.md and _traffic.json from
+    the DEQUANT_PROFILE_COMMANDS output in d."""
+    import csv
+    import workloads
+    cfg = workloads.get(cfg_name)
+    tag = f"dequant_{cfg_name}_m{M}"
+    shape = (f"X {M} x {cfg.inp} fp16, packed W {cfg.out}x{cfg.inp} {cfg.bits}-bit "
+             f"g{cfg.group_size}" + (", group-ordered (desc_act layer)" if cfg.desc_act else ""))
+    trace = list(csv.DictReader(open(os.path.join(d, "trace", "t_kernel_trace.csv"))))
+    stats = {}
+    for r in trace:
+        name = r["Kernel_Name"]
+        if not _dq_kernel(name):
+            continue
+        name = next(k for k in DQ_KERNELS if k in name)
+        stats.setdefault(name, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = [f"# rocprofv3 kernel statistics: gptq_dequant_matmul, {cfg_name} ({shape})", "",
+             "Command (run from the repository root on one MI355X):", "",
+             "    " + DEQUANT_PROFILE_COMMANDS["trace"].format(d=d, c=cfg_name, m=M), "",
+             "All calls of the run (50 warm-up and 2 x 50 timed calls, back to back).", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for name, ds in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {name} | {len(ds)} | {sum(ds) / len(ds) / 1e3:.2f} | "
+                     f"{min(ds) / 1e3:.2f} | {max(ds) / 1e3:.2f} |")
+    with open(os.path.join(ROOT, "profiles", f"{tag}_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    GiB = 1 << 30
+    per = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = list(csv.DictReader(open(os.path.join(d, ctr, "p_counter_collection.csv"))))
+        # per call: the main kernel's dispatches count the calls
+        calls = sum(1 for r in rows if ("dq_small_kernel" in r["Kernel_Name"]
+                                        or "dq_mfma_kernel" in r["Kernel_Name"]))
+        tot = sum(float(r["Counter_Value"]) for r in rows if _dq_kernel(r["Kernel_Name"]))
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        per[ctr] = (tot / calls, copy)
+    ff = (GiB / 1024) / per["FETCH_SIZE"][1]
+    wf = (GiB / 1024) / per["WRITE_SIZE"][1]
+    hbm = per["FETCH_SIZE"][0] * 1024 * ff + per["WRITE_SIZE"][0] * 1024 * wf
+    gs = cfg.inp if cfg.group_size == -1 else cfg.group_size
+    G = -(-cfg.inp // gs)
+    alg = (cfg.inp * cfg.bits // 8 * cfg.out + 8 * G * cfg.out + 4 * cfg.inp + 2 * M * cfg.inp
+           + 2 * M * cfg.out + (4 * cfg.inp if cfg.desc_act else 0))
+    out = {
+        "source": "post_weight_quantization_12_amd/csrc/dequant_matmul.hip",
+        "source_sha": kernel_source_sha("dequant_matmul.hip"),
+        "workload": f"{cfg_name}: {shape}",
+        "commands": [DEQUANT_PROFILE_COMMANDS[c].format(d=d, c=cfg_name, m=M)
+                     for c in ("FETCH_SIZE", "WRITE_SIZE")],
+        "counted": "all dequant kernels of the run, divided by the number of calls",
+        "fetch_kib_per_call": round(per["FETCH_SIZE"][0], 1),
+        "write_kib_per_call": round(per["WRITE_SIZE"][0], 1),
+        "copy_probe": {"kernel": "__amd_rocclr_copyBuffer (torch device copy of 1 GiB)",
+                       "fetch_kib": round(per["FETCH_SIZE"][1], 1),
+                       "write_kib": round(per["WRITE_SIZE"][1], 1)},
+        "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+        "hbm_bytes_per_call": int(hbm),
+        "algorithmic_bytes_per_call": alg,
+        "traffic_over_algorithmic": round(hbm / alg, 2),
+    }
+    with open(os.path.join(ROOT, "profiles", f"{tag}_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def summarize(cfg_name: str, d: str):
     """Write the profiles/ summaries from rocprofv3 CSV output in d (the
     PROFILE_COMMANDS run with the default call size).  FETCH_SIZE and
@@ -314,6 +413,13 @@ def dequant_main(args):
         P.dequant_matmul(X, words, scales, zeros, g_idx, cfg.bits, x_order=x_order, Y=Y,
                          workspace=ws if wsb else None, stream=stream)
 
+    if args.copy_probe:
+        src = torch.empty((1 << 30) // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     reps = 50
     for _ in range(args.warmup * reps):
         call()
@@ -357,7 +463,9 @@ def dequant_main(args):
         kernel = ("dq_small_kernel" + (" + dq_reduce_kernel" if wsb else ""))
     else:
         achieved, peak, unit, bound = flops / (call_ms * 1e-3) / 1e12, PEAK_FP16_TFLOPS, "TFLOP/s", "mfma"
-        kernel = ("dq_gather_x_kernel + " if x_order is not None else "") + "dq_mfma_kernel"
+        kernel = (("dq_gather_x_kernel + " if x_order is not None else "") + "dq_mfma_kernel"
+                  + (" + dq_reduce_kernel" if P.dequant_matmul_workspace_bytes(M, n, out) > 0
+                     else ""))
     result = {
         "metric": "dequantize-on-the-fly matmul Y = X W^T from the packed layer, TFLOP/s",
         "value": flops / (call_ms * 1e-3) / 1e12,
@@ -386,7 +494,7 @@ def dequant_main(args):
         "speedup_vs_dense_fp16": dense_ms / call_ms,
         "roofline": {
             "kernel": f"{kernel} = one gptq_dequant_matmul call",
-            "kernel_launches_per_call": 2 if (wsb and (small or x_order is not None)) else 1,
+            "kernel_launches_per_call": kernel.count("+") + 1,
             "bound": bound,
             "achieved": achieved,
             "peak": peak,
@@ -395,7 +503,7 @@ def dequant_main(args):
             "call_ms": call_ms,
             "bytes_per_call": alg_bytes,
             "flops_per_call": flops,
-            "traffic": None,
+            "traffic": load_dequant_traffic(cfg.name, M),
         },
     }
     if not args.no_cpu_baseline:
@@ -430,7 +538,10 @@ def main():
     args = ap.parse_args()
 
     if args.summarize:
-        summarize(args.config, args.summarize)
+        if args.dequant_tokens is not None:
+            summarize_dequant(args.config, args.dequant_tokens, args.summarize)
+        else:
+            summarize(args.config, args.summarize)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this GPTQ build runs on one GPU only (no sharding, no collectives); "
