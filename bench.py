@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (vector and matrix)
 METRIC = "GPTQ weights quantized/sec per layer (4-bit g128) + Hessian TFLOP/s, 1 GPU"
 
 
@@ -242,6 +243,8 @@ def summarize(cfg_name: str, d: str):
     for name, ds in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| {name} | {len(ds)} | {sum(ds) / 1e6:.3f} | {sum(ds) / len(ds) / 1e3:.2f} | "
                      f"{min(ds) / 1e3:.2f} | {max(ds) / 1e3:.2f} |")
+    lines += ["", "## Per-stage roofline (timed steps, mean per step)", ""] + stage_roofline(
+        cfg, [r for r in trace if int(r["Start_Timestamp"]) >= t_timed])
     with open(os.path.join(ROOT, "profiles", f"layer_{cfg_name}_kernel_stats.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -285,6 +288,95 @@ def summarize(cfg_name: str, d: str):
     with open(os.path.join(ROOT, "profiles", f"syrk_{cfg_name}_traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+
+
+# Stages of the layer path and their kernels (base names as rocprofv3 -T
+# prints them; templated kernels keep a mangled name, matched by substring).
+STAGES = [
+    ("a1 Hessian SYRK", ("syrk_",)),
+    ("a2 damp / order / gather", ("diag_stats_kernel", "rank_count_kernel", "rank_scatter_kernel",
+                                  "symmetrize_kernel", "scale_kernel", "gather_kernel",
+                                  "fill_f32_kernel", "gather_w_kernel")),
+    ("a3 factor (Cholesky + inverse, U')", ("cholinv_leaf_kernel", "reverse_inplace_kernel",
+                                             "uprime_kernel", "gemm_f32_dma@prepare")),
+    ("a4 block sweep", ("sweep16_kernel", "sweep_kernel")),
+    ("a5 lazy trailing update", ("row_scale_kernel", "gemm_f32_dma@quantize")),
+    ("a6 pack", ("pack_kernel", "perm_tables_kernel")),
+]
+
+
+def stage_roofline(cfg, rows):
+    """Markdown lines: per stage, the summed kernel time per step, the
+    algorithmic work and its fraction of the stage's bound.  gemm_f32_dma
+    belongs to a3 before the step's first gather_w_kernel (prepare) and to a5
+    after it (quantize).  The factorization runs on three streams, so its
+    wall time (first start to last end per step) is given too."""
+    n, out, b, gs = cfg.inp, cfg.out, cfg.bits, cfg.group_size
+    gs = n if gs == -1 else gs
+    rows = sorted(rows, key=lambda r: int(r["Start_Timestamp"]))
+    steps = sum(1 for r in rows if r["Kernel_Name"].startswith("syrk_dma_kernel")) or 1
+    if cfg.tokens > 32768 and steps > 2:  # whole tiles: one launch per 32768 tokens
+        steps = max(1, steps // ((cfg.tokens + 32767) // 32768))
+    tot = {name: 0 for name, _ in STAGES}
+    a3_wall = 0
+    phase = "prepare"
+    a3_span = None
+    for r in rows:
+        k = r["Kernel_Name"]
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        if k.startswith("syrk_dma_kernel"):
+            phase = "prepare"
+            if a3_span:
+                a3_wall += a3_span[1] - a3_span[0]
+                a3_span = None
+        if "gather_w_kernel" in k:
+            phase = "quantize"
+        key = "gemm_f32_dma@" + phase if k.startswith("gemm_f32_dma") else k
+        for name, ks in STAGES:
+            if any(x in key for x in ks):
+                tot[name] += t1 - t0
+                if name.startswith("a3"):
+                    a3_span = [t0, t1] if a3_span is None else [min(a3_span[0], t0),
+                                                               max(a3_span[1], t1)]
+                break
+    if a3_span:
+        a3_wall += a3_span[1] - a3_span[0]
+    work = {
+        "a1 Hessian SYRK": (float(cfg.tokens) * n * (n + 1), "flop", "fp16 MFMA", PEAK_FP16_TFLOPS * 1e12),
+        "a2 damp / order / gather": (8.0 * n * n + 6.0 * out * n, "B", "HBM", PEAK_HBM_GBS * 1e9),
+        "a3 factor (Cholesky + inverse, U')": (2.0 * n ** 3 / 3, "flop", "fp32 (split-fp16 MFMA)",
+                                               PEAK_FP32_TFLOPS * 1e12),
+        "a4 block sweep": (7.0 * out * n + 8.0 * out * n / gs, "B", "HBM (latency-bound)",
+                           PEAK_HBM_GBS * 1e9),
+        "a5 lazy trailing update": (float(out) * n * (n - cfg.block), "flop", "fp16 MFMA",
+                                    PEAK_FP16_TFLOPS * 1e12),
+        "a6 pack": (out * n * (1 + b / 8.0), "B", "HBM", PEAK_HBM_GBS * 1e9),
+    }
+    lines = ["| stage | kernel ms | algorithmic work | achieved | bound | frac | MFMA pipe |",
+             "|---|---:|---:|---:|---|---:|---:|"]
+    for name, _ in STAGES:
+        t = tot[name] / steps * 1e-9
+        w, unit, bound, peak = work[name]
+        if t <= 0:
+            continue
+        ach = w / t
+        shown = f"{ach / 1e12:.1f} TFLOP/s" if unit == "flop" else f"{ach / 1e9:.0f} GB/s"
+        wshown = f"{w:.3g} {unit}"
+        # the trailing GEMMs multiply split fp32 operands (hi hi + hi lo + lo hi):
+        # three fp16 MFMA products per algorithmic one
+        pipe = f"{3 * ach / (PEAK_FP16_TFLOPS * 1e12):.3f}" if name.startswith("a5") else ""
+        lines.append(f"| {name} | {t * 1e3:.3f} | {wshown} | {shown} | {bound} | "
+                     f"{ach / peak:.3f} | {pipe} |")
+    lines.append("")
+    lines.append(f"a3 wall time per step (first start to last end; its kernels run on three "
+                 f"streams): {a3_wall / steps / 1e6:.3f} ms, "
+                 f"{2.0 * n ** 3 / 3 / (a3_wall / steps * 1e-9) / 1e12:.1f} TFLOP/s.")
+    lines.append("Peaks: fp16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s, HBM 8 TB/s. Work per "
+                 "stage: a1 N n(n+1), a2 8 n^2 + 6 out in bytes, a3 2 n^3 / 3, a4 "
+                 "7 out in + 8 out in / gs bytes, a5 out in (in - B), a6 out in (1 + b/8) bytes. "
+                 "MFMA pipe: fp16 MFMA work actually issued (three products per split-fp32 "
+                 "product) over the fp16 peak.")
+    return lines
 
 
 def collections_sum(rows, pick):
