@@ -606,6 +606,162 @@ def dequant_main(args):
     print(json.dumps(result), flush=True)
 
 
+def block_cpu_baseline(d, inter, bits, gs, sym, desc, X, Wg, Wu, Wd, samples):
+    """The oracle on a bounded sample of the block: Hessians and the forward
+    of one 2048-token sample (scaled to all samples), both factorizations in
+    full, the sweeps of 32 rows of each layer (scaled to all rows); fp64."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    torch.set_num_threads(max(1, len(os.sched_getaffinity(0))))
+    x = X[:2048].cpu().double().numpy()
+    wg, wu, wd = (w.cpu().double().numpy() for w in (Wg, Wu, Wd))
+    rows = 32
+    t = {}
+    t0 = time.perf_counter()
+    H = O.hessian(x)
+    t["hessian_in"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    Hd_, _ = O.condition(H, 0.01)
+    perm = O.column_order(H, desc)
+    U = O.hinv_chol(Hd_, perm)
+    t["prepare_in"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.gptq_sweep(wg[:rows], U, perm, bits, gs, sym)
+    t["sweep_gate"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    G = (x @ wg.T).astype(np.float16)
+    Uu = (x @ wu.T).astype(np.float16)
+    A = O.silu_mul(G, Uu).astype(np.float16)
+    H2 = O.hessian(A)
+    t["forward_hessian_down"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    Hd2, _ = O.condition(H2, 0.01)
+    perm2 = O.column_order(H2, desc)
+    U2 = O.hinv_chol(Hd2, perm2)
+    t["prepare_down"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.gptq_sweep(wd[:rows], U2, perm2, bits, gs, sym)
+    t["sweep_down"] = time.perf_counter() - t0
+    full = ((t["hessian_in"] + t["forward_hessian_down"]) * samples + t["prepare_in"]
+            + t["prepare_down"] + t["sweep_gate"] * 2 * inter / rows + t["sweep_down"] * d / rows)
+    return {
+        "value": 3.0 * d * inter / full,
+        "unit": "weights/s",
+        "cores": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"one 2048-token sample for the Hessians and the forward (scaled x{samples}), "
+                   f"both factorizations in full, 32-row sweeps (scaled to {inter}, {inter} and "
+                   f"{d} rows); fp64 NumPy; "
+                   + ", ".join(f"{k} {v:.2f} s" for k, v in t.items())),
+        "sample_seconds": round(sum(t.values()), 2),
+    }
+
+
+def block_main(args):
+    """--block: layer-wise GPTQ of a Llama-7B-shaped MLP block (gate, up
+    4096 -> 11008, down 11008 -> 4096), calibration through the quantized
+    gate and up layers; one step = the whole block."""
+    import torch
+
+    import post_weight_quantization_12_amd as P
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d, inter = 4096, 11008
+    bits, gs, sym, desc, damp = 4, 128, False, True, 0.01
+    base = workloads.get("c1")
+    t0 = time.perf_counter()
+    mixing = workloads._mixing(base, dev, 0)
+    outl = workloads.outlier_channels(base, dev, 0)
+    T = base.tokens_per_sample
+    X = torch.empty((base.tokens, d), dtype=torch.float16, device=dev)
+    for s in range(base.samples):
+        X[s * T:(s + 1) * T] = workloads.x_sample(base, s, dev, 0, mixing, outl)
+    Wg, Wu, Wd = workloads.mlp_block_weights(d, inter, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] block inputs ready in {time.perf_counter() - t0:.1f} s")
+    stream = torch.cuda.current_stream()
+    recs = []
+
+    def step(record):
+        ev = {}
+
+        def mark(name):
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                ev[name] = e
+        P.block.quantize_mlp_block(X, Wg, Wu, Wd, bits, gs, sym, damp, desc, stream=stream,
+                                   mark=mark)
+        if record:
+            recs.append(ev)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = list(recs[0].keys())
+    phases = {}
+    for a, b in zip(names[:-1], names[1:]):
+        phases[b] = sum(r[a].elapsed_time(r[b]) for r in recs) / len(recs)
+    ms = wall * 1e3 / args.steps
+    weights = 3 * d * inter
+    fwd_flops = 2.0 * base.tokens * d * 2 * inter
+    fwd_ms = phases["forward_hessian_down"]
+    result = {
+        "metric": "GPTQ Llama-7B MLP block (gate, up, down) weights quantized/sec, 1 GPU",
+        "value": weights / (ms * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in, f32 accumulate",
+        "data": "synthetic (seeded; stands in for c4 calibration text and Llama weights)",
+        "config": {
+            "workload": (f"MLP block d={d} inter={inter}: calibration {base.samples}x{T} tokens "
+                         f"fp16, {bits}-bit g{gs} asym desc_act={desc} damp {damp}; down_proj "
+                         "calibrated through the quantized gate and up layers"),
+            "tokens": base.tokens, "d": d, "inter": inter, "bits": bits, "group_size": gs,
+            "desc_act": desc, "chunk_tokens": 32768,
+        },
+        "phase_ms": phases,
+        "roofline": {
+            "kernel": ("forward phase: dq_gather_x_kernel + dq_mfma_kernel (gate and up as one "
+                       "[4096 -> 22016] layer), silu_mul_kernel, syrk_dma_kernel per 32768-token "
+                       "chunk"),
+            "bound": "mfma",
+            "achieved": (fwd_flops + float(base.tokens) * inter * (inter + 1)) / (fwd_ms * 1e-3)
+            / 1e12,
+            "peak": PEAK_FP16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": (fwd_flops + float(base.tokens) * inter * (inter + 1)) / (fwd_ms * 1e-3)
+            / 1e12 / PEAK_FP16_TFLOPS,
+            "phase_ms": fwd_ms,
+            "flops": fwd_flops + float(base.tokens) * inter * (inter + 1),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = block_cpu_baseline(d, inter, bits, gs, sym, desc, X, Wg, Wu, Wd,
+                                                    base.samples)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -621,6 +777,8 @@ def main():
     ap.add_argument("--dequant-tokens", type=int, default=None, metavar="M",
                     help="time gptq_dequant_matmul with M tokens on the config's packed layer "
                          "instead of the quantization step")
+    ap.add_argument("--block", action="store_true",
+                    help="time layer-wise GPTQ of a Llama-7B-shaped MLP block instead")
     ap.add_argument("--dequant-as-packed", action="store_true",
                     help="with --dequant-tokens on an act-order config: use the layer as packed "
                          "instead of its group order")
@@ -642,6 +800,9 @@ def main():
 
     if args.dequant_tokens is not None:
         dequant_main(args)
+        return
+    if args.block:
+        block_main(args)
         return
 
     import torch

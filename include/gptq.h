@@ -274,6 +274,25 @@ int gptq_dequant_group_order(const int32_t* qweight, const int32_t* g_idx, int64
                              int32_t* g_idx_sorted, int32_t* x_order, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * Gated activation of a Llama-style MLP block: A = SiLU(G) * U elementwise,
+ * SiLU(g) = g / (1 + e^-g).
+ *
+ * The layer-wise method takes each layer's calibration inputs from the
+ * block with its earlier layers already quantized (glossary entry "gptq",
+ * paragraph "Method" (1)); the down projection's input is this product of
+ * the gate and up projections' outputs.  The pages name the Llama layers but
+ * not the activation: SiLU gating is the Llama MLP's (a reading).
+ *
+ *   G, U   fp16 [rows x cols], row-major, leading dimensions ldg, ldu >= cols
+ *          (they may be the two halves of one [rows x 2 cols] matrix).
+ *   A      out: fp16 [rows x cols], lda >= cols; may alias G or U exactly.
+ * Arithmetic in fp32 (expf), one rounding to fp16.  rows or cols == 0 is a
+ * no-op.  Errors: INVALID_ARG, HIP.
+ */
+int gptq_silu_mul(const void* G, int64_t ldg, const void* U, int64_t ldu, int64_t rows,
+                  int64_t cols, void* A, int64_t lda, void* stream);
+
 /* Static text for a gptq_status_t value. */
 const char* gptq_status_string(int status);
 

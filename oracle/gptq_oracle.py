@@ -54,6 +54,9 @@ __all__ = [
     "dequantize",
     "dequant_matmul",
     "group_order",
+    "silu_mul",
+    "BlockResult",
+    "mlp_block",
     "layer_error",
 ]
 
@@ -440,6 +443,59 @@ def group_order(qweight, g_idx, bits: int):
     codes = unpack(qweight, bits, n)
     return (pack(codes[:, x_order], bits), g[x_order].astype(np.int32),
             x_order.astype(np.int32))
+
+
+def silu_mul(g, u) -> np.ndarray:
+    """SiLU(g) * u = g / (1 + e^-g) * u elementwise, float64: the gated
+    activation that feeds the down projection of a Llama MLP (the pages name
+    the Llama layers, not the activation; a reading)."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    return g / (1.0 + np.exp(-g)) * u
+
+
+@dataclass
+class BlockResult:
+    H_in: np.ndarray        # 2 X^T X of the block input
+    gate: SweepResult
+    up: SweepResult
+    A: np.ndarray           # the down projection's calibration inputs (fp16 values)
+    H_down: np.ndarray      # 2 A^T A
+    down: SweepResult
+
+
+def mlp_block(X, Wg, Wu, Wd, bits: int, group_size: int, sym: bool, damp_percent: float,
+              desc_act: bool) -> BlockResult:
+    """Layer-wise GPTQ over a Llama-style MLP block y = Wd (SiLU(Wg x) * (Wu x)).
+
+    [GLOSS] paragraph "Method" (1): one layer at a time, with calibration
+    activations computed through the block (3).  Reading: gate and up share
+    the block input, so one Hessian serves both; the down projection's
+    inputs are then computed with the gate and up layers already quantized
+    (their dequantized weights), and its Hessian comes from those.
+    The forward is fp16 as in the model ("keeping others in FP16"; reading):
+    the quantized weights enter it as fp16 values (the scale rounded to fp16,
+    times q - z, rounded), G = X Wg^T and U = X Wu^T are rounded to fp16, and
+    A = SiLU(G) U is evaluated from those and rounded to fp16.
+    """
+    X64 = np.asarray(X, dtype=np.float64)
+    H_in = hessian(X64)
+    gate = gptq(Wg, H_in, bits, group_size, sym, damp_percent, desc_act)
+    up = gptq(Wu, H_in, bits, group_size, sym, damp_percent, desc_act)
+
+    def w16(r):
+        # the forward's fp16 weights: scale rounded to fp16, times the exact
+        # integer q - z, rounded to fp16
+        s16 = r.scales.astype(np.float16).astype(np.float64)[r.g_idx, :].T
+        z = r.zeros.astype(np.float64)[r.g_idx, :].T
+        return (s16 * (r.codes - z)).astype(np.float16).astype(np.float64)
+
+    G = (X64 @ w16(gate).T).astype(np.float16)
+    U = (X64 @ w16(up).T).astype(np.float16)
+    A = silu_mul(G, U).astype(np.float16)
+    H_down = hessian(A)
+    down = gptq(Wd, H_down, bits, group_size, sym, damp_percent, desc_act)
+    return BlockResult(H_in=H_in, gate=gate, up=up, A=A, H_down=H_down, down=down)
 
 
 def layer_error(W, What, H) -> float:

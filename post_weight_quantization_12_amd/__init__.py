@@ -21,4 +21,6 @@ from ._lib import (  # noqa: F401
     prepare_workspace_bytes,
     quantize_layer,
     quantize_workspace_bytes,
+    silu_mul,
 )
+from . import block  # noqa: F401,E402

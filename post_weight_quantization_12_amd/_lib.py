@@ -71,6 +71,8 @@ def load():
     lib.gptq_dequant_group_order.argtypes = [vp, vp, i64, i64, c_int, vp, vp, vp, vp,
                                              ctypes.c_size_t, vp]
     lib.gptq_dequant_group_order.restype = c_int
+    lib.gptq_silu_mul.argtypes = [vp, i64, vp, i64, i64, i64, vp, i64, vp]
+    lib.gptq_silu_mul.restype = c_int
     lib.gptq_status_string.argtypes = [c_int]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_last_error_message.argtypes = []
@@ -305,3 +307,26 @@ def dequant_group_order(qweight, g_idx, bits: int, stream=None):
                                         _ptr(qs), _ptr(gs), _ptr(order), _ptr(ws), ws.numel(),
                                         _stream(stream)))
     return qs, gs, order
+
+
+def silu_mul(G, U, A=None, stream=None):
+    """A = SiLU(G) * U for fp16 [rows x cols] G, U (unit column stride; they
+    may be views of one matrix).  A: fp16 out, allocated when None."""
+    torch = _torch()
+    lib = load()
+    _need_cuda("G", G)
+    _need_cuda("U", U)
+    for name, t in (("G", G), ("U", U)):
+        if t.dtype != torch.float16 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be fp16 [rows x cols] with unit column stride")
+    if tuple(G.shape) != tuple(U.shape):
+        raise ValueError("G and U must have the same shape")
+    rows, cols = G.shape
+    if A is None:
+        A = torch.empty((rows, cols), dtype=torch.float16, device=G.device)
+    if A.dtype != torch.float16 or tuple(A.shape) != (rows, cols) or A.stride(1) != 1:
+        raise ValueError("A must be fp16 [rows x cols] with unit column stride")
+    ld = lambda t: t.stride(0) if rows > 1 else cols
+    _check(lib.gptq_silu_mul(_ptr(G), ld(G), _ptr(U), ld(U), rows, cols, _ptr(A), ld(A),
+                             _stream(stream)))
+    return A

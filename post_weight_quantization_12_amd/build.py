@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgptq_mi355x.so")
-SOURCES = ["api.hip", "syrk.hip", "gemm_f32.hip", "prepare.hip", "quantize.hip", "dequant_matmul.hip"]
+SOURCES = ["api.hip", "syrk.hip", "gemm_f32.hip", "prepare.hip", "quantize.hip", "dequant_matmul.hip",
+           "activation.hip"]
 ARCH = "gfx950"
 
 

@@ -236,6 +236,19 @@ int gptq_dequant_group_order(const int32_t* qweight, const int32_t* g_idx, int64
                     "gptq_dequant_group_order");
 }
 
+int gptq_silu_mul(const void* G, int64_t ldg, const void* U, int64_t ldu, int64_t rows,
+                  int64_t cols, void* A, int64_t lda, void* stream) {
+  clear_error();
+  if (!G || !U || !A) return fail(GPTQ_ERR_INVALID_ARG, "G, U or A is NULL");
+  if (rows < 0 || cols < 0) return fail(GPTQ_ERR_INVALID_ARG, "rows and cols must be >= 0");
+  if (ldg < cols || ldu < cols || lda < cols)
+    return fail(GPTQ_ERR_INVALID_ARG, "leading dimensions must be >= cols");
+  if (rows == 0 || cols == 0) return GPTQ_OK;
+  return hip_status(run_silu_mul(G, ldg, U, ldu, rows, cols, A, lda,
+                                 static_cast<hipStream_t>(stream)),
+                    "gptq_silu_mul");
+}
+
 const char* gptq_status_string(int status) {
   switch (status) {
     case GPTQ_OK: return "GPTQ_OK";

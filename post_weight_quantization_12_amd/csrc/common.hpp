@@ -127,6 +127,10 @@ hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
                               const int32_t* g_idx, const int32_t* x_order, int64_t out, int bits,
                               void* Y, int y_f16, int64_t ldy, void* ws, size_t ws_bytes,
                               hipStream_t s);
+// A = SiLU(G) * U elementwise, fp16 in and out, fp32 arithmetic.
+hipError_t run_silu_mul(const void* G, int64_t ldg, const void* U, int64_t ldu, int64_t rows,
+                        int64_t cols, void* A, int64_t lda, hipStream_t s);
+
 // The layer's input positions re-ordered by group (stable), repacked.
 size_t dequant_group_order_workspace_bytes(int64_t in);
 hipError_t run_dequant_group_order(const int32_t* qweight, const int32_t* g_idx, int64_t in,

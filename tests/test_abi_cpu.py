@@ -22,7 +22,7 @@ def test_exports_every_header_function(lib):
                           "gptq_prepare", "gptq_quantize_workspace_bytes",
                           "gptq_quantize_layer", "gptq_dequant_matmul_workspace_bytes",
                           "gptq_dequant_matmul", "gptq_dequant_group_order_workspace_bytes",
-                          "gptq_dequant_group_order", "gptq_status_string",
+                          "gptq_dequant_group_order", "gptq_silu_mul", "gptq_status_string",
                           "gptq_last_error_message"}
     for n in names:
         assert hasattr(lib, n), n
@@ -178,3 +178,12 @@ def test_dequant_group_order_argument_errors(lib):
     assert call(bits=5) == L.GPTQ_ERR_UNSUPPORTED
     assert call(w=None) == L.GPTQ_ERR_INVALID_ARG
     assert call(wsb=ws - 1) == L.GPTQ_ERR_WORKSPACE
+
+
+def test_silu_mul_argument_errors(lib):
+    f = lib.gptq_silu_mul
+    assert f(None, 8, FAKE, 8, 2, 8, FAKE, 8, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 8, FAKE, 8, -1, 8, FAKE, 8, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, 4, FAKE, 8, 2, 8, FAKE, 8, None) == L.GPTQ_ERR_INVALID_ARG
+    assert b"leading" in lib.gptq_last_error_message()
+    assert f(FAKE, 8, FAKE, 8, 0, 8, FAKE, 8, None) == L.GPTQ_OK   # no-op, no device access

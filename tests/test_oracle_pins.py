@@ -531,3 +531,54 @@ def test_group_order_same_product_exactly(bits):
     assert np.array_equal(y, y2)
     # the ordered layer's chunks of 32 inputs each hold one group
     assert all(len(set(gsrt[c:c + 32].tolist())) == 1 for c in range(0, n, 32))
+
+
+def test_silu_mul_closed_forms():
+    # SiLU(0) = 0; SiLU(ln 3) = ln 3 / (1 + 1/3) = 0.75 ln 3; SiLU(-ln 3) =
+    # -ln 3 / 4; large |g|: g or 0; the up factor multiplies.
+    l3 = np.log(3.0)
+    g = np.array([0.0, l3, -l3, 40.0, -40.0, l3])
+    u = np.array([5.0, 1.0, 1.0, 1.0, 1.0, -2.0])
+    want = np.array([0.0, 0.75 * l3, -0.25 * l3, 40.0, 0.0, -1.5 * l3])
+    got = O.silu_mul(g, u)
+    assert np.allclose(got, want, rtol=1e-15, atol=1e-15)
+
+
+def test_mlp_block_down_hessian_from_quantized_gate_up():
+    # The down projection's Hessian comes from activations computed with the
+    # gate and up layers already quantized: rebuild it by hand from the
+    # returned gate/up results and compare, and check that it differs from
+    # the one the unquantized gate and up layers would give.
+    rng = np.random.default_rng(5)
+    d, inter, t = 32, 64, 256
+    X = rng.normal(size=(t, d)).astype(np.float16).astype(np.float64)
+    Wg = (rng.normal(size=(inter, d)) * 0.1).astype(np.float32)
+    Wu = (rng.normal(size=(inter, d)) * 0.1).astype(np.float32)
+    Wd = (rng.normal(size=(d, inter)) * 0.1).astype(np.float32)
+    r = O.mlp_block(X, Wg, Wu, Wd, 4, 16, False, 0.01, False)
+    def w16(res):   # fp16 scale times q - z, rounded to fp16, element by element
+        Wq = np.zeros(res.codes.shape)
+        for r_ in range(res.codes.shape[0]):
+            for k in range(res.codes.shape[1]):
+                g_ = res.g_idx[k]
+                s16 = float(np.float16(res.scales[g_, r_]))
+                Wq[r_, k] = float(np.float16(s16 * (res.codes[r_, k] - res.zeros[g_, r_])))
+        return Wq
+    G = X @ w16(r.gate).T
+    U = X @ w16(r.up).T
+    A = O.silu_mul(G.astype(np.float16), U.astype(np.float16)).astype(np.float16)
+    assert np.array_equal(A, r.A)
+    Hd = 2.0 * A.astype(np.float64).T @ A.astype(np.float64)
+    assert np.allclose(r.H_down, Hd, rtol=1e-12, atol=1e-9)
+    A16 = O.silu_mul((X @ Wg.astype(np.float64).T).astype(np.float16),
+                     (X @ Wu.astype(np.float64).T).astype(np.float16)).astype(np.float16)
+    H16 = 2.0 * A16.astype(np.float64).T @ A16.astype(np.float64)
+    assert np.linalg.norm(H16 - r.H_down) > 1e-3 * np.linalg.norm(H16)
+    # gate and up use the block input's Hessian: same as quantizing them alone
+    ref = O.gptq(Wg, 2.0 * X.T @ X, 4, 16, False, 0.01, False)
+    assert np.array_equal(ref.codes, r.gate.codes)
+    # the down layer's calibration error beats round-to-nearest on its inputs
+    Wd64 = Wd.astype(np.float64)
+    e = O.layer_error(Wd64, r.down.what, r.H_down)
+    e_rtn = O.layer_error(Wd64, O.rtn(Wd64, 4, 16, False).what, r.H_down)
+    assert e < e_rtn

@@ -27,7 +27,7 @@ import torch
 
 __all__ = ["Config", "CONFIGS", "get", "weight", "x_sample", "x_tokens",
            "outlier_channels", "boundary_safe_weight", "synthetic_hinv_chol",
-           "generator", "packed_layer_draws"]
+           "generator", "packed_layer_draws", "mlp_block_weights"]
 
 
 @dataclass(frozen=True)
@@ -248,3 +248,14 @@ def packed_layer_draws(cfg: Config, device="cpu", seed: int = 0):
     else:
         order = torch.arange(cfg.inp, device=device)
     return words, scales, zeros, order
+
+
+def mlp_block_weights(d: int, inter: int, device="cpu", seed: int = 0):
+    """(Wg, Wu [inter x d], Wd [d x inter]) fp16 for a Llama-style MLP block:
+    N(0, 0.02^2) for the gate and up projections (as the q_proj-shaped
+    layer), N(0, 0.015^2) for the down projection (as the down_proj-shaped
+    layer); drawn in fp32, rounded to fp16."""
+    wg = _randn((inter, d), device, seed, 20, 0, d) * 0.02
+    wu = _randn((inter, d), device, seed, 21, 0, d) * 0.02
+    wd = _randn((d, inter), device, seed, 22, 0, d) * 0.015
+    return wg.to(torch.float16), wu.to(torch.float16), wd.to(torch.float16)
