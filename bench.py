@@ -202,6 +202,55 @@ def summarize_dequant(cfg_name: str, M: int, d: str):
     print(json.dumps(out, indent=1))
 
 
+def _kernel_base_name(name: str) -> str:
+    """The kernel's identifier: mangled names of this library's templated or
+    anonymous-namespace kernels (_ZN4gptq12_GLOBAL__N_1<len><name>...) are cut
+    to <name>."""
+    import re
+    m = re.match(r"_ZN4gptq12_GLOBAL__N_1(\d+)", name)
+    if m:
+        n = int(m.group(1))
+        return name[m.end():m.end() + n]
+    return name.split("(")[0].replace("void ", "")[:60]
+
+
+BLOCK_PROFILE_COMMAND = ("rocprofv3 --kernel-trace --stats -T -d {d}/trace -o t --output-format csv "
+                         "-- python -u bench.py --block --steps 1 --warmup 1 --no-cpu-baseline")
+
+
+def summarize_block(d: str):
+    """profiles/block_mlp_kernel_stats.md from the BLOCK_PROFILE_COMMAND
+    trace in d: per-kernel statistics of the timed step (the second of two)."""
+    import csv
+    trace = list(csv.DictReader(open(os.path.join(d, "trace", "t_kernel_trace.csv"))))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    # each step packs three layers: the warm-up step ends with its third pack
+    packs = [int(r["End_Timestamp"]) for r in trace if r["Kernel_Name"].startswith("pack_kernel")]
+    first = packs[2] if len(packs) >= 6 else 0
+    k = sum(1 for r in trace if int(r["Start_Timestamp"]) < first)
+    stats = {}
+    span = [None, None]
+    for r in trace:
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        if t0 < first:
+            continue
+        name = _kernel_base_name(r["Kernel_Name"])
+        stats.setdefault(name, []).append(t1 - t0)
+        span = [t0 if span[0] is None else min(span[0], t0), t1 if span[1] is None else max(span[1], t1)]
+    lines = ["# rocprofv3 kernel statistics: bench.py --block (Llama-7B MLP block, d 4096, "
+             "inter 11008, 4-bit g128 asym, desc_act on, 128 x 2048 calibration tokens)", "",
+             "Command (run from the repository root on one MI355X):", "",
+             "    " + BLOCK_PROFILE_COMMAND.format(d=d), "",
+             f"The timed step only ({(span[1] - span[0]) / 1e6:.1f} ms from its first kernel "
+             f"to its last under the profiler; {k} earlier launches belong to the warm-up).", "",
+             "| kernel | calls | total ms | avg us |", "|---|---:|---:|---:|"]
+    for name, ds in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {name} | {len(ds)} | {sum(ds) / 1e6:.3f} | {sum(ds) / len(ds) / 1e3:.2f} |")
+    with open(os.path.join(ROOT, "profiles", "block_mlp_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize(cfg_name: str, d: str):
     """Write the profiles/ summaries from rocprofv3 CSV output in d (the
     PROFILE_COMMANDS run with the default call size).  FETCH_SIZE and
@@ -790,6 +839,8 @@ def main():
     if args.summarize:
         if args.dequant_tokens is not None:
             summarize_dequant(args.config, args.dequant_tokens, args.summarize)
+        elif args.block:
+            summarize_block(args.summarize)
         else:
             summarize(args.config, args.summarize)
         return

@@ -49,12 +49,11 @@ def quantize_mlp_block(X, Wg, Wu, Wd, bits: int, group_size: int, sym: bool, dam
         raise ValueError("Wg, Wu must be [inter x d] and Wd [d x inter]")
     chunks = [X[i:i + chunk_tokens] for i in range(0, ntok, chunk_tokens)]
 
-    # gate and up: the block input's Hessian
+    # gate and up: the block input's Hessian (X is resident: one call)
     H_in = torch.zeros((d, d), dtype=torch.float32, device=dev)
     ws = torch.empty((L.hessian_workspace_bytes(d),), dtype=torch.uint8, device=dev)
     mark("start")
-    for c in chunks:
-        L.hessian_accumulate(H_in, c, stream, ws)
+    L.hessian_accumulate(H_in, X, stream, ws)
     mark("hessian_in")
     U_in, perm_in, info_in = L.prepare(H_in, damp, desc_act, stream=stream)
     mark("prepare_in")
