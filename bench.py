@@ -811,6 +811,65 @@ def block_main(args):
     print(json.dumps(result), flush=True)
 
 
+def export_main(args):
+    """--export: gptq_export_params on the config's layer (fp16 scales,
+    packed zeros; HBM roofline) and a save / load of the layer through the
+    local checkpoint writer (host and file time, for context)."""
+    import tempfile
+
+    import torch
+
+    import post_weight_quantization_12_amd as P
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workloads.get(args.config)
+    words, scales, zeros, order = workloads.packed_layer_draws(cfg, dev, 0)
+    gs = cfg.inp if cfg.group_size == -1 else cfg.group_size
+    g_idx = torch.empty((cfg.inp,), dtype=torch.int32, device=dev)
+    g_idx[order] = (torch.arange(cfg.inp, device=dev) // gs).to(torch.int32)
+    G, out = scales.shape
+    reps = 50
+    for _ in range(5):
+        P.export_params(scales, zeros, cfg.bits)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        P.export_params(scales, zeros, cfg.bits)
+    b.record()
+    torch.cuda.synchronize()
+    call_ms = a.elapsed_time(b) / reps
+    alg = G * out * (4 + 4 + 2) + G * out * cfg.bits // 8
+    with tempfile.TemporaryDirectory() as d:
+        t0 = time.perf_counter()
+        P.checkpoint.save_quantized(d, {"layer": (words, scales, zeros, g_idx)}, cfg.bits,
+                                    cfg.group_size, cfg.desc_act, cfg.damp, cfg.sym)
+        t_save = time.perf_counter() - t0
+        size = sum(os.path.getsize(os.path.join(d, f)) for f in os.listdir(d))
+        t0 = time.perf_counter()
+        P.checkpoint.load_quantized(d)
+        torch.cuda.synchronize()
+        t_load = time.perf_counter() - t0
+    achieved = alg / (call_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "gptq_export_params (fp16 scales + packed zeros) GB/s",
+        "value": achieved, "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 5,
+        "ms_per_step": call_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 -> f16, int32 -> b-bit", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} layer parameters: {G} groups x {out} channels, "
+                               f"{cfg.bits}-bit", "groups": G, "out": out, "bits": cfg.bits},
+        "roofline": {"kernel": "export_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "bytes_per_call": alg, "traffic": None},
+        "checkpoint": {"bytes": size, "save_s": t_save, "load_s": t_load,
+                       "save_GBps": size / t_save / 1e9, "load_GBps": size / t_load / 1e9},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -826,6 +885,8 @@ def main():
     ap.add_argument("--dequant-tokens", type=int, default=None, metavar="M",
                     help="time gptq_dequant_matmul with M tokens on the config's packed layer "
                          "instead of the quantization step")
+    ap.add_argument("--export", action="store_true",
+                    help="time gptq_export_params and a checkpoint save / load of the layer")
     ap.add_argument("--block", action="store_true",
                     help="time layer-wise GPTQ of a Llama-7B-shaped MLP block instead")
     ap.add_argument("--dequant-as-packed", action="store_true",
@@ -854,6 +915,9 @@ def main():
         return
     if args.block:
         block_main(args)
+        return
+    if args.export:
+        export_main(args)
         return
 
     import torch

@@ -293,6 +293,33 @@ int gptq_dequant_group_order(const int32_t* qweight, const int32_t* g_idx, int64
 int gptq_silu_mul(const void* G, int64_t ldg, const void* U, int64_t ldu, int64_t rows,
                   int64_t cols, void* A, int64_t lda, void* stream);
 
+/*
+ * Storage form of a layer's group parameters, for saving it.
+ *
+ * The pages save quantized models as safetensors files with a
+ * quantize_config.json ("AutoGPTQ" catalogue page, Safetensors Support;
+ * "GPTQ > Using AutoGPTQ in Practice", saving).  The layout of the stored
+ * tensors is not given there; the reading taken: scales as fp16, and the
+ * zero-points packed like the codes, as a dense little-endian b-bit stream,
+ * here along the output channels: qzeros[g][w] is word w of the stream of
+ * zeros[g][0 .. out-1] (zero r at bits [r b, (r+1) b)); zero-points are
+ * stored as they are (no offset).
+ *
+ *   scales   fp32 [n_groups x out]; zeros int32 [n_groups x out], values in
+ *            [0, 2^bits) (higher bits are dropped).
+ *   scales_f16  out: fp16 [n_groups x out] (round to nearest).
+ *   qzeros   out: int32 [n_groups x out * bits / 32].
+ *   out * bits must be a multiple of 32; bits 2, 3, 4 or 8.
+ * Errors: INVALID_ARG, UNSUPPORTED (bits, out * bits % 32), HIP.
+ */
+int gptq_export_params(const float* scales, const int32_t* zeros, int64_t n_groups, int64_t out,
+                       int bits, void* scales_f16, int32_t* qzeros, void* stream);
+
+/* zeros int32 [n_groups x out] from qzeros as gptq_export_params writes it
+ * (the same conditions; errors as there). */
+int gptq_unpack_zeros(const int32_t* qzeros, int64_t n_groups, int64_t out, int bits,
+                      int32_t* zeros, void* stream);
+
 /* Static text for a gptq_status_t value. */
 const char* gptq_status_string(int status);
 

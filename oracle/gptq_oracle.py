@@ -54,6 +54,8 @@ __all__ = [
     "dequantize",
     "dequant_matmul",
     "group_order",
+    "pack_zeros",
+    "unpack_zeros",
     "silu_mul",
     "BlockResult",
     "mlp_block",
@@ -443,6 +445,33 @@ def group_order(qweight, g_idx, bits: int):
     codes = unpack(qweight, bits, n)
     return (pack(codes[:, x_order], bits), g[x_order].astype(np.int32),
             x_order.astype(np.int32))
+
+
+def pack_zeros(zeros, bits: int) -> np.ndarray:
+    """Zero-points in storage form: row g of the result is the little-endian
+    b-bit stream of zeros[g][0 .. out-1] cut into 32-bit words (zero r at bits
+    [r b, (r+1) b)): the codes' dense packing ([GLOSS] "Quantization
+    targets") applied along the output channels (a reading: the pages store
+    the parameters with the model but do not give their layout)."""
+    z = np.asarray(zeros, dtype=np.int64)
+    G, out = z.shape
+    if (out * bits) % 32:
+        raise ValueError("out * bits must be a multiple of 32")
+    if z.min(initial=0) < 0 or z.max(initial=0) >= (1 << bits):
+        raise ValueError("zero-point out of range")
+    stream = ((z[:, :, None] >> np.arange(bits)[None, None, :]) & 1).reshape(G, out * bits)
+    words = stream.reshape(G, out * bits // 32, 32)
+    vals = (words << np.arange(32, dtype=np.int64)[None, None, :]).sum(axis=2)
+    return vals.astype(np.uint32).view(np.int32)
+
+
+def unpack_zeros(qzeros, bits: int, out: int) -> np.ndarray:
+    """Inverse of pack_zeros."""
+    q = np.asarray(qzeros).astype(np.int32).view(np.uint32).astype(np.int64)
+    G = q.shape[0]
+    stream = ((q[:, :, None] >> np.arange(32, dtype=np.int64)[None, None, :]) & 1).reshape(G, -1)
+    fields = stream[:, : out * bits].reshape(G, out, bits)
+    return (fields << np.arange(bits, dtype=np.int64)[None, None, :]).sum(axis=2)
 
 
 def silu_mul(g, u) -> np.ndarray:

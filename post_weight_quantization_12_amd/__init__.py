@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     dequant_group_order_workspace_bytes,
     dequant_matmul,
     dequant_matmul_workspace_bytes,
+    export_params,
     hessian_accumulate,
     hessian_workspace_bytes,
     header_functions,
@@ -22,5 +23,7 @@ from ._lib import (  # noqa: F401
     quantize_layer,
     quantize_workspace_bytes,
     silu_mul,
+    unpack_zeros,
 )
 from . import block  # noqa: F401,E402
+from . import checkpoint  # noqa: F401,E402

@@ -73,6 +73,10 @@ def load():
     lib.gptq_dequant_group_order.restype = c_int
     lib.gptq_silu_mul.argtypes = [vp, i64, vp, i64, i64, i64, vp, i64, vp]
     lib.gptq_silu_mul.restype = c_int
+    lib.gptq_export_params.argtypes = [vp, vp, i64, i64, c_int, vp, vp, vp]
+    lib.gptq_export_params.restype = c_int
+    lib.gptq_unpack_zeros.argtypes = [vp, i64, i64, c_int, vp, vp]
+    lib.gptq_unpack_zeros.restype = c_int
     lib.gptq_status_string.argtypes = [c_int]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_last_error_message.argtypes = []
@@ -330,3 +334,37 @@ def silu_mul(G, U, A=None, stream=None):
     _check(lib.gptq_silu_mul(_ptr(G), ld(G), _ptr(U), ld(U), rows, cols, _ptr(A), ld(A),
                              _stream(stream)))
     return A
+
+
+def export_params(scales, zeros, bits: int, stream=None):
+    """(scales fp16 [G x out], qzeros int32 [G x out*bits/32]) for saving."""
+    torch = _torch()
+    lib = load()
+    _need_cuda("scales", scales)
+    _need_cuda("zeros", zeros)
+    if scales.dtype != torch.float32 or scales.dim() != 2 or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous fp32 [n_groups x out] tensor")
+    if zeros.dtype != torch.int32 or tuple(zeros.shape) != tuple(scales.shape) \
+            or not zeros.is_contiguous():
+        raise ValueError("zeros must be a contiguous int32 tensor shaped like scales")
+    G, out = scales.shape
+    s16 = torch.empty((G, out), dtype=torch.float16, device=scales.device)
+    qz = torch.empty((G, out * bits // 32), dtype=torch.int32, device=scales.device)
+    _check(lib.gptq_export_params(_ptr(scales), _ptr(zeros), G, out, int(bits), _ptr(s16),
+                                  _ptr(qz), _stream(stream)))
+    return s16, qz
+
+
+def unpack_zeros(qzeros, out: int, bits: int, stream=None):
+    """zeros int32 [G x out] from qzeros int32 [G x out*bits/32]."""
+    torch = _torch()
+    lib = load()
+    _need_cuda("qzeros", qzeros)
+    if qzeros.dtype != torch.int32 or qzeros.dim() != 2 or not qzeros.is_contiguous():
+        raise ValueError("qzeros must be a contiguous int32 [n_groups x out*bits/32] tensor")
+    G = qzeros.shape[0]
+    if qzeros.shape[1] * 32 != out * bits:
+        raise ValueError("qzeros columns must be out * bits / 32")
+    z = torch.empty((G, out), dtype=torch.int32, device=qzeros.device)
+    _check(lib.gptq_unpack_zeros(_ptr(qzeros), G, out, int(bits), _ptr(z), _stream(stream)))
+    return z

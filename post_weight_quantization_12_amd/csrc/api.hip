@@ -249,6 +249,35 @@ int gptq_silu_mul(const void* G, int64_t ldg, const void* U, int64_t ldu, int64_
                     "gptq_silu_mul");
 }
 
+int gptq_export_params(const float* scales, const int32_t* zeros, int64_t n_groups, int64_t out,
+                       int bits, void* scales_f16, int32_t* qzeros, void* stream) {
+  clear_error();
+  if (!scales || !zeros || !scales_f16 || !qzeros)
+    return fail(GPTQ_ERR_INVALID_ARG, "scales, zeros, scales_f16 or qzeros is NULL");
+  if (n_groups < 1 || out < 1) return fail(GPTQ_ERR_INVALID_ARG, "n_groups and out must be >= 1");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits must be 2, 3, 4 or 8");
+  if ((out * bits) % 32 != 0)
+    return fail(GPTQ_ERR_UNSUPPORTED, "out * bits must be a multiple of 32");
+  return hip_status(run_export(scales, zeros, n_groups, out, bits, scales_f16, qzeros,
+                               static_cast<hipStream_t>(stream)),
+                    "gptq_export_params");
+}
+
+int gptq_unpack_zeros(const int32_t* qzeros, int64_t n_groups, int64_t out, int bits,
+                      int32_t* zeros, void* stream) {
+  clear_error();
+  if (!qzeros || !zeros) return fail(GPTQ_ERR_INVALID_ARG, "qzeros or zeros is NULL");
+  if (n_groups < 1 || out < 1) return fail(GPTQ_ERR_INVALID_ARG, "n_groups and out must be >= 1");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits must be 2, 3, 4 or 8");
+  if ((out * bits) % 32 != 0)
+    return fail(GPTQ_ERR_UNSUPPORTED, "out * bits must be a multiple of 32");
+  return hip_status(run_unpack_zeros(qzeros, n_groups, out, bits, zeros,
+                                     static_cast<hipStream_t>(stream)),
+                    "gptq_unpack_zeros");
+}
+
 const char* gptq_status_string(int status) {
   switch (status) {
     case GPTQ_OK: return "GPTQ_OK";

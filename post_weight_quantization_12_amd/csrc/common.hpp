@@ -127,6 +127,13 @@ hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
                               const int32_t* g_idx, const int32_t* x_order, int64_t out, int bits,
                               void* Y, int y_f16, int64_t ldy, void* ws, size_t ws_bytes,
                               hipStream_t s);
+// Storage form of the group parameters: fp16 scales, zeros packed b-bit
+// along the output channels (out * bits % 32 == 0), and the inverse.
+hipError_t run_export(const float* scales, const int32_t* zeros, int64_t G, int64_t out, int bits,
+                      void* scales_f16, int32_t* qzeros, hipStream_t s);
+hipError_t run_unpack_zeros(const int32_t* qzeros, int64_t G, int64_t out, int bits,
+                            int32_t* zeros, hipStream_t s);
+
 // A = SiLU(G) * U elementwise, fp16 in and out, fp32 arithmetic.
 hipError_t run_silu_mul(const void* G, int64_t ldg, const void* U, int64_t ldu, int64_t rows,
                         int64_t cols, void* A, int64_t lda, hipStream_t s);

@@ -22,7 +22,8 @@ def test_exports_every_header_function(lib):
                           "gptq_prepare", "gptq_quantize_workspace_bytes",
                           "gptq_quantize_layer", "gptq_dequant_matmul_workspace_bytes",
                           "gptq_dequant_matmul", "gptq_dequant_group_order_workspace_bytes",
-                          "gptq_dequant_group_order", "gptq_silu_mul", "gptq_status_string",
+                          "gptq_dequant_group_order", "gptq_silu_mul", "gptq_export_params",
+                          "gptq_unpack_zeros", "gptq_status_string",
                           "gptq_last_error_message"}
     for n in names:
         assert hasattr(lib, n), n
@@ -187,3 +188,14 @@ def test_silu_mul_argument_errors(lib):
     assert f(FAKE, 4, FAKE, 8, 2, 8, FAKE, 8, None) == L.GPTQ_ERR_INVALID_ARG
     assert b"leading" in lib.gptq_last_error_message()
     assert f(FAKE, 8, FAKE, 8, 0, 8, FAKE, 8, None) == L.GPTQ_OK   # no-op, no device access
+
+
+def test_export_argument_errors(lib):
+    f = lib.gptq_export_params
+    assert f(None, FAKE, 2, 8, 4, FAKE, FAKE, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 0, 8, 4, FAKE, FAKE, None) == L.GPTQ_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 2, 8, 5, FAKE, FAKE, None) == L.GPTQ_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, 2, 6, 4, FAKE, FAKE, None) == L.GPTQ_ERR_UNSUPPORTED  # 24 bits a row
+    g = lib.gptq_unpack_zeros
+    assert g(None, 2, 8, 4, FAKE, None) == L.GPTQ_ERR_INVALID_ARG
+    assert g(FAKE, 2, 10, 3, FAKE, None) == L.GPTQ_ERR_UNSUPPORTED            # 30 bits a row

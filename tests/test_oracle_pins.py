@@ -582,3 +582,35 @@ def test_mlp_block_down_hessian_from_quantized_gate_up():
     e = O.layer_error(Wd64, r.down.what, r.H_down)
     e_rtn = O.layer_error(Wd64, O.rtn(Wd64, 4, 16, False).what, r.H_down)
     assert e < e_rtn
+
+
+def test_pack_zeros_hand_example():
+    # 4-bit zeros 1..8 of one group row -> one word 0x87654321; 3-bit zeros
+    # 7, 0, 5 start a stream whose low bits are 0b101_000_111 = 0x147;
+    # 8-bit zeros 0x11, 0x22, 0x33, 0x44 -> 0x44332211.
+    z4 = np.arange(1, 9).reshape(1, 8)
+    assert (O.pack_zeros(z4, 4).view(np.uint32) == [[0x87654321]]).all()
+    z3 = np.zeros((1, 32), dtype=np.int64)
+    z3[0, :3] = [7, 0, 5]
+    w3 = O.pack_zeros(z3, 3).view(np.uint32)
+    assert w3.shape == (1, 3) and int(w3[0, 0]) == 0x147 and int(w3[0, 1]) == 0
+    z8 = np.array([[0x11, 0x22, 0x33, 0x44]])
+    assert (O.pack_zeros(z8, 8).view(np.uint32) == [[0x44332211]]).all()
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_pack_zeros_round_trip_bitwise(bits):
+    rng = np.random.default_rng(bits)
+    z = rng.integers(0, 2 ** bits, size=(3, 64))
+    q = O.pack_zeros(z, bits)
+    assert q.shape == (3, 64 * bits // 32)
+    assert np.array_equal(O.unpack_zeros(q, bits, 64), z)
+    # bit by bit: zero r of row g occupies stream bits [r b, (r+1) b)
+    qu = q.view(np.uint32).astype(np.int64)
+    for g in range(3):
+        for r in range(0, 64, 7):
+            v = 0
+            for i in range(bits):
+                pos = r * bits + i
+                v |= ((int(qu[g, pos // 32]) >> (pos % 32)) & 1) << i
+            assert v == z[g, r]
