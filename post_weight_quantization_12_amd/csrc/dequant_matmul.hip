@@ -20,7 +20,7 @@
 //     is staged in LDS as fp16 pairs.  The input dimension is split over
 //     several workgroups (grid >= 2 per compute unit); their partial sums go
 //     to the workspace and a second kernel adds them in a fixed order.
-//   * many tokens (prefill): 128 x 128 tiles on v_mfma_f32_32x32x16_f16.
+//   * many tokens (prefill): 256 x 128 tiles on v_mfma_f32_32x32x16_f16.
 //     Per 32-k chunk the X tile goes to LDS as is (k contiguous: an MFMA A
 //     operand is one 16-byte read) and the weight tile is dequantized into
 //     LDS as fp16 column-major (k contiguous: a B operand is one 16-byte
@@ -368,91 +368,99 @@ dq_reduce_kernel(const float* __restrict__ part, int nsplit, int64_t M, int64_t 
 }
 
 // ---------------------------------------------------------------- MFMA path --
-constexpr int TB = 128;          // tile rows (tokens) and columns (outputs)
+constexpr int TN = 128;          // tile columns (outputs); rows (tokens): TM = 128 or 256
 constexpr int XP = DQ_CHUNK + 8; // LDS pitch in halves (80 bytes, 16-byte aligned rows)
 
-// Grid: (ceil(out / 128), ceil(M / 128), nsplit); 4 waves, each a 64 x 64
-// block.  Split z covers chunks [z cps, min((z + 1) cps, in / 32)); with
-// more than one split the fp32 sums go to part[z][M][out] for
-// dq_reduce_kernel.
-// Two LDS buffers: while the matrix cores work on chunk c, the X tile and
-// the weight words of chunk c + 1 (and the scale and zero of its group) are
-// in flight; they are dequantized into the other buffer afterwards, and one
-// barrier per chunk separates the two.  g_idx is read two chunks ahead.
-template <int B>
-__global__ void __launch_bounds__(256)
+// Grid: (ceil(out / 128), ceil(M / TM), nsplit); 8 waves, TM / 64 x
+// 512 / TM of them, each a 64 x (TM / 4) block (64 x 64 for TM = 256,
+// 64 x 32 for TM = 128, which fits fewer tokens).  Split z covers chunks [z cps, min((z + 1) cps, in / 32));
+// with more than one split the fp32 sums go to part[z][M][out] for
+// dq_reduce_kernel.  Two LDS buffers: while the matrix cores work on chunk
+// c, the X tile and the weight words of chunk c + 1 (and the scale and zero
+// of its group) are in flight; they are dequantized into the other buffer
+// afterwards, and one barrier per chunk separates the two.  g_idx is read
+// two chunks ahead.  A 256-row tile halves the dequantization per matrix-core
+// flop against 128 rows: each thread dequantizes 8 codes of one column.
+template <int B, int TM>
+__global__ void __launch_bounds__(512)
 dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
                const uint32_t* __restrict__ qw, const float* __restrict__ scales,
                const int32_t* __restrict__ zeros, const int32_t* __restrict__ g_idx,
                int64_t out, int64_t cps, float* __restrict__ part, void* __restrict__ Y,
                int y_f16, int64_t ldy) {
-  __shared__ __align__(16) _Float16 Xs[2][TB * XP];
-  __shared__ __align__(16) _Float16 Ws[2][TB * XP];
+  __shared__ __align__(16) _Float16 Xs[2][TM * XP];  // TM: template parameter
+  __shared__ __align__(16) _Float16 Ws[2][TN * XP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
-  const int64_t m0 = (int64_t)blockIdx.y * TB, n0 = (int64_t)blockIdx.x * TB;
-  // weight dequantization: column wc, codes 16 wh .. 16 wh + 15 of each chunk
-  const int wc = tid % TB;
-  const int wh = __builtin_amdgcn_readfirstlane(tid / TB);  // uniform within a wave
+  constexpr int WMN = TM / 64;          // waves along the rows
+  constexpr int FB = TM == 256 ? 2 : 1; // 32-column blocks per wave
+  const int wm = wave % WMN, wn = wave / WMN;
+  const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
+  // weight dequantization: column wc, codes 8 wq .. 8 wq + 7 of each chunk
+  const int wc = tid % TN;
+  const int wq = __builtin_amdgcn_readfirstlane(tid / TN);  // uniform within a wave
   const int64_t wcol = n0 + wc;
   const int64_t wcolc = wcol < out ? wcol : out - 1;  // in-bounds loads; columns >= out never stored
+  // the (at most two) words holding the thread's 8 codes: bits [8 wq B, 8 wq B + 8 B)
+  const int wbit = 8 * wq * B;
+  const int wlo = wbit / 32, woff = wbit % 32;
+  const bool two = woff + 8 * B > 32;  // uniform
   const int64_t nch_all = in / DQ_CHUNK;
   const int64_t cbeg = (int64_t)blockIdx.z * cps;
   const int64_t nch = cbeg + cps < nch_all ? cbeg + cps : nch_all;  // end of this split
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][FB];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < FB; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-  uint4 xr[2];        // X tile part: rows tid / 4 and tid / 4 + 64, k-octet tid % 4
-  uint32_t wr[B + 1]; // the weight words of column wc
-  int gA[16], gB[16]; // groups of the staged chunk's 16 k, and of the chunk after
+  constexpr int XI = TM / 128;
+  uint4 xr[XI];       // X tile part: rows tid / 4 + 128 i, k-octet tid % 4
+  uint32_t w0, w1;    // the weight words of column wc holding its 8 codes
+  int gA[8], gB[8];   // groups of the staged chunk's 8 k, and of the chunk after
   float sA;           // scale and zero of gA[0]
   int32_t zA;
   bool oneA;
   auto load_g = [&](int64_t c, int* g) {
     const int64_t cc = c < nch ? c : nch - 1;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) g[k] = g_idx[cc * DQ_CHUNK + 16 * wh + k];
+    for (int k = 0; k < 8; ++k) g[k] = g_idx[cc * DQ_CHUNK + 8 * wq + k];
   };
   auto fetch = [&](int64_t c) {
     const int64_t kb = c * DQ_CHUNK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = tid / 4 + 64 * i, o = 8 * (tid % 4);
+    for (int i = 0; i < XI; ++i) {
+      const int r = tid / 4 + 128 * i, o = 8 * (tid % 4);
       xr[i] = make_uint4(0u, 0u, 0u, 0u);
       if (m0 + r < M) xr[i] = *reinterpret_cast<const uint4*>(X + (m0 + r) * ldx + kb + o);
     }
-#pragma unroll
-    for (int i = 0; i < B; ++i) wr[i] = qw[(c * B + i) * out + wcolc];
-    wr[B] = 0u;
+    w0 = qw[(c * B + wlo) * out + wcolc];
+    w1 = two ? qw[(c * B + wlo + 1) * out + wcolc] : 0u;
     bool one = true;
 #pragma unroll
-    for (int k = 1; k < 16; ++k) one = one && gA[k] == gA[0];
+    for (int k = 1; k < 8; ++k) one = one && gA[k] == gA[0];
     oneA = one;
     sA = scales[(int64_t)gA[0] * out + wcolc];
     zA = zeros[(int64_t)gA[0] * out + wcolc];
   };
   auto stage = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = tid / 4 + 64 * i, o = 8 * (tid % 4);
+    for (int i = 0; i < XI; ++i) {
+      const int r = tid / 4 + 128 * i, o = 8 * (tid % 4);
       *reinterpret_cast<uint4*>(&Xs[buf][r * XP + o]) = xr[i];
     }
-    half2_t sh[8], zz[8];
+    half2_t sh[4], zz[4];
     if (oneA) {
       const half2_t s2 = {(_Float16)sA, (_Float16)sA};
       const half2_t z2 = {(_Float16)(1024.0f + (float)zA), (_Float16)(1024.0f + (float)zA)};
 #pragma unroll
-      for (int p = 0; p < 8; ++p) { sh[p] = s2; zz[p] = z2; }
+      for (int p = 0; p < 4; ++p) { sh[p] = s2; zz[p] = z2; }
     } else {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
+      for (int p = 0; p < 4; ++p) {
         const float s0 = scales[(int64_t)gA[2 * p] * out + wcolc];
         const float s1 = scales[(int64_t)gA[2 * p + 1] * out + wcolc];
         const float z0 = (float)zeros[(int64_t)gA[2 * p] * out + wcolc];
@@ -461,26 +469,20 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
         zz[p] = (half2_t){(_Float16)(1024.0f + z0), (_Float16)(1024.0f + z1)};
       }
     }
-    uint32_t packed[8];
-    // the code offset 16 wh as a constant: wr is indexed statically (registers)
-    auto deq = [&](auto half) {
-      constexpr int k0 = 16 * decltype(half)::value;
+    // the 8 codes: a 64-bit window of the column's stream starting at woff
+    const uint64_t win = (((uint64_t)w1 << 32) | w0) >> woff;
+    constexpr uint32_t mask = (1u << B) - 1u;
+    uint32_t packed[4];
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const uint32_t q2 = chunk_code<B>(wr, k0 + 2 * p) |
-                            (chunk_code<B>(wr, k0 + 2 * p + 1) << 16) | 0x64006400u;
-        const half2_t d = (__builtin_bit_cast(half2_t, q2) - zz[p]) * sh[p];
-        packed[p] = __builtin_bit_cast(uint32_t, d);
-      }
-    };
-    if (wh == 0)
-      deq(std::integral_constant<int, 0>());
-    else
-      deq(std::integral_constant<int, 1>());
-    *reinterpret_cast<uint4*>(&Ws[buf][wc * XP + 16 * wh]) =
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t q0 = (uint32_t)(win >> (2 * p * B)) & mask;
+      const uint32_t q1 = (uint32_t)(win >> ((2 * p + 1) * B)) & mask;
+      const uint32_t q2 = q0 | (q1 << 16) | 0x64006400u;
+      const half2_t d = (__builtin_bit_cast(half2_t, q2) - zz[p]) * sh[p];
+      packed[p] = __builtin_bit_cast(uint32_t, d);
+    }
+    *reinterpret_cast<uint4*>(&Ws[buf][wc * XP + 8 * wq]) =
         make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    *reinterpret_cast<uint4*>(&Ws[buf][wc * XP + 16 * wh + 8]) =
-        make_uint4(packed[4], packed[5], packed[6], packed[7]);
   };
 
   load_g(cbeg, gA);
@@ -493,26 +495,26 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
     const bool more = c + 1 < nch;  // uniform
     if (more) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) gA[k] = gB[k];
+      for (int k = 0; k < 8; ++k) gA[k] = gB[k];
       fetch(c + 1);
       load_g(c + 2, gB);
     }
 #pragma unroll
     for (int kk = 0; kk < DQ_CHUNK; kk += 16) {
       const int ko = kk + 8 * (lane >> 5);
-      half8_t af[2], bf[2];
+      half8_t af[2], bf[FB];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
         af[a] = *reinterpret_cast<const half8_t*>(
             &Xs[buf][(wm * 64 + a * 32 + (lane & 31)) * XP + ko]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < FB; ++b)
         bf[b] = *reinterpret_cast<const half8_t*>(
-            &Ws[buf][(wn * 64 + b * 32 + (lane & 31)) * XP + ko]);
+            &Ws[buf][(wn * 32 * FB + b * 32 + (lane & 31)) * XP + ko]);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < FB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
     if (more) stage(buf ^ 1);
@@ -523,11 +525,11 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < FB; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t r = m0 + wm * 64 + a * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int64_t cc = n0 + wn * 64 + b * 32 + (lane & 31);
+        const int64_t cc = n0 + wn * 32 * FB + b * 32 + (lane & 31);
         if (r < M && cc < out) {
           if (gridDim.z > 1)
             part[((int64_t)blockIdx.z * M + r) * out + cc] = acc[a][b][v];
@@ -541,9 +543,13 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
 
 // Splits of the input range for the tile kernel: about 512 workgroups, each
 // split at least 8 chunks.
+// 256-row tiles from this many tokens on (fewer: 128 rows, less padding).
+constexpr int64_t TM256_MIN_M = 256;
+inline int mfma_tile_rows(int64_t M) { return M >= TM256_MIN_M ? 256 : 128; }
 int64_t mfma_chunks_per_split(int64_t M, int64_t in, int64_t out) {
   const int64_t nch = in / DQ_CHUNK;
-  const int64_t tiles = ((out + TB - 1) / TB) * ((M + TB - 1) / TB);
+  const int TM = mfma_tile_rows(M);
+  const int64_t tiles = ((out + TN - 1) / TN) * ((M + TM - 1) / TM);
   int64_t ns = (512 + tiles - 1) / tiles;
   if (ns > nch / 8) ns = nch / 8;
   if (ns < 1) ns = 1;
@@ -740,13 +746,27 @@ hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
   const int64_t cps = mfma_chunks_per_split(M, in, out);
   const int64_t ns = (in / DQ_CHUNK + cps - 1) / cps;
   float* part = ns > 1 ? reinterpret_cast<float*>(wsp) : nullptr;
-  dim3 grid((unsigned)((out + TB - 1) / TB), (unsigned)((M + TB - 1) / TB), (unsigned)ns);
-  switch (bits) {
-    case 2: hipLaunchKernelGGL(dq_mfma_kernel<2>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, cps, part, Y, y_f16, ldy); break;
-    case 3: hipLaunchKernelGGL(dq_mfma_kernel<3>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, cps, part, Y, y_f16, ldy); break;
-    case 8: hipLaunchKernelGGL(dq_mfma_kernel<8>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, cps, part, Y, y_f16, ldy); break;
-    default: hipLaunchKernelGGL(dq_mfma_kernel<4>, grid, dim3(256), 0, s, x, M, in, ldx, qw, scales, zeros, g_idx, out, cps, part, Y, y_f16, ldy); break;
+  const int TM = mfma_tile_rows(M);
+  dim3 grid((unsigned)((out + TN - 1) / TN), (unsigned)((M + TM - 1) / TM), (unsigned)ns);
+#define GPTQ_DQ_MFMA(BB, TT)                                                                 \
+  hipLaunchKernelGGL((dq_mfma_kernel<BB, TT>), grid, dim3(512), 0, s, x, M, in, ldx, qw, scales, \
+                     zeros, g_idx, out, cps, part, Y, y_f16, ldy)
+  if (TM == 256) {
+    switch (bits) {
+      case 2: GPTQ_DQ_MFMA(2, 256); break;
+      case 3: GPTQ_DQ_MFMA(3, 256); break;
+      case 8: GPTQ_DQ_MFMA(8, 256); break;
+      default: GPTQ_DQ_MFMA(4, 256); break;
+    }
+  } else {
+    switch (bits) {
+      case 2: GPTQ_DQ_MFMA(2, 128); break;
+      case 3: GPTQ_DQ_MFMA(3, 128); break;
+      case 8: GPTQ_DQ_MFMA(8, 128); break;
+      default: GPTQ_DQ_MFMA(4, 128); break;
+    }
   }
+#undef GPTQ_DQ_MFMA
   GPTQ_HIP_TRY(hipGetLastError());
   if (ns > 1) {
     const int64_t total = M * out;
