@@ -251,6 +251,71 @@ def summarize_block(d: str):
     print("\n".join(lines))
 
 
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
+MFMA_PROFILE_COMMAND = ("rocprofv3 --pmc " + MFMA_COUNTERS + " -T -d {d}/MFMA -o p "
+                        "--output-format csv -- python -u bench.py --config {c} --steps 1 "
+                        "--warmup 1 --no-cpu-baseline")
+
+
+def summarize_mfma(cfg_name: str, d: str):
+    """profiles/layer_<config>_mfma_counters.md from the MFMA_PROFILE_COMMAND
+    run in d/MFMA: per kernel family of the timed step (the run's second),
+    the matrix cores' busy fraction, the fp16 MFMA work issued and the shader
+    clock.  The counters come summed over the 8 XCDs (GRBM_GUI_ACTIVE: 8 x the
+    active cycles) and the 1024 SIMDs (SQ_VALU_MFMA_BUSY_CYCLES)."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(d, "MFMA", "p_counter_collection.csv"))))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    syrk_ids = sorted({int(r["Dispatch_Id"]) for r in rows
+                       if r["Kernel_Name"].startswith("syrk_dma_kernel")})
+    first = syrk_ids[len(syrk_ids) // 2] if syrk_ids else 0
+    fam = {}
+    phase = "prepare"
+    for r in rows:
+        did = int(r["Dispatch_Id"])
+        if did < first:
+            continue
+        k = _kernel_base_name(r["Kernel_Name"])
+        if k.startswith("gather_w_kernel"):
+            phase = "quantize"
+        if k.startswith("syrk_"):
+            phase = "prepare"
+        name = k + (" (" + phase + ")" if k == "gemm_f32_dma" else "")
+        f = fam.setdefault(name, {"dur": {}, "busy": 0.0, "mops": 0.0, "gui": 0.0})
+        f["dur"][did] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        v = float(r["Counter_Value"])
+        key = {"SQ_VALU_MFMA_BUSY_CYCLES": "busy", "SQ_INSTS_VALU_MFMA_MOPS_F16": "mops",
+               "GRBM_GUI_ACTIVE": "gui"}.get(r["Counter_Name"])
+        if key:
+            f[key] += v
+    xcd, simds = 8, 1024
+    lines = [f"# rocprofv3 matrix-core counters: bench.py --config {cfg_name}", "",
+             "Command (run from the repository root on one MI355X):", "",
+             "    " + MFMA_PROFILE_COMMAND.format(d=d, c=cfg_name), "",
+             "Per kernel family, the dispatches of the run's timed step; time = the sum of the "
+             "dispatches' durations under the counters (kernels of the factorization overlap on "
+             "three streams).  Active cycles = GRBM_GUI_ACTIVE / 8 XCDs; MFMA util = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x 1024 SIMDs); fp16 MFMA work issued = "
+             "SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 (the split-fp32 GEMMs issue three fp16 products per "
+             "algorithmic one); clock = active cycles / time, meaningful for long kernels alone "
+             "on the GPU (the SYRK): for short or overlapping dispatches the counting window is "
+             "wider than the kernel.", "",
+             "| kernel | dispatches | ms | MFMA util | fp16 MFMA TFLOP issued | issued TFLOP/s | "
+             "clock GHz |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for name, f in sorted(fam.items(), key=lambda kv: -kv[1]["busy"]):
+        if f["busy"] <= 0 and f["mops"] <= 0:
+            continue
+        t = sum(f["dur"].values()) * 1e-9
+        act = f["gui"] / xcd
+        util = f["busy"] / max(act * simds, 1.0)
+        fl = f["mops"] * 512
+        lines.append(f"| {name} | {len(f['dur'])} | {t * 1e3:.3f} | {util:.3f} | {fl / 1e12:.3f} | "
+                     f"{fl / t / 1e12:.0f} | {act / t / 1e9:.2f} |")
+    with open(os.path.join(ROOT, "profiles", f"layer_{cfg_name}_mfma_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize(cfg_name: str, d: str):
     """Write the profiles/ summaries from rocprofv3 CSV output in d (the
     PROFILE_COMMANDS run with the default call size).  FETCH_SIZE and
@@ -881,6 +946,8 @@ def main():
                          "(default: all of them in one call)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="write the profiles/ summaries from rocprofv3 output in DIR and exit")
+    ap.add_argument("--mfma-counters", action="store_true",
+                    help="with --summarize: write the matrix-core counter summary instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dequant-tokens", type=int, default=None, metavar="M",
                     help="time gptq_dequant_matmul with M tokens on the config's packed layer "
@@ -902,6 +969,8 @@ def main():
             summarize_dequant(args.config, args.dequant_tokens, args.summarize)
         elif args.block:
             summarize_block(args.summarize)
+        elif args.mfma_counters:
+            summarize_mfma(args.config, args.summarize)
         else:
             summarize(args.config, args.summarize)
         return
