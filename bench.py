@@ -577,7 +577,7 @@ def dequant_cpu_baseline(cfg, M, words, scales, zeros, g_idx, x):
 def dequant_main(args):
     """--dequant-tokens M: gptq_dequant_matmul Y = X W^T (X fp16 [M x in], the
     packed layer of the config's shape and bit width, Y fp16) timed on its own.
-    Roofline: HBM for M <= 16 (algorithmic bytes = packed words + scales +
+    Roofline: HBM for M <= 8 (algorithmic bytes = packed words + scales +
     zeros + g_idx + X + Y), fp16 MFMA above (2 M in out flop)."""
     import torch
 
@@ -663,7 +663,7 @@ def dequant_main(args):
     G = scales.shape[0]
     alg_bytes = float(n * cfg.bits // 8 * out + 8 * G * out + 4 * n + 2 * M * n + 2 * M * out
                       + (4 * n if x_order is not None else 0))
-    small = M <= 16
+    small = M <= 8   # the library's few-token kernel
     if small:
         achieved, peak, unit, bound = alg_bytes / (call_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
         kernel = ("dq_small_kernel" + (" + dq_reduce_kernel" if wsb else ""))

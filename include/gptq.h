@@ -195,10 +195,10 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in,
 /* Workspace (bytes) gptq_dequant_matmul needs for M token rows, in inputs and
  * out outputs, with (has_order != 0) or without an x_order: the fp32 partial
  * sums when the input range is split over several workgroups (always for
- * M <= 16, e.g. 16 x 1 x 4096 for one token of a 4096 x 4096 layer; for
- * M > 16 when the output tiles alone would not fill the GPU), plus, for
- * M > 16 with an x_order, the gathered copy of X (M x in fp16).  0 when
- * neither applies (e.g. M = 2048 on a 4096 x 4096 layer). */
+ * M <= 8, e.g. 16 x 1 x 4096 for one token of a 4096 x 4096 layer; for
+ * M > 8 when the output tiles alone would not fill the GPU), plus, for
+ * M > 8 with an x_order, the gathered copy of X (M x in fp16).  0 when
+ * neither applies (e.g. M = 8192 on a 4096 x 4096 layer). */
 size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order);
 
 /*
@@ -226,8 +226,10 @@ size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, i
  *   workspace  device memory of gptq_dequant_matmul_workspace_bytes(M, in,
  *            out, x_order != NULL) bytes, or NULL when that is 0.
  *
- * Arithmetic: M <= 16 dequantizes each weight in fp32 and accumulates fp32
- * FMAs (HBM-bound on qweight); larger M rounds each dequantized weight to
+ * Arithmetic: M <= 8 (HBM-bound on qweight) takes each weight exactly:
+ * q - z as an fp16 integer times the fp16 activation, summed in fp32 over a
+ * 32-input chunk, times the group's fp32 scale (s (q - z) in fp32 per
+ * weight where a chunk mixes groups), fp32 accumulation; larger M rounds each dequantized weight to
  * fp16 (scale rounded to fp16, then one rounding of the product) and
  * multiplies on the fp16 matrix cores with fp32 accumulation.  Results do
  * not depend on timing.  Calls that share a workspace must not overlap.

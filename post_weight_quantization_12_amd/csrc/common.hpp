@@ -120,7 +120,7 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
 // the split input range's partial sums), more the MFMA tiles.
 // With x_order, packed position p reads input column x_order[p]; the
 // matrix-core path gathers X into its workspace first.
-constexpr int DQ_SMALL_M_MAX = 16;
+constexpr int DQ_SMALL_M_MAX = 8;  // measured: the tiles win from 9 tokens on
 size_t dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order);
 hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
                               const int32_t* qweight, const float* scales, const int32_t* zeros,

@@ -11,11 +11,11 @@
 // walks the input dimension 32 k at a time, whatever b is.
 //
 // Two kernels:
-//   * few tokens (M <= 16, decode): HBM-bound on qweight.  Lane = output
+//   * few tokens (M <= 8, decode): HBM-bound on qweight.  Lane = output
 //     column (a wave's 64 columns read 256 contiguous bytes per word row),
 //     the four waves of a workgroup take interleaved chunks of the
 //     workgroup's input range; per chunk, exact (q - z) code pairs in fp16
-//     meet X pairs in v_dot2_f32_f16 (fp32 sums, up to 16 token rows held
+//     meet X pairs in v_dot2_f32_f16 (fp32 sums, up to 8 token rows held
 //     in registers) and the sum is scaled once; X's slice of the input range
 //     is staged in LDS as fp16 pairs.  The input dimension is split over
 //     several workgroups (grid >= 2 per compute unit); their partial sums go
@@ -92,7 +92,7 @@ __host__ __device__ constexpr uint32_t pair_mask() {
 // lane l of every wave owns the CPL adjacent columns from 64 CPL bx + CPL l
 // (CPL = 4: one 16-byte load per word row), and the four waves take
 // interleaved chunks of the range.  MB = token rows held per lane (>= M, a
-// power of two up to 16).
+// power of two up to 8).
 // LDS: xp[pair][MB], the X slice as fp16 pairs in the chunks' pair order
 // (pair p of chunk c at 16 c + p), then cg[cps]: the group of each chunk of
 // the slice when all its 32 k share one, else -1.
@@ -621,7 +621,7 @@ struct SmallPlan {
 // it is taken for up to 4 token rows.
 SmallPlan small_plan(int64_t M, int64_t in, int64_t out, int cpl) {
   SmallPlan p;
-  p.mb = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+  p.mb = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
   p.cpl = cpl;
   const int64_t nch = in / DQ_CHUNK;
   const int64_t cols = 64 * (int64_t)cpl;
@@ -675,8 +675,7 @@ hipError_t launch_small_b(const SmallPlan& p, const _Float16* X, int64_t M, int6
     case 1: return launch_small_t<B, 1, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
     case 2: return launch_small_t<B, 2, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
     case 4: return launch_small_t<B, 4, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
-    case 8: return launch_small_t<B, 8, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
-    default: return launch_small_t<B, 16, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
+    default: return launch_small_t<B, 8, 1>(p, X, M, in, ldx, qw, scales, zeros, g_idx, xo, out, part, Y, y_f16, ldy, s);
   }
 }
 

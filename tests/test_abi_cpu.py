@@ -143,7 +143,8 @@ def test_dequant_matmul_argument_errors(lib):
     assert call(X=ctypes.c_void_p(4098)) == L.GPTQ_ERR_UNSUPPORTED
     # the small-M path splits the input range: a workspace is required
     need = lib.gptq_dequant_matmul_workspace_bytes(1, 4096, 4096, 0)
-    assert need > 0 and lib.gptq_dequant_matmul_workspace_bytes(2048, 4096, 4096, 0) == 0
+    # 8192 tokens: 32 x 32 tiles of 256 x 128 fill the GPU, no split, no workspace
+    assert need > 0 and lib.gptq_dequant_matmul_workspace_bytes(8192, 4096, 4096, 0) == 0
     # 64 tokens: 32 output tiles, the input range split for the rest of the GPU
     assert lib.gptq_dequant_matmul_workspace_bytes(64, 4096, 4096, 0) >= 2 * 64 * 4096 * 4
     assert lib.gptq_dequant_matmul_workspace_bytes(0, 4096, 4096, 0) == 0

@@ -5,7 +5,7 @@ Tolerance, per entry: |Y - Y_o| <= (2^-10 + in 2^-23) sum_k |x_k w_k| + 1e-6
 (+ 2^-11 |Y_o| for fp16 output).  2^-10 covers rounding the dequantized
 weight to fp16 on the matrix-core path (the scale rounded to fp16, then the
 product: two roundings of 2^-11); in 2^-23 bounds fp32 accumulation over in
-terms.  The M <= 16 path dequantizes in fp32 and meets the same bound with
+terms.  The M <= 8 path takes q - z exactly and meets the same bound with
 room to spare.  Results must be identical run to run.
 """
 import numpy as np
