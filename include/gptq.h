@@ -13,6 +13,13 @@
  *   gptq_prepare              damp, order, factor   -> Hinv_chol, perm
  *   gptq_quantize_layer       sweep + pack          -> qweight, scales, zeros, g_idx
  *
+ * and around it:
+ *   gptq_dequant_matmul       Y = X W^T from the packed layer (dequantized on the fly)
+ *   gptq_dequant_group_order  act-order layer -> group-sorted copy + x_order (once)
+ *   gptq_silu_mul             gated activation between the MLP layers of a block
+ *   gptq_export_params        fp16 scales + b-bit packed zeros, for saving
+ *   gptq_unpack_zeros         zeros from their packed form, after loading
+ *
  * Conventions shared by every call
  *   - Every array argument is DEVICE memory owned by the caller (HIP device
  *     pointers), row-major, densely packed unless a leading dimension is given.
