@@ -218,3 +218,30 @@ def test_group_order_full_size_sampled():
     assert np.array_equal(gsrt.cpu().numpy(), gs_o)
     assert np.array_equal(qs[:, cols].cpu().numpy(), qs_o)
     _check(X, qw_d.cpu().numpy(), sc_d.cpu().numpy(), z_d.cpu().numpy(), g_idx, bits, Y, cols)
+
+
+def test_prefill_full_size_sampled():
+    """2048 tokens through the 4096 x 11008 act-order layer (group-ordered), as
+    timed: 256 x 128 tiles with a split input range; sampled columns against
+    the oracle on the layer as packed."""
+    out, inp, bits, gs = 4096, 11008, 4, 128
+    _banner(f"prefill full size M=2048 out={out} in={inp} {bits}b g{gs}")
+    rng = np.random.default_rng(91)
+    g_idx = O.g_index(rng.permutation(inp), gs).astype(np.int32)
+    G = inp // gs
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    qw_d = torch.randint(-2 ** 31, 2 ** 31 - 1, (inp * bits // 32, out), generator=gen,
+                         device=DEV, dtype=torch.int64).to(torch.int32)
+    sc_d = 1e-3 + 4.9e-2 * torch.rand((G, out), generator=gen, device=DEV)
+    z_d = torch.randint(0, 2 ** bits, (G, out), generator=gen, device=DEV, dtype=torch.int32)
+    g_d = torch.from_numpy(g_idx).to(DEV)
+    qs, gsrt, order = P.dequant_group_order(qw_d, g_d, bits)
+    X = torch.randn((2048, inp), generator=torch.Generator().manual_seed(10)).to(torch.float16)
+    Y = P.dequant_matmul(X.to(DEV), qs, sc_d, z_d, gsrt, bits, x_order=order,
+                         out_dtype=torch.float16)
+    Y2 = P.dequant_matmul(X.to(DEV), qs, sc_d, z_d, gsrt, bits, x_order=order,
+                          out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+    cols = np.unique(np.concatenate([[0, 127, 128, out - 1], rng.choice(out, 28, replace=False)]))
+    _check(X, qw_d.cpu().numpy(), sc_d.cpu().numpy(), z_d.cpu().numpy(), g_idx, bits, Y, cols)
