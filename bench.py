@@ -357,8 +357,11 @@ def summarize(cfg_name: str, d: str):
     for name, ds in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| {name} | {len(ds)} | {sum(ds) / 1e6:.3f} | {sum(ds) / len(ds) / 1e3:.2f} | "
                      f"{min(ds) / 1e3:.2f} | {max(ds) / 1e3:.2f} |")
+    timed = [r for r in trace if int(r["Start_Timestamp"]) >= t_timed]
     lines += ["", "## Per-stage roofline (timed steps, mean per step)", ""] + stage_roofline(
-        cfg, [r for r in trace if int(r["Start_Timestamp"]) >= t_timed])
+        cfg, timed)
+    lines += ["", "## HBM traffic per stage (rocprofv3 FETCH_SIZE + WRITE_SIZE)", ""] + \
+        stage_traffic(cfg, d, timed)
     with open(os.path.join(ROOT, "profiles", f"layer_{cfg_name}_kernel_stats.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -490,6 +493,72 @@ def stage_roofline(cfg, rows):
                  "7 out in + 8 out in / gs bytes, a5 out in (in - B), a6 out in (1 + b/8) bytes. "
                  "MFMA pipe: fp16 MFMA work actually issued (three products per split-fp32 "
                  "product) over the fp16 peak.")
+    return lines
+
+
+def _stage_of(kernel_base: str, phase: str):
+    key = "gemm_f32_dma@" + phase if kernel_base.startswith("gemm_f32_dma") else kernel_base
+    for name, ks in STAGES:
+        if any(x in key for x in ks):
+            return name
+    return None
+
+
+def stage_traffic(cfg, d, timed_trace):
+    """Markdown lines: per stage, the HBM bytes the counters saw in the timed
+    step (the second step of the FETCH_SIZE / WRITE_SIZE runs; each counter
+    scaled by what it reads for a 1 GiB copy) and those bytes over the
+    stage's kernel time per step from the trace."""
+    import csv
+    GiB = 1 << 30
+    tot = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = list(csv.DictReader(open(os.path.join(d, ctr, "p_counter_collection.csv"))))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        ids = [int(r["Dispatch_Id"]) for r in rows if r["Kernel_Name"].startswith("syrk_dma_kernel")]
+        first = ids[len(ids) // 2] if ids else 0
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        factor = (GiB / 1024) / copy
+        phase = "prepare"
+        for r in rows:
+            if int(r["Dispatch_Id"]) < first:
+                continue
+            k = _kernel_base_name(r["Kernel_Name"])
+            if k.startswith("gather_w_kernel"):
+                phase = "quantize"
+            if k.startswith("syrk_"):
+                phase = "prepare"
+            st = _stage_of(k, phase)
+            if st:
+                tot.setdefault(st, [0.0, 0.0])[0 if ctr == "FETCH_SIZE" else 1] += \
+                    float(r["Counter_Value"]) * 1024 * factor
+    # kernel time per stage and step (as in the roofline table)
+    steps = sum(1 for r in timed_trace if r["Kernel_Name"].startswith("syrk_dma_kernel")) or 1
+    if cfg.tokens > 32768 and steps > 2:
+        steps = max(1, steps // ((cfg.tokens + 32767) // 32768))
+    tt = {}
+    phase = "prepare"
+    for r in sorted(timed_trace, key=lambda r: int(r["Start_Timestamp"])):
+        k = _kernel_base_name(r["Kernel_Name"])
+        if k.startswith("gather_w_kernel"):
+            phase = "quantize"
+        if k.startswith("syrk_"):
+            phase = "prepare"
+        st = _stage_of(k, phase)
+        if st:
+            tt[st] = tt.get(st, 0) + int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    lines = ["| stage | fetched MB | written MB | kernel ms | measured HBM GB/s | frac of 8 TB/s |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for name, _ in STAGES:
+        if name not in tot or name not in tt:
+            continue
+        f, w = tot[name]
+        t = tt[name] / steps * 1e-9
+        lines.append(f"| {name} | {f / 1e6:.1f} | {w / 1e6:.1f} | {t * 1e3:.3f} | "
+                     f"{(f + w) / t / 1e9:.0f} | {(f + w) / t / 1e9 / PEAK_HBM_GBS:.3f} |")
+    lines.append("")
+    lines.append("FETCH_SIZE counts L2 misses sent to the memory side (some are served by the "
+                 "Infinity Cache), so these are upper bounds on DRAM bytes.")
     return lines
 
 
