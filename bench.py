@@ -615,6 +615,36 @@ def cpu_baseline(cfg, steps_tokens: int):
     }
 
 
+def layer_roofline(cfg, hess_ms: float, prep_ms: float, quant_ms: float) -> dict:
+    """Whole-layer roofline: the sum of the stages' ideal times at their
+    bounds (a1 N n(n+1) flop and a5 out in (in - B) flop at the fp16 MFMA
+    peak, a3 2 n^3 / 3 flop at the fp32 peak, a2 8 n^2 + 6 out in, a4
+    7 out in + 8 out in / gs and a6 out in (1 + b/8) bytes at the HBM peak)
+    over the measured time, with and without the Hessian."""
+    n, out, b = cfg.inp, cfg.out, cfg.bits
+    gs = n if cfg.group_size == -1 else cfg.group_size
+    f16, f32, hbm = PEAK_FP16_TFLOPS * 1e12, PEAK_FP32_TFLOPS * 1e12, PEAK_HBM_GBS * 1e9
+    ideal = {
+        "a1": float(cfg.tokens) * n * (n + 1) / f16,
+        "a2": (8.0 * n * n + 6.0 * out * n) / hbm,
+        "a3": 2.0 * n ** 3 / 3 / f32,
+        "a4": (7.0 * out * n + 8.0 * out * n / gs) / hbm,
+        "a5": float(out) * n * (n - cfg.block) / f16,
+        "a6": out * n * (1 + b / 8.0) / hbm,
+    }
+    t_layer = sum(v for k, v in ideal.items() if k != "a1")
+    t_all = t_layer + ideal["a1"]
+    return {
+        "ideal_ms": {k: v * 1e3 for k, v in ideal.items()},
+        "layer_ideal_ms": t_layer * 1e3,
+        "layer_ms": prep_ms + quant_ms,
+        "layer_frac": t_layer * 1e3 / (prep_ms + quant_ms),
+        "step_ideal_ms": t_all * 1e3,
+        "step_ms": hess_ms + prep_ms + quant_ms,
+        "step_frac": t_all * 1e3 / (hess_ms + prep_ms + quant_ms),
+    }
+
+
 def dequant_cpu_baseline(cfg, M, words, scales, zeros, g_idx, x):
     """The oracle's dequant_matmul, untuned, on a column sample of the layer
     (the first `cols` output columns, all M tokens), scaled to all columns."""
@@ -1184,6 +1214,7 @@ def main():
         "stage_ms": {"hessian": mean(hess_ms), "prepare": mean(prep_ms),
                      "quantize": mean(quant_ms)},
         "layer_weights_per_s": weights / (layer_ms * 1e-3),
+        "layer_roofline": layer_roofline(cfg, mean(hess_ms), mean(prep_ms), mean(quant_ms)),
         "roofline": {
             "kernel": f"{kernels} = one gptq_hessian_accumulate call",
             "kernel_launches_per_call": launches,
