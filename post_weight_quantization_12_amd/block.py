@@ -39,9 +39,14 @@ def quantize_mlp_block(X, Wg, Wu, Wd, bits: int, group_size: int, sym: bool, dam
     [d x inter] (fp16 or fp32).  The calibration tokens go through the block
     in chunks of chunk_tokens (the activations of one chunk live at a time).
     mark: optional callable, called with a phase name at each phase boundary
-    (e.g. to record timing events on the stream)."""
+    (e.g. to record timing events on the stream).  stream: the stream of the
+    library calls; the buffers this function allocates, clears and joins
+    with torch are ordered on torch's current stream, so pass that stream
+    (None: the current stream's handle is taken)."""
     torch = L._torch()
     mark = mark or (lambda name: None)
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
     dev = X.device
     ntok, d = X.shape
     inter = Wg.shape[0]
