@@ -434,6 +434,22 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
     }
   };
 
+  // Trailing update of the lower part after the panel of columns cp..cp+15,
+  // one 16 x 16 tile (ti, tj) on the matrix cores:
+  //     A[r][s] -= sum_q L[r][cp+q] L[s][cp+q]   (r >= s >= cp + 16)
+  auto tile_update = [&](int cp, int ti, int tj) {
+    const int base = cp + 16;
+    float* C = Ls + (base + 16 * ti) * LP + base + 16 * tj;
+    f32x4_t acc = load_tile(C, lane);
+    acc = tile16<true, 16>(Ls + (base + 16 * ti) * LP + cp, Ls + (base + 16 * tj) * LP + cp, acc,
+                           -1.0f, lane);
+    store_tile(C, acc, lane);
+  };
+
+  // Right-looking over 16-column steps with a lookahead of one: each step's
+  // trailing update is split into the next column block (tj = 0), which the
+  // next diagonal block and panel need at once, and the rest, which waves
+  // 1.. apply while wave 0 factors the next diagonal block.
 #pragma unroll 1
   for (int step = 0; step < NSTEP; ++step) {
     const int c = 16 * step;
@@ -482,9 +498,18 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
 #pragma unroll
         for (int k = 0; k < 16; ++k) rinv_s[c + k] = rv[k];
       }
+    } else if (step > 0) {
+      // (c2) the previous step's update beyond its next column block:
+      // tiles 1 <= tj <= ti < nt, over waves 1..
+      const int cp = c - 16, nt = (NB - cp - 16) / 16;
+      for (int t = wave - 1; t < (nt - 1) * nt / 2; t += LEAF_THREADS / 64 - 1) {
+        int u = 0;
+        while ((u + 1) * (u + 2) / 2 <= t) ++u;
+        tile_update(cp, u + 1, t - u * (u + 1) / 2 + 1);
+      }
     }
     __syncthreads();
-      const int rows = NB - c - 16;
+    const int rows = NB - c - 16;
     if (rows > 0) {
       // (b) L[i][c+j] = (A[i][c+j] - sum_{q<j} L[i][c+q] L[c+j][c+q]) / L[c+j][c+j]
       if (tid < rows) {
@@ -508,23 +533,10 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
           *reinterpret_cast<float4*>(row + q) = make_float4(x[q], x[q + 1], x[q + 2], x[q + 3]);
       }
       __syncthreads();
-          // (c) trailing update of the lower part, 16 x 16 tiles on the matrix cores:
-      //     A[r][s] -= sum_q L[r][c+q] L[s][c+q]   (r >= s >= c + 16)
-      {
-        const int nt = rows / 16, base = c + 16;
-        for (int t = wave; t < nt * (nt + 1) / 2; t += LEAF_THREADS / 64) {
-          int ti = 0;
-          while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-          const int tj = t - ti * (ti + 1) / 2;
-          float* C = Ls + (base + 16 * ti) * LP + base + 16 * tj;
-          f32x4_t acc = load_tile(C, lane);
-          acc = tile16<true, 16>(Ls + (base + 16 * ti) * LP + c, Ls + (base + 16 * tj) * LP + c,
-                                 acc, -1.0f, lane);
-          store_tile(C, acc, lane);
-        }
-      }
+      // (c1) this step's update of the next column block: tiles (ti, 0)
+      for (int t = wave; t < rows / 16; t += LEAF_THREADS / 64) tile_update(c, t, 0);
       __syncthreads();
-        }
+    }
   }
   static_assert(NSTEP <= LEAF_THREADS / 64, "one diagonal block per wave");
   if (wave < NSTEP) invert_block(wave);
