@@ -488,47 +488,46 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out
   const int64_t row = row0 + rl;
   const bool live = row < out;
 
-  // Pre-shifted U' window.  Item (j, t, h): the float4 of block columns
-  // 16(j/16 + t) + 4h .. +3 of U' row c0 + j, spread to lanes 4h .. 4h+3;
-  // columns not right of j are stored as 0.
-  {
-    constexpr int ITEMS = B * NR * 4;
-    constexpr int PER = ITEMS / S16_THREADS;
-    static_assert(ITEMS % S16_THREADS == 0, "whole items per thread");
-#pragma unroll
-    for (int p0 = 0; p0 < PER; p0 += 4) {
-      float4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = tid + (p0 + u) * S16_THREADS;
-        const int j = e / (NR * 4), t = (e / 4) % NR, h = e % 4;
-        const int c = 16 * (j / 16 + t) + 4 * h;
-        v[u] = (p0 + u < PER && j < width && c < width)
-                   ? *reinterpret_cast<const float4*>(Up + (c0 + j) * in + c0 + c)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (p0 + u < PER) {
-          const int e = tid + (p0 + u) * S16_THREADS;
-          const int j = e / (NR * 4), t = (e / 4) % NR, h = e % 4;
-          const int c = 16 * (j / 16 + t) + 4 * h;
-          float* d = Ul + (j * 16 + 4 * h) * PITCH + t;
-          d[0 * PITCH] = c + 0 > j ? v[u].x : 0.0f;
-          d[1 * PITCH] = c + 1 > j ? v[u].y : 0.0f;
-          d[2 * PITCH] = c + 2 > j ? v[u].z : 0.0f;
-          d[3 * PITCH] = c + 3 > j ? v[u].w : 0.0f;
-        }
-      }
-    }
-  }
-
+  // This lane's columns of its row (issued first: their HBM latency overlaps
+  // the U' loads below).
   float w[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int col = 16 * r + q;
     w[r] = (live && col < width) ? Wp[row * in + c0 + col] : 0.0f;
   }
+
+  // Pre-shifted U' window.  Item (j, t, h): the float4 of block columns
+  // 16(j/16 + t) + 4h .. +3 of U' row c0 + j, spread to lanes 4h .. 4h+3;
+  // columns not right of j are stored as 0.  All of a thread's loads are in
+  // flight together (one round trip, not one per batch).
+  {
+    constexpr int ITEMS = B * NR * 4;
+    constexpr int PER = ITEMS / S16_THREADS;
+    static_assert(ITEMS % S16_THREADS == 0, "whole items per thread");
+    float4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * S16_THREADS;
+      const int j = e / (NR * 4), t = (e / 4) % NR, h = e % 4;
+      const int c = 16 * (j / 16 + t) + 4 * h;
+      v[u] = (j < width && c < width)
+                 ? *reinterpret_cast<const float4*>(Up + (c0 + j) * in + c0 + c)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + u * S16_THREADS;
+      const int j = e / (NR * 4), t = (e / 4) % NR, h = e % 4;
+      const int c = 16 * (j / 16 + t) + 4 * h;
+      float* d = Ul + (j * 16 + 4 * h) * PITCH + t;
+      d[0 * PITCH] = c + 0 > j ? v[u].x : 0.0f;
+      d[1 * PITCH] = c + 1 > j ? v[u].y : 0.0f;
+      d[2 * PITCH] = c + 2 > j ? v[u].z : 0.0f;
+      d[3 * PITCH] = c + 3 > j ? v[u].w : 0.0f;
+    }
+  }
+
   const float maxq = (float)((1 << bits) - 1);
   float s = 1.0f, z = 0.0f;
   if constexpr (GS == 0) {
@@ -540,16 +539,20 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out
   float rs = 1.0f / s;
   __syncthreads();
 
-  // U' row of the column being swept, loaded one column ahead so the LDS
-  // latency stays off the column-to-column dependency chain.
-  constexpr int NU = (NR + 3) / 4;
-  auto load_u = [&](int j, float4* dst) {
-    const float* urow = Ul + (j * 16 + q) * PITCH;
+  // U' rows of the step's 16 columns, each replaced by the same column of
+  // the next step once used, so the LDS latency (16 columns ahead) stays off
+  // the column-to-column dependency chain.  (Widths are multiples of 16.)
+  constexpr int NU = (NR + 3) / 4, COL = 16 * PITCH;  // floats per column
+  const float* ulane = Ul + q * PITCH;
+  auto load_u = [&](const float* urow, float4* dst) {
 #pragma unroll
     for (int t = 0; t < NU; ++t) dst[t] = *reinterpret_cast<const float4*>(urow + 4 * t);
   };
-  float4 ub[NU];
-  load_u(0, ub);
+  float4 ur[16][NU];
+  if (width >= 16) {
+#pragma unroll
+    for (int o = 0; o < 16; ++o) load_u(ulane + o * COL, ur[o]);
+  }
 
   const int nsteps = width / 16;
   for (int R = 0; R < nsteps; ++R) {
@@ -574,41 +577,64 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out
       }
     }
     float my_err = 0.0f, my_code = 0.0f;  // this lane's column of the step
+    // rint(wj / s) with the quotient correctly rounded, without the division
+    // on the column-to-column dependency chain: y = wj * (1/s) is within
+    // |y| 2^-22 of the rounded quotient, so rint(y) is the same integer
+    // unless y lies that close to a half-integer (|y - rint(y)| +
+    // |y| 2^-20 >= 1/2 flags it, with margin for the rounding of that test),
+    // or 1/s is zero or not finite.  A flag only raises the step's maximum;
+    // after the 16 columns a wave with a flag sweeps them again from the
+    // saved state with true divisions (a branch per column on the chain cost
+    // about a third of the sweep).  Non-finite w gives the same code either
+    // way.
+    float w_in[NR];
 #pragma unroll
-    for (int o = 0; o < 16; ++o) {
-      const int j = 16 * R + o;
-      float4 un[NU];
+    for (int t = 0; t < NR; ++t) w_in[t] = w[t];
+    float flag = fabsf(rs) < INFINITY && rs != 0.0f ? 0.0f : 1.0f;
+    // next step's rows (past the last step: rows in range, not used)
+    const float* unext = ulane + (R + 1 < nsteps ? 16 * (R + 1) * COL : 0);
+    auto columns = [&](const bool exact) {
 #pragma unroll
-      for (int t = 0; t < NU; ++t) un[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (o < 15 || j + 1 < width) load_u(j + 1, un);
-      const float wj = row_bcast16(w[0], o);
-      // rint(wj / s) with the quotient correctly rounded, without the
-      // division on the dependency chain: y = wj * (1/s) is within
-      // |y| 2^-22 of the rounded quotient, so rint(y) is the same integer
-      // unless y lies that close to a half-integer; those rare lanes (and a
-      // zero or non-finite s) divide.
-      const float y = wj * rs;
-      const float qr = rintf(y);
-      // clamp(qr + z, 0, maxq) - z in one step (small integers: exact)
-      float qz = __builtin_amdgcn_fmed3f(qr, -z, maxq - z);
-      float err = wj - s * qz;
-      if (!(0.5f - fabsf(y - qr) >= fabsf(y) * 0x1p-21f + 0x1p-126f)) {
-        qz = __builtin_amdgcn_fmed3f(rintf(wj / s), -z, maxq - z);
-        err = wj - s * qz;
+      for (int o = 0; o < 16; ++o) {
+        float4 ub[NU];
+        if (exact) {
+          load_u(ulane + (16 * R + o) * COL, ub);  // the ring holds the next step
+        } else {
+#pragma unroll
+          for (int t = 0; t < NU; ++t) ub[t] = ur[o][t];
+          load_u(unext + o * COL, ur[o]);
+        }
+        const float wj = row_bcast16(w[0], o);
+        float qz;
+        if (exact) {
+          qz = __builtin_amdgcn_fmed3f(rintf(wj / s), -z, maxq - z);
+        } else {
+          const float y = wj * rs;
+          const float qr = rintf(y);
+          // clamp(qr + z, 0, maxq) - z in one step (small integers: exact)
+          qz = __builtin_amdgcn_fmed3f(qr, -z, maxq - z);
+          flag = fmaxf(flag, fmaf(fabsf(y), 0x1p-20f, fabsf(y - qr)));
+        }
+        const float err = wj - s * qz;
+        my_err = q == o ? err : my_err;
+        my_code = q == o ? qz : my_code;
+#pragma unroll
+        for (int t = 0; t < NR; t += 4) {
+          const float4 u = ub[t / 4];
+          w[t + 0] = fmaf(-err, u.x, w[t + 0]);
+          if (t + 1 < NR) w[t + 1] = fmaf(-err, u.y, w[t + 1]);
+          if (t + 2 < NR) w[t + 2] = fmaf(-err, u.z, w[t + 2]);
+          if (t + 3 < NR) w[t + 3] = fmaf(-err, u.w, w[t + 3]);
+        }
       }
-      my_err = q == o ? err : my_err;
-      my_code = q == o ? qz + z : my_code;
+    };
+    columns(false);
+    if (__builtin_amdgcn_ballot_w64(flag >= 0.5f) != 0) {
 #pragma unroll
-      for (int t = 0; t < NR; t += 4) {
-        const float4 u = ub[t / 4];
-        w[t + 0] = fmaf(-err, u.x, w[t + 0]);
-        if (t + 1 < NR) w[t + 1] = fmaf(-err, u.y, w[t + 1]);
-        if (t + 2 < NR) w[t + 2] = fmaf(-err, u.z, w[t + 2]);
-        if (t + 3 < NR) w[t + 3] = fmaf(-err, u.w, w[t + 3]);
-      }
-#pragma unroll
-      for (int t = 0; t < NU; ++t) ub[t] = un[t];
+      for (int t = 0; t < NR; ++t) w[t] = w_in[t];
+      columns(true);
     }
+    my_code += z;
     Es[rl * EP + 16 * R + q] = my_err;
     Cs[rl * B + 16 * R + q] = (uint8_t)my_code;
 #pragma unroll

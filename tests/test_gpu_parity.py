@@ -235,6 +235,59 @@ def test_h_identity_reduces_to_rtn_bit_exact(bits, gs, sym, block, wdt):
     assert np.array_equal(gi.cpu().numpy(), r.g_idx)
 
 
+@pytest.mark.parametrize("bits,gs,block", [(4, 128, 128), (3, 32, 64), (2, -1, 128),
+                                            (8, 32, 32)])
+def test_sweep_near_half_quotients_bit_exact(bits, gs, block):
+    """Weights at (k + 1/2) s and their fp32 neighbours, where rint(w * (1/s))
+    can differ from rint(w / s): the sweep must decide every code as the
+    correctly rounded fp32 quotient would (the redo path of a flagged step).
+    H = I, so nothing propagates and each code is clamp(rint(w / s) + z)
+    with the layer's own scales and zeros."""
+    _banner(f"near-half quotients bits={bits} gs={gs} block={block}")
+    out, inp = 64, 256
+    g = gs if gs > 0 else inp
+    G = inp // g
+    maxq = (1 << bits) - 1
+    rng = np.random.default_rng(11)
+    W0 = np.zeros((out, inp), np.float32)
+    lo = -rng.uniform(0.5, 2.0, (out, G)).astype(np.float32)
+    hi = rng.uniform(0.5, 2.0, (out, G)).astype(np.float32)
+    W0[:, 0::g] = lo
+    W0[:, 1::g] = hi
+    U, perm, info = P.prepare(torch.eye(inp, device=DEV), 0.01, False)
+    _, sc, zr, _ = P.quantize_layer(torch.from_numpy(W0).to(DEV), U, perm, bits, gs, False, block)
+    s = sc.cpu().numpy()
+    z = zr.cpu().numpy().astype(np.float32)
+    # interior columns: ties k + 1/2 (times s, rounded to fp32) nudged by -1, 0
+    # or +1 ulp, kept inside the group's range so the scales do not move
+    W1 = W0.copy()
+    cols = np.array([c for c in range(inp) if c % g > 1])
+    gi = cols // g
+    sr = s[gi, :].T  # [out, ncols]
+    zz = z[gi, :].T
+    k = rng.integers(0, maxq, (out, cols.size)).astype(np.float32) - zz
+    t = ((k + np.float32(0.5)) * sr).astype(np.float32)
+    nudge = rng.integers(-1, 2, t.shape)
+    t = np.where(nudge < 0, np.nextafter(t, np.float32(-np.inf)),
+                 np.where(nudge > 0, np.nextafter(t, np.float32(np.inf)), t)).astype(np.float32)
+    t = np.clip(t, lo[:, gi], hi[:, gi])
+    W1[:, cols] = t
+    qw, sc1, zr1, _ = P.quantize_layer(torch.from_numpy(W1).to(DEV), U, perm, bits, gs, False,
+                                       block)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    assert np.array_equal(sc1.cpu().numpy(), s) and np.array_equal(zr1.cpu().numpy(), zr.cpu().numpy())
+    sfull = np.repeat(s.T, g, axis=1)
+    zfull = np.repeat(z.T, g, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ref = np.clip(np.rint(W1 / sfull) + zfull, 0, maxq)
+    got = gpu_codes(qw, bits, inp)
+    assert np.array_equal(got, ref.astype(got.dtype))
+    # the fast reciprocal path alone would have missed some of these
+    recip = np.clip(np.rint(W1 * (np.float32(1) / sfull)) + zfull, 0, maxq)
+    print("   codes where rint(w * (1/s)) differs:", int(np.sum(recip != ref)))
+
+
 def _gpu_chain(W, X, n, bits, gs, sym, damp, desc, block):
     H = _hessian_gpu([X], n)
     U, perm, info = P.prepare(H, damp, desc)
