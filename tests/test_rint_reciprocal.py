@@ -1,10 +1,11 @@
 """The sweep kernel decides q = rint(w / s) (fp32 quotient, correctly rounded)
-as rint(w * (1/s)) unless w * (1/s) lies within |y| 2^-21 of a half-integer,
-where it divides.  This checks the claim behind it on the CPU with IEEE fp32
-arithmetic (NumPy): whenever the fast test passes, the two integers agree.
-The check emulates the kernel's instruction sequence: y = fl(w * r) with
-r = fl(1 / s); t = fl(w * r - rint(y)) (one fused rounding); the distance
-0.5 - |t| against fl(|y| 2^-21 + 2^-126) (one fused rounding).
+as rint(w * (1/s)) unless w * (1/s) lies near a half-integer (or 1/s is zero
+or not finite); such a step is swept again with true divisions.  This checks
+the claim behind it on the CPU with IEEE fp32 arithmetic (NumPy): whenever
+the fast test passes, the two integers agree.  The check emulates the
+kernel's instruction sequence: y = fl(w * r) with r = fl(1 / s);
+t = fl(w * r - rint(y)) (one fused rounding); m = fl(|y| 2^-20 + |t|) (one
+fused rounding); the fast path stands when m < 1/2.
 """
 import numpy as np
 
@@ -16,9 +17,8 @@ def fast_decision(w, s):
     y = (w * r).astype(f32)
     qr = np.rint(y)
     t = (w.astype(np.float64) * r.astype(np.float64) - qr.astype(np.float64)).astype(f32)
-    dist = (f32(0.5) - np.abs(t)).astype(f32)
-    delta = (np.abs(y).astype(np.float64) * 2.0 ** -21 + 2.0 ** -126).astype(f32)
-    ok = dist >= delta
+    m = (np.abs(y).astype(np.float64) * 2.0 ** -20 + np.abs(t).astype(np.float64)).astype(f32)
+    ok = (m < f32(0.5)) & np.isfinite(r) & (r != 0)
     return qr, ok
 
 
@@ -54,3 +54,13 @@ def test_ties_and_neighbours_take_the_division():
         # exact ties in the quotient never pass the fast test
         tie = (w / s).astype(f32) == (k + f32(0.5))
         assert not np.any(ok & tie)
+
+
+def test_degenerate_scales_take_the_division():
+    # 1/s zero or not finite (s = 0, a subnormal s whose reciprocal
+    # overflows, s = inf): the fast path never stands
+    s = np.array([0.0, 1e-40, np.inf, 2.0 ** -127], dtype=f32)
+    w = np.array([0.3, 1e-41, 5.0, 2.0 ** -128], dtype=f32)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        _, ok = fast_decision(w, s)
+    assert not np.any(ok[:3])
