@@ -669,18 +669,21 @@ syrk_streamk_fixup(float* __restrict__ H, int64_t n, int nk, const float* __rest
 }
 
 // Token-split schedule: H += 2 * (sum of a tile's partials: blocks in order,
-// pieces in order).  Grid: (tiles, DT / FIX_ROWS).
+// pieces in order).  Grid: (tiles, DT / FIX_ROWS); thread (rq, jx) sums rows
+// r0 + 4 rq .. +3 at columns 4 jx .. +3 with 16-byte loads of the partials.
 __global__ void __launch_bounds__(DT)
 syrk_ksplit_fixup(float* __restrict__ H, int64_t n, int S, int C, const float* __restrict__ partial) {
+  static_assert(FIX_ROWS == 4 * (DT / 64), "four rows per thread");
   const int nt = (int)((n + DT - 1) / DT);
   const int64_t T = (int64_t)nt * (nt + 1) / 2;
   const int64_t o = blockIdx.x;
   int ti, tj;
   tile_of(o, nt, ti, tj);
-  const int r0 = blockIdx.y * FIX_ROWS, jl = threadIdx.x;
-  float sum[FIX_ROWS];
+  const int rq = threadIdx.x / 64, jx = threadIdx.x % 64;
+  const int r0 = blockIdx.y * FIX_ROWS + 4 * rq;
+  float4 sum[4];
 #pragma unroll
-  for (int r = 0; r < FIX_ROWS; ++r) sum[r] = 0.0f;
+  for (int r = 0; r < 4; ++r) sum[r] = make_float4(0.f, 0.f, 0.f, 0.f);
   const int G = 8 / S;
   const int g = (int)((o * G + G - 1) / T);  // first group whose range holds o
   int gg = g;
@@ -692,16 +695,28 @@ syrk_ksplit_fixup(float* __restrict__ H, int64_t n, int S, int C, const float* _
     const int64_t first = lt < whole ? lt : whole + (lt - whole) * k.sp;
     const int cnt = lt < whole ? 1 : k.sp;
     for (int p = 0; p < cnt; ++p) {
-      const float* part = partial + (k.base + first + p) * (int64_t)PART_FLOATS + (int64_t)r0 * DT + jl;
+      const float* part =
+          partial + (k.base + first + p) * (int64_t)PART_FLOATS + (int64_t)r0 * DT + 4 * jx;
+      float4 v[4];
 #pragma unroll
-      for (int r = 0; r < FIX_ROWS; ++r) sum[r] += part[r * DT];
+      for (int r = 0; r < 4; ++r) v[r] = *reinterpret_cast<const float4*>(part + r * DT);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sum[r].x += v[r].x;
+        sum[r].y += v[r].y;
+        sum[r].z += v[r].z;
+        sum[r].w += v[r].w;
+      }
     }
   }
-  const int64_t j = (int64_t)tj * DT + jl;
 #pragma unroll
-  for (int r = 0; r < FIX_ROWS; ++r) {
+  for (int r = 0; r < 4; ++r) {
     const int64_t i = (int64_t)ti * DT + r0 + r;
-    if (i < n && j < n && i <= j) H[i * n + j] += 2.0f * sum[r];
+    const int64_t j = (int64_t)tj * DT + 4 * jx;
+    const float e[4] = {sum[r].x, sum[r].y, sum[r].z, sum[r].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (i < n && j + c < n && i <= j + c) H[i * n + j + c] += 2.0f * e[c];
   }
 }
 
