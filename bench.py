@@ -8,10 +8,12 @@ data already resident in HBM:
     gptq_quantize_layer (sweep + lazy GEMMs + pack)
 value = weights quantized per second = out * in / step time.
 
-Default workload: the Llama-7B q_proj-shaped layer (W 4096 x 4096 fp16,
-128 samples x 2048 tokens of fp16 calibration activations, 4-bit asymmetric,
-group 128, damp 0.01, block 128).  --config c3 selects the 4096 x 11008
-down_proj layer, c4a / c4b the 8192 x 28672 70B down_proj layer.
+Default workload: the Llama-7B down_proj-shaped layer (W 4096 x 11008 fp16,
+128 samples x 2048 tokens of heavy-tailed fp16 calibration activations,
+4-bit asymmetric, group 128, desc_act, damp 0.01, block 128), the 4-bit g128
+layer the throughput is reported on.  --config c1 / c2 select the 4096 x 4096
+q_proj-shaped layer (4-bit, 3-bit desc_act), c4a / c4b the 8192 x 28672 70B
+down_proj layer.
 
 Prints ONE JSON line (rank 0; this build is single-GPU).
 
@@ -574,6 +576,32 @@ def collections_sum(rows, pick):
     return total, names
 
 
+def host_description() -> dict:
+    """The host the CPU baseline runs on: CPU model, the cores this process
+    may use, and the BLAS library NumPy calls with its thread count."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = None, None
+    try:
+        import numpy  # noqa: F401  (loads the BLAS library)
+        from threadpoolctl import threadpool_info
+        for lib in threadpool_info():
+            if lib.get("user_api") == "blas":
+                blas = f"{lib.get('internal_api')} {lib.get('version')}"
+                threads = lib.get("num_threads")
+                break
+    except Exception:
+        pass
+    return {"cpu_model": model, "allowed_cores": len(os.sched_getaffinity(0)),
+            "os_cpu_count": os.cpu_count(), "blas": blas, "blas_threads": threads}
+
+
 def cpu_baseline(cfg, steps_tokens: int):
     """The oracle, untuned, on a bounded sample of the same workload:
     Hessian over one 2048-token sample, the full prepare at the layer's n,
@@ -585,6 +613,7 @@ def cpu_baseline(cfg, steps_tokens: int):
     import workloads
 
     torch.set_num_threads(max(1, len(os.sched_getaffinity(0))))
+    host = host_description()
     X = workloads.x_sample(cfg, 0, "cpu").numpy()
     W = workloads.weight(cfg, "cpu").double().numpy()
     rows = 32
@@ -605,8 +634,9 @@ def cpu_baseline(cfg, steps_tokens: int):
     return {
         "value": weights / t_full,
         "unit": "weights/s",
-        "cores": len(os.sched_getaffinity(0)),
+        "cores": host["blas_threads"] or len(os.sched_getaffinity(0)),
         "kind": "oracle",
+        "host": host,
         "sample": (f"Hessian over 1 of {cfg.samples} samples ({X.shape[0]} tokens, "
                    f"{t_h:.2f} s, scaled x{steps_tokens // X.shape[0]}); full prepare at "
                    f"n={cfg.inp} ({t_p:.2f} s); sweep+pack of {rows} of {cfg.out} rows "
@@ -1039,7 +1069,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", default="c1", choices=["c1", "c2", "c3", "c4a", "c4b"])
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4a", "c4b"])
     ap.add_argument("--chunk-samples", type=int, default=None,
                     help="calibration samples per gptq_hessian_accumulate call "
                          "(default: all of them in one call)")

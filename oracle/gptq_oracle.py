@@ -22,11 +22,11 @@ Sources (web pages, cited by title and passage):
 
 Where the pages leave a step open, the reading taken is stated at the step.
 
-Floating point that decides an integer (a group's zero-point, a code) is
-evaluated in IEEE float32, the precision the GPU kernels decide in: the state
-(the current weight value) is float64 here, it is rounded to float32, and the
-division / rint that picks the integer runs in float32.  Everything else is
-float64.
+Every step, including the ones that decide an integer (a group's zero-point,
+a code), runs in float64.  A second implementation that decides in a lower
+precision can land on the other side of a rounding boundary when its value
+sits within rounding of it; ``gptq_sweep``'s replay mode records the distance
+of each such disagreement so that a caller can check exactly that.
 """
 from __future__ import annotations
 
@@ -180,49 +180,47 @@ def hinv_chol_reverse(Hd: np.ndarray, perm: np.ndarray) -> np.ndarray:
 #   * symmetric: hi = max(-lo, hi), lo = -hi, zero fixed at 2^(b-1);
 #   * a degenerate range lo == hi becomes [-1, +1];
 #   * scale s = (hi - lo) / (2^b - 1); asymmetric zero z = rint(-lo / s);
-#   * rint is round-half-to-even, and these float->integer decisions are
-#     taken in float32 (the kernels' precision).
+#   * rint is round-half-to-even.
 # ---------------------------------------------------------------------------
 def group_params(lo, hi, bits: int, sym: bool):
-    """Per-row (scale fp32, zero int, pre-rounding zero value fp64) for one group.
+    """Per-row (scale, zero, pre-rounding zero value) for one group, float64.
 
     ``lo`` / ``hi`` are the per-row minimum / maximum of the group's current
-    values (float64 arrays).  Returns float32 scales, int64 zeros and the
-    float64 value -lo/s that the zero was rounded from (for boundary checks).
+    values.  Returns float64 scales, int64 zeros and the float64 value the
+    zero was rounded from (for boundary checks).
     """
     maxq = (1 << bits) - 1
-    lo32 = np.minimum(np.asarray(lo, dtype=np.float64), 0.0).astype(np.float32)
-    hi32 = np.maximum(np.asarray(hi, dtype=np.float64), 0.0).astype(np.float32)
+    lo = np.minimum(np.asarray(lo, dtype=np.float64), 0.0)
+    hi = np.maximum(np.asarray(hi, dtype=np.float64), 0.0)
     if sym:
-        hi32 = np.maximum(-lo32, hi32)
-        lo32 = -hi32
-    same = lo32 == hi32
-    lo32 = np.where(same, np.float32(-1.0), lo32)
-    hi32 = np.where(same, np.float32(1.0), hi32)
-    scale = ((hi32 - lo32) / np.float32(maxq)).astype(np.float32)
+        hi = np.maximum(-lo, hi)
+        lo = -hi
+    same = lo == hi
+    lo = np.where(same, -1.0, lo)
+    hi = np.where(same, 1.0, hi)
+    scale = (hi - lo) / maxq
     if sym:
-        zero = np.full(scale.shape, 1 << (bits - 1), dtype=np.int64)
-        zero_pre = zero.astype(np.float64)
+        zero_pre = np.full(scale.shape, float(1 << (bits - 1)))
     else:
-        zero_f = (-lo32 / scale).astype(np.float32)
-        zero = np.rint(zero_f).astype(np.int64)
-        zero_pre = -lo32.astype(np.float64) / scale.astype(np.float64)
+        zero_pre = -lo / scale
+    zero = np.rint(zero_pre).astype(np.int64)
     return scale, zero, zero_pre
 
 
 def quantize_codes(w, scale, zero, bits: int):
-    """q = clamp(rint(w / s) + z, 0, 2^b - 1), decided in float32.
+    """q = clamp(rint(w / s) + z, 0, 2^b - 1), float64.
 
-    Returns (codes int64, dequantized w^ float64, pre-rounding value w/s + z
-    in float64).  w^ = s (q - z) is exact in float64 (s is an fp32 number).
+    Returns (codes int64, dequantized w^ = s (q - z) float64, pre-rounding
+    value w / s + z float64).
     """
     maxq = (1 << bits) - 1
-    w32 = np.asarray(w, dtype=np.float64).astype(np.float32)
-    ratio = (w32 / scale).astype(np.float32)
-    q = np.clip(np.rint(ratio).astype(np.int64) + zero, 0, maxq)
-    what = scale.astype(np.float64) * (q - zero).astype(np.float64)
-    pre = np.asarray(w, dtype=np.float64) / scale.astype(np.float64) + zero
-    return q, what, pre
+    w = np.asarray(w, dtype=np.float64)
+    s = np.asarray(scale, dtype=np.float64)
+    z = np.asarray(zero, dtype=np.int64)
+    ratio = w / s
+    q = np.clip(np.rint(ratio).astype(np.int64) + z, 0, maxq)
+    what = s * (q - z).astype(np.float64)
+    return q, what, ratio + z
 
 
 def _boundary_distance(pre):
@@ -234,7 +232,7 @@ def _boundary_distance(pre):
 class SweepResult:
     codes: np.ndarray          # int64 [out x in], ORIGINAL column order
     codes_perm: np.ndarray     # int64 [out x in], quantization order
-    scales: np.ndarray         # float32 [n_groups x out]
+    scales: np.ndarray         # float64 [n_groups x out]
     zeros: np.ndarray          # int64 [n_groups x out]
     g_idx: np.ndarray          # int64 [in], original column -> group
     perm: np.ndarray           # int64 [in]
@@ -281,7 +279,7 @@ def gptq_sweep(W, U, perm, bits: int, group_size: int, sym: bool,
     Wp = W64[:, perm].copy()
     gs = n if group_size == -1 else int(group_size)
     n_groups = 1 if group_size == -1 else -(-n // gs)
-    scales = np.zeros((n_groups, out), dtype=np.float32)
+    scales = np.zeros((n_groups, out), dtype=np.float64)
     zeros = np.zeros((n_groups, out), dtype=np.int64)
     codes_perm = np.zeros((out, n), dtype=np.int64)
     what_perm = np.zeros((out, n), dtype=np.float64)
@@ -309,7 +307,7 @@ def gptq_sweep(W, U, perm, bits: int, group_size: int, sym: bool,
                 mismatches.append(("code", int(r), j, int(fq[r]), int(q[r]),
                                    float(_boundary_distance(pre[r]))))
             q = fq
-            what = s.astype(np.float64) * (q - z).astype(np.float64)
+            what = s * (q - z).astype(np.float64)
         codes_perm[:, j] = q
         what_perm[:, j] = what
         err = Wp[:, j] - what
@@ -351,7 +349,7 @@ def rtn(W, bits: int, group_size: int, sym: bool) -> SweepResult:
     out, n = W64.shape
     gs = n if group_size == -1 else int(group_size)
     n_groups = 1 if group_size == -1 else -(-n // gs)
-    scales = np.zeros((n_groups, out), dtype=np.float32)
+    scales = np.zeros((n_groups, out), dtype=np.float64)
     zeros = np.zeros((n_groups, out), dtype=np.int64)
     codes = np.zeros((out, n), dtype=np.int64)
     what = np.zeros((out, n), dtype=np.float64)
@@ -488,7 +486,7 @@ class BlockResult:
     H_in: np.ndarray        # 2 X^T X of the block input
     gate: SweepResult
     up: SweepResult
-    A: np.ndarray           # the down projection's calibration inputs (fp16 values)
+    A: np.ndarray           # the down projection's calibration inputs
     H_down: np.ndarray      # 2 A^T A
     down: SweepResult
 
@@ -501,27 +499,15 @@ def mlp_block(X, Wg, Wu, Wd, bits: int, group_size: int, sym: bool, damp_percent
     activations computed through the block (3).  Reading: gate and up share
     the block input, so one Hessian serves both; the down projection's
     inputs are then computed with the gate and up layers already quantized
-    (their dequantized weights), and its Hessian comes from those.
-    The forward is fp16 as in the model ("keeping others in FP16"; reading):
-    the quantized weights enter it as fp16 values (the scale rounded to fp16,
-    times q - z, rounded), G = X Wg^T and U = X Wu^T are rounded to fp16, and
-    A = SiLU(G) U is evaluated from those and rounded to fp16.
+    (their dequantized weights W^), and its Hessian comes from those.  The
+    forward is exact arithmetic in float64: G = X W^g^T, U = X W^u^T,
+    A = SiLU(G) * U.
     """
     X64 = np.asarray(X, dtype=np.float64)
     H_in = hessian(X64)
     gate = gptq(Wg, H_in, bits, group_size, sym, damp_percent, desc_act)
     up = gptq(Wu, H_in, bits, group_size, sym, damp_percent, desc_act)
-
-    def w16(r):
-        # the forward's fp16 weights: scale rounded to fp16, times the exact
-        # integer q - z, rounded to fp16
-        s16 = r.scales.astype(np.float16).astype(np.float64)[r.g_idx, :].T
-        z = r.zeros.astype(np.float64)[r.g_idx, :].T
-        return (s16 * (r.codes - z)).astype(np.float16).astype(np.float64)
-
-    G = (X64 @ w16(gate).T).astype(np.float16)
-    U = (X64 @ w16(up).T).astype(np.float16)
-    A = silu_mul(G, U).astype(np.float16)
+    A = silu_mul(X64 @ gate.what.T, X64 @ up.what.T)
     H_down = hessian(A)
     down = gptq(Wd, H_down, bits, group_size, sym, damp_percent, desc_act)
     return BlockResult(H_in=H_in, gate=gate, up=up, A=A, H_down=H_down, down=down)

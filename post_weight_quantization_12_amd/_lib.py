@@ -8,6 +8,7 @@ missing, loading fails with an error that says how to build it.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -109,6 +110,18 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context for the buffers a wrapper allocates (outputs, workspaces).
+
+    They are allocated on the stream the call is queued on: torch's caching
+    allocator then hands their memory to other work only in that stream's
+    order, so a call on a side stream cannot have its workspace reused by
+    work on the current stream while its kernels still run."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
+
+
 def _dtype_code(dt) -> int:
     torch = _torch()
     if dt == torch.float16:
@@ -165,15 +178,16 @@ def prepare(H, damp_percent: float, desc_act: bool, Hinv_chol=None, perm=None, i
     if H.dtype != torch.float32 or H.dim() != 2 or H.shape[1] != n or not H.is_contiguous():
         raise ValueError("H must be a contiguous fp32 [n x n] tensor")
     dev = H.device
-    if Hinv_chol is None:
-        Hinv_chol = torch.empty((n, n), dtype=torch.float32, device=dev)
-    if perm is None:
-        perm = torch.empty((n,), dtype=torch.int32, device=dev)
-    if info is None:
-        info = torch.empty((1,), dtype=torch.int32, device=dev)
-    need = prepare_workspace_bytes(n)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    with _on(stream):
+        if Hinv_chol is None:
+            Hinv_chol = torch.empty((n, n), dtype=torch.float32, device=dev)
+        if perm is None:
+            perm = torch.empty((n,), dtype=torch.int32, device=dev)
+        if info is None:
+            info = torch.empty((1,), dtype=torch.int32, device=dev)
+        need = prepare_workspace_bytes(n)
+        if workspace is None:
+            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     _check(lib.gptq_prepare(_ptr(H), n, float(damp_percent), int(bool(desc_act)), _ptr(Hinv_chol),
                             _ptr(perm), _ptr(info), _ptr(workspace), workspace.numel(),
                             _stream(stream)))
@@ -207,17 +221,18 @@ def quantize_layer(W, Hinv_chol, perm, bits: int, group_size: int, sym: bool, bl
         raise ValueError("perm must be a GPU int32 [in] tensor")
     dev = W.device
     g = n_groups(inp, group_size)
-    if qweight is None:
-        qweight = torch.empty((max(inp * bits // 32, 1), out), dtype=torch.int32, device=dev)
-    if scales is None:
-        scales = torch.empty((g, out), dtype=torch.float32, device=dev)
-    if zeros is None:
-        zeros = torch.empty((g, out), dtype=torch.int32, device=dev)
-    if g_idx is None:
-        g_idx = torch.empty((inp,), dtype=torch.int32, device=dev)
-    need = quantize_workspace_bytes(out, inp, bits, group_size, block)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    with _on(stream):
+        if qweight is None:
+            qweight = torch.empty((max(inp * bits // 32, 1), out), dtype=torch.int32, device=dev)
+        if scales is None:
+            scales = torch.empty((g, out), dtype=torch.float32, device=dev)
+        if zeros is None:
+            zeros = torch.empty((g, out), dtype=torch.int32, device=dev)
+        if g_idx is None:
+            g_idx = torch.empty((inp,), dtype=torch.int32, device=dev)
+        need = quantize_workspace_bytes(out, inp, bits, group_size, block)
+        if workspace is None:
+            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     _check(lib.gptq_quantize_layer(_ptr(W), _dtype_code(W.dtype), out, inp, _ptr(Hinv_chol),
                                    _ptr(perm), int(bits), int(group_size), int(bool(sym)),
                                    int(block), _ptr(qweight), _ptr(scales), _ptr(zeros),
@@ -264,13 +279,14 @@ def dequant_matmul(X, qweight, scales, zeros, g_idx, bits: int, x_order=None, ou
             raise ValueError("x_order must be an int32 [in] tensor")
     if out_dtype is None:
         out_dtype = torch.float32 if Y is None else Y.dtype
-    if Y is None:
-        Y = torch.empty((M, out), dtype=out_dtype, device=X.device)
+    with _on(stream):
+        if Y is None:
+            Y = torch.empty((M, out), dtype=out_dtype, device=X.device)
+        if workspace is None:
+            need = dequant_matmul_workspace_bytes(M, inp, out, x_order is not None)
+            workspace = torch.empty((need,), dtype=torch.uint8, device=X.device) if need else None
     if Y.dim() != 2 or tuple(Y.shape) != (M, out) or Y.stride(1) != 1:
         raise ValueError("Y must be [M x out] with unit column stride")
-    if workspace is None:
-        need = dequant_matmul_workspace_bytes(M, inp, out, x_order is not None)
-        workspace = torch.empty((need,), dtype=torch.uint8, device=X.device) if need else None
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
     _check(lib.gptq_dequant_matmul(_ptr(X), _dtype_code(X.dtype), M, inp,
                                    X.stride(0) if M > 1 else inp, _ptr(qweight), _ptr(scales),
@@ -302,11 +318,12 @@ def dequant_group_order(qweight, g_idx, bits: int, stream=None):
     if qweight.shape[0] * 32 != inp * bits:
         raise ValueError("qweight rows must be in * bits / 32")
     out = qweight.shape[1]
-    qs = torch.empty_like(qweight)
-    gs = torch.empty_like(g_idx)
-    order = torch.empty_like(g_idx)
-    ws = torch.empty((dequant_group_order_workspace_bytes(inp),), dtype=torch.uint8,
-                     device=qweight.device)
+    with _on(stream):
+        qs = torch.empty_like(qweight)
+        gs = torch.empty_like(g_idx)
+        order = torch.empty_like(g_idx)
+        ws = torch.empty((dequant_group_order_workspace_bytes(inp),), dtype=torch.uint8,
+                         device=qweight.device)
     _check(lib.gptq_dequant_group_order(_ptr(qweight), _ptr(g_idx), inp, out, int(bits),
                                         _ptr(qs), _ptr(gs), _ptr(order), _ptr(ws), ws.numel(),
                                         _stream(stream)))
@@ -327,7 +344,8 @@ def silu_mul(G, U, A=None, stream=None):
         raise ValueError("G and U must have the same shape")
     rows, cols = G.shape
     if A is None:
-        A = torch.empty((rows, cols), dtype=torch.float16, device=G.device)
+        with _on(stream):
+            A = torch.empty((rows, cols), dtype=torch.float16, device=G.device)
     if A.dtype != torch.float16 or tuple(A.shape) != (rows, cols) or A.stride(1) != 1:
         raise ValueError("A must be fp16 [rows x cols] with unit column stride")
     ld = lambda t: t.stride(0) if rows > 1 else cols
@@ -348,8 +366,9 @@ def export_params(scales, zeros, bits: int, stream=None):
             or not zeros.is_contiguous():
         raise ValueError("zeros must be a contiguous int32 tensor shaped like scales")
     G, out = scales.shape
-    s16 = torch.empty((G, out), dtype=torch.float16, device=scales.device)
-    qz = torch.empty((G, out * bits // 32), dtype=torch.int32, device=scales.device)
+    with _on(stream):
+        s16 = torch.empty((G, out), dtype=torch.float16, device=scales.device)
+        qz = torch.empty((G, out * bits // 32), dtype=torch.int32, device=scales.device)
     _check(lib.gptq_export_params(_ptr(scales), _ptr(zeros), G, out, int(bits), _ptr(s16),
                                   _ptr(qz), _stream(stream)))
     return s16, qz
@@ -365,6 +384,7 @@ def unpack_zeros(qzeros, out: int, bits: int, stream=None):
     G = qzeros.shape[0]
     if qzeros.shape[1] * 32 != out * bits:
         raise ValueError("qzeros columns must be out * bits / 32")
-    z = torch.empty((G, out), dtype=torch.int32, device=qzeros.device)
+    with _on(stream):
+        z = torch.empty((G, out), dtype=torch.int32, device=qzeros.device)
     _check(lib.gptq_unpack_zeros(_ptr(qzeros), G, out, int(bits), _ptr(z), _stream(stream)))
     return z

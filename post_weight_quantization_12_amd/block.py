@@ -30,11 +30,17 @@ class BlockResult:
     down: PackedLayer
     H_in: object      # fp32 [d x d], upper triangle
     H_down: object    # fp32 [inter x inter], upper triangle
+    # the factors and column orders the layers were quantized with
+    # (keep_factors=True only; None otherwise)
+    U_in: object = None
+    perm_in: object = None
+    U_down: object = None
+    perm_down: object = None
 
 
 def quantize_mlp_block(X, Wg, Wu, Wd, bits: int, group_size: int, sym: bool, damp: float,
                        desc_act: bool, block: int = 128, chunk_tokens: int = 32768,
-                       stream=None, mark=None) -> BlockResult:
+                       stream=None, mark=None, keep_factors: bool = False) -> BlockResult:
     """X fp16 [tokens x d] (the block input), Wg / Wu [inter x d], Wd
     [d x inter] (fp16 or fp32).  The calibration tokens go through the block
     in chunks of chunk_tokens (the activations of one chunk live at a time).
@@ -42,7 +48,8 @@ def quantize_mlp_block(X, Wg, Wu, Wd, bits: int, group_size: int, sym: bool, dam
     (e.g. to record timing events on the stream).  stream: the stream of the
     library calls; the buffers this function allocates, clears and joins
     with torch are ordered on torch's current stream, so pass that stream
-    (None: the current stream's handle is taken)."""
+    (None: the current stream's handle is taken).  keep_factors: also return
+    the factors and column orders of the two Hessians (for stage checks)."""
     torch = L._torch()
     mark = mark or (lambda name: None)
     if stream is None:
@@ -66,7 +73,8 @@ def quantize_mlp_block(X, Wg, Wu, Wd, bits: int, group_size: int, sym: bool, dam
                                          stream=stream))
     up = PackedLayer(*L.quantize_layer(Wu, U_in, perm_in, bits, group_size, sym, block,
                                        stream=stream))
-    del U_in
+    if not keep_factors:
+        U_in = None
     mark("quantize_gate_up")
 
     # the down projection's inputs, through the quantized gate and up layers
@@ -110,4 +118,6 @@ def quantize_mlp_block(X, Wg, Wu, Wd, bits: int, group_size: int, sym: bool, dam
     if int(info_in.item()) != 0 or int(info_d.item()) != 0:
         raise RuntimeError("gptq_prepare: a block Hessian is not positive definite after "
                            f"damping (info {int(info_in.item())}, {int(info_d.item())})")
-    return BlockResult(gate=gate, up=up, down=down, H_in=H_in, H_down=H_down)
+    kept = (U_in, perm_in, U_d, perm_d) if keep_factors else (None,) * 4
+    return BlockResult(gate=gate, up=up, down=down, H_in=H_in, H_down=H_down, U_in=kept[0],
+                       perm_in=kept[1], U_down=kept[2], perm_down=kept[3])

@@ -26,7 +26,11 @@
 //     LDS as fp16 column-major (k contiguous: a B operand is one 16-byte
 //     read): a code pair becomes the half2 (1024 + q0, 1024 + q1) by OR-ing
 //     it into 0x6400 0x6400, minus (1024 + z) (exact: integers below 2048),
-//     times the fp16 scale (one rounding).
+//     times the scale split into two fp16 parts s = sh + sl (sh = fp16(s),
+//     sl = fp16(s - sh)) as one fused (q - z) sh + fl((q - z) sl): close to
+//     the fp16 rounding of the exact weight.  A scale rounded to fp16 alone
+//     would scale a whole group-row of weights by the same factor (1 + d),
+//     |d| <= 2^-11, an error that does not average out over the group.
 #include "common.hpp"
 
 #include <type_traits>
@@ -452,12 +456,17 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
       const int r = tid / 4 + 128 * i, o = 8 * (tid % 4);
       *reinterpret_cast<uint4*>(&Xs[buf][r * XP + o]) = xr[i];
     }
-    half2_t sh[4], zz[4];
+    half2_t sh[4], sl[4], zz[4];
+    // s = hi + lo in fp16: s - hi is exact in fp32, lo its fp16 rounding
+    auto lo16 = [](float s, _Float16 h) { return (_Float16)(s - (float)h); };
     if (oneA) {
-      const half2_t s2 = {(_Float16)sA, (_Float16)sA};
+      const _Float16 h = (_Float16)sA;
+      const half2_t s2 = {h, h};
+      const _Float16 l = lo16(sA, h);
+      const half2_t l2 = {l, l};
       const half2_t z2 = {(_Float16)(1024.0f + (float)zA), (_Float16)(1024.0f + (float)zA)};
 #pragma unroll
-      for (int p = 0; p < 4; ++p) { sh[p] = s2; zz[p] = z2; }
+      for (int p = 0; p < 4; ++p) { sh[p] = s2; sl[p] = l2; zz[p] = z2; }
     } else {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -465,7 +474,9 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
         const float s1 = scales[(int64_t)gA[2 * p + 1] * out + wcolc];
         const float z0 = (float)zeros[(int64_t)gA[2 * p] * out + wcolc];
         const float z1 = (float)zeros[(int64_t)gA[2 * p + 1] * out + wcolc];
-        sh[p] = (half2_t){(_Float16)s0, (_Float16)s1};
+        const _Float16 h0 = (_Float16)s0, h1 = (_Float16)s1;
+        sh[p] = (half2_t){h0, h1};
+        sl[p] = (half2_t){lo16(s0, h0), lo16(s1, h1)};
         zz[p] = (half2_t){(_Float16)(1024.0f + z0), (_Float16)(1024.0f + z1)};
       }
     }
@@ -478,7 +489,10 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
       const uint32_t q0 = (uint32_t)(win >> (2 * p * B)) & mask;
       const uint32_t q1 = (uint32_t)(win >> ((2 * p + 1) * B)) & mask;
       const uint32_t q2 = q0 | (q1 << 16) | 0x64006400u;
-      const half2_t d = (__builtin_bit_cast(half2_t, q2) - zz[p]) * sh[p];
+      const half2_t qz = __builtin_bit_cast(half2_t, q2) - zz[p];
+      // one rounding of (q - z) sh + fl((q - z) sl): the large product is
+      // exact inside the fused operation
+      const half2_t d = __builtin_elementwise_fma(qz, sh[p], qz * sl[p]);
       packed[p] = __builtin_bit_cast(uint32_t, d);
     }
     *reinterpret_cast<uint4*>(&Ws[buf][wc * XP + 8 * wq]) =

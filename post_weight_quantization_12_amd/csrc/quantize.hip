@@ -56,12 +56,17 @@ __device__ inline void grid_params(float lo, float hi, int bits, int sym, float&
     hi = fmaxf(-lo, hi);
     lo = -hi;
   }
-  if (lo == hi) {
+  // A degenerate range (an all-zero group-row) becomes [-1, 1]; its zero
+  // rint(1 / s) = rint(maxq / 2) is an exact tie that rounds to the even
+  // 2^(b-1).  It is set directly: in fp32, 1 / fl(2 / maxq) falls just below
+  // the tie for 3, 4 and 8 bits and would round down.
+  const bool flat = lo == hi;
+  if (flat) {
     lo = -1.0f;
     hi = 1.0f;
   }
   s = (hi - lo) / maxq;
-  z = sym ? (float)(1 << (bits - 1)) : rintf(-lo / s);
+  z = (sym || flat) ? (float)(1 << (bits - 1)) : rintf(-lo / s);
 }
 
 template <typename T>

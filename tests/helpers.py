@@ -2,9 +2,9 @@
 
 The oracle is run on the very same input bytes the GPU receives.  Where a
 floating-point value decides an integer (a code, a zero-point), the oracle
-decides in float32 like the kernels; a disagreement is accepted only where
-the oracle's own pre-rounding value lies within 1e-3 (code units) of a
-rounding boundary, and at most 0.1 % of entries may disagree.  After such a
+decides in float64 and the kernels in float32; a disagreement is accepted
+only where the oracle's own pre-rounding value lies within 1e-3 (code units)
+of a rounding boundary, and at most 0.1 % of entries may disagree.  After such a
 disagreement the oracle continues from the GPU's decision (teacher forcing),
 so one boundary case cannot cascade along a row and every later value is
 still checked against an exact GPTQ continuation.
@@ -80,3 +80,44 @@ def rel_fro(a, b) -> float:
 def upper_mirror(H: np.ndarray) -> np.ndarray:
     u = np.triu(H)
     return u + np.triu(u, 1).T
+
+
+def with_ties(W, bits, gs, sym):
+    """Boundary-safe W with three rows rewritten (H = I cases):
+    row 0 all zero: every group-row is degenerate (range [-1, 1], zero 2^(b-1));
+    row 1: every value but the group's extremes moved to an exact half-integer
+    multiple of the scale, (c + 1/2) s, so every such code is an exact tie;
+    row 2 (asymmetric): the extremes moved to -(z + 1/2) s and
+    (maxq - z - 1/2) s, so the zero -lo / s = z + 1/2 is an exact tie (the
+    scale stays s) and the other values are clipped into the new range.
+    All values stay exact in fp16."""
+    W = W.clone().double()
+    out, inp = W.shape
+    maxq = (1 << bits) - 1
+    g = inp if gs == -1 else gs
+    r = O.rtn(W[:3].numpy(), bits, gs, sym)      # rows are independent
+    W[0] = 0.0
+    for c0 in range(0, inp, g):
+        grp = W[1, c0:c0 + g]
+        s = float(r.scales[c0 // g, 1])
+        z = int(r.zeros[c0 // g, 1])
+        lo_i, hi_i = int(torch.argmin(grp)), int(torch.argmax(grp))
+        rng = np.random.default_rng(c0 + 7)
+        for j in range(grp.numel()):
+            if j in (lo_i, hi_i):
+                continue
+            if sym:
+                c = int(rng.integers(-(maxq // 2), maxq // 2))        # |c + 1/2| < maxq / 2
+            else:
+                c = int(rng.integers(-z, maxq - z))                   # c + 1/2 inside [-z, maxq - z]
+            W[1, c0 + j] = (c + 0.5) * s
+        if not sym and out > 2:
+            grp2 = W[2, c0:c0 + g]
+            s2 = float(r.scales[c0 // g, 2])
+            z2 = int(r.zeros[c0 // g, 2])
+            z2 = min(max(z2, 1), maxq - 2)
+            lo2, hi2 = -(z2 + 0.5) * s2, (maxq - z2 - 0.5) * s2
+            grp2.clamp_(lo2, hi2)
+            grp2[int(torch.argmin(grp2))] = lo2
+            grp2[int(torch.argmax(grp2))] = hi2
+    return W.float()

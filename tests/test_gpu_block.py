@@ -2,14 +2,18 @@
 the oracle's mlp_block on the same fp16 block input and weights, and the
 gated activation kernel against the oracle's silu_mul.
 
-The block is compared as whole layers are elsewhere: Hessians to relative
-Frobenius error 1e-3, and each layer's calibration error within 2 % of the
-oracle's (measured with the oracle's Hessian of that layer's inputs), below
-round-to-nearest, with codes agreeing on at least 99.9 % of entries for gate
-and up and 97 % for down (its inputs come from the quantized gate and up
-layers through each side's own fp16 forward, so its Hessian differs by
-about 1e-4 and, under desc_act, near-equal diagonal entries may swap in the
-column order; its calibration error still has to match within 2 %).
+Stage by stage, each stage fed the HIP path's own output of the stage
+before: H_in against the oracle's Hessian of the block input (relative
+Frobenius 1e-3); gate and up against the oracle sweep in replay mode with
+the factor and column order the library used; H_down against the Hessian of
+the activations the oracle's fp64 forward gives through the HIP path's
+quantized gate and up (1e-3: the HIP forward holds the dequantized weights
+and the activations in fp16, about 5e-4 apart); the column order of H_down
+exactly; down against the oracle sweep in replay mode with its factor.
+
+End to end, both chains free-running: each layer's calibration error within
+2 % of the oracle's (measured with the oracle's Hessian of that layer's
+inputs) and below round-to-nearest; code agreement reported.
 """
 import numpy as np
 import pytest
@@ -18,7 +22,7 @@ import torch
 import oracle as O
 import post_weight_quantization_12_amd as P
 import workloads
-from helpers import gpu_codes, rel_fro, upper_mirror
+from helpers import check_quantize_parity, gpu_codes, rel_fro, upper_mirror
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -64,13 +68,35 @@ def test_mlp_block_matches_oracle(d, inter, bits, gs, sym, desc):
     X = workloads.x_tokens(base, 0, 2)                      # 4096 tokens, two chunks below
     Wg, Wu, Wd = workloads.mlp_block_weights(d, inter)
     r = P.block.quantize_mlp_block(X.to(DEV), Wg.to(DEV), Wu.to(DEV), Wd.to(DEV), bits, gs,
-                                   sym, 0.01, desc, chunk_tokens=2048)
+                                   sym, 0.01, desc, chunk_tokens=2048, keep_factors=True)
     ref = O.mlp_block(X.numpy(), Wg.float().numpy(), Wu.float().numpy(), Wd.float().numpy(),
                       bits, gs, sym, 0.01, desc)
     h_in = rel_fro(upper_mirror(r.H_in.cpu().double().numpy()), ref.H_in)
     h_dn = rel_fro(upper_mirror(r.H_down.cpu().double().numpy()), ref.H_down)
-    print(f"  H_in rel {h_in:.2e}  H_down rel {h_dn:.2e}")
-    assert h_in <= 1e-3 and h_dn <= 1e-3
+    # H_down free-running (each side's own gate and up) is reported; the
+    # stage check below is the gate
+    print(f"  H_in rel {h_in:.2e}  H_down rel {h_dn:.2e} (free-running)")
+    assert h_in <= 1e-3
+    # ---- stage by stage, each fed the HIP path's previous output ----
+    for name, lay, W in (("gate", r.gate, Wg), ("up", r.up, Wu)):
+        dd = check_quantize_parity(W, r.U_in.cpu(), r.perm_in, bits, gs, sym, lay.qweight,
+                                   lay.scales, lay.zeros, lay.g_idx)
+        print(f"  stage {name}: {dd}")
+    Xn = X.double().numpy()
+
+    def deq(lay, n):
+        return O.dequantize(gpu_codes(lay.qweight, bits, n), lay.scales.cpu().numpy(),
+                            lay.zeros.cpu().numpy(), lay.g_idx.cpu().numpy())
+
+    A = O.silu_mul(Xn @ deq(r.gate, d).T, Xn @ deq(r.up, d).T)
+    Hg_down = upper_mirror(r.H_down.cpu().double().numpy())
+    h_st = rel_fro(Hg_down, O.hessian(A))
+    print(f"  stage H_down rel {h_st:.2e}")
+    assert h_st <= 1e-3
+    assert np.array_equal(r.perm_down.cpu().numpy(), O.column_order(Hg_down, desc))
+    dd = check_quantize_parity(Wd, r.U_down.cpu(), r.perm_down, bits, gs, sym, r.down.qweight,
+                               r.down.scales, r.down.zeros, r.down.g_idx)
+    print(f"  stage down: {dd}")
     for name, lay, W, H, orc in (("gate", r.gate, Wg, ref.H_in, ref.gate),
                                  ("up", r.up, Wu, ref.H_in, ref.up),
                                  ("down", r.down, Wd, ref.H_down, ref.down)):
@@ -87,10 +113,8 @@ def test_mlp_block_matches_oracle(d, inter, bits, gs, sym, desc):
               f"agreement {agree:.5f}")
         assert abs(e_gpu / e_ref - 1.0) <= 0.02
         assert e_gpu < e_rtn
-        # gate and up see the same Hessian (to ~1e-7): the usual 99.9 %; the
-        # down projection's Hessian comes from each side's own forward (1e-4
-        # apart), which moves some decisions and, with desc_act, can swap
-        # near-equal diagonal entries in the column order
-        assert agree >= (0.999 if name != "down" else 0.97)
+        # free-running code agreement is reported only: a value on a rounding
+        # boundary (decided in fp32 here and in fp64 by the oracle) moves the
+        # rest of its row; the stage checks above compare code by code
         if not desc:   # with desc_act near-equal diagonal entries may order either way
             assert np.array_equal(lay.g_idx.cpu().numpy(), orc.g_idx)

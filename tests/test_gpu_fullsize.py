@@ -1,17 +1,28 @@
 """Parity at the full layer sizes (Llama-7B q_proj / down_proj, Llama-70B
-down_proj shapes, 128 x 2048 calibration tokens), in the launch configuration
-bench.py times (32768-token Hessian chunks, one prepare, one quantize call),
-on outputs the oracle can compute one by one:
+down_proj shapes, 128 x 2048 calibration tokens), on outputs the oracle can
+compute one by one:
 
-* Hessian: sampled entries H_ij = 2 sum_t x_ti x_tj in fp64 from the same X
-  columns; |dH_ij| <= 1e-3 * sqrt(H_ii H_jj) per entry (the natural scale of an
-  entry; the relative Frobenius bound 1e-3 is estimated on the sample too).
+* Hessian: the call bench.py times (every calibration token in one
+  gptq_hessian_accumulate call with a workspace: the token-split schedule at
+  n = 4096, whole tiles at n = 11008 and 28672), plus 32768-token calls
+  (stream-K at n = 4096).  Sampled entries H_ij = 2 sum_t x_ti x_tj in fp64
+  from the same X columns; |dH_ij| <= 1e-3 * sqrt(H_ii H_jj) per entry (the
+  natural scale of an entry; the relative Frobenius bound 1e-3 is estimated
+  on the sample too).  Integer X (|x| <= 4, every partial sum an integer
+  below 2^24) through the token-split schedule: sampled entries bit-exact.
 * Prepare: the full oracle factor where it finishes in seconds (n = 4096,
   11008); at n = 28672 the residual (U^T U H_p - I) on sampled columns and the
   exact perm.  The input H is a torch fp32 product, not the HIP path's.
 * Quantize: sampled output rows (rows are independent) against the oracle
   sweep in replay mode, from the oracle's factor (n = 4096) or a synthetic
   dense upper-triangular factor (larger n).
+* End to end (both chains free-running, the HIP chain with its own H and U):
+  the layer error of sampled rows (a sum over rows, so a subset is exact for
+  those rows) within 2 % of the oracle's, at every config's layer shape; the
+  calibration tokens are all 262144 at n = 4096 and a subsample at n = 11008
+  and 28672, where the oracle's fp64 Hessian of every token would take
+  minutes to hours.
+* H = I at the config shapes: bit-exact group round-to-nearest.
 """
 import numpy as np
 import pytest
@@ -20,11 +31,11 @@ import torch
 import oracle as O
 import post_weight_quantization_12_amd as P
 import workloads
-from helpers import check_quantize_parity
+from helpers import check_quantize_parity, gpu_codes, with_ties
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-CHUNK = 16 * 2048  # tokens per gptq_hessian_accumulate call (as bench.py)
+CHUNK = 16 * 2048  # tokens per call in the chunked variant
 
 
 def _banner(msg):
@@ -50,18 +61,29 @@ def _sample_features(cfg, k=10, seed=5):
     return sorted(set(int(i) for i in fixed + outl + rand if 0 <= i < n))
 
 
+def _accumulate(H, X, chunk):
+    n = H.shape[0]
+    ws = torch.empty((P.hessian_workspace_bytes(n),), dtype=torch.uint8, device=DEV)
+    step = X.shape[0] if chunk is None else chunk
+    for t0 in range(0, X.shape[0], step):
+        P.hessian_accumulate(H, X[t0:t0 + step], workspace=ws)
+    torch.cuda.synchronize()
+
+
+HCASES = [("c1", None), ("c1", CHUNK), ("c3", None), ("c4a", None)]
+
+
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cname", ["c1", "c3", "c4a"])
-def test_hessian_full_size_sampled(cname):
+@pytest.mark.parametrize("cname,chunk", HCASES,
+                         ids=[f"{c}-{'one_call' if k is None else k}" for c, k in HCASES])
+def test_hessian_full_size_sampled(cname, chunk):
     cfg = workloads.get(cname)
-    _banner(f"full-size hessian {cname} n={cfg.inp} tokens={cfg.tokens}")
+    _banner(f"full-size hessian {cname} n={cfg.inp} tokens={cfg.tokens} "
+            f"call={'all tokens' if chunk is None else chunk}")
     X = _x_full(cfg)
     n = cfg.inp
     H = torch.zeros((n, n), dtype=torch.float32, device=DEV)
-    ws = torch.empty((P.hessian_workspace_bytes(n),), dtype=torch.uint8, device=DEV)
-    for t0 in range(0, cfg.tokens, CHUNK):
-        P.hessian_accumulate(H, X[t0:t0 + CHUNK], workspace=ws)
-    torch.cuda.synchronize()
+    _accumulate(H, X, chunk)
     idx = _sample_features(cfg)
     cols = X[:, idx].to("cpu").numpy().astype(np.float64)       # the same fp16 bytes
     del X
@@ -80,6 +102,44 @@ def test_hessian_full_size_sampled(cname):
     assert rel <= 1e-3
     # the strictly lower triangle is never written
     assert float(H[1, 0].item()) == 0.0 and float(H[n - 1, 0].item()) == 0.0
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("n", [2048, 4096])
+def test_hessian_token_split_integer_bit_exact(n):
+    """262144 integer-valued tokens in one call with a workspace: at these n
+    the tiles are too few for whole-tile rounds, so the call cuts the tokens
+    into 8 blocks of 1024 stages (the token-split schedule, including the
+    pieces of the tiles left after the whole rounds and the fix-up that adds
+    the partials).  Every product and partial sum is an integer below 2^24,
+    so sampled entries must equal the exact integer sums."""
+    ntok = 262144
+    _banner(f"token-split integer n={n} tokens={ntok}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(n)
+    X = torch.randint(-4, 5, (ntok, n), generator=g, device=DEV, dtype=torch.int16).to(torch.float16)
+    H = torch.zeros((n, n), dtype=torch.float32, device=DEV)
+    _accumulate(H, X, None)
+    rng = np.random.default_rng(n)
+    idx = sorted(set([0, 1, 31, 32, 255, 256, n // 2, n - 1] +
+                     rng.choice(n, 24, replace=False).tolist()))
+    # integer sums below 2^53: fp64 BLAS products are exact here
+    cols = X[:, idx].to("cpu").numpy().astype(np.float64)
+    ref = 2.0 * (cols.T @ cols)
+    Hs = H[idx][:, idx].cpu().numpy().astype(np.float64)
+    iu = np.triu_indices(len(idx))
+    assert np.array_equal(Hs[iu], ref[iu])
+    assert np.all(np.tril(Hs, -1) == 0)
+    # a whole band of rows (all tiles of a row of tiles) against the exact sums
+    band = slice(n // 2 - 128, n // 2 + 128)
+    Xb = X[:, band].to("cpu").numpy().astype(np.float64)
+    Xa = X.to("cpu").numpy().astype(np.float64)
+    del X
+    rows = 2.0 * (Xb.T @ Xa)                                    # [256 x n]
+    Hb = H[band].cpu().numpy().astype(np.float64)
+    for i in range(256):
+        r = n // 2 - 128 + i
+        assert np.array_equal(Hb[i, r:], rows[i, r:]), f"row {r}"
 
 
 def _torch_hessian(cfg):
@@ -180,3 +240,109 @@ def test_quantize_full_size_sampled_rows(cname, factor):
     d = check_quantize_parity(W.cpu(), U32, perm_t, cfg.bits, cfg.group_size, cfg.sym, qw, sc,
                               zr, gi, rows=rows)
     print("  ", d)
+
+
+# ------------------------------------------------ end to end (free-running) --
+E2E_TOKENS = {"c1": 262144, "c2": 262144, "c3": 32768, "c4a": 8192, "c4b": 8192}
+_ORACLE = {}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _drop_oracle_cache():
+    yield
+    _ORACLE.clear()
+
+
+def _oracle_chain(cfg, Xc):
+    """(H, perm, U) of the oracle for the calibration tokens Xc (fp16 numpy).
+    H is kept for the next config with the same tokens (c1 and c2, c4a and
+    c4b share them), U for the next with the same damping and order too."""
+    hkey = (cfg.cfg_id, Xc.shape[0])
+    ukey = hkey + (cfg.damp, cfg.desc_act)
+    if _ORACLE.get("hkey") != hkey:
+        _ORACLE.clear()
+        _ORACLE["hkey"], _ORACLE["H"] = hkey, O.hessian(Xc)
+    H = _ORACLE["H"]
+    if _ORACLE.get("ukey") != ukey:
+        _ORACLE.pop("U", None)
+        Hd, _ = O.condition(H, cfg.damp)
+        perm = O.column_order(H, cfg.desc_act)
+        _ORACLE["ukey"], _ORACLE["perm"], _ORACLE["U"] = ukey, perm, O.hinv_chol(Hd, perm)
+        del Hd
+    return H, _ORACLE["perm"], _ORACLE["U"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cname", ["c1", "c2", "c3", "c4a", "c4b"])
+def test_end_to_end_full_shape_sampled_rows(cname):
+    """Both chains free-running on the same fp16 X and W: the HIP chain is the
+    bench step (one gptq_hessian_accumulate call with a workspace over every
+    token, gptq_prepare, gptq_quantize_layer of the whole layer), the oracle
+    chain its fp64 Hessian, factor and unblocked sweep of sampled rows.  The
+    rows' layer error ||X (W - W^)^T||^2 (the oracle's undamped H) within 2 %."""
+    cfg = workloads.get(cname)
+    out, n = cfg.out, cfg.inp
+    ntok = E2E_TOKENS[cname]
+    samples = ntok // cfg.tokens_per_sample
+    _banner(f"end-to-end full shape {cname} {out}x{n} {cfg.bits}b g{cfg.group_size} "
+            f"sym={cfg.sym} desc={cfg.desc_act} tokens={ntok}")
+    X = _x_full(cfg.shrink(samples=samples))
+    W = workloads.weight(cfg, DEV)
+    H = torch.zeros((n, n), dtype=torch.float32, device=DEV)
+    _accumulate(H, X, None)
+    U, perm, info = P.prepare(H, cfg.damp, cfg.desc_act)
+    qw, sc, zr, gi = P.quantize_layer(W, U, perm, cfg.bits, cfg.group_size, cfg.sym, cfg.block)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    Xc = X.cpu().numpy()
+    del X, H, U
+    Ho, perm_o, Uo = _oracle_chain(cfg, Xc)
+    del Xc
+    rows = sorted(set([0, 1, out // 2, out - 1] +
+                      np.random.default_rng(17).choice(out, 8, replace=False).tolist()))
+    Wr = W[rows].double().cpu().numpy()
+    ref = O.gptq_sweep(Wr, Uo, perm_o, cfg.bits, cfg.group_size, cfg.sym)
+    rsel = torch.tensor(rows, device=DEV)
+    codes = O.unpack(qw[:, rsel].cpu().numpy(), cfg.bits, n)
+    Wq = O.dequantize(codes, sc[:, rsel].cpu().numpy(), zr[:, rsel].cpu().numpy(),
+                      gi.cpu().numpy())
+    e_gpu = O.layer_error(Wr, Wq, Ho)
+    e_ref = O.layer_error(Wr, ref.what, Ho)
+    agree = float(np.mean(codes == ref.codes))
+    same_perm = bool(np.array_equal(perm.cpu().numpy(), perm_o))
+    print(f"  rows {len(rows)}: E_gpu {e_gpu:.6g}  E_oracle {e_ref:.6g}  "
+          f"ratio {e_gpu / e_ref:.5f}  code agreement {agree:.5f}  same perm {same_perm}")
+    assert abs(e_gpu / e_ref - 1.0) <= 0.02
+
+
+# ------------------------------------------------------------ H = I, full --
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cname", ["c1", "c2", "c4a", "c4b"])
+def test_h_identity_full_shape_bit_exact(cname):
+    """H = I at the config's layer shape, bits, groups and symmetry: the whole
+    path (prepare of I, every sweep block and trailing product, the pack) must
+    give group round-to-nearest bit for bit on boundary-safe weights with an
+    all-zero row and exact ties."""
+    cfg = workloads.get(cname)
+    out, n, bits, gs, sym = cfg.out, cfg.inp, cfg.bits, cfg.group_size, cfg.sym
+    _banner(f"H=I full shape {cname} {out}x{n} {bits}b g{gs} sym={sym}")
+    W = with_ties(workloads.boundary_safe_weight(out, n, bits, gs, sym), bits, gs, sym)
+    W = W.to(cfg.w_dtype)
+    U, perm, info = P.prepare(torch.eye(n, device=DEV), cfg.damp, cfg.desc_act)
+    qw, sc, zr, gi = P.quantize_layer(W.to(DEV), U, perm, bits, gs, sym, cfg.block)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    assert np.array_equal(perm.cpu().numpy(), np.arange(n))
+    del U
+    qwn, scn, zrn, gin = (t.cpu().numpy() for t in (qw, sc, zr, gi))
+    Wd = W.double().numpy()
+    step = 1024
+    for r0 in range(0, out, step):
+        r1 = min(out, r0 + step)
+        r = O.rtn(Wd[r0:r1], bits, gs, sym)
+        assert np.array_equal(O.unpack(qwn[:, r0:r1], bits, n), r.codes), f"rows {r0}:{r1}"
+        assert np.array_equal(qwn[:, r0:r1], O.pack(r.codes, bits))
+        assert np.array_equal(scn[:, r0:r1], r.scales.astype(np.float32))
+        assert np.array_equal(zrn[:, r0:r1], r.zeros)
+        if r0 == 0:
+            assert np.array_equal(gin, r.g_idx)

@@ -13,7 +13,7 @@ import torch
 import oracle as O
 import post_weight_quantization_12_amd as P
 import workloads
-from helpers import check_quantize_parity, gpu_codes, rel_fro, upper_mirror
+from helpers import check_quantize_parity, gpu_codes, rel_fro, upper_mirror, with_ties
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -203,12 +203,26 @@ def test_quantize_matches_oracle(case):
     perm = O.column_order(H64, desc)
     U32 = O.hinv_chol(Hd, perm).astype(np.float32)       # the oracle's factor, fp32
     W = workloads.weight(cfg).to(wdt)
+    # all-zero group-rows: the first group in quantization order of two rows
+    # (no earlier error reaches it) and one whole row (it stays zero, so every
+    # one of its groups is degenerate)
+    g0 = torch.from_numpy(perm[: (inp if gs == -1 else gs)])
+    W[1, g0] = 0
+    W[out // 2, g0] = 0
+    W[3] = 0
     perm_t = torch.from_numpy(perm.astype(np.int32)).to(DEV)
     qw, sc, zr, gi = P.quantize_layer(W.to(DEV), torch.from_numpy(U32).to(DEV), perm_t, bits, gs,
                                       sym, block)
     torch.cuda.synchronize()
     d = check_quantize_parity(W, torch.from_numpy(U32), perm_t, bits, gs, sym, qw, sc, zr, gi)
     print("  ", d)
+    # the degenerate range [-1, 1]: s = 2 / maxq, zero 2^(b-1), w^ = 0
+    maxq = (1 << bits) - 1
+    zrn, scn = zr.cpu().numpy(), sc.cpu().numpy()
+    for r in (1, out // 2, 3):
+        assert zrn[0, r] == 2 ** (bits - 1) and scn[0, r] == np.float32(2.0) / np.float32(maxq)
+    assert np.all(zrn[:, 3] == 2 ** (bits - 1))
+    assert np.all(gpu_codes(qw, bits, inp)[3] == 2 ** (bits - 1))
 
 
 @pytest.mark.parametrize("bits,gs,sym,block,wdt", [(4, 32, False, 32, torch.float32),
@@ -219,18 +233,25 @@ def test_quantize_matches_oracle(case):
                                                    (3, 32, True, 64, torch.float32)])
 def test_h_identity_reduces_to_rtn_bit_exact(bits, gs, sym, block, wdt):
     """With H = I the factor is diagonal, no error is propagated, and GPTQ is
-    group round-to-nearest: codes, zeros, scales, g_idx and qweight bit-exact."""
+    group round-to-nearest: codes, zeros, scales, g_idx and qweight bit-exact,
+    including an all-zero row and exact rounding ties (half to even)."""
     _banner(f"H=I bits={bits} gs={gs} sym={sym} block={block}")
     out, inp = 48, 512
-    W = workloads.boundary_safe_weight(out, inp, bits, gs, sym).to(wdt)
+    W = with_ties(workloads.boundary_safe_weight(out, inp, bits, gs, sym), bits, gs, sym).to(wdt)
     U, perm, info = P.prepare(torch.eye(inp, device=DEV), 0.01, True)
     qw, sc, zr, gi = P.quantize_layer(W.to(DEV), U, perm, bits, gs, sym, block)
     torch.cuda.synchronize()
     assert int(info.item()) == 0
     r = O.rtn(W.double().numpy(), bits, gs, sym)
+    # the constructed ties are there: row 1 codes sit on half-integers, row 0 is degenerate
+    pre1 = W[1].double().numpy() / r.scales[r.g_idx, 1]
+    assert np.sum(np.abs(pre1 - np.floor(pre1) - 0.5) == 0) > inp // 2
+    assert np.all(r.zeros[:, 0] == 2 ** (bits - 1))
     assert np.array_equal(gpu_codes(qw, bits, inp), r.codes)
     assert np.array_equal(qw.cpu().numpy(), O.pack(r.codes, bits))
-    assert np.array_equal(sc.cpu().numpy(), r.scales)
+    # scales are fp32 outputs: the oracle's value rounded to fp32 (exact for
+    # the powers of two; 2 / maxq for the all-zero row)
+    assert np.array_equal(sc.cpu().numpy(), r.scales.astype(np.float32))
     assert np.array_equal(zr.cpu().numpy(), r.zeros)
     assert np.array_equal(gi.cpu().numpy(), r.g_idx)
 
@@ -326,3 +347,27 @@ def test_end_to_end_layer_error_within_2pct(cname, out, inp, bits, gs, sym, desc
     print(f"  E_gpu {e_gpu:.6g}  E_oracle {e_ref:.6g}  E_rtn {e_rtn:.6g}  code agreement {agree:.5f}")
     assert abs(e_gpu / e_ref - 1.0) <= 0.02
     assert e_gpu < e_rtn
+
+
+def test_quantize_on_side_stream_keeps_its_buffers():
+    """gptq_quantize_layer queued on a side stream with the binding allocating
+    its outputs and workspace: they belong to that stream, so the memory that
+    torch hands out and fills on the current stream meanwhile cannot overlap
+    them; the result equals a run on the current stream."""
+    _banner("quantize on a side stream")
+    cfg = workloads.get("c1").shrink(out=512, inp=2048, tokens_per_sample=4096, n_outliers=4)
+    _, H32 = _oracle_h(cfg)
+    H = torch.from_numpy(H32).to(DEV)
+    U, perm, info = P.prepare(H, 0.01, True)
+    W = workloads.weight(cfg, DEV)
+    ref = P.quantize_layer(W, U, perm, 4, 128, False, 128)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = P.quantize_layer(W, U, perm, 4, 128, False, 128, stream=side)
+    junk = [torch.full((1 << 22,), 7.0, device=DEV) for _ in range(16)]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    del junk
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)

@@ -162,11 +162,11 @@ def test_t2_trace_desc_act_groups():
     assert res.g_idx.tolist() == [1, 0, 1, 0]
     assert res.codes.tolist() == [[3, 3, 0, 0], [0, 3, 3, 0]]
     assert res.zeros.tolist() == [[1, 1], [1, 0]]
-    assert np.allclose(res.scales, np.array([[8 / 15, 1 / 3], [37 / 90, 19 / 45]], np.float32))
+    assert np.allclose(res.scales, np.array([[8 / 15, 1 / 3], [37 / 90, 19 / 45]]),
+                       rtol=1e-14, atol=0)
     # quality: sum_r d^T H d = 511/1620 for GPTQ
     d = T2_W - res.what
-    # (scales are fp32, so the dequantized values carry fp32 rounding)
-    assert float(np.sum((d @ T2_H) * d)) == pytest.approx(511 / 1620, rel=1e-6)
+    assert float(np.sum((d @ T2_H) * d)) == pytest.approx(511 / 1620, rel=1e-12)
     # RTN, natural-order groups {0,1}, {2,3}; row 0 by hand: [1, 1] -> s = 1/3,
     # z = 0 -> codes 3, 3; [-1/5, -3/5] -> s = 1/5, z = 3 -> codes 2, 0.
     # (Row 1 lands on exact rounding ties and is not pinned.)
@@ -307,6 +307,71 @@ def test_prefix_optimality_reconstructs_codes():
         assert np.array_equal(q[ok], res.codes_perm[ok, j])
         checked += int(ok.sum())
     assert checked > 0.99 * W.size
+
+
+# ------------------------------------------ grid: degenerate range, ties --
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_all_zero_group_row_hand_trace(bits):
+    """An all-zero group-row has lo = hi = 0, so its range becomes [-1, 1]:
+    s = 2 / maxq and z = rint(1 / s) = rint(maxq / 2), an exact tie that
+    round-half-to-even sends to 2^(b-1) (1.5 -> 2, 3.5 -> 4, 7.5 -> 8,
+    127.5 -> 128); every code is then z and every w^ exactly 0.  The group is
+    the row's first, so no earlier error reaches it, and its own errors are 0,
+    so nothing moves inside it even with a correlated H."""
+    maxq = 2 ** bits - 1
+    cfg, W, H = _c0_problem(rows=4)
+    W = W.copy()
+    W[1, :32] = 0.0
+    res = O.gptq(W, H, bits, 32, False, 0.01, False)
+    want_z = {2: 2, 3: 4, 4: 8, 8: 128}[bits]
+    assert want_z == 2 ** (bits - 1)
+    assert res.zeros[0, 1] == want_z
+    assert res.scales[0, 1] == pytest.approx(2.0 / maxq, rel=1e-15)
+    assert res.codes[1, :32].tolist() == [want_z] * 32
+    assert np.all(res.what[1, :32] == 0.0)
+    # symmetric: the zero is 2^(b-1) by definition and the scale the same
+    rs = O.gptq(W, H, bits, 32, True, 0.01, False)
+    assert rs.zeros[0, 1] == want_z and rs.codes[1, :32].tolist() == [want_z] * 32
+    assert rs.scales[0, 1] == pytest.approx(2.0 / maxq, rel=1e-15)
+
+
+def test_exact_ties_round_half_to_even():
+    """Values that land exactly on a half-integer (H = I: nothing propagates).
+
+    Row 0, 4-bit asym, one group: lo = -2, hi = 1.75 -> s = 3.75 / 15 = 1/4,
+    z = rint(8) = 8.  w / s = 2.5, -1.5, 0.5, 3.5, -0.5 round (half to even)
+    to 2, -2, 0, 4, -0 -> codes 10, 6, 8, 12, 8.  Half-up would give
+    11, 7, 9, 12, 8 and half-away-from-zero 11, 6, 9, 12, 7.
+    Row 1: lo = -0.625, hi = 3.125 -> s = 1/4 and -lo / s = 2.5 -> z = 2
+    (half-up: 3); w / s = -2.5, 12.5, 1.5, -2.5 -> rint -2, 12, 2, -2 ->
+    codes 0, 14, 4, 0 (half-up: 12.5 -> 13 -> code 15).
+    """
+    W = np.array([[-2.0, 1.75, 0.625, -0.375, 0.125, 0.875, -0.125, 0.0],
+                  [-0.625, 3.125, 0.375, -0.625, 0.0, 0.0, 0.0, 0.0]])
+    res = O.gptq(W, np.eye(8), 4, -1, False, 0.01, False)
+    assert res.scales[0].tolist() == [0.25, 0.25]
+    assert res.zeros[0].tolist() == [8, 2]
+    assert res.codes[0].tolist() == [0, 15, 10, 6, 8, 12, 8, 8]
+    assert res.codes[1].tolist() == [0, 14, 4, 0, 2, 2, 2, 2]
+    assert np.array_equal(O.rtn(W, 4, -1, False).codes, res.codes)
+
+
+def test_layer_error_is_output_error_on_explicit_tokens():
+    """layer_error(W, W^, 2 X^T X) equals the squared Frobenius norm of the
+    layer's output error X (W - W^)^T, summed here token by token and output
+    by output with scalar loops."""
+    rng = np.random.default_rng(3)
+    t, n, out = 7, 5, 3
+    X = rng.normal(size=(t, n))
+    W = rng.normal(size=(out, n))
+    Wh = W + rng.normal(size=(out, n)) * 0.1
+    want = 0.0
+    for tt in range(t):
+        for r in range(out):
+            y = sum(X[tt, k] * (W[r, k] - Wh[r, k]) for k in range(n))
+            want += y * y
+    assert O.layer_error(W, Wh, O.hessian(X)) == pytest.approx(want, rel=1e-13)
+    assert O.layer_error(W, W, O.hessian(X)) == 0.0
 
 
 # ------------------------------------------------------------ invariants --
@@ -544,43 +609,53 @@ def test_silu_mul_closed_forms():
     assert np.allclose(got, want, rtol=1e-15, atol=1e-15)
 
 
+def _silu_scalar(g):
+    return g / (1.0 + math.exp(-g))
+
+
 def test_mlp_block_down_hessian_from_quantized_gate_up():
-    # The down projection's Hessian comes from activations computed with the
-    # gate and up layers already quantized: rebuild it by hand from the
-    # returned gate/up results and compare, and check that it differs from
-    # the one the unquantized gate and up layers would give.
+    """The down projection's Hessian comes from activations computed with the
+    gate and up layers already quantized.  Rebuilt here token by token with
+    scalar loops from the dequantized weights (w^ = s (q - z), read from the
+    returned codes, scales, zeros and g_idx), and checked to differ from the
+    Hessian the unquantized gate and up layers would give."""
     rng = np.random.default_rng(5)
-    d, inter, t = 32, 64, 256
+    d, inter, t = 8, 12, 40
     X = rng.normal(size=(t, d)).astype(np.float16).astype(np.float64)
-    Wg = (rng.normal(size=(inter, d)) * 0.1).astype(np.float32)
-    Wu = (rng.normal(size=(inter, d)) * 0.1).astype(np.float32)
-    Wd = (rng.normal(size=(d, inter)) * 0.1).astype(np.float32)
-    r = O.mlp_block(X, Wg, Wu, Wd, 4, 16, False, 0.01, False)
-    def w16(res):   # fp16 scale times q - z, rounded to fp16, element by element
-        Wq = np.zeros(res.codes.shape)
-        for r_ in range(res.codes.shape[0]):
-            for k in range(res.codes.shape[1]):
-                g_ = res.g_idx[k]
-                s16 = float(np.float16(res.scales[g_, r_]))
-                Wq[r_, k] = float(np.float16(s16 * (res.codes[r_, k] - res.zeros[g_, r_])))
-        return Wq
-    G = X @ w16(r.gate).T
-    U = X @ w16(r.up).T
-    A = O.silu_mul(G.astype(np.float16), U.astype(np.float16)).astype(np.float16)
-    assert np.array_equal(A, r.A)
-    Hd = 2.0 * A.astype(np.float64).T @ A.astype(np.float64)
-    assert np.allclose(r.H_down, Hd, rtol=1e-12, atol=1e-9)
-    A16 = O.silu_mul((X @ Wg.astype(np.float64).T).astype(np.float16),
-                     (X @ Wu.astype(np.float64).T).astype(np.float16)).astype(np.float16)
-    H16 = 2.0 * A16.astype(np.float64).T @ A16.astype(np.float64)
-    assert np.linalg.norm(H16 - r.H_down) > 1e-3 * np.linalg.norm(H16)
+    Wg = (rng.normal(size=(inter, d)) * 0.3).astype(np.float32)
+    Wu = (rng.normal(size=(inter, d)) * 0.3).astype(np.float32)
+    Wd = (rng.normal(size=(d, inter)) * 0.3).astype(np.float32)
+    r = O.mlp_block(X, Wg, Wu, Wd, 3, 4, False, 0.01, True)
+
+    def wq(res, i, k):
+        g = int(res.g_idx[k])
+        return float(res.scales[g, i]) * (int(res.codes[i, k]) - int(res.zeros[g, i]))
+
+    def act(Wgate, Wup):
+        A = [[0.0] * inter for _ in range(t)]
+        for tt in range(t):
+            for i in range(inter):
+                gv = sum(X[tt, k] * Wgate(i, k) for k in range(d))
+                uv = sum(X[tt, k] * Wup(i, k) for k in range(d))
+                A[tt][i] = _silu_scalar(gv) * uv
+        return A
+
+    A = act(lambda i, k: wq(r.gate, i, k), lambda i, k: wq(r.up, i, k))
+    Hd = np.zeros((inter, inter))
+    for a in range(inter):
+        for b in range(inter):
+            Hd[a, b] = 2.0 * sum(A[tt][a] * A[tt][b] for tt in range(t))
+    assert np.allclose(r.H_down, Hd, rtol=1e-12, atol=1e-12)
+    A0 = act(lambda i, k: float(Wg[i, k]), lambda i, k: float(Wu[i, k]))
+    H0 = 2.0 * np.array(A0).T @ np.array(A0)
+    assert np.linalg.norm(H0 - r.H_down) > 1e-3 * np.linalg.norm(H0)
     # gate and up use the block input's Hessian: same as quantizing them alone
-    ref = O.gptq(Wg, 2.0 * X.T @ X, 4, 16, False, 0.01, False)
+    ref = O.gptq(Wg, 2.0 * X.T @ X, 3, 4, False, 0.01, True)
     assert np.array_equal(ref.codes, r.gate.codes)
     # the down layer's calibration error beats round-to-nearest on its inputs
     Wd64 = Wd.astype(np.float64)
     e = O.layer_error(Wd64, r.down.what, r.H_down)
-    e_rtn = O.layer_error(Wd64, O.rtn(Wd64, 4, 16, False).what, r.H_down)
+    e_rtn = O.layer_error(Wd64, O.rtn(Wd64, 3, 4, False).what, r.H_down)
     assert e < e_rtn
 
 
