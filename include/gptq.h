@@ -236,9 +236,11 @@ size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, i
  * Arithmetic: M <= 8 (HBM-bound on qweight) takes each weight exactly:
  * q - z as an fp16 integer times the fp16 activation, summed in fp32 over a
  * 32-input chunk, times the group's fp32 scale (s (q - z) in fp32 per
- * weight where a chunk mixes groups), fp32 accumulation; larger M rounds each dequantized weight to
- * fp16 (scale rounded to fp16, then one rounding of the product) and
- * multiplies on the fp16 matrix cores with fp32 accumulation.  Results do
+ * weight where a chunk mixes groups), fp32 accumulation; larger M rounds
+ * each dequantized weight to fp16 (the scale split into two fp16 parts and
+ * the weight formed in one fused rounding, close to the fp16 rounding of the
+ * exact s (q - z)) and multiplies on the fp16 matrix cores with fp32
+ * accumulation.  Results do
  * not depend on timing.  Calls that share a workspace must not overlap.
  * A chunk of 32 positions whose g_idx entries are all equal is dequantized
  * with one scale and zero; chunks that mix groups (act-order layers as
