@@ -15,6 +15,7 @@
  *
  * and around it:
  *   gptq_dequant_matmul       Y = X W^T from the packed layer (dequantized on the fly)
+ *   gptq_dequant_matmul_noalloc  the same without a workspace (fixed scratch)
  *   gptq_dequant_group_order  act-order layer -> group-sorted copy + x_order (once)
  *   gptq_silu_mul             gated activation between the MLP layers of a block
  *   gptq_export_params        fp16 scales + b-bit packed zeros, for saving
@@ -24,7 +25,8 @@
  *   - Every array argument is DEVICE memory owned by the caller (HIP device
  *     pointers), row-major, densely packed unless a leading dimension is given.
  *     The library never allocates or frees device memory; scratch space comes
- *     from the caller's workspace, sized by the *_workspace_bytes queries.
+ *     from the caller's workspace, sized by the *_workspace_bytes queries
+ *     (gptq_dequant_matmul_noalloc: a fixed per-device array instead).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *     work on it and return; nothing is synchronised.  Results are valid once
  *     the stream has reached that point.
@@ -254,6 +256,33 @@ int gptq_dequant_matmul(const void* X, int x_dtype, int64_t M, int64_t in, int64
                         const int32_t* g_idx, const int32_t* x_order, int64_t n_groups,
                         int64_t out, int bits, void* Y, int y_dtype, int64_t ldy,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Scratch (bytes) of gptq_dequant_matmul_noalloc: one fixed array per device. */
+#define GPTQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * gptq_dequant_matmul without a workspace, for callers that cannot allocate
+ * device memory: code under HIP stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments (minus the workspace), kernels and results, bit for bit, as
+ * gptq_dequant_matmul.  Its scratch is a fixed device array of
+ * GPTQ_NOALLOC_SCRATCH_BYTES (16 MiB) that each device holds until the
+ * process ends.  Every product with M <= 8 fits; a larger M fits while
+ * gptq_dequant_matmul_workspace_bytes(M, in, out, x_order != NULL) is at
+ * most that size, otherwise the call returns GPTQ_ERR_WORKSPACE before
+ * anything is enqueued.  The call allocates nothing (its first call on a
+ * device looks up that device's array address, once).  The stream must
+ * belong to the current device (else INVALID_ARG).  Calls that overlap on
+ * one device (two streams, two host threads) share its array and race:
+ * serialise them.
+ * Errors: as gptq_dequant_matmul; WORKSPACE when the scratch is too small.
+ */
+int gptq_dequant_matmul_noalloc(const void* X, int x_dtype, int64_t M, int64_t in, int64_t ldx,
+                                const int32_t* qweight, const float* scales, const int32_t* zeros,
+                                const int32_t* g_idx, const int32_t* x_order, int64_t n_groups,
+                                int64_t out, int bits, void* Y, int y_dtype, int64_t ldy,
+                                void* stream);
 
 /* Workspace (bytes) of gptq_dequant_group_order for in input positions. */
 size_t gptq_dequant_group_order_workspace_bytes(int64_t in);

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     dequant_group_order,
     dequant_group_order_workspace_bytes,
     dequant_matmul,
+    dequant_matmul_noalloc,
     dequant_matmul_workspace_bytes,
     export_params,
     hessian_accumulate,

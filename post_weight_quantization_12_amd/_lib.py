@@ -67,6 +67,9 @@ def load():
     lib.gptq_dequant_matmul.argtypes = [vp, c_int, i64, i64, i64, vp, vp, vp, vp, vp, i64, i64,
                                         c_int, vp, c_int, i64, vp, ctypes.c_size_t, vp]
     lib.gptq_dequant_matmul.restype = c_int
+    lib.gptq_dequant_matmul_noalloc.argtypes = [vp, c_int, i64, i64, i64, vp, vp, vp, vp, vp, i64,
+                                                i64, c_int, vp, c_int, i64, vp]
+    lib.gptq_dequant_matmul_noalloc.restype = c_int
     lib.gptq_dequant_group_order_workspace_bytes.argtypes = [i64]
     lib.gptq_dequant_group_order_workspace_bytes.restype = ctypes.c_size_t
     lib.gptq_dequant_group_order.argtypes = [vp, vp, i64, i64, c_int, vp, vp, vp, vp,
@@ -294,6 +297,46 @@ def dequant_matmul(X, qweight, scales, zeros, g_idx, bits: int, x_order=None, ou
                                    None if x_order is None else _ptr(x_order), G, out, bits,
                                    _ptr(Y), _dtype_code(Y.dtype), Y.stride(0) if M > 1 else out,
                                    ws_ptr, ws_bytes, _stream(stream)))
+    return Y
+
+
+def dequant_matmul_noalloc(X, qweight, scales, zeros, g_idx, bits: int, Y, x_order=None,
+                           stream=None):
+    """dequant_matmul through gptq_dequant_matmul_noalloc: no workspace (the
+    library's fixed per-device scratch) and no allocation here either, so Y
+    (fp32 or fp16 [M x out]) must be given."""
+    torch = _torch()
+    lib = load()
+    for name, t in (("X", X), ("qweight", qweight), ("scales", scales), ("zeros", zeros),
+                    ("g_idx", g_idx), ("Y", Y)):
+        _need_cuda(name, t)
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be [M x in] with unit column stride")
+    M, inp = X.shape
+    if qweight.dtype != torch.int32 or qweight.dim() != 2 or not qweight.is_contiguous():
+        raise ValueError("qweight must be a contiguous int32 [in*bits/32 x out] tensor")
+    if qweight.shape[0] * 32 != inp * bits:
+        raise ValueError("qweight rows must be in * bits / 32")
+    out = qweight.shape[1]
+    G = scales.shape[0]
+    if scales.dtype != torch.float32 or tuple(scales.shape) != (G, out) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous fp32 [n_groups x out] tensor")
+    if zeros.dtype != torch.int32 or tuple(zeros.shape) != (G, out) or not zeros.is_contiguous():
+        raise ValueError("zeros must be a contiguous int32 [n_groups x out] tensor")
+    if g_idx.dtype != torch.int32 or tuple(g_idx.shape) != (inp,):
+        raise ValueError("g_idx must be an int32 [in] tensor")
+    if x_order is not None:
+        _need_cuda("x_order", x_order)
+        if x_order.dtype != torch.int32 or tuple(x_order.shape) != (inp,):
+            raise ValueError("x_order must be an int32 [in] tensor")
+    if Y.dim() != 2 or tuple(Y.shape) != (M, out) or Y.stride(1) != 1:
+        raise ValueError("Y must be [M x out] with unit column stride")
+    _check(lib.gptq_dequant_matmul_noalloc(_ptr(X), _dtype_code(X.dtype), M, inp,
+                                           X.stride(0) if M > 1 else inp, _ptr(qweight),
+                                           _ptr(scales), _ptr(zeros), _ptr(g_idx),
+                                           None if x_order is None else _ptr(x_order), G, out,
+                                           bits, _ptr(Y), _dtype_code(Y.dtype),
+                                           Y.stride(0) if M > 1 else out, _stream(stream)))
     return Y
 
 

@@ -127,6 +127,12 @@ hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
                               const int32_t* g_idx, const int32_t* x_order, int64_t out, int bits,
                               void* Y, int y_f16, int64_t ldy, void* ws, size_t ws_bytes,
                               hipStream_t s);
+// Host-side argument checks of the dequantize-on-the-fly entry points: a
+// gptq_status_t (GPTQ_OK, or the failure with gptq_last_error_message set).
+int dequant_check(const void* X, int x_dtype, int64_t M, int64_t in, int64_t ldx,
+                  const int32_t* qweight, const float* scales, const int32_t* zeros,
+                  const int32_t* g_idx, int64_t n_groups, int64_t out, int bits, const void* Y,
+                  int y_dtype, int64_t ldy);
 // Storage form of the group parameters: fp16 scales, zeros packed b-bit
 // along the output channels (out * bits % 32 == 0), and the inverse.
 hipError_t run_export(const float* scales, const int32_t* zeros, int64_t G, int64_t out, int bits,

@@ -21,7 +21,8 @@ def test_exports_every_header_function(lib):
                           "gptq_prepare_workspace_bytes",
                           "gptq_prepare", "gptq_quantize_workspace_bytes",
                           "gptq_quantize_layer", "gptq_dequant_matmul_workspace_bytes",
-                          "gptq_dequant_matmul", "gptq_dequant_group_order_workspace_bytes",
+                          "gptq_dequant_matmul", "gptq_dequant_matmul_noalloc",
+                          "gptq_dequant_group_order_workspace_bytes",
                           "gptq_dequant_group_order", "gptq_silu_mul", "gptq_export_params",
                           "gptq_unpack_zeros", "gptq_status_string",
                           "gptq_last_error_message"}
@@ -200,3 +201,28 @@ def test_export_argument_errors(lib):
     g = lib.gptq_unpack_zeros
     assert g(None, 2, 8, 4, FAKE, None) == L.GPTQ_ERR_INVALID_ARG
     assert g(FAKE, 2, 10, 3, FAKE, None) == L.GPTQ_ERR_UNSUPPORTED            # 30 bits a row
+
+
+def test_dequant_matmul_noalloc_host_checks(lib):
+    """The fixed-scratch variant checks its arguments like gptq_dequant_matmul
+    and refuses, before any HIP call, a product whose scratch would exceed
+    the fixed size."""
+    f = lib.gptq_dequant_matmul_noalloc
+    A16 = ctypes.c_void_p(4096)
+
+    def call(M=2, inp=64, out=8, X=A16, xo=None, bits=4):
+        return f(X, L.GPTQ_F16, M, inp, inp, FAKE, FAKE, FAKE, FAKE, xo, 2, out, bits, FAKE,
+                 L.GPTQ_F32, out, None)
+
+    assert call(X=None) == L.GPTQ_ERR_INVALID_ARG
+    assert call(bits=5) == L.GPTQ_ERR_UNSUPPORTED
+    assert call(M=0) == L.GPTQ_OK
+    # 2048 act-order tokens of the 11008-input layer: the gathered X alone is
+    # 2048 * 11008 * 2 bytes, beyond the fixed 16 MiB
+    assert lib.gptq_dequant_matmul_workspace_bytes(2048, 11008, 4096, 1) > 16 << 20
+    assert call(M=2048, inp=11008, out=4096, xo=FAKE) == L.GPTQ_ERR_WORKSPACE
+    assert b"16777216" in lib.gptq_last_error_message()
+    # every decode product (M <= 8) fits, up to the 70B down_proj shape
+    for M in (1, 2, 4, 8):
+        for inp, out in ((4096, 4096), (11008, 4096), (28672, 8192), (8192, 28672)):
+            assert lib.gptq_dequant_matmul_workspace_bytes(M, inp, out, 1) <= 16 << 20
