@@ -18,6 +18,8 @@
  *   gptq_dequant_matmul_noalloc  the same without a workspace (fixed scratch)
  *   gptq_dequant_group_order  act-order layer -> group-sorted copy + x_order (once)
  *   gptq_silu_mul             gated activation between the MLP layers of a block
+ *   gptq_attention_forward    attention between the q/k/v and o projections of a block
+ *   gptq_residual_rmsnorm     residual add + RMS norm between the attention and the MLP
  *   gptq_export_params        fp16 scales + b-bit packed zeros, for saving
  *   gptq_unpack_zeros         zeros from their packed form, after loading
  *
@@ -332,6 +334,55 @@ int gptq_dequant_group_order(const int32_t* qweight, const int32_t* g_idx, int64
  */
 int gptq_silu_mul(const void* G, int64_t ldg, const void* U, int64_t ldu, int64_t rows,
                   int64_t cols, void* A, int64_t lda, void* stream);
+
+/*
+ * Multi-head attention of a Llama-style decoder block, per sequence:
+ *     O[t][h] = sum_{s} softmax_s(Q[t][h] . K[s][h] / sqrt(head_dim)) V[s][h],
+ * s over the keys of t's own sequence (s <= t when causal != 0).
+ *
+ * The layer-wise method quantizes one layer at a time from calibration
+ * activations computed through the block (glossary entry "gptq", paragraph
+ * "Method" (1) and (3)); the output projection's calibration inputs are
+ * this attention of the query, key and value projections.  The pages do not
+ * give the block's arithmetic: causal softmax attention without positional
+ * rotation is a reading (rotation changes the inputs, not the method).
+ *
+ *   Q, K, V  fp16 [seqs * seq_len x >= heads * head_dim], row-major with
+ *            leading dimensions ldq, ldk, ldv; sequence b is rows
+ *            b * seq_len .. b * seq_len + seq_len - 1; head h is columns
+ *            h * head_dim .. + head_dim - 1 (they may be the three parts of
+ *            one [tokens x 3 d] matrix).
+ *   O        out: fp16, same layout, leading dimension ldo.
+ *   head_dim 64 or 128; heads <= 65535; seqs <= 65535 per call.
+ *   Pointers 16-byte aligned, leading dimensions multiples of 8.
+ * Arithmetic: fp32 scores, softmax (exp2) and accumulation; the softmax
+ * weights enter the value product as fp16; O rounded once to fp16.  seqs or
+ * seq_len == 0 is a no-op.  Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+int gptq_attention_forward(const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V,
+                           int64_t ldv, void* O, int64_t ldo, int64_t seqs, int64_t seq_len,
+                           int heads, int head_dim, int causal, void* stream);
+
+/*
+ * Residual add and RMS normalization between the attention and MLP halves of
+ * a Llama-style decoder block, per row r:
+ *     Hs[r] = X[r] + A[r]                         (the residual stream, fp16)
+ *     U[r]  = Hs[r] / sqrt(mean_c Hs[r][c]^2 + eps) * gamma
+ *
+ * The MLP's calibration inputs are computed through the block with the
+ * attention layers already quantized (glossary entry "gptq", paragraph
+ * "Method" (1)); the normalization is the Llama block's (a reading).
+ *
+ *   X, A     fp16 [rows x d] (leading dimensions ldx, lda >= d).
+ *   gamma    fp16 [d].
+ *   Hs, U    out: fp16 [rows x d] (ldh, ldu >= d).
+ *   eps      finite, >= 0.
+ * Sums in fp32 over the fp16 Hs; one rounding of each output.  rows == 0 is
+ * a no-op.  Errors: INVALID_ARG, HIP.
+ */
+int gptq_residual_rmsnorm(const void* X, int64_t ldx, const void* A, int64_t lda,
+                          const void* gamma, int64_t rows, int64_t d, float eps, void* Hs,
+                          int64_t ldh, void* U, int64_t ldu, void* stream);
 
 /*
  * Storage form of a layer's group parameters, for saving it.

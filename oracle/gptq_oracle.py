@@ -59,6 +59,10 @@ __all__ = [
     "silu_mul",
     "BlockResult",
     "mlp_block",
+    "attention",
+    "residual_rmsnorm",
+    "DecoderResult",
+    "decoder_block",
     "layer_error",
 ]
 
@@ -511,6 +515,90 @@ def mlp_block(X, Wg, Wu, Wd, bits: int, group_size: int, sym: bool, damp_percent
     H_down = hessian(A)
     down = gptq(Wd, H_down, bits, group_size, sym, damp_percent, desc_act)
     return BlockResult(H_in=H_in, gate=gate, up=up, A=A, H_down=H_down, down=down)
+
+
+def attention(Q, K, V, seq_len: int, heads: int, causal: bool = True) -> np.ndarray:
+    """Multi-head softmax attention per sequence, float64.
+
+    [GLOSS] paragraph "Method" (1) and (3): each layer's calibration inputs
+    are computed through the model; in a Llama decoder block the output
+    projection's input is the attention of the query, key and value
+    projections.  The pages do not give the block's arithmetic; the reading
+    is plain scaled dot-product attention per head, causal (a decoder
+    model), without positional rotation:
+        O[t, head] = sum_s P[t, s] V[s, head],
+        P[t, :] = softmax_s(Q[t, head] . K[s, head] / sqrt(hd)), s <= t.
+    Q, K, V: [tokens x heads * hd], tokens = seqs * seq_len, sequences
+    contiguous.  The largest score of a row is subtracted before the
+    exponential (the same softmax in exact arithmetic).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    tokens, w = Q.shape
+    hd = w // heads
+    O = np.zeros((tokens, w))
+    for b in range(tokens // seq_len):
+        rows = slice(b * seq_len, (b + 1) * seq_len)
+        for h in range(heads):
+            cols = slice(h * hd, (h + 1) * hd)
+            S = Q[rows, cols] @ K[rows, cols].T / math.sqrt(hd)
+            if causal:
+                S[np.triu_indices(seq_len, 1)] = -np.inf
+            S = S - S.max(axis=1, keepdims=True)
+            P = np.exp(S)
+            P /= P.sum(axis=1, keepdims=True)
+            O[rows, cols] = P @ V[rows, cols]
+    return O
+
+
+def residual_rmsnorm(X, A, gamma, eps: float):
+    """(Hs, U): the residual stream Hs = X + A and its RMS normalization
+    U = Hs / sqrt(mean(Hs^2) + eps) * gamma per row, float64 (the Llama
+    block's normalization before the MLP; a reading, the pages do not give
+    the block's arithmetic)."""
+    Hs = np.asarray(X, dtype=np.float64) + np.asarray(A, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(Hs * Hs, axis=1, keepdims=True) + float(eps))
+    return Hs, Hs * r * np.asarray(gamma, dtype=np.float64)[None, :]
+
+
+@dataclass
+class DecoderResult:
+    H_x: np.ndarray         # 2 X^T X of the block input (q, k, v)
+    q: SweepResult
+    k: SweepResult
+    v: SweepResult
+    O: np.ndarray           # attention output: the output projection's inputs
+    H_o: np.ndarray         # 2 O^T O
+    o: SweepResult
+    U: np.ndarray           # normalized residual stream: the MLP's inputs
+    mlp: BlockResult        # gate, up (H = 2 U^T U), down
+
+
+def decoder_block(X, Wq, Wk, Wv, Wo, gamma, Wg, Wu, Wd, heads: int, seq_len: int, eps: float,
+                  bits: int, group_size: int, sym: bool, damp_percent: float,
+                  desc_act: bool) -> DecoderResult:
+    """Layer-wise GPTQ over a Llama-style decoder block, float64 forward.
+
+    [GLOSS] paragraph "Method" (1): one layer at a time, each from
+    calibration activations computed through the block with the layers
+    before it already quantized.  Readings: q, k and v share the block
+    input, hence one Hessian; the output projection is calibrated on the
+    attention of the quantized q, k, v; the MLP on the normalized residual
+    stream X + O W^o^T after the quantized output projection (then as in
+    ``mlp_block``).
+    """
+    X64 = np.asarray(X, dtype=np.float64)
+    H_x = hessian(X64)
+    q = gptq(Wq, H_x, bits, group_size, sym, damp_percent, desc_act)
+    k = gptq(Wk, H_x, bits, group_size, sym, damp_percent, desc_act)
+    v = gptq(Wv, H_x, bits, group_size, sym, damp_percent, desc_act)
+    O = attention(X64 @ q.what.T, X64 @ k.what.T, X64 @ v.what.T, seq_len, heads)
+    H_o = hessian(O)
+    o = gptq(Wo, H_o, bits, group_size, sym, damp_percent, desc_act)
+    _, U = residual_rmsnorm(X64, O @ o.what.T, gamma, eps)
+    mlp = mlp_block(U, Wg, Wu, Wd, bits, group_size, sym, damp_percent, desc_act)
+    return DecoderResult(H_x=H_x, q=q, k=k, v=v, O=O, H_o=H_o, o=o, U=U, mlp=mlp)
 
 
 def layer_error(W, What, H) -> float:

@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     GPTQ_BF16,
     GPTQ_F16,
     GPTQ_F32,
+    attention_forward,
     dequant_group_order,
     dequant_group_order_workspace_bytes,
     dequant_matmul,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     prepare_workspace_bytes,
     quantize_layer,
     quantize_workspace_bytes,
+    residual_rmsnorm,
     silu_mul,
     unpack_zeros,
 )

@@ -77,6 +77,12 @@ def load():
     lib.gptq_dequant_group_order.restype = c_int
     lib.gptq_silu_mul.argtypes = [vp, i64, vp, i64, i64, i64, vp, i64, vp]
     lib.gptq_silu_mul.restype = c_int
+    lib.gptq_attention_forward.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, c_int,
+                                           c_int, c_int, vp]
+    lib.gptq_attention_forward.restype = c_int
+    lib.gptq_residual_rmsnorm.argtypes = [vp, i64, vp, i64, vp, i64, i64, ctypes.c_float, vp,
+                                          i64, vp, i64, vp]
+    lib.gptq_residual_rmsnorm.restype = c_int
     lib.gptq_export_params.argtypes = [vp, vp, i64, i64, c_int, vp, vp, vp]
     lib.gptq_export_params.restype = c_int
     lib.gptq_unpack_zeros.argtypes = [vp, i64, i64, c_int, vp, vp]
@@ -395,6 +401,67 @@ def silu_mul(G, U, A=None, stream=None):
     _check(lib.gptq_silu_mul(_ptr(G), ld(G), _ptr(U), ld(U), rows, cols, _ptr(A), ld(A),
                              _stream(stream)))
     return A
+
+
+def attention_forward(Q, K, V, seq_len: int, heads: int, causal: bool = True, O=None,
+                      stream=None):
+    """O = softmax(Q K^T / sqrt(hd)) V per sequence and head for fp16
+    Q, K, V [tokens x heads * hd] (unit column stride; views of one matrix
+    are fine); tokens = seqs * seq_len, hd = 64 or 128.  O: fp16 out,
+    allocated when None."""
+    torch = _torch()
+    lib = load()
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        _need_cuda(name, t)
+        if t.dtype != torch.float16 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be fp16 [tokens x heads*hd] with unit column stride")
+    if not (Q.shape == K.shape == V.shape):
+        raise ValueError("Q, K and V must have the same shape")
+    tokens, w = Q.shape
+    if seq_len < 1 or tokens % seq_len:
+        raise ValueError("tokens must be a multiple of seq_len")
+    if heads < 1 or w % heads:
+        raise ValueError("the width must be heads * head_dim")
+    if O is None:
+        with _on(stream):
+            O = torch.empty((tokens, w), dtype=torch.float16, device=Q.device)
+    if O.dtype != torch.float16 or tuple(O.shape) != (tokens, w) or O.stride(1) != 1:
+        raise ValueError("O must be fp16 [tokens x heads*hd] with unit column stride")
+    ld = lambda t: t.stride(0) if tokens > 1 else w
+    _check(lib.gptq_attention_forward(_ptr(Q), ld(Q), _ptr(K), ld(K), _ptr(V), ld(V), _ptr(O),
+                                      ld(O), tokens // seq_len, seq_len, heads, w // heads,
+                                      int(bool(causal)), _stream(stream)))
+    return O
+
+
+def residual_rmsnorm(X, A, gamma, eps: float, Hs=None, U=None, stream=None):
+    """(Hs, U): Hs = X + A, U = Hs / sqrt(mean(Hs^2) + eps) * gamma, rows of
+    fp16 [rows x d] (unit column stride), gamma fp16 [d]."""
+    torch = _torch()
+    lib = load()
+    for name, t in (("X", X), ("A", A), ("gamma", gamma)):
+        _need_cuda(name, t)
+    for name, t in (("X", X), ("A", A)):
+        if t.dtype != torch.float16 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be fp16 [rows x d] with unit column stride")
+    if X.shape != A.shape:
+        raise ValueError("X and A must have the same shape")
+    rows, d = X.shape
+    if gamma.dtype != torch.float16 or tuple(gamma.shape) != (d,) or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous fp16 [d] tensor")
+    with _on(stream):
+        if Hs is None:
+            Hs = torch.empty((rows, d), dtype=torch.float16, device=X.device)
+        if U is None:
+            U = torch.empty((rows, d), dtype=torch.float16, device=X.device)
+    for name, t in (("Hs", Hs), ("U", U)):
+        if t.dtype != torch.float16 or tuple(t.shape) != (rows, d) or t.stride(1) != 1:
+            raise ValueError(f"{name} must be fp16 [rows x d] with unit column stride")
+    ld = lambda t: t.stride(0) if rows > 1 else d
+    _check(lib.gptq_residual_rmsnorm(_ptr(X), ld(X), _ptr(A), ld(A), _ptr(gamma), rows, d,
+                                     float(eps), _ptr(Hs), ld(Hs), _ptr(U), ld(U),
+                                     _stream(stream)))
+    return Hs, U
 
 
 def export_params(scales, zeros, bits: int, stream=None):

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgptq_mi355x.so")
 SOURCES = ["api.hip", "syrk.hip", "gemm_f32.hip", "prepare.hip", "quantize.hip", "dequant_matmul.hip",
-           "activation.hip", "export.hip", "noalloc.hip"]
+           "activation.hip", "attention.hip", "export.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

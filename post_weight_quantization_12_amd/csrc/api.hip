@@ -263,6 +263,48 @@ int gptq_silu_mul(const void* G, int64_t ldg, const void* U, int64_t ldu, int64_
                     "gptq_silu_mul");
 }
 
+int gptq_attention_forward(const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V,
+                           int64_t ldv, void* O, int64_t ldo, int64_t seqs, int64_t seq_len,
+                           int heads, int head_dim, int causal, void* stream) {
+  clear_error();
+  if (!Q || !K || !V || !O) return fail(GPTQ_ERR_INVALID_ARG, "Q, K, V or O is NULL");
+  if (seqs < 0 || seq_len < 0) return fail(GPTQ_ERR_INVALID_ARG, "seqs and seq_len must be >= 0");
+  if (heads < 1 || heads > 65535) return fail(GPTQ_ERR_INVALID_ARG, "heads must be in [1, 65535]");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(GPTQ_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  const int64_t w = (int64_t)heads * head_dim;
+  if (ldq < w || ldk < w || ldv < w || ldo < w)
+    return fail(GPTQ_ERR_INVALID_ARG, "leading dimensions must be >= heads * head_dim");
+  if (ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8 ||
+      ((reinterpret_cast<uintptr_t>(Q) | reinterpret_cast<uintptr_t>(K) |
+        reinterpret_cast<uintptr_t>(V) | reinterpret_cast<uintptr_t>(O)) & 15))
+    return fail(GPTQ_ERR_UNSUPPORTED,
+                "Q, K, V, O must be 16-byte aligned with leading dimensions a multiple of 8");
+  if (seqs > 65535) return fail(GPTQ_ERR_UNSUPPORTED, "seqs must be <= 65535 per call");
+  if (seq_len > (int64_t)1 << 30) return fail(GPTQ_ERR_UNSUPPORTED, "seq_len must be <= 2^30");
+  if (seqs == 0 || seq_len == 0) return GPTQ_OK;
+  return hip_status(run_attention(Q, ldq, K, ldk, V, ldv, O, ldo, seqs, seq_len, heads, head_dim,
+                                  causal ? 1 : 0, static_cast<hipStream_t>(stream)),
+                    "gptq_attention_forward");
+}
+
+int gptq_residual_rmsnorm(const void* X, int64_t ldx, const void* A, int64_t lda,
+                          const void* gamma, int64_t rows, int64_t d, float eps, void* Hs,
+                          int64_t ldh, void* U, int64_t ldu, void* stream) {
+  clear_error();
+  if (!X || !A || !gamma || !Hs || !U)
+    return fail(GPTQ_ERR_INVALID_ARG, "X, A, gamma, Hs or U is NULL");
+  if (rows < 0 || d < 1) return fail(GPTQ_ERR_INVALID_ARG, "rows must be >= 0 and d >= 1");
+  if (ldx < d || lda < d || ldh < d || ldu < d)
+    return fail(GPTQ_ERR_INVALID_ARG, "leading dimensions must be >= d");
+  if (!(eps >= 0.0f) || !std::isfinite(eps))
+    return fail(GPTQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (rows == 0) return GPTQ_OK;
+  return hip_status(run_residual_rmsnorm(X, ldx, A, lda, gamma, rows, d, eps, Hs, ldh, U, ldu,
+                                         static_cast<hipStream_t>(stream)),
+                    "gptq_residual_rmsnorm");
+}
+
 int gptq_export_params(const float* scales, const int32_t* zeros, int64_t n_groups, int64_t out,
                        int bits, void* scales_f16, int32_t* qzeros, void* stream) {
   clear_error();

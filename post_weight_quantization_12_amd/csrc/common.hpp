@@ -144,6 +144,16 @@ hipError_t run_unpack_zeros(const int32_t* qzeros, int64_t G, int64_t out, int b
 hipError_t run_silu_mul(const void* G, int64_t ldg, const void* U, int64_t ldu, int64_t rows,
                         int64_t cols, void* A, int64_t lda, hipStream_t s);
 
+// Causal (or full) multi-head attention per sequence, fp16 in and out, fp32
+// softmax and accumulation; head_dim 64 or 128.
+hipError_t run_attention(const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V,
+                         int64_t ldv, void* O, int64_t ldo, int64_t seqs, int64_t seq_len,
+                         int heads, int head_dim, int causal, hipStream_t s);
+// Hs = X + A and U = RMSNorm(Hs) * gamma, rows of d fp16 values.
+hipError_t run_residual_rmsnorm(const void* X, int64_t ldx, const void* A, int64_t lda,
+                                const void* gamma, int64_t rows, int64_t d, float eps, void* Hs,
+                                int64_t ldh, void* U, int64_t ldu, hipStream_t s);
+
 // The layer's input positions re-ordered by group (stable), repacked.
 size_t dequant_group_order_workspace_bytes(int64_t in);
 hipError_t run_dequant_group_order(const int32_t* qweight, const int32_t* g_idx, int64_t in,

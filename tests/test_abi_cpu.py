@@ -23,7 +23,8 @@ def test_exports_every_header_function(lib):
                           "gptq_quantize_layer", "gptq_dequant_matmul_workspace_bytes",
                           "gptq_dequant_matmul", "gptq_dequant_matmul_noalloc",
                           "gptq_dequant_group_order_workspace_bytes",
-                          "gptq_dequant_group_order", "gptq_silu_mul", "gptq_export_params",
+                          "gptq_dequant_group_order", "gptq_silu_mul", "gptq_attention_forward",
+                          "gptq_residual_rmsnorm", "gptq_export_params",
                           "gptq_unpack_zeros", "gptq_status_string",
                           "gptq_last_error_message"}
     for n in names:

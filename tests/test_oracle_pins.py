@@ -659,6 +659,111 @@ def test_mlp_block_down_hessian_from_quantized_gate_up():
     assert e < e_rtn
 
 
+def _attn_scalar(Q, K, V, seq_len, heads, causal):
+    """Attention with scalar loops and math.exp (no max subtraction)."""
+    tokens, w = len(Q), len(Q[0])
+    hd = w // heads
+    O = [[0.0] * w for _ in range(tokens)]
+    for t in range(tokens):
+        b0 = (t // seq_len) * seq_len
+        for h in range(heads):
+            keys = range(b0, t + 1) if causal else range(b0, b0 + seq_len)
+            sc = {s_: math.exp(sum(Q[t][h * hd + i] * K[s_][h * hd + i] for i in range(hd))
+                               / math.sqrt(hd)) for s_ in keys}
+            z = sum(sc.values())
+            for i in range(hd):
+                O[t][h * hd + i] = sum(sc[s_] * V[s_][h * hd + i] for s_ in keys) / z
+    return np.array(O)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_brute_force(causal):
+    rng = np.random.default_rng(21)
+    seq_len, heads, hd = 4, 2, 3
+    Q, K, V = (rng.normal(size=(2 * seq_len, heads * hd)) for _ in range(3))
+    got = O.attention(Q, K, V, seq_len, heads, causal)
+    want = _attn_scalar(Q.tolist(), K.tolist(), V.tolist(), seq_len, heads, causal)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(22)
+    seq_len, heads, hd = 5, 2, 4
+    Q = rng.normal(size=(2 * seq_len, heads * hd))
+    V = rng.normal(size=(2 * seq_len, heads * hd))
+    # equal scores (K = 0): causal attention is the running mean of V within
+    # each sequence, full attention the sequence mean
+    Oc = O.attention(Q, np.zeros_like(Q), V, seq_len, heads, True)
+    Of = O.attention(Q, np.zeros_like(Q), V, seq_len, heads, False)
+    for b in range(2):
+        blk = V[b * seq_len:(b + 1) * seq_len]
+        run = np.cumsum(blk, axis=0) / np.arange(1, seq_len + 1)[:, None]
+        assert np.allclose(Oc[b * seq_len:(b + 1) * seq_len], run, rtol=1e-13, atol=1e-14)
+        assert np.allclose(Of[b * seq_len:(b + 1) * seq_len], blk.mean(axis=0), rtol=1e-13)
+    # the first token of a causal sequence attends to itself only
+    Oq = O.attention(Q, rng.normal(size=Q.shape), V, seq_len, heads, True)
+    assert np.allclose(Oq[[0, seq_len]], V[[0, seq_len]], rtol=1e-14)
+
+
+def test_residual_rmsnorm_closed_forms():
+    rng = np.random.default_rng(23)
+    X = rng.normal(size=(3, 6))
+    A = rng.normal(size=(3, 6))
+    g = rng.normal(size=6)
+    Hs, U = O.residual_rmsnorm(X, A, g, 1e-5)
+    assert np.array_equal(Hs, X + A)
+    for r in range(3):
+        ms = sum(v * v for v in Hs[r]) / 6
+        for c in range(6):
+            assert U[r, c] == pytest.approx(Hs[r, c] / math.sqrt(ms + 1e-5) * g[c], rel=1e-13)
+    # a constant row c with eps = 0 normalizes to sign(c) * gamma
+    _, Uc = O.residual_rmsnorm(np.full((2, 6), -2.5), np.zeros((2, 6)), g, 0.0)
+    assert np.allclose(Uc, -g[None, :], rtol=1e-15)
+
+
+def test_decoder_block_hessians_through_quantized_layers():
+    """The output projection's Hessian is 2 O^T O with O the attention of the
+    quantized q, k, v; the MLP's is 2 U^T U with U the normalized residual
+    stream after the quantized o.  Rebuilt with scalar loops from the
+    dequantized weights (codes, scales, zeros, g_idx) of the returned
+    layers; the unquantized path gives a different H_o."""
+    rng = np.random.default_rng(24)
+    d, inter, heads, seq_len, seqs = 8, 12, 2, 5, 2
+    X = rng.normal(size=(seqs * seq_len, d)).astype(np.float16).astype(np.float64)
+    Ws = [(rng.normal(size=(d, d)) * 0.3) for _ in range(4)]
+    gamma = 1.0 + 0.1 * rng.normal(size=d)
+    Wg, Wu = rng.normal(size=(inter, d)) * 0.3, rng.normal(size=(inter, d)) * 0.3
+    Wd = rng.normal(size=(d, inter)) * 0.3
+    r = O.decoder_block(X, *Ws, gamma, Wg, Wu, Wd, heads, seq_len, 1e-6, 3, 4, False, 0.01, True)
+
+    def wq(res, i, k):
+        g = int(res.g_idx[k])
+        return float(res.scales[g, i]) * (int(res.codes[i, k]) - int(res.zeros[g, i]))
+
+    def proj(Xl, res):
+        return [[sum(Xl[t][k] * wq(res, i, k) for k in range(len(Xl[0])))
+                 for i in range(res.codes.shape[0])] for t in range(len(Xl))]
+
+    Xl = X.tolist()
+    Oat = _attn_scalar(proj(Xl, r.q), proj(Xl, r.k), proj(Xl, r.v), seq_len, heads, True)
+    assert np.allclose(r.O, Oat, rtol=1e-11, atol=1e-12)
+    Ho = np.array([[2.0 * sum(Oat[t, a] * Oat[t, b] for t in range(len(Xl)))
+                    for b in range(d)] for a in range(d)])
+    assert np.allclose(r.H_o, Ho, rtol=1e-11, atol=1e-12)
+    O0 = _attn_scalar((X @ Ws[0].T).tolist(), (X @ Ws[1].T).tolist(), (X @ Ws[2].T).tolist(),
+                      seq_len, heads, True)
+    H0 = 2.0 * O0.T @ O0
+    assert np.linalg.norm(H0 - r.H_o) > 1e-4 * np.linalg.norm(H0)
+    AO = proj(Oat.tolist(), r.o)
+    U = np.zeros((len(Xl), d))
+    for t in range(len(Xl)):
+        hs = [Xl[t][c] + AO[t][c] for c in range(d)]
+        rr = 1.0 / math.sqrt(sum(v * v for v in hs) / d + 1e-6)
+        U[t] = [hs[c] * rr * gamma[c] for c in range(d)]
+    assert np.allclose(r.U, U, rtol=1e-11, atol=1e-12)
+    assert np.allclose(r.mlp.H_in, 2.0 * U.T @ U, rtol=1e-11, atol=1e-12)
+
+
 def test_pack_zeros_hand_example():
     # 4-bit zeros 1..8 of one group row -> one word 0x87654321; 3-bit zeros
     # 7, 0, 5 start a stream whose low bits are 0b101_000_111 = 0x147;

@@ -27,7 +27,7 @@ import torch
 
 __all__ = ["Config", "CONFIGS", "get", "weight", "x_sample", "x_tokens",
            "outlier_channels", "boundary_safe_weight", "synthetic_hinv_chol",
-           "generator", "packed_layer_draws", "mlp_block_weights"]
+           "generator", "packed_layer_draws", "mlp_block_weights", "decoder_block_weights"]
 
 
 @dataclass(frozen=True)
@@ -259,3 +259,14 @@ def mlp_block_weights(d: int, inter: int, device="cpu", seed: int = 0):
     wu = _randn((inter, d), device, seed, 21, 0, d) * 0.02
     wd = _randn((d, inter), device, seed, 22, 0, d) * 0.015
     return wg.to(torch.float16), wu.to(torch.float16), wd.to(torch.float16)
+
+
+def decoder_block_weights(d: int, inter: int, device="cpu", seed: int = 0):
+    """(Wq, Wk, Wv, Wo [d x d], gamma [d], Wg, Wu [inter x d], Wd [d x inter])
+    fp16 for a Llama-style decoder block: the projections ~ N(0, 0.02^2)
+    (N(0, 0.015^2) for the down projection, as the down_proj-shaped layer),
+    the norm weight 1 + N(0, 0.05^2); drawn in fp32, rounded to fp16."""
+    wq, wk, wv, wo = (_randn((d, d), device, seed, 23 + i, 0, d) * 0.02 for i in range(4))
+    gamma = 1.0 + 0.05 * _randn((d,), device, seed, 27, 0, d)
+    wg, wu, wd = mlp_block_weights(d, inter, device, seed)
+    return tuple(t.to(torch.float16) for t in (wq, wk, wv, wo, gamma)) + (wg, wu, wd)
