@@ -875,9 +875,7 @@ def block_cpu_baseline(d, inter, bits, gs, sym, desc, X, Wg, Wu, Wd, samples):
     O.gptq_sweep(wg[:rows], U, perm, bits, gs, sym)
     t["sweep_gate"] = time.perf_counter() - t0
     t0 = time.perf_counter()
-    G = (x @ wg.T).astype(np.float16)
-    Uu = (x @ wu.T).astype(np.float16)
-    A = O.silu_mul(G, Uu).astype(np.float16)
+    A = O.silu_mul(x @ wg.T, x @ wu.T)
     H2 = O.hessian(A)
     t["forward_hessian_down"] = time.perf_counter() - t0
     t0 = time.perf_counter()
@@ -1005,6 +1003,159 @@ def block_main(args):
     print(json.dumps(result), flush=True)
 
 
+def decoder_cpu_baseline(d, inter, heads, seq_len, bits, gs, sym, desc, X, Ws, samples):
+    """The oracle on a bounded sample of the decoder block: the Hessians and
+    the forward of one sequence (scaled to all sequences), the four
+    factorizations in full, 32-row sweeps of each layer (scaled to all
+    rows); fp64 NumPy."""
+    import torch
+
+    import oracle as O
+
+    torch.set_num_threads(max(1, len(os.sched_getaffinity(0))))
+    x = X[:seq_len].cpu().double().numpy()
+    wq, wk, wv, wo, gm, wg, wu, wd = (w.cpu().double().numpy() for w in Ws)
+    rows = 32
+    t = {"hessians_forward": 0.0, "prepare": 0.0, "sweeps": 0.0}
+
+    def timed(key, f, *a):
+        t0 = time.perf_counter()
+        r = f(*a)
+        t[key] += time.perf_counter() - t0
+        return r
+
+    def factor(H):
+        Hd_, _ = O.condition(H, 0.01)
+        perm = O.column_order(H, desc)
+        return O.hinv_chol(Hd_, perm), perm
+
+    Hx = timed("hessians_forward", O.hessian, x)
+    Ux, px = timed("prepare", factor, Hx)
+    for w in (wq, wk, wv):
+        timed("sweeps", O.gptq_sweep, w[:rows], Ux, px, bits, gs, sym)
+    att = timed("hessians_forward", lambda: O.attention(x @ wq.T, x @ wk.T, x @ wv.T, seq_len,
+                                                         heads))
+    Ho = timed("hessians_forward", O.hessian, att)
+    Uo, po = timed("prepare", factor, Ho)
+    timed("sweeps", O.gptq_sweep, wo[:rows], Uo, po, bits, gs, sym)
+    _, u = timed("hessians_forward", O.residual_rmsnorm, x, att @ wo.T, gm, 1e-5)
+    Hm = timed("hessians_forward", O.hessian, u)
+    Um, pm = timed("prepare", factor, Hm)
+    for w in (wg, wu):
+        timed("sweeps", O.gptq_sweep, w[:rows], Um, pm, bits, gs, sym)
+    a = timed("hessians_forward", lambda: O.silu_mul(u @ wg.T, u @ wu.T))
+    Hd2 = timed("hessians_forward", O.hessian, a)
+    Ud, pd = timed("prepare", factor, Hd2)
+    t_sd = time.perf_counter()
+    O.gptq_sweep(wd[:rows], Ud, pd, bits, gs, sym)
+    t_sd = time.perf_counter() - t_sd
+    t["sweeps"] += t_sd
+    # rows: q, k, v, o, down have d rows, gate and up inter rows (32 each swept)
+    t_sweep_full = (t["sweeps"] - t_sd) / 6 * (4 * d + 2 * inter) / rows + t_sd * d / rows
+    full = t["hessians_forward"] * samples + t["prepare"] + t_sweep_full
+    return {
+        "value": (4.0 * d * d + 3.0 * d * inter) / full,
+        "unit": "weights/s",
+        "cores": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "host": host_description(),
+        "sample": (f"one {seq_len}-token sequence for the Hessians and the forward (scaled "
+                   f"x{samples}), the four factorizations in full, 32-row sweeps of each layer "
+                   "(scaled to all rows); fp64 NumPy; "
+                   + ", ".join(f"{k} {v:.2f} s" for k, v in t.items())),
+        "sample_seconds": round(sum(t.values()), 2),
+    }
+
+
+def decoder_main(args):
+    """--decoder: layer-wise GPTQ of a Llama-7B-shaped decoder block (q, k, v,
+    o 4096 x 4096, 32 heads of 128; gate, up 4096 -> 11008, down 11008 ->
+    4096), 128 calibration sequences of 2048 tokens; one step = the block."""
+    import torch
+
+    import post_weight_quantization_12_amd as P
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d, inter, heads, eps = 4096, 11008, 32, 1e-5
+    bits, gs, sym, desc, damp = 4, 128, False, True, 0.01
+    base = workloads.get("c1")
+    L = base.tokens_per_sample
+    t0 = time.perf_counter()
+    mixing = workloads._mixing(base, dev, 0)
+    outl = workloads.outlier_channels(base, dev, 0)
+    X = torch.empty((base.tokens, d), dtype=torch.float16, device=dev)
+    for s in range(base.samples):
+        X[s * L:(s + 1) * L] = workloads.x_sample(base, s, dev, 0, mixing, outl)
+    Ws = workloads.decoder_block_weights(d, inter, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] decoder inputs ready in {time.perf_counter() - t0:.1f} s")
+    stream = torch.cuda.current_stream()
+    recs = []
+
+    def step(record):
+        ev = {}
+
+        def mark(name):
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                ev[f"{len(ev):02d}_{name}"] = e
+        P.block.quantize_decoder_block(X, *Ws, heads, L, eps, bits, gs, sym, damp, desc,
+                                       stream=stream, mark=mark)
+        if record:
+            recs.append(ev)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = sorted(recs[0].keys())
+    phases = {}
+    for a, b in zip(names[:-1], names[1:]):
+        phases[b[3:] if b[3:] not in phases else b] = \
+            sum(r[a].elapsed_time(r[b]) for r in recs) / len(recs)
+    ms = wall * 1e3 / args.steps
+    weights = 4 * d * d + 3 * d * inter
+    att_flops = 2.0 * base.samples * heads * L * L * (d // heads)   # causal: half of 4 L^2 hd
+    result = {
+        "metric": "GPTQ Llama-7B decoder block (q, k, v, o, gate, up, down) weights quantized/sec, 1 GPU",
+        "value": weights / (ms * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in, f32 accumulate",
+        "data": "synthetic (seeded; stands in for c4 calibration text and Llama weights)",
+        "config": {
+            "workload": (f"decoder block d={d} heads={heads} inter={inter}: calibration "
+                         f"{base.samples} sequences x {L} tokens fp16, {bits}-bit g{gs} asym "
+                         f"desc_act={desc} damp {damp}; each layer calibrated through the "
+                         "quantized layers before it"),
+            "tokens": base.tokens, "d": d, "heads": heads, "inter": inter, "bits": bits,
+            "group_size": gs, "desc_act": desc,
+        },
+        "phase_ms": phases,
+        "attention_flops_algorithmic": att_flops,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = decoder_cpu_baseline(d, inter, heads, L, bits, gs, sym, desc, X,
+                                                      Ws, base.samples)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def export_main(args):
     """--export: gptq_export_params on the config's layer (fp16 scales,
     packed zeros; HBM roofline) and a save / load of the layer through the
@@ -1085,6 +1236,8 @@ def main():
                     help="time gptq_export_params and a checkpoint save / load of the layer")
     ap.add_argument("--block", action="store_true",
                     help="time layer-wise GPTQ of a Llama-7B-shaped MLP block instead")
+    ap.add_argument("--decoder", action="store_true",
+                    help="time layer-wise GPTQ of a whole Llama-7B-shaped decoder block instead")
     ap.add_argument("--dequant-as-packed", action="store_true",
                     help="with --dequant-tokens on an act-order config: use the layer as packed "
                          "instead of its group order")
@@ -1113,6 +1266,9 @@ def main():
         return
     if args.block:
         block_main(args)
+        return
+    if args.decoder:
+        decoder_main(args)
         return
     if args.export:
         export_main(args)

@@ -489,6 +489,169 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
   }
 }
 
+// ---------------------------------------------------------------------------
+// Error-update GEMM of the column sweep: C -= E V^T on two fp16 products.
+//   E  fp32 [M x K] (row-major, k-contiguous; each row scaled by a power of
+//      two first, from the sweeps' per-row error maxima over the K range),
+//      split x = hi + lo as split16 does;
+//   V  fp16 [N x K] (k-contiguous: the coefficient matrix stored transposed
+//      and rounded to nearest fp16 once);
+//   C  fp32 [M x N] -= (E_hi V + E_lo V) / scale.
+// 128 x 128 tiles, four 64 x 64 waves, 32 k per stage, three stages of
+// direct-to-LDS loads.  The fp16 rows of V are 64 bytes per stage: chunk c
+// of row r sits at c ^ ((r >> 2) & 3), so a 16-lane pass of 16-byte reads of
+// 16 consecutive rows covers all 64 banks.
+constexpr int E2_BM = 128, E2_BN = 128, E2_NS = 3;
+constexpr int E2_AIPW = E2_BM / 32;      // fp32 A: 4 KiB per wave-wide load round
+constexpr int E2_BIPW = E2_BN / 64;      // fp16 B: 64 rows x 64 bytes per round
+constexpr int E2_AF = E2_BM * DK;        // floats per A stage
+constexpr int E2_BH = E2_BN * DK;        // halves per B stage
+
+__global__ void __launch_bounds__(256)
+gemm_e2_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+            const _Float16* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
+            const float* __restrict__ emax, int64_t eld, int64_t eb0, int64_t eb1) {
+  __shared__ __align__(16) float sa[E2_NS][E2_AF];
+  __shared__ __align__(16) _Float16 sb[E2_NS][E2_BH];
+  __shared__ float rsl[E2_BM];
+  using TA_ = OpTile<E2_BM, true>;
+  static_assert(TA_::IPW == E2_AIPW, "A loads per wave");
+
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int tiles_n = (int)((N + E2_BN - 1) / E2_BN);
+  const int t = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  const int ti = t / tiles_n, tj = t % tiles_n;
+  const int64_t i0 = (int64_t)ti * E2_BM, j0 = (int64_t)tj * E2_BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1, h = lane >> 5;
+
+  // Row scales of the tile: 2^(14 - e) for the rows' largest error m = f 2^e
+  // (f in [0.5, 1)) over the K range, so every scaled error is below 2^14.
+  if (tid < E2_BM) {
+    const int64_t r = i0 + tid;
+    float m = 0.0f;
+    if (r < M)
+      for (int64_t k = eb0; k < eb1; ++k) m = fmaxf(m, emax[k * eld + r]);
+    int e = 0;
+    (void)frexpf(m, &e);
+    rsl[tid] = (m > 0.0f && m < INFINITY) ? ldexpf(1.0f, 14 - e) : 1.0f;
+  }
+
+  const float* abase = A + i0 * lda;
+  const int64_t aext = ((M - i0 - 1) * lda + K) * 4;
+  const _Float16* bbase = B + j0 * ldb;
+  const int64_t bext = ((N - j0 - 1) * ldb + K) * 2;
+  const int nk = (int)(K / DK);
+  uint32_t va[E2_AIPW], vb[E2_BIPW];
+#pragma unroll
+  for (int q = 0; q < E2_AIPW; ++q) va[q] = TA_::voff(wave, q, lane, lda);
+#pragma unroll
+  for (int q = 0; q < E2_BIPW; ++q) {
+    const int slot = (wave * E2_BIPW + q) * 64 + lane;
+    const int row = slot >> 2, lch = (slot & 3) ^ ((row >> 2) & 3);
+    vb[q] = (uint32_t)(((int64_t)row * ldb + lch * 8) * 2);
+  }
+  auto issue = [&](int st, int buf) __device__ __attribute__((always_inline)) {
+    const bool live = st < nk;
+    issue_stage<E2_AIPW>(live ? (const char*)abase + (int64_t)st * DK * 4 : (const char*)A,
+                         live ? aext - (int64_t)st * DK * 4 : 0, va,
+                         &sa[buf][0] + wave * E2_AIPW * 256);
+    __amdgpu_buffer_rsrc_t rs = rsrc(live ? (const char*)bbase + (int64_t)st * DK * 2 : (const char*)B,
+                                     live ? bext - (int64_t)st * DK * 2 : 0);
+#pragma unroll
+    for (int q = 0; q < E2_BIPW; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, GPTQ_LDS(&sb[buf][0] + (wave * E2_BIPW + q) * 512), 16, vb[q], 0, 0, 0);
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+
+  issue(0, 0);
+  issue(1, 1);
+  __syncthreads();  // row scales
+  float rsa[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) rsa[a] = rsl[wm * 64 + a * 32 + (lane & 31)];
+
+  auto compute = [&](int buf) __device__ __attribute__((always_inline)) {
+    float av[2][16];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) TA_::frag(&sa[buf][0], wm * 64 + a * 32 + (lane & 31), h, av[a]);
+    half8_t bq[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = wn * 64 + c * 32 + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ph = (2 * h + q) ^ ((row >> 2) & 3);
+        bq[c][q] = *reinterpret_cast<const half8_t*>(&sb[buf][row * DK + ph * 8]);
+      }
+    }
+    half8_t ah[2][2], al[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) av[a][u] *= rsa[a];
+      split16(av[a], ah[a], al[a]);
+    }
+    // MFMA k-step q takes this lane's k = 16 h + 8 q + e (e < 8) of A and B
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[a][q], bq[c][q], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[a][q], bq[c][q], acc[a][c], 0, 0, 0);
+        }
+  };
+  constexpr int IPW = E2_AIPW + E2_BIPW;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt % E2_NS;
+    wait_vmcnt<(E2_NS - 2) * IPW>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + E2_NS - 1, (kt + E2_NS - 1) % E2_NS);
+    compute(buf);
+  }
+  wait_vmcnt<0>();
+
+  // C += -acc / scale, through a buffer descriptor (outside rows / columns dropped)
+  const int64_t cext = ((M - i0 - 1) * ldc + (N - j0)) * 4;
+  __amdgpu_buffer_rsrc_t rc = rsrc(C + i0 * ldc + j0, cext);
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    float ralpha[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      ralpha[v] = -1.0f / rsl[wm * 64 + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int jl = wn * 64 + c * 32 + (lane & 31);
+      uint32_t off[16];
+      float cv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int il = wm * 64 + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const bool in = i0 + il < M && j0 + jl < N;
+        off[v] = in ? (uint32_t)(((int64_t)il * ldc + jl) * 4) : 0x80000000u;
+        cv[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, (int)off[v], 0, 0));
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(ralpha[v], acc[a][c][v], cv[v])),
+                                              rc, (int)off[v], 0, 0);
+    }
+  }
+}
+
 template <int BM, int BN, int NS, bool TA, bool TB, bool X3>
 hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
@@ -507,6 +670,20 @@ hipError_t launch_dma_t(const GemmArgs& g, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_gemm_e2(int64_t M, int64_t N, int64_t K, const float* E, int64_t lde,
+                          const _Float16* V, int64_t ldv, float* C, int64_t ldc,
+                          const float* emax, int64_t eld, int64_t eb0, int64_t eb1,
+                          hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (K % DK != 0 || lde % 4 != 0 || ldv % 8 != 0 || !al16(E) ||
+      (reinterpret_cast<uintptr_t>(V) & 15) != 0)
+    return hipErrorInvalidValue;
+  const int64_t tiles = ((M + E2_BM - 1) / E2_BM) * ((N + E2_BN - 1) / E2_BN);
+  hipLaunchKernelGGL(gemm_e2_dma, dim3((unsigned)tiles), dim3(256), 0, s, M, N, K, E, lde, V, ldv,
+                     C, ldc, emax, eld, eb0, eb1);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;

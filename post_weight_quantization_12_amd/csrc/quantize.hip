@@ -160,6 +160,26 @@ uprime_kernel(const float* __restrict__ U, int64_t n, float* __restrict__ Up) {
   }
 }
 
+// Vt[c][r] = fp16(Up[r][c]) (round to nearest) for the strictly upper part
+// r < c: U' transposed for the error-update GEMMs, which read it
+// k-contiguous.  64 x 64 tiles through LDS; tiles below the diagonal exit.
+__global__ void __launch_bounds__(256)
+uprime_t16_kernel(const float* __restrict__ Up, int64_t n, _Float16* __restrict__ Vt) {
+  __shared__ float tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  if (r0 > c0 + 63) return;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < n && c < n && r < c) ? Up[r * n + c] : 0.0f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < n && r < n && r < c) Vt[c * n + r] = (_Float16)tile[tx][i];
+  }
+}
+
 // pinv[perm[j]] = j;  g_idx[perm[j]] = j / gs (0 for one group per row).
 __global__ void perm_tables_kernel(const int32_t* __restrict__ perm, int64_t in, int gs,
                                    int32_t* __restrict__ pinv, int32_t* __restrict__ g_idx) {
@@ -754,30 +774,16 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
   return hipGetLastError();
 }
 
-// rs[r] = 2^(14 - e) with m = max over blocks [b0, b1) of emax = f 2^e
-// (f in [0.5, 1)), so every scaled error of the row is below 2^14 in
-// magnitude; 1 for an all-zero (or non-finite) row.
-__global__ void row_scale_kernel(const float* __restrict__ emax, int64_t out, int64_t b0,
-                                 int64_t b1, float* __restrict__ rs) {
-  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (r >= out) return;
-  float m = 0.0f;
-  for (int64_t k = b0; k < b1; ++k) m = fmaxf(m, emax[k * out + r]);
-  int e = 0;
-  (void)frexpf(m, &e);
-  rs[r] = (m > 0.0f && m < INFINITY) ? ldexpf(1.0f, 14 - e) : 1.0f;
-}
-
 struct QCtx {
   float* Wp;
   const float* Up;
+  const _Float16* Vt;  // U' transposed, fp16 (the error-update GEMMs' operand)
   int64_t out, in;
   int bits, gs, sym, block;
   float* scales;
   int32_t* zeros;
   uint8_t* codes;
   float* emax;  // [in / block][out] largest |error| per row and block
-  float* rs;    // [out] row scales of the current trailing GEMM
   hipStream_t s;
 };
 
@@ -795,8 +801,9 @@ hipError_t sweep_block(QCtx& c, int64_t a, int64_t b) {
 
 // Columns [a, b): sweep the left half, carry its updates to the right half
 // with one GEMM, then the right half.  GEMMs over 512 or more columns of
-// errors use split fp16 products with each error row scaled by a power of two
-// (from the sweeps' per-row maxima) so that it spans the fp16 range.
+// errors take the errors as two fp16 parts, each row scaled by a power of two
+// (from the sweeps' per-row maxima) so that it spans the fp16 range, times
+// U' rounded once to fp16 (launch_gemm_e2); smaller ones run in fp32.
 constexpr int64_t SPLIT_MIN_K = 512;
 hipError_t process(QCtx& c, int64_t a, int64_t b) {
   const int64_t B = c.block;
@@ -804,26 +811,24 @@ hipError_t process(QCtx& c, int64_t a, int64_t b) {
   const int64_t nblk = (b - a + B - 1) / B;
   const int64_t m = a + B * ((nblk + 1) / 2);
   GPTQ_HIP_TRY(process(c, a, m));
-  GemmArgs g{c.out, b - m, m - a, c.Wp + a, c.in, false, c.Up + a * c.in + m, c.in, false,
-             c.Wp + m, c.in, -1.0f, 1.0f, KR_FULL, false};
   if (m - a >= SPLIT_MIN_K) {
-    hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((c.out + 255) / 256)), dim3(256), 0, c.s,
-                       c.emax, c.out, a / B, m / B, c.rs);
-    GPTQ_HIP_TRY(hipGetLastError());
-    g.split16 = true;
-    g.row_scale = c.rs;
+    GPTQ_HIP_TRY(launch_gemm_e2(c.out, b - m, m - a, c.Wp + a, c.in, c.Vt + m * c.in + a, c.in,
+                                c.Wp + m, c.in, c.emax, c.out, a / B, m / B, c.s));
+  } else {
+    GemmArgs g{c.out, b - m, m - a, c.Wp + a, c.in, false, c.Up + a * c.in + m, c.in, false,
+               c.Wp + m, c.in, -1.0f, 1.0f, KR_FULL, false};
+    GPTQ_HIP_TRY(launch_gemm_f32(g, c.s));
   }
-  GPTQ_HIP_TRY(launch_gemm_f32(g, c.s));
   return process(c, m, b);
 }
 
 struct QLayout {
   float* Wp;
   float* Up;
+  _Float16* Vt;
   uint8_t* codes;
   int32_t* pinv;
   float* emax;
-  float* rs;
   size_t bytes;
 };
 
@@ -832,10 +837,11 @@ QLayout carve(void* ws, int64_t out, int64_t in, int block) {
   QLayout l;
   l.Wp = c.take<float>((size_t)out * in);
   l.Up = c.take<float>((size_t)in * in);
+  // only read where K >= SPLIT_MIN_K, i.e. for in > 2 SPLIT_MIN_K - block
+  l.Vt = in > SPLIT_MIN_K ? c.take<_Float16>((size_t)in * in) : nullptr;
   l.codes = c.take<uint8_t>((size_t)out * in);
   l.pinv = c.take<int32_t>((size_t)in);
   l.emax = c.take<float>((size_t)out * (size_t)((in + block - 1) / block));
-  l.rs = c.take<float>((size_t)out);
   l.bytes = c.used;
   return l;
 }
@@ -875,6 +881,11 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
   hipLaunchKernelGGL(uprime_kernel, dim3((unsigned)((in / 4 + 256) / 256), (unsigned)in), dim3(256),
                      0, s, U, in, l.Up);
   GPTQ_HIP_TRY(hipGetLastError());
+  if (l.Vt) {
+    const unsigned nt = (unsigned)((in + 63) / 64);
+    hipLaunchKernelGGL(uprime_t16_kernel, dim3(nt, nt), dim3(256), 0, s, l.Up, in, l.Vt);
+    GPTQ_HIP_TRY(hipGetLastError());
+  }
   hipLaunchKernelGGL(perm_tables_kernel, dim3((unsigned)((in + 255) / 256)), dim3(256), 0, s, perm,
                      in, gs, l.pinv, g_idx);
   GPTQ_HIP_TRY(hipGetLastError());
@@ -883,7 +894,7 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                        bits, sym, scales, zeros);
     GPTQ_HIP_TRY(hipGetLastError());
   }
-  QCtx c{l.Wp, l.Up, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.emax, l.rs, s};
+  QCtx c{l.Wp, l.Up, l.Vt, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.emax, s};
   GPTQ_HIP_TRY(process(c, 0, in));
   // rows per packing workgroup: as many (up to 16) as fit next to pinv in 160 KiB of LDS
   int R = 16;
