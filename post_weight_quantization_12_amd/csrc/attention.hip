@@ -11,9 +11,10 @@
 //   attn_fwd_kernel: causal multi-head attention per sequence,
 //       O[t] = sum_{s <= t} softmax_s(Q[t] . K[s] / sqrt(hd)) V[s],
 //     fp16 Q, K, V in, fp32 scores, softmax and accumulation, fp16 O out.
-//     One workgroup = 64 queries of one head of one sequence, four waves of
-//     16 queries; key blocks of 64 are staged in LDS (K as is, V transposed)
-//     and walked with an online softmax.  The matrix cores compute
+//     One workgroup = 128 queries of one head of one sequence, eight waves
+//     of 16 queries; key blocks of 64 are staged in LDS (double-buffered)
+//     and walked with an online softmax; under the causal mask a wave skips
+//     the 16-key tiles past its last query.  The matrix cores compute
 //     S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x16_f16: in that
 //     orientation the S^T accumulator of a lane (query l % 16, keys
 //     4 (l / 16) + 0..3 of a 16-key slice) is exactly its B operand for the
@@ -32,12 +33,25 @@ namespace {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
-constexpr int AQ = 64;   // queries per workgroup (16 per wave)
-constexpr int AK = 64;   // keys per staged block
+constexpr int AW = 8;         // waves per workgroup
+constexpr int AQ = 16 * AW;   // queries per workgroup (16 per wave)
+constexpr int AK = 64;        // keys per staged block
 
 __device__ inline float4_t mfma16(half4_t a, half4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: in each 16-lane group, lane j receives element j % 4
+// of the 8-byte reads of lanes j / 4 + 4 i (i < 4).  A lane pointing at
+// (row r0 + j / 4, columns c0 + 4 (j % 4) ..) therefore receives column
+// c0 + j of rows r0 .. r0 + 3.
+__device__ inline half4_t ds_read_tr16(const _Float16* p) {
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (v4i16_t __attribute__((address_space(3)))*)(
+          (__attribute__((address_space(3))) _Float16*)(p)));
+  return __builtin_bit_cast(half4_t, v);
 }
 
 // Max / sum over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48).
@@ -50,28 +64,35 @@ __device__ inline float group4_sum(float v) {
   return v + __shfl_xor(v, 32);
 }
 
-// Grid: (ceil(seq_len / 64), heads, seqs); 256 threads.  Q, K, V, O rows are
+// Grid: (ceil(seq_len / 128), heads, seqs); 512 threads.  Q, K, V, O rows are
 // tokens (sequence b occupies rows b * seq_len ...), head h the columns
 // h * HD .. h * HD + HD - 1; every row start and ld a multiple of 8 halves.
+// K and V blocks are staged row-major (16-byte stores) in two buffers: the
+// next block's global loads are in flight while the current one is used.
+// K rows are HD + 8 halves apart (a wave's 8-byte reads of 16 rows cover
+// all banks), V rows HD + 16 (the transposing reads of 8 rows do).
 template <int HD>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 attn_fwd_kernel(const _Float16* __restrict__ Q, int64_t ldq, const _Float16* __restrict__ K,
                 int64_t ldk, const _Float16* __restrict__ V, int64_t ldv,
                 _Float16* __restrict__ O, int64_t ldo, int seq_len, float scale_log2e,
                 int causal) {
-  constexpr int KP = HD + 8;   // K rows in LDS (halves): 8-byte reads spread over the banks
-  constexpr int VP = AK + 8;   // V^T rows in LDS (halves)
-  constexpr int NS = HD / 16;  // 16-wide slices of the head dimension
-  __shared__ __align__(16) _Float16 Ks[AK * KP];
-  __shared__ __align__(16) _Float16 Vt[HD * VP];
+  constexpr int KP = HD + 8, VP = HD + 16;
+  constexpr int NS = HD / 16;                      // 16-wide slices of the head dimension
+  constexpr int CH = AK * HD / 8;                  // 16-byte chunks of a K (or V) block
+  constexpr int PT = CH / (AW * 64);               // chunks per thread
+  static_assert(CH % (AW * 64) == 0, "whole chunks per thread");
+  __shared__ __align__(16) _Float16 Ks[2][AK * KP];
+  __shared__ __align__(16) _Float16 Vs[2][AK * VP];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.y;
   const int64_t tok0 = (int64_t)blockIdx.z * seq_len;       // first token of the sequence
   const int qb0 = blockIdx.x * AQ;                          // first query of the workgroup
-  const int qw = qb0 + wave * 16 + (lane & 15);             // this lane's query
-  const int kq = 4 * (lane >> 4);                           // this lane's 4-slot offset
+  const int qw0 = qb0 + wave * 16;                          // first query of the wave
+  const int qw = qw0 + (lane & 15);                         // this lane's query
+  const int g = lane >> 4, kq = 4 * g;                      // lane group, its 4-slot offset
 
   // Q^T as B operands, one per 16-wide slice: (query qw, dims 16 s + kq ..).
   half4_t qf[NS];
@@ -91,80 +112,106 @@ attn_fwd_kernel(const _Float16* __restrict__ Q, int64_t ldq, const _Float16* __r
 
   const int qlast = qb0 + AQ - 1 < seq_len - 1 ? qb0 + AQ - 1 : seq_len - 1;
   const int kend = causal ? qlast + 1 : seq_len;            // keys [0, kend)
-  for (int kb = 0; kb < kend; kb += AK) {
-    __syncthreads();  // the previous block's LDS reads are done
-    // stage K (row-major) and V^T: 64 keys x HD dims, 16-byte chunks
-    for (int c = tid; c < AK * HD / 8; c += 256) {
+  const int wlast = qw0 + 15 < seq_len - 1 ? qw0 + 15 : seq_len - 1;  // the wave's last query
+
+  uint4 kr[PT], vr[PT];
+  auto fetch = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int c = tid + u * AW * 64;
       const int r = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
       const int key = kb + r;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
       if (key < seq_len) {
-        kv = *reinterpret_cast<const uint4*>(K + (tok0 + key) * ldk + h * HD + d0);
-        vv = *reinterpret_cast<const uint4*>(V + (tok0 + key) * ldv + h * HD + d0);
-      }
-      *reinterpret_cast<uint4*>(&Ks[r * KP + d0]) = kv;
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Vt[(d0 + 2 * j) * VP + r] = __builtin_bit_cast(_Float16, (uint16_t)(w[j] & 0xFFFFu));
-        Vt[(d0 + 2 * j + 1) * VP + r] = __builtin_bit_cast(_Float16, (uint16_t)(w[j] >> 16));
+        kr[u] = *reinterpret_cast<const uint4*>(K + (tok0 + key) * ldk + h * HD + d0);
+        vr[u] = *reinterpret_cast<const uint4*>(V + (tok0 + key) * ldv + h * HD + d0);
       }
     }
-    __syncthreads();
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int c = tid + u * AW * 64;
+      const int r = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
+      *reinterpret_cast<uint4*>(&Ks[buf][r * KP + d0]) = kr[u];
+      *reinterpret_cast<uint4*>(&Vs[buf][r * VP + d0]) = vr[u];
+    }
+  };
 
-    // S^T (64 keys x 16 queries) in four 16 x 16 tiles
-    float4_t sacc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      sacc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const half4_t kf = __builtin_bit_cast(
-            half4_t, *reinterpret_cast<const uint2*>(&Ks[(16 * t + (lane & 15)) * KP + 16 * s + kq]));
-        sacc[t] = mfma16(kf, qf[s], sacc[t]);
-      }
-    }
-    // mask (causal, past the sequence), block max over this lane's keys
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + 16 * t + kq + i;
-        const bool ok = key < seq_len && (!causal || key <= qw);
-        sacc[t][i] = ok ? sacc[t][i] : -INFINITY;
-        bmax = fmaxf(bmax, sacc[t][i]);
-      }
-    bmax = group4_max(bmax);
-    const float mnew = fmaxf(m, bmax);
-    const float mref = mnew == -INFINITY ? 0.0f : mnew;     // a query with no key yet
-    const float alpha = exp2f((m - mref) * scale_log2e);    // exp2(-inf) = 0 on the first block
-    float psum = 0.0f;
-    half4_t pf[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = exp2f((sacc[t][i] - mref) * scale_log2e);
-        psum += p[i];
-      }
-      pf[t] = (half4_t){(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-    }
-    l = alpha * l + group4_sum(psum);
-    m = mnew;
-    // O^T (HD x 16 queries) = alpha O^T + V^T P^T
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      float4_t o = oacc[s] * alpha;
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  for (int kb = 0, buf = 0; kb < kend; kb += AK, buf ^= 1) {
+    const bool more = kb + AK < kend;  // uniform
+    if (more) fetch(kb + AK);
+    // 16-key tiles of this block the wave needs (causal: keys <= its last query)
+    const int nt = causal ? (wlast - kb >= AK - 1 ? 4 : wlast >= kb ? (wlast - kb) / 16 + 1 : 0) : 4;
+    if (nt > 0) {
+      const _Float16* ks = Ks[buf];
+      const _Float16* vs = Vs[buf];
+      // S^T (16 t + key, query) tiles
+      float4_t sacc[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const half4_t vf = __builtin_bit_cast(
-            half4_t, *reinterpret_cast<const uint2*>(&Vt[(16 * s + (lane & 15)) * VP + 16 * t + kq]));
-        o = mfma16(vf, pf[t], o);
+        sacc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+        if (t < nt) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const half4_t kf = __builtin_bit_cast(
+                half4_t, *reinterpret_cast<const uint2*>(&ks[(16 * t + (lane & 15)) * KP + 16 * s + kq]));
+            sacc[t] = mfma16(kf, qf[s], sacc[t]);
+          }
+        }
       }
-      oacc[s] = o;
+      // mask (causal, past the sequence, tiles not computed), block max
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + 16 * t + kq + i;
+          const bool ok = t < nt && key < seq_len && (!causal || key <= qw);
+          sacc[t][i] = ok ? sacc[t][i] : -INFINITY;
+          bmax = fmaxf(bmax, sacc[t][i]);
+        }
+      bmax = group4_max(bmax);
+      const float mnew = fmaxf(m, bmax);
+      const float mref = mnew == -INFINITY ? 0.0f : mnew;   // a query with no key yet
+      const float alpha = exp2f((m - mref) * scale_log2e);  // exp2(-inf) = 0 on the first block
+      float psum = 0.0f;
+      half4_t pf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = exp2f((sacc[t][i] - mref) * scale_log2e);
+          psum += p[i];
+        }
+        pf[t] = (half4_t){(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+      }
+      l = alpha * l + group4_sum(psum);
+      m = mnew;
+      // O^T (HD x 16 queries) = alpha O^T + V^T P^T; the A operand (dims 16 s + j,
+      // keys 16 t + kq ..) from row-major V by transposing reads
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        float4_t o = oacc[s] * alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t < nt) {
+            const half4_t vf =
+                ds_read_tr16(&vs[(16 * t + kq + ((lane & 15) >> 2)) * VP + 16 * s + 4 * (lane & 3)]);
+            o = mfma16(vf, pf[t], o);
+          }
+        }
+        oacc[s] = o;
+      }
     }
+    if (more) {
+      stage(buf ^ 1);  // the other buffer: everyone finished it before the last barrier
+    }
+    __syncthreads();
   }
   if (qw >= seq_len) return;
   const float inv = 1.0f / l;
@@ -217,10 +264,10 @@ hipError_t run_attention(const void* Q, int64_t ldq, const void* K, int64_t ldk,
   auto v = static_cast<const _Float16*>(V);
   auto o = static_cast<_Float16*>(O);
   if (head_dim == 64)
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(256), 0, s, q, ldq, k, ldk, v, ldv, o, ldo,
-                       (int)seq_len, scale_log2e, causal);
+    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(AW * 64), 0, s, q, ldq, k, ldk, v, ldv, o,
+                       ldo, (int)seq_len, scale_log2e, causal);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(256), 0, s, q, ldq, k, ldk, v, ldv, o,
+    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(AW * 64), 0, s, q, ldq, k, ldk, v, ldv, o,
                        ldo, (int)seq_len, scale_log2e, causal);
   return hipGetLastError();
 }
