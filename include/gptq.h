@@ -173,10 +173,10 @@ size_t gptq_quantize_workspace_bytes(int64_t out, int64_t in, int bits,
  * `block` columns; the update of the columns right of a block is applied as a
  * matrix product on the matrix cores (the set of updates is the same): in
  * fp32 for fewer than 512 columns of errors, above that with each error
- * (its row scaled by a power of two) split into two fp16 parts and
- * (e / U_jj) U_jk's factor U_jk / U_jj rounded once to fp16, fp32 sums
- * (about 2^-12 relative per term; the pre-rounding values move by at most
- * a few 1e-4 code units against exact arithmetic).
+ * (its row scaled by a power of two) split into two fp16 parts times the
+ * factor U_jk / U_jj in fp16, fp32 sums: the factor rounded once to fp16
+ * for in <= 16384 (pre-rounding values move by a few 1e-4 code units
+ * against exact arithmetic), as two fp16 parts for wider layers (~1e-5).
  *
  *   W          [out x in] row-major, dtype F16 / BF16 / F32, ORIGINAL column
  *              order; not modified.

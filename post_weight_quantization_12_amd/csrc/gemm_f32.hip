@@ -501,7 +501,7 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
 // direct-to-LDS loads.  The fp16 rows of V are 64 bytes per stage: chunk c
 // of row r sits at c ^ ((r >> 2) & 3), so a 16-lane pass of 16-byte reads of
 // 16 consecutive rows covers all 64 banks.
-constexpr int E2_BM = 128, E2_BN = 128, E2_NS = 3;
+constexpr int E2_BM = 128, E2_BN = 128, E2_NS = 3;  // 72 KiB of LDS: two workgroups per CU
 constexpr int E2_AIPW = E2_BM / 32;      // fp32 A: 4 KiB per wave-wide load round
 constexpr int E2_BIPW = E2_BN / 64;      // fp16 B: 64 rows x 64 bytes per round
 constexpr int E2_AF = E2_BM * DK;        // floats per A stage
@@ -527,15 +527,32 @@ gemm_e2_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_
   const int wm = wave & 1, wn = wave >> 1, h = lane >> 5;
 
   // Row scales of the tile: 2^(14 - e) for the rows' largest error m = f 2^e
-  // (f in [0.5, 1)) over the K range, so every scaled error is below 2^14.
-  if (tid < E2_BM) {
-    const int64_t r = i0 + tid;
+  // (f in [0.5, 1)) over the K range's blocks, so every scaled error is below
+  // 2^14.  Two threads per row, each every second block, eight loads in
+  // flight (a K range holds up to in / block blocks).
+  {
+    const int rr = tid & (E2_BM - 1), half = tid >> 7;
+    const int64_t r = i0 + rr;
     float m = 0.0f;
-    if (r < M)
-      for (int64_t k = eb0; k < eb1; ++k) m = fmaxf(m, emax[k * eld + r]);
-    int e = 0;
-    (void)frexpf(m, &e);
-    rsl[tid] = (m > 0.0f && m < INFINITY) ? ldexpf(1.0f, 14 - e) : 1.0f;
+    if (r < M) {
+      int64_t k = eb0 + half;
+      for (; k + 14 < eb1; k += 16) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = emax[(k + 2 * u) * eld + r];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m = fmaxf(m, v[u]);
+      }
+      for (; k < eb1; k += 2) m = fmaxf(m, emax[k * eld + r]);
+    }
+    if (half) rsl[rr] = m;
+    __syncthreads();
+    if (!half) {
+      m = fmaxf(m, rsl[rr]);
+      int e = 0;
+      (void)frexpf(m, &e);
+      rsl[rr] = (m > 0.0f && m < INFINITY) ? ldexpf(1.0f, 14 - e) : 1.0f;
+    }
   }
 
   const float* abase = A + i0 * lda;
@@ -573,8 +590,8 @@ gemm_e2_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
 
-  issue(0, 0);
-  issue(1, 1);
+#pragma unroll
+  for (int st = 0; st + 1 < E2_NS; ++st) issue(st, st);
   __syncthreads();  // row scales
   float rsa[2];
 #pragma unroll

@@ -774,16 +774,31 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
   return hipGetLastError();
 }
 
+// rs[r] = 2^(14 - e) with m = max over blocks [b0, b1) of emax = f 2^e
+// (f in [0.5, 1)), so every scaled error of the row is below 2^14 in
+// magnitude; 1 for an all-zero (or non-finite) row.
+__global__ void row_scale_kernel(const float* __restrict__ emax, int64_t out, int64_t b0,
+                                 int64_t b1, float* __restrict__ rs) {
+  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (r >= out) return;
+  float m = 0.0f;
+  for (int64_t k = b0; k < b1; ++k) m = fmaxf(m, emax[k * out + r]);
+  int e = 0;
+  (void)frexpf(m, &e);
+  rs[r] = (m > 0.0f && m < INFINITY) ? ldexpf(1.0f, 14 - e) : 1.0f;
+}
+
 struct QCtx {
   float* Wp;
   const float* Up;
-  const _Float16* Vt;  // U' transposed, fp16 (the error-update GEMMs' operand)
+  const _Float16* Vt;  // U' transposed, fp16 (two-product GEMMs), or null
   int64_t out, in;
   int bits, gs, sym, block;
   float* scales;
   int32_t* zeros;
   uint8_t* codes;
   float* emax;  // [in / block][out] largest |error| per row and block
+  float* rs;    // [out] row scales of the current three-product GEMM, or null
   hipStream_t s;
 };
 
@@ -802,21 +817,36 @@ hipError_t sweep_block(QCtx& c, int64_t a, int64_t b) {
 // Columns [a, b): sweep the left half, carry its updates to the right half
 // with one GEMM, then the right half.  GEMMs over 512 or more columns of
 // errors take the errors as two fp16 parts, each row scaled by a power of two
-// (from the sweeps' per-row maxima) so that it spans the fp16 range, times
-// U' rounded once to fp16 (launch_gemm_e2); smaller ones run in fp32.
+// (from the sweeps' per-row maxima) so that it spans the fp16 range; smaller
+// ones run in fp32.  Up to TWO_PRODUCT_MAX_IN columns U' enters rounded once
+// to fp16 (two products per term, launch_gemm_e2 on U' stored transposed);
+// above it U' is split into two fp16 parts as well (three products,
+// launch_gemm_f32 with split16).  The rounding of U' moves a pre-rounding
+// value by a sum over every earlier column, which grows with the layer width:
+// largest shifts measured in a CPU emulation of the two-product form were
+// 3.5e-4 code units at 4096 columns, 4.2e-4 at 11008 and 1.1e-3 at 28672,
+// against a 1e-3 boundary window; three products keep 9e-6 at 28672.
 constexpr int64_t SPLIT_MIN_K = 512;
+constexpr int64_t TWO_PRODUCT_MAX_IN = 16384;
 hipError_t process(QCtx& c, int64_t a, int64_t b) {
   const int64_t B = c.block;
   if (b - a <= B) return sweep_block(c, a, b);
   const int64_t nblk = (b - a + B - 1) / B;
   const int64_t m = a + B * ((nblk + 1) / 2);
   GPTQ_HIP_TRY(process(c, a, m));
-  if (m - a >= SPLIT_MIN_K) {
+  if (m - a >= SPLIT_MIN_K && c.Vt) {
     GPTQ_HIP_TRY(launch_gemm_e2(c.out, b - m, m - a, c.Wp + a, c.in, c.Vt + m * c.in + a, c.in,
                                 c.Wp + m, c.in, c.emax, c.out, a / B, m / B, c.s));
   } else {
     GemmArgs g{c.out, b - m, m - a, c.Wp + a, c.in, false, c.Up + a * c.in + m, c.in, false,
                c.Wp + m, c.in, -1.0f, 1.0f, KR_FULL, false};
+    if (m - a >= SPLIT_MIN_K) {
+      hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((c.out + 255) / 256)), dim3(256), 0,
+                         c.s, c.emax, c.out, a / B, m / B, c.rs);
+      GPTQ_HIP_TRY(hipGetLastError());
+      g.split16 = true;
+      g.row_scale = c.rs;
+    }
     GPTQ_HIP_TRY(launch_gemm_f32(g, c.s));
   }
   return process(c, m, b);
@@ -826,6 +856,7 @@ struct QLayout {
   float* Wp;
   float* Up;
   _Float16* Vt;
+  float* rs;
   uint8_t* codes;
   int32_t* pinv;
   float* emax;
@@ -837,8 +868,11 @@ QLayout carve(void* ws, int64_t out, int64_t in, int block) {
   QLayout l;
   l.Wp = c.take<float>((size_t)out * in);
   l.Up = c.take<float>((size_t)in * in);
-  // only read where K >= SPLIT_MIN_K, i.e. for in > 2 SPLIT_MIN_K - block
-  l.Vt = in > SPLIT_MIN_K ? c.take<_Float16>((size_t)in * in) : nullptr;
+  // the GEMMs with K >= SPLIT_MIN_K (only for in > 2 SPLIT_MIN_K - block)
+  // read Vt up to TWO_PRODUCT_MAX_IN columns and rs above it
+  const bool split = in > SPLIT_MIN_K;
+  l.Vt = split && in <= TWO_PRODUCT_MAX_IN ? c.take<_Float16>((size_t)in * in) : nullptr;
+  l.rs = split && in > TWO_PRODUCT_MAX_IN ? c.take<float>((size_t)out) : nullptr;
   l.codes = c.take<uint8_t>((size_t)out * in);
   l.pinv = c.take<int32_t>((size_t)in);
   l.emax = c.take<float>((size_t)out * (size_t)((in + block - 1) / block));
@@ -894,7 +928,8 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                        bits, sym, scales, zeros);
     GPTQ_HIP_TRY(hipGetLastError());
   }
-  QCtx c{l.Wp, l.Up, l.Vt, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.emax, s};
+  QCtx c{l.Wp, l.Up, l.Vt, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.emax, l.rs,
+         s};
   GPTQ_HIP_TRY(process(c, 0, in));
   // rows per packing workgroup: as many (up to 16) as fit next to pinv in 160 KiB of LDS
   int R = 16;
