@@ -217,18 +217,29 @@ def _kernel_base_name(name: str) -> str:
 
 
 BLOCK_PROFILE_COMMAND = ("rocprofv3 --kernel-trace --stats -T -d {d}/trace -o t --output-format csv "
-                         "-- python -u bench.py --block --steps 1 --warmup 1 --no-cpu-baseline")
+                         "-- python -u bench.py --{mode} --steps 1 --warmup 1 --no-cpu-baseline")
+BLOCK_TITLES = {
+    "block": ("block_mlp_kernel_stats.md", 3,
+              "bench.py --block (Llama-7B MLP block, d 4096, inter 11008, 4-bit g128 asym, "
+              "desc_act on, 128 x 2048 calibration tokens)"),
+    "decoder": ("decoder_block_kernel_stats.md", 7,
+                "bench.py --decoder (Llama-7B decoder block: q, k, v, o 4096 x 4096 with 32 "
+                "heads of 128, gate, up, down 4096 / 11008, 4-bit g128 asym, desc_act on, 128 "
+                "sequences of 2048 tokens)"),
+}
 
 
-def summarize_block(d: str):
-    """profiles/block_mlp_kernel_stats.md from the BLOCK_PROFILE_COMMAND
-    trace in d: per-kernel statistics of the timed step (the second of two)."""
+def summarize_block(d: str, mode: str = "block"):
+    """profiles/<block|decoder>_..._kernel_stats.md from the
+    BLOCK_PROFILE_COMMAND trace in d: per-kernel statistics of the timed
+    step (the second of two)."""
     import csv
+    fname, layers, title = BLOCK_TITLES[mode]
     trace = list(csv.DictReader(open(os.path.join(d, "trace", "t_kernel_trace.csv"))))
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
-    # each step packs three layers: the warm-up step ends with its third pack
+    # each step packs every layer once: the warm-up step ends with its last pack
     packs = [int(r["End_Timestamp"]) for r in trace if r["Kernel_Name"].startswith("pack_kernel")]
-    first = packs[2] if len(packs) >= 6 else 0
+    first = packs[layers - 1] if len(packs) >= 2 * layers else 0
     k = sum(1 for r in trace if int(r["Start_Timestamp"]) < first)
     stats = {}
     span = [None, None]
@@ -239,16 +250,15 @@ def summarize_block(d: str):
         name = _kernel_base_name(r["Kernel_Name"])
         stats.setdefault(name, []).append(t1 - t0)
         span = [t0 if span[0] is None else min(span[0], t0), t1 if span[1] is None else max(span[1], t1)]
-    lines = ["# rocprofv3 kernel statistics: bench.py --block (Llama-7B MLP block, d 4096, "
-             "inter 11008, 4-bit g128 asym, desc_act on, 128 x 2048 calibration tokens)", "",
+    lines = ["# rocprofv3 kernel statistics: " + title, "",
              "Command (run from the repository root on one MI355X):", "",
-             "    " + BLOCK_PROFILE_COMMAND.format(d=d), "",
+             "    " + BLOCK_PROFILE_COMMAND.format(d=d, mode=mode), "",
              f"The timed step only ({(span[1] - span[0]) / 1e6:.1f} ms from its first kernel "
              f"to its last under the profiler; {k} earlier launches belong to the warm-up).", "",
              "| kernel | calls | total ms | avg us |", "|---|---:|---:|---:|"]
     for name, ds in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| {name} | {len(ds)} | {sum(ds) / 1e6:.3f} | {sum(ds) / len(ds) / 1e3:.2f} |")
-    with open(os.path.join(ROOT, "profiles", "block_mlp_kernel_stats.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", fname), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -419,7 +429,8 @@ STAGES = [
     ("a3 factor (Cholesky + inverse, U')", ("cholinv_leaf_kernel", "reverse_inplace_kernel",
                                              "uprime_kernel", "gemm_f32_dma@prepare")),
     ("a4 block sweep", ("sweep16_kernel", "sweep_kernel")),
-    ("a5 lazy trailing update", ("row_scale_kernel", "gemm_f32_dma@quantize")),
+    ("a5 lazy trailing update", ("gemm_e2_dma", "uprime_t16_kernel", "row_scale_kernel",
+                                  "gemm_f32_dma@quantize")),
     ("a6 pack", ("pack_kernel", "perm_tables_kernel")),
 ]
 
@@ -481,9 +492,10 @@ def stage_roofline(cfg, rows):
         ach = w / t
         shown = f"{ach / 1e12:.1f} TFLOP/s" if unit == "flop" else f"{ach / 1e9:.0f} GB/s"
         wshown = f"{w:.3g} {unit}"
-        # the trailing GEMMs multiply split fp32 operands (hi hi + hi lo + lo hi):
-        # three fp16 MFMA products per algorithmic one
-        pipe = f"{3 * ach / (PEAK_FP16_TFLOPS * 1e12):.3f}" if name.startswith("a5") else ""
+        # the trailing GEMMs over >= 512 error columns (nearly all the work)
+        # multiply the errors as two fp16 parts by U' in fp16: two fp16 MFMA
+        # products per algorithmic one
+        pipe = f"{2 * ach / (PEAK_FP16_TFLOPS * 1e12):.3f}" if name.startswith("a5") else ""
         lines.append(f"| {name} | {t * 1e3:.3f} | {wshown} | {shown} | {bound} | "
                      f"{ach / peak:.3f} | {pipe} |")
     lines.append("")
@@ -493,8 +505,8 @@ def stage_roofline(cfg, rows):
     lines.append("Peaks: fp16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s, HBM 8 TB/s. Work per "
                  "stage: a1 N n(n+1), a2 8 n^2 + 6 out in bytes, a3 2 n^3 / 3, a4 "
                  "7 out in + 8 out in / gs bytes, a5 out in (in - B), a6 out in (1 + b/8) bytes. "
-                 "MFMA pipe: fp16 MFMA work actually issued (three products per split-fp32 "
-                 "product) over the fp16 peak.")
+                 "MFMA pipe: fp16 MFMA work actually issued (two products per algorithmic "
+                 "one in the trailing GEMMs) over the fp16 peak.")
     return lines
 
 
@@ -1250,7 +1262,9 @@ def main():
         if args.dequant_tokens is not None:
             summarize_dequant(args.config, args.dequant_tokens, args.summarize)
         elif args.block:
-            summarize_block(args.summarize)
+            summarize_block(args.summarize, "block")
+        elif args.decoder:
+            summarize_block(args.summarize, "decoder")
         elif args.mfma_counters:
             summarize_mfma(args.config, args.summarize)
         else:
