@@ -308,10 +308,12 @@ def summarize_mfma(cfg_name: str, d: str):
              "dispatches' durations under the counters (kernels of the factorization overlap on "
              "three streams).  Active cycles = GRBM_GUI_ACTIVE / 8 XCDs; MFMA util = "
              "SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x 1024 SIMDs); fp16 MFMA work issued = "
-             "SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 (the split-fp32 GEMMs issue three fp16 products per "
-             "algorithmic one); clock = active cycles / time, meaningful for long kernels alone "
-             "on the GPU (the SYRK): for short or overlapping dispatches the counting window is "
-             "wider than the kernel.", "",
+             "SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 (gemm_e2_dma issues two fp16 products per "
+             "algorithmic one, gemm_f32_dma with split operands three; gemm_f32_dma over fewer "
+             "than 512 error columns runs fp32 MFMAs, which this counter leaves out); clock = "
+             "active cycles / time, given for the SYRK only: it runs long and alone on the GPU, "
+             "while for short or overlapping dispatches the counting window is wider than the "
+             "kernel.", "",
              "| kernel | dispatches | ms | MFMA util | fp16 MFMA TFLOP issued | issued TFLOP/s | "
              "clock GHz |", "|---|---:|---:|---:|---:|---:|---:|"]
     for name, f in sorted(fam.items(), key=lambda kv: -kv[1]["busy"]):
@@ -321,8 +323,9 @@ def summarize_mfma(cfg_name: str, d: str):
         act = f["gui"] / xcd
         util = f["busy"] / max(act * simds, 1.0)
         fl = f["mops"] * 512
+        clock = f"{act / t / 1e9:.2f}" if name.startswith("syrk_") else ""
         lines.append(f"| {name} | {len(f['dur'])} | {t * 1e3:.3f} | {util:.3f} | {fl / 1e12:.3f} | "
-                     f"{fl / t / 1e12:.0f} | {act / t / 1e9:.2f} |")
+                     f"{fl / t / 1e12:.0f} | {clock} |")
     with open(os.path.join(ROOT, "profiles", f"layer_{cfg_name}_mfma_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -352,10 +355,7 @@ def summarize(cfg_name: str, d: str):
     for r in trace:
         if int(r["Start_Timestamp"]) < t_timed:
             continue
-        name = r["Kernel_Name"]
-        if name.startswith("_Z"):
-            name = name[:60]
-        name = name.split("(")[0].replace("void ", "")[:70]
+        name = _kernel_base_name(r["Kernel_Name"])
         dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         stats.setdefault(name, []).append(dur)
     lines = [f"# rocprofv3 kernel statistics: bench.py --config {cfg_name} ({shape})", "",
@@ -493,9 +493,11 @@ def stage_roofline(cfg, rows):
         shown = f"{ach / 1e12:.1f} TFLOP/s" if unit == "flop" else f"{ach / 1e9:.0f} GB/s"
         wshown = f"{w:.3g} {unit}"
         # the trailing GEMMs over >= 512 error columns (nearly all the work)
-        # multiply the errors as two fp16 parts by U' in fp16: two fp16 MFMA
-        # products per algorithmic one
-        pipe = f"{2 * ach / (PEAK_FP16_TFLOPS * 1e12):.3f}" if name.startswith("a5") else ""
+        # multiply the errors as two fp16 parts by U' in fp16 (two fp16 MFMA
+        # products per algorithmic one), above 16384 columns by U' as two
+        # fp16 parts as well (three)
+        prods = 3 if n > 16384 else 2
+        pipe = f"{prods * ach / (PEAK_FP16_TFLOPS * 1e12):.3f}" if name.startswith("a5") else ""
         lines.append(f"| {name} | {t * 1e3:.3f} | {wshown} | {shown} | {bound} | "
                      f"{ach / peak:.3f} | {pipe} |")
     lines.append("")
@@ -505,8 +507,9 @@ def stage_roofline(cfg, rows):
     lines.append("Peaks: fp16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s, HBM 8 TB/s. Work per "
                  "stage: a1 N n(n+1), a2 8 n^2 + 6 out in bytes, a3 2 n^3 / 3, a4 "
                  "7 out in + 8 out in / gs bytes, a5 out in (in - B), a6 out in (1 + b/8) bytes. "
-                 "MFMA pipe: fp16 MFMA work actually issued (two products per algorithmic "
-                 "one in the trailing GEMMs) over the fp16 peak.")
+                 "MFMA pipe: fp16 MFMA work actually issued (" +
+                 ("three" if n > 16384 else "two") + " products per algorithmic one in the "
+                 "trailing GEMMs) over the fp16 peak.")
     return lines
 
 
