@@ -254,9 +254,11 @@ size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, i
  * A chunk of 32 positions whose g_idx entries are all equal is dequantized
  * with one scale and zero; chunks that mix groups (act-order layers as
  * packed) read them per position and run several times slower:
- * gptq_dequant_group_order turns such a layer into one without them.
- * Errors: INVALID_ARG, UNSUPPORTED (x_dtype not F16, bits, alignment),
- *         WORKSPACE, HIP.
+ * gptq_dequant_group_order turns such a layer into one without them (from
+ * 256 tokens on the check is per 16 positions).
+ * Errors: INVALID_ARG, UNSUPPORTED (x_dtype not F16, bits, alignment;
+ *         qweight, scales or zeros of 2 GiB or more; ldx above 2^22 with
+ *         M > 8), WORKSPACE, HIP.
  */
 int gptq_dequant_matmul(const void* X, int x_dtype, int64_t M, int64_t in, int64_t ldx,
                         const int32_t* qweight, const float* scales, const int32_t* zeros,

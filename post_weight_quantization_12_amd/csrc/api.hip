@@ -62,6 +62,12 @@ int dequant_check(const void* X, int x_dtype, int64_t M, int64_t in, int64_t ldx
     return bad(GPTQ_ERR_UNSUPPORTED, "bits must be 2, 3, 4 or 8");
   if (ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(X) & 15) != 0)
     return bad(GPTQ_ERR_UNSUPPORTED, "X rows must be 16-byte aligned (ldx a multiple of 8)");
+  // the matrix-core kernels address qweight, scales, zeros and a 256-row X
+  // tile with 32-bit buffer offsets
+  if ((in / 32) * bits * out > (int64_t(1) << 29) || n_groups * out > (int64_t(1) << 29))
+    return bad(GPTQ_ERR_UNSUPPORTED, "qweight, scales and zeros must each be below 2 GiB");
+  if (M > 8 && ldx > (int64_t(1) << 22))
+    return bad(GPTQ_ERR_UNSUPPORTED, "from 9 tokens on, ldx must be at most 2^22");
   return GPTQ_OK;
 }
 }  // namespace gptq

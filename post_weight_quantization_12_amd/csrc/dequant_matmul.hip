@@ -20,7 +20,8 @@
 //     is staged in LDS as fp16 pairs.  The input dimension is split over
 //     several workgroups (grid >= 2 per compute unit); their partial sums go
 //     to the workspace and a second kernel adds them in a fixed order.
-//   * many tokens (prefill): 256 x 128 tiles on v_mfma_f32_32x32x16_f16.
+//   * many tokens (prefill): 256 x 256 tiles from 256 tokens on, 128 x 128
+//     below, on v_mfma_f32_32x32x16_f16.
 //     Per 32-k chunk the X tile goes to LDS as is (k contiguous: an MFMA A
 //     operand is one 16-byte read) and the weight tile is dequantized into
 //     LDS as fp16 column-major (k contiguous: a B operand is one 16-byte
@@ -555,19 +556,442 @@ dq_mfma_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ld
       }
 }
 
-// Splits of the input range for the tile kernel: about 512 workgroups, each
-// split at least 8 chunks.
-// 256-row tiles from this many tokens on (fewer: 128 rows, less padding).
-constexpr int64_t TM256_MIN_M = 256;
-inline int mfma_tile_rows(int64_t M) { return M >= TM256_MIN_M ? 256 : 128; }
-int64_t mfma_chunks_per_split(int64_t M, int64_t in, int64_t out) {
+// ------------------------------------------------------- 256 x 256 tiles --
+// Prefill from 256 tokens on.  Workgroup tile: 256 tokens x 256 outputs, 8
+// waves as 2 x 4 blocks of 128 tokens x 64 outputs (4 x 2 blocks of 32 x 32,
+// 8 MFMAs per 16 k).  A stage is one 32-k chunk of two 16-k substeps.
+//   * X goes from memory straight into LDS (buffer_load ... lds), and so do
+//     the weight words, scales and zeros: all of stage s + 6 at the middle
+//     of stage s, into a ring of six stage slots.  A stage's loads are 16 X
+//     pieces, b word rows and the scale and zero rows, 1 KiB each, dealt
+//     round-robin to the 8 waves: wave w issues loads w, w + 8, ... (K or
+//     K - 1 of them, K = 3, 4 for 8 bits; a direct-to-LDS load costs the
+//     compute unit about 44 cycles whatever its size, so none is issued
+//     for nothing).  Loads complete in issue order, so "the loads of stage
+//     s + 1 have landed" is vmcnt <= 4 K_w at the middle of stage s.
+//   * The A operands (X) are read from LDS: per MFMA 512 bytes (128-token
+//     blocks).  The B operands never touch LDS as weights: each lane reads
+//     the one to three words holding its 8 codes (column, 8-k group) and
+//     the column's scale and zero, and dequantizes them in registers (the
+//     two-part scale of the 128 x 128 kernel, bit-identical weights); the
+//     two waves that share a column range both do so.  A substep's
+//     dequantization runs between the MFMAs of the substep before it, so
+//     the matrix cores keep running while it executes.
+//   * X rows are 64 bytes, four 16-byte chunks; chunk q of row r sits at
+//     position q ^ swz(r), swz(r) = (r >> 2) & 3: the 16-byte reads of 16
+//     adjacent lanes (rows) hit distinct banks of the 64.  Token rows past
+//     M read as zeros (buffer range).
+//   * Each chunk's group (or -1 where its 32 g_idx entries differ) comes
+//     from a table a small kernel writes first; a mixed chunk takes scale
+//     and zero per weight from memory (after the one-group result, which it
+//     replaces).
+//   * One barrier per stage, between its two substeps (s_barrier with
+//     explicit waits: a fence would drain the loads in flight).
+//   * Needs out % 4 == 0 and 16-byte aligned qweight, scales and zeros (the
+//     launcher falls back to the 128 x 128 kernel otherwise); buffer offsets
+//     are 32-bit (the argument check bounds qweight, scales and zeros below
+//     2 GiB and, from 9 tokens on, ldx by 2^22).
+// Tiles: a 1-D grid over (token tile, split, column tile), column tiles
+// fastest; block b runs logical tile (b % 8) per_xcd + b / 8, so each XCD
+// (blocks dispatched round-robin) walks a contiguous run and its ~32
+// resident workgroups share one X tile in its L2.
+constexpr int QT = 256;
+constexpr int QT_L = 6;  // ring slots
+template <int B>
+__host__ __device__ constexpr int qt_loads_per_wave() { return B == 8 ? 4 : 3; }
+constexpr int QT_STAGE = QT * DQ_CHUNK * 2;  // bytes of one 256 x 32 fp16 tile
+
+// 16 lanes of a 16-byte LDS access are served together from 64 banks
+// (256 bytes): rows r and r + 4 k share banks unless their chunks differ.
+__device__ inline int qt_swz(int r) { return (r >> 2) & 3; }
+
+__device__ inline void qt_dma(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) char*)lds),
+      16, voff, 0, 0, 0);
+}
+
+// cgroup[c] = the group of chunk c when its 32 g_idx entries are equal, else -1.
+__global__ void __launch_bounds__(256)
+dq_chunk_group_kernel(const int32_t* __restrict__ g_idx, int64_t nch, int32_t* __restrict__ cgroup) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= nch) return;
+  const int32_t* g = g_idx + c * DQ_CHUNK;
+  const int32_t g0 = g[0];
+  int diff = 0;
+  for (int k = 1; k < DQ_CHUNK; ++k) diff |= g[k] ^ g0;
+  cgroup[c] = diff == 0 ? g0 : -1;
+}
+
+// Codes 8 kg .. 8 kg + 7 of a chunk (a lane's B operand) from the chunk's
+// word rows wq[i * QT + col]: the 1 - 3 words holding them, as a window
+// with code j at bits B j.
+template <int B>
+__device__ inline uint64_t qt_window(const uint32_t* wq, int col, int kg) {
+  constexpr int bit0 = 0;
+  (void)bit0;
+  const int bit = 8 * kg * B, w = bit >> 5, off = bit & 31;
+  if constexpr (B == 4) {
+    return wq[kg * QT + col];
+  } else if constexpr (B == 8) {
+    return (uint64_t)wq[(2 * kg) * QT + col] | ((uint64_t)wq[(2 * kg + 1) * QT + col] << 32);
+  } else if constexpr (B == 2) {
+    return wq[(kg >> 1) * QT + col] >> (16 * (kg & 1));
+  } else {  // B == 3: 24 bits at bit 24 kg, in words w and w + 1 (w + 1 <= 2)
+    const uint32_t lo = wq[w * QT + col];
+    const uint32_t hi = w + 1 < 3 ? wq[(w + 1) * QT + col] : 0u;
+    return ((((uint64_t)hi << 32) | lo) >> off);
+  }
+}
+
+// The 8 weights s (q - z) of a lane, rounded as the 128 x 128 kernel rounds
+// them ((q - z) sh + fl((q - z) sl) in one fused fp16 rounding), in k order.
+// pm = pair_mask<B>() and pmagic = 0x64006400 live in registers (and_or).
+template <int B>
+__device__ inline half8_t qt_dequant8(uint64_t win, half2_t sh, half2_t sl, half2_t zz,
+                                      uint32_t pm, uint32_t pmagic) {
+  const uint32_t magic = pmagic;
+  half2_t q[4];  // (1024 + code, 1024 + code) pairs
+  if constexpr (B == 4 || B == 2) {
+    // pairs (j, j + 4): one AND-OR each on the (for b = 2: doubled) window
+    uint32_t v = (uint32_t)win;
+    if constexpr (B == 2) v = (v & 0xFFFFu) | ((v & 0xFFFFu) << 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = __builtin_bit_cast(half2_t, and_or(v >> (B * j), pm, pmagic));
+  } else if constexpr (B == 8) {
+    // pairs (j, j + 2) of each word
+    const uint32_t w0 = (uint32_t)win, w1 = (uint32_t)(win >> 32);
+    q[0] = __builtin_bit_cast(half2_t, and_or(w0, pm, pmagic));
+    q[1] = __builtin_bit_cast(half2_t, and_or(w0 >> 8, pm, pmagic));
+    q[2] = __builtin_bit_cast(half2_t, and_or(w1, pm, pmagic));
+    q[3] = __builtin_bit_cast(half2_t, and_or(w1 >> 8, pm, pmagic));
+  } else {  // B == 3: pairs (2j, 2j + 1)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = (uint32_t)(win >> (6 * j)) & 7u, b = (uint32_t)(win >> (6 * j + 3)) & 7u;
+      q[j] = __builtin_bit_cast(half2_t, a | (b << 16) | magic);
+    }
+  }
+  half2_t d[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const half2_t qz = q[j] - zz;
+    d[j] = __builtin_elementwise_fma(qz, sh, qz * sl);
+  }
+  // k order
+  if constexpr (B == 4 || B == 2) {  // d[j] = (k j, k j + 4)
+    return (half8_t){d[0][0], d[1][0], d[2][0], d[3][0], d[0][1], d[1][1], d[2][1], d[3][1]};
+  } else if constexpr (B == 8) {  // d[0] = (0, 2), d[1] = (1, 3), d[2] = (4, 6), d[3] = (5, 7)
+    return (half8_t){d[0][0], d[1][0], d[0][1], d[1][1], d[2][0], d[3][0], d[2][1], d[3][1]};
+  } else {
+    return (half8_t){d[0][0], d[0][1], d[1][0], d[1][1], d[2][0], d[2][1], d[3][0], d[3][1]};
+  }
+}
+
+template <int B>
+__global__ void __launch_bounds__(512)
+dq_tile_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
+               const uint32_t* __restrict__ qw, const float* __restrict__ scales,
+               const int32_t* __restrict__ zeros, const int32_t* __restrict__ g_idx,
+               const int32_t* __restrict__ cgroup, int64_t out, int64_t cps, int ntn, int ns,
+               int64_t total, float* __restrict__ part, void* __restrict__ Y, int y_f16,
+               int64_t ldy) {
+  // One LDS object per ring slot: the stage's X tile, its weight words,
+  // scale and zero rows, and the pad for the spare loads.  The compiler
+  // tracks direct-to-LDS loads per object (up to eight), so with one object
+  // per slot it can tell that the slot read is not the target of a load in
+  // flight.
+  constexpr int L = QT_L, K = qt_loads_per_wave<B>();
+  constexpr int WOFF = QT_STAGE, PAD = QT_STAGE + (B + 2) * QT * 4;
+  constexpr int SLOT = PAD;
+  static_assert(L * SLOT <= 160 * 1024, "LDS");
+  static_assert(16 + B + 2 <= 8 * K && 16 + B + 2 > 8 * (K - 1), "loads per stage");
+  __shared__ __align__(16) char sl0[SLOT];
+  __shared__ __align__(16) char sl1[SLOT];
+  __shared__ __align__(16) char sl2[SLOT];
+  __shared__ __align__(16) char sl3[SLOT];
+  __shared__ __align__(16) char sl4[SLOT];
+  __shared__ __align__(16) char sl5[SLOT];
+  const int64_t per_xcd = (total + 7) / 8;
+  const int64_t o = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (o >= total) return;
+  const int tn = (int)(o % ntn);
+  const int64_t rest = o / ntn;
+  const int z = (int)(rest % ns);
+  const int64_t tm = rest / ns;
+  const int64_t m0 = tm * QT, n0 = (int64_t)tn * QT;
+  const int64_t nch_all = in / DQ_CHUNK;
+  const int64_t cb = (int64_t)z * cps;
+  const int64_t ce = cb + cps < nch_all ? cb + cps : nch_all;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;  // 128-token half, 64-output quarter
+  const int l32 = lane & 31, hi8 = lane >> 5;
+
+  // ---- loads
+  const int64_t rows = M - m0 < QT ? M - m0 : QT;
+  const int64_t cols = out - n0 < QT ? out - n0 : QT;  // a multiple of 4
+  uint32_t voff[2];  // X pieces wave and wave + 8
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 16 * (wave + 8 * q) + (lane >> 2), pos = lane & 3;
+    voff[q] = (uint32_t)(((int64_t)r * ldx + 8 * (pos ^ qt_swz(r))) * 2);
+  }
+  const uint32_t loff = (uint32_t)lane * 16;  // 4 columns of a word, scale or zero row
+  // load t of a stage (wave w issues t = w + 8 j, j < K): X piece t (rows
+  // 16 t .. 16 t + 15) for t < 16, then word row t - 16, then the scale and
+  // the zero row, then pads
+  auto issue = [&](int64_t c, int grp, char* sd) {
+    const bool live = c < ce;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int t = wave + 8 * j;  // wave-uniform
+      const void* base = X;
+      int bytes = 0;
+      uint32_t vo = loff;
+      int dst = PAD;
+      if (j < 2) {  // t < 16 (wave < 8)
+        vo = voff[j];
+        dst = t * 1024;
+        if (live) {
+          base = X + m0 * ldx + c * DQ_CHUNK;
+          bytes = (int)(((rows - 1) * ldx + (in - c * DQ_CHUNK)) * 2);
+        }
+      } else if (t < 16 + B) {
+        dst = WOFF + (t - 16) * QT * 4;
+        if (live) {
+          base = qw + (c * B + (t - 16)) * out + n0;
+          bytes = (int)(cols * 4);
+        }
+      } else if (t < 18 + B) {
+        dst = WOFF + (t - 16) * QT * 4;
+        if (live && grp >= 0) {
+          base = t == 16 + B ? (const void*)(scales + grp * out + n0)
+                             : (const void*)(zeros + grp * out + n0);
+          bytes = (int)(cols * 4);
+        }
+      }
+      if (t < 18 + B) {  // a pad when not (each costs as much as a real load)
+        __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+        qt_dma(rs, vo, sd + dst);
+      }
+    }
+  };
+  // the loads of stage s + 1 have landed: L - 2 stages were issued after
+  // them, K or K - 1 loads each (waves whose last load would be a pad)
+  const bool full = wave + 8 * (K - 1) < 18 + B;
+  auto wait_next = [&]() {
+    if (full)
+      wait_vmcnt<(L - 2) * K>();
+    else
+      wait_vmcnt<(L - 2) * (K - 1)>();
+  };
+  // the chunk's group (cgroup: one group, or -1), one scalar load
+  auto group_of = [&](int64_t c) -> int {
+    return __builtin_amdgcn_readfirstlane(cgroup[c < ce ? c : ce - 1]);
+  };
+
+  // ---- operands
+  const int rsw = qt_swz(l32);
+  const uint32_t pm = pair_mask<B>(), pmagic = 0x64006400u;
+  struct AFr {
+    half8_t a[4];
+  };
+  struct BFr {
+    half8_t b[2];
+  };
+  struct Scl {
+    half2_t sh[2], sl[2], zz[2];
+  };
+  auto load_a = [&](AFr& F, const char* xb, int sub) {
+    const int cpos = ((2 * sub + hi8) ^ rsw) * 16;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      F.a[a] = *reinterpret_cast<const half8_t*>(xb + (wm * 128 + a * 32 + l32) * 64 + cpos);
+  };
+  // column of block b of this lane (local), and its global index for the
+  // per-weight path
+  auto colb = [&](int b) { return wn * 64 + b * 32 + l32; };
+  auto scales_of = [&](const char* wd, Scl& S) {
+    const uint32_t* sz = reinterpret_cast<const uint32_t*>(wd) + B * QT;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float s = __uint_as_float(sz[colb(b)]);
+      const int32_t zi = (int32_t)sz[QT + colb(b)];
+      const _Float16 hs = (_Float16)s, ls = (_Float16)(s - (float)hs);
+      const _Float16 zh = (_Float16)(1024.0f + (float)zi);
+      S.sh[b] = (half2_t){hs, hs};
+      S.sl[b] = (half2_t){ls, ls};
+      S.zz[b] = (half2_t){zh, zh};
+    }
+  };
+  auto dequant_b = [&](BFr& F, const char* wd, const Scl& S, int sub) {
+    const uint32_t* wq = reinterpret_cast<const uint32_t*>(wd);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      F.b[b] = qt_dequant8<B>(qt_window<B>(wq, colb(b), 2 * sub + hi8), S.sh[b], S.sl[b], S.zz[b],
+                              pm, pmagic);
+  };
+  // several groups in the chunk: scale and zero per weight from memory
+  auto dequant_b_mixed = [&](BFr& F, const char* wd, int64_t c, int sub) {
+    const uint32_t* wq = reinterpret_cast<const uint32_t*>(wd);
+    const int kg = 2 * sub + hi8;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = n0 + colb(b) < out ? n0 + colb(b) : out - 1;
+      const uint64_t win = qt_window<B>(wq, colb(b), kg);
+      half8_t r;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t g = g_idx[c * DQ_CHUNK + 8 * kg + j];
+        const float s = scales[g * out + col];
+        const _Float16 hs = (_Float16)s, ls = (_Float16)(s - (float)hs);
+        const _Float16 qz = (_Float16)((float)((win >> (B * j)) & ((1u << B) - 1u)) -
+                                       (float)zeros[g * out + col]);
+        r[j] = __builtin_elementwise_fma(qz, hs, qz * ls);
+      }
+      F.b[b] = r;
+    }
+    wait_vmcnt<0>();  // this path's own loads (the compiler's waits assume none in flight)
+  };
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+  auto mma = [&](const AFr& A, const BFr& Bf) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A.a[a], Bf.b[b], acc[a][b], 0, 0, 0);
+  };
+  // interleave: the substep's VALU work between its 8 MFMAs
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads first
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+    }
+  };
+
+  // ---- prologue: loads of stages cb .. cb + L - 1 issued, stage cb's
+  // landed and its first substep operands ready
+  int g0 = group_of(cb), g1 = group_of(cb + 1), g2 = group_of(cb + 2);
+  int g3 = group_of(cb + 3), g4 = group_of(cb + 4), g5 = group_of(cb + 5);
+  issue(cb + 0, g0, sl0);
+  issue(cb + 1, g1, sl1);
+  issue(cb + 2, g2, sl2);
+  issue(cb + 3, g3, sl3);
+  issue(cb + 4, g4, sl4);
+  issue(cb + 5, g5, sl5);
+  wait_vmcnt<(L - 1) * K>();  // stage cb landed; the rest stays in flight
+  __builtin_amdgcn_s_barrier();
+  AFr A0, A1;
+  BFr B0, B1;
+  Scl S;
+  load_a(A0, sl0, 0);
+  scales_of(sl0 + WOFF, S);
+  dequant_b(B0, sl0 + WOFF, S, 0);
+  if (g0 < 0) dequant_b_mixed(B0, sl0 + WOFF, cb, 0);
+
+  // Stage c in slot xc (group gcur), the next stage in slot xn (group
+  // gnxt); gi: group of stage c + L, whose loads go to slot xc at the
+  // middle of stage c.
+  int64_t c = cb;
+  auto step = [&](char* xc, int gcur, char* xn, int gnxt, int gi)
+      __attribute__((always_inline)) {
+    const char* wcs = xc + WOFF;
+    const char* wns = xn + WOFF;
+    // substep 0: MFMAs on A0/B0 while substep 1's operands are formed
+    load_a(A1, xc, 1);
+    mma(A0, B0);
+    dequant_b(B1, wcs, S, 1);
+    interleave();
+    if (gcur < 0) dequant_b_mixed(B1, wcs, c, 1);
+    // stage c + 1 landed and visible; stage c's slot free after the barrier
+    wait_next();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    issue(c + L, gi, xc);
+    // substep 1: MFMAs on A1/B1 while stage c + 1's first operands are formed
+    load_a(A0, xn, 0);
+    scales_of(wns, S);
+    mma(A1, B1);
+    dequant_b(B0, wns, S, 0);
+    interleave();
+    if (gnxt < 0 && c + 1 < ce) dequant_b_mixed(B0, wns, c + 1, 0);
+    ++c;
+  };
+  // g0 .. g(L-1): groups of stages c .. c + L - 1.  Whole rounds of L
+  // stages run in a loop with one exit, the rest one stage at a time after
+  // it: with an exit after every stage the compiler loses track of the
+  // loads in flight at the loop head and waits for all of them there.
+  int gn;
+#define GPTQ_QT_STEP(XC, XN)                             \
+  gn = group_of(c + L);                                 \
+  step(XC, g0, XN, g1, gn);                             \
+  g0 = g1; g1 = g2; g2 = g3; g3 = g4; g4 = g5; g5 = gn;
+  while (c + 6 <= ce) {
+    GPTQ_QT_STEP(sl0, sl1)
+    GPTQ_QT_STEP(sl1, sl2)
+    GPTQ_QT_STEP(sl2, sl3)
+    GPTQ_QT_STEP(sl3, sl4)
+    GPTQ_QT_STEP(sl4, sl5)
+    GPTQ_QT_STEP(sl5, sl0)
+  }
+  if (c < ce) { GPTQ_QT_STEP(sl0, sl1) }
+  if (c < ce) { GPTQ_QT_STEP(sl1, sl2) }
+  if (c < ce) { GPTQ_QT_STEP(sl2, sl3) }
+  if (c < ce) { GPTQ_QT_STEP(sl3, sl4) }
+  if (c < ce) { GPTQ_QT_STEP(sl4, sl5) }
+#undef GPTQ_QT_STEP
+  wait_vmcnt<0>();  // no load may land in LDS after the workgroup ends
+  wait_lgkm0();
+
+  // 32 x 32 block layout: element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4,
+  // column l % 32
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t r = m0 + wm * 128 + a * 32 + 8 * (v >> 2) + 4 * hi8 + (v & 3);
+        const int64_t cc = n0 + colb(b);
+        if (r < M && cc < out) {
+          if (ns > 1)
+            part[((int64_t)z * M + r) * out + cc] = acc[a][b][v];
+          else if (y_f16)
+            static_cast<_Float16*>(Y)[r * ldy + cc] = (_Float16)acc[a][b][v];
+          else
+            static_cast<float*>(Y)[r * ldy + cc] = acc[a][b][v];
+        }
+      }
+}
+
+// Splits of the input range: about 512 workgroups for the 128 x 128 kernel
+// (two per compute unit), 256 for the 256 x 256 one (one per compute unit),
+// each split at least 8 chunks.  The 256 x 256 tiles take 256 tokens on.
+constexpr int64_t QT_MIN_M = 256;
+int64_t mfma_chunks_per_split(int64_t M, int64_t in, int64_t out, bool big) {
   const int64_t nch = in / DQ_CHUNK;
-  const int TM = mfma_tile_rows(M);
-  const int64_t tiles = ((out + TN - 1) / TN) * ((M + TM - 1) / TM);
-  int64_t ns = (512 + tiles - 1) / tiles;
+  const int64_t tm = big ? QT : 128, tn = big ? QT : TN, want = big ? 256 : 512;
+  const int64_t tiles = ((out + tn - 1) / tn) * ((M + tm - 1) / tm);
+  int64_t ns = (want + tiles - 1) / tiles;
   if (ns > nch / 8) ns = nch / 8;
   if (ns < 1) ns = 1;
   return (nch + ns - 1) / ns;
+}
+size_t mfma_partial_bytes(int64_t M, int64_t in, int64_t out, bool big) {
+  const int64_t cps = mfma_chunks_per_split(M, in, out, big);
+  const int64_t ns = (in / DQ_CHUNK + cps - 1) / cps;
+  return ns > 1 ? align_up((size_t)ns * M * out * sizeof(float)) : 0;
 }
 
 // ------------------------------------------------------------ group order --
@@ -697,11 +1121,16 @@ hipError_t launch_small_b(const SmallPlan& p, const _Float16* X, int64_t M, int6
 
 size_t dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order) {
   if (M > DQ_SMALL_M_MAX) {
-    // [gathered X when has_order][split partials when more than one split]
-    const int64_t cps = mfma_chunks_per_split(M, in, out);
-    const int64_t ns = (in / DQ_CHUNK + cps - 1) / cps;
-    return (has_order ? align_up((size_t)M * in * sizeof(_Float16)) : 0) +
-           (ns > 1 ? align_up((size_t)ns * M * out * sizeof(float)) : 0);
+    // [gathered X when has_order][split partials when more than one split];
+    // from 256 tokens either tile kernel may run (alignment decides): the
+    // larger need
+    size_t parts = mfma_partial_bytes(M, in, out, false);
+    if (M >= QT_MIN_M && out % 4 == 0) {  // + the chunk group table
+      const size_t b = align_up((size_t)(in / DQ_CHUNK) * sizeof(int32_t)) +
+                       mfma_partial_bytes(M, in, out, true);
+      parts = b > parts ? b : parts;
+    }
+    return (has_order ? align_up((size_t)M * in * sizeof(_Float16)) : 0) + parts;
   }
   // either column layout may run (alignment decides): the larger need
   size_t need = 0;
@@ -756,27 +1185,42 @@ hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
     ldx = in;
     wsp += align_up((size_t)M * in * sizeof(_Float16));
   }
-  const int64_t cps = mfma_chunks_per_split(M, in, out);
+  const bool big = M >= QT_MIN_M && out % 4 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(qweight) | reinterpret_cast<uintptr_t>(scales) |
+                     reinterpret_cast<uintptr_t>(zeros)) & 15) == 0;
+  const int64_t cps = mfma_chunks_per_split(M, in, out, big);
   const int64_t ns = (in / DQ_CHUNK + cps - 1) / cps;
   float* part = ns > 1 ? reinterpret_cast<float*>(wsp) : nullptr;
-  const int TM = mfma_tile_rows(M);
-  dim3 grid((unsigned)((out + TN - 1) / TN), (unsigned)((M + TM - 1) / TM), (unsigned)ns);
-#define GPTQ_DQ_MFMA(BB, TT)                                                                 \
-  hipLaunchKernelGGL((dq_mfma_kernel<BB, TT>), grid, dim3(512), 0, s, x, M, in, ldx, qw, scales, \
-                     zeros, g_idx, out, cps, part, Y, y_f16, ldy)
-  if (TM == 256) {
+  if (big) {
+    int32_t* cgroup = reinterpret_cast<int32_t*>(wsp);
+    const int64_t nch = in / DQ_CHUNK;
+    part = ns > 1 ? reinterpret_cast<float*>(wsp + align_up((size_t)nch * sizeof(int32_t))) : nullptr;
+    hipLaunchKernelGGL(dq_chunk_group_kernel, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, s,
+                       g_idx, nch, cgroup);
+    GPTQ_HIP_TRY(hipGetLastError());
+    const int64_t ntn = (out + QT - 1) / QT, total = ((M + QT - 1) / QT) * ns * ntn;
+    const dim3 grid((unsigned)(8 * ((total + 7) / 8)));
+#define GPTQ_DQ_TILE(BB)                                                                     \
+  hipLaunchKernelGGL((dq_tile_kernel<BB>), grid, dim3(512), 0, s, x, M, in, ldx, qw, scales, \
+                     zeros, g_idx, cgroup, out, cps, (int)ntn, (int)ns, total, part, Y, y_f16,  \
+                     ldy)
     switch (bits) {
-      case 2: GPTQ_DQ_MFMA(2, 256); break;
-      case 3: GPTQ_DQ_MFMA(3, 256); break;
-      case 8: GPTQ_DQ_MFMA(8, 256); break;
-      default: GPTQ_DQ_MFMA(4, 256); break;
+      case 2: GPTQ_DQ_TILE(2); break;
+      case 3: GPTQ_DQ_TILE(3); break;
+      case 8: GPTQ_DQ_TILE(8); break;
+      default: GPTQ_DQ_TILE(4); break;
     }
+#undef GPTQ_DQ_TILE
   } else {
+    dim3 grid((unsigned)((out + TN - 1) / TN), (unsigned)((M + 127) / 128), (unsigned)ns);
+#define GPTQ_DQ_MFMA(BB)                                                                     \
+  hipLaunchKernelGGL((dq_mfma_kernel<BB, 128>), grid, dim3(512), 0, s, x, M, in, ldx, qw,    \
+                     scales, zeros, g_idx, out, cps, part, Y, y_f16, ldy)
     switch (bits) {
-      case 2: GPTQ_DQ_MFMA(2, 128); break;
-      case 3: GPTQ_DQ_MFMA(3, 128); break;
-      case 8: GPTQ_DQ_MFMA(8, 128); break;
-      default: GPTQ_DQ_MFMA(4, 128); break;
+      case 2: GPTQ_DQ_MFMA(2); break;
+      case 3: GPTQ_DQ_MFMA(3); break;
+      case 8: GPTQ_DQ_MFMA(8); break;
+      default: GPTQ_DQ_MFMA(4); break;
     }
   }
 #undef GPTQ_DQ_MFMA

@@ -65,6 +65,15 @@ CASES = [
     ("m17_2b_f16", 17, 256, 130, 2, 32, True, torch.float16),
     ("m200_4b_desc", 200, 1024, 384, 4, 128, True, torch.float32),
     ("m512_3b_g64", 512, 2048, 1024, 3, 64, False, torch.float32),
+    # 256 x 256 tiles (from 256 tokens): ragged token and column tiles, a
+    # split input range, an input range shorter than the load pipeline, act
+    # order as packed (groups mixed inside every 16 positions), 2/4/8 bits
+    ("m300_4b_g128_ragged_f16", 300, 4096, 600, 4, 128, False, torch.float16),
+    ("m256_8b_g32_split", 256, 512, 256, 8, 32, False, torch.float32),
+    ("m1000_2b_g64", 1000, 1024, 520, 2, 64, False, torch.float32),
+    ("m640_4b_rowgroup_short", 640, 96, 300, 4, -1, False, torch.float32),
+    ("m384_4b_g128_desc_packed", 384, 1024, 264, 4, 128, True, torch.float16),
+    ("m257_3b_g32_desc_packed", 257, 256, 513, 3, 32, True, torch.float32),
     # four columns per lane (out % 4 == 0, M <= 4), ragged last workgroup
     ("m3_4b_g64_ragged", 3, 512, 260, 4, 64, False, torch.float16),
     ("m2_8b_g32_desc", 2, 256, 132, 8, 32, True, torch.float32),
@@ -222,7 +231,7 @@ def test_group_order_full_size_sampled():
 
 def test_prefill_full_size_sampled():
     """2048 tokens through the 4096 x 11008 act-order layer (group-ordered), as
-    timed: 256 x 128 tiles with a split input range; sampled columns against
+    timed: 256 x 256 tiles with a split input range; sampled columns against
     the oracle on the layer as packed."""
     out, inp, bits, gs = 4096, 11008, 4, 128
     _banner(f"prefill full size M=2048 out={out} in={inp} {bits}b g{gs}")
