@@ -116,7 +116,8 @@ DEQUANT_PROFILE_COMMANDS = {
                    "python -u bench.py --config {c} --dequant-tokens {m} --steps 1 --warmup 1 "
                    "--no-cpu-baseline --copy-probe"),
 }
-DQ_KERNELS = ("dq_small_kernel", "dq_reduce_kernel", "dq_mfma_kernel", "dq_gather_x_kernel")
+DQ_KERNELS = ("dq_small_kernel", "dq_reduce_kernel", "dq_mfma_kernel", "dq_tile_kernel",
+              "dq_chunk_group_kernel", "dq_gather_x_kernel", "dq_gather_x_cols_kernel")
 
 
 def _dq_kernel(name: str) -> bool:
@@ -171,7 +172,8 @@ def summarize_dequant(cfg_name: str, M: int, d: str):
         rows = list(csv.DictReader(open(os.path.join(d, ctr, "p_counter_collection.csv"))))
         # per call: the main kernel's dispatches count the calls
         calls = sum(1 for r in rows if ("dq_small_kernel" in r["Kernel_Name"]
-                                        or "dq_mfma_kernel" in r["Kernel_Name"]))
+                                        or "dq_mfma_kernel" in r["Kernel_Name"]
+                                        or "dq_tile_kernel" in r["Kernel_Name"]))
         tot = sum(float(r["Counter_Value"]) for r in rows if _dq_kernel(r["Kernel_Name"]))
         copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
         per[ctr] = (tot / calls, copy)
@@ -813,9 +815,12 @@ def dequant_main(args):
         kernel = ("dq_small_kernel" + (" + dq_reduce_kernel" if wsb else ""))
     else:
         achieved, peak, unit, bound = flops / (call_ms * 1e-3) / 1e12, PEAK_FP16_TFLOPS, "TFLOP/s", "mfma"
-        kernel = (("dq_gather_x_kernel + " if x_order is not None else "") + "dq_mfma_kernel"
-                  + (" + dq_reduce_kernel" if P.dequant_matmul_workspace_bytes(M, n, out) > 0
-                     else ""))
+        # from 256 tokens (out % 4 == 0, aligned weights): the 256 x 256 tiles
+        tiles = ("dq_chunk_group_kernel + dq_tile_kernel" if M >= 256 and out % 4 == 0
+                 else "dq_mfma_kernel")
+        kernel = (("dq_gather_x_kernel + " if x_order is not None else "") + tiles
+                  + (" + dq_reduce_kernel (split input range)" if M < 256 or out % 4 else
+                     " [+ dq_reduce_kernel when the input range is split]"))
     result = {
         "metric": "dequantize-on-the-fly matmul Y = X W^T from the packed layer, TFLOP/s",
         "value": flops / (call_ms * 1e-3) / 1e12,
@@ -994,7 +999,7 @@ def block_main(args):
         },
         "phase_ms": phases,
         "roofline": {
-            "kernel": ("forward phase: dq_gather_x_kernel + dq_mfma_kernel (gate and up as one "
+            "kernel": ("forward phase: dq_gather_x_kernel + dq_tile_kernel (gate and up as one "
                        "[4096 -> 22016] layer), silu_mul_kernel, syrk_dma_kernel per 32768-token "
                        "chunk"),
             "bound": "mfma",

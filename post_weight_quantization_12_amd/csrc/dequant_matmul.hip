@@ -996,9 +996,47 @@ size_t mfma_partial_bytes(int64_t M, int64_t in, int64_t out, bool big) {
 
 // ------------------------------------------------------------ group order --
 // Xp[m][p] = X[m][x_order[p]] (the matrix-core path's X in packed order).
+// A workgroup copies rows m0 .. m0 + R - 1 of X into LDS with 16-byte loads
+// (R in <= 32768 halves), then each thread takes 8 consecutive positions p:
+// one read of their x_order entries serves every staged row, and the 8
+// gathered values leave as one 16-byte store per row.  (A thread per
+// position and row read 2 bytes from scattered columns: 1.4 TB/s.)
+constexpr int64_t GATHER_LDS_HALVES = 32768;
+constexpr int64_t GATHER_MAX_IN = 65536;  // one 128 KiB row; wider: a thread per column
+int gather_rows(int64_t in) {
+  const int64_t r = GATHER_LDS_HALVES / in;
+  return (int)(r >= 8 ? 8 : r < 1 ? 1 : r);
+}
 __global__ void __launch_bounds__(256)
 dq_gather_x_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
-                   const int32_t* __restrict__ x_order, _Float16* __restrict__ Xp) {
+                   const int32_t* __restrict__ x_order, int R, _Float16* __restrict__ Xp) {
+  extern __shared__ __align__(16) _Float16 xrows[];  // [R][in]
+  const int64_t m0 = (int64_t)blockIdx.x * R;
+  const int nr = M - m0 < R ? (int)(M - m0) : R;
+  for (int r = 0; r < nr; ++r)
+    for (int64_t c = (int64_t)threadIdx.x * 8; c < in; c += 256 * 8)
+      *reinterpret_cast<uint4*>(&xrows[r * in + c]) =
+          *reinterpret_cast<const uint4*>(X + (m0 + r) * ldx + c);
+  __syncthreads();
+  for (int64_t p = (int64_t)threadIdx.x * 8; p < in; p += 256 * 8) {
+    int idx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) idx[j] = x_order[p + j];
+    for (int r = 0; r < nr; ++r) {
+      const _Float16* row = xrows + r * in;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)__builtin_bit_cast(uint16_t, row[idx[2 * j]]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, row[idx[2 * j + 1]]) << 16);
+      *reinterpret_cast<uint4*>(Xp + (m0 + r) * in + p) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+// Rows longer than GATHER_MAX_IN: one thread per position, rows strided.
+__global__ void __launch_bounds__(256)
+dq_gather_x_cols_kernel(const _Float16* __restrict__ X, int64_t M, int64_t in, int64_t ldx,
+                        const int32_t* __restrict__ x_order, _Float16* __restrict__ Xp) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (p >= in) return;
   const int64_t k = x_order[p];
@@ -1178,8 +1216,18 @@ hipError_t run_dequant_matmul(const void* X, int64_t M, int64_t in, int64_t ldx,
   if (xo) {
     // X in packed order into the workspace, then the plain product on it
     _Float16* xp = reinterpret_cast<_Float16*>(wsp);
-    hipLaunchKernelGGL(dq_gather_x_kernel, dim3((unsigned)((in + 255) / 256), (unsigned)(M < 1024 ? M : 1024)),
-                       dim3(256), 0, s, x, M, in, ldx, xo, xp);
+    if (in <= GATHER_MAX_IN) {
+      const int R = gather_rows(in);
+      const size_t lds = (size_t)R * in * sizeof(_Float16);
+      if (lds > 64 * 1024)
+        GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)dq_gather_x_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+      hipLaunchKernelGGL(dq_gather_x_kernel, dim3((unsigned)((M + R - 1) / R)), dim3(256), lds, s,
+                         x, M, in, ldx, xo, R, xp);
+    } else {
+      hipLaunchKernelGGL(dq_gather_x_cols_kernel, dim3((unsigned)((in + 255) / 256),
+                         (unsigned)(M < 1024 ? M : 1024)), dim3(256), 0, s, x, M, in, ldx, xo, xp);
+    }
     GPTQ_HIP_TRY(hipGetLastError());
     x = xp;
     ldx = in;
