@@ -213,8 +213,11 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in,
  * sums when the input range is split over several workgroups (always for
  * M <= 8, e.g. 16 x 1 x 4096 for one token of a 4096 x 4096 layer; for
  * M > 8 when the output tiles alone would not fill the GPU), plus, for
+ * M >= 256 with out a multiple of 4, a table of one int per 32 inputs (the
+ * group of each 32-position chunk, or -1 where it mixes groups), plus, for
  * M > 8 with an x_order, the gathered copy of X (M x in fp16).  0 when
- * neither applies (e.g. M = 8192 on a 4096 x 4096 layer). */
+ * none applies (e.g. M = 64 on a 4096 x 4096 layer needs only partial sums;
+ * M = 8192 on it needs only the 512-byte table). */
 size_t gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t in, int64_t out, int has_order);
 
 /*
