@@ -310,9 +310,9 @@ def summarize_mfma(cfg_name: str, d: str):
              "dispatches' durations under the counters (kernels of the factorization overlap on "
              "three streams).  Active cycles = GRBM_GUI_ACTIVE / 8 XCDs; MFMA util = "
              "SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x 1024 SIMDs); fp16 MFMA work issued = "
-             "SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 (gemm_e2_dma issues two fp16 products per "
-             "algorithmic one, gemm_f32_dma with split operands three; gemm_f32_dma over fewer "
-             "than 512 error columns runs fp32 MFMAs, which this counter leaves out); clock = "
+             "SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 (gemm_eh_dma issues two fp16 products per "
+             "algorithmic one over 512 or more error columns in layers up to 16384 wide, three "
+             "otherwise; gemm_f32_dma with split operands three); clock = "
              "active cycles / time, given for the SYRK only: it runs long and alone on the GPU, "
              "while for short or overlapping dispatches the counting window is wider than the "
              "kernel.", "",
@@ -431,8 +431,7 @@ STAGES = [
     ("a3 factor (Cholesky + inverse, U')", ("cholinv_leaf_kernel", "reverse_inplace_kernel",
                                              "uprime_kernel", "gemm_f32_dma@prepare")),
     ("a4 block sweep", ("sweep16_kernel", "sweep_kernel")),
-    ("a5 lazy trailing update", ("gemm_e2_dma", "uprime_t16_kernel", "row_scale_kernel",
-                                  "gemm_f32_dma@quantize")),
+    ("a5 lazy trailing update", ("gemm_eh_dma", "uprime_t16_kernel", "gemm_f32_dma@quantize")),
     ("a6 pack", ("pack_kernel", "perm_tables_kernel")),
 ]
 
@@ -496,8 +495,8 @@ def stage_roofline(cfg, rows):
         wshown = f"{w:.3g} {unit}"
         # the trailing GEMMs over >= 512 error columns (nearly all the work)
         # multiply the errors as two fp16 parts by U' in fp16 (two fp16 MFMA
-        # products per algorithmic one), above 16384 columns by U' as two
-        # fp16 parts as well (three)
+        # products per algorithmic one), above 16384 columns by U' and its
+        # fp16 remainder (three)
         prods = 3 if n > 16384 else 2
         pipe = f"{prods * ach / (PEAK_FP16_TFLOPS * 1e12):.3f}" if name.startswith("a5") else ""
         lines.append(f"| {name} | {t * 1e3:.3f} | {wshown} | {shown} | {bound} | "

@@ -92,16 +92,17 @@ struct GemmArgs {
   const float* row_scale = nullptr;
 };
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
-// C[M x N] -= E[M x K] V[N x K]^T with E fp32 (leading dimension lde, a
-// multiple of 4, 16-byte aligned), V fp16 (ldv a multiple of 8, 16-byte
-// aligned), K a multiple of 32: E split into two fp16 parts after scaling
-// each row by the power of two 2^(14 - e), m = f 2^e the row's largest
-// emax[k][row] (k in [eb0, eb1), row stride eld), two fp16 products per
-// term, fp32 accumulation, the scale undone in the epilogue.
-hipError_t launch_gemm_e2(int64_t M, int64_t N, int64_t K, const float* E, int64_t lde,
-                          const _Float16* V, int64_t ldv, float* C, int64_t ldc,
-                          const float* emax, int64_t eld, int64_t eb0, int64_t eb1,
-                          hipStream_t s);
+// Error-update GEMM of the column sweep on the errors the sweep stored split:
+//   C[M x N] -= sum over sweep blocks b (kb columns each) of
+//               einv[b][r] * (Ehi + Elo)_b (V + Vl)_b^T
+// E: per 16 columns of a row, 16 fp16 high parts then 16 fp16 remainders of
+// the errors scaled by 1 / einv (row stride lde floats, 16-byte aligned);
+// V, Vl: fp16 [N x K], k-contiguous (ldv a multiple of 8); Vl == nullptr
+// drops the third product (Ehi Vl); einv fp32 [K / kb][eld]; kb 32, 64 or
+// 128 dividing K.
+hipError_t launch_gemm_eh(int64_t M, int64_t N, int64_t K, const float* E, int64_t lde,
+                          const _Float16* V, const _Float16* Vl, int64_t ldv, float* C,
+                          int64_t ldc, const float* einv, int64_t eld, int kb, hipStream_t s);
 
 // Hessian SYRK: H(upper) += 2 X^T X.  ws (optional) enables the stream-K schedule.
 size_t syrk_workspace_bytes(int64_t n);

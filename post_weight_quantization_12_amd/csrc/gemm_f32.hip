@@ -490,165 +490,255 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
 }
 
 // ---------------------------------------------------------------------------
-// Error-update GEMM of the column sweep: C -= E V^T on two fp16 products.
-//   E  fp32 [M x K] (row-major, k-contiguous; each row scaled by a power of
-//      two first, from the sweeps' per-row error maxima over the K range),
-//      split x = hi + lo as split16 does;
-//   V  fp16 [N x K] (k-contiguous: the coefficient matrix stored transposed
-//      and rounded to nearest fp16 once);
-//   C  fp32 [M x N] -= (E_hi V + E_lo V) / scale.
-// 128 x 128 tiles, four 64 x 64 waves, 32 k per stage, three stages of
-// direct-to-LDS loads.  The fp16 rows of V are 64 bytes per stage: chunk c
-// of row r sits at c ^ ((r >> 2) & 3), so a 16-lane pass of 16-byte reads of
-// 16 consecutive rows covers all 64 banks.
-constexpr int E2_BM = 128, E2_BN = 128, E2_NS = 3;  // 72 KiB of LDS: two workgroups per CU
-constexpr int E2_AIPW = E2_BM / 32;      // fp32 A: 4 KiB per wave-wide load round
-constexpr int E2_BIPW = E2_BN / 64;      // fp16 B: 64 rows x 64 bytes per round
-constexpr int E2_AF = E2_BM * DK;        // floats per A stage
-constexpr int E2_BH = E2_BN * DK;        // halves per B stage
+// Error-update GEMM of the column sweep, on errors the sweep stored already
+// split:
+//   C[M x N] -= sum over the K range's sweep blocks b (32 SPB columns each) of
+//               einv[b][r] * (Ehi_b + Elo_b) (Vhi_b + Vlo_b)^T
+//   E   the sweep's errors, each row and block scaled by 1 / einv (a power of
+//       two), in place of the block's fp32 columns: per 16 columns, 16 fp16
+//       high parts then 16 fp16 remainders (64 bytes; row stride lde floats);
+//   V   fp16 [N x K] (k-contiguous: U' transposed, rounded to nearest once);
+//   Vl  fp16 remainders of U' - V (VLO: a third product, Ehi Vl; else unused);
+//   einv fp32 [blocks][eld]: the block's inverse row scales.
+// Every product is exact in the fp32 accumulator of its block; a block's sum
+// is multiplied by its (exact) power of two and added to the tile's total, so
+// rows and blocks of very different magnitude keep their relative precision.
+//
+// 128 x BN tiles (BN = 256: eight waves; 128: four), each wave a 64 x 64
+// block (2 x 2 accumulators plus the total), 32 k per stage, four stages of
+// direct-to-LDS loads in flight behind the one being read.  Every stage
+// buffer is an LDS object of its own and the loop is unrolled over the four,
+// so the compiler tracks each buffer's direct loads separately and waits
+// only for the stage it reads (with one indexed array it waits for every
+// load in flight before each read, and nothing overlaps).  A stage holds the
+// E rows (128 bytes each, 16-byte chunk c of row r at c ^ ((r >> 1) & 7)),
+// the V rows (64 bytes, chunk c at c ^ ((r >> 2) & 3)): a 16-lane pass of
+// 16-byte reads of 16 consecutive rows covers all 64 banks).  The inverse
+// scales of all the call's blocks (at most EH_KB_MAX) are put in LDS before
+// the loop: loads into registers inside it, or direct loads into LDS read
+// back, made the compiler wait for every stage in flight.
+constexpr int EH_BM = 128, EH_NS = 4, EH_KB_MAX = 48;
 
-__global__ void __launch_bounds__(256)
-gemm_e2_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
-            const _Float16* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
-            const float* __restrict__ emax, int64_t eld, int64_t eb0, int64_t eb1) {
-  __shared__ __align__(16) float sa[E2_NS][E2_AF];
-  __shared__ __align__(16) _Float16 sb[E2_NS][E2_BH];
-  __shared__ float rsl[E2_BM];
-  using TA_ = OpTile<E2_BM, true>;
-  static_assert(TA_::IPW == E2_AIPW, "A loads per wave");
+template <bool VLO, int BN>
+struct EhStage {
+  static constexpr int NW = 2 * BN / 64;           // waves (2 x BN/64 of 64 x 64): 2 BN threads
+  static constexpr int A = EH_BM * DK * 4;         // E image (hi + lo): 16 KiB
+  static constexpr int B = BN * DK * 2;            // V image
+  static constexpr int BYTES = A + (VLO ? 2 : 1) * B;
+  static constexpr int AIPW = A / 1024 / NW;       // 16-byte direct loads per wave
+  static constexpr int BIPW = B / 1024 / NW;
+  static constexpr int IPW = AIPW + (VLO ? 2 : 1) * BIPW;
+};
 
+// 16 bytes from LDS through an LDS-typed pointer (the waitcnt pass then keeps
+// its reads apart from the direct loads into the other stage buffers).
+__device__ inline half8_t lds_read_h8(const char* p) {
+  return *(const __attribute__((address_space(3))) half8_t*)(
+      (const __attribute__((address_space(3))) char*)(p));
+}
+
+__device__ inline f32x4_t lds_read_f4(const char* base, int off) {
+  return *(const __attribute__((address_space(3))) f32x4_t*)(
+      (const __attribute__((address_space(3))) char*)(base) + off);
+}
+
+template <bool VLO, int SPB, int BN>
+__global__ void __launch_bounds__(2 * BN)
+gemm_eh_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+            const _Float16* __restrict__ B, const _Float16* __restrict__ Bl, int64_t ldb,
+            float* __restrict__ C, int64_t ldc, const float* __restrict__ einv, int64_t eld) {
+  using S = EhStage<VLO, BN>;
+  static_assert(4 % SPB == 0 && EH_NS == 4, "a block of stages ends on a stage buffer");
+  __shared__ __align__(16) char st0[S::BYTES];
+  __shared__ __align__(16) char st1[S::BYTES];
+  __shared__ __align__(16) char st2[S::BYTES];
+  __shared__ __align__(16) char st3[S::BYTES];
+  __shared__ __align__(16) float scl[EH_KB_MAX * EH_BM];  // inverse scales, [block][tile row]
+  constexpr int OB = S::A, OBL = S::A + S::B;
+
+  // Tile order: each XCD (block b -> XCD b % 8) takes a contiguous run of a
+  // grouped order (bands of 8 row tiles, column by column, the band's rows
+  // inside a column), so the tiles an XCD runs together share A rows and V
+  // columns in its L2.
   const int nb = gridDim.x, b = blockIdx.x;
-  const int tiles_n = (int)((N + E2_BN - 1) / E2_BN);
-  const int t = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
-  const int ti = t / tiles_n, tj = t % tiles_n;
-  const int64_t i0 = (int64_t)ti * E2_BM, j0 = (int64_t)tj * E2_BN;
+  const int tiles_n = (int)((N + BN - 1) / BN), tiles_m = nb / tiles_n;
+  int ti, tj;
+  {
+    const int x = b % 8, r = b / 8, q = nb / 8, rem = nb % 8;
+    const int t = x * q + (x < rem ? x : rem) + r;
+    const int band = t / (8 * tiles_n), w = t % (8 * tiles_n);
+    const int rows = tiles_m - 8 * band < 8 ? tiles_m - 8 * band : 8;
+    tj = w / rows;
+    ti = 8 * band + w % rows;
+  }
+  const int64_t i0 = (int64_t)ti * EH_BM, j0 = (int64_t)tj * BN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1, h = lane >> 5;
 
-  // Row scales of the tile: 2^(14 - e) for the rows' largest error m = f 2^e
-  // (f in [0.5, 1)) over the K range's blocks, so every scaled error is below
-  // 2^14.  Two threads per row, each every second block, eight loads in
-  // flight (a K range holds up to in / block blocks).
-  {
-    const int rr = tid & (E2_BM - 1), half = tid >> 7;
-    const int64_t r = i0 + rr;
-    float m = 0.0f;
-    if (r < M) {
-      int64_t k = eb0 + half;
-      for (; k + 14 < eb1; k += 16) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = emax[(k + 2 * u) * eld + r];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) m = fmaxf(m, v[u]);
-      }
-      for (; k < eb1; k += 2) m = fmaxf(m, emax[k * eld + r]);
-    }
-    if (half) rsl[rr] = m;
-    __syncthreads();
-    if (!half) {
-      m = fmaxf(m, rsl[rr]);
-      int e = 0;
-      (void)frexpf(m, &e);
-      rsl[rr] = (m > 0.0f && m < INFINITY) ? ldexpf(1.0f, 14 - e) : 1.0f;
-    }
-  }
-
-  const float* abase = A + i0 * lda;
+  const char* abase = reinterpret_cast<const char*>(A + i0 * lda);
   const int64_t aext = ((M - i0 - 1) * lda + K) * 4;
-  const _Float16* bbase = B + j0 * ldb;
+  const char* bbase = reinterpret_cast<const char*>(B + j0 * ldb);
+  const char* blbase = VLO ? reinterpret_cast<const char*>(Bl + j0 * ldb) : nullptr;
   const int64_t bext = ((N - j0 - 1) * ldb + K) * 2;
   const int nk = (int)(K / DK);
-  uint32_t va[E2_AIPW], vb[E2_BIPW];
+  uint32_t va[S::AIPW], vb[S::BIPW];
 #pragma unroll
-  for (int q = 0; q < E2_AIPW; ++q) va[q] = TA_::voff(wave, q, lane, lda);
+  for (int q = 0; q < S::AIPW; ++q) {
+    const int slot = (wave * S::AIPW + q) * 64 + lane;
+    const int row = slot >> 3, lch = (slot & 7) ^ ((row >> 1) & 7);
+    va[q] = (uint32_t)(((int64_t)row * lda + lch * 4) * 4);
+  }
 #pragma unroll
-  for (int q = 0; q < E2_BIPW; ++q) {
-    const int slot = (wave * E2_BIPW + q) * 64 + lane;
+  for (int q = 0; q < S::BIPW; ++q) {
+    const int slot = (wave * S::BIPW + q) * 64 + lane;
     const int row = slot >> 2, lch = (slot & 3) ^ ((row >> 2) & 3);
     vb[q] = (uint32_t)(((int64_t)row * ldb + lch * 8) * 2);
   }
-  auto issue = [&](int st, int buf) __device__ __attribute__((always_inline)) {
+  // (the direct loads go through issue_stage: a load builtin written in
+  // the lambda itself keeps the host compiler from emitting the kernel)
+  auto issue = [&](int st, char* stage) __device__ __attribute__((always_inline)) {
     const bool live = st < nk;
-    issue_stage<E2_AIPW>(live ? (const char*)abase + (int64_t)st * DK * 4 : (const char*)A,
+    issue_stage<S::AIPW>(live ? abase + (int64_t)st * DK * 4 : (const char*)A,
                          live ? aext - (int64_t)st * DK * 4 : 0, va,
-                         &sa[buf][0] + wave * E2_AIPW * 256);
-    __amdgpu_buffer_rsrc_t rs = rsrc(live ? (const char*)bbase + (int64_t)st * DK * 2 : (const char*)B,
-                                     live ? bext - (int64_t)st * DK * 2 : 0);
-#pragma unroll
-    for (int q = 0; q < E2_BIPW; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, GPTQ_LDS(&sb[buf][0] + (wave * E2_BIPW + q) * 512), 16, vb[q], 0, 0, 0);
+                         reinterpret_cast<float*>(stage + wave * S::AIPW * 1024));
+    issue_stage<S::BIPW>(live ? bbase + (int64_t)st * DK * 2 : (const char*)B,
+                         live ? bext - (int64_t)st * DK * 2 : 0, vb,
+                         reinterpret_cast<float*>(stage + OB + wave * S::BIPW * 1024));
+    if constexpr (VLO)
+      issue_stage<S::BIPW>(live ? blbase + (int64_t)st * DK * 2 : (const char*)Bl,
+                           live ? bext - (int64_t)st * DK * 2 : 0, vb,
+                           reinterpret_cast<float*>(stage + OBL + wave * S::BIPW * 1024));
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][2], tot[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
+      for (int v = 0; v < 16; ++v) {
+        acc[a][c][v] = 0.0f;
+        tot[a][c][v] = 0.0f;
+      }
 
+  // MFMA k-step q takes k = 16 q + 8 h + e (e < 8): E chunks 4q + h (high
+  // parts) and 4q + 2 + h (remainders), V chunk 2q + h.  first: the stage
+  // opens a block (its sums start from zero); last: it closes one (tot +=
+  // einv * acc).
+  // This lane's LDS byte offsets inside a stage buffer, computed once (a
+  // single offset from the buffer keeps every read attributable to its LDS
+  // object, which is what lets the compiler wait only for that stage).
+  int offah[2][2], offal[2][2], offb[2][2];
 #pragma unroll
-  for (int st = 0; st + 1 < E2_NS; ++st) issue(st, st);
-  __syncthreads();  // row scales
-  float rsa[2];
+  for (int a = 0; a < 2; ++a) {
+    const int row = wm * 64 + a * 32 + (lane & 31), sw = (row >> 1) & 7;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) rsa[a] = rsl[wm * 64 + a * 32 + (lane & 31)];
-
-  auto compute = [&](int buf) __device__ __attribute__((always_inline)) {
-    float av[2][16];
+    for (int q = 0; q < 2; ++q) {
+      offah[a][q] = row * 128 + (((4 * q + h) ^ sw) * 16);
+      offal[a][q] = row * 128 + (((4 * q + 2 + h) ^ sw) * 16);
+    }
+  }
 #pragma unroll
-    for (int a = 0; a < 2; ++a) TA_::frag(&sa[buf][0], wm * 64 + a * 32 + (lane & 31), h, av[a]);
-    half8_t bq[2][2];
+  for (int c = 0; c < 2; ++c) {
+    const int row = wn * 64 + c * 32 + (lane & 31), sw = (row >> 2) & 3;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int row = wn * 64 + c * 32 + (lane & 31);
+    for (int q = 0; q < 2; ++q) offb[c][q] = OB + row * 64 + (((2 * q + h) ^ sw) * 16);
+  }
+  auto compute = [&](const char* stage, int kb, bool first, bool last) __device__ __attribute__((always_inline)) {
+    half8_t ah[2][2], al[2][2], bh[2][2], bl[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int ph = (2 * h + q) ^ ((row >> 2) & 3);
-        bq[c][q] = *reinterpret_cast<const half8_t*>(&sb[buf][row * DK + ph * 8]);
+        ah[a][q] = lds_read_h8(stage + offah[a][q]);
+        al[a][q] = lds_read_h8(stage + offal[a][q]);
       }
-    }
-    half8_t ah[2][2], al[2][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) av[a][u] *= rsa[a];
-      split16(av[a], ah[a], al[a]);
-    }
-    // MFMA k-step q takes this lane's k = 16 h + 8 q + e (e < 8) of A and B
+      for (int q = 0; q < 2; ++q) {
+        bh[c][q] = lds_read_h8(stage + offb[c][q]);
+        if constexpr (VLO) bl[c][q] = lds_read_h8(stage + (offb[c][q] + (OBL - OB)));
+      }
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[a][q], bq[c][q], acc[a][c], 0, 0, 0);
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[a][q], bq[c][q], acc[a][c], 0, 0, 0);
+          f32x16_t x = acc[a][c];
+          if (first && q == 0) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x[v] = 0.0f;
+          }
+          if constexpr (VLO) x = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[a][q], bl[c][q], x, 0, 0, 0);
+          x = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[a][q], bh[c][q], x, 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[a][q], bh[c][q], x, 0, 0, 0);
         }
+    if (last) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // one opaque offset per read: constant parts split off into
+          // further address steps hide the LDS object from the waitcnt pass
+          int o = (kb * EH_BM + wm * 64 + a * 32 + g * 8 + h * 4) * 4;
+          asm volatile("" : "+v"(o));
+          const f32x4_t s4 = lds_read_f4(reinterpret_cast<const char*>(scl), o);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            tot[a][c][4 * g + 0] = fmaf(s4[0], acc[a][c][4 * g + 0], tot[a][c][4 * g + 0]);
+            tot[a][c][4 * g + 1] = fmaf(s4[1], acc[a][c][4 * g + 1], tot[a][c][4 * g + 1]);
+            tot[a][c][4 * g + 2] = fmaf(s4[2], acc[a][c][4 * g + 2], tot[a][c][4 * g + 2]);
+            tot[a][c][4 * g + 3] = fmaf(s4[3], acc[a][c][4 * g + 3], tot[a][c][4 * g + 3]);
+          }
+        }
+      }
+    }
   };
-  constexpr int IPW = E2_AIPW + E2_BIPW;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt % E2_NS;
-    wait_vmcnt<(E2_NS - 2) * IPW>();
+  // Stage kt (buffer kt % 4): own loads of kt landed, barrier (everyone's
+  // landed, nobody reads kt - 1 any more), refill kt - 1's buffer with
+  // kt + 3, compute kt.  Stages past K read zeros (zero-size descriptor):
+  // whole rounds of four stages, no data-dependent branches.
+  auto step = [&](int kt, const char* cur, char* prev, int u) __device__ __attribute__((always_inline)) {
+    const int kb = kt / SPB;
+    wait_vmcnt<(EH_NS - 2) * S::IPW>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
-    issue(kt + E2_NS - 1, (kt + E2_NS - 1) % E2_NS);
-    compute(buf);
+    issue(kt + EH_NS - 1, prev);
+    compute(cur, kb, u % SPB == 0, u % SPB == SPB - 1);
+  };
+  // Every block's inverse scales of the tile's rows (rows past M: 0) are
+  // loaded before the first stages (so waiting for them does not wait for
+  // the stages) and stored to LDS after; the first step's barrier makes
+  // them visible.
+  constexpr int SPT = EH_KB_MAX * EH_BM / (S::NW * 64);  // scales per thread, at most
+  float sv[SPT];
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const int e = tid + u * S::NW * 64;
+    const int64_t r = i0 + (e % EH_BM);
+    sv[u] = (e < (nk / SPB) * EH_BM && r < M) ? einv[(int64_t)(e / EH_BM) * eld + r] : 0.0f;
+  }
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) scl[tid + u * S::NW * 64] = sv[u];
+  for (int kt = 0; kt < nk; kt += 4) {
+    step(kt + 0, st0, st3, 0);
+    step(kt + 1, st1, st0, 1);
+    step(kt + 2, st2, st1, 2);
+    step(kt + 3, st3, st2, 3);
   }
   wait_vmcnt<0>();
 
-  // C += -acc / scale, through a buffer descriptor (outside rows / columns dropped)
+  // C -= tot, through a buffer descriptor (outside rows / columns dropped)
   const int64_t cext = ((M - i0 - 1) * ldc + (N - j0)) * 4;
   __amdgpu_buffer_rsrc_t rc = rsrc(C + i0 * ldc + j0, cext);
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    float ralpha[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      ralpha[v] = -1.0f / rsl[wm * 64 + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int jl = wn * 64 + c * 32 + (lane & 31);
@@ -656,15 +746,15 @@ gemm_e2_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_
       float cv[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int il = wm * 64 + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int il = wm * 64 + a * 32 + (v >> 2) * 8 + h * 4 + (v & 3);
         const bool in = i0 + il < M && j0 + jl < N;
         off[v] = in ? (uint32_t)(((int64_t)il * ldc + jl) * 4) : 0x80000000u;
         cv[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, (int)off[v], 0, 0));
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(ralpha[v], acc[a][c][v], cv[v])),
-                                              rc, (int)off[v], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cv[v] - tot[a][c][v]), rc,
+                                              (int)off[v], 0, 0);
     }
   }
 }
@@ -688,17 +778,44 @@ hipError_t launch_dma_t(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm_e2(int64_t M, int64_t N, int64_t K, const float* E, int64_t lde,
-                          const _Float16* V, int64_t ldv, float* C, int64_t ldc,
-                          const float* emax, int64_t eld, int64_t eb0, int64_t eb1,
-                          hipStream_t s) {
+hipError_t launch_gemm_eh(int64_t M, int64_t N, int64_t K, const float* E, int64_t lde,
+                          const _Float16* V, const _Float16* Vl, int64_t ldv, float* C,
+                          int64_t ldc, const float* einv, int64_t eld, int kb, hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
-  if (K % DK != 0 || lde % 4 != 0 || ldv % 8 != 0 || !al16(E) ||
-      (reinterpret_cast<uintptr_t>(V) & 15) != 0)
+  if (K % kb != 0 || (kb != 32 && kb != 64 && kb != 128) || lde % 4 != 0 || ldv % 8 != 0 ||
+      !al16(E) || (reinterpret_cast<uintptr_t>(V) & 15) != 0 ||
+      (Vl && (reinterpret_cast<uintptr_t>(Vl) & 15) != 0) || (reinterpret_cast<uintptr_t>(einv) & 3))
     return hipErrorInvalidValue;
-  const int64_t tiles = ((M + E2_BM - 1) / E2_BM) * ((N + E2_BN - 1) / E2_BN);
-  hipLaunchKernelGGL(gemm_e2_dma, dim3((unsigned)tiles), dim3(256), 0, s, M, N, K, E, lde, V, ldv,
-                     C, ldc, emax, eld, eb0, eb1);
+  if (K > (int64_t)EH_KB_MAX * kb) {  // sequential launches of at most EH_KB_MAX blocks each
+    for (int64_t k0 = 0; k0 < K; k0 += (int64_t)EH_KB_MAX * kb) {
+      const int64_t kc = K - k0 < (int64_t)EH_KB_MAX * kb ? K - k0 : (int64_t)EH_KB_MAX * kb;
+      GPTQ_HIP_TRY(launch_gemm_eh(M, N, kc, E + k0, lde, V + k0, Vl ? Vl + k0 : nullptr, ldv, C,
+                                  ldc, einv + (k0 / kb) * eld, eld, kb, s));
+    }
+    return hipSuccess;
+  }
+  const int64_t tm = (M + EH_BM - 1) / EH_BM;
+  // 128 x 256 tiles where they fill the CUs for two rounds or more (two-product
+  // 128-column blocks: the per-stage block sums of smaller blocks do not fit
+  // the registers of eight waves), else 128 x 128
+  const bool wide = !Vl && kb == 128 && tm * ((N + 255) / 256) >= 512;
+  const int bn = wide ? 256 : 128;
+  const dim3 grid((unsigned)(tm * ((N + bn - 1) / bn)));
+#define GPTQ_EH(VL, SPB, BN)                                                                    \
+  hipLaunchKernelGGL((gemm_eh_dma<VL, SPB, BN>), grid, dim3(EhStage<VL, BN>::NW * 64), 0, s, M, \
+                     N, K, E, lde, V, Vl, ldv, C, ldc, einv, eld)
+  if (Vl) {
+    if (kb == 32) GPTQ_EH(true, 1, 128);
+    else if (kb == 64) GPTQ_EH(true, 2, 128);
+    else GPTQ_EH(true, 4, 128);
+  } else if (wide) {
+    GPTQ_EH(false, 4, 256);
+  } else {
+    if (kb == 32) GPTQ_EH(false, 1, 128);
+    else if (kb == 64) GPTQ_EH(false, 2, 128);
+    else GPTQ_EH(false, 4, 128);
+  }
+#undef GPTQ_EH
   return hipGetLastError();
 }
 

@@ -69,6 +69,42 @@ __device__ inline void grid_params(float lo, float hi, int bits, int sym, float&
   z = (sym || flat) ? (float)(1 << (bits - 1)) : rintf(-lo / s);
 }
 
+// Row scale of a block's errors for the trailing GEMMs: 2^(14 - e) for the
+// row's largest |error| m = f 2^e (f in [0.5, 1)), so every scaled error is
+// below 2^14 (the exponent capped at 126); 1 for an all-zero or non-finite
+// row.
+__device__ inline float error_row_scale(float m) {
+  if (!(m > 0.0f && m < INFINITY)) return 1.0f;
+  int e = 0;
+  (void)frexpf(m, &e);
+  return ldexpf(1.0f, min(14 - e, 126));
+}
+
+// Eight consecutive errors of a row (src, 16-byte aligned), scaled by rsc and
+// split for the trailing GEMMs: x = hi + lo with hi = x rounded toward zero
+// to fp16 and lo = x - hi (exact in fp32) rounded toward zero to fp16, so
+// |x - hi - lo| <= 2^-21 |x| in the fp16 normal range.  grp is the row's
+// 16-column group (64 bytes: 16 high parts, then 16 remainders); hh picks the
+// group's first or second eight columns.
+__device__ inline void store_split8(const float* src, float rsc, float* grp, int hh) {
+  const float4 a = *reinterpret_cast<const float4*>(src);
+  const float4 b = *reinterpret_cast<const float4*>(src + 4);
+  const float x[8] = {a.x * rsc, a.y * rsc, a.z * rsc, a.w * rsc,
+                      b.x * rsc, b.y * rsc, b.z * rsc, b.w * rsc};
+  half8_t hi, lo;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const auto hp = __builtin_amdgcn_cvt_pkrtz(x[e], x[e + 1]);
+    const auto lp = __builtin_amdgcn_cvt_pkrtz(x[e] - (float)hp[0], x[e + 1] - (float)hp[1]);
+    hi[e] = hp[0];
+    hi[e + 1] = hp[1];
+    lo[e] = lp[0];
+    lo[e + 1] = lp[1];
+  }
+  *reinterpret_cast<half8_t*>(grp + 4 * hh) = hi;
+  *reinterpret_cast<half8_t*>(grp + 8 + 4 * hh) = lo;
+}
+
 template <typename T>
 __device__ inline float to_f32(T v);
 template <>
@@ -160,11 +196,14 @@ uprime_kernel(const float* __restrict__ U, int64_t n, float* __restrict__ Up) {
   }
 }
 
-// Vt[c][r] = fp16(Up[r][c]) (round to nearest) for the strictly upper part
-// r < c: U' transposed for the error-update GEMMs, which read it
-// k-contiguous.  64 x 64 tiles through LDS; tiles below the diagonal exit.
+// Vt[c][r] = fp16(Up[r][c]) (round to nearest) and Vl[c][r] = the remainder
+// Up[r][c] - Vt[c][r] (exact in fp32) rounded toward zero to fp16, for the
+// strictly upper part r < c: U' transposed for the error-update GEMMs, which
+// read it k-contiguous.  64 x 64 tiles through LDS; tiles below the diagonal
+// exit.
 __global__ void __launch_bounds__(256)
-uprime_t16_kernel(const float* __restrict__ Up, int64_t n, _Float16* __restrict__ Vt) {
+uprime_t16_kernel(const float* __restrict__ Up, int64_t n, _Float16* __restrict__ Vt,
+                  _Float16* __restrict__ Vl) {
   __shared__ float tile[64][65];
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
   if (r0 > c0 + 63) return;
@@ -176,7 +215,12 @@ uprime_t16_kernel(const float* __restrict__ Up, int64_t n, _Float16* __restrict_
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
     const int64_t c = c0 + i, r = r0 + tx;
-    if (c < n && r < n && r < c) Vt[c * n + r] = (_Float16)tile[tx][i];
+    if (c < n && r < n && r < c) {
+      const float u = tile[tx][i];
+      const _Float16 hi = (_Float16)u;
+      Vt[c * n + r] = hi;
+      Vl[c * n + r] = __builtin_amdgcn_cvt_pkrtz(u - (float)hi, 0.0f)[0];
+    }
   }
 }
 
@@ -245,7 +289,7 @@ __global__ void __launch_bounds__(SW_THREADS)
 sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, int64_t in,
              int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
              int32_t* __restrict__ zeros, uint8_t* __restrict__ codes,
-             float* __restrict__ emax) {
+             float* __restrict__ einv) {
   using SM = SweepSmem<B>;
   constexpr int NR = SM::NR, PITCH = SM::PITCH, EP = SM::EP;
   extern __shared__ __align__(16) float smem[];
@@ -350,22 +394,21 @@ sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, 
   }
   __syncthreads();
 
-  // Largest |error| of each row in this block (sizes the split products of
-  // the trailing GEMMs).
+  // The block's errors for the trailing GEMMs, in place of its columns of
+  // Wp: each row scaled by error_row_scale of its largest |error| (einv
+  // keeps the inverse) and split by store_split8; lane q of a row's quad
+  // writes the eight-column pieces q, q + 4, ...
   {
     float m = 0.0f;
     for (int c = q; c < width; c += 4) m = fmaxf(m, fabsf(Es[rl * EP + c]));
     m = fmaxf(m, dpp_xor1(m));
     m = fmaxf(m, dpp_xor2(m));
-    if (live && q == 0) emax[(c0 / B) * out + row] = m;
-  }
-  // Errors (read by the trailing GEMMs) and codes, written out row-contiguous.
-  const int wq = width / 4;
-  for (int e = tid; e < SW_ROWS * wq; e += SW_THREADS) {
-    const int r = e / wq, c = (e % wq) * 4;
-    if (row0 + r < out)
-      *reinterpret_cast<float4*>(Wp + (row0 + r) * in + c0 + c) =
-          *reinterpret_cast<const float4*>(Es + r * EP + c);
+    const float rsc = error_row_scale(m);
+    if (live) {
+      if (q == 0) einv[(c0 / B) * out + row] = 1.0f / rsc;
+      for (int p = q; 8 * p < width; p += 4)
+        store_split8(Es + rl * EP + 8 * p, rsc, Wp + row * in + c0 + 16 * (p >> 1), p & 1);
+    }
   }
   const int w16 = width / 16;
   for (int e = tid; e < SW_ROWS * w16; e += SW_THREADS) {
@@ -498,7 +541,7 @@ __global__ void __launch_bounds__(S16_THREADS)
 sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, int64_t in,
                int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
                int32_t* __restrict__ zeros, uint8_t* __restrict__ codes,
-               float* __restrict__ emax) {
+               float* __restrict__ einv) {
   using SM = Sweep16Smem<B>;
   constexpr int NR = SM::NR, PITCH = SM::PITCH, EP = SM::EP;
   static_assert(GS % 16 == 0, "group size a multiple of 16 (0: one group per row)");
@@ -668,21 +711,20 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out
   }
   __syncthreads();
 
-  // Largest |error| of each row in this block (sizes the split products of
-  // the trailing GEMMs).
+  // The block's errors for the trailing GEMMs, in place of its columns of
+  // Wp: each row scaled by error_row_scale of its largest |error| (einv
+  // keeps the inverse) and split by store_split8; lane q of a row writes
+  // the eight-column piece q.
   {
     float m = 0.0f;
     for (int c = q; c < width; c += 16) m = fmaxf(m, fabsf(Es[rl * EP + c]));
     m = row_max16(m);
-    if (live && q == 0) emax[(c0 / B) * out + row] = m;
-  }
-  // Errors (read by the trailing GEMMs) and codes, written out row-contiguous.
-  const int wq = width / 4;
-  for (int e = tid; e < S16_ROWS * wq; e += S16_THREADS) {
-    const int r = e / wq, c = (e % wq) * 4;
-    if (row0 + r < out)
-      *reinterpret_cast<float4*>(Wp + (row0 + r) * in + c0 + c) =
-          *reinterpret_cast<const float4*>(Es + r * EP + c);
+    const float rsc = error_row_scale(m);
+    if (live) {
+      if (q == 0) einv[(c0 / B) * out + row] = 1.0f / rsc;
+      if (8 * q < width)
+        store_split8(Es + rl * EP + 8 * q, rsc, Wp + row * in + c0 + 16 * (q >> 1), q & 1);
+    }
   }
   const int w16 = width / 16;
   for (int e = tid; e < S16_ROWS * w16; e += S16_THREADS) {
@@ -696,38 +738,38 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out
 template <int B, int GS>
 hipError_t launch_sweep16(float* Wp, const float* Up, int64_t out, int64_t in, int64_t c0,
                           int width, int bits, int sym, float* scales, int32_t* zeros,
-                          uint8_t* codes, float* emax, hipStream_t s) {
+                          uint8_t* codes, float* einv, hipStream_t s) {
   auto k = sweep16_kernel<B, GS>;
   const size_t lds = Sweep16Smem<B>::BYTES;
   GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)lds));
   hipLaunchKernelGGL(k, dim3((unsigned)((out + S16_ROWS - 1) / S16_ROWS)), dim3(S16_THREADS), lds,
-                     s, Wp, Up, out, in, c0, width, bits, sym, scales, zeros, codes, emax);
+                     s, Wp, Up, out, in, c0, width, bits, sym, scales, zeros, codes, einv);
   return hipGetLastError();
 }
 
 template <int B>
 hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t in, int64_t c0,
                         int width, int bits, int sym, float* scales, int32_t* zeros,
-                        uint8_t* codes, float* emax, hipStream_t s) {
+                        uint8_t* codes, float* einv, hipStream_t s) {
   if (gs > B) return hipErrorInvalidValue;
   // 16 lanes per row where the group size allows it.
   switch (gs > 0 ? gs : 0) {
     case 0: return launch_sweep16<B, 0>(Wp, Up, out, in, c0, width, bits, sym, scales, zeros,
-                                        codes, emax, s);
+                                        codes, einv, s);
     case 16: return launch_sweep16<B, 16>(Wp, Up, out, in, c0, width, bits, sym, scales, zeros,
-                                          codes, emax, s);
+                                          codes, einv, s);
     case 32: return launch_sweep16<B, 32>(Wp, Up, out, in, c0, width, bits, sym, scales, zeros,
-                                          codes, emax, s);
+                                          codes, einv, s);
     case 64:
       if constexpr (B >= 64)
         return launch_sweep16<B, (B >= 64 ? 64 : 16)>(Wp, Up, out, in, c0, width, bits, sym,
-                                                       scales, zeros, codes, emax, s);
+                                                       scales, zeros, codes, einv, s);
       break;
     case 128:
       if constexpr (B >= 128)
         return launch_sweep16<B, (B >= 128 ? 128 : 16)>(Wp, Up, out, in, c0, width, bits, sym,
-                                                         scales, zeros, codes, emax, s);
+                                                         scales, zeros, codes, einv, s);
       break;
     default:
       break;
@@ -740,7 +782,7 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
     GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,                                           \
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));   \
     hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,  \
-                       zeros, codes, emax);                                                    \
+                       zeros, codes, einv);                                                    \
     break;                                                                                     \
   }
   switch (gs > 0 ? gs : 0) {
@@ -755,7 +797,7 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
         GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
         hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,
-                           zeros, codes, emax);
+                           zeros, codes, einv);
       }
       break;
     case 128:
@@ -764,7 +806,7 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
         GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
         hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,
-                           zeros, codes, emax);
+                           zeros, codes, einv);
       }
       break;
     default:
@@ -774,31 +816,17 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
   return hipGetLastError();
 }
 
-// rs[r] = 2^(14 - e) with m = max over blocks [b0, b1) of emax = f 2^e
-// (f in [0.5, 1)), so every scaled error of the row is below 2^14 in
-// magnitude; 1 for an all-zero (or non-finite) row.
-__global__ void row_scale_kernel(const float* __restrict__ emax, int64_t out, int64_t b0,
-                                 int64_t b1, float* __restrict__ rs) {
-  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (r >= out) return;
-  float m = 0.0f;
-  for (int64_t k = b0; k < b1; ++k) m = fmaxf(m, emax[k * out + r]);
-  int e = 0;
-  (void)frexpf(m, &e);
-  rs[r] = (m > 0.0f && m < INFINITY) ? ldexpf(1.0f, 14 - e) : 1.0f;
-}
-
 struct QCtx {
   float* Wp;
   const float* Up;
-  const _Float16* Vt;  // U' transposed, fp16 (two-product GEMMs), or null
+  const _Float16* Vt;  // U' transposed, rounded to fp16
+  const _Float16* Vl;  // remainders U' - Vt, rounded toward zero to fp16
   int64_t out, in;
   int bits, gs, sym, block;
   float* scales;
   int32_t* zeros;
   uint8_t* codes;
-  float* emax;  // [in / block][out] largest |error| per row and block
-  float* rs;    // [out] row scales of the current three-product GEMM, or null
+  float* einv;  // [ceil(in / block)][out] inverse row scales of the stored errors
   hipStream_t s;
 };
 
@@ -806,22 +834,22 @@ hipError_t sweep_block(QCtx& c, int64_t a, int64_t b) {
   const int width = (int)(b - a);
   switch (c.block) {
     case 32: return launch_sweep<32>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
-                                     c.scales, c.zeros, c.codes, c.emax, c.s);
+                                     c.scales, c.zeros, c.codes, c.einv, c.s);
     case 64: return launch_sweep<64>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
-                                     c.scales, c.zeros, c.codes, c.emax, c.s);
+                                     c.scales, c.zeros, c.codes, c.einv, c.s);
     default: return launch_sweep<128>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
-                                      c.scales, c.zeros, c.codes, c.emax, c.s);
+                                      c.scales, c.zeros, c.codes, c.einv, c.s);
   }
 }
 
 // Columns [a, b): sweep the left half, carry its updates to the right half
-// with one GEMM, then the right half.  GEMMs over 512 or more columns of
-// errors take the errors as two fp16 parts, each row scaled by a power of two
-// (from the sweeps' per-row maxima) so that it spans the fp16 range; smaller
-// ones run in fp32.  Up to TWO_PRODUCT_MAX_IN columns U' enters rounded once
-// to fp16 (two products per term, launch_gemm_e2 on U' stored transposed);
-// above it U' is split into two fp16 parts as well (three products,
-// launch_gemm_f32 with split16).  The rounding of U' moves a pre-rounding
+// with one GEMM, then the right half.  The GEMMs read the errors the sweeps
+// stored split into two fp16 parts (per row and block scaled by a power of
+// two) and multiply them by U' rounded once to fp16 (two products per term),
+// plus its fp16 remainder (a third product) where the rounding of U' would
+// move pre-rounding values too far: for GEMMs over fewer than SPLIT_MIN_K
+// error columns (the pairs of nearby columns, cheap in flops), and in layers
+// wider than TWO_PRODUCT_MAX_IN.  The rounding of U' moves a pre-rounding
 // value by a sum over every earlier column, which grows with the layer width:
 // largest shifts measured in a CPU emulation of the two-product form were
 // 3.5e-4 code units at 4096 columns, 4.2e-4 at 11008 and 1.1e-3 at 28672,
@@ -834,21 +862,10 @@ hipError_t process(QCtx& c, int64_t a, int64_t b) {
   const int64_t nblk = (b - a + B - 1) / B;
   const int64_t m = a + B * ((nblk + 1) / 2);
   GPTQ_HIP_TRY(process(c, a, m));
-  if (m - a >= SPLIT_MIN_K && c.Vt) {
-    GPTQ_HIP_TRY(launch_gemm_e2(c.out, b - m, m - a, c.Wp + a, c.in, c.Vt + m * c.in + a, c.in,
-                                c.Wp + m, c.in, c.emax, c.out, a / B, m / B, c.s));
-  } else {
-    GemmArgs g{c.out, b - m, m - a, c.Wp + a, c.in, false, c.Up + a * c.in + m, c.in, false,
-               c.Wp + m, c.in, -1.0f, 1.0f, KR_FULL, false};
-    if (m - a >= SPLIT_MIN_K) {
-      hipLaunchKernelGGL(row_scale_kernel, dim3((unsigned)((c.out + 255) / 256)), dim3(256), 0,
-                         c.s, c.emax, c.out, a / B, m / B, c.rs);
-      GPTQ_HIP_TRY(hipGetLastError());
-      g.split16 = true;
-      g.row_scale = c.rs;
-    }
-    GPTQ_HIP_TRY(launch_gemm_f32(g, c.s));
-  }
+  const bool three = m - a < SPLIT_MIN_K || c.in > TWO_PRODUCT_MAX_IN;
+  GPTQ_HIP_TRY(launch_gemm_eh(c.out, b - m, m - a, c.Wp + a, c.in, c.Vt + m * c.in + a,
+                              three ? c.Vl + m * c.in + a : nullptr, c.in, c.Wp + m, c.in,
+                              c.einv + (a / B) * c.out, c.out, (int)B, c.s));
   return process(c, m, b);
 }
 
@@ -856,10 +873,10 @@ struct QLayout {
   float* Wp;
   float* Up;
   _Float16* Vt;
-  float* rs;
+  _Float16* Vl;
   uint8_t* codes;
   int32_t* pinv;
-  float* emax;
+  float* einv;
   size_t bytes;
 };
 
@@ -868,14 +885,13 @@ QLayout carve(void* ws, int64_t out, int64_t in, int block) {
   QLayout l;
   l.Wp = c.take<float>((size_t)out * in);
   l.Up = c.take<float>((size_t)in * in);
-  // the GEMMs with K >= SPLIT_MIN_K (only for in > 2 SPLIT_MIN_K - block)
-  // read Vt up to TWO_PRODUCT_MAX_IN columns and rs above it
-  const bool split = in > SPLIT_MIN_K;
-  l.Vt = split && in <= TWO_PRODUCT_MAX_IN ? c.take<_Float16>((size_t)in * in) : nullptr;
-  l.rs = split && in > TWO_PRODUCT_MAX_IN ? c.take<float>((size_t)out) : nullptr;
+  // the trailing GEMMs (only when the layer is wider than one block)
+  const bool gemms = in > block;
+  l.Vt = gemms ? c.take<_Float16>((size_t)in * in) : nullptr;
+  l.Vl = gemms ? c.take<_Float16>((size_t)in * in) : nullptr;
   l.codes = c.take<uint8_t>((size_t)out * in);
   l.pinv = c.take<int32_t>((size_t)in);
-  l.emax = c.take<float>((size_t)out * (size_t)((in + block - 1) / block));
+  l.einv = c.take<float>((size_t)out * (size_t)((in + block - 1) / block));
   l.bytes = c.used;
   return l;
 }
@@ -917,7 +933,7 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
   GPTQ_HIP_TRY(hipGetLastError());
   if (l.Vt) {
     const unsigned nt = (unsigned)((in + 63) / 64);
-    hipLaunchKernelGGL(uprime_t16_kernel, dim3(nt, nt), dim3(256), 0, s, l.Up, in, l.Vt);
+    hipLaunchKernelGGL(uprime_t16_kernel, dim3(nt, nt), dim3(256), 0, s, l.Up, in, l.Vt, l.Vl);
     GPTQ_HIP_TRY(hipGetLastError());
   }
   hipLaunchKernelGGL(perm_tables_kernel, dim3((unsigned)((in + 255) / 256)), dim3(256), 0, s, perm,
@@ -928,7 +944,7 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                        bits, sym, scales, zeros);
     GPTQ_HIP_TRY(hipGetLastError());
   }
-  QCtx c{l.Wp, l.Up, l.Vt, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.emax, l.rs,
+  QCtx c{l.Wp, l.Up, l.Vt, l.Vl, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.einv,
          s};
   GPTQ_HIP_TRY(process(c, 0, in));
   // rows per packing workgroup: as many (up to 16) as fit next to pinv in 160 KiB of LDS
