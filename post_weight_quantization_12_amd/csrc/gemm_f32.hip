@@ -795,10 +795,12 @@ hipError_t launch_gemm_eh(int64_t M, int64_t N, int64_t K, const float* E, int64
     return hipSuccess;
   }
   const int64_t tm = (M + EH_BM - 1) / EH_BM;
-  // 128 x 256 tiles where they fill the CUs for two rounds or more (two-product
-  // 128-column blocks: the per-stage block sums of smaller blocks do not fit
-  // the registers of eight waves), else 128 x 128
-  const bool wide = !Vl && kb == 128 && tm * ((N + 255) / 256) >= 512;
+  // 128 x 256 tiles from half a round of them on (C3's 4096 x 2688 x 2816:
+  // 194 -> 173 us, 4096 x 1408 x 1408: 63 -> 47 us; a third of a round, at
+  // 4096 x 640 x 768, 21 -> 25 us), for two-product 128-column blocks (the
+  // per-stage block sums of smaller blocks do not fit the registers of eight
+  // waves); else 128 x 128
+  const bool wide = !Vl && kb == 128 && tm * ((N + 255) / 256) >= 128;
   const int bn = wide ? 256 : 128;
   const dim3 grid((unsigned)(tm * ((N + bn - 1) / bn)));
 #define GPTQ_EH(VL, SPB, BN)                                                                    \
