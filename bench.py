@@ -429,9 +429,9 @@ STAGES = [
                                   "symmetrize_kernel", "scale_kernel", "gather_kernel",
                                   "fill_f32_kernel", "gather_w_kernel")),
     ("a3 factor (Cholesky + inverse, U')", ("cholinv_leaf_kernel", "reverse_inplace_kernel",
-                                             "uprime_kernel", "gemm_f32_dma@prepare")),
+                                             "gemm_f32_dma@prepare")),
     ("a4 block sweep", ("sweep16_kernel", "sweep_kernel")),
-    ("a5 lazy trailing update", ("gemm_eh_dma", "uprime_t16_kernel", "gemm_f32_dma@quantize")),
+    ("a5 lazy trailing update", ("gemm_eh_dma", "uprime_split_kernel", "gemm_f32_dma@quantize")),
     ("a6 pack", ("pack_kernel", "perm_tables_kernel")),
 ]
 

@@ -171,48 +171,39 @@ gather_w_kernel(const T* __restrict__ W, int64_t out, int64_t in, const int32_t*
   }
 }
 
-// Up[j][k] = U[j][k] / U[j][j] for k > j and 0 for 4*floor(j/4) <= k <= j.
-// Columns further left are never read (the sweep's window of row j starts at
-// column 4*floor(j/4); the trailing GEMMs read only columns right of their
-// rows) and are not written.  One float4 per thread.
+// The forms of U' = diag(U)^-1 U the later kernels read, from U (upper, n x n
+// fp32) in one pass:
+//   Ub[b][j][k] = U'[bB + j][bB + k] for the sweep's diagonal B x B blocks
+//               (k > j; 0 for k <= j);
+//   Vt[c][r] = fp16(U'[r][c]) (round to nearest) and Vl[c][r] = the
+//   remainder U'[r][c] - Vt[c][r] (exact in fp32) rounded toward zero to
+//   fp16, for r < c: U' transposed for the trailing GEMMs, which read it
+//   k-contiguous (null when the layer has no trailing GEMM).
+// 64 x 64 tiles of U through LDS; tiles below the diagonal exit (the parts
+// of a diagonal block they cover are never read: a sweep row's window
+// starts at most 15 columns left of its diagonal, inside the same tile).
 __global__ void __launch_bounds__(256)
-uprime_kernel(const float* __restrict__ U, int64_t n, float* __restrict__ Up) {
-  const int64_t j = blockIdx.y;
-  const int64_t k0 = 4 * (j / 4) + 4 * (blockIdx.x * (int64_t)blockDim.x + threadIdx.x);
-  if (k0 >= n) return;
-  const float d = U[j * n + j];
-  const float* src = U + j * n + k0;
-  float* dst = Up + j * n + k0;
-  if (k0 + 4 <= n && (n & 3) == 0) {
-    const float4 u = *reinterpret_cast<const float4*>(src);
-    float4 r;
-    r.x = k0 + 0 > j ? u.x / d : 0.0f;
-    r.y = k0 + 1 > j ? u.y / d : 0.0f;
-    r.z = k0 + 2 > j ? u.z / d : 0.0f;
-    r.w = k0 + 3 > j ? u.w / d : 0.0f;
-    *reinterpret_cast<float4*>(dst) = r;
-  } else {
-    for (int e = 0; e < 4 && k0 + e < n; ++e) dst[e] = k0 + e > j ? src[e] / d : 0.0f;
-  }
-}
-
-// Vt[c][r] = fp16(Up[r][c]) (round to nearest) and Vl[c][r] = the remainder
-// Up[r][c] - Vt[c][r] (exact in fp32) rounded toward zero to fp16, for the
-// strictly upper part r < c: U' transposed for the error-update GEMMs, which
-// read it k-contiguous.  64 x 64 tiles through LDS; tiles below the diagonal
-// exit.
-__global__ void __launch_bounds__(256)
-uprime_t16_kernel(const float* __restrict__ Up, int64_t n, _Float16* __restrict__ Vt,
-                  _Float16* __restrict__ Vl) {
+uprime_split_kernel(const float* __restrict__ U, int64_t n, int B, float* __restrict__ Ub,
+                    _Float16* __restrict__ Vt, _Float16* __restrict__ Vl) {
   __shared__ float tile[64][65];
+  __shared__ float dg[64];
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
   if (r0 > c0 + 63) return;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < n && c < n && r < c) ? Up[r * n + c] : 0.0f;
+  if (threadIdx.x < 64) {
+    const int64_t r = r0 + threadIdx.x;
+    dg[threadIdx.x] = r < n ? U[r * n + r] : 1.0f;
   }
   __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    if (r >= n || c >= n) continue;
+    const float v = r < c ? U[r * n + c] / dg[i] : 0.0f;
+    tile[i][tx] = v;
+    if (r / B == c / B) Ub[(r / B) * B * B + (r % B) * B + (c % B)] = v;
+  }
+  __syncthreads();
+  if (Vt == nullptr) return;
   for (int i = ty; i < 64; i += 4) {
     const int64_t c = c0 + i, r = r0 + tx;
     if (c < n && r < n && r < c) {
@@ -286,7 +277,7 @@ struct SweepSmem {
 
 template <int B, int GS>
 __global__ void __launch_bounds__(SW_THREADS)
-sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, int64_t in,
+sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Ub, int64_t out, int64_t in,
              int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
              int32_t* __restrict__ zeros, uint8_t* __restrict__ codes,
              float* __restrict__ einv) {
@@ -313,7 +304,7 @@ sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, 
       const int j = e / NR, t = e % NR;
       const int c = 4 * (j / 4 + t);
       v[p] = (j < width && c < width)
-                 ? *reinterpret_cast<const float4*>(Up + (c0 + j) * in + c0 + c)
+                 ? *reinterpret_cast<const float4*>(Ub + j * B + c)
                  : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
@@ -538,7 +529,7 @@ __device__ inline float row_max16(float v) {
 
 template <int B, int GS>
 __global__ void __launch_bounds__(S16_THREADS)
-sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out, int64_t in,
+sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Ub, int64_t out, int64_t in,
                int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
                int32_t* __restrict__ zeros, uint8_t* __restrict__ codes,
                float* __restrict__ einv) {
@@ -580,7 +571,7 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out
       const int j = e / (NR * 4), t = (e / 4) % NR, h = e % 4;
       const int c = 16 * (j / 16 + t) + 4 * h;
       v[u] = (j < width && c < width)
-                 ? *reinterpret_cast<const float4*>(Up + (c0 + j) * in + c0 + c)
+                 ? *reinterpret_cast<const float4*>(Ub + j * B + c)
                  : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
@@ -736,7 +727,7 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Up, int64_t out
 }
 
 template <int B, int GS>
-hipError_t launch_sweep16(float* Wp, const float* Up, int64_t out, int64_t in, int64_t c0,
+hipError_t launch_sweep16(float* Wp, const float* Ub, int64_t out, int64_t in, int64_t c0,
                           int width, int bits, int sym, float* scales, int32_t* zeros,
                           uint8_t* codes, float* einv, hipStream_t s) {
   auto k = sweep16_kernel<B, GS>;
@@ -744,31 +735,31 @@ hipError_t launch_sweep16(float* Wp, const float* Up, int64_t out, int64_t in, i
   GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)lds));
   hipLaunchKernelGGL(k, dim3((unsigned)((out + S16_ROWS - 1) / S16_ROWS)), dim3(S16_THREADS), lds,
-                     s, Wp, Up, out, in, c0, width, bits, sym, scales, zeros, codes, einv);
+                     s, Wp, Ub, out, in, c0, width, bits, sym, scales, zeros, codes, einv);
   return hipGetLastError();
 }
 
 template <int B>
-hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t in, int64_t c0,
+hipError_t launch_sweep(int gs, float* Wp, const float* Ub, int64_t out, int64_t in, int64_t c0,
                         int width, int bits, int sym, float* scales, int32_t* zeros,
                         uint8_t* codes, float* einv, hipStream_t s) {
   if (gs > B) return hipErrorInvalidValue;
   // 16 lanes per row where the group size allows it.
   switch (gs > 0 ? gs : 0) {
-    case 0: return launch_sweep16<B, 0>(Wp, Up, out, in, c0, width, bits, sym, scales, zeros,
+    case 0: return launch_sweep16<B, 0>(Wp, Ub, out, in, c0, width, bits, sym, scales, zeros,
                                         codes, einv, s);
-    case 16: return launch_sweep16<B, 16>(Wp, Up, out, in, c0, width, bits, sym, scales, zeros,
+    case 16: return launch_sweep16<B, 16>(Wp, Ub, out, in, c0, width, bits, sym, scales, zeros,
                                           codes, einv, s);
-    case 32: return launch_sweep16<B, 32>(Wp, Up, out, in, c0, width, bits, sym, scales, zeros,
+    case 32: return launch_sweep16<B, 32>(Wp, Ub, out, in, c0, width, bits, sym, scales, zeros,
                                           codes, einv, s);
     case 64:
       if constexpr (B >= 64)
-        return launch_sweep16<B, (B >= 64 ? 64 : 16)>(Wp, Up, out, in, c0, width, bits, sym,
+        return launch_sweep16<B, (B >= 64 ? 64 : 16)>(Wp, Ub, out, in, c0, width, bits, sym,
                                                        scales, zeros, codes, einv, s);
       break;
     case 128:
       if constexpr (B >= 128)
-        return launch_sweep16<B, (B >= 128 ? 128 : 16)>(Wp, Up, out, in, c0, width, bits, sym,
+        return launch_sweep16<B, (B >= 128 ? 128 : 16)>(Wp, Ub, out, in, c0, width, bits, sym,
                                                          scales, zeros, codes, einv, s);
       break;
     default:
@@ -781,7 +772,7 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
     auto k = sweep_kernel<B, (G > 0 ? G : 0)>;                                                 \
     GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,                                           \
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));   \
-    hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,  \
+    hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Ub, out, in, c0, width, bits, sym, scales,  \
                        zeros, codes, einv);                                                    \
     break;                                                                                     \
   }
@@ -796,7 +787,7 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
         auto k = sweep_kernel<B, (B >= 64 ? 64 : 4)>;
         GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-        hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,
+        hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Ub, out, in, c0, width, bits, sym, scales,
                            zeros, codes, einv);
       }
       break;
@@ -805,7 +796,7 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
         auto k = sweep_kernel<B, (B >= 128 ? 128 : 4)>;
         GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-        hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Up, out, in, c0, width, bits, sym, scales,
+        hipLaunchKernelGGL(k, grid, block, lds, s, Wp, Ub, out, in, c0, width, bits, sym, scales,
                            zeros, codes, einv);
       }
       break;
@@ -818,7 +809,7 @@ hipError_t launch_sweep(int gs, float* Wp, const float* Up, int64_t out, int64_t
 
 struct QCtx {
   float* Wp;
-  const float* Up;
+  const float* Ub;     // U' diagonal blocks, [ceil(in / block)][block][block]
   const _Float16* Vt;  // U' transposed, rounded to fp16
   const _Float16* Vl;  // remainders U' - Vt, rounded toward zero to fp16
   int64_t out, in;
@@ -833,11 +824,11 @@ struct QCtx {
 hipError_t sweep_block(QCtx& c, int64_t a, int64_t b) {
   const int width = (int)(b - a);
   switch (c.block) {
-    case 32: return launch_sweep<32>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
+    case 32: return launch_sweep<32>(c.gs, c.Wp, c.Ub + (a / 32) * 32 * 32, c.out, c.in, a, width, c.bits, c.sym,
                                      c.scales, c.zeros, c.codes, c.einv, c.s);
-    case 64: return launch_sweep<64>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
+    case 64: return launch_sweep<64>(c.gs, c.Wp, c.Ub + (a / 64) * 64 * 64, c.out, c.in, a, width, c.bits, c.sym,
                                      c.scales, c.zeros, c.codes, c.einv, c.s);
-    default: return launch_sweep<128>(c.gs, c.Wp, c.Up, c.out, c.in, a, width, c.bits, c.sym,
+    default: return launch_sweep<128>(c.gs, c.Wp, c.Ub + (a / 128) * 128 * 128, c.out, c.in, a, width, c.bits, c.sym,
                                       c.scales, c.zeros, c.codes, c.einv, c.s);
   }
 }
@@ -871,7 +862,7 @@ hipError_t process(QCtx& c, int64_t a, int64_t b) {
 
 struct QLayout {
   float* Wp;
-  float* Up;
+  float* Ub;
   _Float16* Vt;
   _Float16* Vl;
   uint8_t* codes;
@@ -884,7 +875,8 @@ QLayout carve(void* ws, int64_t out, int64_t in, int block) {
   Carver c(ws);
   QLayout l;
   l.Wp = c.take<float>((size_t)out * in);
-  l.Up = c.take<float>((size_t)in * in);
+  const int64_t nblk = (in + block - 1) / block;
+  l.Ub = c.take<float>((size_t)nblk * block * block);
   // the trailing GEMMs (only when the layer is wider than one block)
   const bool gemms = in > block;
   l.Vt = gemms ? c.take<_Float16>((size_t)in * in) : nullptr;
@@ -928,12 +920,10 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                        out, in, perm, l.Wp);
   }
   GPTQ_HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(uprime_kernel, dim3((unsigned)((in / 4 + 256) / 256), (unsigned)in), dim3(256),
-                     0, s, U, in, l.Up);
-  GPTQ_HIP_TRY(hipGetLastError());
-  if (l.Vt) {
+  {
     const unsigned nt = (unsigned)((in + 63) / 64);
-    hipLaunchKernelGGL(uprime_t16_kernel, dim3(nt, nt), dim3(256), 0, s, l.Up, in, l.Vt, l.Vl);
+    hipLaunchKernelGGL(uprime_split_kernel, dim3(nt, nt), dim3(256), 0, s, U, in, block, l.Ub, l.Vt,
+                       l.Vl);
     GPTQ_HIP_TRY(hipGetLastError());
   }
   hipLaunchKernelGGL(perm_tables_kernel, dim3((unsigned)((in + 255) / 256)), dim3(256), 0, s, perm,
@@ -944,7 +934,7 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                        bits, sym, scales, zeros);
     GPTQ_HIP_TRY(hipGetLastError());
   }
-  QCtx c{l.Wp, l.Up, l.Vt, l.Vl, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.einv,
+  QCtx c{l.Wp, l.Ub, l.Vt, l.Vl, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.einv,
          s};
   GPTQ_HIP_TRY(process(c, 0, in));
   // rows per packing workgroup: as many (up to 16) as fit next to pinv in 160 KiB of LDS
