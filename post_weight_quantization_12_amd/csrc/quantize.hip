@@ -527,16 +527,19 @@ __device__ inline float row_max16(float v) {
   return v;
 }
 
+// One block of the sweep for the workgroup's 16 rows (smem16: the
+// workgroup's Sweep16Smem<B>).  delta (LDS, [16 rows][B], or null): an
+// update of the block's columns still to be subtracted from the values
+// loaded from Wp.
 template <int B, int GS>
-__global__ void __launch_bounds__(S16_THREADS)
-sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Ub, int64_t out, int64_t in,
-               int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
-               int32_t* __restrict__ zeros, uint8_t* __restrict__ codes,
-               float* __restrict__ einv) {
+__device__ __attribute__((always_inline)) inline void sweep16_body(
+    float* smem16, float* __restrict__ Wp, const float* __restrict__ Ub, int64_t out, int64_t in,
+    int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
+    int32_t* __restrict__ zeros, uint8_t* __restrict__ codes, float* __restrict__ einv,
+    const float* delta) {
   using SM = Sweep16Smem<B>;
   constexpr int NR = SM::NR, PITCH = SM::PITCH, EP = SM::EP;
   static_assert(GS % 16 == 0, "group size a multiple of 16 (0: one group per row)");
-  extern __shared__ __align__(16) float smem16[];
   float* Ul = smem16;
   float* Es = smem16 + SM::UL;
   uint8_t* Cs = reinterpret_cast<uint8_t*>(Es + SM::ES);
@@ -597,6 +600,10 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Ub, int64_t out
   }
   float rs = 1.0f / s;
   __syncthreads();
+  if (delta != nullptr) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) w[r] -= delta[rl * B + 16 * r + q];
+  }
 
   // U' rows of the step's 16 columns, each replaced by the same column of
   // the next step once used, so the LDS latency (16 columns ahead) stays off
@@ -727,6 +734,88 @@ sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Ub, int64_t out
 }
 
 template <int B, int GS>
+__global__ void __launch_bounds__(S16_THREADS)
+sweep16_kernel(float* __restrict__ Wp, const float* __restrict__ Ub, int64_t out, int64_t in,
+               int64_t c0, int width, int bits, int sym, float* __restrict__ scales,
+               int32_t* __restrict__ zeros, uint8_t* __restrict__ codes,
+               float* __restrict__ einv) {
+  extern __shared__ __align__(16) float smem16[];
+  sweep16_body<B, GS>(smem16, Wp, Ub, out, in, c0, width, bits, sym, scales, zeros, codes, einv,
+                      nullptr);
+}
+
+// Two adjacent full 128-column blocks in one launch: the first block's sweep,
+// its update of the second block for the workgroup's rows, the second
+// block's sweep.  The update (the trailing product of the pair, otherwise a
+// GEMM launch of its own between two sweep launches) runs on the matrix
+// cores in fp32: the first block's fp32 errors (still in LDS) times U' of
+// the pair, rebuilt in fp32 from its fp16 parts (Vt + Vl, U' transposed) and
+// staged in the space of the sweep's U' window.
+constexpr int PAIR_B = 128;
+template <int GS>
+__global__ void __launch_bounds__(S16_THREADS)
+sweep16_pair_kernel(float* __restrict__ Wp, const float* __restrict__ Ub,
+                    const _Float16* __restrict__ Vt, const _Float16* __restrict__ Vl, int64_t out,
+                    int64_t in, int64_t c0, int bits, int sym, float* __restrict__ scales,
+                    int32_t* __restrict__ zeros, uint8_t* __restrict__ codes,
+                    float* __restrict__ einv) {
+  constexpr int B = PAIR_B;
+  using SM = Sweep16Smem<B>;
+  constexpr int UP = B + 4;  // pitch of the staged U' block (rows 4 banks apart)
+  static_assert(SM::UL >= (size_t)B * UP, "the pair's U' block fits the window's space");
+  extern __shared__ __align__(16) float smem16[];
+  float* delta = smem16 + (SM::BYTES / sizeof(float));  // [16 rows][B]
+  sweep16_body<B, GS>(smem16, Wp, Ub, out, in, c0, B, bits, sym, scales, zeros, codes, einv,
+                      nullptr);
+  __syncthreads();  // the window and the first block's errors are final
+  const int tid = threadIdx.x;
+  float* Us = smem16;                 // Us[k * UP + j] = U'[c0 + k][c0 + B + j]
+  const float* Es = smem16 + SM::UL;  // the first block's errors, [16 rows][EP]
+  {
+    const int j = tid >> 1, kh = (tid & 1) * (B / 2);
+    const _Float16* vt = Vt + (c0 + B + j) * in + c0 + kh;
+    const _Float16* vl = Vl + (c0 + B + j) * in + c0 + kh;
+    half8_t hv[B / 16], lv[B / 16];
+#pragma unroll
+    for (int u = 0; u < B / 16; ++u) {
+      hv[u] = *reinterpret_cast<const half8_t*>(vt + 8 * u);
+      lv[u] = *reinterpret_cast<const half8_t*>(vl + 8 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < B / 16; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Us[(kh + 8 * u + e) * UP + j] = (float)hv[u][e] + (float)lv[u][e];
+  }
+  __syncthreads();
+  {
+    // v_mfma_f32_16x16x4f32: lane l supplies E[l % 16][k + l / 16] and
+    // U'[k + l / 16][j + l % 16] and holds rows 4 (l / 16) .. +3 of column
+    // j + l % 16; wave v takes columns 32 v .. 32 v + 31.
+    const int l = tid & 63, v = tid >> 6;
+    f32x4_t d[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[t][i] = 0.0f;
+#pragma unroll 4
+    for (int k = 0; k < B; k += 4) {
+      const float a = Es[(l & 15) * SM::EP + k + (l >> 4)];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        d[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+            a, Us[(k + (l >> 4)) * UP + 32 * v + 16 * t + (l & 15)], d[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) delta[(4 * (l >> 4) + i) * B + 32 * v + 16 * t + (l & 15)] = d[t][i];
+  }
+  __syncthreads();
+  sweep16_body<B, GS>(smem16, Wp, Ub + B * B, out, in, c0 + B, B, bits, sym, scales, zeros, codes,
+                      einv, delta);
+}
+
+template <int B, int GS>
 hipError_t launch_sweep16(float* Wp, const float* Ub, int64_t out, int64_t in, int64_t c0,
                           int width, int bits, int sym, float* scales, int32_t* zeros,
                           uint8_t* codes, float* einv, hipStream_t s) {
@@ -736,6 +825,20 @@ hipError_t launch_sweep16(float* Wp, const float* Ub, int64_t out, int64_t in, i
                                    (int)lds));
   hipLaunchKernelGGL(k, dim3((unsigned)((out + S16_ROWS - 1) / S16_ROWS)), dim3(S16_THREADS), lds,
                      s, Wp, Ub, out, in, c0, width, bits, sym, scales, zeros, codes, einv);
+  return hipGetLastError();
+}
+
+template <int GS>
+hipError_t launch_sweep16_pair(float* Wp, const float* Ub, const _Float16* Vt, const _Float16* Vl,
+                               int64_t out, int64_t in, int64_t c0, int bits, int sym,
+                               float* scales, int32_t* zeros, uint8_t* codes, float* einv,
+                               hipStream_t s) {
+  auto k = sweep16_pair_kernel<GS>;
+  const size_t lds = Sweep16Smem<PAIR_B>::BYTES + (size_t)S16_ROWS * PAIR_B * sizeof(float);
+  GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)lds));
+  hipLaunchKernelGGL(k, dim3((unsigned)((out + S16_ROWS - 1) / S16_ROWS)), dim3(S16_THREADS), lds,
+                     s, Wp, Ub, Vt, Vl, out, in, c0, bits, sym, scales, zeros, codes, einv);
   return hipGetLastError();
 }
 
@@ -847,9 +950,35 @@ hipError_t sweep_block(QCtx& c, int64_t a, int64_t b) {
 // against a 1e-3 boundary window; three products keep 9e-6 at 28672.
 constexpr int64_t SPLIT_MIN_K = 512;
 constexpr int64_t TWO_PRODUCT_MAX_IN = 16384;
+// Two full 128-column blocks in one launch (sweep16_pair_kernel), for the
+// group sizes the 16-lane sweep takes.
+hipError_t sweep_pair(QCtx& c, int64_t a) {
+  const float* Ub = c.Ub + (a / PAIR_B) * PAIR_B * PAIR_B;
+  switch (c.gs > 0 ? c.gs : 0) {
+#define GPTQ_PAIR_CASE(G)                                                                     \
+  case G:                                                                                     \
+    return launch_sweep16_pair<G>(c.Wp, Ub, c.Vt, c.Vl, c.out, c.in, a, c.bits, c.sym,        \
+                                  c.scales, c.zeros, c.codes, c.einv, c.s);
+    GPTQ_PAIR_CASE(0)
+    GPTQ_PAIR_CASE(16)
+    GPTQ_PAIR_CASE(32)
+    GPTQ_PAIR_CASE(64)
+    GPTQ_PAIR_CASE(128)
+#undef GPTQ_PAIR_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+bool pair_fits(const QCtx& c) {
+  const int g = c.gs > 0 ? c.gs : 0;
+  return c.block == PAIR_B && c.Vt != nullptr &&
+         (g == 0 || g == 16 || g == 32 || g == 64 || g == 128);
+}
+
 hipError_t process(QCtx& c, int64_t a, int64_t b) {
   const int64_t B = c.block;
   if (b - a <= B) return sweep_block(c, a, b);
+  if (b - a == 2 * B && pair_fits(c)) return sweep_pair(c, a);
   const int64_t nblk = (b - a + B - 1) / B;
   const int64_t m = a + B * ((nblk + 1) / 2);
   GPTQ_HIP_TRY(process(c, a, m));
