@@ -430,10 +430,29 @@ STAGES = [
                                   "fill_f32_kernel", "gather_w_kernel")),
     ("a3 factor (Cholesky + inverse, U')", ("cholinv_leaf_kernel", "reverse_inplace_kernel",
                                              "gemm_f32_dma@prepare")),
-    ("a4 block sweep", ("sweep16_kernel", "sweep_kernel")),
+    ("a4 block sweep", ("sweep16_kernel", "sweep16_pair_kernel", "sweep_kernel")),
     ("a5 lazy trailing update", ("gemm_eh_dma", "uprime_split_kernel", "gemm_f32_dma@quantize")),
     ("a6 pack", ("pack_kernel", "perm_tables_kernel")),
 ]
+
+
+def sweep_pairs(cfg):
+    """Pairs of adjacent full 128-column blocks the quantize recursion sweeps
+    in one kernel (both halves of a two-block range), for this layer."""
+    B, n = cfg.block, cfg.inp
+    gs = cfg.group_size if cfg.group_size > 0 else 0
+    if B != 128 or gs not in (0, 16, 32, 64, 128) or n <= B:
+        return 0
+
+    def rec(a, b):
+        if b - a <= B:
+            return 0
+        if b - a == 2 * B:
+            return 1
+        nblk = (b - a + B - 1) // B
+        m = a + B * ((nblk + 1) // 2)
+        return rec(a, m) + rec(m, b)
+    return rec(0, n)
 
 
 def stage_roofline(cfg, rows):
@@ -472,6 +491,9 @@ def stage_roofline(cfg, rows):
                 break
     if a3_span:
         a3_wall += a3_span[1] - a3_span[0]
+    # the update of each pair of adjacent 128-column blocks (2 out B^2 flop)
+    # runs inside the pair's sweep kernel (a4); a5 counts the GEMMs' share
+    a5_flop = float(out) * n * (n - cfg.block) - sweep_pairs(cfg) * 2.0 * out * cfg.block ** 2
     work = {
         "a1 Hessian SYRK": (float(cfg.tokens) * n * (n + 1), "flop", "fp16 MFMA", PEAK_FP16_TFLOPS * 1e12),
         "a2 damp / order / gather": (8.0 * n * n + 6.0 * out * n, "B", "HBM", PEAK_HBM_GBS * 1e9),
@@ -479,8 +501,7 @@ def stage_roofline(cfg, rows):
                                                PEAK_FP32_TFLOPS * 1e12),
         "a4 block sweep": (7.0 * out * n + 8.0 * out * n / gs, "B", "HBM (latency-bound)",
                            PEAK_HBM_GBS * 1e9),
-        "a5 lazy trailing update": (float(out) * n * (n - cfg.block), "flop", "fp16 MFMA",
-                                    PEAK_FP16_TFLOPS * 1e12),
+        "a5 lazy trailing update": (a5_flop, "flop", "fp16 MFMA", PEAK_FP16_TFLOPS * 1e12),
         "a6 pack": (out * n * (1 + b / 8.0), "B", "HBM", PEAK_HBM_GBS * 1e9),
     }
     lines = ["| stage | kernel ms | algorithmic work | achieved | bound | frac | MFMA pipe |",
@@ -507,7 +528,9 @@ def stage_roofline(cfg, rows):
                  f"{2.0 * n ** 3 / 3 / (a3_wall / steps * 1e-9) / 1e12:.1f} TFLOP/s.")
     lines.append("Peaks: fp16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s, HBM 8 TB/s. Work per "
                  "stage: a1 N n(n+1), a2 8 n^2 + 6 out in bytes, a3 2 n^3 / 3, a4 "
-                 "7 out in + 8 out in / gs bytes, a5 out in (in - B), a6 out in (1 + b/8) bytes. "
+                 "7 out in + 8 out in / gs bytes, a5 out in (in - B) less 2 out B^2 per pair of "
+                 "adjacent blocks swept by one kernel (" + str(sweep_pairs(cfg)) + " pairs; their "
+                 "update runs in a4), a6 out in (1 + b/8) bytes. "
                  "MFMA pipe: fp16 MFMA work actually issued (" +
                  ("three" if n > 16384 else "two") + " products per algorithmic one in the "
                  "trailing GEMMs) over the fp16 peak.")

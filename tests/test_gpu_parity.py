@@ -184,6 +184,10 @@ QCASES = [
     ("2bit_rowgroup_b32_f32", "c1", 40, 640, 2, -1, False, True, 32, torch.float32),
     ("4bit_sym_g64", "c3", 130, 1024, 4, 64, True, True, 128, torch.float16),
     ("4bit_g4_b32", "c1", 33, 256, 4, 4, False, False, 32, torch.float16),
+    # two-block ranges swept by one kernel with the pair's update inside it:
+    # groups of 16, and one group per row
+    ("4bit_g16_b128_pairs", "c1", 48, 768, 4, 16, False, True, 128, torch.float16),
+    ("3bit_rowgroup_b128_pairs", "c3", 40, 640, 3, -1, True, True, 128, torch.float32),
     # in > 4096: blocks of four sweep blocks with the helper-stream updates
     ("wide_in_b64", "c1", 40, 4640, 4, 64, False, True, 64, torch.float16),
     ("wide_in_b128_sym", "c3", 24, 5024, 4, 128, True, True, 128, torch.float16),
