@@ -238,7 +238,13 @@ gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict_
 //   T = L21 X11, X21 = -X22 T, again in 16 x 16 MFMA tiles over all waves.
 // Rows >= m are padded with the identity (so every pivot is defined).  Only
 // X is written back (lower part, rows and columns < m): the recursion never
-// reads L again.
+// reads L again.  L and X share one LDS array: L in the strict lower
+// triangle, X transposed in the upper one and on the diagonal
+// (X[i][j], i >= j, at [j][i]; L's own diagonal is not read once the
+// reciprocals 1 / L_jj are kept).  68 KiB instead of 135: the leaf then fits
+// on a compute unit beside a GEMM workgroup of the helper streams, instead
+// of waiting for one to drain (leaves waited 15 us on average at n = 11008
+// and 65 us at n = 28672 with L and X apart).
 constexpr int LP = NB + 4;  // padded LDS row (16-byte aligned rows)
 constexpr int LEAF_THREADS = 512;
 constexpr int NSTEP = NB / 16;
@@ -316,17 +322,48 @@ __device__ inline void store_tile(float* C, f32x4_t v, int lane) {
 }
 
 // One doubling level of the leaf's inverse: for each pair of SZ-blocks on the
-// diagonal, T = L21 X11 (into the X21 area), then X21 = -X22 T.
+// diagonal, T = L21 X11 (into the X21 area), then X21 = -X22 T.  X (and T)
+// are read and written transposed in the upper triangle of Ls; the zeros of
+// the triangular X11 and X22 (whose places hold L) are supplied by masks.
+// Tiles as tile16: lane l supplies a(l%16, k) and b(k, l%16) for k = 4i + l/16
+// and holds rows 4(l/16)..+3 of column l%16; the K/4 products go to up to four
+// accumulators in turn.
 template <int SZ>
-__device__ inline void doubling_level(const float* Ls, float* Xs, int wave, int lane) {
+__device__ inline void doubling_level(float* Ls, int wave, int lane) {
   constexpr int PER = (SZ / 16) * (SZ / 16), TILES = (NB / (2 * SZ)) * PER;
   constexpr int NWAVE = LEAF_THREADS / 64, HOLD = (TILES + NWAVE - 1) / NWAVE;
+  constexpr int NK = SZ / 4, NA = NK < 4 ? NK : 4;
+  const int r = lane & 15, kq = lane >> 4;
+  auto mma = [&](const float (&a)[NK], const float (&b)[NK]) {
+    f32x4_t part[NA];
+#pragma unroll
+    for (int p = 0; p < NA; ++p) part[p] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+      part[i % NA] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], part[i % NA], 0, 0, 0);
+#pragma unroll
+    for (int p = 1; p < NA; ++p) part[0] += part[p];
+    return part[0];
+  };
+  // element (4(l/16) + q, l%16) of the tile at rows/columns (ri, cj) of the
+  // X21 area (block rows o+SZ.., columns o..), stored transposed
+  auto store_t = [&](int o, int ri, int cj, f32x4_t v) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      Ls[(o + cj + r) * LP + o + SZ + ri + 4 * kq + q] = v[q];
+  };
   for (int t = wave; t < TILES; t += NWAVE) {
     const int o = (t / PER) * 2 * SZ, ti = (t % PER) / (SZ / 16), tj = (t % PER) % (SZ / 16);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    acc = tile16<false, SZ>(Ls + (o + SZ + 16 * ti) * LP + o, Xs + o * LP + o + 16 * tj, acc,
-                            1.0f, lane);
-    store_tile(Xs + (o + SZ + 16 * ti) * LP + o + 16 * tj, acc, lane);
+    // T[16ti + .][16tj + c] = sum_k L[o+SZ+16ti+.][o+k] X11[k][16tj + c]   (X11[k][c] = 0 for k < c)
+    float a[NK], b[NK];
+    const int c = 16 * tj + r;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int k = 4 * i + kq;
+      a[i] = Ls[(o + SZ + 16 * ti + r) * LP + o + k];
+      b[i] = k >= c ? Ls[(o + c) * LP + o + k] : 0.0f;
+    }
+    store_t(o, 16 * ti, 16 * tj, mma(a, b));
   }
   __syncthreads();
   f32x4_t res[HOLD];
@@ -336,8 +373,16 @@ __device__ inline void doubling_level(const float* Ls, float* Xs, int wave, int 
     res[h] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     if (t < TILES) {
       const int o = (t / PER) * 2 * SZ, ti = (t % PER) / (SZ / 16), tj = (t % PER) % (SZ / 16);
-      res[h] = tile16<false, SZ>(Xs + (o + SZ + 16 * ti) * LP + o + SZ,
-                                 Xs + (o + SZ) * LP + o + 16 * tj, res[h], -1.0f, lane);
+      // X21[16ti + i][.] = -sum_k X22[16ti + i][k] T[k][.]   (X22[i][k] = 0 for k > i)
+      float a[NK], b[NK];
+      const int ri = 16 * ti + r;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int k = 4 * i + kq;
+        a[i] = k <= ri ? -Ls[(o + SZ + k) * LP + o + SZ + ri] : 0.0f;
+        b[i] = Ls[(o + 16 * tj + r) * LP + o + SZ + k];
+      }
+      res[h] = mma(a, b);
     }
   }
   __syncthreads();
@@ -346,7 +391,7 @@ __device__ inline void doubling_level(const float* Ls, float* Xs, int wave, int 
     const int t = wave + h * NWAVE;
     if (t < TILES) {
       const int o = (t / PER) * 2 * SZ, ti = (t % PER) / (SZ / 16), tj = (t % PER) % (SZ / 16);
-      store_tile(Xs + (o + SZ + 16 * ti) * LP + o + 16 * tj, res[h], lane);
+      store_t(o, 16 * ti, 16 * tj, res[h]);
     }
   }
   __syncthreads();
@@ -355,8 +400,7 @@ __device__ inline void doubling_level(const float* Ls, float* Xs, int wave, int 
 __global__ void __launch_bounds__(LEAF_THREADS)
 cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t off,
                     int m, int32_t* __restrict__ info) {
-  __shared__ __align__(16) float Ls[NB * LP];
-  __shared__ __align__(16) float Xs[NB * LP];
+  __shared__ __align__(16) float Ls[NB * LP];  // L lower, X transposed upper and diagonal
   __shared__ float rinv_s[NB];  // 1 / L_jj
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15;
@@ -381,7 +425,6 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
       l.z = j + 2 <= i ? v[u].z : 0.0f;
       l.w = j + 3 <= i ? v[u].w : 0.0f;
       *reinterpret_cast<float4*>(Ls + i * LP + j) = l;
-      *reinterpret_cast<float4*>(Xs + i * LP + j) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   } else {
     // 8 loads per thread in flight (addresses of masked-out elements are
@@ -401,14 +444,14 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
         const int e = tid + LEAF_THREADS * (q0 + u), i = e / NB, j = e % NB;
         const bool ok = i < m && j <= i;
         Ls[i * LP + j] = ok ? v[u] : (i == j ? 1.0f : 0.0f);
-        Xs[i * LP + j] = 0.0f;
       }
     }
   }
   __syncthreads();
 
-  // Y = (diagonal block b of L)^-1 into Xs, by one wave (lanes 0..15 hold rows):
-  // row k of Y = (e_k - sum_{j<k} L_kj Y_j) / L_kk, rows broadcast by readlane.
+  // Y = (diagonal block b of L)^-1, by one wave (lanes 0..15 hold rows):
+  // row k of Y = (e_k - sum_{j<k} L_kj Y_j) / L_kk, rows broadcast by readlane;
+  // stored transposed into the block's upper part and diagonal.
   auto invert_block = [&](int b) {
     const int c = 16 * b;
     float d[16], y[16];
@@ -430,7 +473,8 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
     }
     if (lane < 16) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) Xs[(c + li) * LP + c + j] = j <= li ? y[j] : 0.0f;
+      for (int j = 0; j < 16; ++j)
+        if (j <= li) Ls[(c + j) * LP + c + li] = y[j];
     }
   };
 
@@ -545,24 +589,27 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
   // Off-diagonal blocks of X by doubling: for blocks of 2s (s = 16, 32, 64)
   //   T = L21 X11 (into the X21 area), X21 = -X22 T,
   // with every level's tiles spread over the 8 waves (16 x 16 MFMA tiles).
-  doubling_level<16>(Ls, Xs, wave, lane);
-  doubling_level<32>(Ls, Xs, wave, lane);
-  doubling_level<64>(Ls, Xs, wave, lane);
+  doubling_level<16>(Ls, wave, lane);
+  doubling_level<32>(Ls, wave, lane);
+  doubling_level<64>(Ls, wave, lane);
   static_assert(NB == 128, "three doubling levels");
 
   if (vec) {
-    // whole rows of the block: the entries above the diagonal are the zeros
-    // X already holds there
+    // whole rows of the block, zeros above the diagonal
 #pragma unroll
     for (int u = 0; u < NB * NB / 4 / LEAF_THREADS; ++u) {
       const int e = tid + LEAF_THREADS * u, i = e / (NB / 4), j = 4 * (e % (NB / 4));
-      *reinterpret_cast<float4*>(X + (off + i) * n + off + j) =
-          *reinterpret_cast<const float4*>(Xs + i * LP + j);
+      float4 v;
+      v.x = j + 0 <= i ? Ls[(j + 0) * LP + i] : 0.0f;
+      v.y = j + 1 <= i ? Ls[(j + 1) * LP + i] : 0.0f;
+      v.z = j + 2 <= i ? Ls[(j + 2) * LP + i] : 0.0f;
+      v.w = j + 3 <= i ? Ls[(j + 3) * LP + i] : 0.0f;
+      *reinterpret_cast<float4*>(X + (off + i) * n + off + j) = v;
     }
   } else {
     for (int i = tid / NB; i < m; i += LEAF_THREADS / NB) {
       const int j = tid % NB;
-      if (j <= i) X[(off + i) * n + off + j] = Xs[i * LP + j];
+      if (j <= i) X[(off + i) * n + off + j] = Ls[j * LP + i];
     }
   }
 }
