@@ -15,12 +15,15 @@
 //     of 16 queries; key blocks of 64 are staged in LDS (double-buffered)
 //     and walked with an online softmax; under the causal mask a wave skips
 //     the 16-key tiles past its last query.  The matrix cores compute
-//     S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x16_f16: in that
-//     orientation the S^T accumulator of a lane (query l % 16, keys
-//     4 (l / 16) + 0..3 of a 16-key slice) is exactly its B operand for the
-//     second product, and the O^T accumulator of a lane belongs to the same
-//     query as the softmax statistics the lane holds, so nothing is moved
-//     between lanes except the max / sum reductions over keys.
+//     S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_f16 (gfx950's
+//     full-rate 16 x 16 fp16 product; k slot j of lane group g pairs A and B
+//     alike): in that orientation the S^T accumulator of a lane (query
+//     l % 16, keys 4 (l / 16) + 0..3 of a 16-key tile) is exactly its part of
+//     the B operand of the second product (two tiles per product: k slots
+//     0..3 the first, 4..7 the second), and the O^T accumulator of a lane
+//     belongs to the same query as the softmax statistics the lane holds, so
+//     nothing is moved between lanes except the max / sum reductions over
+//     keys.
 //
 //   residual_rmsnorm_kernel: Hs = X + A (the residual stream, fp16) and
 //     U = Hs / sqrt(mean(Hs^2) + eps) * gamma (fp16), one row per workgroup.
@@ -32,6 +35,7 @@ namespace gptq {
 namespace {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
@@ -39,8 +43,11 @@ constexpr int AW = 8;         // waves per workgroup
 constexpr int AQ = 16 * AW;   // queries per workgroup (16 per wave)
 constexpr int AK = 64;        // keys per staged block
 
-__device__ inline float4_t mfma16(half4_t a, half4_t b, float4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+__device__ inline float4_t mfma16(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ inline half8_t cat8(half4_t lo, half4_t hi) {
+  return (half8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // ds_read_b64_tr_b16: in each 16-lane group, lane j receives element j % 4
@@ -54,14 +61,28 @@ __device__ inline half4_t ds_read_tr16(const _Float16* p) {
   return __builtin_bit_cast(half4_t, v);
 }
 
-// Max / sum over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48).
+// Max / sum over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48),
+// with gfx950's row swaps: v_permlane16_swap of a register with itself
+// leaves lane l's value in one result and lane l ^ 16's in the other (which
+// one depends on the row), so a symmetric operation on the two is the pair's
+// reduction; v_permlane32_swap likewise for l ^ 32.  (VALU only; a shuffle
+// through ds_bpermute put an LDS round trip on the softmax's critical path.)
+__device__ inline float vmax(float a, float b) { return __builtin_fmaxf(a, b); }
 __device__ inline float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return vmax(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 __device__ inline float group4_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 // Grid: (ceil(seq_len / 128), heads, seqs); 512 threads.  Q, K, V, O rows are
@@ -79,6 +100,7 @@ attn_fwd_kernel(const _Float16* __restrict__ Q, int64_t ldq, const _Float16* __r
                 int causal) {
   constexpr int KP = HD + 8, VP = HD + 16;
   constexpr int NS = HD / 16;                      // 16-wide slices of the head dimension
+  constexpr int NS2 = HD / 32;                     // 32-wide slices (k of the S^T product)
   constexpr int CH = AK * HD / 8;                  // 16-byte chunks of a K (or V) block
   constexpr int PT = CH / (AW * 64);               // chunks per thread
   static_assert(CH % (AW * 64) == 0, "whole chunks per thread");
@@ -94,15 +116,16 @@ attn_fwd_kernel(const _Float16* __restrict__ Q, int64_t ldq, const _Float16* __r
   const int qw = qw0 + (lane & 15);                         // this lane's query
   const int g = lane >> 4, kq = 4 * g;                      // lane group, its 4-slot offset
 
-  // Q^T as B operands, one per 16-wide slice: (query qw, dims 16 s + kq ..).
-  half4_t qf[NS];
+  // Q^T as B operands, one per 32-wide slice: (query qw, dims 32 s + 8 g ..).
+  half8_t qf[NS2];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
+  for (int s = 0; s < NS2; ++s) {
     if (qw < seq_len) {
-      const uint2 v = *reinterpret_cast<const uint2*>(Q + (tok0 + qw) * ldq + h * HD + 16 * s + kq);
-      qf[s] = __builtin_bit_cast(half4_t, v);
+      const uint4 v =
+          *reinterpret_cast<const uint4*>(Q + (tok0 + qw) * ldq + h * HD + 32 * s + 8 * g);
+      qf[s] = __builtin_bit_cast(half8_t, v);
     } else {
-      qf[s] = (half4_t){0, 0, 0, 0};
+      qf[s] = (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
   float4_t oacc[NS];
@@ -156,28 +179,39 @@ attn_fwd_kernel(const _Float16* __restrict__ Q, int64_t ldq, const _Float16* __r
         sacc[t] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
         if (t < nt) {
 #pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            const half4_t kf = __builtin_bit_cast(
-                half4_t, *reinterpret_cast<const uint2*>(&ks[(16 * t + (lane & 15)) * KP + 16 * s + kq]));
+          for (int s = 0; s < NS2; ++s) {
+            const half8_t kf = __builtin_bit_cast(
+                half8_t,
+                *reinterpret_cast<const uint4*>(&ks[(16 * t + (lane & 15)) * KP + 32 * s + 8 * g]));
             sacc[t] = mfma16(kf, qf[s], sacc[t]);
           }
         }
       }
-      // mask (causal, past the sequence, tiles not computed), block max
+      // mask (causal, past the sequence, tiles not computed) where the block
+      // is not wholly visible to every query of the wave; block max
+      const bool whole = kb + AK <= seq_len && (!causal || kb + AK - 1 <= qw0);  // uniform
       float bmax = -INFINITY;
+      if (!whole) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb + 16 * t + kq + i;
+            const bool ok = t < nt && key < seq_len && (!causal || key <= qw);
+            sacc[t][i] = ok ? sacc[t][i] : -INFINITY;
+          }
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb + 16 * t + kq + i;
-          const bool ok = t < nt && key < seq_len && (!causal || key <= qw);
-          sacc[t][i] = ok ? sacc[t][i] : -INFINITY;
-          bmax = fmaxf(bmax, sacc[t][i]);
-        }
+        for (int i = 0; i < 4; ++i) bmax = vmax(bmax, sacc[t][i]);
       bmax = group4_max(bmax);
-      const float mnew = fmaxf(m, bmax);
+      const float mnew = vmax(m, bmax);
       const float mref = mnew == -INFINITY ? 0.0f : mnew;   // a query with no key yet
-      const float alpha = exp2f((m - mref) * scale_log2e);  // exp2(-inf) = 0 on the first block
+      // v_exp_f32 directly (exp2(-inf) = 0 on the first block; results below
+      // 2^-126 flush to zero, which the sums cannot feel)
+      const float alpha = __builtin_amdgcn_exp2f((m - mref) * scale_log2e);
+      const float mc = mref * scale_log2e;
       float psum = 0.0f;
       half4_t pf[4];
 #pragma unroll
@@ -185,24 +219,31 @@ attn_fwd_kernel(const _Float16* __restrict__ Q, int64_t ldq, const _Float16* __r
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = exp2f((sacc[t][i] - mref) * scale_log2e);
+          p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[t][i], scale_log2e, -mc));
           psum += p[i];
         }
         pf[t] = (half4_t){(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
       }
       l = alpha * l + group4_sum(psum);
       m = mnew;
-      // O^T (HD x 16 queries) = alpha O^T + V^T P^T; the A operand (dims 16 s + j,
-      // keys 16 t + kq ..) from row-major V by transposing reads
+      // the running maximum rarely moves after the first blocks: rescale O
+      // only when it did for some query of the wave
+      const bool rescale = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
+      // O^T (HD x 16 queries) = alpha O^T + V^T P^T, 32 keys (tiles 2u, 2u + 1)
+      // per product; the A operand (dims 16 s + j, keys 16 t + kq ..) from
+      // row-major V by transposing reads.  A tile past the wave's last one
+      // (odd nt) has P = 0.
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        float4_t o = oacc[s] * alpha;
+        float4_t o = rescale ? oacc[s] * alpha : oacc[s];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (t < nt) {
-            const half4_t vf =
-                ds_read_tr16(&vs[(16 * t + kq + ((lane & 15) >> 2)) * VP + 16 * s + 4 * (lane & 3)]);
-            o = mfma16(vf, pf[t], o);
+        for (int u = 0; u < 2; ++u) {
+          if (2 * u < nt) {
+            const half4_t v0 = ds_read_tr16(
+                &vs[(32 * u + kq + ((lane & 15) >> 2)) * VP + 16 * s + 4 * (lane & 3)]);
+            const half4_t v1 = ds_read_tr16(
+                &vs[(32 * u + 16 + kq + ((lane & 15) >> 2)) * VP + 16 * s + 4 * (lane & 3)]);
+            o = mfma16(cat8(v0, v1), cat8(pf[2 * u], pf[2 * u + 1]), o);
           }
         }
         oacc[s] = o;
