@@ -85,11 +85,6 @@ struct GemmArgs {
   // resolved down to ~2^-24 absolute).  Used only where the operands are
   // scaled to that range; falls back to fp32 MFMAs on unaligned shapes.
   bool split16 = false;
-  // With split16: optional per-row powers of two for op(A) (length M).  Row i
-  // of op(A) is multiplied by row_scale[i] before the split and row i of the
-  // product by 1 / row_scale[i] after it (exact), so rows of very different
-  // magnitude each keep full relative precision.
-  const float* row_scale = nullptr;
 };
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 // Error-update GEMM of the column sweep on the errors the sweep stored split:

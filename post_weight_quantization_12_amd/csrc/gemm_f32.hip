@@ -299,8 +299,7 @@ template <int BM, int BN, int NS, bool TA, bool TB, bool X3>
 __global__ void __launch_bounds__(256)
 gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
              const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
-             float alpha, float beta, int kmode, int lower_only, int tiles_n,
-             const float* __restrict__ row_scale) {
+             float alpha, float beta, int kmode, int lower_only, int tiles_n) {
   constexpr bool AKC = !TA, BKC = TB;  // k-contiguous in memory
   using TA_ = OpTile<BM, AKC>;
   using TB_ = OpTile<BN, BKC>;
@@ -375,13 +374,6 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
       for (int v = 0; v < 16; ++v) acc[a][c][v] = 0.0f;
 
   const int h = lane >> 5;
-  // Per-row scale of this lane's A fragment rows (X3 with row_scale only).
-  float rsa[FM];
-#pragma unroll
-  for (int a = 0; a < FM; ++a) {
-    const int64_t r = i0 + wm * (BM / 2) + a * 32 + (lane & 31);
-    rsa[a] = (X3 && row_scale != nullptr && r < M) ? row_scale[r] : 1.0f;
-  }
   auto compute = [&](const float* stage) __device__ __attribute__((always_inline)) {
     float av[FM][16], bv[FN][16];
 #pragma unroll
@@ -403,11 +395,7 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
       // k-step q (16 k) takes this lane's values 8q..8q+7 (k = 16h + 8q + e).
       half8_t ah[FM][2], al[FM][2], bh[FN][2], bl[FN][2];
 #pragma unroll
-      for (int a = 0; a < FM; ++a) {
-#pragma unroll
-        for (int u = 0; u < 16; ++u) av[a][u] *= rsa[a];
-        split16(av[a], ah[a], al[a]);
-      }
+      for (int a = 0; a < FM; ++a) split16(av[a], ah[a], al[a]);
 #pragma unroll
       for (int c = 0; c < FN; ++c) split16(bv[c], bh[c], bl[c]);
 #pragma unroll
@@ -460,12 +448,6 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
   const bool rd = beta != 0.0f;
 #pragma unroll
   for (int a = 0; a < FM; ++a) {
-    float ralpha[16];  // alpha / row_scale of each accumulator row
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t r = i0 + wm * (BM / 2) + a * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-      ralpha[v] = (X3 && row_scale != nullptr && r < M) ? alpha / row_scale[r] : alpha;
-    }
 #pragma unroll
     for (int c = 0; c < FN; ++c) {
       const int jl = wn * (BN / 2) + c * 32 + (lane & 31);
@@ -481,7 +463,7 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float r = ralpha[v] * acc[a][c][v];
+        const float r = alpha * acc[a][c][v];
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(rd ? r + beta * cv[v] : r), rc,
                                               (int)off[v], 0, 0);
       }
@@ -764,7 +746,7 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
   const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
   hipLaunchKernelGGL((gemm_f32_dma<BM, BN, NS, TA, TB, X3>), dim3((unsigned)(tm * tn)), dim3(256),
                      0, s, g.M, g.N, g.K, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, g.alpha, g.beta,
-                     g.kmode, (int)g.lower_only, (int)tn, g.row_scale);
+                     g.kmode, (int)g.lower_only, (int)tn);
   return hipGetLastError();
 }
 
