@@ -980,7 +980,14 @@ hipError_t process(QCtx& c, int64_t a, int64_t b) {
   if (b - a <= B) return sweep_block(c, a, b);
   if (b - a == 2 * B && pair_fits(c)) return sweep_pair(c, a);
   const int64_t nblk = (b - a + B - 1) / B;
-  const int64_t m = a + B * ((nblk + 1) / 2);
+  // Where the pair kernel applies, split on pair boundaries (the left part
+  // an even number of blocks), so the leaves are pairs wherever the block
+  // count allows and single blocks stay rare; else halve by blocks.
+  int64_t m = a + B * ((nblk + 1) / 2);
+  if (pair_fits(c)) {
+    const int64_t mp = a + 2 * B * (((nblk + 1) / 2 + 1) / 2);
+    if (mp < b) m = mp;
+  }
   GPTQ_HIP_TRY(process(c, a, m));
   const bool three = m - a < SPLIT_MIN_K || c.in > TWO_PRODUCT_MAX_IN;
   GPTQ_HIP_TRY(launch_gemm_eh(c.out, b - m, m - a, c.Wp + a, c.in, c.Vt + m * c.in + a,
