@@ -438,7 +438,8 @@ STAGES = [
 
 def sweep_pairs(cfg):
     """Pairs of adjacent full 128-column blocks the quantize recursion sweeps
-    in one kernel (both halves of a two-block range), for this layer."""
+    in one kernel (both halves of a two-block range; the recursion splits on
+    pair boundaries), for this layer."""
     B, n = cfg.block, cfg.inp
     gs = cfg.group_size if cfg.group_size > 0 else 0
     if B != 128 or gs not in (0, 16, 32, 64, 128) or n <= B:
@@ -451,6 +452,9 @@ def sweep_pairs(cfg):
             return 1
         nblk = (b - a + B - 1) // B
         m = a + B * ((nblk + 1) // 2)
+        mp = a + 2 * B * (((nblk + 1) // 2 + 1) // 2)  # split on pair boundaries
+        if mp < b:
+            m = mp
         return rec(a, m) + rec(m, b)
     return rec(0, n)
 
