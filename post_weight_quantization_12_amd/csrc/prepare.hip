@@ -122,32 +122,27 @@ __global__ void rank_scatter_kernel(const int32_t* __restrict__ rank, int64_t n,
 }
 
 // S = H with the lower triangle mirrored from the upper (S fully symmetric).
+// Grid: (nb, nb) 64 x 64 tiles, the workgroups of tiles below the diagonal
+// exit at once; tile (bi, bj), bi <= bj, of H's upper part is read once
+// (coalesced) and written twice: as is, and transposed through LDS into tile
+// (bj, bi) (a diagonal tile mirrors its own upper part).
+constexpr int SYM_T = 64;
 __global__ void __launch_bounds__(256)
 symmetrize_kernel(const float* __restrict__ H, int64_t n, float* __restrict__ S) {
-  __shared__ float t[32][33];
+  __shared__ float t[SYM_T][SYM_T + 1];
   const int64_t bi = blockIdx.y, bj = blockIdx.x;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  if (bi < bj) {
-    for (int r = ty; r < 32; r += 8) {
-      const int64_t i = bi * 32 + r, j = bj * 32 + tx;
-      if (i < n && j < n) S[i * n + j] = H[i * n + j];
-    }
-    return;
-  }
-  // Tile (bj, bi) of H's upper part, read coalesced, written transposed.
-  for (int r = ty; r < 32; r += 8) {
-    const int64_t i = bj * 32 + r, j = bi * 32 + tx;
-    t[r][tx] = (i < n && j < n) ? H[i * n + j] : 0.0f;
+  if (bi > bj) return;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
+  for (int r = ty; r < SYM_T; r += 4) {
+    const int64_t i = bi * SYM_T + r, j = bj * SYM_T + tx;
+    const float v = (i < n && j < n) ? H[i * n + j] : 0.0f;
+    t[r][tx] = v;
+    if (bi < bj && i < n && j < n) S[i * n + j] = v;
   }
   __syncthreads();
-  for (int r = ty; r < 32; r += 8) {
-    const int64_t i = bi * 32 + r, j = bj * 32 + tx;
-    if (i < n && j < n) {
-      float v;
-      if (bi > bj) v = t[tx][r];
-      else v = (r <= tx) ? t[r][tx] : t[tx][r];  // diagonal tile: upper as is, lower mirrored
-      S[i * n + j] = v;
-    }
+  for (int r = ty; r < SYM_T; r += 4) {
+    const int64_t i = bj * SYM_T + r, j = bi * SYM_T + tx;
+    if (i < n && j < n) S[i * n + j] = (bi < bj || r > tx) ? t[tx][r] : t[r][tx];
   }
 }
 
@@ -892,8 +887,8 @@ hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, floa
   GPTQ_HIP_TRY(hipGetLastError());
   // S (symmetric H) is staged in the output buffer, gathered into A, then the
   // output buffer is cleared and receives L^-1.
-  const unsigned nb32 = (unsigned)((n + 31) / 32);
-  hipLaunchKernelGGL(symmetrize_kernel, dim3(nb32, nb32), dim3(256), 0, s, H, n, U);
+  const unsigned nbs = (unsigned)((n + SYM_T - 1) / SYM_T);
+  hipLaunchKernelGGL(symmetrize_kernel, dim3(nbs, nbs), dim3(256), 0, s, H, n, U);
   GPTQ_HIP_TRY(hipGetLastError());
   const size_t lds = (size_t)n * sizeof(float);
   GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)gather_kernel,

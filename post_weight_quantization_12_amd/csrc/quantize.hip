@@ -411,23 +411,22 @@ sweep_kernel(float* __restrict__ Wp, const float* __restrict__ Ub, int64_t out, 
 }
 
 // qweight[u*bits + t][r]: word t of the 32-code unit u of row r (original
-// column order).  A workgroup stages pinv and R rows of codes (quantization
-// order) in LDS, then packs (unit, row) pairs with the R rows of a unit on
-// neighbouring threads, so the permuted reads hit LDS and the word stores of
-// a unit cover R consecutive rows.
+// column order).  A workgroup stages R rows of codes (quantization order) in
+// LDS, rows PACK_PAD bytes longer than the codes so that the R rows of a
+// column fall in different LDS banks, then packs (unit, row) pairs with the R
+// rows of a unit on neighbouring threads: each thread takes its unit's 32
+// pinv entries from memory (the R threads of a unit read the same 128 bytes),
+// the permuted code reads hit LDS, and the word stores of a unit cover R
+// consecutive rows.
+constexpr int PACK_PAD = 16;
 __global__ void __launch_bounds__(256)
 pack_kernel(const uint8_t* __restrict__ codes, const int32_t* __restrict__ pinv, int64_t out,
             int64_t in, int bits, int R, int32_t* __restrict__ qweight) {
-  extern __shared__ __align__(16) uint8_t psm[];
-  int32_t* pl = reinterpret_cast<int32_t*>(psm);
-  uint8_t* cl = psm + in * sizeof(int32_t);
+  extern __shared__ __align__(16) uint8_t cl[];
+  const int64_t cp = in + PACK_PAD;  // LDS row pitch (16-byte aligned: in is a multiple of 32)
   const int64_t r0 = (int64_t)blockIdx.x * R;
   const int rows = (int)(out - r0 < R ? out - r0 : R);
-  for (int64_t j = threadIdx.x; j < in; j += blockDim.x) {
-    int32_t p = pinv[j];
-    pl[j] = (uint32_t)p < (uint32_t)in ? p : 0;  // never read outside the row
-  }
-  const int64_t v16 = in / 16;  // in is a multiple of 32
+  const int64_t v16 = in / 16;
   for (int64_t e0 = threadIdx.x; e0 < rows * v16; e0 += 4 * (int64_t)blockDim.x) {
     uint4 v[4];
 #pragma unroll
@@ -439,7 +438,8 @@ pack_kernel(const uint8_t* __restrict__ codes, const int32_t* __restrict__ pinv,
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t e = e0 + u * (int64_t)blockDim.x;
-      if (e < rows * v16) *reinterpret_cast<uint4*>(cl + e * 16) = v[u];
+      if (e < rows * v16)
+        *reinterpret_cast<uint4*>(cl + (e / v16) * cp + (e % v16) * 16) = v[u];
     }
   }
   __syncthreads();
@@ -448,13 +448,19 @@ pack_kernel(const uint8_t* __restrict__ codes, const int32_t* __restrict__ pinv,
     const int64_t u = t / R;
     const int rr = (int)(t % R);
     if (rr >= rows) continue;
-    const uint8_t* crow = cl + (int64_t)rr * in;
-    const int32_t* pu = pl + u * 32;
+    int32_t pu[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int4 v = *reinterpret_cast<const int4*>(pinv + u * 32 + 4 * q);
+      pu[4 * q + 0] = v.x; pu[4 * q + 1] = v.y; pu[4 * q + 2] = v.z; pu[4 * q + 3] = v.w;
+    }
+    const uint8_t* crow = cl + (int64_t)rr * cp;
     uint64_t acc = 0;
     int nb = 0, w = 0;
 #pragma unroll
     for (int c = 0; c < 32; ++c) {
-      acc |= (uint64_t)crow[pu[c]] << nb;
+      const int32_t p = (uint32_t)pu[c] < (uint32_t)in ? pu[c] : 0;  // never read outside the row
+      acc |= (uint64_t)crow[p] << nb;
       nb += bits;
       if (nb >= 32) {
         qweight[(u * bits + w) * out + r0 + rr] = (int32_t)(uint32_t)acc;
@@ -1073,10 +1079,12 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
   QCtx c{l.Wp, l.Ub, l.Vt, l.Vl, out, in, bits, gs, sym, block, scales, zeros, l.codes, l.einv,
          s};
   GPTQ_HIP_TRY(process(c, 0, in));
-  // rows per packing workgroup: as many (up to 16) as fit next to pinv in 160 KiB of LDS
-  int R = 16;
-  while (R > 1 && (size_t)in * (4 + R) > 160 * 1024) R /= 2;
-  const size_t plds = (size_t)in * (4 + R);
+  // rows per packing workgroup: 4 (several workgroups per compute unit to
+  // cover the latency of the per-unit pinv reads; 16 rows per workgroup
+  // took 117 us against 99 at 4096 x 11008), fewer if 4 rows do not fit
+  int R = 4;
+  while (R > 1 && (size_t)R * (in + PACK_PAD) > 160 * 1024) --R;
+  const size_t plds = (size_t)R * (in + PACK_PAD);
   GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)pack_kernel,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds));
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((out + R - 1) / R)), dim3(256), plds, s, l.codes,
