@@ -163,8 +163,10 @@ __global__ void scale_kernel(const float* __restrict__ H, int64_t n,
 }
 
 // A[a][b] (b <= a) = dsc[a] dsc[b] S[q(a)][q(b)] with q(a) = perm[n-1-a];
-// diagonal: dead fix + damp before scaling.
-__global__ void __launch_bounds__(256)
+// diagonal: dead fix + damp before scaling.  256 threads, or 1024 where the
+// staged row leaves room for at most two workgroups per compute unit (n above
+// 16384), so that enough loads are in flight.
+__global__ void __launch_bounds__(1024)
 gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict__ perm,
               const float* __restrict__ damp_add, const float* __restrict__ dsc,
               float* __restrict__ A) {
@@ -172,7 +174,7 @@ gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict_
   const int64_t a = blockIdx.x;
   const int64_t src = perm[n - 1 - a];
   // Stage the source row, 4 float4 loads per thread in flight.
-  if ((n & 3) == 0) {
+  if (((n & 3) | (reinterpret_cast<uintptr_t>(S) & 15)) == 0) {
     const float4* s4 = reinterpret_cast<const float4*>(S + src * n);
     float4* r4 = reinterpret_cast<float4*>(row);
     const int64_t n4 = n / 4;
@@ -614,22 +616,64 @@ cholinv_leaf_kernel(const float* __restrict__ A, float* __restrict__ X, int64_t 
 // X = X' D (column b of the computed X' times dsc[b]).  X' is lower
 // triangular, so every strictly lower (a, b) moves to the strictly upper
 // (n-1-a, n-1-b) (which holds 0) and diagonal entries swap in pairs.
+// Workgroup r takes the source rows r and c = n-1-r: the strictly lower part
+// of each lands in the strictly upper part of the other, so the two rows
+// hold n-1 moved entries together (every workgroup the same work) and no
+// other workgroup touches them; the diagonal pair (r, r), (c, c) is swapped
+// by one thread.  For n a multiple of 4 the whole 4-column chunks left of
+// the diagonal move as 16-byte loads and stores when U and dsc are 16-byte
+// aligned (chunk k of row a lands, reversed, in chunk n/4-1-k of row n-1-a),
+// four chunks per thread in flight; the rest column by column.
 __global__ void __launch_bounds__(256)
 reverse_inplace_kernel(float* __restrict__ U, int64_t n, const float* __restrict__ dsc) {
-  const int64_t a = blockIdx.y;  // source row
-  for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b <= a;
-       b += (int64_t)gridDim.x * blockDim.x) {
-    if (b < a) {
-      const float v = U[a * n + b] * dsc[b];
-      U[(n - 1 - a) * n + (n - 1 - b)] = v;
-      U[a * n + b] = 0.0f;
-    } else if (a < n - 1 - a) {
-      const int64_t c = n - 1 - a;
-      const float v = U[a * n + a] * dsc[a];
-      U[a * n + a] = U[c * n + c] * dsc[c];
+  const int64_t r = blockIdx.x, c = n - 1 - r;
+  if (r > c) return;
+  for (int side = 0; side < (r < c ? 2 : 1); ++side) {
+    const int64_t a = side ? c : r;
+    float* __restrict__ src = U + a * n;
+    float* __restrict__ dst = U + (n - 1 - a) * n;
+    int64_t b0 = 0;
+    if (((n & 3) | (reinterpret_cast<uintptr_t>(U) & 15) | (reinterpret_cast<uintptr_t>(dsc) & 15)) ==
+        0) {
+      const int64_t full = a >> 2, n4 = n >> 2;  // chunks k with 4k + 3 < a
+      float4* s4 = reinterpret_cast<float4*>(src);
+      float4* d4 = reinterpret_cast<float4*>(dst);
+      const float4* c4 = reinterpret_cast<const float4*>(dsc);
+      for (int64_t k0 = threadIdx.x; k0 < full; k0 += 4 * (int64_t)blockDim.x) {
+        float4 v[4], sc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t k = k0 + u * (int64_t)blockDim.x;
+          if (k < full) {
+            v[u] = s4[k];
+            sc[u] = c4[k];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t k = k0 + u * (int64_t)blockDim.x;
+          if (k < full) {
+            d4[n4 - 1 - k] = make_float4(v[u].w * sc[u].w, v[u].z * sc[u].z, v[u].y * sc[u].y,
+                                         v[u].x * sc[u].x);
+            s4[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          }
+        }
+      }
+      b0 = full << 2;
+    }
+    for (int64_t b = b0 + threadIdx.x; b < a; b += blockDim.x) {
+      const float v = src[b] * dsc[b];
+      dst[n - 1 - b] = v;
+      src[b] = 0.0f;
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (r < c) {
+      const float v = U[r * n + r] * dsc[r];
+      U[r * n + r] = U[c * n + c] * dsc[c];
       U[c * n + c] = v;
-    } else if (a == n - 1 - a) {
-      U[a * n + a] *= dsc[a];
+    } else {
+      U[r * n + r] *= dsc[r];
     }
   }
 }
@@ -896,15 +940,15 @@ hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, floa
   hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, H, n, perm,
                      l.damp_add, l.dsc);
   GPTQ_HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)n), dim3(256), lds, s, U, n, perm, l.damp_add,
-                     l.dsc, l.A);
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)n), dim3(lds > 64 * 1024 ? 1024 : 256), lds, s, U,
+                     n, perm, l.damp_add, l.dsc, l.A);
   GPTQ_HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(fill_f32_kernel, dim3(2048), dim3(256), 0, s, U, n * n, 0.0f);
   GPTQ_HIP_TRY(hipGetLastError());
   PrepCtx c{l.A, U, l.T, l.T2, n, info, s};
   GPTQ_HIP_TRY(cholinv_blocked(c, l.TB));
-  const unsigned gx = (unsigned)((n + 255) / 256);
-  hipLaunchKernelGGL(reverse_inplace_kernel, dim3(gx, (unsigned)n), dim3(256), 0, s, U, n, l.dsc);
+  hipLaunchKernelGGL(reverse_inplace_kernel, dim3((unsigned)((n + 1) / 2)), dim3(256), 0, s, U, n,
+                     l.dsc);
   return hipGetLastError();
 }
 
