@@ -114,9 +114,12 @@ __device__ inline float to_f32<_Float16>(_Float16 v) { return (float)v; }
 template <>
 __device__ inline float to_f32<uint16_t>(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// Wp[r][j] = W[r][perm[j]] as fp32 (perm == nullptr: identity).
+// Wp[r][j] = W[r][perm[j]] as fp32 (perm == nullptr: identity).  256
+// threads, or 1024 where the staged row leaves room for at most two
+// workgroups per compute unit (in above 16384), so that enough loads are in
+// flight.
 template <typename T>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(1024)
 gather_w_kernel(const T* __restrict__ W, int64_t out, int64_t in, const int32_t* __restrict__ perm,
                 float* __restrict__ Wp) {
   extern __shared__ __align__(16) float rowbuf[];
@@ -1042,23 +1045,24 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                         void* ws, hipStream_t s) {
   QLayout l = carve(ws, out, in, block);
   const size_t lds = (size_t)in * sizeof(float);
+  const unsigned gw_threads = lds > 64 * 1024 ? 1024 : 256;
   if (wdtype == 0) {
     auto k = gather_w_kernel<_Float16>;
     GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds));
-    hipLaunchKernelGGL(k, dim3((unsigned)out), dim3(256), lds, s,
+    hipLaunchKernelGGL(k, dim3((unsigned)out), dim3(gw_threads), lds, s,
                        static_cast<const _Float16*>(W), out, in, perm, l.Wp);
   } else if (wdtype == 1) {
     auto k = gather_w_kernel<uint16_t>;
     GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds));
-    hipLaunchKernelGGL(k, dim3((unsigned)out), dim3(256), lds, s,
+    hipLaunchKernelGGL(k, dim3((unsigned)out), dim3(gw_threads), lds, s,
                        static_cast<const uint16_t*>(W), out, in, perm, l.Wp);
   } else {
     auto k = gather_w_kernel<float>;
     GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds));
-    hipLaunchKernelGGL(k, dim3((unsigned)out), dim3(256), lds, s, static_cast<const float*>(W),
+    hipLaunchKernelGGL(k, dim3((unsigned)out), dim3(gw_threads), lds, s, static_cast<const float*>(W),
                        out, in, perm, l.Wp);
   }
   GPTQ_HIP_TRY(hipGetLastError());
