@@ -185,6 +185,9 @@ gather_w_kernel(const T* __restrict__ W, int64_t out, int64_t in, const int32_t*
 // 64 x 64 tiles of U through LDS; tiles below the diagonal exit (the parts
 // of a diagonal block they cover are never read: a sweep row's window
 // starts at most 15 columns left of its diagonal, inside the same tile).
+// Whole tiles with 16-byte aligned rows move 4 columns per access (16-byte
+// loads of U and stores of Ub, 8-byte stores of Vt and Vl); ragged or
+// unaligned tiles element by element.  Both give the same values.
 __global__ void __launch_bounds__(256)
 uprime_split_kernel(const float* __restrict__ U, int64_t n, int B, float* __restrict__ Ub,
                     _Float16* __restrict__ Vt, _Float16* __restrict__ Vl) {
@@ -198,22 +201,75 @@ uprime_split_kernel(const float* __restrict__ U, int64_t n, int B, float* __rest
     dg[threadIdx.x] = r < n ? U[r * n + r] : 1.0f;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    if (r >= n || c >= n) continue;
-    const float v = r < c ? U[r * n + c] / dg[i] : 0.0f;
-    tile[i][tx] = v;
-    if (r / B == c / B) Ub[(r / B) * B * B + (r % B) * B + (c % B)] = v;
+  const bool vec = (n & 3) == 0 && c0 + 64 <= n &&
+                   ((reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(Ub)) & 15) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(Vt) | reinterpret_cast<uintptr_t>(Vl)) & 7) == 0;
+  const int q4 = 4 * (threadIdx.x & 15), g = threadIdx.x >> 4;  // 16 x 16 threads
+  if (vec) {
+    // rows g, g + 16, ...; columns q4 .. q4 + 3 (r0 + 64 <= c0 + 64 <= n)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = g + 16 * u;
+      const int64_t r = r0 + i, c = c0 + q4;
+      const float4 x = *reinterpret_cast<const float4*>(U + r * n + c);
+      const float d = dg[i];
+      float4 v;
+      v.x = r < c ? x.x / d : 0.0f;
+      v.y = r < c + 1 ? x.y / d : 0.0f;
+      v.z = r < c + 2 ? x.z / d : 0.0f;
+      v.w = r < c + 3 ? x.w / d : 0.0f;
+      tile[i][q4] = v.x;
+      tile[i][q4 + 1] = v.y;
+      tile[i][q4 + 2] = v.z;
+      tile[i][q4 + 3] = v.w;
+      if (r / B == c / B)  // B is a multiple of 4: the chunk lies in one block
+        *reinterpret_cast<float4*>(Ub + (r / B) * B * B + (r % B) * B + (c % B)) = v;
+    }
+  } else {
+    for (int i = ty; i < 64; i += 4) {
+      const int64_t r = r0 + i, c = c0 + tx;
+      if (r >= n || c >= n) continue;
+      const float v = r < c ? U[r * n + c] / dg[i] : 0.0f;
+      tile[i][tx] = v;
+      if (r / B == c / B) Ub[(r / B) * B * B + (r % B) * B + (c % B)] = v;
+    }
   }
   __syncthreads();
   if (Vt == nullptr) return;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < n && r < n && r < c) {
-      const float u = tile[tx][i];
-      const _Float16 hi = (_Float16)u;
-      Vt[c * n + r] = hi;
-      Vl[c * n + r] = __builtin_amdgcn_cvt_pkrtz(u - (float)hi, 0.0f)[0];
+  if (vec) {
+    // Vt[c][r .. r + 3] for c = c0 + g + 16u, r = r0 + q4
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = g + 16 * u;
+      const int64_t c = c0 + i, r = r0 + q4;
+      if (r + 3 < c) {
+        _Float16 hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = tile[q4 + e][i];
+          hi[e] = (_Float16)x;
+          lo[e] = __builtin_amdgcn_cvt_pkrtz(x - (float)hi[e], 0.0f)[0];
+        }
+        *reinterpret_cast<uint2*>(Vt + c * n + r) = *reinterpret_cast<const uint2*>(hi);
+        *reinterpret_cast<uint2*>(Vl + c * n + r) = *reinterpret_cast<const uint2*>(lo);
+      } else {
+        for (int e = 0; e < 4 && r + e < c; ++e) {
+          const float x = tile[q4 + e][i];
+          const _Float16 hi = (_Float16)x;
+          Vt[c * n + r + e] = hi;
+          Vl[c * n + r + e] = __builtin_amdgcn_cvt_pkrtz(x - (float)hi, 0.0f)[0];
+        }
+      }
+    }
+  } else {
+    for (int i = ty; i < 64; i += 4) {
+      const int64_t c = c0 + i, r = r0 + tx;
+      if (c < n && r < n && r < c) {
+        const float u = tile[tx][i];
+        const _Float16 hi = (_Float16)u;
+        Vt[c * n + r] = hi;
+        Vl[c * n + r] = __builtin_amdgcn_cvt_pkrtz(u - (float)hi, 0.0f)[0];
+      }
     }
   }
 }
