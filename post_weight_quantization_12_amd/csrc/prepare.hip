@@ -163,9 +163,10 @@ __global__ void scale_kernel(const float* __restrict__ H, int64_t n,
 }
 
 // A[a][b] (b <= a) = dsc[a] dsc[b] S[q(a)][q(b)] with q(a) = perm[n-1-a];
-// diagonal: dead fix + damp before scaling.  256 threads, or 1024 where the
-// staged row leaves room for at most two workgroups per compute unit (n above
-// 16384), so that enough loads are in flight.
+// diagonal: dead fix + damp before scaling.  256 threads; 512 where the
+// staged row leaves room for at most four workgroups per compute unit (n
+// above 8192), 1024 where it leaves room for at most two (n above 16384), so
+// that enough loads are in flight.
 __global__ void __launch_bounds__(1024)
 gather_kernel(const float* __restrict__ S, int64_t n, const int32_t* __restrict__ perm,
               const float* __restrict__ damp_add, const float* __restrict__ dsc,
@@ -940,7 +941,7 @@ hipError_t run_prepare(const float* H, int64_t n, float damp, int desc_act, floa
   hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, H, n, perm,
                      l.damp_add, l.dsc);
   GPTQ_HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)n), dim3(lds > 64 * 1024 ? 1024 : 256), lds, s, U,
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)n), dim3(lds > 64 * 1024 ? 1024 : lds > 32 * 1024 ? 512 : 256), lds, s, U,
                      n, perm, l.damp_add, l.dsc, l.A);
   GPTQ_HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(fill_f32_kernel, dim3(2048), dim3(256), 0, s, U, n * n, 0.0f);

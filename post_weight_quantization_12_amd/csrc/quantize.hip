@@ -115,9 +115,9 @@ template <>
 __device__ inline float to_f32<uint16_t>(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
 // Wp[r][j] = W[r][perm[j]] as fp32 (perm == nullptr: identity).  256
-// threads, or 1024 where the staged row leaves room for at most two
-// workgroups per compute unit (in above 16384), so that enough loads are in
-// flight.
+// threads; 512 where the staged row leaves room for at most four workgroups
+// per compute unit (in above 8192), 1024 where it leaves room for at most two
+// (in above 16384), so that enough loads are in flight.
 template <typename T>
 __global__ void __launch_bounds__(1024)
 gather_w_kernel(const T* __restrict__ W, int64_t out, int64_t in, const int32_t* __restrict__ perm,
@@ -1101,7 +1101,7 @@ hipError_t run_quantize(const void* W, int wdtype, int64_t out, int64_t in, cons
                         void* ws, hipStream_t s) {
   QLayout l = carve(ws, out, in, block);
   const size_t lds = (size_t)in * sizeof(float);
-  const unsigned gw_threads = lds > 64 * 1024 ? 1024 : 256;
+  const unsigned gw_threads = lds > 64 * 1024 ? 1024 : lds > 32 * 1024 ? 512 : 256;
   if (wdtype == 0) {
     auto k = gather_w_kernel<_Float16>;
     GPTQ_HIP_TRY(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
