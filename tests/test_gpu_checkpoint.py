@@ -30,7 +30,9 @@ def test_export_params_matches_oracle(G, out, bits):
     z = rng.integers(0, 2 ** bits, size=(G, out)).astype(np.int32)
     s16, qz = P.export_params(torch.from_numpy(sc).to(DEV), torch.from_numpy(z).to(DEV), bits)
     torch.cuda.synchronize()
-    assert np.array_equal(s16.cpu().numpy(), sc.astype(np.float16))
+    with np.errstate(over="ignore"):  # the planted out-of-range scale is meant to overflow
+        want = sc.astype(np.float16)
+    assert np.array_equal(s16.cpu().numpy(), want)
     assert np.array_equal(qz.cpu().numpy(), O.pack_zeros(z, bits))
     zb = P.unpack_zeros(qz, out, bits)
     torch.cuda.synchronize()
