@@ -87,6 +87,11 @@ struct GemmArgs {
   bool split16 = false;
 };
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
+// Two independent products (no operand of one is written by the other) in
+// one launch where both take the 64 x 64 split-fp16 tiles, the first with B
+// transposed and the second not (A not transposed in either); otherwise two
+// launches.  Each result is what launch_gemm_f32 gives.
+hipError_t launch_gemm_f32_pair(const GemmArgs& a, const GemmArgs& b, hipStream_t s);
 // Error-update GEMM of the column sweep on the errors the sweep stored split:
 //   C[M x N] -= sum over sweep blocks b (kb columns each) of
 //               einv[b][r] * (Ehi + Elo)_b (V + Vl)_b^T

@@ -295,27 +295,31 @@ __device__ __attribute__((always_inline)) inline void issue_stage(const char* ba
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GPTQ_LDS(lds + q * 256), 16, voff[q], 0, 0, 0);
 }
 
+// One workgroup's tile of a product: block b of the product's nb blocks,
+// the stage buffers st0..st2 (LDS objects of the calling kernel, one per
+// stage, STAGE floats each; st2 unused with two stages).
+template <int BM, int BN, bool TA, bool TB>
+struct DmaShape {
+  using TA_ = OpTile<BM, !TA>;
+  using TB_ = OpTile<BN, TB>;
+  static constexpr int STAGE = TA_::FLOATS + TB_::FLOATS;
+};
 template <int BM, int BN, int NS, bool TA, bool TB, bool X3>
-__global__ void __launch_bounds__(256)
-gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
-             const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
-             float alpha, float beta, int kmode, int lower_only, int tiles_n) {
+__device__ __attribute__((always_inline)) inline void gemm_f32_dma_tile(
+    int b, int nb, int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+    const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc, float alpha,
+    float beta, int kmode, int lower_only, int tiles_n, float* st0, float* st1, float* st2) {
   constexpr bool AKC = !TA, BKC = TB;  // k-contiguous in memory
   using TA_ = OpTile<BM, AKC>;
   using TB_ = OpTile<BN, BKC>;
   constexpr int FM = BM / 64, FN = BN / 64;
   constexpr int IPW = TA_::IPW + TB_::IPW;
-  constexpr int STAGE = TA_::FLOATS + TB_::FLOATS;
   static_assert(NS == 2 || NS == 3, "2 or 3 stages");
-  __shared__ __align__(16) float st0[STAGE];
-  __shared__ __align__(16) float st1[STAGE];
-  __shared__ __align__(16) float st2[NS == 3 ? STAGE : 4];
 
   // Tile order.  Full K: XCD-contiguous runs of the row-major order (blocks
   // are dispatched to the 8 XCDs round-robin, so neighbouring tiles share an
   // L2).  Triangular K ranges: the tiles with the most k go first (longest
   // processing time first), so the last wave is not a few long tiles.
-  const int nb = gridDim.x, b = blockIdx.x;
   const int tiles_m = nb / tiles_n;
   int ti, tj;
   if (kmode == KR_LE_COL) {
@@ -469,6 +473,52 @@ gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64
       }
     }
   }
+}
+
+template <int BM, int BN, int NS, bool TA, bool TB, bool X3>
+__global__ void __launch_bounds__(256)
+gemm_f32_dma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda,
+             const float* __restrict__ B, int64_t ldb, float* __restrict__ C, int64_t ldc,
+             float alpha, float beta, int kmode, int lower_only, int tiles_n) {
+  constexpr int STAGE = DmaShape<BM, BN, TA, TB>::STAGE;
+  __shared__ __align__(16) float st0[STAGE];
+  __shared__ __align__(16) float st1[STAGE];
+  __shared__ __align__(16) float st2[NS == 3 ? STAGE : 4];
+  gemm_f32_dma_tile<BM, BN, NS, TA, TB, X3>(blockIdx.x, gridDim.x, M, N, K, A, lda, B, ldb, C,
+                                            ldc, alpha, beta, kmode, lower_only, tiles_n, st0,
+                                            st1, st2);
+}
+
+// Two independent products in one launch (blocks [0, nb1) take the first,
+// the rest the second), both with A not transposed, sharing the stage
+// buffers; the first takes its B transposed, the second not.  Each block
+// computes exactly what it would in a launch of its own.
+struct DmaProblem {
+  int64_t M, N, K;
+  const float* A; int64_t lda;
+  const float* B; int64_t ldb;
+  float* C; int64_t ldc;
+  float alpha, beta;
+  int kmode, lower_only, tiles_n, nb;
+};
+template <int BM, int BN, int NS, bool X3>
+__global__ void __launch_bounds__(256)
+gemm_f32_dma_pair(DmaProblem p, DmaProblem q) {
+  constexpr int S1 = DmaShape<BM, BN, false, true>::STAGE, S2 = DmaShape<BM, BN, false, false>::STAGE;
+  constexpr int STAGE = S1 > S2 ? S1 : S2;
+  __shared__ __align__(16) float st0[STAGE];
+  __shared__ __align__(16) float st1[STAGE];
+  __shared__ __align__(16) float st2[NS == 3 ? STAGE : 4];
+  const int b = blockIdx.x;
+  if (b < p.nb)
+    gemm_f32_dma_tile<BM, BN, NS, false, true, X3>(b, p.nb, p.M, p.N, p.K, p.A, p.lda, p.B,
+                                                   p.ldb, p.C, p.ldc, p.alpha, p.beta, p.kmode,
+                                                   p.lower_only, p.tiles_n, st0, st1, st2);
+  else
+    gemm_f32_dma_tile<BM, BN, NS, false, false, X3>(b - p.nb, q.nb, q.M, q.N, q.K, q.A, q.lda,
+                                                    q.B, q.ldb, q.C, q.ldc, q.alpha, q.beta,
+                                                    q.kmode, q.lower_only, q.tiles_n, st0, st1,
+                                                    st2);
 }
 
 // ---------------------------------------------------------------------------
@@ -800,6 +850,32 @@ hipError_t launch_gemm_eh(int64_t M, int64_t N, int64_t K, const float* E, int64
     else GPTQ_EH(false, 4, 128);
   }
 #undef GPTQ_EH
+  return hipGetLastError();
+}
+
+// The conditions under which launch_gemm_f32 takes 64 x 64 tiles, three
+// stages and split fp16 products for g.
+bool dma64_split(const GemmArgs& g) {
+  const bool vec = al16(g.A) && al16(g.B) && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
+                   g.M % 4 == 0 && g.N % 4 == 0 && g.K % 4 == 0;
+  const int64_t big = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+  return g.M > 0 && g.N > 0 && vec && g.K % DK == 0 && g.K > 0 && g.split16 && big < 256;
+}
+
+hipError_t launch_gemm_f32_pair(const GemmArgs& g1, const GemmArgs& g2, hipStream_t s) {
+  if (!(dma64_split(g1) && dma64_split(g2) && !g1.transA && g1.transB && !g2.transA &&
+        !g2.transB)) {
+    GPTQ_HIP_TRY(launch_gemm_f32(g1, s));
+    return launch_gemm_f32(g2, s);
+  }
+  auto prob = [](const GemmArgs& g) {
+    const int64_t tm = (g.M + 63) / 64, tn = (g.N + 63) / 64;
+    return DmaProblem{g.M, g.N, g.K, g.A, g.lda, g.B, g.ldb, g.C, g.ldc, g.alpha, g.beta,
+                      g.kmode, (int)g.lower_only, (int)tn, (int)(tm * tn)};
+  };
+  const DmaProblem p = prob(g1), q = prob(g2);
+  hipLaunchKernelGGL((gemm_f32_dma_pair<64, 64, 3, true>), dim3((unsigned)(p.nb + q.nb)), dim3(256),
+                     0, s, p, q);
   return hipGetLastError();
 }
 

@@ -721,12 +721,12 @@ hipError_t cholinv(PrepCtx& c, int64_t off, int64_t m, float* t2) {
   // L21 = A21 * X11^T  (X11 lower: op(B)[k][j] = X11[j][k] vanishes for k > j)
   GPTQ_HIP_TRY(gemm(c, m2, m1, m1, A21, n, false, X11, n, true, c.T, m1, 1.0f, 0.0f, KR_LE_COL,
                     false));
-  // A22 -= L21 L21^T (lower tiles)
-  GPTQ_HIP_TRY(gemm(c, m2, m2, m1, c.T, m1, false, c.T, m1, true, A22, n, -1.0f, 1.0f, KR_FULL,
-                    true));
-  // T2 = L21 * X11 (X11[k][j] vanishes for k < j)
-  GPTQ_HIP_TRY(gemm(c, m2, m1, m1, c.T, m1, false, X11, n, false, t2, m1, 1.0f, 0.0f, KR_GE_COL,
-                    false));
+  // A22 -= L21 L21^T (lower tiles) and T2 = L21 * X11 (X11[k][j] vanishes
+  // for k < j): both read only L21 and X11, so one launch carries both
+  GemmArgs upd{m2, m2, m1, c.T, m1, false, c.T, m1, true, A22, n, -1.0f, 1.0f, KR_FULL, true};
+  GemmArgs t2p{m2, m1, m1, c.T, m1, false, X11, n, false, t2, m1, 1.0f, 0.0f, KR_GE_COL, false};
+  upd.split16 = t2p.split16 = true;  // operands are O(1) after the scaling
+  GPTQ_HIP_TRY(launch_gemm_f32_pair(upd, t2p, c.s));
   GPTQ_HIP_TRY(cholinv(c, off + m1, m2, next));
   // X21 = -X22 * T2 (X22[i][k] vanishes for k > i)
   GPTQ_HIP_TRY(gemm(c, m2, m1, m2, X22, n, false, t2, m1, false, X21, n, -1.0f, 0.0f, KR_LE_ROW,
