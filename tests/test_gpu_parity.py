@@ -119,9 +119,12 @@ def _oracle_h(cfg, s1=1, tokens=None):
 # n <= 4096 factors 128-column blocks one leaf at a time; above, 512-column
 # blocks through the recursion (4500: eight whole blocks and a ragged one).
 # Odd n (7, 131) take the column-by-column paths of the gather and the final
-# reversal and have a middle row that is its own mirror.
+# reversal and have a middle row that is its own mirror.  4502 (not a
+# multiple of 4) also takes the separate launches where a node's A22 update
+# and T2 otherwise share one (its last block's right child is 150 wide).
 @pytest.mark.parametrize("n,desc", [(7, False), (128, False), (128, True), (131, True),
-                                    (200, True), (1000, True), (1024, False), (4500, True)])
+                                    (200, True), (1000, True), (1024, False), (4500, True),
+                                    (4502, True)])
 def test_prepare_matches_oracle(n, desc):
     _banner(f"prepare n={n} desc={desc}")
     cfg = workloads.get("c1").shrink(inp=n, tokens_per_sample=max(2 * n, 256))
